@@ -1,0 +1,112 @@
+"""Negative controls: copies of the oracle with a planted mistake must fail a pin.
+
+Each mutation edits one line of a copy of oracle/ssd_oracle.c (in a temporary
+directory; the oracle itself is untouched), compiles it, and runs every pin.
+A mutation that no pin catches would mean the pins cannot tell that mistake
+from the correct recurrence.
+"""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ssd_oracle.c")
+
+# (name, exact text in the oracle, replacement)
+MUTATIONS = [
+    ("input_term_dropped", "hp[n] = decay * hp[n] + u * Bt[n];", "hp[n] = decay * hp[n];"),
+    ("decay_dropped", "hp[n] = decay * hp[n] + u * Bt[n];", "hp[n] = hp[n] + u * Bt[n];"),
+    ("decay_applied_to_own_input", "hp[n] = decay * hp[n] + u * Bt[n];",
+     "hp[n] = decay * (hp[n] + u * Bt[n]);"),
+    ("decay_sign_flipped", "const double decay = exp(dtt * Ah);",
+     "const double decay = exp(-dtt * Ah);"),
+    ("skip_term_dropped", "yt[p] = acc + Dh * xt[p];", "yt[p] = acc;"),
+    ("output_reads_B_not_C", "acc += Ct[n] * hp[n];", "acc += Bt[n] * hp[n];"),
+    ("wrong_group_map", "g = hd / heads_per_group;", "g = hd % G;"),
+    ("checkpoint_row_shifted", "const int64_t row = chunk_cu[s] + k / Q;",
+     "const int64_t row = chunk_cu[s] + (k / Q == 0 ? 0 : k / Q - 1);"),
+    ("initial_state_ignored", "if (use_init)\n                memcpy", "if (0)\n                memcpy"),
+    ("dt_not_applied_to_input", "const double u = dtt * xt[p];", "const double u = xt[p];"),
+]
+
+
+def _build_mutant(tmp, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation {name}: text not found in the oracle"
+    mutated = src.replace(old, new, 1)
+    path_c = os.path.join(tmp, f"{name}.c")
+    path_so = os.path.join(tmp, f"lib{name}.so")
+    with open(path_c, "w") as f:
+        f.write(mutated)
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-o",
+                           path_so, path_c, "-lm"])
+    return oracle.load_lib(path_so)
+
+
+@pytest.mark.parametrize("mut", MUTATIONS, ids=lambda m: m[0])
+def test_mutation_is_caught(mut):
+    name, old, new = mut
+    with tempfile.TemporaryDirectory() as tmp:
+        lib = _build_mutant(tmp, name, old, new)
+        caught = []
+        for pin in oracle_pins.ALL_PINS:
+            try:
+                pin(lib=lib)
+            except (AssertionError, ValueError, FloatingPointError):
+                caught.append(pin.__name__)
+        assert caught, f"no pin catches the planted mistake '{name}'"
+
+
+# Planted mistakes in the chunked steps (oracle.chunked), swapped in with monkeypatch.
+import numpy as np  # noqa: E402
+
+from oracle import chunked  # noqa: E402
+
+
+def _bad_chunk_state_sign(x, B, cum, dtp, meta):
+    flipped = cum.copy()
+    for c in range(len(meta["seq"])):
+        ln = int(meta["len"][c])
+        flipped[:, c, :ln] = 2 * cum[:, c, ln - 1][:, None] - cum[:, c, :ln]
+    return _orig["chunk_state"](x, B, flipped, dtp, meta)
+
+
+def _bad_state_passing_no_decay(states, cum, meta, init=None, has_init=None):
+    return _orig["state_passing"](states, np.zeros_like(cum), meta, init, has_init)
+
+
+def _bad_bmm_transposed(B, C, meta, Q):
+    return np.swapaxes(_orig["bmm"](B, C, meta, Q), 2, 3)
+
+
+def _bad_chunk_scan_no_inter(x, C, D, CB, cum, dtp, entering, meta):
+    return _orig["chunk_scan"](x, C, D, CB, cum, dtp, np.zeros_like(entering), meta)
+
+
+def _bad_cumsum_exclusive(dt, A, meta, Q):
+    cum, dtp = _orig["chunk_cumsum"](dt, A, meta, Q)
+    shifted = np.zeros_like(cum)
+    shifted[:, :, 1:] = cum[:, :, :-1]
+    return shifted, dtp
+
+
+_orig = {k: getattr(chunked, k) for k in ("chunk_state", "state_passing", "bmm", "chunk_scan",
+                                            "chunk_cumsum")}
+
+CHUNKED_MUTATIONS = [("chunk_state", _bad_chunk_state_sign),
+                     ("state_passing", _bad_state_passing_no_decay),
+                     ("bmm", _bad_bmm_transposed),
+                     ("chunk_scan", _bad_chunk_scan_no_inter),
+                     ("chunk_cumsum", _bad_cumsum_exclusive)]
+
+
+@pytest.mark.parametrize("mut", CHUNKED_MUTATIONS, ids=lambda m: m[1].__name__)
+def test_chunked_mutation_is_caught(mut, monkeypatch):
+    name, bad = mut
+    monkeypatch.setattr(chunked, name, bad)
+    with pytest.raises(AssertionError):
+        oracle_pins.pin_chunk_size_independence()
