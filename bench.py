@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Throughput of the MI355X SSD varlen prefill scan (and the MTP state update).
+
+One step = one ssd_combined_varlen call (chunk cumsum, bmm, chunk state,
+state passing, chunk scan) over the single-sequence Mamba2 layer prefill:
+L = 4096 tokens, 80 heads, headdim 64, d_state 128, 1 group, chunk 256, bf16
+x/B/C/dt, fp32 A/D/state. Inputs are seeded synthetic draws, resident in HBM
+before the timed region. `value` = tokens / s of that call (one layer).
+
+The same JSON line also carries:
+  roofline      the dominant prefill kernel's algorithmic bytes per launch over
+                its HIP-event-timed average duration, against HBM peak
+  kernels       every prefill kernel's average duration and achieved GB/s
+  decode        the MTP verify state update (128 requests x 3 tokens, 128 heads,
+                bf16 cache of 512 slots, intermediate states kept): updates / s
+                and its roofline
+  cpu_baseline  the CPU oracle (float64 recurrence) on the same prefill, timed on
+                this host's cores
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 256 MiB device copy (for scaling HBM counters)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------------------
+# algorithmic bytes per launch of each prefill kernel (what the kernel must move at least)
+
+def prefill_bytes(T, S, H, P, N, G, Q, nc, ex, es, s_init, checkpoints):
+    f = 4
+    st = nc * H * P * N * f                 # chunk states / entering states (fp32)
+    per_chunk = 2 * H * nc * Q * f          # dA_cumsum + dt per chunk position (fp32)
+    cb = nc * G * (Q // 16) * (Q // 16 + 1) // 2 * 256 * f   # causal 16x16 tiles of CB
+    return {
+        "chunk_cumsum": T * H * ex + per_chunk,
+        "bmm_chunk": 2 * T * G * N * ex + cb,
+        "chunk_state": T * H * P * ex + T * G * N * ex + per_chunk + st,
+        "state_passing": 2 * st + (s_init + S) * H * P * N * es
+                         + (nc * H * P * N * es if checkpoints else 0),
+        "chunk_scan": 2 * T * H * P * ex + T * G * N * ex + per_chunk + cb + st,
+    }
+
+
+def source_sha(path):
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel):
+    """HBM traffic of a kernel from committed counter runs (profiles/traffic_<kernel>.json),
+    valid only while the kernel source it was taken on is unchanged."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    src = os.path.join(ROOT, rec.get("source", ""))
+    if not os.path.exists(src) or source_sha(src) != rec.get("source_sha"):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported; the scan shards by heads or sequences with no exchange, so "
+              "the one-GPU figure is the per-GPU figure.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import ssd_synth as sy
+    import state_space_model_varlen_amd as ssd
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    # ------------------------------------------------------------------ prefill inputs
+    cfg = sy.C1
+    inp = sy.make_prefill(cfg)
+    T, S, H, P, N, G, Q = (cfg.total_tokens, cfg.num_seqs, cfg.nheads, cfg.headdim, cfg.d_state,
+                           cfg.ngroups, cfg.chunk_size)
+    p = ssd.make_problem(T, S, H, P, N, G, Q, 1, cfg.in_dtype, cfg.state_dtype)
+    x, dt, A, B, C, D = (t.to(dev) for t in (inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D))
+    cu, idx = inp.cu_seqlens.to(dev), inp.state_indices.to(dev)
+    cache = torch.zeros(1, H, P, N, dtype=cfg.state_dtype, device=dev)
+    y = torch.empty(T, H, P, dtype=cfg.in_dtype, device=dev)
+    ws = ssd.alloc_workspace(p, dev)
+    torch.cuda.synchronize()
+
+    def step():
+        ssd.ssd_combined_varlen(p, x, dt, A, B, C, D, cu, cache, idx, None, y, None, ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    elapsed = max(wall, gpu_ms / 1e3)
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = T * args.steps / elapsed
+
+    # ------------------------------------------------------------------ per-kernel timing
+    nc = int(np.ceil(T / Q))
+    buf = ssd.alloc_step_buffers(p, dev)
+    launches = {
+        "chunk_cumsum": lambda: ssd.ssd_chunk_cumsum(p, dt, A, cu, buf["chunk_meta"],
+                                                     buf["dA_cumsum"], buf["dt_chunk"], stream),
+        "bmm_chunk": lambda: ssd.ssd_bmm_chunk(p, B, C, buf["chunk_meta"], buf["CB"], stream),
+        "chunk_state": lambda: ssd.ssd_chunk_state(p, x, B, buf["chunk_meta"], buf["dA_cumsum"],
+                                                   buf["dt_chunk"], buf["chunk_states"], stream),
+        "state_passing": lambda: ssd.ssd_state_passing(p, buf["chunk_states"], buf["dA_cumsum"],
+                                                       buf["chunk_meta"], cache, idx, None,
+                                                       buf["entering"], None, stream),
+        "chunk_scan": lambda: ssd.ssd_chunk_scan(p, x, C, D, buf["chunk_meta"], buf["dA_cumsum"],
+                                                 buf["dt_chunk"], buf["CB"], buf["entering"], y,
+                                                 stream),
+    }
+    for fn in launches.values():      # one pass to fill every intermediate
+        fn()
+    torch.cuda.synchronize()
+    nb = prefill_bytes(T, S, H, P, N, G, Q, nc, 2, 4, 0, False)
+    kernels = {}
+    reps = max(args.steps, 10)
+    for name, fn in launches.items():
+        for _ in range(3):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+        kernels[name] = {"avg_us": round(us, 3), "bytes": nb[name],
+                         "GBps": round(nb[name] / (us * 1e-6) / 1e9, 1)}
+    dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    dk = kernels[dom]
+    traffic = load_traffic(dom)
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": dk["GBps"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(dk["GBps"] / HBM_PEAK_GBS, 4),
+                "traffic": traffic}
+
+    # ------------------------------------------------------------------ decode / MTP verify
+    dcfg = sy.C4
+    dd = sy.make_decode(dcfg)
+    R, TT, DH, DP, DN, DG = (dcfg.num_reqs, dcfg.tokens_per_req, dcfg.nheads, dcfg.headdim,
+                             dcfg.d_state, dcfg.ngroups)
+    up = ssd.make_ssu_problem(R, TT, DH, DP, DN, DG, dcfg.num_slots, dcfg.in_dtype,
+                              dcfg.state_dtype)
+    gen = torch.Generator(device=dev).manual_seed(4)
+    dcache = (torch.randn(dcfg.num_slots, DH, DP, DN, device=dev, generator=gen) * 0.03
+              ).to(dcfg.state_dtype)
+    dx, ddt, dA, dB, dC, dD = (t.to(dev) for t in (dd.x, dd.dt, dd.A, dd.B, dd.C, dd.D))
+    didx = dd.state_indices.to(dev)
+    dy = torch.empty(R, TT, DH, DP, dtype=dcfg.in_dtype, device=dev)
+    inter = torch.empty(R, TT, DH, DP, DN, dtype=dcfg.state_dtype, device=dev)
+    for _ in range(3):
+        ssd.selective_state_update(up, dcache, didx, dx, ddt, dA, dB, dC, dD, dy, inter, stream)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        ssd.selective_state_update(up, dcache, didx, dx, ddt, dA, dB, dC, dD, dy, inter, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ssu_us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    es = 2
+    ssu_bytes = R * DH * DP * DN * es * (1 + TT) + R * TT * (2 * DH * DP + 2 * DG * DN + DH) * 2
+    decode = {"workload": "mtp_verify R=128 T=3 H=128 P=64 N=128 G=8 bf16 cache 512 slots",
+              "metric": "decode updates/s", "value": round(R * TT / (ssu_us * 1e-6), 1),
+              "unit": "updates/s", "avg_us": round(ssu_us, 3),
+              "roofline": {"kernel": "selective_state_update", "bound": "hbm",
+                           "achieved": round(ssu_bytes / (ssu_us * 1e-6) / 1e9, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(ssu_bytes / (ssu_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                           "traffic": load_traffic("selective_state_update"),
+                           "bytes": ssu_bytes}}
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    # ------------------------------------------------------------------ CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        nthreads = oracle.max_threads()
+        xs, dts, Bs, Cs = (oracle.f64(t) for t in (inp.x, inp.dt, inp.B, inp.C))
+        best = None
+        for _ in range(3):
+            t1 = time.perf_counter()
+            oracle.recurrence(xs, dts, inp.A, Bs, Cs, inp.D, inp.cu_seqlens.numpy(), Q,
+                              nthreads=nthreads)
+            d = time.perf_counter() - t1
+            best = d if best is None else min(best, d)
+        cpu = {"value": round(T / best, 1), "unit": "tokens/s", "cores": nthreads,
+               "kind": "oracle",
+               "sample": f"the whole layer prefill (4096 tokens x 80 heads, float64 recurrence), "
+                         f"best of 3 wall-clock runs of {best:.3f} s on {nthreads} threads"}
+
+    out = {
+        "metric": "SSD prefill tokens/s per layer + decode updates/s; % MFMA / HBM roofline",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "mamba2_ssd_prefill_L4096_H80_P64_N128_G1_Q256",
+                   "seq_len": T, "num_seqs": S, "nheads": H, "headdim": P, "d_state": N,
+                   "ngroups": G, "chunk_size": Q, "inputs": "bf16 x/B/C/dt, fp32 A/D/state",
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "kernels": kernels,
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

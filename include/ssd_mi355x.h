@@ -1,0 +1,251 @@
+/*
+ * ssd_mi355x.h - C ABI of the MI355X (gfx950) Mamba2 SSD varlen scan and the
+ * decode / MTP selective state update.
+ *
+ * What the operations compute (per head h, group g = h / (H / G), state h_t
+ * of shape [P x N]):
+ *
+ *     h_t = exp(dt_t * A_h) * h_{t-1} + dt_t * x_t (outer) B_t
+ *     y_t = h_t . C_t + D_h * x_t                         (contraction over N)
+ *
+ * the selective state-space recurrence whose recurrent state the pages cache
+ * and roll back (vLLM PR #52928 "[Mamba] Add FlashInfer ReplaySSM support
+ * for MTP", section "Summary") and whose FP32 recurrence they keep (vLLM PR
+ * #62922, section "Details"). Prefill evaluates it with the chunked SSD scan
+ * in the pages' five steps - chunk cumsum, chunk state, state passing, bmm,
+ * chunk scan (vLLM PR #61501, section "Details") - over packed varlen batches
+ * given by cu_seqlens, with initial states read from a slot-indexed state
+ * cache inside state passing and every chunk's entering state kept in the
+ * workspace for chunk scan (vLLM PR #62922, sections "Overview", "Details").
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Pointers are device pointers unless the argument says "host". Problem
+ *   descriptors (ssd_problem, ssu_problem) are host structs read during the
+ *   call only.
+ * - Layouts are row-major and contiguous, last index fastest:
+ *     x, y [T,H,P]; dt [T,H]; A, D [H] float32; B, C [T,G,N];
+ *     cu_seqlens [S+1] int32 with cu_seqlens[0] = 0, non-decreasing,
+ *       cu_seqlens[S] = T; state_indices [S] int32; has_initial_state [S] uint8;
+ *     state cache [num_slots,H,P,N]; checkpoints [max_chunks,H,P,N].
+ *   Every array pointer must be 16-byte aligned.
+ * - Chunks: sequence s is split into ceil(L_s / Q) chunks of Q tokens starting
+ *   at its first token, the last one possibly partial; no chunk spans two
+ *   sequences. chunk_cu[s] = sum over s' < s of ceil(L_s' / Q) numbers them;
+ *   nc = chunk_cu[S] <= max_chunks = T / Q + S (ssd_max_chunks).
+ * - Ownership: the caller allocates every buffer, workspace included. The
+ *   library allocates nothing, keeps no pointer after returning and holds no
+ *   mutable global state, so concurrent calls on different buffers are safe.
+ * - Asynchrony: every call only enqueues work on `stream` (a hipStream_t;
+ *   NULL = the default stream) and never synchronises the host.
+ * - Errors: arguments are validated on the host before anything is enqueued;
+ *   a failed check returns its status and writes nothing. SSD_ERR_HIP reports
+ *   a launch failure. Device-resident values (cu_seqlens, state_indices,
+ *   num_accepted) are not read by the host: kernels clamp token ranges to
+ *   [0, T) and chunk numbers to max_chunks, skip a slot index outside
+ *   [0, num_slots) (its initial state counts as zero and nothing is written
+ *   there) and skip an accepted count outside [0, tokens_per_req), so bad
+ *   device data gives wrong numbers, never an out-of-bounds access.
+ *   Duplicate slot indices within one call are a caller error (the writes
+ *   race).
+ * - Precision: all recurrence arithmetic in float32. With bf16 inputs the
+ *   dense intra-chunk contractions run on bf16 MFMA with float32 accumulation;
+ *   results are rounded to their storage dtype (round to nearest even) only
+ *   when stored.
+ * - Supported on the GPU: headdim P in {16, 64}, d_state N in {16, 128},
+ *   chunk_size Q in {32, 64, 128, 256}, dtypes float32 and bfloat16. Other
+ *   shapes return SSD_ERR_UNSUPPORTED.
+ */
+#ifndef SSD_MI355X_H
+#define SSD_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_ABI_VERSION 1
+
+enum ssd_status {
+    SSD_OK = 0,
+    SSD_ERR_NULL = 1,        /* a required pointer is NULL */
+    SSD_ERR_SHAPE = 2,       /* a size is negative / zero where it must not be, or H % G != 0 */
+    SSD_ERR_DTYPE = 3,       /* unknown dtype code */
+    SSD_ERR_UNSUPPORTED = 4, /* valid but not built for the GPU (P, N, Q outside the sets above) */
+    SSD_ERR_WORKSPACE = 5,   /* workspace smaller than ssd_workspace_bytes() */
+    SSD_ERR_HIP = 6,         /* a kernel launch failed */
+    SSD_ERR_ALIGN = 7        /* an array pointer is not 16-byte aligned */
+};
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+/* One packed varlen prefill (host struct). */
+typedef struct {
+    int32_t total_tokens; /* T: tokens of all sequences together */
+    int32_t num_seqs;     /* S */
+    int32_t nheads;       /* H */
+    int32_t headdim;      /* P */
+    int32_t d_state;      /* N */
+    int32_t ngroups;      /* G: heads h share B, C group h / (H / G) */
+    int32_t chunk_size;   /* Q */
+    int32_t num_slots;    /* rows of the state cache */
+    int32_t in_dtype;     /* ssd_dtype of x, dt, B, C, y */
+    int32_t state_dtype;  /* ssd_dtype of the state cache and the checkpoints */
+} ssd_problem;
+
+/* One decode / MTP verify batch (host struct). */
+typedef struct {
+    int32_t num_reqs;       /* R */
+    int32_t tokens_per_req; /* T: 1 for plain decode, 1 + drafts for MTP verify */
+    int32_t nheads;         /* H */
+    int32_t headdim;        /* P */
+    int32_t d_state;        /* N */
+    int32_t ngroups;        /* G */
+    int32_t num_slots;      /* rows of the state cache */
+    int32_t in_dtype;       /* ssd_dtype of x, dt, B, C, y */
+    int32_t state_dtype;    /* ssd_dtype of the state cache and the intermediate states */
+} ssu_problem;
+
+/* SSD_ABI_VERSION of the built library. */
+int ssd_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char *ssd_status_string(int status);
+
+/* Host-side sizing helpers; they validate `p` and return 0 when it is invalid. */
+int64_t ssd_max_chunks(const ssd_problem *p);      /* T / Q + S */
+int64_t ssd_chunk_meta_count(const ssd_problem *p); /* int32 entries of chunk_meta */
+size_t ssd_workspace_bytes(const ssd_problem *p);  /* for ssd_combined_varlen */
+
+/*
+ * Step 1 - chunk metadata and chunk cumsum (vLLM PR #61501, section
+ * "Details": the first of the five steps; chunk metadata derived on the device
+ * from cu_seqlens, so no host synchronisation is needed).
+ *   dt          [T,H] in_dtype, post-activation step sizes
+ *   A           [H] float32
+ *   cu_seqlens  [S+1] int32
+ *   chunk_meta  out, int32 [ssd_chunk_meta_count]:
+ *                 [0..S]            chunk_cu
+ *                 [S+1+3c+0,1,2]    sequence, first token, token count of chunk c
+ *                                   (-1, 0, 0 for c >= nc)
+ *   dA_cumsum   out, float32 [H, max_chunks, Q]: inclusive cumsum of dt*A_h over
+ *               the chunk's tokens; positions past the chunk's end hold its last value
+ *   dt_chunk    out, float32 [H, max_chunks, Q]: dt per chunk position, 0 past the end
+ * Rows c >= nc of dA_cumsum / dt_chunk are left unwritten.
+ */
+int ssd_chunk_cumsum(const ssd_problem *p, const void *dt, const float *A,
+                     const int32_t *cu_seqlens, int32_t *chunk_meta, float *dA_cumsum,
+                     float *dt_chunk, void *stream);
+
+/*
+ * Step 2 - chunk state (vLLM PR #61501, section "Details"): the state each
+ * chunk produces from a zero entering state,
+ *   S_c[h,p,n] = sum_t exp(cum_last - cum_t) * dt_t * x_t[h,p] * B_t[g,n].
+ *   x [T,H,P], B [T,G,N] in_dtype; chunk_meta, dA_cumsum, dt_chunk from step 1
+ *   chunk_states out, float32 [max_chunks,H,P,N] (rows c >= nc unwritten)
+ */
+int ssd_chunk_state(const ssd_problem *p, const void *x, const void *B,
+                    const int32_t *chunk_meta, const float *dA_cumsum, const float *dt_chunk,
+                    float *chunk_states, void *stream);
+
+/*
+ * Step 3 - state passing, reading initial states from the cache by slot and
+ * writing final states back in place (vLLM PR #62922, sections "Overview" and
+ * "Details"; vLLM PR #61501, section "Details": gather only where a sequence
+ * has an initial state, scatter final states into their slots in the cache
+ * dtype; checkpoints for prefills that store every chunk state). Per sequence
+ * s and head h, sequentially over its chunks:
+ *   H_0 = has_initial_state[s] ? cache[state_indices[s], h] : 0
+ *   entering_states[c] = H_c;  H_{c+1} = exp(cum_last(c)) * H_c + S_c
+ *   checkpoints[c] = round(H_{c+1})       (exit state of chunk c)
+ *   cache[state_indices[s], h] = round(H_last)   (after all reads of that slot)
+ *   state_cache       in/out [num_slots,H,P,N] state_dtype; slots not named in
+ *                     state_indices are not touched
+ *   state_indices     [S] int32
+ *   has_initial_state [S] uint8, or NULL: no sequence reads its slot
+ *   entering_states   out float32 [max_chunks,H,P,N]; may be the same buffer as
+ *                     chunk_states (each element is read before it is overwritten)
+ *   checkpoints       out [max_chunks,H,P,N] state_dtype, or NULL to skip
+ * A zero-length sequence writes its initial state (or zeros) back to its slot.
+ */
+int ssd_state_passing(const ssd_problem *p, const float *chunk_states, const float *dA_cumsum,
+                      const int32_t *chunk_meta, void *state_cache,
+                      const int32_t *state_indices, const uint8_t *has_initial_state,
+                      float *entering_states, void *checkpoints, void *stream);
+
+/*
+ * Step 4 - bmm (vLLM PR #61501, section "Details"): CB[c,g,i,j] = C_i . B_j
+ * inside each chunk. B, C [T,G,N] in_dtype; CB out float32
+ * [max_chunks,G,Q,Q]. Defined for j <= i < chunk length (the causal part chunk
+ * scan reads); other entries are unspecified.
+ */
+int ssd_bmm_chunk(const ssd_problem *p, const void *B, const void *C,
+                  const int32_t *chunk_meta, float *CB, void *stream);
+
+/*
+ * Step 5 - chunk scan (vLLM PR #61501, section "Details"; entering states from
+ * the workspace, vLLM PR #62922, section "Details"):
+ *   y_i = sum_{j<=i} CB[i,j] * exp(cum_i - cum_j) * dt_j * x_j
+ *         + exp(cum_i) * (H_in . C_i) + D_h * x_i
+ *   x [T,H,P], C [T,G,N] in_dtype; D [H] float32 or NULL (= 0); CB from step 4;
+ *   entering_states from step 3; y out [T,H,P] in_dtype.
+ */
+int ssd_chunk_scan(const ssd_problem *p, const void *x, const void *C, const float *D,
+                   const int32_t *chunk_meta, const float *dA_cumsum, const float *dt_chunk,
+                   const float *CB, const float *entering_states, void *y, void *stream);
+
+/*
+ * The whole prefill: steps 1-5 enqueued on one stream with no host
+ * synchronisation, intermediates in the caller's workspace (vLLM PR #61501,
+ * sections "Details" and "Claims"; vLLM PR #62922, section "Details").
+ * Semantics are those of the five steps composed: every initial state is
+ * read as it was before the call even though the call overwrites the slot.
+ *   workspace        device buffer of at least ssd_workspace_bytes(p) bytes,
+ *                    256-byte aligned; its contents on entry do not matter
+ *   checkpoints      [max_chunks,H,P,N] state_dtype or NULL
+ * Sizes with num_seqs = 0 or total_tokens = 0 enqueue nothing beyond
+ * zero-length write-backs.
+ */
+int ssd_combined_varlen(const ssd_problem *p, const void *x, const void *dt, const float *A,
+                        const void *B, const void *C, const float *D, const int32_t *cu_seqlens,
+                        void *state_cache, const int32_t *state_indices,
+                        const uint8_t *has_initial_state, void *y, void *checkpoints,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Decode / MTP verify state update (vLLM PR #52928, sections "Summary" and
+ * "Design": one target token plus draft tokens per request, (batch, tokens, ...)
+ * inputs; vLLM PR #55688, review of the SSU dispatch: the plain
+ * selective_state_update next to the ReplaySSM kernels). Per request r and head h, starting from
+ * state_cache[state_indices[r], h], the recurrence runs over the request's T
+ * tokens in float32; y_t is written for every token. With
+ * intermediate_states non-NULL the state after token t is stored (rounded)
+ * at intermediate_states[r, t] - what a rollback to t accepted drafts reads -
+ * and the cache is not written; with NULL the state after the last token is
+ * rounded and written back to the slot.
+ *   x, y [R,T,H,P]; dt [R,T,H]; B, C [R,T,G,N] in_dtype; A, D [H] float32 (D may be NULL)
+ *   state_cache [num_slots,H,P,N] state_dtype; state_indices [R] int32
+ *   intermediate_states [R,T,H,P,N] state_dtype or NULL
+ */
+int selective_state_update(const ssu_problem *p, void *state_cache, const int32_t *state_indices,
+                           const void *x, const void *dt, const float *A, const void *B,
+                           const void *C, const float *D, void *y, void *intermediate_states,
+                           void *stream);
+
+/*
+ * Rollback / commit to the accepted count (vLLM PR #52928, section "Summary":
+ * the accepted length decides the next state): for every request r with
+ * 0 <= num_accepted[r] < T, copy intermediate_states[r, num_accepted[r]] into
+ * state_cache[state_indices[r]]. num_accepted [R] int32 counts accepted draft
+ * tokens (the target token is always accepted).
+ */
+int ssd_state_commit(const ssu_problem *p, void *state_cache, const int32_t *state_indices,
+                     const void *intermediate_states, const int32_t *num_accepted, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_MI355X_H */

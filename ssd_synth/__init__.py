@@ -16,7 +16,8 @@ Generator: numpy PCG64 seeded with ``[cfg, stream, ...]``.
   stream 0 -> layer parameters, drawn in the order A, dt_bias, D
   stream 1 -> tokens, drawn in the order x, z (dt pre-activation), B, C
   stream 2 -> state_indices (a random permutation of the cache slots)
-  stream [3, s] -> the prefix tokens of sequence / request s
+  stream [3, s] -> the prefix tokens of sequence / request s (drawn on demand)
+  stream 4 -> accepted-draft counts of the MTP verify batch
 Values are drawn in float64 and then cast to the input dtype (round to nearest
 even, through torch).
 
@@ -156,7 +157,17 @@ class PrefillInputs:
     cu_seqlens: torch.Tensor  # [S+1] int32
     state_indices: torch.Tensor  # [S] int32
     has_initial: Optional[torch.Tensor]  # [S] uint8 or None
-    prefix: list             # per sequence: None or (x, dt, B, C) of its prefix, in_dtype
+    dt_bias: np.ndarray = None
+
+    def prefix_tokens(self, s: int):
+        """(x, dt, B, C) of sequence s's seeded prefix (in_dtype), or None when the
+        sequence starts from zero. Drawn on demand from stream [seed, 3, s]."""
+        if self.has_initial is None or not int(self.has_initial[s]):
+            return None
+        c = self.cfg
+        px, pdt, pB, pC = token_block(_rng(c.seed, 3, s), c.prefix_len, c.nheads, c.headdim,
+                                      c.ngroups, c.d_state, self.dt_bias)
+        return tuple(to_dtype(v, c.in_dtype) for v in (px, pdt, pB, pC))
 
 
 def make_prefill(cfg: PrefillConfig, seqlens: Optional[Sequence[int]] = None) -> PrefillInputs:
@@ -172,22 +183,16 @@ def make_prefill(cfg: PrefillConfig, seqlens: Optional[Sequence[int]] = None) ->
     perm = _rng(cfg.seed, 2).permutation(cfg.num_slots).astype(np.int32)
     idx = perm[: len(lens)]
     has_init = None
-    prefix = [None] * len(lens)
     if cfg.any_initial:
         flags = [bool(cfg.has_initial[i % len(cfg.has_initial)]) for i in range(len(lens))]
         has_init = torch.tensor([1 if f else 0 for f in flags], dtype=torch.uint8)
-        for s, f in enumerate(flags):
-            if f:
-                px, pdt, pB, pC = token_block(_rng(cfg.seed, 3, s), cfg.prefix_len, H, P, G, N,
-                                              dt_bias)
-                prefix[s] = tuple(to_dtype(v, cfg.in_dtype) for v in (px, pdt, pB, pC))
     return PrefillInputs(
         cfg=cfg,
         x=to_dtype(x, cfg.in_dtype), dt=to_dtype(dt, cfg.in_dtype),
         A=to_dtype(A, torch.float32), B=to_dtype(B, cfg.in_dtype), C=to_dtype(C, cfg.in_dtype),
         D=to_dtype(D, torch.float32),
         cu_seqlens=torch.from_numpy(cu), state_indices=torch.from_numpy(idx.copy()),
-        has_initial=has_init, prefix=prefix)
+        has_initial=has_init, dt_bias=dt_bias)
 
 
 @dataclasses.dataclass
@@ -201,7 +206,14 @@ class DecodeInputs:
     D: torch.Tensor    # [H] float32
     state_indices: torch.Tensor  # [R] int32
     num_accepted: torch.Tensor   # [R] int32 in [0, T)
-    prefix: list       # per request: (x, dt, B, C) of its prefix [L,H,P] etc.
+    dt_bias: np.ndarray = None
+
+    def prefix_tokens(self, r: int):
+        """(x [L,H,P], dt [L,H], B [L,G,N], C [L,G,N]) of request r's seeded prefix."""
+        c = self.cfg
+        px, pdt, pB, pC = token_block(_rng(c.seed, 3, r), c.prefix_len, c.nheads, c.headdim,
+                                      c.ngroups, c.d_state, self.dt_bias)
+        return tuple(to_dtype(v, c.in_dtype) for v in (px, pdt, pB, pC))
 
 
 def make_decode(cfg: DecodeConfig, num_reqs: Optional[int] = None) -> DecodeInputs:
@@ -211,10 +223,6 @@ def make_decode(cfg: DecodeConfig, num_reqs: Optional[int] = None) -> DecodeInpu
     x, dt, B, C = token_block(_rng(cfg.seed, 1), R * T, H, P, G, N, dt_bias)
     perm = _rng(cfg.seed, 2).permutation(cfg.num_slots).astype(np.int32)
     acc = _rng(cfg.seed, 4).integers(0, T, size=R).astype(np.int32)
-    prefix = []
-    for r in range(R):
-        px, pdt, pB, pC = token_block(_rng(cfg.seed, 3, r), cfg.prefix_len, H, P, G, N, dt_bias)
-        prefix.append(tuple(to_dtype(v, cfg.in_dtype) for v in (px, pdt, pB, pC)))
     return DecodeInputs(
         cfg=cfg,
         x=to_dtype(x.reshape(R, T, H, P), cfg.in_dtype),
@@ -224,8 +232,7 @@ def make_decode(cfg: DecodeConfig, num_reqs: Optional[int] = None) -> DecodeInpu
         C=to_dtype(C.reshape(R, T, G, N), cfg.in_dtype),
         D=to_dtype(D, torch.float32),
         state_indices=torch.from_numpy(perm[:R].copy()),
-        num_accepted=torch.from_numpy(acc),
-        prefix=prefix)
+        num_accepted=torch.from_numpy(acc), dt_bias=dt_bias)
 
 
 def random_problem(seed: int, seqlens: Sequence[int], nheads: int, headdim: int, d_state: int,

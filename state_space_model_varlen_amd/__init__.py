@@ -1,0 +1,303 @@
+"""Python binding of the MI355X SSD library (``libssd_mi355x.so``, C ABI in
+``include/ssd_mi355x.h``).
+
+Argument marshalling only: every function checks the torch tensors it is
+given against the problem sizes (device, dtype, shape, contiguity), passes
+their device pointers and the current HIP stream to the C entry point of the
+same name, and raises on a non-zero status. All arithmetic runs in the HIP
+kernels; there is no CPU or PyTorch fallback - importing this package fails
+loudly when the library has not been built.
+
+Layouts (row-major): x, y [T,H,P]; dt [T,H]; A, D [H] float32; B, C [T,G,N];
+cu_seqlens [S+1] int32; state_indices [S] int32; has_initial_state [S] uint8;
+state cache [num_slots,H,P,N]; checkpoints [max_chunks,H,P,N].
+Decode: x, y [R,T,H,P]; dt [R,T,H]; B, C [R,T,G,N]; intermediate states
+[R,T,H,P,N]; num_accepted [R] int32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libssd_mi355x.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+        "or `python state_space_model_varlen_amd/_build.py` (hipcc, gfx950)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+SSD_OK = 0
+F32, BF16 = 0, 1
+_DT = {torch.float32: F32, torch.bfloat16: BF16}
+_TORCH = {F32: torch.float32, BF16: torch.bfloat16}
+
+
+class ssd_problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "total_tokens", "num_seqs", "nheads", "headdim", "d_state", "ngroups", "chunk_size",
+        "num_slots", "in_dtype", "state_dtype")]
+
+
+class ssu_problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_reqs", "tokens_per_req", "nheads", "headdim", "d_state", "ngroups", "num_slots",
+        "in_dtype", "state_dtype")]
+
+
+_vp = ctypes.c_void_p
+_pp = ctypes.POINTER(ssd_problem)
+_up = ctypes.POINTER(ssu_problem)
+_SIGS = {
+    "ssd_abi_version": ([], ctypes.c_int),
+    "ssd_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "ssd_max_chunks": ([_pp], ctypes.c_int64),
+    "ssd_chunk_meta_count": ([_pp], ctypes.c_int64),
+    "ssd_workspace_bytes": ([_pp], ctypes.c_size_t),
+    "ssd_chunk_cumsum": ([_pp] + [_vp] * 7, ctypes.c_int),
+    "ssd_chunk_state": ([_pp] + [_vp] * 7, ctypes.c_int),
+    "ssd_state_passing": ([_pp] + [_vp] * 9, ctypes.c_int),
+    "ssd_bmm_chunk": ([_pp] + [_vp] * 5, ctypes.c_int),
+    "ssd_chunk_scan": ([_pp] + [_vp] * 10, ctypes.c_int),
+    "ssd_combined_varlen": ([_pp] + [_vp] * 13 + [ctypes.c_size_t, _vp], ctypes.c_int),
+    "selective_state_update": ([_up] + [_vp] * 11, ctypes.c_int),
+    "ssd_state_commit": ([_up] + [_vp] * 5, ctypes.c_int),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _res
+
+EXPORTED = tuple(_SIGS)
+
+
+class SSDError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def abi_version() -> int:
+    return int(_lib.ssd_abi_version())
+
+
+def status_string(status: int) -> str:
+    return _lib.ssd_status_string(int(status)).decode()
+
+
+# ---------------------------------------------------------------------------
+# problem descriptors
+
+def make_problem(total_tokens: int, num_seqs: int, nheads: int, headdim: int, d_state: int,
+                 ngroups: int, chunk_size: int, num_slots: int, in_dtype: torch.dtype,
+                 state_dtype: torch.dtype) -> ssd_problem:
+    return ssd_problem(int(total_tokens), int(num_seqs), int(nheads), int(headdim), int(d_state),
+                       int(ngroups), int(chunk_size), int(num_slots), _DT[in_dtype],
+                       _DT[state_dtype])
+
+
+def make_ssu_problem(num_reqs: int, tokens_per_req: int, nheads: int, headdim: int, d_state: int,
+                     ngroups: int, num_slots: int, in_dtype: torch.dtype,
+                     state_dtype: torch.dtype) -> ssu_problem:
+    return ssu_problem(int(num_reqs), int(tokens_per_req), int(nheads), int(headdim),
+                       int(d_state), int(ngroups), int(num_slots), _DT[in_dtype],
+                       _DT[state_dtype])
+
+
+def max_chunks(p: ssd_problem) -> int:
+    return int(_lib.ssd_max_chunks(ctypes.byref(p)))
+
+
+def chunk_meta_count(p: ssd_problem) -> int:
+    return int(_lib.ssd_chunk_meta_count(ctypes.byref(p)))
+
+
+def workspace_bytes(p: ssd_problem) -> int:
+    return int(_lib.ssd_workspace_bytes(ctypes.byref(p)))
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+
+def _stream(stream) -> _vp:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return _vp(stream.cuda_stream)
+    return _vp(int(stream))
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, shape=None, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return _vp(t.data_ptr()) if t.numel() else _vp(t.data_ptr() or 16)
+
+
+def _check(fn: str, rc: int):
+    if rc != SSD_OK:
+        raise SSDError(fn, rc)
+
+
+def _dims(p: ssd_problem):
+    return (p.total_tokens, p.num_seqs, p.nheads, p.headdim, p.d_state, p.ngroups, p.chunk_size,
+            max_chunks(p))
+
+
+# ---------------------------------------------------------------------------
+# prefill steps
+
+def ssd_chunk_cumsum(p: ssd_problem, dt, A, cu_seqlens, chunk_meta, dA_cumsum, dt_chunk,
+                     stream=None):
+    T, S, H, P, N, G, Q, mc = _dims(p)
+    ti = _TORCH[p.in_dtype]
+    rc = _lib.ssd_chunk_cumsum(
+        ctypes.byref(p), _ptr(dt, "dt", ti, (T, H)), _ptr(A, "A", torch.float32, (H,)),
+        _ptr(cu_seqlens, "cu_seqlens", torch.int32, (S + 1,)),
+        _ptr(chunk_meta, "chunk_meta", torch.int32, (chunk_meta_count(p),)),
+        _ptr(dA_cumsum, "dA_cumsum", torch.float32, (H, mc, Q)),
+        _ptr(dt_chunk, "dt_chunk", torch.float32, (H, mc, Q)), _stream(stream))
+    _check("ssd_chunk_cumsum", rc)
+
+
+def ssd_chunk_state(p: ssd_problem, x, B, chunk_meta, dA_cumsum, dt_chunk, chunk_states,
+                    stream=None):
+    T, S, H, P, N, G, Q, mc = _dims(p)
+    ti = _TORCH[p.in_dtype]
+    rc = _lib.ssd_chunk_state(
+        ctypes.byref(p), _ptr(x, "x", ti, (T, H, P)), _ptr(B, "B", ti, (T, G, N)),
+        _ptr(chunk_meta, "chunk_meta", torch.int32, (chunk_meta_count(p),)),
+        _ptr(dA_cumsum, "dA_cumsum", torch.float32, (H, mc, Q)),
+        _ptr(dt_chunk, "dt_chunk", torch.float32, (H, mc, Q)),
+        _ptr(chunk_states, "chunk_states", torch.float32, (mc, H, P, N)), _stream(stream))
+    _check("ssd_chunk_state", rc)
+
+
+def ssd_state_passing(p: ssd_problem, chunk_states, dA_cumsum, chunk_meta, state_cache,
+                      state_indices, has_initial_state, entering_states, checkpoints=None,
+                      stream=None):
+    T, S, H, P, N, G, Q, mc = _dims(p)
+    ts = _TORCH[p.state_dtype]
+    rc = _lib.ssd_state_passing(
+        ctypes.byref(p), _ptr(chunk_states, "chunk_states", torch.float32, (mc, H, P, N)),
+        _ptr(dA_cumsum, "dA_cumsum", torch.float32, (H, mc, Q)),
+        _ptr(chunk_meta, "chunk_meta", torch.int32, (chunk_meta_count(p),)),
+        _ptr(state_cache, "state_cache", ts, (p.num_slots, H, P, N)),
+        _ptr(state_indices, "state_indices", torch.int32, (S,)),
+        _ptr(has_initial_state, "has_initial_state", torch.uint8, (S,), optional=True),
+        _ptr(entering_states, "entering_states", torch.float32, (mc, H, P, N)),
+        _ptr(checkpoints, "checkpoints", ts, (mc, H, P, N), optional=True), _stream(stream))
+    _check("ssd_state_passing", rc)
+
+
+def ssd_bmm_chunk(p: ssd_problem, B, C, chunk_meta, CB, stream=None):
+    T, S, H, P, N, G, Q, mc = _dims(p)
+    ti = _TORCH[p.in_dtype]
+    rc = _lib.ssd_bmm_chunk(
+        ctypes.byref(p), _ptr(B, "B", ti, (T, G, N)), _ptr(C, "C", ti, (T, G, N)),
+        _ptr(chunk_meta, "chunk_meta", torch.int32, (chunk_meta_count(p),)),
+        _ptr(CB, "CB", torch.float32, (mc, G, Q, Q)), _stream(stream))
+    _check("ssd_bmm_chunk", rc)
+
+
+def ssd_chunk_scan(p: ssd_problem, x, C, D, chunk_meta, dA_cumsum, dt_chunk, CB,
+                   entering_states, y, stream=None):
+    T, S, H, P, N, G, Q, mc = _dims(p)
+    ti = _TORCH[p.in_dtype]
+    rc = _lib.ssd_chunk_scan(
+        ctypes.byref(p), _ptr(x, "x", ti, (T, H, P)), _ptr(C, "C", ti, (T, G, N)),
+        _ptr(D, "D", torch.float32, (H,), optional=True),
+        _ptr(chunk_meta, "chunk_meta", torch.int32, (chunk_meta_count(p),)),
+        _ptr(dA_cumsum, "dA_cumsum", torch.float32, (H, mc, Q)),
+        _ptr(dt_chunk, "dt_chunk", torch.float32, (H, mc, Q)),
+        _ptr(CB, "CB", torch.float32, (mc, G, Q, Q)),
+        _ptr(entering_states, "entering_states", torch.float32, (mc, H, P, N)),
+        _ptr(y, "y", ti, (T, H, P)), _stream(stream))
+    _check("ssd_chunk_scan", rc)
+
+
+def ssd_combined_varlen(p: ssd_problem, x, dt, A, B, C, D, cu_seqlens, state_cache,
+                        state_indices, has_initial_state, y, checkpoints, workspace,
+                        stream=None):
+    T, S, H, P, N, G, Q, mc = _dims(p)
+    ti, ts = _TORCH[p.in_dtype], _TORCH[p.state_dtype]
+    if workspace is None or workspace.dtype != torch.uint8 or workspace.dim() != 1:
+        raise ValueError("workspace must be a 1-D uint8 GPU tensor")
+    rc = _lib.ssd_combined_varlen(
+        ctypes.byref(p), _ptr(x, "x", ti, (T, H, P)), _ptr(dt, "dt", ti, (T, H)),
+        _ptr(A, "A", torch.float32, (H,)), _ptr(B, "B", ti, (T, G, N)),
+        _ptr(C, "C", ti, (T, G, N)), _ptr(D, "D", torch.float32, (H,), optional=True),
+        _ptr(cu_seqlens, "cu_seqlens", torch.int32, (S + 1,)),
+        _ptr(state_cache, "state_cache", ts, (p.num_slots, H, P, N)),
+        _ptr(state_indices, "state_indices", torch.int32, (S,)),
+        _ptr(has_initial_state, "has_initial_state", torch.uint8, (S,), optional=True),
+        _ptr(y, "y", ti, (T, H, P)),
+        _ptr(checkpoints, "checkpoints", ts, (mc, H, P, N), optional=True),
+        _ptr(workspace, "workspace", torch.uint8), ctypes.c_size_t(workspace.numel()),
+        _stream(stream))
+    _check("ssd_combined_varlen", rc)
+
+
+# ---------------------------------------------------------------------------
+# decode / MTP
+
+def selective_state_update(p: ssu_problem, state_cache, state_indices, x, dt, A, B, C, D, y,
+                           intermediate_states=None, stream=None):
+    R, T, H, P, N, G = (p.num_reqs, p.tokens_per_req, p.nheads, p.headdim, p.d_state, p.ngroups)
+    ti, ts = _TORCH[p.in_dtype], _TORCH[p.state_dtype]
+    rc = _lib.selective_state_update(
+        ctypes.byref(p), _ptr(state_cache, "state_cache", ts, (p.num_slots, H, P, N)),
+        _ptr(state_indices, "state_indices", torch.int32, (R,)),
+        _ptr(x, "x", ti, (R, T, H, P)), _ptr(dt, "dt", ti, (R, T, H)),
+        _ptr(A, "A", torch.float32, (H,)), _ptr(B, "B", ti, (R, T, G, N)),
+        _ptr(C, "C", ti, (R, T, G, N)), _ptr(D, "D", torch.float32, (H,), optional=True),
+        _ptr(y, "y", ti, (R, T, H, P)),
+        _ptr(intermediate_states, "intermediate_states", ts, (R, T, H, P, N), optional=True),
+        _stream(stream))
+    _check("selective_state_update", rc)
+
+
+def ssd_state_commit(p: ssu_problem, state_cache, state_indices, intermediate_states,
+                     num_accepted, stream=None):
+    R, T, H, P, N = p.num_reqs, p.tokens_per_req, p.nheads, p.headdim, p.d_state
+    ts = _TORCH[p.state_dtype]
+    rc = _lib.ssd_state_commit(
+        ctypes.byref(p), _ptr(state_cache, "state_cache", ts, (p.num_slots, H, P, N)),
+        _ptr(state_indices, "state_indices", torch.int32, (R,)),
+        _ptr(intermediate_states, "intermediate_states", ts, (R, T, H, P, N)),
+        _ptr(num_accepted, "num_accepted", torch.int32, (R,)), _stream(stream))
+    _check("ssd_state_commit", rc)
+
+
+# ---------------------------------------------------------------------------
+# allocation helpers (torch plumbing; no arithmetic)
+
+def alloc_workspace(p: ssd_problem, device="cuda") -> torch.Tensor:
+    return torch.empty(max(workspace_bytes(p), 256), dtype=torch.uint8, device=device)
+
+
+def alloc_step_buffers(p: ssd_problem, device="cuda") -> dict:
+    """Buffers the five prefill steps exchange when called one by one."""
+    T, S, H, P, N, G, Q, mc = _dims(p)
+    f = dict(dtype=torch.float32, device=device)
+    return dict(
+        chunk_meta=torch.empty(chunk_meta_count(p), dtype=torch.int32, device=device),
+        dA_cumsum=torch.empty((H, mc, Q), **f), dt_chunk=torch.empty((H, mc, Q), **f),
+        chunk_states=torch.empty((mc, H, P, N), **f), entering=torch.empty((mc, H, P, N), **f),
+        CB=torch.empty((mc, G, Q, Q), **f))

@@ -1,0 +1,44 @@
+"""Build the HIP library ``libssd_mi355x.so`` in-tree for gfx950 with hipcc."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libssd_mi355x.so")
+SOURCES = ["ssd_api.cpp", "ssd_prefill.hip", "ssd_decode.hip"]
+HEADERS = ["ssd_device.h", "ssd_launch.h"]
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    # packed fp32 instructions stay off (the compiler would otherwise form
+    # v_pk_* from float2 code)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return os.path.join(rocm, "bin", "hipcc")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into the shared library (always rebuilds)."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = LIB + f".tmp{os.getpid()}"
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-I", os.path.join(PKG, "..", "include"), "-o", tmp] + srcs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building libssd_mi355x.so")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

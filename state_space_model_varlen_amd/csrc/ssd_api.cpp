@@ -1,0 +1,286 @@
+// C ABI of the MI355X SSD library: host-side validation, workspace layout and
+// dispatch to the kernel launchers. Nothing here reads device memory or
+// synchronises; every check runs before the first launch of a call.
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+#include "ssd_launch.h"
+#include "../../include/ssd_mi355x.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dtype_ok(int32_t d) { return d == SSD_F32 || d == SSD_BF16; }
+
+bool gpu_shape_ok(int P, int N) { return (P == 16 || P == 64) && (N == 16 || N == 128); }
+
+bool chunk_ok(int Q) { return Q == 32 || Q == 64 || Q == 128 || Q == 256; }
+
+// Shape / dtype checks of a prefill descriptor (no pointers).
+int check_problem(const ssd_problem *p)
+{
+    if (!p) return SSD_ERR_NULL;
+    if (p->total_tokens < 0 || p->num_seqs < 0 || p->nheads <= 0 || p->headdim <= 0 ||
+        p->d_state <= 0 || p->ngroups <= 0 || p->chunk_size <= 0 || p->num_slots < 0)
+        return SSD_ERR_SHAPE;
+    if (p->nheads % p->ngroups != 0) return SSD_ERR_SHAPE;
+    if (p->num_seqs > 0 && p->num_slots <= 0) return SSD_ERR_SHAPE;
+    if (!dtype_ok(p->in_dtype) || !dtype_ok(p->state_dtype)) return SSD_ERR_DTYPE;
+    if (!gpu_shape_ok(p->headdim, p->d_state) || !chunk_ok(p->chunk_size)) return SSD_ERR_UNSUPPORTED;
+    // grid limits: chunks and heads index grid dimensions
+    const int64_t mc = (int64_t)p->total_tokens / p->chunk_size + p->num_seqs;
+    if (mc > 0x7fffffff || p->nheads > 65535) return SSD_ERR_UNSUPPORTED;
+    if ((int64_t)p->num_seqs * p->nheads * ((p->headdim * p->d_state + 1023) / 1024) > 0x7fffffffLL)
+        return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+int check_ssu(const ssu_problem *p)
+{
+    if (!p) return SSD_ERR_NULL;
+    if (p->num_reqs < 0 || p->tokens_per_req < 0 || p->nheads <= 0 || p->headdim <= 0 ||
+        p->d_state <= 0 || p->ngroups <= 0 || p->num_slots < 0)
+        return SSD_ERR_SHAPE;
+    if (p->nheads % p->ngroups != 0) return SSD_ERR_SHAPE;
+    if (p->num_reqs > 0 && p->num_slots <= 0) return SSD_ERR_SHAPE;
+    if (!dtype_ok(p->in_dtype) || !dtype_ok(p->state_dtype)) return SSD_ERR_DTYPE;
+    if (!gpu_shape_ok(p->headdim, p->d_state)) return SSD_ERR_UNSUPPORTED;
+    if (p->nheads > 0x7fffffff / 2 || p->num_reqs > 65535) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+ssd::PrefillDims dims_of(const ssd_problem *p)
+{
+    ssd::PrefillDims d;
+    d.T = p->total_tokens;
+    d.S = p->num_seqs;
+    d.H = p->nheads;
+    d.P = p->headdim;
+    d.N = p->d_state;
+    d.G = p->ngroups;
+    d.Q = p->chunk_size;
+    d.max_chunks = (int)((int64_t)p->total_tokens / p->chunk_size + p->num_seqs);
+    d.num_slots = p->num_slots;
+    d.in_bf16 = p->in_dtype == SSD_BF16;
+    d.state_bf16 = p->state_dtype == SSD_BF16;
+    return d;
+}
+
+ssd::DecodeDims dims_of(const ssu_problem *p)
+{
+    ssd::DecodeDims d;
+    d.R = p->num_reqs;
+    d.T = p->tokens_per_req;
+    d.H = p->nheads;
+    d.P = p->headdim;
+    d.N = p->d_state;
+    d.G = p->ngroups;
+    d.num_slots = p->num_slots;
+    d.in_bf16 = p->in_dtype == SSD_BF16;
+    d.state_bf16 = p->state_dtype == SSD_BF16;
+    return d;
+}
+
+int launch_status()
+{
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+size_t round_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Workspace of ssd_combined_varlen, 256-byte aligned pieces in this order.
+struct Workspace {
+    size_t meta, cum, dt, cb, states, total;
+};
+
+Workspace workspace_layout(const ssd_problem *p)
+{
+    const size_t mc = (size_t)((int64_t)p->total_tokens / p->chunk_size + p->num_seqs);
+    const size_t H = p->nheads, P = p->headdim, N = p->d_state, G = p->ngroups, Q = p->chunk_size;
+    Workspace w;
+    w.meta = 0;
+    w.cum = w.meta + round_up(sizeof(int32_t) * ((size_t)p->num_seqs + 1 + 3 * mc));
+    w.dt = w.cum + round_up(sizeof(float) * H * mc * Q);
+    w.cb = w.dt + round_up(sizeof(float) * H * mc * Q);
+    w.states = w.cb + round_up(sizeof(float) * mc * G * Q * Q);
+    w.total = w.states + round_up(sizeof(float) * mc * H * P * N);
+    return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssd_abi_version(void) { return SSD_ABI_VERSION; }
+
+const char *ssd_status_string(int status)
+{
+    switch (status) {
+    case SSD_OK: return "ok";
+    case SSD_ERR_NULL: return "a required pointer is NULL";
+    case SSD_ERR_SHAPE: return "invalid sizes";
+    case SSD_ERR_DTYPE: return "unknown dtype";
+    case SSD_ERR_UNSUPPORTED: return "shape not supported by the GPU kernels";
+    case SSD_ERR_WORKSPACE: return "workspace too small";
+    case SSD_ERR_HIP: return "HIP launch failure";
+    case SSD_ERR_ALIGN: return "array pointer not 16-byte aligned";
+    default: return "unknown status";
+    }
+}
+
+int64_t ssd_max_chunks(const ssd_problem *p)
+{
+    if (check_problem(p) != SSD_OK) return 0;
+    return (int64_t)p->total_tokens / p->chunk_size + p->num_seqs;
+}
+
+int64_t ssd_chunk_meta_count(const ssd_problem *p)
+{
+    if (check_problem(p) != SSD_OK) return 0;
+    return (int64_t)p->num_seqs + 1 + 3 * ssd_max_chunks(p);
+}
+
+size_t ssd_workspace_bytes(const ssd_problem *p)
+{
+    if (check_problem(p) != SSD_OK) return 0;
+    return workspace_layout(p).total;
+}
+
+int ssd_chunk_cumsum(const ssd_problem *p, const void *dt, const float *A,
+                     const int32_t *cu_seqlens, int32_t *chunk_meta, float *dA_cumsum,
+                     float *dt_chunk, void *stream)
+{
+    int rc = check_problem(p);
+    if (rc) return rc;
+    if (!dt || !A || !cu_seqlens || !chunk_meta || !dA_cumsum || !dt_chunk) return SSD_ERR_NULL;
+    if (!aligned16(dA_cumsum) || !aligned16(dt_chunk)) return SSD_ERR_ALIGN;
+    ssd::launch_chunk_cumsum(dims_of(p), dt, A, cu_seqlens, chunk_meta, dA_cumsum, dt_chunk, stream);
+    return launch_status();
+}
+
+int ssd_chunk_state(const ssd_problem *p, const void *x, const void *B,
+                    const int32_t *chunk_meta, const float *dA_cumsum, const float *dt_chunk,
+                    float *chunk_states, void *stream)
+{
+    int rc = check_problem(p);
+    if (rc) return rc;
+    if (!x || !B || !chunk_meta || !dA_cumsum || !dt_chunk || !chunk_states) return SSD_ERR_NULL;
+    if (!aligned16(x) || !aligned16(B) || !aligned16(chunk_states)) return SSD_ERR_ALIGN;
+    ssd::launch_chunk_state(dims_of(p), x, B, chunk_meta, dA_cumsum, dt_chunk, chunk_states, stream);
+    return launch_status();
+}
+
+int ssd_state_passing(const ssd_problem *p, const float *chunk_states, const float *dA_cumsum,
+                      const int32_t *chunk_meta, void *state_cache,
+                      const int32_t *state_indices, const uint8_t *has_initial_state,
+                      float *entering_states, void *checkpoints, void *stream)
+{
+    int rc = check_problem(p);
+    if (rc) return rc;
+    if (!chunk_states || !dA_cumsum || !chunk_meta || !state_cache || !state_indices ||
+        !entering_states)
+        return SSD_ERR_NULL;
+    if (!aligned16(chunk_states) || !aligned16(state_cache) || !aligned16(entering_states) ||
+        !aligned16(checkpoints))
+        return SSD_ERR_ALIGN;
+    ssd::launch_state_passing(dims_of(p), chunk_states, dA_cumsum, chunk_meta, state_cache,
+                              state_indices, has_initial_state, entering_states, checkpoints,
+                              stream);
+    return launch_status();
+}
+
+int ssd_bmm_chunk(const ssd_problem *p, const void *B, const void *C,
+                  const int32_t *chunk_meta, float *CB, void *stream)
+{
+    int rc = check_problem(p);
+    if (rc) return rc;
+    if (!B || !C || !chunk_meta || !CB) return SSD_ERR_NULL;
+    if (!aligned16(B) || !aligned16(C) || !aligned16(CB)) return SSD_ERR_ALIGN;
+    ssd::launch_bmm(dims_of(p), B, C, chunk_meta, CB, stream);
+    return launch_status();
+}
+
+int ssd_chunk_scan(const ssd_problem *p, const void *x, const void *C, const float *D,
+                   const int32_t *chunk_meta, const float *dA_cumsum, const float *dt_chunk,
+                   const float *CB, const float *entering_states, void *y, void *stream)
+{
+    int rc = check_problem(p);
+    if (rc) return rc;
+    if (!x || !C || !chunk_meta || !dA_cumsum || !dt_chunk || !CB || !entering_states || !y)
+        return SSD_ERR_NULL;
+    if (!aligned16(x) || !aligned16(C) || !aligned16(CB) || !aligned16(entering_states) ||
+        !aligned16(y))
+        return SSD_ERR_ALIGN;
+    ssd::launch_chunk_scan(dims_of(p), x, C, D, chunk_meta, dA_cumsum, dt_chunk, CB,
+                           entering_states, y, stream);
+    return launch_status();
+}
+
+int ssd_combined_varlen(const ssd_problem *p, const void *x, const void *dt, const float *A,
+                        const void *B, const void *C, const float *D, const int32_t *cu_seqlens,
+                        void *state_cache, const int32_t *state_indices,
+                        const uint8_t *has_initial_state, void *y, void *checkpoints,
+                        void *workspace, size_t workspace_bytes, void *stream)
+{
+    int rc = check_problem(p);
+    if (rc) return rc;
+    if (!x || !dt || !A || !B || !C || !cu_seqlens || !state_cache || !state_indices || !y ||
+        !workspace)
+        return SSD_ERR_NULL;
+    if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(y) ||
+        !aligned16(state_cache) || !aligned16(checkpoints) ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return SSD_ERR_ALIGN;
+    const Workspace w = workspace_layout(p);
+    if (workspace_bytes < w.total) return SSD_ERR_WORKSPACE;
+
+    const ssd::PrefillDims d = dims_of(p);
+    char *base = static_cast<char *>(workspace);
+    int32_t *meta = reinterpret_cast<int32_t *>(base + w.meta);
+    float *cum = reinterpret_cast<float *>(base + w.cum);
+    float *dtc = reinterpret_cast<float *>(base + w.dt);
+    float *cb = reinterpret_cast<float *>(base + w.cb);
+    float *states = reinterpret_cast<float *>(base + w.states);
+
+    ssd::launch_chunk_cumsum(d, dt, A, cu_seqlens, meta, cum, dtc, stream);
+    ssd::launch_bmm(d, B, C, meta, cb, stream);
+    ssd::launch_chunk_state(d, x, B, meta, cum, dtc, states, stream);
+    // entering states overwrite the chunk states in place
+    ssd::launch_state_passing(d, states, cum, meta, state_cache, state_indices, has_initial_state,
+                              states, checkpoints, stream);
+    ssd::launch_chunk_scan(d, x, C, D, meta, cum, dtc, cb, states, y, stream);
+    return launch_status();
+}
+
+int selective_state_update(const ssu_problem *p, void *state_cache, const int32_t *state_indices,
+                           const void *x, const void *dt, const float *A, const void *B,
+                           const void *C, const float *D, void *y, void *intermediate_states,
+                           void *stream)
+{
+    int rc = check_ssu(p);
+    if (rc) return rc;
+    if (!state_cache || !state_indices || !x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL;
+    if (!aligned16(state_cache) || !aligned16(B) || !aligned16(C) ||
+        !aligned16(intermediate_states))
+        return SSD_ERR_ALIGN;
+    ssd::launch_state_update(dims_of(p), state_cache, state_indices, x, dt, A, B, C, D, y,
+                             intermediate_states, stream);
+    return launch_status();
+}
+
+int ssd_state_commit(const ssu_problem *p, void *state_cache, const int32_t *state_indices,
+                     const void *intermediate_states, const int32_t *num_accepted, void *stream)
+{
+    int rc = check_ssu(p);
+    if (rc) return rc;
+    if (!state_cache || !state_indices || !intermediate_states || !num_accepted) return SSD_ERR_NULL;
+    if (!aligned16(state_cache) || !aligned16(intermediate_states)) return SSD_ERR_ALIGN;
+    ssd::launch_state_commit(dims_of(p), state_cache, state_indices, intermediate_states,
+                             num_accepted, stream);
+    return launch_status();
+}
+
+}  // extern "C"

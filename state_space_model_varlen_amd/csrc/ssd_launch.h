@@ -1,0 +1,46 @@
+// Internal launcher interface between the C ABI (ssd_api.cpp) and the kernels.
+// Every launcher only enqueues on the given stream; arguments are validated
+// by the caller.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssd {
+
+struct PrefillDims {
+    int T, S, H, P, N, G, Q;
+    int max_chunks;
+    int num_slots;
+    bool in_bf16;
+    bool state_bf16;
+};
+
+struct DecodeDims {
+    int R, T, H, P, N, G;
+    int num_slots;
+    bool in_bf16;
+    bool state_bf16;
+};
+
+void launch_chunk_cumsum(const PrefillDims &d, const void *dt, const float *A, const int32_t *cu,
+                         int32_t *meta, float *cum, float *dto, void *stream);
+void launch_chunk_state(const PrefillDims &d, const void *x, const void *B, const int32_t *meta,
+                        const float *cum, const float *dtc, float *states, void *stream);
+void launch_state_passing(const PrefillDims &d, const float *states, const float *cum,
+                          const int32_t *meta, void *cache, const int32_t *idx,
+                          const uint8_t *has_init, float *entering, void *ckpt, void *stream);
+void launch_bmm(const PrefillDims &d, const void *B, const void *C, const int32_t *meta, float *CB,
+                void *stream);
+void launch_chunk_scan(const PrefillDims &d, const void *x, const void *C, const float *D,
+                       const int32_t *meta, const float *cum, const float *dtc, const float *CB,
+                       const float *entering, void *y, void *stream);
+size_t chunk_scan_smem_bytes(const PrefillDims &d);
+
+void launch_state_update(const DecodeDims &d, void *cache, const int32_t *idx, const void *x,
+                         const void *dt, const float *A, const void *B, const void *C,
+                         const float *D, void *y, void *inter, void *stream);
+void launch_state_commit(const DecodeDims &d, void *cache, const int32_t *idx, const void *inter,
+                         const int32_t *accepted, void *stream);
+
+}  // namespace ssd

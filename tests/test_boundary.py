@@ -1,0 +1,124 @@
+"""The C-ABI library loads, exports every function include/ssd_mi355x.h declares,
+and rejects bad arguments on the host before anything reaches the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd_mi355x.h")
+
+ssd = pytest.importorskip("state_space_model_varlen_amd")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+def test_header_functions_are_exported():
+    names = declared_functions()
+    assert len(names) >= 13, names
+    lib = ctypes.CDLL(ssd.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in the header but not exported"
+    assert set(names) == set(ssd.EXPORTED)
+
+
+def test_version_and_status_strings():
+    assert ssd.abi_version() == 1
+    for s in range(8):
+        assert ssd.status_string(s)
+    assert ssd.status_string(99) == "unknown status"
+
+
+def P(**kw):
+    base = dict(total_tokens=256, num_seqs=1, nheads=4, headdim=16, d_state=16, ngroups=1,
+                chunk_size=64, num_slots=1, in_dtype=torch.float32, state_dtype=torch.float32)
+    base.update(kw)
+    return ssd.make_problem(**base)
+
+
+def test_sizes():
+    p = P()
+    assert ssd.max_chunks(p) == 256 // 64 + 1
+    assert ssd.chunk_meta_count(p) == 2 + 3 * 5
+    ws = ssd.workspace_bytes(p)
+    # meta, cumsum, dt, CB and chunk states, each rounded up to 256 bytes
+    r = lambda v: (v + 255) // 256 * 256
+    want = r(4 * 17) + 2 * r(4 * 4 * 5 * 64) + r(4 * 5 * 1 * 64 * 64) + r(4 * 5 * 4 * 16 * 16)
+    assert ws == want
+    big = P(total_tokens=4096, nheads=80, headdim=64, d_state=128, chunk_size=256,
+            in_dtype=torch.bfloat16)
+    assert ssd.max_chunks(big) == 17
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nheads=0), 2), (dict(total_tokens=-1), 2), (dict(nheads=6, ngroups=4), 2),
+    (dict(num_slots=0), 2), (dict(headdim=32), 4), (dict(d_state=64), 4),
+    (dict(chunk_size=48), 4), (dict(chunk_size=512), 4),
+])
+def test_invalid_problems_rejected(kw, status):
+    p = P(**kw)
+    assert ssd.workspace_bytes(p) == 0
+    assert ssd.max_chunks(p) == 0
+    lib = ssd._lib
+    fake = ctypes.c_void_p(256)
+    rc = lib.ssd_combined_varlen(ctypes.byref(p), *([fake] * 13), ctypes.c_size_t(1 << 30), None)
+    assert rc == status
+
+
+def test_bad_dtype_code():
+    p = P()
+    p.in_dtype = 7
+    rc = ssd._lib.ssd_chunk_cumsum(ctypes.byref(p), *([ctypes.c_void_p(256)] * 6), None)
+    assert rc == 3
+
+
+def test_null_and_alignment_and_workspace():
+    p = P()
+    lib = ssd._lib
+    ok = ctypes.c_void_p(256)
+    args = [ok] * 13
+    # NULL x
+    a = list(args)
+    a[0] = None
+    assert lib.ssd_combined_varlen(ctypes.byref(p), *a, ctypes.c_size_t(1 << 30), None) == 1
+    # misaligned x
+    a = list(args)
+    a[0] = ctypes.c_void_p(258)
+    assert lib.ssd_combined_varlen(ctypes.byref(p), *a, ctypes.c_size_t(1 << 30), None) == 7
+    # workspace not 256-byte aligned
+    a = list(args)
+    a[12] = ctypes.c_void_p(272)
+    assert lib.ssd_combined_varlen(ctypes.byref(p), *a, ctypes.c_size_t(1 << 30), None) == 7
+    # workspace too small
+    assert lib.ssd_combined_varlen(ctypes.byref(p), *args,
+                                   ctypes.c_size_t(ssd.workspace_bytes(p) - 1), None) == 5
+    # the step entry points check their pointers too
+    assert lib.ssd_chunk_scan(ctypes.byref(p), *([ok] * 6), None, ok, ok, None) == 1
+    assert lib.ssd_state_passing(ctypes.byref(p), ok, ok, ok, None, ok, None, ok, None, None) == 1
+
+
+def test_decode_validation():
+    lib = ssd._lib
+    ok = ctypes.c_void_p(256)
+    up = ssd.make_ssu_problem(2, 3, 8, 64, 128, 2, 4, torch.bfloat16, torch.bfloat16)
+    assert lib.selective_state_update(ctypes.byref(up), ok, ok, ok, ok, ok, ok, None, None, ok,
+                                      None, None) == 1
+    bad = ssd.make_ssu_problem(2, 3, 8, 64, 128, 3, 4, torch.bfloat16, torch.bfloat16)
+    assert lib.selective_state_update(ctypes.byref(bad), *([ok] * 10), None, None) == 2
+    un = ssd.make_ssu_problem(2, 3, 8, 32, 128, 2, 4, torch.bfloat16, torch.bfloat16)
+    assert lib.ssd_state_commit(ctypes.byref(un), ok, ok, ok, ok, None) == 4
+    assert lib.ssd_state_commit(ctypes.byref(up), ok, ok, ctypes.c_void_p(264), ok, None) == 7
+
+
+def test_binding_checks_shapes_before_the_library():
+    p = P()
+    x = torch.empty(10, 4, 16)   # CPU tensor: rejected by the binding
+    with pytest.raises(ValueError):
+        ssd.ssd_chunk_state(p, x, x, x, x, x, x)

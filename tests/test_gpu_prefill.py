@@ -1,0 +1,351 @@
+"""GPU parity of the SSD varlen prefill against the CPU oracle.
+
+Step by step (each of the five steps vs oracle.chunked) and end to end
+(ssd_combined_varlen vs the sequential recurrence with cache semantics), on
+small problems that still span several chunks, 16-row tiles and ragged tails,
+and on the full-size workloads with sampled heads / sequences.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ssd_synth as sy
+from gpu_helpers import (DEV, assert_close, gpu_prefill, looser, prefix_final_states,
+                         select_heads, to64, tol)
+from oracle import chunked
+
+pytestmark = pytest.mark.gpu
+
+F32, BF16 = torch.float32, torch.bfloat16
+
+
+def _ssd():
+    import state_space_model_varlen_amd as ssd
+    return ssd
+
+
+def _cache_with_states(inp, num_slots, dtype, scale=0.05, seed=0, nan_unused=True):
+    """A cache whose used slots of sequences with an initial state hold random
+    states (rounded to the cache dtype) and whose other slots are NaN."""
+    H, P, N = inp.x.shape[1], inp.x.shape[2], inp.B.shape[2]
+    cache = sy.nan_cache(num_slots, H, P, N, dtype) if nan_unused else \
+        torch.zeros(num_slots, H, P, N, dtype=dtype)
+    g = torch.Generator().manual_seed(seed)
+    if inp.has_initial is not None:
+        for s in range(len(inp.state_indices)):
+            if int(inp.has_initial[s]):
+                cache[int(inp.state_indices[s])] = (torch.randn(H, P, N, generator=g) * scale
+                                                    ).to(dtype)
+    return cache
+
+
+# --------------------------------------------------------------------------------------
+# step by step
+
+STEP_CASES = [
+    # seqlens, H, P, N, G, Q, in_dtype, state_dtype
+    ((100, 156), 4, 16, 16, 1, 64, F32, F32),
+    ((1, 17, 0, 255, 64, 31), 4, 16, 16, 2, 32, F32, F32),
+    ((300, 5, 513), 4, 64, 128, 2, 128, BF16, F32),
+    ((256, 1, 700, 16), 4, 64, 128, 1, 256, BF16, BF16),
+    ((129, 64), 2, 16, 128, 1, 64, BF16, F32),
+    ((77, 200), 2, 64, 16, 2, 64, BF16, BF16),
+    ((90, 33), 2, 64, 128, 2, 64, F32, F32),
+]
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: f"L{sum(c[0])}_P{c[2]}N{c[3]}Q{c[5]}_"
+                         f"{str(c[6])[6:]}_{str(c[7])[6:]}")
+def test_steps_match_chunked_oracle(case):
+    lens, H, P, N, G, Q, ti, ts = case
+    S = len(lens)
+    inp = sy.random_problem(STEP_CASES.index(case), lens, H, P, N, G, Q, ti, ts, num_slots=S + 3,
+                            has_initial=[s % 2 == 0 for s in range(S)])
+    cache = _cache_with_states(inp, S + 3, ts)
+    ssd = _ssd()
+    T = sum(lens)
+    p = ssd.make_problem(T, S, H, P, N, G, Q, S + 3, ti, ts)
+    buf = ssd.alloc_step_buffers(p, DEV)
+    mc = ssd.max_chunks(p)
+    x, dt, A, B, C, D = (t.to(DEV) for t in (inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D))
+    cu, idx, hi = inp.cu_seqlens.to(DEV), inp.state_indices.to(DEV), inp.has_initial.to(DEV)
+    g_cache = cache.to(DEV)
+    ckpt = torch.empty(mc, H, P, N, dtype=ts, device=DEV)
+    y = torch.empty(T, H, P, dtype=ti, device=DEV)
+
+    ssd.ssd_chunk_cumsum(p, dt, A, cu, buf["chunk_meta"], buf["dA_cumsum"], buf["dt_chunk"])
+    ssd.ssd_chunk_state(p, x, B, buf["chunk_meta"], buf["dA_cumsum"], buf["dt_chunk"],
+                        buf["chunk_states"])
+    ssd.ssd_bmm_chunk(p, B, C, buf["chunk_meta"], buf["CB"])
+    ssd.ssd_state_passing(p, buf["chunk_states"], buf["dA_cumsum"], buf["chunk_meta"], g_cache,
+                          idx, hi, buf["entering"], ckpt)
+    ssd.ssd_chunk_scan(p, x, C, D, buf["chunk_meta"], buf["dA_cumsum"], buf["dt_chunk"],
+                       buf["CB"], buf["entering"], y)
+    torch.cuda.synchronize()
+
+    # oracle steps on the same (exactly widened) inputs
+    init = oracle.f64(cache[inp.state_indices.long()])
+    hin = inp.has_initial.numpy()
+    init[hin == 0] = 0.0
+    r = chunked.scan(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.cu_seqlens.numpy(), Q,
+                     init=init, has_init=hin)
+    meta = r["meta"]
+    nc = len(meta["seq"])
+
+    # 1. chunk metadata: exact
+    gm = buf["chunk_meta"].cpu().numpy()
+    assert gm[: S + 1].tolist() == meta["chunk_cu"].tolist()
+    trip = gm[S + 1:].reshape(mc, 3)
+    assert trip[:nc, 0].tolist() == meta["seq"].tolist()
+    assert trip[:nc, 1].tolist() == meta["start"].tolist()
+    assert trip[:nc, 2].tolist() == meta["len"].tolist()
+    assert (trip[nc:, 2] == 0).all() and (trip[nc:, 0] == -1).all()
+
+    # 1. cumsum: within summation rounding; dt per chunk position: exact copy
+    gcum = to64(buf["dA_cumsum"][:, :nc])
+    scale = np.abs(r["dA_cumsum"]).max() + 1.0
+    assert np.abs(gcum - r["dA_cumsum"]).max() <= Q * 1.2e-7 * scale
+    assert np.array_equal(to64(buf["dt_chunk"][:, :nc]), r["dt"])
+
+    # 4. bmm: causal part inside each chunk
+    gcb = to64(buf["CB"][:nc])
+    for c in range(nc):
+        ln = int(meta["len"][c])
+        low = np.tril(np.ones((ln, ln), dtype=bool))
+        diff = np.abs(gcb[c][:, :ln, :ln] - r["CB"][c][:, :ln, :ln])[:, low]
+        assert diff.max(initial=0.0) <= 1e-5 * (1 + np.abs(r["CB"][c]).max()), c
+
+    # 2, 3, 5
+    assert_close(buf["chunk_states"][:nc], r["chunk_states"], ti, "chunk_states")
+    assert_close(buf["entering"][:nc], r["entering"], ti, "entering states")
+    assert_close(ckpt[:nc], r["ckpt"], looser(ti, ts), "checkpoints")
+    assert_close(y, r["y"], ti, "y")
+
+
+# --------------------------------------------------------------------------------------
+# end to end vs the sequential recurrence
+
+E2E_CASES = [
+    ((256,), 4, 16, 16, 1, 64, F32, F32, False),
+    ((5, 0, 300, 1, 64, 129), 4, 16, 16, 2, 64, F32, F32, True),
+    ((600, 32, 1, 0, 257), 8, 64, 128, 2, 256, BF16, F32, True),
+    ((33, 32, 31, 200), 8, 64, 128, 8, 128, BF16, BF16, True),
+    ((1000,), 2, 64, 128, 1, 256, BF16, F32, False),
+    ((150, 90), 4, 16, 128, 2, 32, BF16, BF16, True),
+    ((90, 150), 4, 64, 16, 4, 64, F32, BF16, True),
+]
+
+
+def _e2e(case, D=True):
+    lens, H, P, N, G, Q, ti, ts, ck = case
+    S = len(lens)
+    slots = 2 * S + 2
+    inp = sy.random_problem(100 + E2E_CASES.index(case), lens, H, P, N, G, Q, ti, ts, num_slots=slots,
+                            has_initial=[s % 3 != 1 for s in range(S)])
+    cache = _cache_with_states(inp, slots, ts)
+    y, cache_after, ckpt = gpu_prefill(inp, cache, Q, checkpoints=ck, D=D)
+    ref = oracle.prefill(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D if D else None,
+                         inp.cu_seqlens, inp.state_indices, inp.has_initial, cache, Q,
+                         checkpoints=ck)
+    return inp, cache, y, cache_after, ckpt, ref
+
+
+@pytest.mark.parametrize("case", E2E_CASES, ids=lambda c: f"S{len(c[0])}_P{c[2]}N{c[3]}Q{c[5]}_"
+                         f"{str(c[6])[6:]}_{str(c[7])[6:]}")
+def test_combined_matches_recurrence(case):
+    lens, H, P, N, G, Q, ti, ts, ck = case
+    inp, cache, y, cache_after, ckpt, ref = _e2e(case)
+    assert_close(y, ref["y"], ti, "y", normalised=False)
+    used = inp.state_indices.long()
+    assert_close(cache_after[used], ref["final"], looser(ti, ts), "final states")
+    # slots that are not in state_indices keep their exact bits (NaN included)
+    others = [s for s in range(cache.shape[0]) if s not in set(used.tolist())]
+    assert torch.equal(cache_after[others].view(torch.int16 if ts == BF16 else torch.int32),
+                       cache[others].view(torch.int16 if ts == BF16 else torch.int32))
+    if ck:
+        nc = int(oracle.chunk_counts(inp.cu_seqlens.numpy(), Q)[-1])
+        assert_close(ckpt[:nc], ref["ckpt"], looser(ti, ts), "checkpoints")
+
+
+@pytest.mark.parametrize("case", [c for c in E2E_CASES if c[6] == BF16],
+                         ids=lambda c: f"S{len(c[0])}_Q{c[5]}")
+def test_ssm_part_normalised_error(case):
+    """With D = 0, y is the SSM part alone: its normalised error must be small."""
+    inp, cache, y, cache_after, ckpt, ref = _e2e(case, D=False)
+    assert_close(y, ref["y"], case[6], "y (D = 0)")
+
+
+def test_deterministic_and_inputs_untouched():
+    case = E2E_CASES[2]
+    lens, H, P, N, G, Q, ti, ts, ck = case
+    S = len(lens)
+    inp = sy.random_problem(5, lens, H, P, N, G, Q, ti, ts, num_slots=2 * S,
+                            has_initial=[True] * S)
+    cache = _cache_with_states(inp, 2 * S, ts)
+    keep = [t.clone() for t in (inp.x, inp.dt, inp.B, inp.C, inp.A, inp.D)]
+    y1, c1, k1 = gpu_prefill(inp, cache, Q, checkpoints=True)
+    y2, c2, k2 = gpu_prefill(inp, cache, Q, checkpoints=True)
+    bits = lambda t: t.view(torch.int16) if t.dtype == BF16 else t.view(torch.int32)
+    nc = int(oracle.chunk_counts(inp.cu_seqlens.numpy(), Q)[-1])
+    assert torch.equal(bits(y1), bits(y2))
+    assert torch.equal(bits(c1), bits(c2))          # NaN slots compared by their bits
+    assert torch.equal(bits(k1[:nc]), bits(k2[:nc]))
+    for a, b in zip(keep, (inp.x, inp.dt, inp.B, inp.C, inp.A, inp.D)):
+        assert torch.equal(a, b)
+
+
+def test_packing_is_bitwise_invariant():
+    """A packed batch gives the same bits as each sequence run alone: chunks
+    start at every sequence's first token, so the work per sequence is identical."""
+    lens, H, P, N, G, Q = (300, 17, 513, 64), 4, 64, 128, 2, 128
+    S = len(lens)
+    inp = sy.random_problem(9, lens, H, P, N, G, Q, BF16, F32, num_slots=S,
+                            has_initial=[True, False, True, True])
+    cache = _cache_with_states(inp, S, F32)
+    y, c_after, _ = gpu_prefill(inp, cache, Q)
+    cu = inp.cu_seqlens.tolist()
+    for s in range(S):
+        a, b = cu[s], cu[s + 1]
+        one = sy.PrefillInputs(cfg=inp.cfg, x=inp.x[a:b].contiguous(), dt=inp.dt[a:b].contiguous(),
+                               A=inp.A, B=inp.B[a:b].contiguous(), C=inp.C[a:b].contiguous(),
+                               D=inp.D, cu_seqlens=torch.tensor([0, b - a], dtype=torch.int32),
+                               state_indices=inp.state_indices[s:s + 1].clone(),
+                               has_initial=inp.has_initial[s:s + 1].clone())
+        y1, c1, _ = gpu_prefill(one, cache, Q)
+        assert torch.equal(y1, y[a:b]), s
+        slot = int(inp.state_indices[s])
+        assert torch.equal(c1[slot], c_after[slot]), s
+
+
+def test_chunk_size_invariance():
+    """Q = 64, 128, 256 each match the oracle; their results agree with each other."""
+    lens = (700, 130, 1)
+    inp = sy.random_problem(11, lens, 4, 64, 128, 2, 64, BF16, F32, num_slots=3,
+                            has_initial=[True, True, False])
+    cache = _cache_with_states(inp, 3, F32)
+    ref = oracle.prefill(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.cu_seqlens,
+                         inp.state_indices, inp.has_initial, cache, 64)
+    outs = []
+    for Q in (32, 64, 128, 256):
+        y, c, _ = gpu_prefill(inp, cache, Q)
+        assert_close(y, ref["y"], BF16, f"y Q={Q}", normalised=False)
+        assert_close(c[inp.state_indices.long()], ref["final"], BF16, f"final Q={Q}")
+        outs.append(y)
+    for o in outs[1:]:
+        assert_close(o, to64(outs[0]), BF16, "y across chunk sizes", normalised=False)
+
+
+def test_empty_batch_and_zero_length_sequences():
+    ssd = _ssd()
+    # S = 0, T = 0: nothing to do
+    p = ssd.make_problem(0, 0, 4, 16, 16, 1, 64, 1, F32, F32)
+    cache = torch.zeros(1, 4, 16, 16, device=DEV)
+    ssd.ssd_combined_varlen(p, torch.empty(0, 4, 16, device=DEV), torch.empty(0, 4, device=DEV),
+                            torch.ones(4, device=DEV), torch.empty(0, 1, 16, device=DEV),
+                            torch.empty(0, 1, 16, device=DEV), None,
+                            torch.zeros(1, dtype=torch.int32, device=DEV), cache,
+                            torch.empty(0, dtype=torch.int32, device=DEV), None,
+                            torch.empty(0, 4, 16, dtype=F32, device=DEV), None,
+                            ssd.alloc_workspace(p, DEV))
+    torch.cuda.synchronize()
+    assert (cache == 0).all()
+    # only zero-length sequences: each writes its initial state (or zeros) back
+    inp = sy.random_problem(13, (0, 0, 0), 4, 16, 16, 1, 64, F32, F32, num_slots=5,
+                            has_initial=[True, False, True])
+    c = _cache_with_states(inp, 5, F32)
+    y, after, _ = gpu_prefill(inp, c, 64)
+    ref = oracle.prefill(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.cu_seqlens,
+                         inp.state_indices, inp.has_initial, c, 64)
+    assert torch.equal(after.view(torch.int32), ref["cache"].view(torch.int32))
+
+
+def test_bad_device_indices_do_not_fault():
+    """Slot indices outside [0, num_slots) are skipped on the device: the
+    sequence starts from zero and nothing is written."""
+    lens = (40, 70)
+    inp = sy.random_problem(15, lens, 4, 16, 16, 1, 64, F32, F32, num_slots=2,
+                            has_initial=[True, True])
+    cache = _cache_with_states(inp, 2, F32, nan_unused=False)
+    inp.state_indices[:] = torch.tensor([7, -3], dtype=torch.int32)
+    y, after, _ = gpu_prefill(inp, cache, 64)
+    assert torch.equal(after, cache)
+    ref = oracle.prefill(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.cu_seqlens,
+                         torch.tensor([0, 1]), None, cache, 64)
+    assert_close(y, ref["y"], F32, "y from zero")
+
+
+# --------------------------------------------------------------------------------------
+# full-size workloads
+
+def test_c0_tiny_fp32_full():
+    inp = sy.make_prefill(sy.C0)
+    cache = torch.full((1, 4, 16, 16), float("nan"))
+    y, after, _ = gpu_prefill(inp, cache, 64)
+    ref = oracle.prefill(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.cu_seqlens,
+                         inp.state_indices, None, cache, 64)
+    err_y = assert_close(y, ref["y"], F32, "c0 y")
+    err_s = assert_close(after[0], ref["final"][0], F32, "c0 final state")
+    assert err_y <= 1e-4 and err_s <= 1e-4
+
+
+def test_c1_layer_prefill_full():
+    inp = sy.make_prefill(sy.C1)
+    cache = torch.full((1, 80, 64, 128), float("nan"))
+    y, after, _ = gpu_prefill(inp, cache, 256)
+    ref = oracle.prefill(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.cu_seqlens,
+                         inp.state_indices, None, cache, 256)
+    assert_close(y, ref["y"], BF16, "c1 y", normalised=False)
+    assert_close(after[0], ref["final"][0], BF16, "c1 final state")
+    yd, _, _ = gpu_prefill(inp, cache, 256, D=False)
+    assert_close(yd, ref["y"] - to64(inp.D)[None, :, None] * to64(inp.x), BF16, "c1 y (D = 0)")
+
+
+def _sampled_continuation(cfg, seqs, heads, checkpoints):
+    """Full-size prefill whose initial states come from the oracle over each
+    sequence's seeded prefix for the sampled (sequence, head) pairs; the other
+    cached states are random of the same scale. The oracle then checks the
+    sampled pairs."""
+    inp = sy.make_prefill(cfg)
+    H, P, N, G, Q = cfg.nheads, cfg.headdim, cfg.d_state, cfg.ngroups, cfg.chunk_size
+    cache = sy.nan_cache(cfg.num_slots, H, P, N, cfg.state_dtype)
+    g = torch.Generator().manual_seed(17)
+    init_seqs = [s for s in range(cfg.num_seqs) if int(inp.has_initial[s])]
+    for s in init_seqs:
+        cache[int(inp.state_indices[s])] = (torch.randn(H, P, N, generator=g) * 0.03
+                                            ).to(cfg.state_dtype)
+    sampled_init = [s for s in seqs if s in init_seqs]
+    pre = prefix_final_states(inp, sampled_init, heads)
+    for k, s in enumerate(sampled_init):
+        slot = int(inp.state_indices[s])
+        for j, h in enumerate(heads):
+            cache[slot, h] = oracle.round_to(pre[k, j], cfg.state_dtype)
+    y, after, ckpt = gpu_prefill(inp, cache, Q, checkpoints=checkpoints)
+    cu = inp.cu_seqlens.tolist()
+    chunk_cu = oracle.chunk_counts(cu, Q)
+    for s in seqs:
+        a, b = cu[s], cu[s + 1]
+        x, dt, A, B, C, D = select_heads(inp.x[a:b], inp.dt[a:b], inp.A, inp.B[a:b], inp.C[a:b],
+                                         inp.D, heads, G)
+        slot = int(inp.state_indices[s])
+        init = oracle.f64(cache[slot][heads])[None] if s in init_seqs else None
+        ry, rf, rk = oracle.recurrence(x, dt, A, B, C, D, [0, b - a], Q, init=init,
+                                       checkpoints=checkpoints)
+        assert_close(y[a:b][:, heads], ry, cfg.in_dtype, f"{cfg.name} y seq {s}",
+                     normalised=False)
+        assert_close(after[slot][heads], rf[0], cfg.in_dtype, f"{cfg.name} final seq {s}")
+        if checkpoints:
+            assert_close(ckpt[chunk_cu[s]:chunk_cu[s + 1]][:, heads], rk, cfg.in_dtype,
+                         f"{cfg.name} checkpoints seq {s}")
+    # slots no sequence uses are untouched (NaN bits)
+    used = set(inp.state_indices.tolist())
+    others = [k for k in range(cfg.num_slots) if k not in used]
+    assert torch.isnan(after[others].float()).all()
+
+
+def test_c2_cached_short_continuation_full():
+    _sampled_continuation(sy.C2, seqs=[0, 5, 13, 31], heads=[0, 21, 42, 63], checkpoints=False)
+
+
+def test_c3_mixed_varlen_full():
+    _sampled_continuation(sy.C3, seqs=list(range(8)), heads=[0, 9, 36, 63], checkpoints=True)

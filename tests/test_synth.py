@@ -18,7 +18,8 @@ def test_prefill_shapes_and_determinism():
     assert a.has_initial.tolist() == [0, 1, 0, 1, 0, 1, 0, 1]
     assert len(set(a.state_indices.tolist())) == 8
     assert all(0 <= i < 256 for i in a.state_indices.tolist())
-    assert a.prefix[0] is None and a.prefix[1][0].shape == (4224, 64, 64)
+    assert a.prefix_tokens(0) is None and a.prefix_tokens(1)[0].shape == (4224, 64, 64)
+    assert torch.equal(a.prefix_tokens(1)[2], b.prefix_tokens(1)[2])
 
 
 def test_value_ranges():
