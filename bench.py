@@ -50,17 +50,17 @@ def parse():
 # algorithmic bytes per launch of each prefill kernel (what the kernel must move at least)
 
 def prefill_bytes(T, S, H, P, N, G, Q, nc, ex, es, s_init, checkpoints):
-    f = 4
-    st = nc * H * P * N * f                 # chunk states / entering states (fp32)
-    per_chunk = 2 * H * nc * Q * f          # dA_cumsum + dt per chunk position (fp32)
-    cb = nc * G * (Q // 16) * (Q // 16 + 1) // 2 * 256 * f   # causal 16x16 tiles of CB
+    st = nc * H * P * N * 4                 # chunk states (fp32)
+    ent = nc * H * P * N * ex               # entering states (input dtype)
+    per_chunk = 2 * H * nc * Q * 4          # dA_cumsum + dt per chunk position (fp32)
+    cb = nc * G * (Q // 16) * (Q // 16 + 1) // 2 * 256 * ex   # causal 16x16 tiles of CB
     return {
         "chunk_cumsum": T * H * ex + per_chunk,
         "bmm_chunk": 2 * T * G * N * ex + cb,
         "chunk_state": T * H * P * ex + T * G * N * ex + per_chunk + st,
-        "state_passing": 2 * st + (s_init + S) * H * P * N * es
+        "state_passing": st + ent + (s_init + S) * H * P * N * es
                          + (nc * H * P * N * es if checkpoints else 0),
-        "chunk_scan": 2 * T * H * P * ex + T * G * N * ex + per_chunk + cb + st,
+        "chunk_scan": 2 * T * H * P * ex + T * G * N * ex + per_chunk + cb + ent,
     }
 
 
@@ -213,6 +213,19 @@ def main():
                            "traffic": load_traffic("selective_state_update"),
                            "bytes": ssu_bytes}}
 
+    # achievable HBM bandwidth on this machine, for context: a plain 1 GiB device copy
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    ca, cb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ca.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    cb.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * (1 << 30) * 5 / (ca.elapsed_time(cb) * 1e-3) / 1e9
+    del src, dst
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -255,6 +268,7 @@ def main():
                    "ngroups": G, "chunk_size": Q, "inputs": "bf16 x/B/C/dt, fp32 A/D/state",
                    "parallelism": "single GPU"},
         "roofline": roofline,
+        "hbm_copy_GBps": round(copy_gbps, 1),
         "kernels": kernels,
         "decode": decode,
         "cpu_baseline": cpu,

@@ -165,24 +165,25 @@ int ssd_chunk_state(const ssd_problem *p, const void *x, const void *B,
  *                     state_indices are not touched
  *   state_indices     [S] int32
  *   has_initial_state [S] uint8, or NULL: no sequence reads its slot
- *   entering_states   out float32 [max_chunks,H,P,N]; may be the same buffer as
- *                     chunk_states (each element is read before it is overwritten)
+ *   entering_states   out [max_chunks,H,P,N] in in_dtype (the precision chunk scan
+ *                     multiplies it in); must not overlap chunk_states
  *   checkpoints       out [max_chunks,H,P,N] state_dtype, or NULL to skip
  * A zero-length sequence writes its initial state (or zeros) back to its slot.
  */
 int ssd_state_passing(const ssd_problem *p, const float *chunk_states, const float *dA_cumsum,
                       const int32_t *chunk_meta, void *state_cache,
                       const int32_t *state_indices, const uint8_t *has_initial_state,
-                      float *entering_states, void *checkpoints, void *stream);
+                      void *entering_states, void *checkpoints, void *stream);
 
 /*
  * Step 4 - bmm (vLLM PR #61501, section "Details"): CB[c,g,i,j] = C_i . B_j
- * inside each chunk. B, C [T,G,N] in_dtype; CB out float32
- * [max_chunks,G,Q,Q]. Defined for j <= i < chunk length (the causal part chunk
- * scan reads); other entries are unspecified.
+ * inside each chunk, float32 accumulation. B, C [T,G,N] in_dtype; CB out
+ * [max_chunks,G,Q,Q] in in_dtype (chunk scan multiplies in that precision).
+ * Defined for j <= i < chunk length (the causal part chunk scan reads); other
+ * entries are unspecified.
  */
 int ssd_bmm_chunk(const ssd_problem *p, const void *B, const void *C,
-                  const int32_t *chunk_meta, float *CB, void *stream);
+                  const int32_t *chunk_meta, void *CB, void *stream);
 
 /*
  * Step 5 - chunk scan (vLLM PR #61501, section "Details"; entering states from
@@ -190,11 +191,11 @@ int ssd_bmm_chunk(const ssd_problem *p, const void *B, const void *C,
  *   y_i = sum_{j<=i} CB[i,j] * exp(cum_i - cum_j) * dt_j * x_j
  *         + exp(cum_i) * (H_in . C_i) + D_h * x_i
  *   x [T,H,P], C [T,G,N] in_dtype; D [H] float32 or NULL (= 0); CB from step 4;
- *   entering_states from step 3; y out [T,H,P] in_dtype.
+ *   entering_states from step 3 (in_dtype); y out [T,H,P] in_dtype.
  */
 int ssd_chunk_scan(const ssd_problem *p, const void *x, const void *C, const float *D,
                    const int32_t *chunk_meta, const float *dA_cumsum, const float *dt_chunk,
-                   const float *CB, const float *entering_states, void *y, void *stream);
+                   const void *CB, const void *entering_states, void *y, void *stream);
 
 /*
  * The whole prefill: steps 1-5 enqueued on one stream with no host

@@ -201,7 +201,7 @@ def ssd_state_passing(p: ssd_problem, chunk_states, dA_cumsum, chunk_meta, state
         _ptr(state_cache, "state_cache", ts, (p.num_slots, H, P, N)),
         _ptr(state_indices, "state_indices", torch.int32, (S,)),
         _ptr(has_initial_state, "has_initial_state", torch.uint8, (S,), optional=True),
-        _ptr(entering_states, "entering_states", torch.float32, (mc, H, P, N)),
+        _ptr(entering_states, "entering_states", _TORCH[p.in_dtype], (mc, H, P, N)),
         _ptr(checkpoints, "checkpoints", ts, (mc, H, P, N), optional=True), _stream(stream))
     _check("ssd_state_passing", rc)
 
@@ -212,7 +212,7 @@ def ssd_bmm_chunk(p: ssd_problem, B, C, chunk_meta, CB, stream=None):
     rc = _lib.ssd_bmm_chunk(
         ctypes.byref(p), _ptr(B, "B", ti, (T, G, N)), _ptr(C, "C", ti, (T, G, N)),
         _ptr(chunk_meta, "chunk_meta", torch.int32, (chunk_meta_count(p),)),
-        _ptr(CB, "CB", torch.float32, (mc, G, Q, Q)), _stream(stream))
+        _ptr(CB, "CB", ti, (mc, G, Q, Q)), _stream(stream))
     _check("ssd_bmm_chunk", rc)
 
 
@@ -226,8 +226,8 @@ def ssd_chunk_scan(p: ssd_problem, x, C, D, chunk_meta, dA_cumsum, dt_chunk, CB,
         _ptr(chunk_meta, "chunk_meta", torch.int32, (chunk_meta_count(p),)),
         _ptr(dA_cumsum, "dA_cumsum", torch.float32, (H, mc, Q)),
         _ptr(dt_chunk, "dt_chunk", torch.float32, (H, mc, Q)),
-        _ptr(CB, "CB", torch.float32, (mc, G, Q, Q)),
-        _ptr(entering_states, "entering_states", torch.float32, (mc, H, P, N)),
+        _ptr(CB, "CB", ti, (mc, G, Q, Q)),
+        _ptr(entering_states, "entering_states", ti, (mc, H, P, N)),
         _ptr(y, "y", ti, (T, H, P)), _stream(stream))
     _check("ssd_chunk_scan", rc)
 
@@ -299,5 +299,6 @@ def alloc_step_buffers(p: ssd_problem, device="cuda") -> dict:
     return dict(
         chunk_meta=torch.empty(chunk_meta_count(p), dtype=torch.int32, device=device),
         dA_cumsum=torch.empty((H, mc, Q), **f), dt_chunk=torch.empty((H, mc, Q), **f),
-        chunk_states=torch.empty((mc, H, P, N), **f), entering=torch.empty((mc, H, P, N), **f),
-        CB=torch.empty((mc, G, Q, Q), **f))
+        chunk_states=torch.empty((mc, H, P, N), **f),
+        entering=torch.empty((mc, H, P, N), dtype=_TORCH[p.in_dtype], device=device),
+        CB=torch.empty((mc, G, Q, Q), dtype=_TORCH[p.in_dtype], device=device))

@@ -31,7 +31,8 @@ int check_problem(const ssd_problem *p)
     if (!gpu_shape_ok(p->headdim, p->d_state) || !chunk_ok(p->chunk_size)) return SSD_ERR_UNSUPPORTED;
     // grid limits: chunks and heads index grid dimensions
     const int64_t mc = (int64_t)p->total_tokens / p->chunk_size + p->num_seqs;
-    if (mc > 0x7fffffff || p->nheads > 65535) return SSD_ERR_UNSUPPORTED;
+    if (mc > 65535 || p->nheads > 65535) return SSD_ERR_UNSUPPORTED;
+    if (mc * p->nheads * 2 > 0x7fffffffLL) return SSD_ERR_UNSUPPORTED;
     if ((int64_t)p->num_seqs * p->nheads * ((p->headdim * p->d_state + 1023) / 1024) > 0x7fffffffLL)
         return SSD_ERR_UNSUPPORTED;
     return SSD_OK;
@@ -93,7 +94,7 @@ size_t round_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // Workspace of ssd_combined_varlen, 256-byte aligned pieces in this order.
 struct Workspace {
-    size_t meta, cum, dt, cb, states, total;
+    size_t meta, cum, dt, cb, states, entering, total;
 };
 
 Workspace workspace_layout(const ssd_problem *p)
@@ -105,8 +106,10 @@ Workspace workspace_layout(const ssd_problem *p)
     w.cum = w.meta + round_up(sizeof(int32_t) * ((size_t)p->num_seqs + 1 + 3 * mc));
     w.dt = w.cum + round_up(sizeof(float) * H * mc * Q);
     w.cb = w.dt + round_up(sizeof(float) * H * mc * Q);
-    w.states = w.cb + round_up(sizeof(float) * mc * G * Q * Q);
-    w.total = w.states + round_up(sizeof(float) * mc * H * P * N);
+    const size_t ein = p->in_dtype == SSD_BF16 ? 2 : 4;
+    w.states = w.cb + round_up(ein * mc * G * Q * Q);
+    w.entering = w.states + round_up(sizeof(float) * mc * H * P * N);
+    w.total = w.entering + round_up(ein * mc * H * P * N);
     return w;
 }
 
@@ -176,7 +179,7 @@ int ssd_chunk_state(const ssd_problem *p, const void *x, const void *B,
 int ssd_state_passing(const ssd_problem *p, const float *chunk_states, const float *dA_cumsum,
                       const int32_t *chunk_meta, void *state_cache,
                       const int32_t *state_indices, const uint8_t *has_initial_state,
-                      float *entering_states, void *checkpoints, void *stream)
+                      void *entering_states, void *checkpoints, void *stream)
 {
     int rc = check_problem(p);
     if (rc) return rc;
@@ -193,7 +196,7 @@ int ssd_state_passing(const ssd_problem *p, const float *chunk_states, const flo
 }
 
 int ssd_bmm_chunk(const ssd_problem *p, const void *B, const void *C,
-                  const int32_t *chunk_meta, float *CB, void *stream)
+                  const int32_t *chunk_meta, void *CB, void *stream)
 {
     int rc = check_problem(p);
     if (rc) return rc;
@@ -205,7 +208,7 @@ int ssd_bmm_chunk(const ssd_problem *p, const void *B, const void *C,
 
 int ssd_chunk_scan(const ssd_problem *p, const void *x, const void *C, const float *D,
                    const int32_t *chunk_meta, const float *dA_cumsum, const float *dt_chunk,
-                   const float *CB, const float *entering_states, void *y, void *stream)
+                   const void *CB, const void *entering_states, void *y, void *stream)
 {
     int rc = check_problem(p);
     if (rc) return rc;
@@ -242,16 +245,16 @@ int ssd_combined_varlen(const ssd_problem *p, const void *x, const void *dt, con
     int32_t *meta = reinterpret_cast<int32_t *>(base + w.meta);
     float *cum = reinterpret_cast<float *>(base + w.cum);
     float *dtc = reinterpret_cast<float *>(base + w.dt);
-    float *cb = reinterpret_cast<float *>(base + w.cb);
+    void *cb = base + w.cb;
     float *states = reinterpret_cast<float *>(base + w.states);
+    void *entering = base + w.entering;
 
     ssd::launch_chunk_cumsum(d, dt, A, cu_seqlens, meta, cum, dtc, stream);
     ssd::launch_bmm(d, B, C, meta, cb, stream);
     ssd::launch_chunk_state(d, x, B, meta, cum, dtc, states, stream);
-    // entering states overwrite the chunk states in place
     ssd::launch_state_passing(d, states, cum, meta, state_cache, state_indices, has_initial_state,
-                              states, checkpoints, stream);
-    ssd::launch_chunk_scan(d, x, C, D, meta, cum, dtc, cb, states, y, stream);
+                              entering, checkpoints, stream);
+    ssd::launch_chunk_scan(d, x, C, D, meta, cum, dtc, cb, entering, y, stream);
     return launch_status();
 }
 

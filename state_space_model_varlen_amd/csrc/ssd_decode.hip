@@ -11,6 +11,20 @@
 
 namespace ssd {
 
+// Non-temporal store of 8 state values (16 bytes of bf16, 32 bytes of float).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store8_nt(bf16 *p, const float *v) {
+    bf16x8 q;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = static_cast<bf16>(v[i]);
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, q), reinterpret_cast<u32x4 *>(p));
+}
+__device__ __forceinline__ void store8_nt(float *p, const float *v) {
+    const f32x4 lo = {v[0], v[1], v[2], v[3]}, hi = {v[4], v[5], v[6], v[7]};
+    __builtin_nontemporal_store(lo, reinterpret_cast<f32x4 *>(p));
+    __builtin_nontemporal_store(hi, reinterpret_cast<f32x4 *>(p) + 1);
+}
+
 // Block (h, r), 256 threads. The state is cut into 16-byte chunks of 8
 // elements; chunk q = tid + 256 k covers row p = q / (N / 8), columns
 // 8 (q % (N / 8)) .. +7, so every vector access of the block is contiguous and
@@ -90,13 +104,9 @@ __global__ __launch_bounds__(256) void state_update_kernel(
                 part = group_sum(part, CPR);
                 if ((tid % CPR) == 0) yr[p] = from_f32<TIn>(part + Dh * xv);
                 if (inter) {
+                    // written once and read only by a later rollback: stream past the caches
                     TS *ip = inter + (rt * H + h) * PN + (int64_t)p * N + n0;
-                    if constexpr (sizeof(TS) == 2) {
-                        Vec16<TS>::store(ip, st[k]);
-                    } else {
-                        Vec16<TS>::store(ip, st[k]);
-                        Vec16<TS>::store(ip + 4, st[k] + 4);
-                    }
+                    store8_nt(ip, st[k]);
                 }
             }
         }

@@ -120,6 +120,73 @@ __device__ __forceinline__ float group_sum(float v, int width) {
 }
 
 // ---------------------------------------------------------------------------
+// 4-element loads / stores (16 bytes of float, 8 bytes of bf16) widened to float.
+template <typename T> __device__ __forceinline__ void load4(const T *p, float *v);
+template <> __device__ __forceinline__ void load4<float>(const float *p, float *v) {
+    const float4 q = *reinterpret_cast<const float4 *>(p);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+}
+template <> __device__ __forceinline__ void load4<bf16>(const bf16 *p, float *v) {
+    const uint2 q = *reinterpret_cast<const uint2 *>(p);
+    v[0] = __uint_as_float(q.x << 16);
+    v[1] = __uint_as_float(q.x & 0xffff0000u);
+    v[2] = __uint_as_float(q.y << 16);
+    v[3] = __uint_as_float(q.y & 0xffff0000u);
+}
+template <typename T> __device__ __forceinline__ void store4(T *p, const float *v);
+template <> __device__ __forceinline__ void store4<float>(float *p, const float *v) {
+    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+template <> __device__ __forceinline__ void store4<bf16>(bf16 *p, const float *v) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 q;
+    q[0] = static_cast<bf16>(v[0]);
+    q[1] = static_cast<bf16>(v[1]);
+    q[2] = static_cast<bf16>(v[2]);
+    q[3] = static_cast<bf16>(v[3]);
+    *reinterpret_cast<bf16x4 *>(p) = q;
+}
+
+// ---------------------------------------------------------------------------
+// LDS transpose read (gfx950 ds_read_b64_tr_b16). Each lane names an 8-byte
+// word (4 bf16); inside every group of 16 lanes, lane i receives element
+// (i % 4) of the words named by lanes 4 v + i / 4, v = 0 .. 3.
+//
+// mfma_frag_tr() builds the 16x16x32 operand fragment (8 K-values for one
+// M/N index per lane, K = 8 (lane / 16) + v) from a row-major LDS tile whose
+// rows are the K index and whose 16 columns starting at `col0` are the M/N
+// index: lane j of a group names row k0 + 8 kg + j / 4, columns col0 + 4 (j % 4),
+// so lane i gets rows k0 + 8 kg + v of column col0 + i. Two reads give v = 0..7.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4i16 lds_read_tr16(const bf16 *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16 *)(p));
+}
+__device__ __forceinline__ bf16x8 mfma_frag_tr(const bf16 *tile, int ld, int k0, int col0,
+                                               int lane) {
+    const int kg = lane >> 4, j = lane & 15;
+    const bf16 *p = tile + (k0 + 8 * kg + (j >> 2)) * ld + col0 + 4 * (j & 3);
+    const v4i16 lo = lds_read_tr16(p);
+    const v4i16 hi = lds_read_tr16(p + 4 * ld);
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, both);
+}
+
+// ---------------------------------------------------------------------------
+// XCD-aware block order. Workgroups are dispatched round-robin over the 8 XCDs
+// (each with its own L2); this maps the hardware block id to a logical id so
+// that each XCD works on one contiguous range of logical ids, which keeps
+// blocks that share data (the same chunk's B, C and CB) on one L2.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_logical_block(int pid, int nblocks) {
+    const int q = nblocks / kXcds, r = nblocks % kXcds;
+    const int xcd = pid % kXcds, slot = pid / kXcds;
+    const int base = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
+    return base + slot;
+}
+
+// ---------------------------------------------------------------------------
 // Chunk metadata as written by the cumsum kernel (int32):
 //   meta[0 .. S]               chunk_cu
 //   meta[S + 1 + 3c + {0,1,2}] sequence, first token, token count of chunk c

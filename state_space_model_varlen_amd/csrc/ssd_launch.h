@@ -29,13 +29,12 @@ void launch_chunk_state(const PrefillDims &d, const void *x, const void *B, cons
                         const float *cum, const float *dtc, float *states, void *stream);
 void launch_state_passing(const PrefillDims &d, const float *states, const float *cum,
                           const int32_t *meta, void *cache, const int32_t *idx,
-                          const uint8_t *has_init, float *entering, void *ckpt, void *stream);
-void launch_bmm(const PrefillDims &d, const void *B, const void *C, const int32_t *meta, float *CB,
+                          const uint8_t *has_init, void *entering, void *ckpt, void *stream);
+void launch_bmm(const PrefillDims &d, const void *B, const void *C, const int32_t *meta, void *CB,
                 void *stream);
 void launch_chunk_scan(const PrefillDims &d, const void *x, const void *C, const float *D,
-                       const int32_t *meta, const float *cum, const float *dtc, const float *CB,
-                       const float *entering, void *y, void *stream);
-size_t chunk_scan_smem_bytes(const PrefillDims &d);
+                       const int32_t *meta, const float *cum, const float *dtc, const void *CB,
+                       const void *entering, void *y, void *stream);
 
 void launch_state_update(const DecodeDims &d, void *cache, const int32_t *idx, const void *x,
                          const void *dt, const float *A, const void *B, const void *C,

@@ -14,12 +14,12 @@ namespace ssd {
 
 // ===========================================================================
 // Step 1: chunk metadata + chunk cumsum.
-// Grid (max_chunks, ceil(H / kCumsumHeads)), 256 threads. Every block finds
-// its own chunk from cu_seqlens with a block-wide scan of per-sequence chunk
-// counts (no host sync, no extra launch); blocks with blockIdx.y == 0 publish
-// the metadata. Each wave then runs a wavefront prefix sum of dt * A over the
-// chunk for its heads.
-constexpr int kCumsumHeads = 16;
+// Grid (max_chunks, ceil(H / 4)), 256 threads: one wave per head. Every block
+// finds its own chunk from cu_seqlens with a block-wide scan of per-sequence
+// chunk counts (no host sync, no extra launch); blocks with blockIdx.y == 0
+// publish the metadata. Each wave then runs a wavefront prefix sum of dt * A
+// over the chunk (Q / 64 consecutive positions per lane).
+constexpr int kCumsumHeadsPerBlock = 4;
 
 __device__ __forceinline__ int wave_inclusive_sum_int(int v, int lane) {
 #pragma unroll
@@ -32,22 +32,14 @@ __device__ __forceinline__ int wave_inclusive_sum_int(int v, int lane) {
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
-template <typename TIn>
-__global__ __launch_bounds__(256) void chunk_cumsum_kernel(
-    int T, int S, int H, int Q, int max_chunks, const TIn *__restrict__ dt,
-    const float *__restrict__ A, const int32_t *__restrict__ cu, int32_t *__restrict__ meta,
-    float *__restrict__ cum_out, float *__restrict__ dt_out)
+// Block-wide: locate chunk c among the sequences of cu_seqlens. Writes
+// chunk_cu to meta[0..S] when `publish_cu`. Returns (seq, k) through shared
+// memory: chunk c is chunk k of sequence seq, seq = -1 when c >= nc.
+__device__ void find_chunk(int T, int S, int Q, int max_chunks, const int32_t *__restrict__ cu,
+                           int c, bool publish_cu, int32_t *__restrict__ meta, int *s_found,
+                           int *s_wave_tot)
 {
-    __shared__ int s_wave_tot[4];
-    __shared__ int s_found[2];
-    __shared__ float s_dt[256][kCumsumHeads + 1];
-
-    const int c = blockIdx.x;
-    const int hb = blockIdx.y * kCumsumHeads;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const bool publish = blockIdx.y == 0;
-    const bool publish_cu = publish && blockIdx.x == 0;
-
     if (tid == 0) {
         s_found[0] = -1;
         s_found[1] = 0;
@@ -62,7 +54,7 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(
             const int L = b > a ? b - a : 0;
             cnt = (L + Q - 1) / Q;
         }
-        int incl = wave_inclusive_sum_int(cnt, lane);
+        const int incl = wave_inclusive_sum_int(cnt, lane);
         if (lane == 63) s_wave_tot[wave] = incl;
         __syncthreads();
         int wave_off = 0, tile_tot = 0;
@@ -83,6 +75,20 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(
     }
     if (publish_cu && tid == 0) meta[S] = running < max_chunks ? running : max_chunks;
     __syncthreads();
+}
+
+template <typename TIn>
+__global__ __launch_bounds__(256) void chunk_cumsum_kernel(
+    int T, int S, int H, int Q, int max_chunks, const TIn *__restrict__ dt,
+    const float *__restrict__ A, const int32_t *__restrict__ cu, int32_t *__restrict__ meta,
+    float *__restrict__ cum_out, float *__restrict__ dt_out)
+{
+    __shared__ int s_wave_tot[4];
+    __shared__ int s_found[2];
+    const int c = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const bool publish = blockIdx.y == 0;
+    find_chunk(T, S, Q, max_chunks, cu, c, publish && blockIdx.x == 0, meta, s_found, s_wave_tot);
 
     const int seq = s_found[0];
     int start = 0, len = 0;
@@ -91,46 +97,37 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(
         start = a + s_found[1] * Q;
         len = b - start < Q ? b - start : Q;
     }
-    if (publish && tid == 0) {
+    if (publish && threadIdx.x == 0) {
         int32_t *m = meta + (S + 1) + 3 * c;
         m[0] = seq;
         m[1] = start;
         m[2] = len;
     }
-    if (len <= 0) return;
-
-    const int nh = H - hb < kCumsumHeads ? H - hb : kCumsumHeads;
-    for (int idx = tid; idx < Q * kCumsumHeads; idx += 256) {
-        const int i = idx / kCumsumHeads, hh = idx % kCumsumHeads;
-        float v = 0.0f;
-        if (i < len && hh < nh) v = to_f32(dt[(int64_t)(start + i) * H + hb + hh]);
-        s_dt[i][hh] = v;
-    }
-    __syncthreads();
+    const int h = blockIdx.y * kCumsumHeadsPerBlock + wave;
+    if (len <= 0 || h >= H) return;
 
     const int E = (Q + kWave - 1) / kWave;  // positions per lane (<= 4)
-    for (int hh = wave; hh < nh; hh += 4) {
-        const int h = hb + hh;
-        const float Ah = A[h];
-        float vals[4], loc[4], run = 0.0f;
+    const float Ah = A[h];
+    float vals[4], loc[4], run = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = lane * E + e;
-            const float d = (e < E && i < Q) ? s_dt[i][hh] : 0.0f;
-            vals[e] = d;
-            run += d * Ah;
-            loc[e] = run;
-        }
-        const float incl = wave_inclusive_sum(run, lane);
-        const float off = incl - run;
-        const int64_t row = ((int64_t)h * max_chunks + c) * Q;
+    for (int e = 0; e < 4; ++e) {
+        const int i = lane * E + e;
+        vals[e] = (e < E && i < len) ? to_f32(dt[(int64_t)(start + i) * H + h]) : 0.0f;
+    }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = lane * E + e;
-            if (e < E && i < Q) {
-                cum_out[row + i] = off + loc[e];
-                dt_out[row + i] = vals[e];
-            }
+    for (int e = 0; e < 4; ++e) {
+        run += vals[e] * Ah;
+        loc[e] = run;
+    }
+    const float incl = wave_inclusive_sum(run, lane);
+    const float off = incl - run;
+    const int64_t row = ((int64_t)h * max_chunks + c) * Q;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int i = lane * E + e;
+        if (e < E && i < Q) {
+            cum_out[row + i] = off + loc[e];
+            dt_out[row + i] = vals[e];
         }
     }
 }
@@ -187,7 +184,7 @@ template <typename TIn> __host__ __device__ constexpr int padded(int len) {
 }
 
 // ===========================================================================
-// Step 2: chunk state. Grid (H, max_chunks), 256 threads (4 waves).
+// Step 2: chunk state (generic path). Grid (H, max_chunks), 256 threads (4 waves).
 // S_c = (w * x)^T [P x len] . B [len x N] on MFMA, w_t = exp(cum_last - cum_t) dt_t,
 // with x and B staged transposed through LDS in slabs of 64 tokens.
 constexpr int kStateSlab = 64;
@@ -271,40 +268,14 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(
 // ===========================================================================
 // Step 3: state passing. Grid (S * H * EB), 256 threads, 4 consecutive state
 // elements per thread (EB = ceil(P*N / 1024) blocks per (sequence, head)).
-// Sequential over the sequence's chunks; bandwidth-bound.
-template <typename TS>
-__device__ __forceinline__ void load4(const TS *p, float *v);
-template <> __device__ __forceinline__ void load4<float>(const float *p, float *v) {
-    const float4 q = *reinterpret_cast<const float4 *>(p);
-    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-}
-template <> __device__ __forceinline__ void load4<bf16>(const bf16 *p, float *v) {
-    const uint2 q = *reinterpret_cast<const uint2 *>(p);
-    v[0] = __uint_as_float(q.x << 16);
-    v[1] = __uint_as_float(q.x & 0xffff0000u);
-    v[2] = __uint_as_float(q.y << 16);
-    v[3] = __uint_as_float(q.y & 0xffff0000u);
-}
-template <typename TS>
-__device__ __forceinline__ void store4(TS *p, const float *v);
-template <> __device__ __forceinline__ void store4<float>(float *p, const float *v) {
-    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
-}
-template <> __device__ __forceinline__ void store4<bf16>(bf16 *p, const float *v) {
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    bf16x4 q;
-    q[0] = static_cast<bf16>(v[0]);
-    q[1] = static_cast<bf16>(v[1]);
-    q[2] = static_cast<bf16>(v[2]);
-    q[3] = static_cast<bf16>(v[3]);
-    *reinterpret_cast<bf16x4 *>(p) = q;
-}
-
-template <typename TS>
+// Sequential over the sequence's chunks in float32 registers; bandwidth-bound.
+// The entering states are stored in the dtype chunk scan feeds its MFMA
+// (TE = input dtype), the checkpoints and the final state in the cache dtype.
+template <typename TS, typename TE>
 __global__ __launch_bounds__(256) void state_passing_kernel(
     int S, int H, int PN, int Q, int max_chunks, int num_slots, const float *states,
     const float *__restrict__ cum, const int32_t *__restrict__ meta, TS *cache,
-    const int32_t *__restrict__ idx, const uint8_t *__restrict__ has_init, float *entering,
+    const int32_t *__restrict__ idx, const uint8_t *__restrict__ has_init, TE *entering,
     TS *__restrict__ ckpt)
 {
     const int EB = (PN + 1023) / 1024;
@@ -326,75 +297,93 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
     int c0 = meta[s], c1 = meta[s + 1];
     c0 = c0 < max_chunks ? c0 : max_chunks;
     c1 = c1 < max_chunks ? c1 : max_chunks;
-    for (int c = c0; c < c1; ++c) {
-        const int len = meta[(S + 1) + 3 * c + 2];
-        const float decay = len > 0 ? __expf(cum[((int64_t)h * max_chunks + c) * Q + len - 1]) : 1.0f;
-        const int64_t off = ((int64_t)c * H + h) * PN + e;
-        float sc[4];
-        load4<float>(states + off, sc);
-        float nh[4];
+    // chunks in batches of 8: every chunk state of a batch is loaded before the
+    // sequential recurrence over the batch runs (8 loads in flight per thread)
+    for (int cb = c0; cb < c1; cb += 8) {
+        const int nb = c1 - cb < 8 ? c1 - cb : 8;
+        float sc[8][4], dec[8];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) nh[k] = decay * hs[k] + sc[k];
-        // the chunk state at `off` is consumed above before the entering state
-        // (possibly the same buffer) overwrites it
-        store4<float>(entering + off, hs);
-        if (ckpt) store4<TS>(ckpt + off, nh);
+        for (int k = 0; k < 8; ++k) {
+            if (k < nb) {
+                const int c = cb + k;
+                load4<float>(states + ((int64_t)c * H + h) * PN + e, sc[k]);
+                const int len = meta[(S + 1) + 3 * c + 2];
+                dec[k] = len > 0 ? __expf(cum[((int64_t)h * max_chunks + c) * Q + len - 1]) : 1.0f;
+            }
+        }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) hs[k] = nh[k];
+        for (int k = 0; k < 8; ++k) {
+            if (k < nb) {
+                const int64_t off = ((int64_t)(cb + k) * H + h) * PN + e;
+                // the chunk state at `off` was loaded above, before the entering
+                // state (which may share its memory) is stored
+                store4<TE>(entering + off, hs);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) hs[q] = dec[k] * hs[q] + sc[k][q];
+                if (ckpt) store4<TS>(ckpt + off, hs);
+            }
+        }
     }
     if (slot_ok) store4<TS>(cslot, hs);
 }
 
 // ===========================================================================
-// Step 4: bmm. Grid (max_chunks, G, ceil(Q / 64)), 256 threads. Wave w computes
-// CB rows [64 z + 16 w, +16) against every 16-column tile at or left of the
-// diagonal: C rows (A operand) and B rows (B operand) load straight from HBM
-// because d_state is the contiguous index of both.
+// Step 4: bmm. Grid (max_chunks, G, Q / 16), 256 threads. Block z owns CB rows
+// [16 z, 16 z + 16); its 4 waves share the 16-column tiles at or left of the
+// diagonal (wave w: tiles w, w + 4, ...). Each tile is computed transposed,
+// CB^T = B . C^T (A operand: B rows, B operand: C rows - both load straight
+// from HBM because d_state is their contiguous index), so that each lane ends
+// up holding 4 consecutive columns of one CB row and stores them at once.
+// CB is stored in the input dtype: chunk scan rounds its masked product to
+// that dtype for the MFMA in any case.
 template <typename TIn, int N>
 __global__ __launch_bounds__(256) void bmm_kernel(int S, int G, int Q, int max_chunks,
                                                   const TIn *__restrict__ B,
                                                   const TIn *__restrict__ C,
                                                   const int32_t *__restrict__ meta,
-                                                  float *__restrict__ CB)
+                                                  TIn *__restrict__ CB)
 {
     typedef Mma<TIn> M;
     constexpr int NK = (N + M::K - 1) / M::K;
     const int c = blockIdx.x, g = blockIdx.y;
     const ChunkInfo ci = chunk_info(meta, S, c);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, kg = lane >> 4;
-    const int i0 = blockIdx.z * 64 + wave * 16;
+    const int i0 = blockIdx.z * 16;
     if (ci.len <= 0 || i0 >= ci.len) return;
 
-    typename M::frag af[NK];
+    typename M::frag cf[NK];       // C rows i0 .. i0 + 15 (B operand)
     const int i = i0 + r16;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
         const int n = kk * M::K + kg * M::KPL;
-        af[kk] = (i < ci.len && n < N) ? M::load(C + ((int64_t)(ci.start + i) * G + g) * N + n)
+        cf[kk] = (i < ci.len && n < N) ? M::load(C + ((int64_t)(ci.start + i) * G + g) * N + n)
                                        : M::zero();
     }
-    float *out = CB + ((int64_t)c * G + g) * Q * Q;
-    for (int jt = 0; jt <= i0 / 16; ++jt) {
+    TIn *row = CB + ((int64_t)c * G + g) * Q * Q + (int64_t)i * Q;
+    for (int jt = wave; jt <= i0 / 16; jt += 4) {
         const int j = jt * 16 + r16;
-        f32x4 acc = zero4();
+        typename M::frag bfr[NK];  // B rows j (A operand)
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
             const int n = kk * M::K + kg * M::KPL;
-            const typename M::frag bf = (j < ci.len && n < N)
+            bfr[kk] = (j < ci.len && n < N)
                 ? M::load(B + ((int64_t)(ci.start + j) * G + g) * N + n) : M::zero();
-            acc = M::run(af[kk], bf, acc);
         }
+        f32x4 acc = zero4();
 #pragma unroll
-        for (int v = 0; v < 4; ++v) out[(int64_t)(i0 + kg * 4 + v) * Q + jt * 16 + r16] = acc[v];
+        for (int kk = 0; kk < NK; ++kk) acc = M::run(bfr[kk], cf[kk], acc);
+        // lane holds CB^T[16 jt + 4 kg + v][i] = CB[i][16 jt + 4 kg + v], v = 0..3
+        float v4[4] = {acc[0], acc[1], acc[2], acc[3]};
+        store4<TIn>(row + jt * 16 + 4 * kg, v4);
     }
 }
 
 // ===========================================================================
-// Step 5: chunk scan. Grid (H, max_chunks), 256 threads (4 waves). x of the
-// whole chunk is staged transposed in LDS (MFMA B operand for the intra-chunk
-// product), the entering state as bf16/f32 [P][N] in LDS (B operand of the
-// state term). Wave w handles the 16-row tiles r with r mod 8 in {w, 7 - w}
+// Step 5: chunk scan (generic path: float32, and the bf16 shapes without a
+// fast kernel). Grid (H, max_chunks), 256 threads (4 waves). x of the whole
+// chunk is staged transposed in LDS (MFMA B operand for the intra-chunk
+// product), the entering state [P][N] in LDS (B operand of the state term). Wave w handles the 16-row tiles r with r mod 8 in {w, 7 - w}
 // so that the causal work is balanced. Per row tile:
 //   acc  = sum_j (CB[i,j] exp(cum_i - cum_j) dt_j [j <= i]) x_j      (MFMA)
 //   acc += (exp(cum_i) C_i) . H_in^T                                  (MFMA)
@@ -403,8 +392,8 @@ template <typename TIn, int P, int N>
 __global__ __launch_bounds__(256) void chunk_scan_kernel(
     int S, int H, int G, int Q, int max_chunks, const TIn *__restrict__ x,
     const TIn *__restrict__ C, const float *__restrict__ D, const int32_t *__restrict__ meta,
-    const float *__restrict__ cum, const float *__restrict__ dtc, const float *__restrict__ CB,
-    const float *__restrict__ entering, TIn *__restrict__ y)
+    const float *__restrict__ cum, const float *__restrict__ dtc, const TIn *__restrict__ CB,
+    const TIn *__restrict__ entering, TIn *__restrict__ y)
 {
     typedef Mma<TIn> M;
     constexpr int KPL = M::KPL, KS = M::K;
@@ -435,20 +424,18 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
     stage_transposed<TIn, P, false>(xs, LDX, x + ((int64_t)ci.start * H + h) * P, (int64_t)H * P,
                                     len, (Q + 7) / 8 * 8, nullptr, tid, 256);
     {
-        const float *hin = entering + ((int64_t)c * H + h) * P * N;
+        const TIn *hin = entering + ((int64_t)c * H + h) * P * N;
         for (int e = tid * 4; e < P * N; e += 256 * 4) {
-            float v[4];
-            load4<float>(hin + e, v);
             const int p = e / N, n = e % N;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) hsm[p * LDH + n + k] = from_f32<TIn>(v[k]);
+            for (int k = 0; k < 4; ++k) hsm[p * LDH + n + k] = hin[e + k];
         }
     }
     __syncthreads();
 
     const float Dh = D ? D[h] : 0.0f;
     const TIn *Cbase = C + ((int64_t)ci.start * G + g) * N;
-    const float *CBc = CB + ((int64_t)c * G + g) * Q * Q;
+    const TIn *CBc = CB + ((int64_t)c * G + g) * Q * Q;
     const int ntiles = (len + 15) / 16;
 
     for (int rr = 0; rr < (Q / 16 + 7) / 8 * 2; ++rr) {
@@ -468,15 +455,12 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
         for (int j0 = 0; j0 <= i0 + 15; j0 += KS) {
             const int jb = j0 + kg * KPL;
             typename M::frag af;
-            float cbv[KPL];
+            float cbv[Vec16<TIn>::kElems > KPL ? Vec16<TIn>::kElems : KPL];
             if constexpr (KPL == 8) {
-                const float4 q0 = *reinterpret_cast<const float4 *>(CBc + (int64_t)i * Q + jb);
-                const float4 q1 = *reinterpret_cast<const float4 *>(CBc + (int64_t)i * Q + jb + 4);
-                cbv[0] = q0.x; cbv[1] = q0.y; cbv[2] = q0.z; cbv[3] = q0.w;
-                cbv[4] = q1.x; cbv[5] = q1.y; cbv[6] = q1.z; cbv[7] = q1.w;
+                Vec16<TIn>::load(CBc + (int64_t)i * Q + jb, cbv);
             } else {
 #pragma unroll
-                for (int v = 0; v < KPL; ++v) cbv[v] = CBc[(int64_t)i * Q + jb + v];
+                for (int v = 0; v < KPL; ++v) cbv[v] = to_f32(CBc[(int64_t)i * Q + jb + v]);
             }
 #pragma unroll
             for (int v = 0; v < KPL; ++v) {
@@ -533,14 +517,305 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
 }
 
 // ===========================================================================
+// Fast bf16 kernels for headdim 64, d_state 128 (gfx950).
+//
+// Tiles are staged in LDS row-major - token rows, 16-byte copies straight
+// from HBM - and MFMA operands that need the token index contiguous per lane
+// are read with the LDS transpose read (mfma_frag_tr). Rows are padded by 16
+// bytes (LD = 72 elements = 36 dwords), which puts the four rows one 16-lane
+// group reads in disjoint bank ranges. Blocks are put in XCD-aware order so
+// the heads sharing a chunk's B, C and CB run on one L2.
+constexpr int kFastLD = 72;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ uint4 ld16(const bf16 *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ void st16(bf16 *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
+__device__ __forceinline__ uint4 zero16() { return make_uint4(0u, 0u, 0u, 0u); }
+
+// Chunk state, bf16, P = 64, N = 128 split in two 64-column halves.
+// Grid: max_chunks * 2 * H blocks of 256 threads, logical order (chunk, half, head).
+// Wave w computes rows p in [16 w, 16 w + 16) of the [64 x 64] half-state:
+//   S[p][n] = sum_t (w_t x_t[p]) B_t[n],  w_t = exp(cum_last - cum_t) dt_t.
+__global__ __launch_bounds__(256) void chunk_state_fast_kernel(
+    int S, int H, int G, int Q, int max_chunks, const bf16 *__restrict__ x,
+    const bf16 *__restrict__ B, const int32_t *__restrict__ meta, const float *__restrict__ cum,
+    const float *__restrict__ dtc, float *__restrict__ states)
+{
+    constexpr int P = 64, N = 128, NH = 64, LD = kFastLD;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    bf16 *xs = reinterpret_cast<bf16 *>(smem);   // [Q][LD]  w_t * x_t
+    bf16 *bs = xs + Q * LD;                      // [Q][LD]  B_t, one column half
+    float *ws = reinterpret_cast<float *>(bs + Q * LD);
+
+    const int nblk = max_chunks * 2 * H;
+    const int lb = xcd_logical_block(blockIdx.x, nblk);
+    const int h = lb % H, nh = (lb / H) & 1, c = lb / (2 * H);
+    const ChunkInfo ci = chunk_info(meta, S, c);
+    if (ci.len <= 0) return;
+    const int g = h / (H / G);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int len = ci.len;
+
+    // issue every global load of the chunk first: x rows and B half-rows, 8 vectors of
+    // 8 bf16 per row, Q rows each -> Q / 32 vectors of each per thread (<= 8)
+    uint4 xr[8], br[8];
+    const bf16 *xsrc = x + ((int64_t)ci.start * H + h) * P;
+    const bf16 *bsrc = B + ((int64_t)ci.start * G + g) * N + nh * NH;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int u = tid + 256 * k;
+        const int t = u >> 3, c8 = u & 7;
+        const bool ok = u < Q * 8 && t < len;
+        xr[k] = ok ? ld16(xsrc + (int64_t)t * H * P + 8 * c8) : zero16();
+        br[k] = ok ? ld16(bsrc + (int64_t)t * G * N + 8 * c8) : zero16();
+    }
+    const float *cumrow = cum + ((int64_t)h * max_chunks + c) * Q;
+    const float *dtrow = dtc + ((int64_t)h * max_chunks + c) * Q;
+    const float cum_last = cumrow[len - 1];
+    for (int t = tid; t < Q; t += 256)
+        ws[t] = t < len ? __expf(cum_last - cumrow[t]) * dtrow[t] : 0.0f;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int u = tid + 256 * k;
+        if (u < Q * 8) {
+            const int t = u >> 3, c8 = u & 7;
+            float v[8];
+            const uint32_t w4[4] = {xr[k].x, xr[k].y, xr[k].z, xr[k].w};
+            const float wt = ws[t];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = __uint_as_float(w4[i] << 16) * wt;
+                v[2 * i + 1] = __uint_as_float(w4[i] & 0xffff0000u) * wt;
+            }
+            Vec16<bf16>::store(xs + t * LD + 8 * c8, v);
+            st16(bs + t * LD + 8 * c8, br[k]);
+        }
+    }
+    __syncthreads();
+
+    f32x4 acc[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[ct] = zero4();
+    const int nk = (len + 31) / 32;
+    for (int ks = 0; ks < nk; ++ks) {
+        const int t0 = 32 * ks;
+        const bf16x8 af = mfma_frag_tr(xs, LD, t0, 16 * wave, lane);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            const bf16x8 bf = mfma_frag_tr(bs, LD, t0, 16 * ct, lane);
+            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[ct], 0, 0, 0);
+        }
+    }
+    // direct stores: for each (ct, v) 16 lanes write 64 contiguous bytes. (Staging
+    // this tile through LDS for 16-byte stores was tried; the compiler merged the
+    // LDS writes into ds_write2_b32 with wrong offsets, so it is not done.)
+    float *out = states + ((int64_t)c * H + h) * P * N + nh * NH;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            out[(16 * wave + 4 * kg + v) * N + 16 * ct + r16] = acc[ct][v];
+}
+
+// Chunk scan, bf16, P = 64, N = 128. Grid: max_chunks * H blocks of 2 Q threads
+// (Q / 32 waves), logical order (chunk, head). Wave w owns the 16-row tiles w and
+// Q / 16 - 1 - w, which balances the causal work. Per row tile (rows i):
+//   acc  = sum_{j <= i} (CB[i,j] exp(cum_i - cum_j) dt_j) x_j    A: registers, B: x tr-read
+//   acc += (exp(cum_i) C_i) . H_in^T                               A: C from HBM, B: H_in (LDS)
+//   y_i  = acc + D_h x_i
+// Every CB fragment a wave needs (at most Q / 32 + 1 of 16 bytes per lane) is
+// requested before the staging barrier, so the intra-chunk loop never waits
+// on memory; y leaves through a per-wave LDS tile as 16-byte row stores.
+constexpr int kScanMaxSteps = 9;   // CB fragments per wave for Q <= 256
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__global__ __launch_bounds__(512) void chunk_scan_fast_kernel(
+    int S, int H, int G, int Q, int max_chunks, const bf16 *__restrict__ x,
+    const bf16 *__restrict__ C, const float *__restrict__ D, const int32_t *__restrict__ meta,
+    const float *__restrict__ cum, const float *__restrict__ dtc, const bf16 *__restrict__ CB,
+    const bf16 *__restrict__ entering, bf16 *__restrict__ y)
+{
+    constexpr int P = 64, N = 128, LDX = kFastLD, LDH = N + 8, LDY = P + 8;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    bf16 *xs = reinterpret_cast<bf16 *>(smem);                // [Q][LDX]
+    bf16 *hs = xs + Q * LDX;                                   // [P][LDH]
+    bf16 *ys = hs + P * LDH;                                   // [Q / 32][16][LDY]
+    float *scum = reinterpret_cast<float *>(ys + (Q / 32) * 16 * LDY);  // [Q] cum * log2(e)
+    float *sdt = scum + Q;                                     // [Q]
+
+    const int nblk = max_chunks * H;
+    const int lb = xcd_logical_block(blockIdx.x, nblk);
+    const int h = lb % H, c = lb / H;
+    const ChunkInfo ci = chunk_info(meta, S, c);
+    if (ci.len <= 0) return;
+    const int g = h / (H / G);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nthr = blockDim.x;          // 2 Q
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int len = ci.len;
+
+    const int ntiles = (len + 15) / 16;
+    const int rtA = wave, rtB = Q / 16 - 1 - wave;
+    const int nkA = rtA < ntiles ? (16 * rtA + 15) / 32 + 1 : 0;
+    const int nkB = rtB < ntiles ? (16 * rtB + 15) / 32 + 1 : 0;
+
+    // CB fragments of both row tiles: slot s < nkA is step s of tile A, slot
+    // nkA <= s < nkA + nkB is step s - nkA of tile B
+    const bf16 *CBc = CB + ((int64_t)c * G + g) * Q * Q;
+    uint4 cbf[kScanMaxSteps];
+#pragma unroll
+    for (int s2 = 0; s2 < kScanMaxSteps; ++s2) {
+        const bool isA = s2 < nkA;
+        const int ks = isA ? s2 : s2 - nkA;
+        const int i = 16 * (isA ? rtA : rtB) + r16;
+        cbf[s2] = s2 < nkA + nkB ? ld16(CBc + (int64_t)i * Q + 32 * ks + 8 * kg) : zero16();
+    }
+
+    // stage x (raw, row-major), the entering state, cum and dt
+    {
+        const bf16 *xsrc = x + ((int64_t)ci.start * H + h) * P;
+        uint4 xr[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {        // Q rows x 8 vectors over 2 Q threads
+            const int u = tid + nthr * k;
+            const int t = u >> 3, c8 = u & 7;
+            xr[k] = t < len ? ld16(xsrc + (int64_t)t * H * P + 8 * c8) : zero16();
+        }
+        const bf16 *hin = entering + ((int64_t)c * H + h) * P * N;
+        for (int u = tid; u < P * N / 8; u += nthr) {
+            const int p = u >> 4, c8 = u & 15;
+            st16(hs + p * LDH + 8 * c8, ld16(hin + p * N + 8 * c8));
+        }
+        const float *cumrow = cum + ((int64_t)h * max_chunks + c) * Q;
+        const float *dtrow = dtc + ((int64_t)h * max_chunks + c) * Q;
+        for (int i = tid; i < Q; i += nthr) {
+            scum[i] = cumrow[i] * kLog2e;
+            sdt[i] = dtrow[i];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int u = tid + nthr * k;
+            st16(xs + (u >> 3) * LDX + 8 * (u & 7), xr[k]);
+        }
+    }
+    __syncthreads();
+
+    const float Dh = D ? D[h] : 0.0f;
+    const bf16 *Cb = C + ((int64_t)ci.start * G + g) * N;
+    bf16 *yw = ys + wave * 16 * LDY;
+
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+        const int nk = half ? nkB : nkA;
+        if (nk == 0) continue;
+        const int i0 = 16 * (half ? rtB : rtA);
+        const int i = i0 + r16;
+        const float ci2 = scum[i];
+
+        uint4 cr[N / 32];                    // C rows of the state term
+#pragma unroll
+        for (int kk = 0; kk < N / 32; ++kk)
+            cr[kk] = i < len ? ld16(Cb + (int64_t)i * G * N + 32 * kk + 8 * kg) : zero16();
+
+        f32x4 acc[P / 16];
+#pragma unroll
+        for (int pt = 0; pt < P / 16; ++pt) acc[pt] = zero4();
+
+        // intra-chunk product over the prefetched CB fragments
+#pragma unroll
+        for (int s2 = 0; s2 < kScanMaxSteps; ++s2) {
+            const bool mine = half ? (s2 >= nkA && s2 < nkA + nkB) : (s2 < nkA);
+            if (mine) {
+                const int j0 = 32 * (half ? s2 - nkA : s2), jb = j0 + 8 * kg;
+                const uint32_t w4[4] = {cbf[s2].x, cbf[s2].y, cbf[s2].z, cbf[s2].w};
+                bf16x8 af;
+#pragma unroll
+                for (int v = 0; v < 8; ++v) {
+                    const int j = jb + v;
+                    const float cbv = __uint_as_float((v & 1) ? (w4[v >> 1] & 0xffff0000u)
+                                                              : (w4[v >> 1] << 16));
+                    const float m = cbv * __builtin_amdgcn_exp2f(ci2 - scum[j]) * sdt[j];
+                    af[v] = static_cast<bf16>(j <= i ? m : 0.0f);
+                }
+#pragma unroll
+                for (int pt = 0; pt < P / 16; ++pt) {
+                    const bf16x8 bf = mfma_frag_tr(xs, LDX, j0, 16 * pt, lane);
+                    acc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[pt], 0, 0, 0);
+                }
+            }
+        }
+
+        // state term
+        const float ei = __builtin_amdgcn_exp2f(ci2);
+#pragma unroll
+        for (int kk = 0; kk < N / 32; ++kk) {
+            const int n = 32 * kk + 8 * kg;
+            const uint32_t w4[4] = {cr[kk].x, cr[kk].y, cr[kk].z, cr[kk].w};
+            bf16x8 af;
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+                const float cv = __uint_as_float((v & 1) ? (w4[v >> 1] & 0xffff0000u)
+                                                         : (w4[v >> 1] << 16));
+                af[v] = static_cast<bf16>(ei * cv);
+            }
+#pragma unroll
+            for (int pt = 0; pt < P / 16; ++pt) {
+                const bf16x8 bf = *reinterpret_cast<const bf16x8 *>(hs + (16 * pt + r16) * LDH + n);
+                acc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[pt], 0, 0, 0);
+            }
+        }
+
+        // epilogue: + D x into the wave's LDS tile, then 16-byte row stores
+#pragma unroll
+        for (int pt = 0; pt < P / 16; ++pt) {
+            const int p = 16 * pt + r16;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int il = 4 * kg + v;
+                const float xv = static_cast<float>(xs[(i0 + il) * LDX + p]);
+                yw[il * LDY + p] = static_cast<bf16>(acc[pt][v] + Dh * xv);
+            }
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int u = lane + 64 * k;      // 16 rows x 8 vectors
+            const int il = u >> 3, c8 = u & 7;
+            if (i0 + il < len)
+                st16(y + ((int64_t)(ci.start + i0 + il) * H + h) * P + 8 * c8,
+                     ld16(yw + il * LDY + 8 * c8));
+        }
+        wave_lds_sync();
+    }
+}
+
+// ===========================================================================
 // Launchers.
 static inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+static inline bool use_fast(const PrefillDims &d) { return d.in_bf16 && d.P == 64 && d.N == 128; }
+
+// Raise a kernel's dynamic LDS limit once (idempotent; only needed above 64 KiB).
+static void allow_lds(const void *fn, size_t bytes, bool &done)
+{
+    if (bytes > 65536 && !done) {
+        done = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) ==
+               hipSuccess;
+    }
+}
 
 template <typename TIn>
 static void launch_cumsum_t(const PrefillDims &d, const void *dt, const float *A, const int32_t *cu,
                             int32_t *meta, float *cum, float *dto, hipStream_t st)
 {
-    dim3 grid(d.max_chunks, (d.H + kCumsumHeads - 1) / kCumsumHeads);
+    dim3 grid(d.max_chunks, (d.H + kCumsumHeadsPerBlock - 1) / kCumsumHeadsPerBlock);
     hipLaunchKernelGGL(chunk_cumsum_kernel<TIn>, grid, dim3(256), 0, st, d.T, d.S, d.H, d.Q,
                        d.max_chunks, static_cast<const TIn *>(dt), A, cu, meta, cum, dto);
 }
@@ -565,11 +840,12 @@ static void launch_state_t(const PrefillDims &d, const void *x, const void *B, c
 
 template <typename TIn, int N>
 static void launch_bmm_t(const PrefillDims &d, const void *B, const void *C, const int32_t *meta,
-                         float *CB, hipStream_t st)
+                         void *CB, hipStream_t st)
 {
-    dim3 grid(d.max_chunks, d.G, (d.Q + 63) / 64);
+    dim3 grid(d.max_chunks, d.G, d.Q / 16);
     hipLaunchKernelGGL((bmm_kernel<TIn, N>), grid, dim3(256), 0, st, d.S, d.G, d.Q, d.max_chunks,
-                       static_cast<const TIn *>(B), static_cast<const TIn *>(C), meta, CB);
+                       static_cast<const TIn *>(B), static_cast<const TIn *>(C), meta,
+                       static_cast<TIn *>(CB));
 }
 
 template <typename TIn, int P, int N>
@@ -581,23 +857,17 @@ static size_t scan_smem(int Q)
 
 template <typename TIn, int P, int N>
 static void launch_scan_t(const PrefillDims &d, const void *x, const void *C, const float *D,
-                          const int32_t *meta, const float *cum, const float *dtc, const float *CB,
-                          const float *entering, void *y, hipStream_t st)
+                          const int32_t *meta, const float *cum, const float *dtc, const void *CB,
+                          const void *entering, void *y, hipStream_t st)
 {
     dim3 grid(d.H, d.max_chunks);
     const size_t smem = scan_smem<TIn, P, N>(d.Q);
-    if (smem > 65536) {
-        // raise the dynamic LDS limit of this instantiation once (idempotent)
-        static bool raised = false;
-        if (!raised) {
-            hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_scan_kernel<TIn, P, N>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-            raised = true;
-        }
-    }
+    static bool raised = false;
+    allow_lds(reinterpret_cast<const void *>(&chunk_scan_kernel<TIn, P, N>), smem, raised);
     hipLaunchKernelGGL((chunk_scan_kernel<TIn, P, N>), grid, dim3(256), smem, st, d.S, d.H, d.G,
                        d.Q, d.max_chunks, static_cast<const TIn *>(x), static_cast<const TIn *>(C),
-                       D, meta, cum, dtc, CB, entering, static_cast<TIn *>(y));
+                       D, meta, cum, dtc, static_cast<const TIn *>(CB),
+                       static_cast<const TIn *>(entering), static_cast<TIn *>(y));
 }
 
 #define SSD_DISPATCH_PN(d, FN, TIN, ...)                                 \
@@ -613,11 +883,21 @@ void launch_chunk_state(const PrefillDims &d, const void *x, const void *B, cons
 {
     if (d.max_chunks <= 0) return;
     hipStream_t st = as_stream(stream);
+    if (use_fast(d)) {
+        const size_t smem = (size_t)d.Q * (2 * kFastLD * sizeof(bf16) + sizeof(float));
+        static bool raised = false;
+        allow_lds(reinterpret_cast<const void *>(&chunk_state_fast_kernel), smem, raised);
+        const unsigned nblk = (unsigned)((int64_t)d.max_chunks * 2 * d.H);
+        hipLaunchKernelGGL(chunk_state_fast_kernel, dim3(nblk), dim3(256), smem, st, d.S, d.H, d.G,
+                           d.Q, d.max_chunks, static_cast<const bf16 *>(x),
+                           static_cast<const bf16 *>(B), meta, cum, dtc, states);
+        return;
+    }
     if (d.in_bf16) SSD_DISPATCH_PN(d, launch_state_t, bf16, d, x, B, meta, cum, dtc, states, st);
     else SSD_DISPATCH_PN(d, launch_state_t, float, d, x, B, meta, cum, dtc, states, st);
 }
 
-void launch_bmm(const PrefillDims &d, const void *B, const void *C, const int32_t *meta, float *CB,
+void launch_bmm(const PrefillDims &d, const void *B, const void *C, const int32_t *meta, void *CB,
                 void *stream)
 {
     if (d.max_chunks <= 0) return;
@@ -631,50 +911,58 @@ void launch_bmm(const PrefillDims &d, const void *B, const void *C, const int32_
     }
 }
 
-void launch_state_passing(const PrefillDims &d, const float *states, const float *cum,
-                          const int32_t *meta, void *cache, const int32_t *idx,
-                          const uint8_t *has_init, float *entering, void *ckpt, void *stream)
+template <typename TS, typename TE>
+static void launch_sp_t(const PrefillDims &d, const float *states, const float *cum,
+                        const int32_t *meta, void *cache, const int32_t *idx,
+                        const uint8_t *has_init, void *entering, void *ckpt, hipStream_t st)
 {
-    if (d.S <= 0) return;
     const int PN = d.P * d.N;
     const int EB = (PN + 1023) / 1024;
     dim3 grid((unsigned)((int64_t)d.S * d.H * EB));
+    hipLaunchKernelGGL((state_passing_kernel<TS, TE>), grid, dim3(256), 0, st, d.S, d.H, PN, d.Q,
+                       d.max_chunks, d.num_slots, states, cum, meta, static_cast<TS *>(cache), idx,
+                       has_init, static_cast<TE *>(entering), static_cast<TS *>(ckpt));
+}
+
+void launch_state_passing(const PrefillDims &d, const float *states, const float *cum,
+                          const int32_t *meta, void *cache, const int32_t *idx,
+                          const uint8_t *has_init, void *entering, void *ckpt, void *stream)
+{
+    if (d.S <= 0) return;
     hipStream_t st = as_stream(stream);
-    if (d.state_bf16)
-        hipLaunchKernelGGL(state_passing_kernel<bf16>, grid, dim3(256), 0, st, d.S, d.H, PN, d.Q,
-                           d.max_chunks, d.num_slots, states, cum, meta,
-                           static_cast<bf16 *>(cache), idx, has_init, entering,
-                           static_cast<bf16 *>(ckpt));
-    else
-        hipLaunchKernelGGL(state_passing_kernel<float>, grid, dim3(256), 0, st, d.S, d.H, PN, d.Q,
-                           d.max_chunks, d.num_slots, states, cum, meta,
-                           static_cast<float *>(cache), idx, has_init, entering,
-                           static_cast<float *>(ckpt));
+    if (d.state_bf16) {
+        if (d.in_bf16) launch_sp_t<bf16, bf16>(d, states, cum, meta, cache, idx, has_init, entering, ckpt, st);
+        else launch_sp_t<bf16, float>(d, states, cum, meta, cache, idx, has_init, entering, ckpt, st);
+    } else {
+        if (d.in_bf16) launch_sp_t<float, bf16>(d, states, cum, meta, cache, idx, has_init, entering, ckpt, st);
+        else launch_sp_t<float, float>(d, states, cum, meta, cache, idx, has_init, entering, ckpt, st);
+    }
 }
 
 void launch_chunk_scan(const PrefillDims &d, const void *x, const void *C, const float *D,
-                       const int32_t *meta, const float *cum, const float *dtc, const float *CB,
-                       const float *entering, void *y, void *stream)
+                       const int32_t *meta, const float *cum, const float *dtc, const void *CB,
+                       const void *entering, void *y, void *stream)
 {
     if (d.max_chunks <= 0) return;
     hipStream_t st = as_stream(stream);
+    if (use_fast(d)) {
+        const size_t smem = (size_t)d.Q * (kFastLD * sizeof(bf16) + 2 * sizeof(float)) +
+                            (size_t)64 * (128 + 8) * sizeof(bf16) +
+                            (size_t)(d.Q / 32) * 16 * (64 + 8) * sizeof(bf16);
+        static bool raised = false;
+        allow_lds(reinterpret_cast<const void *>(&chunk_scan_fast_kernel), smem, raised);
+        const unsigned nblk = (unsigned)((int64_t)d.max_chunks * d.H);
+        hipLaunchKernelGGL(chunk_scan_fast_kernel, dim3(nblk), dim3(2 * d.Q), smem, st, d.S, d.H,
+                           d.G, d.Q, d.max_chunks, static_cast<const bf16 *>(x),
+                           static_cast<const bf16 *>(C), D, meta, cum, dtc,
+                           static_cast<const bf16 *>(CB), static_cast<const bf16 *>(entering),
+                           static_cast<bf16 *>(y));
+        return;
+    }
     if (d.in_bf16)
         SSD_DISPATCH_PN(d, launch_scan_t, bf16, d, x, C, D, meta, cum, dtc, CB, entering, y, st);
     else
         SSD_DISPATCH_PN(d, launch_scan_t, float, d, x, C, D, meta, cum, dtc, CB, entering, y, st);
-}
-
-size_t chunk_scan_smem_bytes(const PrefillDims &d)
-{
-    size_t s;
-    if (d.in_bf16) {
-        if (d.P == 64) s = d.N == 128 ? scan_smem<bf16, 64, 128>(d.Q) : scan_smem<bf16, 64, 16>(d.Q);
-        else s = d.N == 128 ? scan_smem<bf16, 16, 128>(d.Q) : scan_smem<bf16, 16, 16>(d.Q);
-    } else {
-        if (d.P == 64) s = d.N == 128 ? scan_smem<float, 64, 128>(d.Q) : scan_smem<float, 64, 16>(d.Q);
-        else s = d.N == 128 ? scan_smem<float, 16, 128>(d.Q) : scan_smem<float, 16, 16>(d.Q);
-    }
-    return s;
 }
 
 }  // namespace ssd

@@ -50,7 +50,8 @@ def test_sizes():
     ws = ssd.workspace_bytes(p)
     # meta, cumsum, dt, CB and chunk states, each rounded up to 256 bytes
     r = lambda v: (v + 255) // 256 * 256
-    want = r(4 * 17) + 2 * r(4 * 4 * 5 * 64) + r(4 * 5 * 1 * 64 * 64) + r(4 * 5 * 4 * 16 * 16)
+    want = (r(4 * 17) + 2 * r(4 * 4 * 5 * 64) + r(4 * 5 * 1 * 64 * 64) + r(4 * 5 * 4 * 16 * 16)
+            + r(4 * 5 * 4 * 16 * 16))   # fp32 inputs: CB and entering states in fp32
     assert ws == want
     big = P(total_tokens=4096, nheads=80, headdim=64, d_state=128, chunk_size=256,
             in_dtype=torch.bfloat16)
