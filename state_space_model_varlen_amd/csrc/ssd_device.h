@@ -173,6 +173,23 @@ __device__ __forceinline__ bf16x8 mfma_frag_tr(const bf16 *tile, int ld, int k0,
     return __builtin_bit_cast(bf16x8, both);
 }
 
+// Same fragment with the "split" K order: lane group kg holds K = 4 kg + v for
+// v < 4 and K = 16 + 4 kg + (v - 4) for v >= 4. Each read then covers 16
+// consecutive tile rows across the wave, so with a row pitch of 40 dwords
+// the 8 rows one 32-lane half reads start in 8 distinct 8-bank groups (no
+// bank conflicts), and with 36 dwords they overlap in 4 banks only. Both
+// operands of an MFMA must use the same K order.
+__device__ __forceinline__ bf16x8 mfma_frag_tr_split(const bf16 *tile, int ld, int k0, int col0,
+                                                     int lane) {
+    const int kg = lane >> 4, j = lane & 15;
+    const bf16 *p = tile + (k0 + 4 * kg + (j >> 2)) * ld + col0 + 4 * (j & 3);
+    const v4i16 lo = lds_read_tr16(p);
+    const v4i16 hi = lds_read_tr16(p + 16 * ld);
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, both);
+}
+
 // ---------------------------------------------------------------------------
 // XCD-aware block order. Workgroups are dispatched round-robin over the 8 XCDs
 // (each with its own L2); this maps the hardware block id to a logical id so

@@ -297,13 +297,14 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
     int c0 = meta[s], c1 = meta[s + 1];
     c0 = c0 < max_chunks ? c0 : max_chunks;
     c1 = c1 < max_chunks ? c1 : max_chunks;
-    // chunks in batches of 8: every chunk state of a batch is loaded before the
-    // sequential recurrence over the batch runs (8 loads in flight per thread)
-    for (int cb = c0; cb < c1; cb += 8) {
-        const int nb = c1 - cb < 8 ? c1 - cb : 8;
-        float sc[8][4], dec[8];
+    // chunks in batches of kBatch: every chunk state of a batch is loaded before
+    // the sequential recurrence over the batch runs (kBatch loads in flight)
+    constexpr int kBatch = 16;
+    for (int cb = c0; cb < c1; cb += kBatch) {
+        const int nb = c1 - cb < kBatch ? c1 - cb : kBatch;
+        float sc[kBatch][4], dec[kBatch];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < kBatch; ++k) {
             if (k < nb) {
                 const int c = cb + k;
                 load4<float>(states + ((int64_t)c * H + h) * PN + e, sc[k]);
@@ -312,7 +313,7 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
             }
         }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < kBatch; ++k) {
             if (k < nb) {
                 const int64_t off = ((int64_t)(cb + k) * H + h) * PN + e;
                 // the chunk state at `off` was loaded above, before the entering
@@ -525,7 +526,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
 // bytes (LD = 72 elements = 36 dwords), which puts the four rows one 16-lane
 // group reads in disjoint bank ranges. Blocks are put in XCD-aware order so
 // the heads sharing a chunk's B, C and CB run on one L2.
-constexpr int kFastLD = 72;
+constexpr int kFastLD = 72;   // row pitch of token-major tiles (64 bf16 + 8 pad)
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ uint4 ld16(const bf16 *p) { return *reinterpret_cast<const uint4 *>(p); }
@@ -536,8 +537,9 @@ __device__ __forceinline__ uint4 zero16() { return make_uint4(0u, 0u, 0u, 0u); }
 // Grid: max_chunks * 2 * H blocks of 256 threads, logical order (chunk, half, head).
 // Wave w computes rows p in [16 w, 16 w + 16) of the [64 x 64] half-state:
 //   S[p][n] = sum_t (w_t x_t[p]) B_t[n],  w_t = exp(cum_last - cum_t) dt_t.
+template <int Q>
 __global__ __launch_bounds__(256) void chunk_state_fast_kernel(
-    int S, int H, int G, int Q, int max_chunks, const bf16 *__restrict__ x,
+    int S, int H, int G, int max_chunks, const bf16 *__restrict__ x,
     const bf16 *__restrict__ B, const int32_t *__restrict__ meta, const float *__restrict__ cum,
     const float *__restrict__ dtc, float *__restrict__ states)
 {
@@ -559,14 +561,15 @@ __global__ __launch_bounds__(256) void chunk_state_fast_kernel(
 
     // issue every global load of the chunk first: x rows and B half-rows, 8 vectors of
     // 8 bf16 per row, Q rows each -> Q / 32 vectors of each per thread (<= 8)
-    uint4 xr[8], br[8];
+    constexpr int kVec = Q / 32;          // vectors of each tile per thread
+    uint4 xr[kVec], br[kVec];
     const bf16 *xsrc = x + ((int64_t)ci.start * H + h) * P;
     const bf16 *bsrc = B + ((int64_t)ci.start * G + g) * N + nh * NH;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < kVec; ++k) {
         const int u = tid + 256 * k;
         const int t = u >> 3, c8 = u & 7;
-        const bool ok = u < Q * 8 && t < len;
+        const bool ok = t < len;
         xr[k] = ok ? ld16(xsrc + (int64_t)t * H * P + 8 * c8) : zero16();
         br[k] = ok ? ld16(bsrc + (int64_t)t * G * N + 8 * c8) : zero16();
     }
@@ -577,9 +580,9 @@ __global__ __launch_bounds__(256) void chunk_state_fast_kernel(
         ws[t] = t < len ? __expf(cum_last - cumrow[t]) * dtrow[t] : 0.0f;
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < kVec; ++k) {
         const int u = tid + 256 * k;
-        if (u < Q * 8) {
+        {
             const int t = u >> 3, c8 = u & 7;
             float v[8];
             const uint32_t w4[4] = {xr[k].x, xr[k].y, xr[k].z, xr[k].w};
@@ -601,10 +604,10 @@ __global__ __launch_bounds__(256) void chunk_state_fast_kernel(
     const int nk = (len + 31) / 32;
     for (int ks = 0; ks < nk; ++ks) {
         const int t0 = 32 * ks;
-        const bf16x8 af = mfma_frag_tr(xs, LD, t0, 16 * wave, lane);
+        const bf16x8 af = mfma_frag_tr_split(xs, LD, t0, 16 * wave, lane);
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
-            const bf16x8 bf = mfma_frag_tr(bs, LD, t0, 16 * ct, lane);
+            const bf16x8 bf = mfma_frag_tr_split(bs, LD, t0, 16 * ct, lane);
             acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[ct], 0, 0, 0);
         }
     }
@@ -621,14 +624,25 @@ __global__ __launch_bounds__(256) void chunk_state_fast_kernel(
 
 // Chunk scan, bf16, P = 64, N = 128. Grid: max_chunks * H blocks of 2 Q threads
 // (Q / 32 waves), logical order (chunk, head). Wave w owns the 16-row tiles w and
-// Q / 16 - 1 - w, which balances the causal work. Per row tile (rows i):
-//   acc  = sum_{j <= i} (CB[i,j] exp(cum_i - cum_j) dt_j) x_j    A: registers, B: x tr-read
-//   acc += (exp(cum_i) C_i) . H_in^T                               A: C from HBM, B: H_in (LDS)
+// Q / 16 - 1 - w, which balances the causal work.
+//
+// The segment decay exp(cum_i - cum_j) is split at R_k, the cumsum at the last
+// position of the 32-token K block k that holds j:
+//     exp(cum_i - cum_j) dt_j = exp(cum_i - R_k) * [exp(R_k - cum_j) dt_j]
+// The bracket depends on j only; it scales x once per block while the x tile is
+// staged (B operand x'_j). What remains per A element is the CB value times
+// one per-(row, K block) factor: one exponential per lane per K step instead
+// of eight. Within a block both factors stay in [exp(-span), exp(span)], span
+// = |cum| change over the block; a block whose span exceeds kMaxSpan (where
+// float32/bf16 range could be lost) is computed with the exact per-element
+// exponentials on unscaled x instead.
+//   acc  = sum_j A_ij x'_j,   A_ij = CB[i,j] exp(cum_i - R_k) [j <= i]    (MFMA)
+//   acc += (exp(cum_i) C_i) . H_in^T                                        (MFMA)
 //   y_i  = acc + D_h x_i
-// Every CB fragment a wave needs (at most Q / 32 + 1 of 16 bytes per lane) is
-// requested before the staging barrier, so the intra-chunk loop never waits
-// on memory; y leaves through a per-wave LDS tile as 16-byte row stores.
-constexpr int kScanMaxSteps = 9;   // CB fragments per wave for Q <= 256
+// CB fragments (two 8-byte pieces per lane per K step, split K order) are all
+// requested before the staging barrier; y leaves through a per-wave LDS tile
+// as 16-byte row stores.
+constexpr float kMaxSpan = 60.0f;    // natural-log units
 
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -636,16 +650,158 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__global__ __launch_bounds__(512) void chunk_scan_fast_kernel(
-    int S, int H, int G, int Q, int max_chunks, const bf16 *__restrict__ x,
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// CB fragments of one row tile: row i, K steps 0 .. nk-1, split K order
+// (columns 32 ks + 4 kg + 0..3 and 32 ks + 16 + 4 kg + 0..3).
+template <int K>
+__device__ __forceinline__ void load_cb_frags(const bf16 *CBc, int Q, int i, int kg, int nk,
+                                              uint2 *lo, uint2 *hi)
+{
+#pragma unroll
+    for (int ks = 0; ks < K; ++ks) {
+        const bf16 *src = CBc + (int64_t)i * Q + 32 * ks + 4 * kg;
+        lo[ks] = ks < nk ? *reinterpret_cast<const uint2 *>(src) : make_uint2(0u, 0u);
+        hi[ks] = ks < nk ? *reinterpret_cast<const uint2 *>(src + 16) : make_uint2(0u, 0u);
+    }
+}
+
+// One 16-row tile of the chunk scan (rows i0 .. i0 + 15) for one wave; see the
+// kernel comment. When `prefetch_next`, the CB fragments of the next tile
+// (row tile nrt, nnk steps) are requested after this tile's intra-chunk loop.
+template <int Q, int K, int KN>
+__device__ __forceinline__ void scan_row_tile(
+    int i0, int nk, const uint2 *cbl, const uint2 *cbh, bool exact, int len, int lane,
+    const bf16 *Cb, int G, const float *scum, const float *sdt, const bf16 *xs, const bf16 *hs,
+    bf16 *yw, const bf16 *xsrc, int H, float Dh, bf16 *yout, const bf16 *CBc, int nrt, int nnk,
+    uint2 *ncl, uint2 *nch, bool prefetch_next)
+{
+    constexpr int P = 64, N = 128, LDX = kFastLD, LDH = N + 8, LDY = P + 8;
+    if (nk == 0) {
+        if (prefetch_next) load_cb_frags<KN>(CBc, Q, 16 * nrt + (lane & 15), lane >> 4, nnk, ncl, nch);
+        return;
+    }
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int i = i0 + r16;
+    const float ci2 = scum[i];
+
+    uint4 cr[N / 32];                    // C rows of the state term (raw bf16 A operand)
+#pragma unroll
+    for (int kk = 0; kk < N / 32; ++kk)
+        cr[kk] = i < len ? ld16(Cb + (int64_t)i * G * N + 32 * kk + 8 * kg) : zero16();
+    uint4 xe[2];                         // x rows for the D x term of the epilogue
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int u = lane + 64 * k, il = u >> 3;
+        xe[k] = i0 + il < len ? ld16(xsrc + (int64_t)(i0 + il) * H * P + 8 * (u & 7)) : zero16();
+    }
+
+    f32x4 acc[P / 16];
+#pragma unroll
+    for (int pt = 0; pt < P / 16; ++pt) acc[pt] = zero4();
+
+#pragma unroll
+    for (int ks = 0; ks < K; ++ks) {
+        if (ks < nk) {
+            const int j0 = 32 * ks;
+            const float cbv[8] = {bf16_lo(cbl[ks].x), bf16_hi(cbl[ks].x), bf16_lo(cbl[ks].y),
+                                  bf16_hi(cbl[ks].y), bf16_lo(cbh[ks].x), bf16_hi(cbh[ks].x),
+                                  bf16_lo(cbh[ks].y), bf16_hi(cbh[ks].y)};
+            bf16x8 af;
+            if (!exact) {
+                const float e = __builtin_amdgcn_exp2f(ci2 - scum[j0 + 31 < Q ? j0 + 31 : Q - 1]);
+                if (ks < nk - 1) {               // strictly below the diagonal: no mask
+#pragma unroll
+                    for (int v = 0; v < 8; ++v) af[v] = static_cast<bf16>(cbv[v] * e);
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 8; ++v) {
+                        const int j = j0 + 4 * kg + (v & 3) + ((v >> 2) << 4);
+                        af[v] = static_cast<bf16>(j <= i ? cbv[v] * e : 0.0f);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int v = 0; v < 8; ++v) {
+                    const int j = j0 + 4 * kg + (v & 3) + ((v >> 2) << 4);
+                    const float m = cbv[v] * __builtin_amdgcn_exp2f(ci2 - scum[j]) * sdt[j];
+                    af[v] = static_cast<bf16>(j <= i ? m : 0.0f);
+                }
+            }
+#pragma unroll
+            for (int pt = 0; pt < P / 16; ++pt) {
+                const bf16x8 bf = mfma_frag_tr_split(xs, LDX, j0, 16 * pt, lane);
+                acc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[pt], 0, 0, 0);
+            }
+        }
+    }
+    if (prefetch_next) load_cb_frags<KN>(CBc, Q, 16 * nrt + r16, kg, nnk, ncl, nch);
+
+    // state term: acc2 = C . H_in^T on raw C, then each output row i gets
+    // exp(cum_i) * acc2 (the lane's rows are i0 + 4 kg + v)
+    f32x4 acc2[P / 16];
+#pragma unroll
+    for (int pt = 0; pt < P / 16; ++pt) acc2[pt] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < N / 32; ++kk) {
+        const int n = 32 * kk + 8 * kg;
+        const bf16x8 af = __builtin_bit_cast(bf16x8, cr[kk]);
+#pragma unroll
+        for (int pt = 0; pt < P / 16; ++pt) {
+            const bf16x8 bf = *reinterpret_cast<const bf16x8 *>(hs + (16 * pt + r16) * LDH + n);
+            acc2[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc2[pt], 0, 0, 0);
+        }
+    }
+    float erow[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) erow[v] = __builtin_amdgcn_exp2f(scum[i0 + 4 * kg + v]);
+#pragma unroll
+    for (int pt = 0; pt < P / 16; ++pt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[pt][v] += erow[v] * acc2[pt][v];
+
+    // epilogue: the SSM part goes through the wave's LDS tile into row order,
+    // where D x is added from 16-byte x loads (L2-resident) before the store
+#pragma unroll
+    for (int pt = 0; pt < P / 16; ++pt) {
+        const int p = 16 * pt + r16;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) yw[(4 * kg + v) * LDY + p] = static_cast<bf16>(acc[pt][v]);
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int u = lane + 64 * k;      // 16 rows x 8 vectors
+        const int il = u >> 3, c8 = u & 7;
+        if (i0 + il < len) {
+            const int64_t row = (int64_t)(i0 + il) * H * P + 8 * c8;
+            const uint4 xv = xe[k], sv = ld16(yw + il * LDY + 8 * c8);
+            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, sw[4] = {sv.x, sv.y, sv.z, sv.w};
+            float o[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                o[2 * q] = bf16_lo(sw[q]) + Dh * bf16_lo(xw[q]);
+                o[2 * q + 1] = bf16_hi(sw[q]) + Dh * bf16_hi(xw[q]);
+            }
+            Vec16<bf16>::store(yout + row, o);
+        }
+    }
+    wave_lds_sync();
+}
+
+template <int Q>
+__global__ __launch_bounds__(2 * Q) __attribute__((amdgpu_waves_per_eu(4)))
+void chunk_scan_fast_kernel(
+    int S, int H, int G, int max_chunks, const bf16 *__restrict__ x,
     const bf16 *__restrict__ C, const float *__restrict__ D, const int32_t *__restrict__ meta,
     const float *__restrict__ cum, const float *__restrict__ dtc, const bf16 *__restrict__ CB,
     const bf16 *__restrict__ entering, bf16 *__restrict__ y)
 {
     constexpr int P = 64, N = 128, LDX = kFastLD, LDH = N + 8, LDY = P + 8;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    bf16 *xs = reinterpret_cast<bf16 *>(smem);                // [Q][LDX]
-    bf16 *hs = xs + Q * LDX;                                   // [P][LDH]
+    bf16 *xs = reinterpret_cast<bf16 *>(smem);                // [Q][LDX]  x' (or x)
+    bf16 *hs = xs + Q * LDX;                                   // [P][LDH]  entering state
     bf16 *ys = hs + P * LDH;                                   // [Q / 32][16][LDY]
     float *scum = reinterpret_cast<float *>(ys + (Q / 32) * 16 * LDY);  // [Q] cum * log2(e)
     float *sdt = scum + Q;                                     // [Q]
@@ -657,7 +813,10 @@ __global__ __launch_bounds__(512) void chunk_scan_fast_kernel(
     if (ci.len <= 0) return;
     const int g = h / (H / G);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nthr = blockDim.x;          // 2 Q
+    constexpr int nthr = 2 * Q;
+    constexpr int kStepsB = Q / 32;                   // K steps of row tile B (at most)
+    constexpr int kStepsA = Q / 64 > 0 ? Q / 64 : 1;  // K steps of row tile A (at most)
+    constexpr int kHVec = P * N / 8 / nthr > 0 ? P * N / 8 / nthr : 1;
     const int r16 = lane & 15, kg = lane >> 4;
     const int len = ci.len;
 
@@ -666,32 +825,22 @@ __global__ __launch_bounds__(512) void chunk_scan_fast_kernel(
     const int nkA = rtA < ntiles ? (16 * rtA + 15) / 32 + 1 : 0;
     const int nkB = rtB < ntiles ? (16 * rtB + 15) / 32 + 1 : 0;
 
-    // CB fragments of both row tiles: slot s < nkA is step s of tile A, slot
-    // nkA <= s < nkA + nkB is step s - nkA of tile B
-    const bf16 *CBc = CB + ((int64_t)c * G + g) * Q * Q;
-    uint4 cbf[kScanMaxSteps];
+    // stage cum, dt, the entering state and x' (or x in exact mode)
+    const bf16 *xsrc = x + ((int64_t)ci.start * H + h) * P;
+    uint4 xr[4];
 #pragma unroll
-    for (int s2 = 0; s2 < kScanMaxSteps; ++s2) {
-        const bool isA = s2 < nkA;
-        const int ks = isA ? s2 : s2 - nkA;
-        const int i = 16 * (isA ? rtA : rtB) + r16;
-        cbf[s2] = s2 < nkA + nkB ? ld16(CBc + (int64_t)i * Q + 32 * ks + 8 * kg) : zero16();
+    for (int k = 0; k < 4; ++k) {        // Q rows x 8 vectors over 2 Q threads
+        const int u = tid + nthr * k;
+        const int t = u >> 3, c8 = u & 7;
+        xr[k] = t < len ? ld16(xsrc + (int64_t)t * H * P + 8 * c8) : zero16();
     }
-
-    // stage x (raw, row-major), the entering state, cum and dt
     {
-        const bf16 *xsrc = x + ((int64_t)ci.start * H + h) * P;
-        uint4 xr[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {        // Q rows x 8 vectors over 2 Q threads
-            const int u = tid + nthr * k;
-            const int t = u >> 3, c8 = u & 7;
-            xr[k] = t < len ? ld16(xsrc + (int64_t)t * H * P + 8 * c8) : zero16();
-        }
         const bf16 *hin = entering + ((int64_t)c * H + h) * P * N;
-        for (int u = tid; u < P * N / 8; u += nthr) {
-            const int p = u >> 4, c8 = u & 15;
-            st16(hs + p * LDH + 8 * c8, ld16(hin + p * N + 8 * c8));
+        uint4 hr[kHVec];
+#pragma unroll
+        for (int k = 0; k < kHVec; ++k) {
+            const int u = tid + nthr * k;
+            hr[k] = ld16(hin + (u >> 4) * N + 8 * (u & 15));
         }
         const float *cumrow = cum + ((int64_t)h * max_chunks + c) * Q;
         const float *dtrow = dtc + ((int64_t)h * max_chunks + c) * Q;
@@ -700,9 +849,44 @@ __global__ __launch_bounds__(512) void chunk_scan_fast_kernel(
             sdt[i] = dtrow[i];
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < kHVec; ++k) {
             const int u = tid + nthr * k;
-            st16(xs + (u >> 3) * LDX + 8 * (u & 7), xr[k]);
+            st16(hs + (u >> 4) * LDH + 8 * (u & 15), hr[k]);
+        }
+    }
+    // CB fragments (split K order) of the larger row tile B, requested now so
+    // that they arrive during the staging barriers; tile A's follow later
+    const bf16 *CBc = CB + ((int64_t)c * G + g) * Q * Q;
+    uint2 cbl[kStepsB], cbh[kStepsB];
+    load_cb_frags<kStepsB>(CBc, Q, 16 * rtB + r16, kg, nkB, cbl, cbh);
+    __syncthreads();
+    // scaling factors of x: G_j = exp(R_k - cum_j) dt_j; exact mode when a span is too large
+    bool big = false;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int t = (tid + nthr * k) >> 3;
+        const float rk = scum[(t | 31) < Q ? (t | 31) : Q - 1];
+        big |= fabsf(rk - scum[t]) > kMaxSpan * kLog2e;
+    }
+    const bool exact = __syncthreads_or(big) != 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int u = tid + nthr * k;
+        const int t = u >> 3, c8 = u & 7;
+        uint4 v = xr[k];
+        if (!exact) {
+            const float gt = __builtin_amdgcn_exp2f(scum[(t | 31) < Q ? (t | 31) : Q - 1] - scum[t]) *
+                             sdt[t];
+            float f[8];
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                f[2 * q] = bf16_lo(w4[q]) * gt;
+                f[2 * q + 1] = bf16_hi(w4[q]) * gt;
+            }
+            Vec16<bf16>::store(xs + t * LDX + 8 * c8, f);
+        } else {
+            st16(xs + t * LDX + 8 * c8, v);
         }
     }
     __syncthreads();
@@ -711,89 +895,14 @@ __global__ __launch_bounds__(512) void chunk_scan_fast_kernel(
     const bf16 *Cb = C + ((int64_t)ci.start * G + g) * N;
     bf16 *yw = ys + wave * 16 * LDY;
 
-#pragma unroll 1
-    for (int half = 0; half < 2; ++half) {
-        const int nk = half ? nkB : nkA;
-        if (nk == 0) continue;
-        const int i0 = 16 * (half ? rtB : rtA);
-        const int i = i0 + r16;
-        const float ci2 = scum[i];
-
-        uint4 cr[N / 32];                    // C rows of the state term
-#pragma unroll
-        for (int kk = 0; kk < N / 32; ++kk)
-            cr[kk] = i < len ? ld16(Cb + (int64_t)i * G * N + 32 * kk + 8 * kg) : zero16();
-
-        f32x4 acc[P / 16];
-#pragma unroll
-        for (int pt = 0; pt < P / 16; ++pt) acc[pt] = zero4();
-
-        // intra-chunk product over the prefetched CB fragments
-#pragma unroll
-        for (int s2 = 0; s2 < kScanMaxSteps; ++s2) {
-            const bool mine = half ? (s2 >= nkA && s2 < nkA + nkB) : (s2 < nkA);
-            if (mine) {
-                const int j0 = 32 * (half ? s2 - nkA : s2), jb = j0 + 8 * kg;
-                const uint32_t w4[4] = {cbf[s2].x, cbf[s2].y, cbf[s2].z, cbf[s2].w};
-                bf16x8 af;
-#pragma unroll
-                for (int v = 0; v < 8; ++v) {
-                    const int j = jb + v;
-                    const float cbv = __uint_as_float((v & 1) ? (w4[v >> 1] & 0xffff0000u)
-                                                              : (w4[v >> 1] << 16));
-                    const float m = cbv * __builtin_amdgcn_exp2f(ci2 - scum[j]) * sdt[j];
-                    af[v] = static_cast<bf16>(j <= i ? m : 0.0f);
-                }
-#pragma unroll
-                for (int pt = 0; pt < P / 16; ++pt) {
-                    const bf16x8 bf = mfma_frag_tr(xs, LDX, j0, 16 * pt, lane);
-                    acc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[pt], 0, 0, 0);
-                }
-            }
-        }
-
-        // state term
-        const float ei = __builtin_amdgcn_exp2f(ci2);
-#pragma unroll
-        for (int kk = 0; kk < N / 32; ++kk) {
-            const int n = 32 * kk + 8 * kg;
-            const uint32_t w4[4] = {cr[kk].x, cr[kk].y, cr[kk].z, cr[kk].w};
-            bf16x8 af;
-#pragma unroll
-            for (int v = 0; v < 8; ++v) {
-                const float cv = __uint_as_float((v & 1) ? (w4[v >> 1] & 0xffff0000u)
-                                                         : (w4[v >> 1] << 16));
-                af[v] = static_cast<bf16>(ei * cv);
-            }
-#pragma unroll
-            for (int pt = 0; pt < P / 16; ++pt) {
-                const bf16x8 bf = *reinterpret_cast<const bf16x8 *>(hs + (16 * pt + r16) * LDH + n);
-                acc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[pt], 0, 0, 0);
-            }
-        }
-
-        // epilogue: + D x into the wave's LDS tile, then 16-byte row stores
-#pragma unroll
-        for (int pt = 0; pt < P / 16; ++pt) {
-            const int p = 16 * pt + r16;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int il = 4 * kg + v;
-                const float xv = static_cast<float>(xs[(i0 + il) * LDX + p]);
-                yw[il * LDY + p] = static_cast<bf16>(acc[pt][v] + Dh * xv);
-            }
-        }
-        wave_lds_sync();
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int u = lane + 64 * k;      // 16 rows x 8 vectors
-            const int il = u >> 3, c8 = u & 7;
-            if (i0 + il < len)
-                st16(y + ((int64_t)(ci.start + i0 + il) * H + h) * P + 8 * c8,
-                     ld16(yw + il * LDY + 8 * c8));
-        }
-        wave_lds_sync();
-    }
+    // tile B first (larger); tile A's CB fragments are requested once B's are consumed
+    uint2 cal[kStepsA], cah[kStepsA];
+    scan_row_tile<Q, kStepsB, kStepsA>(16 * rtB, nkB, cbl, cbh, exact, len, lane, Cb, G, scum, sdt, xs, hs,
+                              yw, xsrc, H, Dh, y + ((int64_t)ci.start * H + h) * P, CBc, rtA, nkA,
+                              cal, cah, true);
+    scan_row_tile<Q, kStepsA, kStepsA>(16 * rtA, nkA, cal, cah, exact, len, lane, Cb, G, scum, sdt, xs, hs,
+                              yw, xsrc, H, Dh, y + ((int64_t)ci.start * H + h) * P, CBc, 0, 0,
+                              cal, cah, false);
 }
 
 // ===========================================================================
@@ -802,12 +911,14 @@ static inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream
 
 static inline bool use_fast(const PrefillDims &d) { return d.in_bf16 && d.P == 64 && d.N == 128; }
 
-// Raise a kernel's dynamic LDS limit once (idempotent; only needed above 64 KiB).
-static void allow_lds(const void *fn, size_t bytes, bool &done)
+// Raise a kernel's dynamic LDS limit to what a launch needs (only needed above
+// 64 KiB; the limit must leave room for the kernel's static LDS).
+static void allow_lds(const void *fn, size_t bytes, size_t &raised_to)
 {
-    if (bytes > 65536 && !done) {
-        done = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) ==
-               hipSuccess;
+    if (bytes > 65536 && bytes > raised_to) {
+        if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) ==
+            hipSuccess)
+            raised_to = bytes;
     }
 }
 
@@ -862,12 +973,43 @@ static void launch_scan_t(const PrefillDims &d, const void *x, const void *C, co
 {
     dim3 grid(d.H, d.max_chunks);
     const size_t smem = scan_smem<TIn, P, N>(d.Q);
-    static bool raised = false;
+    static size_t raised = 0;
     allow_lds(reinterpret_cast<const void *>(&chunk_scan_kernel<TIn, P, N>), smem, raised);
     hipLaunchKernelGGL((chunk_scan_kernel<TIn, P, N>), grid, dim3(256), smem, st, d.S, d.H, d.G,
                        d.Q, d.max_chunks, static_cast<const TIn *>(x), static_cast<const TIn *>(C),
                        D, meta, cum, dtc, static_cast<const TIn *>(CB),
                        static_cast<const TIn *>(entering), static_cast<TIn *>(y));
+}
+
+template <int Q>
+static void launch_state_fast(const PrefillDims &d, const void *x, const void *B,
+                              const int32_t *meta, const float *cum, const float *dtc,
+                              float *states, hipStream_t st)
+{
+    const size_t smem = (size_t)Q * (2 * kFastLD * sizeof(bf16) + sizeof(float));
+    static size_t raised = 0;
+    allow_lds(reinterpret_cast<const void *>(&chunk_state_fast_kernel<Q>), smem, raised);
+    const unsigned nblk = (unsigned)((int64_t)d.max_chunks * 2 * d.H);
+    hipLaunchKernelGGL(chunk_state_fast_kernel<Q>, dim3(nblk), dim3(256), smem, st, d.S, d.H, d.G,
+                       d.max_chunks, static_cast<const bf16 *>(x), static_cast<const bf16 *>(B),
+                       meta, cum, dtc, states);
+}
+
+template <int Q>
+static void launch_scan_fast(const PrefillDims &d, const void *x, const void *C, const float *D,
+                             const int32_t *meta, const float *cum, const float *dtc,
+                             const void *CB, const void *entering, void *y, hipStream_t st)
+{
+    const size_t smem = (size_t)Q * (kFastLD * sizeof(bf16) + 2 * sizeof(float)) +
+                        (size_t)64 * (128 + 8) * sizeof(bf16) +
+                        (size_t)(Q / 32) * 16 * (64 + 8) * sizeof(bf16);
+    static size_t raised = 0;
+    allow_lds(reinterpret_cast<const void *>(&chunk_scan_fast_kernel<Q>), smem, raised);
+    const unsigned nblk = (unsigned)((int64_t)d.max_chunks * d.H);
+    hipLaunchKernelGGL(chunk_scan_fast_kernel<Q>, dim3(nblk), dim3(2 * Q), smem, st, d.S, d.H, d.G,
+                       d.max_chunks, static_cast<const bf16 *>(x), static_cast<const bf16 *>(C), D,
+                       meta, cum, dtc, static_cast<const bf16 *>(CB),
+                       static_cast<const bf16 *>(entering), static_cast<bf16 *>(y));
 }
 
 #define SSD_DISPATCH_PN(d, FN, TIN, ...)                                 \
@@ -884,13 +1026,12 @@ void launch_chunk_state(const PrefillDims &d, const void *x, const void *B, cons
     if (d.max_chunks <= 0) return;
     hipStream_t st = as_stream(stream);
     if (use_fast(d)) {
-        const size_t smem = (size_t)d.Q * (2 * kFastLD * sizeof(bf16) + sizeof(float));
-        static bool raised = false;
-        allow_lds(reinterpret_cast<const void *>(&chunk_state_fast_kernel), smem, raised);
-        const unsigned nblk = (unsigned)((int64_t)d.max_chunks * 2 * d.H);
-        hipLaunchKernelGGL(chunk_state_fast_kernel, dim3(nblk), dim3(256), smem, st, d.S, d.H, d.G,
-                           d.Q, d.max_chunks, static_cast<const bf16 *>(x),
-                           static_cast<const bf16 *>(B), meta, cum, dtc, states);
+        switch (d.Q) {
+        case 32: launch_state_fast<32>(d, x, B, meta, cum, dtc, states, st); break;
+        case 64: launch_state_fast<64>(d, x, B, meta, cum, dtc, states, st); break;
+        case 128: launch_state_fast<128>(d, x, B, meta, cum, dtc, states, st); break;
+        default: launch_state_fast<256>(d, x, B, meta, cum, dtc, states, st); break;
+        }
         return;
     }
     if (d.in_bf16) SSD_DISPATCH_PN(d, launch_state_t, bf16, d, x, B, meta, cum, dtc, states, st);
@@ -946,17 +1087,12 @@ void launch_chunk_scan(const PrefillDims &d, const void *x, const void *C, const
     if (d.max_chunks <= 0) return;
     hipStream_t st = as_stream(stream);
     if (use_fast(d)) {
-        const size_t smem = (size_t)d.Q * (kFastLD * sizeof(bf16) + 2 * sizeof(float)) +
-                            (size_t)64 * (128 + 8) * sizeof(bf16) +
-                            (size_t)(d.Q / 32) * 16 * (64 + 8) * sizeof(bf16);
-        static bool raised = false;
-        allow_lds(reinterpret_cast<const void *>(&chunk_scan_fast_kernel), smem, raised);
-        const unsigned nblk = (unsigned)((int64_t)d.max_chunks * d.H);
-        hipLaunchKernelGGL(chunk_scan_fast_kernel, dim3(nblk), dim3(2 * d.Q), smem, st, d.S, d.H,
-                           d.G, d.Q, d.max_chunks, static_cast<const bf16 *>(x),
-                           static_cast<const bf16 *>(C), D, meta, cum, dtc,
-                           static_cast<const bf16 *>(CB), static_cast<const bf16 *>(entering),
-                           static_cast<bf16 *>(y));
+        switch (d.Q) {
+        case 32: launch_scan_fast<32>(d, x, C, D, meta, cum, dtc, CB, entering, y, st); break;
+        case 64: launch_scan_fast<64>(d, x, C, D, meta, cum, dtc, CB, entering, y, st); break;
+        case 128: launch_scan_fast<128>(d, x, C, D, meta, cum, dtc, CB, entering, y, st); break;
+        default: launch_scan_fast<256>(d, x, C, D, meta, cum, dtc, CB, entering, y, st); break;
+        }
         return;
     }
     if (d.in_bf16)
