@@ -177,8 +177,14 @@ int ssd_state_passing(const ssd_problem *p, const float *chunk_states, const flo
 
 /*
  * Step 4 - bmm (vLLM PR #61501, section "Details"): CB[c,g,i,j] = C_i . B_j
- * inside each chunk, float32 accumulation. B, C [T,G,N] in_dtype; CB out
- * [max_chunks,G,Q,Q] in in_dtype (chunk scan multiplies in that precision).
+ * inside each chunk, float32 accumulation. B, C [T,G,N] in_dtype; CB out:
+ * Q*Q elements per (chunk, group) at offset (c*G + g)*Q*Q, in in_dtype (chunk
+ * scan multiplies in that precision). Layout inside a (chunk, group) block:
+ *   float32 inputs: row-major, element (i, j) at i*Q + j;
+ *   bf16 inputs: MFMA fragment order - element (i, j) at
+ *     ((i/16 * Q/32 + j/32) * 64 + lane) * 8 + v, lane = i%16 + 16*kg,
+ *     where j%32 = 4*kg + v%4 + 16*(v/4) (one contiguous 1 KiB block per
+ *     16-row x 32-column operand tile).
  * Defined for j <= i < chunk length (the causal part chunk scan reads); other
  * entries are unspecified.
  */

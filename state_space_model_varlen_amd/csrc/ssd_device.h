@@ -191,6 +191,18 @@ __device__ __forceinline__ bf16x8 mfma_frag_tr_split(const bf16 *tile, int ld, i
 }
 
 // ---------------------------------------------------------------------------
+// CB in MFMA fragment order (bf16 inputs). For row tile rt = i / 16 and K block
+// ks = j / 32 of a chunk, the 16 x 32 A fragment of the intra-chunk product is
+// stored as 64 lanes x 8 bf16 (one contiguous 1 KiB wave load): lane
+// i % 16 + 16 kg, element v, in the split K order j % 32 = 4 kg + v % 4 + 16 (v / 4).
+__host__ __device__ __forceinline__ int64_t cb_frag_offset(int Q, int i, int j) {
+    const int rt = i >> 4, ks = j >> 5, jl = j & 31;
+    const int kg = (jl & 15) >> 2, v = (jl & 3) + ((jl >> 4) << 2);
+    const int lane = (i & 15) + 16 * kg;
+    return (((int64_t)rt * (Q >> 5) + ks) * 64 + lane) * 8 + v;
+}
+
+// ---------------------------------------------------------------------------
 // XCD-aware block order. Workgroups are dispatched round-robin over the 8 XCDs
 // (each with its own L2); this maps the hardware block id to a logical id so
 // that each XCD works on one contiguous range of logical ids, which keeps

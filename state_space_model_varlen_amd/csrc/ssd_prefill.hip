@@ -335,8 +335,9 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
 // CB^T = B . C^T (A operand: B rows, B operand: C rows - both load straight
 // from HBM because d_state is their contiguous index), so that each lane ends
 // up holding 4 consecutive columns of one CB row and stores them at once.
-// CB is stored in the input dtype: chunk scan rounds its masked product to
-// that dtype for the MFMA in any case.
+// CB is stored in the input dtype (chunk scan rounds its masked product to
+// that dtype for the MFMA in any case): row-major for float32 inputs, MFMA
+// fragment order (cb_frag_offset) for bf16 inputs.
 template <typename TIn, int N>
 __global__ __launch_bounds__(256) void bmm_kernel(int S, int G, int Q, int max_chunks,
                                                   const TIn *__restrict__ B,
@@ -361,7 +362,7 @@ __global__ __launch_bounds__(256) void bmm_kernel(int S, int G, int Q, int max_c
         cf[kk] = (i < ci.len && n < N) ? M::load(C + ((int64_t)(ci.start + i) * G + g) * N + n)
                                        : M::zero();
     }
-    TIn *row = CB + ((int64_t)c * G + g) * Q * Q + (int64_t)i * Q;
+    TIn *cbc = CB + ((int64_t)c * G + g) * Q * Q;
     for (int jt = wave; jt <= i0 / 16; jt += 4) {
         const int j = jt * 16 + r16;
         typename M::frag bfr[NK];  // B rows j (A operand)
@@ -374,9 +375,13 @@ __global__ __launch_bounds__(256) void bmm_kernel(int S, int G, int Q, int max_c
         f32x4 acc = zero4();
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) acc = M::run(bfr[kk], cf[kk], acc);
-        // lane holds CB^T[16 jt + 4 kg + v][i] = CB[i][16 jt + 4 kg + v], v = 0..3
+        // lane holds CB^T[16 jt + 4 kg + v][i] = CB[i][16 jt + 4 kg + v], v = 0..3:
+        // 4 consecutive elements in either layout (row-major for float32 inputs,
+        // MFMA fragment order for bf16 inputs)
         float v4[4] = {acc[0], acc[1], acc[2], acc[3]};
-        store4<TIn>(row + jt * 16 + 4 * kg, v4);
+        const int jc = jt * 16 + 4 * kg;
+        if constexpr (sizeof(TIn) == 2) store4<TIn>(cbc + cb_frag_offset(Q, i, jc), v4);
+        else store4<TIn>(cbc + (int64_t)i * Q + jc, v4);
     }
 }
 
@@ -458,20 +463,32 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
             typename M::frag af;
             float cbv[Vec16<TIn>::kElems > KPL ? Vec16<TIn>::kElems : KPL];
             if constexpr (KPL == 8) {
-                Vec16<TIn>::load(CBc + (int64_t)i * Q + jb, cbv);
+                // fragment order: the 8 values are j = j0 + 4 kg + v % 4 + 16 (v / 4)
+                Vec16<TIn>::load(CBc + cb_frag_offset(Q, i, j0 + 4 * kg), cbv);
             } else {
 #pragma unroll
                 for (int v = 0; v < KPL; ++v) cbv[v] = to_f32(CBc[(int64_t)i * Q + jb + v]);
             }
 #pragma unroll
             for (int v = 0; v < KPL; ++v) {
-                const int j = jb + v;
+                const int j = KPL == 8 ? j0 + 4 * kg + (v & 3) + ((v >> 2) << 4) : jb + v;
                 const float m = (j <= i) ? cbv[v] * __expf(cum_i - scum[j]) * sdt[j] : 0.0f;
                 M::set(af, v, m);
             }
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
-                const typename M::frag bf = M::load(&xs[(pt * 16 + r16) * LDX + jb]);
+                typename M::frag bf;
+                if constexpr (KPL == 8) {     // split K order, as the CB fragment
+                    const TIn *xp = &xs[(pt * 16 + r16) * LDX + j0 + 4 * kg];
+                    typedef short v4s __attribute__((ext_vector_type(4)));
+                    const v4s lo = *reinterpret_cast<const v4s *>(xp);
+                    const v4s hi = *reinterpret_cast<const v4s *>(xp + 16);
+                    typedef short v8s __attribute__((ext_vector_type(8)));
+                    const v8s both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    bf = __builtin_bit_cast(typename M::frag, both);
+                } else {
+                    bf = M::load(&xs[(pt * 16 + r16) * LDX + jb]);
+                }
                 acc[pt] = M::run(af, bf, acc[pt]);
             }
         }
@@ -639,8 +656,8 @@ __global__ __launch_bounds__(256) void chunk_state_fast_kernel(
 //   acc  = sum_j A_ij x'_j,   A_ij = CB[i,j] exp(cum_i - R_k) [j <= i]    (MFMA)
 //   acc += (exp(cum_i) C_i) . H_in^T                                        (MFMA)
 //   y_i  = acc + D_h x_i
-// CB fragments (two 8-byte pieces per lane per K step, split K order) are all
-// requested before the staging barrier; y leaves through a per-wave LDS tile
+// CB fragments (one contiguous 1 KiB wave load per K step) are requested
+// before the staging barrier; y leaves through a per-wave LDS tile
 // as 16-byte row stores.
 constexpr float kMaxSpan = 60.0f;    // natural-log units
 
@@ -653,18 +670,15 @@ __device__ __forceinline__ void wave_lds_sync() {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// CB fragments of one row tile: row i, K steps 0 .. nk-1, split K order
-// (columns 32 ks + 4 kg + 0..3 and 32 ks + 16 + 4 kg + 0..3).
+// CB fragments of one row tile (MFMA fragment order, cb_frag_offset): K steps
+// 0 .. nk-1, one contiguous 1 KiB wave load each.
 template <int K>
-__device__ __forceinline__ void load_cb_frags(const bf16 *CBc, int Q, int i, int kg, int nk,
-                                              uint2 *lo, uint2 *hi)
+__device__ __forceinline__ void load_cb_frags(const bf16 *CBc, int Q, int rt, int lane, int nk,
+                                              uint4 *f)
 {
+    const bf16 *base = CBc + ((int64_t)rt * (Q >> 5) * 64 + lane) * 8;
 #pragma unroll
-    for (int ks = 0; ks < K; ++ks) {
-        const bf16 *src = CBc + (int64_t)i * Q + 32 * ks + 4 * kg;
-        lo[ks] = ks < nk ? *reinterpret_cast<const uint2 *>(src) : make_uint2(0u, 0u);
-        hi[ks] = ks < nk ? *reinterpret_cast<const uint2 *>(src + 16) : make_uint2(0u, 0u);
-    }
+    for (int ks = 0; ks < K; ++ks) f[ks] = ks < nk ? ld16(base + (int64_t)ks * 512) : zero16();
 }
 
 // One 16-row tile of the chunk scan (rows i0 .. i0 + 15) for one wave; see the
@@ -672,14 +686,14 @@ __device__ __forceinline__ void load_cb_frags(const bf16 *CBc, int Q, int i, int
 // (row tile nrt, nnk steps) are requested after this tile's intra-chunk loop.
 template <int Q, int K, int KN>
 __device__ __forceinline__ void scan_row_tile(
-    int i0, int nk, const uint2 *cbl, const uint2 *cbh, bool exact, int len, int lane,
+    int i0, int nk, const uint4 *cbf, bool exact, int len, int lane,
     const bf16 *Cb, int G, const float *scum, const float *sdt, const bf16 *xs, const bf16 *hs,
     bf16 *yw, const bf16 *xsrc, int H, float Dh, bf16 *yout, const bf16 *CBc, int nrt, int nnk,
-    uint2 *ncl, uint2 *nch, bool prefetch_next)
+    uint4 *ncf, bool prefetch_next)
 {
     constexpr int P = 64, N = 128, LDX = kFastLD, LDH = N + 8, LDY = P + 8;
     if (nk == 0) {
-        if (prefetch_next) load_cb_frags<KN>(CBc, Q, 16 * nrt + (lane & 15), lane >> 4, nnk, ncl, nch);
+        if (prefetch_next) load_cb_frags<KN>(CBc, Q, nrt, lane, nnk, ncf);
         return;
     }
     const int r16 = lane & 15, kg = lane >> 4;
@@ -705,9 +719,9 @@ __device__ __forceinline__ void scan_row_tile(
     for (int ks = 0; ks < K; ++ks) {
         if (ks < nk) {
             const int j0 = 32 * ks;
-            const float cbv[8] = {bf16_lo(cbl[ks].x), bf16_hi(cbl[ks].x), bf16_lo(cbl[ks].y),
-                                  bf16_hi(cbl[ks].y), bf16_lo(cbh[ks].x), bf16_hi(cbh[ks].x),
-                                  bf16_lo(cbh[ks].y), bf16_hi(cbh[ks].y)};
+            const float cbv[8] = {bf16_lo(cbf[ks].x), bf16_hi(cbf[ks].x), bf16_lo(cbf[ks].y),
+                                  bf16_hi(cbf[ks].y), bf16_lo(cbf[ks].z), bf16_hi(cbf[ks].z),
+                                  bf16_lo(cbf[ks].w), bf16_hi(cbf[ks].w)};
             bf16x8 af;
             if (!exact) {
                 const float e = __builtin_amdgcn_exp2f(ci2 - scum[j0 + 31 < Q ? j0 + 31 : Q - 1]);
@@ -736,7 +750,7 @@ __device__ __forceinline__ void scan_row_tile(
             }
         }
     }
-    if (prefetch_next) load_cb_frags<KN>(CBc, Q, 16 * nrt + r16, kg, nnk, ncl, nch);
+    if (prefetch_next) load_cb_frags<KN>(CBc, Q, nrt, lane, nnk, ncf);
 
     // state term: acc2 = C . H_in^T on raw C, then each output row i gets
     // exp(cum_i) * acc2 (the lane's rows are i0 + 4 kg + v)
@@ -857,8 +871,8 @@ void chunk_scan_fast_kernel(
     // CB fragments (split K order) of the larger row tile B, requested now so
     // that they arrive during the staging barriers; tile A's follow later
     const bf16 *CBc = CB + ((int64_t)c * G + g) * Q * Q;
-    uint2 cbl[kStepsB], cbh[kStepsB];
-    load_cb_frags<kStepsB>(CBc, Q, 16 * rtB + r16, kg, nkB, cbl, cbh);
+    uint4 cbf[kStepsB];
+    load_cb_frags<kStepsB>(CBc, Q, rtB, lane, nkB, cbf);
     __syncthreads();
     // scaling factors of x: G_j = exp(R_k - cum_j) dt_j; exact mode when a span is too large
     bool big = false;
@@ -896,13 +910,14 @@ void chunk_scan_fast_kernel(
     bf16 *yw = ys + wave * 16 * LDY;
 
     // tile B first (larger); tile A's CB fragments are requested once B's are consumed
-    uint2 cal[kStepsA], cah[kStepsA];
-    scan_row_tile<Q, kStepsB, kStepsA>(16 * rtB, nkB, cbl, cbh, exact, len, lane, Cb, G, scum, sdt, xs, hs,
-                              yw, xsrc, H, Dh, y + ((int64_t)ci.start * H + h) * P, CBc, rtA, nkA,
-                              cal, cah, true);
-    scan_row_tile<Q, kStepsA, kStepsA>(16 * rtA, nkA, cal, cah, exact, len, lane, Cb, G, scum, sdt, xs, hs,
-                              yw, xsrc, H, Dh, y + ((int64_t)ci.start * H + h) * P, CBc, 0, 0,
-                              cal, cah, false);
+    uint4 caf[kStepsA];
+    scan_row_tile<Q, kStepsB, kStepsA>(16 * rtB, nkB, cbf, exact, len, lane, Cb, G, scum, sdt,
+                                       xs, hs, yw, xsrc, H, Dh,
+                                       y + ((int64_t)ci.start * H + h) * P, CBc, rtA, nkA, caf,
+                                       true);
+    scan_row_tile<Q, kStepsA, kStepsA>(16 * rtA, nkA, caf, exact, len, lane, Cb, G, scum, sdt,
+                                       xs, hs, yw, xsrc, H, Dh,
+                                       y + ((int64_t)ci.start * H + h) * P, CBc, 0, 0, caf, false);
 }
 
 // ===========================================================================

@@ -106,3 +106,19 @@ def gpu_prefill(inp, cache, chunk_size, checkpoints=False, D=True, has_initial="
                             ssd.alloc_workspace(p, DEV))
     torch.cuda.synchronize()
     return y.cpu(), g_cache.cpu(), None if ck is None else ck.cpu()
+
+
+def cb_fragment_to_dense(cb: np.ndarray, Q: int) -> np.ndarray:
+    """CB of bf16 problems is stored in MFMA fragment order (include/ssd_mi355x.h,
+    ssd_bmm_chunk): for row tile i // 16 and K block j // 32 a 1 KiB block of 64
+    lanes x 8 values, lane = i % 16 + 16 kg, value v, with j % 32 = 4 kg + v % 4
+    + 16 (v // 4). Returns the [..., Q, Q] row-major matrix."""
+    i = np.arange(Q)[:, None]
+    j = np.arange(Q)[None, :]
+    jl = j % 32
+    kg = (jl % 16) // 4
+    v = jl % 4 + 4 * (jl // 16)
+    lane = i % 16 + 16 * kg
+    off = (((i // 16) * (Q // 32) + j // 32) * 64 + lane) * 8 + v
+    flat = cb.reshape(cb.shape[:-2] + (Q * Q,))
+    return flat[..., off]

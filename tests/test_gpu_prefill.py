@@ -11,8 +11,8 @@ import torch
 
 import oracle
 import ssd_synth as sy
-from gpu_helpers import (DEV, assert_close, gpu_prefill, looser, prefix_final_states,
-                         select_heads, to64, tol)
+from gpu_helpers import (DEV, assert_close, cb_fragment_to_dense, gpu_prefill, looser,
+                         prefix_final_states, select_heads, to64, tol)
 from oracle import chunked
 
 pytestmark = pytest.mark.gpu
@@ -111,6 +111,8 @@ def test_steps_match_chunked_oracle(case):
     # 4. bmm: causal part inside each chunk; fp32 accumulation, stored in the input
     # dtype (bf16 rounding: relative 2^-8 bound per element)
     gcb = to64(buf["CB"][:nc])
+    if ti == BF16:
+        gcb = cb_fragment_to_dense(gcb, Q)
     for c in range(nc):
         ln = int(meta["len"][c])
         low = np.tril(np.ones((ln, ln), dtype=bool))
