@@ -1,8 +1,8 @@
 #!/usr/bin/env python3
 """Throughput of the MI355X SSD varlen prefill scan (and the MTP state update).
 
-One step = one ssd_combined_varlen call (chunk cumsum, bmm, chunk state,
-state passing, chunk scan) over the single-sequence Mamba2 layer prefill:
+One step = one ssd_combined_varlen call (chunk cumsum, bmm, chunk state with
+state passing in one kernel, chunk scan) over the single-sequence Mamba2 layer prefill:
 L = 4096 tokens, 80 heads, headdim 64, d_state 128, 1 group, chunk 256, bf16
 x/B/C/dt, fp32 A/D/state. Inputs are seeded synthetic draws, resident in HBM
 before the timed region. `value` = tokens / s of that call (one layer).
@@ -60,6 +60,11 @@ def prefill_bytes(T, S, H, P, N, G, Q, nc, ex, es, s_init, checkpoints):
         "chunk_state": T * H * P * ex + T * G * N * ex + per_chunk + st,
         "state_passing": st + ent + (s_init + S) * H * P * N * es
                          + (nc * H * P * N * es if checkpoints else 0),
+        # fused chunk state + state passing: x and B in, entering states out; the
+        # chunk states stay on chip
+        "chunk_state_passing": T * H * P * ex + T * G * N * ex + per_chunk + ent
+                               + (s_init + S) * H * P * N * es
+                               + (nc * H * P * N * es if checkpoints else 0),
         "chunk_scan": 2 * T * H * P * ex + T * G * N * ex + per_chunk + cb + ent,
     }
 
@@ -141,11 +146,10 @@ def main():
         "chunk_cumsum": lambda: ssd.ssd_chunk_cumsum(p, dt, A, cu, buf["chunk_meta"],
                                                      buf["dA_cumsum"], buf["dt_chunk"], stream),
         "bmm_chunk": lambda: ssd.ssd_bmm_chunk(p, B, C, buf["chunk_meta"], buf["CB"], stream),
-        "chunk_state": lambda: ssd.ssd_chunk_state(p, x, B, buf["chunk_meta"], buf["dA_cumsum"],
-                                                   buf["dt_chunk"], buf["chunk_states"], stream),
-        "state_passing": lambda: ssd.ssd_state_passing(p, buf["chunk_states"], buf["dA_cumsum"],
-                                                       buf["chunk_meta"], cache, idx, None,
-                                                       buf["entering"], None, stream),
+        # what ssd_combined_varlen runs for bf16 inputs with headdim 64, d_state 128
+        "chunk_state_passing": lambda: ssd.ssd_chunk_state_passing(
+            p, x, B, buf["chunk_meta"], buf["dA_cumsum"], buf["dt_chunk"], cache, idx, None,
+            buf["entering"], None, stream),
         "chunk_scan": lambda: ssd.ssd_chunk_scan(p, x, C, D, buf["chunk_meta"], buf["dA_cumsum"],
                                                  buf["dt_chunk"], buf["CB"], buf["entering"], y,
                                                  stream),

@@ -176,6 +176,25 @@ int ssd_state_passing(const ssd_problem *p, const float *chunk_states, const flo
                       void *entering_states, void *checkpoints, void *stream);
 
 /*
+ * Steps 2 and 3 in one launch (same pages and sections as steps 2 and 3):
+ * the chunk states are folded into the running state as they are produced
+ * and never stored, so no chunk_states buffer exists. Outputs and cache
+ * semantics are exactly those of ssd_state_passing (entering_states in
+ * in_dtype, checkpoints and the final state in state_dtype, zero-length
+ * sequences write their initial state or zeros back). Only bf16 inputs with
+ * headdim 64 and d_state 128 are supported (SSD_ERR_UNSUPPORTED otherwise);
+ * ssd_combined_varlen uses it for exactly those shapes.
+ *   x [T,H,P], B [T,G,N] bf16; chunk_meta, dA_cumsum, dt_chunk from step 1;
+ *   state_cache, state_indices, has_initial_state, entering_states,
+ *   checkpoints as for ssd_state_passing.
+ */
+int ssd_chunk_state_passing(const ssd_problem *p, const void *x, const void *B,
+                            const int32_t *chunk_meta, const float *dA_cumsum,
+                            const float *dt_chunk, void *state_cache,
+                            const int32_t *state_indices, const uint8_t *has_initial_state,
+                            void *entering_states, void *checkpoints, void *stream);
+
+/*
  * Step 4 - bmm (vLLM PR #61501, section "Details"): CB[c,g,i,j] = C_i . B_j
  * inside each chunk, float32 accumulation. B, C [T,G,N] in_dtype; CB out:
  * Q*Q elements per (chunk, group) at offset (c*G + g)*Q*Q, in in_dtype (chunk
@@ -209,6 +228,8 @@ int ssd_chunk_scan(const ssd_problem *p, const void *x, const void *C, const flo
  * sections "Details" and "Claims"; vLLM PR #62922, section "Details").
  * Semantics are those of the five steps composed: every initial state is
  * read as it was before the call even though the call overwrites the slot.
+ * For bf16 inputs with headdim 64 and d_state 128, steps 2 and 3 run as
+ * ssd_chunk_state_passing (and the workspace holds no chunk states).
  *   workspace        device buffer of at least ssd_workspace_bytes(p) bytes,
  *                    256-byte aligned; its contents on entry do not matter
  *   checkpoints      [max_chunks,H,P,N] state_dtype or NULL

@@ -62,6 +62,7 @@ _SIGS = {
     "ssd_chunk_cumsum": ([_pp] + [_vp] * 7, ctypes.c_int),
     "ssd_chunk_state": ([_pp] + [_vp] * 7, ctypes.c_int),
     "ssd_state_passing": ([_pp] + [_vp] * 9, ctypes.c_int),
+    "ssd_chunk_state_passing": ([_pp] + [_vp] * 11, ctypes.c_int),
     "ssd_bmm_chunk": ([_pp] + [_vp] * 5, ctypes.c_int),
     "ssd_chunk_scan": ([_pp] + [_vp] * 10, ctypes.c_int),
     "ssd_combined_varlen": ([_pp] + [_vp] * 13 + [ctypes.c_size_t, _vp], ctypes.c_int),
@@ -204,6 +205,24 @@ def ssd_state_passing(p: ssd_problem, chunk_states, dA_cumsum, chunk_meta, state
         _ptr(entering_states, "entering_states", _TORCH[p.in_dtype], (mc, H, P, N)),
         _ptr(checkpoints, "checkpoints", ts, (mc, H, P, N), optional=True), _stream(stream))
     _check("ssd_state_passing", rc)
+
+
+def ssd_chunk_state_passing(p: ssd_problem, x, B, chunk_meta, dA_cumsum, dt_chunk,
+                            state_cache, state_indices, has_initial_state, entering_states,
+                            checkpoints=None, stream=None):
+    T, S, H, P, N, G, Q, mc = _dims(p)
+    ti, ts = _TORCH[p.in_dtype], _TORCH[p.state_dtype]
+    rc = _lib.ssd_chunk_state_passing(
+        ctypes.byref(p), _ptr(x, "x", ti, (T, H, P)), _ptr(B, "B", ti, (T, G, N)),
+        _ptr(chunk_meta, "chunk_meta", torch.int32, (chunk_meta_count(p),)),
+        _ptr(dA_cumsum, "dA_cumsum", torch.float32, (H, mc, Q)),
+        _ptr(dt_chunk, "dt_chunk", torch.float32, (H, mc, Q)),
+        _ptr(state_cache, "state_cache", ts, (p.num_slots, H, P, N)),
+        _ptr(state_indices, "state_indices", torch.int32, (S,)),
+        _ptr(has_initial_state, "has_initial_state", torch.uint8, (S,), optional=True),
+        _ptr(entering_states, "entering_states", ti, (mc, H, P, N)),
+        _ptr(checkpoints, "checkpoints", ts, (mc, H, P, N), optional=True), _stream(stream))
+    _check("ssd_chunk_state_passing", rc)
 
 
 def ssd_bmm_chunk(p: ssd_problem, B, C, chunk_meta, CB, stream=None):

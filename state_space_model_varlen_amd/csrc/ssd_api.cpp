@@ -108,7 +108,9 @@ Workspace workspace_layout(const ssd_problem *p)
     w.cb = w.dt + round_up(sizeof(float) * H * mc * Q);
     const size_t ein = p->in_dtype == SSD_BF16 ? 2 : 4;
     w.states = w.cb + round_up(ein * mc * G * Q * Q);
-    w.entering = w.states + round_up(sizeof(float) * mc * H * P * N);
+    // the fused state kernel keeps chunk states in registers: no buffer for them
+    const size_t nstates = ssd::fused_state_path(dims_of(p)) ? 0 : mc * H * P * N;
+    w.entering = w.states + round_up(sizeof(float) * nstates);
     w.total = w.entering + round_up(ein * mc * H * P * N);
     return w;
 }
@@ -195,6 +197,27 @@ int ssd_state_passing(const ssd_problem *p, const float *chunk_states, const flo
     return launch_status();
 }
 
+int ssd_chunk_state_passing(const ssd_problem *p, const void *x, const void *B,
+                            const int32_t *chunk_meta, const float *dA_cumsum,
+                            const float *dt_chunk, void *state_cache,
+                            const int32_t *state_indices, const uint8_t *has_initial_state,
+                            void *entering_states, void *checkpoints, void *stream)
+{
+    int rc = check_problem(p);
+    if (rc) return rc;
+    const ssd::PrefillDims d = dims_of(p);
+    if (!ssd::fused_state_path(d)) return SSD_ERR_UNSUPPORTED;
+    if (!x || !B || !chunk_meta || !dA_cumsum || !dt_chunk || !state_cache || !state_indices ||
+        !entering_states)
+        return SSD_ERR_NULL;
+    if (!aligned16(x) || !aligned16(B) || !aligned16(state_cache) ||
+        !aligned16(entering_states) || !aligned16(checkpoints))
+        return SSD_ERR_ALIGN;
+    ssd::launch_state_scan(d, x, B, chunk_meta, dA_cumsum, dt_chunk, state_cache, state_indices,
+                           has_initial_state, entering_states, checkpoints, stream);
+    return launch_status();
+}
+
 int ssd_bmm_chunk(const ssd_problem *p, const void *B, const void *C,
                   const int32_t *chunk_meta, void *CB, void *stream)
 {
@@ -251,9 +274,14 @@ int ssd_combined_varlen(const ssd_problem *p, const void *x, const void *dt, con
 
     ssd::launch_chunk_cumsum(d, dt, A, cu_seqlens, meta, cum, dtc, stream);
     ssd::launch_bmm(d, B, C, meta, cb, stream);
-    ssd::launch_chunk_state(d, x, B, meta, cum, dtc, states, stream);
-    ssd::launch_state_passing(d, states, cum, meta, state_cache, state_indices, has_initial_state,
-                              entering, checkpoints, stream);
+    if (ssd::fused_state_path(d)) {
+        ssd::launch_state_scan(d, x, B, meta, cum, dtc, state_cache, state_indices,
+                               has_initial_state, entering, checkpoints, stream);
+    } else {
+        ssd::launch_chunk_state(d, x, B, meta, cum, dtc, states, stream);
+        ssd::launch_state_passing(d, states, cum, meta, state_cache, state_indices,
+                                  has_initial_state, entering, checkpoints, stream);
+    }
     ssd::launch_chunk_scan(d, x, C, D, meta, cum, dtc, cb, entering, y, stream);
     return launch_status();
 }

@@ -191,6 +191,39 @@ __device__ __forceinline__ bf16x8 mfma_frag_tr_split(const bf16 *tile, int ld, i
 }
 
 // ---------------------------------------------------------------------------
+// M consecutive elements (M a multiple of 8 for bf16, of 4 for float) as
+// 16-byte vector loads / stores, widened to / narrowed from float.
+template <typename T, int M> __device__ __forceinline__ void load_run(const T *p, float *v) {
+    constexpr int E = Vec16<T>::kElems;
+    static_assert(M % E == 0, "whole 16-byte vectors only");
+#pragma unroll
+    for (int i = 0; i < M / E; ++i) Vec16<T>::load(p + E * i, v + E * i);
+}
+template <typename T, int M> __device__ __forceinline__ void store_run(T *p, const float *v) {
+    constexpr int E = Vec16<T>::kElems;
+    static_assert(M % E == 0, "whole 16-byte vectors only");
+#pragma unroll
+    for (int i = 0; i < M / E; ++i) Vec16<T>::store(p + E * i, v + E * i);
+}
+
+// ---------------------------------------------------------------------------
+// Raw buffer loads (gfx9 buffer resource: base address, no stride, a size in
+// bytes, dword 3 = 0x00020000). A load at a byte offset at or past the size
+// returns zeros and touches no memory: the prefill kernels give each chunk's
+// tile a resource ending at the chunk's last row, so rows past the end come
+// back as zeros with no branch and no clamped address.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_ld16(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ float buf_ldf(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
+// ---------------------------------------------------------------------------
 // CB in MFMA fragment order (bf16 inputs). For row tile rt = i / 16 and K block
 // ks = j / 32 of a chunk, the 16 x 32 A fragment of the intra-chunk product is
 // stored as 64 lanes x 8 bf16 (one contiguous 1 KiB wave load): lane

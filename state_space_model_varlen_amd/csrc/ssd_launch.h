@@ -30,6 +30,13 @@ void launch_chunk_state(const PrefillDims &d, const void *x, const void *B, cons
 void launch_state_passing(const PrefillDims &d, const float *states, const float *cum,
                           const int32_t *meta, void *cache, const int32_t *idx,
                           const uint8_t *has_init, void *entering, void *ckpt, void *stream);
+// Chunk state and state passing in one launch (bf16 inputs, headdim 64,
+// d_state 128 only: fused_state_path()); writes what state passing writes and
+// needs no chunk-state buffer.
+bool fused_state_path(const PrefillDims &d);
+void launch_state_scan(const PrefillDims &d, const void *x, const void *B, const int32_t *meta,
+                       const float *cum, const float *dtc, void *cache, const int32_t *idx,
+                       const uint8_t *has_init, void *entering, void *ckpt, void *stream);
 void launch_bmm(const PrefillDims &d, const void *B, const void *C, const int32_t *meta, void *CB,
                 void *stream);
 void launch_chunk_scan(const PrefillDims &d, const void *x, const void *C, const float *D,

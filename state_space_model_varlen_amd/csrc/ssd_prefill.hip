@@ -639,6 +639,202 @@ __global__ __launch_bounds__(256) void chunk_state_fast_kernel(
             out[(16 * wave + 4 * kg + v) * N + 16 * ct + r16] = acc[ct][v];
 }
 
+// Chunk state and state passing in one pass, bf16, P = 64, N = 128 (used by
+// the combined call). One block of 512 threads per (sequence, head, half of
+// the state columns), walking the sequence's chunks in order; the running
+// state H lives in the MFMA accumulators (wave w owns rows 16 (w % 4) .. + 15
+// and columns 32 (w / 4) .. + 31 of the half, as two 16 x 16 tiles):
+//   entering[c] = H;   H <- exp(cum_last) H + sum_t x_t (w_t B_t)^T,
+//   w_t = exp(cum_last - cum_t) dt_t,
+// and checkpoints / the final state are written from the same registers, so
+// chunk states never go to memory. The tiles of the next DEPTH chunks are in
+// flight to registers (buffer loads that return zeros past the chunk's end)
+// while chunk c is contracted; x is staged as loaded, B scaled by w_t.
+constexpr int kScanLDX = 80;   // x row pitch in LDS (bf16): conflict-free transpose reads
+constexpr int kScanNSL = 64;   // state columns per block
+constexpr int kScanLDB = kScanNSL + 16;
+
+template <int Q> struct StateScanRegs {
+    static constexpr int kXV = (Q * 8 + 511) / 512;    // x vectors (8 bf16) per thread
+    static constexpr int kBV = (Q * 8 + 511) / 512;    // B vectors per thread (8 per row)
+    uint4 x[kXV], b[kBV];
+    float cm[kBV], dt[kBV];                            // cum and dt of the B rows
+    float cl;                                          // cum at the chunk's last token
+};
+
+template <int Q, int DEPTH, bool CKPT, typename TS>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
+void state_scan_fast_kernel(
+    int S, int H, int G, int max_chunks, int num_slots, const bf16 *__restrict__ x,
+    const bf16 *__restrict__ B, const int32_t *__restrict__ meta, const float *__restrict__ cum,
+    const float *__restrict__ dtc, TS *cache, const int32_t *__restrict__ idx,
+    const uint8_t *__restrict__ has_init, bf16 *__restrict__ entering, TS *__restrict__ ckpt)
+{
+    constexpr int P = 64, N = 128, NSL = kScanNSL, NS = N / NSL;
+    constexpr int LDX = kScanLDX, LDB = kScanLDB;
+    typedef StateScanRegs<Q> Regs;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    bf16 *xs = reinterpret_cast<bf16 *>(smem);   // [Q][LDX]  x_t
+    bf16 *bs = xs + Q * LDX;                     // [Q][LDB]  w_t B_t (slice columns)
+
+    const int nblk = S * H * NS;
+    const int lb = xcd_logical_block(blockIdx.x, nblk);
+    const int q = lb % NS, h = (lb / NS) % H, s = lb / (NS * H);
+    const int g = h / (H / G);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int pw = wave & 3, nh = wave >> 2;
+    const int n0 = q * NSL;
+    const int PN = P * N;
+    // this lane's state elements: row 16 pw + r16, columns n0 + 32 nh + 16 j + 4 kg + 0..3
+    const int64_t run = (int64_t)(16 * pw + r16) * N + n0 + 32 * nh + 4 * kg;
+
+    int c0 = meta[s], c1 = meta[s + 1];
+    c0 = c0 < max_chunks ? c0 : max_chunks;
+    c1 = c1 < max_chunks ? c1 : max_chunks;
+    const int slot = idx[s];
+    const bool slot_ok = slot >= 0 && slot < num_slots;
+    const bool read_init = slot_ok && (has_init != nullptr && has_init[s] != 0);
+    TS *cslot = cache + ((int64_t)(slot_ok ? slot : 0) * H + h) * PN + run;
+
+    f32x4 acc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (read_init) load4<TS>(cslot + 16 * j, v);
+        acc[j][0] = v[0]; acc[j][1] = v[1]; acc[j][2] = v[2]; acc[j][3] = v[3];
+    }
+
+    // token range of the sequence: chunk c starts at first + (c - c0) Q
+    int first = 0, end = 0;
+    if (c0 < c1) {
+        first = chunk_info(meta, S, c0).start;
+        const ChunkInfo la = chunk_info(meta, S, c1 - 1);
+        end = la.start + la.len;
+    }
+    // byte offsets inside a chunk's tiles (the same for every chunk)
+    const uint32_t xrow = (uint32_t)H * P * 2, brow = (uint32_t)G * N * 2;
+    uint32_t xo[Regs::kXV], bo[Regs::kBV], to[Regs::kBV];
+#pragma unroll
+    for (int k = 0; k < Regs::kXV; ++k) {
+        const int u = tid + 512 * k;
+        xo[k] = u < Q * 8 ? (uint32_t)(u >> 3) * xrow + 16 * (u & 7) : 0xfffffff0u;
+    }
+#pragma unroll
+    for (int k = 0; k < Regs::kBV; ++k) {
+        const int u = tid + 512 * k;
+        bo[k] = u < Q * 8 ? (uint32_t)(u >> 3) * brow + 16 * (u & 7) : 0xfffffff0u;
+        to[k] = u < Q * 8 ? (uint32_t)(u >> 3) * 4 : 0xfffffff0u;
+    }
+
+    auto fetch = [&](Regs &R, int c) {
+        c = c < c1 ? c : c1 - 1;     // past the last chunk: the last one again (unused)
+        const int st = first + (c - c0) * Q;
+        const int len = end - st < Q ? end - st : Q;
+        const rsrc_t rx = make_rsrc(x + ((int64_t)st * H + h) * P, (uint32_t)(len - 1) * xrow + P * 2);
+        const rsrc_t rb = make_rsrc(B + ((int64_t)st * G + g) * N + n0,
+                                    (uint32_t)(len - 1) * brow + NSL * 2);
+        const int64_t row = ((int64_t)h * max_chunks + c) * Q;
+        const rsrc_t rc = make_rsrc(cum + row, (uint32_t)len * 4);
+        const rsrc_t rd = make_rsrc(dtc + row, (uint32_t)len * 4);
+#pragma unroll
+        for (int k = 0; k < Regs::kXV; ++k) R.x[k] = buf_ld16(rx, xo[k]);
+#pragma unroll
+        for (int k = 0; k < Regs::kBV; ++k) {
+            R.b[k] = buf_ld16(rb, bo[k]);
+            R.cm[k] = buf_ldf(rc, to[k]);
+            R.dt[k] = buf_ldf(rd, to[k]);
+        }
+        R.cl = cum[row + len - 1];
+    };
+
+    // one iteration: stage chunk c from R into LDS, refill R with chunk c + DEPTH,
+    // then fold chunk c into the running state
+    auto step = [&](Regs &R, int c) {
+        const int st = first + (c - c0) * Q;
+        const int len = end - st < Q ? end - st : Q;
+        __syncthreads();   // the previous chunk's MFMA reads of xs / bs are done
+#pragma unroll
+        for (int k = 0; k < Regs::kXV; ++k) {
+            const int u = tid + 512 * k;
+            if (u < Q * 8) st16(xs + (u >> 3) * LDX + 8 * (u & 7), R.x[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < Regs::kBV; ++k) {
+            const int u = tid + 512 * k;
+            if (u < Q * 8) {
+                const int t = u >> 3;
+                const float w = t < len ? __expf(R.cl - R.cm[k]) * R.dt[k] : 0.0f;
+                const uint32_t w4[4] = {R.b[k].x, R.b[k].y, R.b[k].z, R.b[k].w};
+                float f[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    f[2 * i] = __uint_as_float(w4[i] << 16) * w;
+                    f[2 * i + 1] = __uint_as_float(w4[i] & 0xffff0000u) * w;
+                }
+                Vec16<bf16>::store(bs + t * LDB + 8 * (u & 7), f);
+            }
+        }
+        const float decay = __expf(R.cl);
+        fetch(R, c + DEPTH);
+        __syncthreads();
+
+        const int64_t off = ((int64_t)c * H + h) * PN + run;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            float v[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+            store4<bf16>(entering + off + 16 * j, v);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[j][e] *= decay;
+        }
+        const int nk = (len + 31) >> 5;
+        // (unrolled by 2 only: fully unrolled, every fragment is loaded ahead and
+        // the registers of the next chunks' tiles spill)
+#pragma unroll 2
+        for (int ks = 0; ks < nk; ++ks) {
+            const bf16x8 xf = mfma_frag_tr_split(xs, LDX, 32 * ks, 16 * pw, lane);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const bf16x8 bf = mfma_frag_tr_split(bs, LDB, 32 * ks, 32 * nh + 16 * j, lane);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf, xf, acc[j], 0, 0, 0);
+            }
+        }
+        if constexpr (CKPT) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                float w[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+                store4<TS>(ckpt + off + 16 * j, w);
+            }
+        }
+    };
+
+    // DEPTH register sets in flight: chunk c + DEPTH is requested while chunk c is
+    // folded in. The main loop is unrolled over the sets (each stays in registers)
+    // and no branch separates a load from its use, so the compiler's wait counts
+    // stay exact; the last chunks are done one by one after it.
+    Regs R[DEPTH];
+    if (c0 < c1) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) fetch(R[d], c0 + d);
+    }
+    int c = c0;
+    for (; c + DEPTH <= c1; c += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) step(R[d], c + d);
+    }
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; ++d)
+        if (c + d < c1) step(R[d], c + d);
+
+    if (slot_ok) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            float v[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+            store4<TS>(cslot + 16 * j, v);
+        }
+    }
+}
+
 // Chunk scan, bf16, P = 64, N = 128. Grid: max_chunks * H blocks of 2 Q threads
 // (Q / 32 waves), logical order (chunk, head). Wave w owns the 16-row tiles w and
 // Q / 16 - 1 - w, which balances the causal work.
@@ -1093,6 +1289,66 @@ void launch_state_passing(const PrefillDims &d, const float *states, const float
         if (d.in_bf16) launch_sp_t<float, bf16>(d, states, cum, meta, cache, idx, has_init, entering, ckpt, st);
         else launch_sp_t<float, float>(d, states, cum, meta, cache, idx, has_init, entering, ckpt, st);
     }
+}
+
+template <int Q, int DEPTH, bool CKPT, typename TS>
+static void launch_state_scan_k(const PrefillDims &d, const void *x, const void *B,
+                                const int32_t *meta, const float *cum, const float *dtc,
+                                void *cache, const int32_t *idx, const uint8_t *has_init,
+                                void *entering, void *ckpt, hipStream_t st)
+{
+    const size_t smem = (size_t)Q * (kScanLDX + kScanLDB) * sizeof(bf16);
+    static size_t raised = 0;
+    allow_lds(reinterpret_cast<const void *>(&state_scan_fast_kernel<Q, DEPTH, CKPT, TS>), smem,
+              raised);
+    const unsigned nblk = (unsigned)((int64_t)d.S * d.H * (128 / kScanNSL));
+    hipLaunchKernelGGL((state_scan_fast_kernel<Q, DEPTH, CKPT, TS>), dim3(nblk), dim3(512), smem,
+                       st, d.S, d.H, d.G, d.max_chunks, d.num_slots, static_cast<const bf16 *>(x),
+                       static_cast<const bf16 *>(B), meta, cum, dtc, static_cast<TS *>(cache), idx,
+                       has_init, static_cast<bf16 *>(entering), static_cast<TS *>(ckpt));
+}
+
+template <int Q, typename TS>
+static void launch_state_scan_q(const PrefillDims &d, const void *x, const void *B,
+                                const int32_t *meta, const float *cum, const float *dtc,
+                                void *cache, const int32_t *idx, const uint8_t *has_init,
+                                void *entering, void *ckpt, hipStream_t st)
+{
+    constexpr int DEPTH = 1;
+    if (ckpt)
+        launch_state_scan_k<Q, DEPTH, true, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init,
+                                                entering, ckpt, st);
+    else
+        launch_state_scan_k<Q, DEPTH, false, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init,
+                                                 entering, ckpt, st);
+}
+
+template <typename TS>
+static void launch_state_scan_t(const PrefillDims &d, const void *x, const void *B,
+                                const int32_t *meta, const float *cum, const float *dtc,
+                                void *cache, const int32_t *idx, const uint8_t *has_init,
+                                void *entering, void *ckpt, hipStream_t st)
+{
+    switch (d.Q) {
+    case 32: launch_state_scan_q<32, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, st); break;
+    case 64: launch_state_scan_q<64, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, st); break;
+    case 128: launch_state_scan_q<128, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, st); break;
+    default: launch_state_scan_q<256, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, st); break;
+    }
+}
+
+bool fused_state_path(const PrefillDims &d) { return use_fast(d); }
+
+void launch_state_scan(const PrefillDims &d, const void *x, const void *B, const int32_t *meta,
+                       const float *cum, const float *dtc, void *cache, const int32_t *idx,
+                       const uint8_t *has_init, void *entering, void *ckpt, void *stream)
+{
+    if (d.S <= 0) return;
+    hipStream_t st = as_stream(stream);
+    if (d.state_bf16)
+        launch_state_scan_t<bf16>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, st);
+    else
+        launch_state_scan_t<float>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, st);
 }
 
 void launch_chunk_scan(const PrefillDims &d, const void *x, const void *C, const float *D,

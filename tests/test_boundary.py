@@ -56,6 +56,11 @@ def test_sizes():
     big = P(total_tokens=4096, nheads=80, headdim=64, d_state=128, chunk_size=256,
             in_dtype=torch.bfloat16)
     assert ssd.max_chunks(big) == 17
+    # bf16 inputs, headdim 64, d_state 128: the fused state kernel needs no chunk states
+    mc, H, Q = 17, 80, 256
+    want_big = (r(4 * (2 + 3 * mc)) + 2 * r(4 * H * mc * Q) + r(2 * mc * 1 * Q * Q)
+                + r(2 * mc * H * 64 * 128))
+    assert ssd.workspace_bytes(big) == want_big
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -103,6 +108,22 @@ def test_null_and_alignment_and_workspace():
     # the step entry points check their pointers too
     assert lib.ssd_chunk_scan(ctypes.byref(p), *([ok] * 6), None, ok, ok, None) == 1
     assert lib.ssd_state_passing(ctypes.byref(p), ok, ok, ok, None, ok, None, ok, None, None) == 1
+
+
+def test_fused_state_entry_point_shapes():
+    """ssd_chunk_state_passing serves bf16 inputs with headdim 64, d_state 128 only."""
+    lib = ssd._lib
+    ok = ctypes.c_void_p(256)
+    args = [ok] * 7 + [None, ok, None, None]
+    assert lib.ssd_chunk_state_passing(ctypes.byref(P()), *args) == 4
+    assert lib.ssd_chunk_state_passing(ctypes.byref(P(in_dtype=torch.bfloat16)), *args) == 4
+    fast = P(headdim=64, d_state=128, in_dtype=torch.bfloat16)
+    a = list(args)
+    a[0] = None
+    assert lib.ssd_chunk_state_passing(ctypes.byref(fast), *a) == 1
+    a = list(args)
+    a[8] = ctypes.c_void_p(264)
+    assert lib.ssd_chunk_state_passing(ctypes.byref(fast), *a) == 7
 
 
 def test_decode_validation():

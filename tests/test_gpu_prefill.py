@@ -266,11 +266,38 @@ def test_empty_batch_and_zero_length_sequences():
     assert torch.equal(after.view(torch.int32), ref["cache"].view(torch.int32))
 
 
-def test_bad_device_indices_do_not_fault():
+@pytest.mark.parametrize("ti,ts", [(F32, F32), (BF16, BF16), (BF16, F32)])
+def test_zero_length_sequences_between_others(ti, ts):
+    """Empty sequences among non-empty ones (bf16 inputs with headdim 64 and
+    d_state 128 take the fused chunk state + state passing kernel): each empty
+    one writes its initial state (or zeros) back unchanged."""
+    P, N = (64, 128) if ti == BF16 else (16, 16)
+    lens = (0, 70, 0, 0, 300, 0)
+    S = len(lens)
+    inp = sy.random_problem(14, lens, 4, P, N, 2, 64, ti, ts, num_slots=S + 2,
+                            has_initial=[True, True, False, True, False, True])
+    cache = _cache_with_states(inp, S + 2, ts)
+    y, after, ckpt = gpu_prefill(inp, cache, 64, checkpoints=True)
+    ref = oracle.prefill(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.cu_seqlens,
+                         inp.state_indices, inp.has_initial, cache, 64, checkpoints=True)
+    assert_close(y, ref["y"], ti, "y", normalised=False)
+    used = inp.state_indices.long()
+    assert_close(after[used], ref["final"], looser(ti, ts), "final states")
+    nc = int(oracle.chunk_counts(inp.cu_seqlens.numpy(), 64)[-1])
+    assert_close(ckpt[:nc], ref["ckpt"], looser(ti, ts), "checkpoints")
+    bits = torch.int16 if ts == BF16 else torch.int32
+    for s in (0, 3, 5):      # empty with an initial state: bits unchanged
+        slot = int(inp.state_indices[s])
+        assert torch.equal(after[slot].view(bits), cache[slot].view(bits)), s
+    assert (after[int(inp.state_indices[2])] == 0).all()   # empty, no initial state
+
+
+@pytest.mark.parametrize("ti,P,N", [(F32, 16, 16), (BF16, 64, 128)])
+def test_bad_device_indices_do_not_fault(ti, P, N):
     """Slot indices outside [0, num_slots) are skipped on the device: the
     sequence starts from zero and nothing is written."""
     lens = (40, 70)
-    inp = sy.random_problem(15, lens, 4, 16, 16, 1, 64, F32, F32, num_slots=2,
+    inp = sy.random_problem(15, lens, 4, P, N, 1, 64, ti, F32, num_slots=2,
                             has_initial=[True, True])
     cache = _cache_with_states(inp, 2, F32, nan_unused=False)
     inp.state_indices[:] = torch.tensor([7, -3], dtype=torch.int32)
@@ -278,7 +305,7 @@ def test_bad_device_indices_do_not_fault():
     assert torch.equal(after, cache)
     ref = oracle.prefill(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.cu_seqlens,
                          torch.tensor([0, 1]), None, cache, 64)
-    assert_close(y, ref["y"], F32, "y from zero")
+    assert_close(y, ref["y"], ti, "y from zero", normalised=False)
 
 
 # --------------------------------------------------------------------------------------
