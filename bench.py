@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (for scaling HBM counters)")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write the profiles/ summaries from rocprofv3 output of this script "
+                         "(no GPU work)")
     return ap.parse_args()
 
 
@@ -69,27 +72,125 @@ def prefill_bytes(T, S, H, P, N, G, Q, nc, ex, es, s_init, checkpoints):
     }
 
 
-def source_sha(path):
-    with open(path, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+# kernel name fragment (as rocprofv3 prints it) -> (name used here, source files it is built from)
+KERNELS = {
+    "chunk_cumsum_kernel": ("chunk_cumsum", ["ssd_prefill.hip", "ssd_device.h"]),
+    "bmm_kernel": ("bmm_chunk", ["ssd_prefill.hip", "ssd_device.h"]),
+    "state_scan_fast_kernel": ("chunk_state_passing", ["ssd_prefill.hip", "ssd_device.h"]),
+    "chunk_scan_fast_kernel": ("chunk_scan", ["ssd_prefill.hip", "ssd_device.h"]),
+    "state_update_kernel": ("selective_state_update", ["ssd_decode.hip", "ssd_device.h"]),
+}
+CSRC = os.path.join("state_space_model_varlen_amd", "csrc")
+CALIBRATION_BYTES = 256 << 20   # the --copy-calibration copy
+
+
+def source_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(kernel):
-    """HBM traffic of a kernel from committed counter runs (profiles/traffic_<kernel>.json),
-    valid only while the kernel source it was taken on is unchanged."""
+    """HBM bytes per launch of a kernel from committed counter runs
+    (profiles/traffic_<kernel>.json), valid only while the sources the kernel is
+    built from are unchanged since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    src = os.path.join(ROOT, rec.get("source", ""))
-    if not os.path.exists(src) or source_sha(src) != rec.get("source_sha"):
+    srcs = rec.get("sources", [])
+    if not srcs or not all(os.path.exists(os.path.join(ROOT, p)) for p in srcs):
+        return None
+    if source_sha(srcs) != rec.get("source_sha"):
         return None
     return rec.get("bytes_per_launch")
 
 
+def summarize_profiles(trace_dir, fetch_dir, write_dir, cmds):
+    """Turn the rocprofv3 output of the three profiling runs of this script
+    (kernel trace; FETCH_SIZE; WRITE_SIZE, both with --copy-calibration) into the
+    committed summaries: profiles/kernel_trace_*.md, profiles/hbm_traffic_*.md and
+    one profiles/traffic_<kernel>.json per kernel. Counter values (KiB per
+    dispatch) are scaled by what the same counter reads for the 256 MiB
+    calibration copy (the last copy dispatch of the run)."""
+    import csv
+
+    def short(name):
+        for frag, (nm, _) in KERNELS.items():
+            if frag in name:
+                return nm
+        return None
+
+    stats = list(csv.DictReader(open(os.path.join(trace_dir, "c1_kernel_stats.csv"))))
+    counters = {}
+    scale = {}
+    for ctr, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = list(csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))))
+        copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        cal = max(copies, key=lambda r: int(r["Dispatch_Id"]))
+        scale[ctr] = CALIBRATION_BYTES / (float(cal["Counter_Value"]) * 1024.0)
+        per = {}
+        for r in rows:
+            nm = short(r["Kernel_Name"])
+            if nm:
+                per.setdefault(nm, []).append(float(r["Counter_Value"]))
+        counters[ctr] = {k: sum(v) / len(v) for k, v in per.items()}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    lines = ["# Kernel trace: SSD prefill (L=4096, 80 heads) and MTP verify update (128 x 3 tokens)",
+             "", "Command (MI355X, one GPU, from the repository root):", "```", cmds[0], "```",
+             "Source: `c1_kernel_stats.csv` written by that command (rocprofv3 `--stats`). "
+             "Prefill kernels run inside ssd_combined_varlen (warm-up + timed steps) and alone "
+             "(per-kernel timing); torch kernels (input casts, copies) omitted.", "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in stats:
+        nm = short(r["Name"])
+        if nm:
+            lines.append(f"| {nm} (`{r['Name'][:48]}...`) | {r['Calls']} | "
+                         f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                         f"{float(r['MaxNs']) / 1e3:.2f} |")
+    with open(os.path.join(ROOT, "profiles", "kernel_trace_prefill_L4096_and_mtp_verify.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    lines = ["# HBM traffic per dispatch: SSD prefill (L=4096, 80 heads) and MTP verify update",
+             "", "Commands (MI355X, one GPU, from the repository root), one counter per run:", "```",
+             cmds[1], cmds[2], "```",
+             f"Scale factors from the 256 MiB calibration copy in the same runs: FETCH_SIZE x "
+             f"{scale['FETCH_SIZE']:.4f}, WRITE_SIZE x {scale['WRITE_SIZE']:.4f}.", "",
+             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch (scaled) |",
+             "|---|---|---|---|"]
+    for nm in sorted(set(counters["FETCH_SIZE"]) & set(counters["WRITE_SIZE"])):
+        f, w = counters["FETCH_SIZE"][nm], counters["WRITE_SIZE"][nm]
+        fb, wb = f * 1024 * scale["FETCH_SIZE"], w * 1024 * scale["WRITE_SIZE"]
+        lines.append(f"| {nm} | {f:.1f} | {w:.1f} | {fb + wb:.0f} |")
+        srcs = [os.path.join(CSRC, p) for p in next(v[1] for v in KERNELS.values() if v[0] == nm)]
+        with open(os.path.join(ROOT, "profiles", f"traffic_{nm}.json"), "w") as fh:
+            json.dump({"kernel": nm, "sources": srcs, "source_sha": source_sha(srcs),
+                       "fetch_bytes": round(fb), "write_bytes": round(wb),
+                       "bytes_per_launch": round(fb + wb), "fetch_scale": scale["FETCH_SIZE"],
+                       "write_scale": scale["WRITE_SIZE"], "commands": cmds[1:]}, fh, indent=1)
+            fh.write("\n")
+    with open(os.path.join(ROOT, "profiles", "hbm_traffic_prefill_L4096_and_mtp_verify.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+PROFILE_COMMANDS = [
+    "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof/trace -o c1 -- "
+    "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof/fetch -o run -- "
+    "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof/write -o run -- "
+    "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration",
+]
+
+
 def main():
     args = parse()
+    if args.summarize_profiles:
+        summarize_profiles(*args.summarize_profiles, PROFILE_COMMANDS)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} (WORLD_SIZE={world}) is not "
@@ -160,17 +261,25 @@ def main():
     nb = prefill_bytes(T, S, H, P, N, G, Q, nc, 2, 4, 0, False)
     kernels = {}
     reps = max(args.steps, 10)
-    for name, fn in launches.items():
+    def avg_us(fn):
+        """Average duration of back-to-back launches of fn, from HIP events recorded on
+        the stream the kernels run on. A spin kernel queued first keeps the GPU busy
+        while the host enqueues every launch, so host-side call overhead does not
+        show up as idle time between the events."""
         for _ in range(3):
             fn()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)]
-        for a, b in evs:
-            a.record(stream)
-            fn()
-            b.record(stream)
         torch.cuda.synchronize()
-        us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(20_000_000)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
+    for name, fn in launches.items():
+        us = avg_us(fn)
         kernels[name] = {"avg_us": round(us, 3), "bytes": nb[name],
                          "GBps": round(nb[name] / (us * 1e-6) / 1e9, 1)}
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
@@ -194,17 +303,8 @@ def main():
     didx = dd.state_indices.to(dev)
     dy = torch.empty(R, TT, DH, DP, dtype=dcfg.in_dtype, device=dev)
     inter = torch.empty(R, TT, DH, DP, DN, dtype=dcfg.state_dtype, device=dev)
-    for _ in range(3):
-        ssd.selective_state_update(up, dcache, didx, dx, ddt, dA, dB, dC, dD, dy, inter, stream)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
-    for a, b in evs:
-        a.record(stream)
-        ssd.selective_state_update(up, dcache, didx, dx, ddt, dA, dB, dC, dD, dy, inter, stream)
-        b.record(stream)
-    torch.cuda.synchronize()
-    ssu_us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    ssu_us = avg_us(lambda: ssd.selective_state_update(up, dcache, didx, dx, ddt, dA, dB, dC, dD,
+                                                       dy, inter, stream))
     es = 2
     ssu_bytes = R * DH * DP * DN * es * (1 + TT) + R * TT * (2 * DH * DP + 2 * DG * DN + DH) * 2
     decode = {"workload": "mtp_verify R=128 T=3 H=128 P=64 N=128 G=8 bf16 cache 512 slots",
