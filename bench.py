@@ -1,8 +1,8 @@
 #!/usr/bin/env python3
 """Throughput of the MI355X SSD varlen prefill scan (and the MTP state update).
 
-One step = one ssd_combined_varlen call (chunk cumsum, bmm, chunk state with
-state passing in one kernel, chunk scan) over the single-sequence Mamba2 layer prefill:
+One step = one ssd_combined_varlen call (three launches: chunk cumsum with bmm,
+chunk state with state passing, chunk scan) over the single-sequence Mamba2 layer prefill:
 L = 4096 tokens, 80 heads, headdim 64, d_state 128, 1 group, chunk 256, bf16
 x/B/C/dt, fp32 A/D/state. Inputs are seeded synthetic draws, resident in HBM
 before the timed region. `value` = tokens / s of that call (one layer).
@@ -74,6 +74,7 @@ def prefill_bytes(T, S, H, P, N, G, Q, nc, ex, es, s_init, checkpoints):
 
 # kernel name fragment (as rocprofv3 prints it) -> (name used here, source files it is built from)
 KERNELS = {
+    "chunk_prep_kernel": ("chunk_prep", ["ssd_prefill.hip", "ssd_device.h"]),
     "chunk_cumsum_kernel": ("chunk_cumsum", ["ssd_prefill.hip", "ssd_device.h"]),
     "bmm_kernel": ("bmm_chunk", ["ssd_prefill.hip", "ssd_device.h"]),
     "state_scan_fast_kernel": ("chunk_state_passing", ["ssd_prefill.hip", "ssd_device.h"]),

@@ -272,8 +272,7 @@ int ssd_combined_varlen(const ssd_problem *p, const void *x, const void *dt, con
     float *states = reinterpret_cast<float *>(base + w.states);
     void *entering = base + w.entering;
 
-    ssd::launch_chunk_cumsum(d, dt, A, cu_seqlens, meta, cum, dtc, stream);
-    ssd::launch_bmm(d, B, C, meta, cb, stream);
+    ssd::launch_chunk_prep(d, dt, A, cu_seqlens, meta, cum, dtc, B, C, cb, stream);
     if (ssd::fused_state_path(d)) {
         ssd::launch_state_scan(d, x, B, meta, cum, dtc, state_cache, state_indices,
                                has_initial_state, entering, checkpoints, stream);

@@ -25,6 +25,10 @@ struct DecodeDims {
 
 void launch_chunk_cumsum(const PrefillDims &d, const void *dt, const float *A, const int32_t *cu,
                          int32_t *meta, float *cum, float *dto, void *stream);
+// Steps 1 and 4 (cumsum with chunk metadata, and CB) in one launch.
+void launch_chunk_prep(const PrefillDims &d, const void *dt, const float *A, const int32_t *cu,
+                       int32_t *meta, float *cum, float *dto, const void *B, const void *C,
+                       void *CB, void *stream);
 void launch_chunk_state(const PrefillDims &d, const void *x, const void *B, const int32_t *meta,
                         const float *cum, const float *dtc, float *states, void *stream);
 void launch_state_passing(const PrefillDims &d, const float *states, const float *cum,

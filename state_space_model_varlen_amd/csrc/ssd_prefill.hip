@@ -77,42 +77,36 @@ __device__ void find_chunk(int T, int S, int Q, int max_chunks, const int32_t *_
     __syncthreads();
 }
 
-template <typename TIn>
-__global__ __launch_bounds__(256) void chunk_cumsum_kernel(
-    int T, int S, int H, int Q, int max_chunks, const TIn *__restrict__ dt,
-    const float *__restrict__ A, const int32_t *__restrict__ cu, int32_t *__restrict__ meta,
-    float *__restrict__ cum_out, float *__restrict__ dt_out)
+// Chunk (seq, start, len) of chunk c after find_chunk, from cu_seqlens.
+__device__ __forceinline__ ChunkInfo found_chunk(int T, int Q, const int32_t *__restrict__ cu,
+                                                 const int *s_found)
 {
-    __shared__ int s_wave_tot[4];
-    __shared__ int s_found[2];
-    const int c = blockIdx.x;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const bool publish = blockIdx.y == 0;
-    find_chunk(T, S, Q, max_chunks, cu, c, publish && blockIdx.x == 0, meta, s_found, s_wave_tot);
-
-    const int seq = s_found[0];
-    int start = 0, len = 0;
-    if (seq >= 0) {
-        const int a = clampi(cu[seq], 0, T), b = clampi(cu[seq + 1], 0, T);
-        start = a + s_found[1] * Q;
-        len = b - start < Q ? b - start : Q;
+    ChunkInfo ci;
+    ci.seq = s_found[0];
+    ci.start = 0;
+    ci.len = 0;
+    if (ci.seq >= 0) {
+        const int a = clampi(cu[ci.seq], 0, T), b = clampi(cu[ci.seq + 1], 0, T);
+        ci.start = a + s_found[1] * Q;
+        ci.len = b - ci.start < Q ? b - ci.start : Q;
     }
-    if (publish && threadIdx.x == 0) {
-        int32_t *m = meta + (S + 1) + 3 * c;
-        m[0] = seq;
-        m[1] = start;
-        m[2] = len;
-    }
-    const int h = blockIdx.y * kCumsumHeadsPerBlock + wave;
-    if (len <= 0 || h >= H) return;
+    return ci;
+}
 
+// Wavefront prefix sum of dt * A_h over chunk c for head h (one wave).
+template <typename TIn>
+__device__ __forceinline__ void cumsum_wave(int H, int Q, int max_chunks, int c, int h,
+                                            const ChunkInfo &ci, int lane,
+                                            const TIn *__restrict__ dt, const float *__restrict__ A,
+                                            float *__restrict__ cum_out, float *__restrict__ dt_out)
+{
     const int E = (Q + kWave - 1) / kWave;  // positions per lane (<= 4)
     const float Ah = A[h];
     float vals[4], loc[4], run = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int i = lane * E + e;
-        vals[e] = (e < E && i < len) ? to_f32(dt[(int64_t)(start + i) * H + h]) : 0.0f;
+        vals[e] = (e < E && i < ci.len) ? to_f32(dt[(int64_t)(ci.start + i) * H + h]) : 0.0f;
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -130,6 +124,34 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(
             dt_out[row + i] = vals[e];
         }
     }
+}
+
+__device__ __forceinline__ void publish_chunk(int S, int c, const ChunkInfo &ci,
+                                              int32_t *__restrict__ meta)
+{
+    int32_t *m = meta + (S + 1) + 3 * c;
+    m[0] = ci.seq;
+    m[1] = ci.start;
+    m[2] = ci.len;
+}
+
+template <typename TIn>
+__global__ __launch_bounds__(256) void chunk_cumsum_kernel(
+    int T, int S, int H, int Q, int max_chunks, const TIn *__restrict__ dt,
+    const float *__restrict__ A, const int32_t *__restrict__ cu, int32_t *__restrict__ meta,
+    float *__restrict__ cum_out, float *__restrict__ dt_out)
+{
+    __shared__ int s_wave_tot[4];
+    __shared__ int s_found[2];
+    const int c = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const bool publish = blockIdx.y == 0;
+    find_chunk(T, S, Q, max_chunks, cu, c, publish && blockIdx.x == 0, meta, s_found, s_wave_tot);
+    const ChunkInfo ci = found_chunk(T, Q, cu, s_found);
+    if (publish && threadIdx.x == 0) publish_chunk(S, c, ci, meta);
+    const int h = blockIdx.y * kCumsumHeadsPerBlock + wave;
+    if (ci.len <= 0 || h >= H) return;
+    cumsum_wave<TIn>(H, Q, max_chunks, c, h, ci, lane, dt, A, cum_out, dt_out);
 }
 
 // ===========================================================================
@@ -338,20 +360,17 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
 // CB is stored in the input dtype (chunk scan rounds its masked product to
 // that dtype for the MFMA in any case): row-major for float32 inputs, MFMA
 // fragment order (cb_frag_offset) for bf16 inputs.
+// Row tile z of CB for chunk c, group g (one block of 256 threads).
 template <typename TIn, int N>
-__global__ __launch_bounds__(256) void bmm_kernel(int S, int G, int Q, int max_chunks,
-                                                  const TIn *__restrict__ B,
-                                                  const TIn *__restrict__ C,
-                                                  const int32_t *__restrict__ meta,
-                                                  TIn *__restrict__ CB)
+__device__ __forceinline__ void bmm_rows(int G, int Q, int c, int g, int z, const ChunkInfo &ci,
+                                         const TIn *__restrict__ B, const TIn *__restrict__ C,
+                                         TIn *__restrict__ CB)
 {
     typedef Mma<TIn> M;
     constexpr int NK = (N + M::K - 1) / M::K;
-    const int c = blockIdx.x, g = blockIdx.y;
-    const ChunkInfo ci = chunk_info(meta, S, c);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, kg = lane >> 4;
-    const int i0 = blockIdx.z * 16;
+    const int i0 = z * 16;
     if (ci.len <= 0 || i0 >= ci.len) return;
 
     typename M::frag cf[NK];       // C rows i0 .. i0 + 15 (B operand)
@@ -382,6 +401,47 @@ __global__ __launch_bounds__(256) void bmm_kernel(int S, int G, int Q, int max_c
         const int jc = jt * 16 + 4 * kg;
         if constexpr (sizeof(TIn) == 2) store4<TIn>(cbc + cb_frag_offset(Q, i, jc), v4);
         else store4<TIn>(cbc + (int64_t)i * Q + jc, v4);
+    }
+}
+
+template <typename TIn, int N>
+__global__ __launch_bounds__(256) void bmm_kernel(int S, int G, int Q, int max_chunks,
+                                                  const TIn *__restrict__ B,
+                                                  const TIn *__restrict__ C,
+                                                  const int32_t *__restrict__ meta,
+                                                  TIn *__restrict__ CB)
+{
+    const int c = blockIdx.x;
+    bmm_rows<TIn, N>(G, Q, c, blockIdx.y, blockIdx.z, chunk_info(meta, S, c), B, C, CB);
+}
+
+// Steps 1 and 4 in one launch (the combined call): grid (max_chunks, HB + G Q / 16),
+// HB = ceil(H / 4). Blocks with blockIdx.y < HB are cumsum blocks (four heads,
+// metadata published by blockIdx.y == 0), the others compute one CB row tile.
+// Every block finds its chunk from cu_seqlens itself, so the two halves do not
+// wait for each other.
+template <typename TIn, int N>
+__global__ __launch_bounds__(256) void chunk_prep_kernel(
+    int T, int S, int H, int G, int Q, int max_chunks, const TIn *__restrict__ dt,
+    const float *__restrict__ A, const int32_t *__restrict__ cu, int32_t *__restrict__ meta,
+    float *__restrict__ cum_out, float *__restrict__ dt_out, const TIn *__restrict__ B,
+    const TIn *__restrict__ C, TIn *__restrict__ CB)
+{
+    __shared__ int s_wave_tot[4];
+    __shared__ int s_found[2];
+    const int c = blockIdx.x;
+    const int HB = (H + kCumsumHeadsPerBlock - 1) / kCumsumHeadsPerBlock;
+    const bool publish = blockIdx.y == 0;
+    find_chunk(T, S, Q, max_chunks, cu, c, publish && blockIdx.x == 0, meta, s_found, s_wave_tot);
+    const ChunkInfo ci = found_chunk(T, Q, cu, s_found);
+    if ((int)blockIdx.y < HB) {
+        if (publish && threadIdx.x == 0) publish_chunk(S, c, ci, meta);
+        const int h = blockIdx.y * kCumsumHeadsPerBlock + (threadIdx.x >> 6);
+        if (ci.len <= 0 || h >= H) return;
+        cumsum_wave<TIn>(H, Q, max_chunks, c, h, ci, threadIdx.x & 63, dt, A, cum_out, dt_out);
+    } else {
+        const int y = blockIdx.y - HB, tiles = Q / 16;
+        bmm_rows<TIn, N>(G, Q, c, y / tiles, y % tiles, ci, B, C, CB);
     }
 }
 
@@ -1140,6 +1200,34 @@ static void launch_cumsum_t(const PrefillDims &d, const void *dt, const float *A
     dim3 grid(d.max_chunks, (d.H + kCumsumHeadsPerBlock - 1) / kCumsumHeadsPerBlock);
     hipLaunchKernelGGL(chunk_cumsum_kernel<TIn>, grid, dim3(256), 0, st, d.T, d.S, d.H, d.Q,
                        d.max_chunks, static_cast<const TIn *>(dt), A, cu, meta, cum, dto);
+}
+
+template <typename TIn, int N>
+static void launch_prep_t(const PrefillDims &d, const void *dt, const float *A, const int32_t *cu,
+                          int32_t *meta, float *cum, float *dto, const void *B, const void *C,
+                          void *CB, hipStream_t st)
+{
+    const int HB = (d.H + kCumsumHeadsPerBlock - 1) / kCumsumHeadsPerBlock;
+    dim3 grid(d.max_chunks, HB + d.G * (d.Q / 16));
+    hipLaunchKernelGGL((chunk_prep_kernel<TIn, N>), grid, dim3(256), 0, st, d.T, d.S, d.H, d.G, d.Q,
+                       d.max_chunks, static_cast<const TIn *>(dt), A, cu, meta, cum, dto,
+                       static_cast<const TIn *>(B), static_cast<const TIn *>(C),
+                       static_cast<TIn *>(CB));
+}
+
+void launch_chunk_prep(const PrefillDims &d, const void *dt, const float *A, const int32_t *cu,
+                       int32_t *meta, float *cum, float *dto, const void *B, const void *C,
+                       void *CB, void *stream)
+{
+    if (d.max_chunks <= 0) return;
+    hipStream_t st = as_stream(stream);
+    if (d.in_bf16) {
+        if (d.N == 128) launch_prep_t<bf16, 128>(d, dt, A, cu, meta, cum, dto, B, C, CB, st);
+        else launch_prep_t<bf16, 16>(d, dt, A, cu, meta, cum, dto, B, C, CB, st);
+    } else {
+        if (d.N == 128) launch_prep_t<float, 128>(d, dt, A, cu, meta, cum, dto, B, C, CB, st);
+        else launch_prep_t<float, 16>(d, dt, A, cu, meta, cum, dto, B, C, CB, st);
+    }
 }
 
 void launch_chunk_cumsum(const PrefillDims &d, const void *dt, const float *A, const int32_t *cu,
