@@ -204,8 +204,10 @@ int ssd_chunk_state_passing(const ssd_problem *p, const void *x, const void *B,
  *     ((i/16 * Q/32 + j/32) * 64 + lane) * 8 + v, lane = i%16 + 16*kg,
  *     where j%32 = 4*kg + v%4 + 16*(v/4) (one contiguous 1 KiB block per
  *     16-row x 32-column operand tile).
- * Defined for j <= i < chunk length (the causal part chunk scan reads); other
- * entries are unspecified.
+ * Defined for j <= i < chunk length (the causal part chunk scan reads); for
+ * bf16 inputs also for every (i, j) with i < chunk length in the 16-row x
+ * 32-column blocks that hold the diagonal, as zero where j > i (chunk scan
+ * then needs no causal mask). Other entries are unspecified.
  */
 int ssd_bmm_chunk(const ssd_problem *p, const void *B, const void *C,
                   const int32_t *chunk_meta, void *CB, void *stream);

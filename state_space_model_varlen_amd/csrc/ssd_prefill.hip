@@ -382,7 +382,17 @@ __device__ __forceinline__ void bmm_rows(int G, int Q, int c, int g, int z, cons
                                        : M::zero();
     }
     TIn *cbc = CB + ((int64_t)c * G + g) * Q * Q;
-    for (int jt = wave; jt <= i0 / 16; jt += 4) {
+    // bf16 (fragment order): the 16 x 32 blocks holding the diagonal are written
+    // whole, zero above the diagonal, so that chunk scan needs no causal mask
+    const int jd = i0 / 16;
+    const int jmax = sizeof(TIn) == 2 && (jd & 1) == 0 ? jd + 1 : jd;
+    for (int jt = wave; jt <= jmax; jt += 4) {
+        const int jc = jt * 16 + 4 * kg;
+        if (jt > jd) {
+            const float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            store4<TIn>(cbc + cb_frag_offset(Q, i, jc), z);
+            continue;
+        }
         const int j = jt * 16 + r16;
         typename M::frag bfr[NK];  // B rows j (A operand)
 #pragma unroll
@@ -398,7 +408,10 @@ __device__ __forceinline__ void bmm_rows(int G, int Q, int c, int g, int z, cons
         // 4 consecutive elements in either layout (row-major for float32 inputs,
         // MFMA fragment order for bf16 inputs)
         float v4[4] = {acc[0], acc[1], acc[2], acc[3]};
-        const int jc = jt * 16 + 4 * kg;
+        if (jt == jd) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) v4[v] = jc + v <= i ? v4[v] : 0.0f;
+        }
         if constexpr (sizeof(TIn) == 2) store4<TIn>(cbc + cb_frag_offset(Q, i, jc), v4);
         else store4<TIn>(cbc + (int64_t)i * Q + jc, v4);
     }
@@ -916,6 +929,7 @@ void state_scan_fast_kernel(
 // before the staging barrier; y leaves through a per-wave LDS tile
 // as 16-byte row stores.
 constexpr float kMaxSpan = 60.0f;    // natural-log units
+constexpr int kScanLDR = 20;         // p-major y tile pitch (bf16) of the epilogue
 
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -947,7 +961,7 @@ __device__ __forceinline__ void scan_row_tile(
     bf16 *yw, const bf16 *xsrc, int H, float Dh, bf16 *yout, const bf16 *CBc, int nrt, int nnk,
     uint4 *ncf, bool prefetch_next)
 {
-    constexpr int P = 64, N = 128, LDX = kFastLD, LDH = N + 8, LDY = P + 8;
+    constexpr int P = 64, N = 128, LDX = kFastLD, LDH = N + 8;
     if (nk == 0) {
         if (prefetch_next) load_cb_frags<KN>(CBc, Q, nrt, lane, nnk, ncf);
         return;
@@ -960,12 +974,10 @@ __device__ __forceinline__ void scan_row_tile(
 #pragma unroll
     for (int kk = 0; kk < N / 32; ++kk)
         cr[kk] = i < len ? ld16(Cb + (int64_t)i * G * N + 32 * kk + 8 * kg) : zero16();
-    uint4 xe[2];                         // x rows for the D x term of the epilogue
+    uint4 xe[2];                         // x of the D x term: row r16, p = 32 k + 8 kg + 0..7
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int u = lane + 64 * k, il = u >> 3;
-        xe[k] = i0 + il < len ? ld16(xsrc + (int64_t)(i0 + il) * H * P + 8 * (u & 7)) : zero16();
-    }
+    for (int k = 0; k < 2; ++k)
+        xe[k] = i < len ? ld16(xsrc + (int64_t)i * H * P + 32 * k + 8 * kg) : zero16();
 
     f32x4 acc[P / 16];
 #pragma unroll
@@ -980,17 +992,10 @@ __device__ __forceinline__ void scan_row_tile(
                                   bf16_lo(cbf[ks].w), bf16_hi(cbf[ks].w)};
             bf16x8 af;
             if (!exact) {
+                // CB is zero above the diagonal (see bmm), and e is finite: no mask
                 const float e = __builtin_amdgcn_exp2f(ci2 - scum[j0 + 31 < Q ? j0 + 31 : Q - 1]);
-                if (ks < nk - 1) {               // strictly below the diagonal: no mask
 #pragma unroll
-                    for (int v = 0; v < 8; ++v) af[v] = static_cast<bf16>(cbv[v] * e);
-                } else {
-#pragma unroll
-                    for (int v = 0; v < 8; ++v) {
-                        const int j = j0 + 4 * kg + (v & 3) + ((v >> 2) << 4);
-                        af[v] = static_cast<bf16>(j <= i ? cbv[v] * e : 0.0f);
-                    }
-                }
+                for (int v = 0; v < 8; ++v) af[v] = static_cast<bf16>(cbv[v] * e);
             } else {
 #pragma unroll
                 for (int v = 0; v < 8; ++v) {
@@ -1031,30 +1036,33 @@ __device__ __forceinline__ void scan_row_tile(
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[pt][v] += erow[v] * acc2[pt][v];
 
-    // epilogue: the SSM part goes through the wave's LDS tile into row order,
-    // where D x is added from 16-byte x loads (L2-resident) before the store
+    // epilogue: the SSM part goes through the wave's LDS tile, stored p-major
+    // (yw[p][r], r = row in the tile) with one 8-byte write of 4 rows per p tile,
+    // and comes back with transpose reads as 8 consecutive p of one row (r16),
+    // where D x is added from 16-byte x loads before the 16-byte store
 #pragma unroll
     for (int pt = 0; pt < P / 16; ++pt) {
-        const int p = 16 * pt + r16;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) yw[(4 * kg + v) * LDY + p] = static_cast<bf16>(acc[pt][v]);
+        const float v4[4] = {acc[pt][0], acc[pt][1], acc[pt][2], acc[pt][3]};
+        store4<bf16>(yw + (16 * pt + r16) * kScanLDR + 4 * kg, v4);
     }
     wave_lds_sync();
+    // (the transpose reads run with every lane active: each lane's result is
+    // gathered from words named by other lanes)
+    bf16x8 sv[2];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int u = lane + 64 * k;      // 16 rows x 8 vectors
-        const int il = u >> 3, c8 = u & 7;
-        if (i0 + il < len) {
-            const int64_t row = (int64_t)(i0 + il) * H * P + 8 * c8;
-            const uint4 xv = xe[k], sv = ld16(yw + il * LDY + 8 * c8);
-            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, sw[4] = {sv.x, sv.y, sv.z, sv.w};
+    for (int k = 0; k < 2; ++k) sv[k] = mfma_frag_tr(yw, kScanLDR, 32 * k, 0, lane);
+    if (i < len) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const uint4 su = __builtin_bit_cast(uint4, sv[k]), xv = xe[k];
+            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, sw[4] = {su.x, su.y, su.z, su.w};
             float o[8];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 o[2 * q] = bf16_lo(sw[q]) + Dh * bf16_lo(xw[q]);
                 o[2 * q + 1] = bf16_hi(sw[q]) + Dh * bf16_hi(xw[q]);
             }
-            Vec16<bf16>::store(yout + row, o);
+            Vec16<bf16>::store(yout + (int64_t)i * H * P + 32 * k + 8 * kg, o);
         }
     }
     wave_lds_sync();
@@ -1068,12 +1076,12 @@ void chunk_scan_fast_kernel(
     const float *__restrict__ cum, const float *__restrict__ dtc, const bf16 *__restrict__ CB,
     const bf16 *__restrict__ entering, bf16 *__restrict__ y)
 {
-    constexpr int P = 64, N = 128, LDX = kFastLD, LDH = N + 8, LDY = P + 8;
+    constexpr int P = 64, N = 128, LDX = kFastLD, LDH = N + 8;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     bf16 *xs = reinterpret_cast<bf16 *>(smem);                // [Q][LDX]  x' (or x)
     bf16 *hs = xs + Q * LDX;                                   // [P][LDH]  entering state
-    bf16 *ys = hs + P * LDH;                                   // [Q / 32][16][LDY]
-    float *scum = reinterpret_cast<float *>(ys + (Q / 32) * 16 * LDY);  // [Q] cum * log2(e)
+    bf16 *ys = hs + P * LDH;                                   // [Q / 32][P][kScanLDR]
+    float *scum = reinterpret_cast<float *>(ys + (Q / 32) * P * kScanLDR);  // [Q] cum * log2(e)
     float *sdt = scum + Q;                                     // [Q]
 
     const int nblk = max_chunks * H;
@@ -1163,7 +1171,7 @@ void chunk_scan_fast_kernel(
 
     const float Dh = D ? D[h] : 0.0f;
     const bf16 *Cb = C + ((int64_t)ci.start * G + g) * N;
-    bf16 *yw = ys + wave * 16 * LDY;
+    bf16 *yw = ys + wave * P * kScanLDR;
 
     // tile B first (larger); tile A's CB fragments are requested once B's are consumed
     uint4 caf[kStepsA];
@@ -1301,7 +1309,7 @@ static void launch_scan_fast(const PrefillDims &d, const void *x, const void *C,
 {
     const size_t smem = (size_t)Q * (kFastLD * sizeof(bf16) + 2 * sizeof(float)) +
                         (size_t)64 * (128 + 8) * sizeof(bf16) +
-                        (size_t)(Q / 32) * 16 * (64 + 8) * sizeof(bf16);
+                        (size_t)(Q / 32) * 64 * kScanLDR * sizeof(bf16);
     static size_t raised = 0;
     allow_lds(reinterpret_cast<const void *>(&chunk_scan_fast_kernel<Q>), smem, raised);
     const unsigned nblk = (unsigned)((int64_t)d.max_chunks * d.H);
