@@ -6,6 +6,8 @@
 //
 // Bandwidth-bound: per (request, head) the [P x N] state streams in once and
 // out once per kept token; the float32 state lives in registers across tokens.
+#include <type_traits>
+
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -25,12 +27,72 @@ __device__ __forceinline__ void store8_nt(float *p, const float *v) {
     __builtin_nontemporal_store(hi, reinterpret_cast<f32x4 *>(p) + 1);
 }
 
+// 8 consecutive elements kept as loaded (16 bytes of bf16, 32 bytes of float)
+// and widened to float only where they are used.
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16> {
+    uint4 w;
+    __device__ __forceinline__ void load(const bf16 *p) { w = *reinterpret_cast<const uint4 *>(p); }
+    __device__ __forceinline__ void mask(uint32_t m) { w.x &= m; w.y &= m; w.z &= m; w.w &= m; }
+    __device__ __forceinline__ void widen(float *f) const {
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(u[i] << 16);
+            f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+        }
+    }
+};
+template <> struct Raw8<float> {
+    uint4 lo, hi;
+    __device__ __forceinline__ void load(const float *p) {
+        lo = *reinterpret_cast<const uint4 *>(p);
+        hi = *reinterpret_cast<const uint4 *>(p + 4);
+    }
+    __device__ __forceinline__ void mask(uint32_t m) {
+        lo.x &= m; lo.y &= m; lo.z &= m; lo.w &= m; hi.x &= m; hi.y &= m; hi.z &= m; hi.w &= m;
+    }
+    __device__ __forceinline__ void widen(float *f) const {
+        f[0] = __uint_as_float(lo.x); f[1] = __uint_as_float(lo.y);
+        f[2] = __uint_as_float(lo.z); f[3] = __uint_as_float(lo.w);
+        f[4] = __uint_as_float(hi.x); f[5] = __uint_as_float(hi.y);
+        f[6] = __uint_as_float(hi.z); f[7] = __uint_as_float(hi.w);
+    }
+};
+
+// Sum over each aligned group of W lanes (W = N / 8: 16 or 2), every lane of
+// the group ending with the total, with DPP lane moves (no LDS traffic): four
+// rotations of a 16-lane row, or the swap of neighbouring lanes.
+template <int W> __device__ __forceinline__ float row_sum(float v) {
+    static_assert(W == 16 || W == 2, "group width");
+    auto mv = [](float a, auto ctrl) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a),
+                                                                      decltype(ctrl)::value, 0xf,
+                                                                      0xf, false));
+    };
+    if constexpr (W == 16) {
+        v += mv(v, std::integral_constant<int, 0x128>());   // row_ror:8
+        v += mv(v, std::integral_constant<int, 0x124>());   // row_ror:4
+        v += mv(v, std::integral_constant<int, 0x122>());   // row_ror:2
+        v += mv(v, std::integral_constant<int, 0x121>());   // row_ror:1
+    } else {
+        v += mv(v, std::integral_constant<int, 0xb1>());    // quad_perm:[1,0,3,2]
+    }
+    return v;
+}
+
 // Block (h, r), 256 threads. The state is cut into 16-byte chunks of 8
 // elements; chunk q = tid + 256 k covers row p = q / (N / 8), columns
 // 8 (q % (N / 8)) .. +7, so every vector access of the block is contiguous and
 // the N / 8 lanes sharing a row sit next to each other in one wave (their
-// partial dot products with C are summed with lane shuffles).
-template <typename TIn, typename TS, int P, int N>
+// partial dot products with C are summed across the lanes).
+//
+// Tokens are handled TM at a time: every load of a group (the state, and dt,
+// x, B, C of its TM tokens) is issued before any arithmetic, with no branch
+// between a load and its use (token indices past T are clamped, the state of an
+// invalid slot is loaded from slot 0 and zeroed), so the block waits on memory
+// once per group instead of once per load.
+template <typename TIn, typename TS, int P, int N, int TM>
 __global__ __launch_bounds__(256) void state_update_kernel(
     int T, int H, int G, int num_slots, TS *cache, const int32_t *__restrict__ idx,
     const TIn *__restrict__ x, const TIn *__restrict__ dt, const float *__restrict__ A,
@@ -40,6 +102,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(
     constexpr int CPR = N / 8;                       // chunks per state row
     constexpr int NCH = P * N / 8;                   // chunks per (request, head)
     constexpr int KC = (NCH + 255) / 256;            // chunks per thread
+    static_assert(NCH % 256 == 0 || KC == 1, "chunk split");
     const int h = blockIdx.x, r = blockIdx.y;
     const int tid = threadIdx.x;
     const int g = h / (H / G);
@@ -50,81 +113,87 @@ __global__ __launch_bounds__(256) void state_update_kernel(
     const int64_t PN = (int64_t)P * N;
     TS *cs = cache + ((int64_t)(slot_ok ? slot : 0) * H + h) * PN;
 
-    float st[KC][8];
+    int qk[KC], pk[KC];
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
         const int q = tid + 256 * k;
-        if (q < NCH && slot_ok) {
-            const int p = q / CPR;
-            if constexpr (sizeof(TS) == 2) {
-                Vec16<TS>::load(cs + (int64_t)p * N + n0, st[k]);
-            } else {
-                Vec16<TS>::load(cs + (int64_t)p * N + n0, st[k]);
-                Vec16<TS>::load(cs + (int64_t)p * N + n0 + 4, st[k] + 4);
-            }
-        } else {
+        qk[k] = q < NCH ? q : NCH - 1;       // (only when NCH < 256: duplicates, not stored)
+        pk[k] = qk[k] / CPR;
+    }
+    const float Ah = A[h];
+    const float Dh = D ? D[h] : 0.0f;
+    float dtv[TM], xv[TM][KC];
+    Raw8<TIn> braw[TM], craw[TM];
+    // requests dt, x, B, C of tokens t0 .. t0 + TM - 1 (clamped to T - 1)
+    auto load_group = [&](int t0) {
 #pragma unroll
-            for (int v = 0; v < 8; ++v) st[k][v] = 0.0f;
+        for (int j = 0; j < TM; ++j) {
+            const int t = t0 + j < T ? t0 + j : T - 1;
+            const int64_t rt = (int64_t)r * T + t;
+            dtv[j] = to_f32(dt[rt * H + h]);
+            braw[j].load(B + (rt * G + g) * N + n0);
+            craw[j].load(C + (rt * G + g) * N + n0);
+#pragma unroll
+            for (int k = 0; k < KC; ++k) xv[j][k] = to_f32(x[(rt * H + h) * P + pk[k]]);
+        }
+    };
+
+    // the state and the first token group are requested together; the state of an
+    // invalid slot is loaded from slot 0 and cleared bit-wise (no branch)
+    const uint32_t keep = slot_ok ? 0xffffffffu : 0u;
+    float st[KC][8];
+    {
+        Raw8<TS> sr[KC];
+        load_group(0);
+#pragma unroll
+        for (int k = 0; k < KC; ++k) sr[k].load(cs + (int64_t)pk[k] * N + n0);
+        __builtin_amdgcn_sched_barrier(0);   // keep every request of the group ahead of the waits
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+            sr[k].mask(keep);
+            sr[k].widen(st[k]);
         }
     }
 
-    const float Ah = A[h];
-    const float Dh = D ? D[h] : 0.0f;
-    for (int t = 0; t < T; ++t) {
-        const int64_t rt = (int64_t)r * T + t;
-        const float dtv = to_f32(dt[rt * H + h]);
-        const float decay = __expf(dtv * Ah);
-        float b8[8], c8[8];
-        const TIn *bp = B + (rt * G + g) * N + n0;
-        const TIn *cp = C + (rt * G + g) * N + n0;
-        if constexpr (sizeof(TIn) == 2) {
-            Vec16<TIn>::load(bp, b8);
-            Vec16<TIn>::load(cp, c8);
-        } else {
-            Vec16<TIn>::load(bp, b8);
-            Vec16<TIn>::load(bp + 4, b8 + 4);
-            Vec16<TIn>::load(cp, c8);
-            Vec16<TIn>::load(cp + 4, c8 + 4);
-        }
-        const TIn *xr = x + (rt * H + h) * P;
-        TIn *yr = y + (rt * H + h) * P;
+    // (T >= 1: the launcher enqueues nothing for T = 0, so the first group always
+    // runs and its loads are not sunk past a loop-entry test)
+    int t0 = 0;
+    do {
+        if (t0 > 0) load_group(t0);
 #pragma unroll
-        for (int k = 0; k < KC; ++k) {
-            const int q = tid + 256 * k;
-            if (q < NCH) {
-                const int p = q / CPR;
-                const float xv = to_f32(xr[p]);
-                const float u = dtv * xv;
+        for (int j = 0; j < TM; ++j) {
+            if (t0 + j >= T) break;
+            const int64_t rt = (int64_t)r * T + t0 + j;
+            const float decay = __expf(dtv[j] * Ah);
+            float b8[8], c8[8];
+            braw[j].widen(b8);
+            craw[j].widen(c8);
+            TIn *yr = y + (rt * H + h) * P;
+#pragma unroll
+            for (int k = 0; k < KC; ++k) {
+                const float u = dtv[j] * xv[j][k];
                 float part = 0.0f;
 #pragma unroll
                 for (int v = 0; v < 8; ++v) {
                     st[k][v] = decay * st[k][v] + u * b8[v];
                     part += c8[v] * st[k][v];
                 }
-                part = group_sum(part, CPR);
-                if ((tid % CPR) == 0) yr[p] = from_f32<TIn>(part + Dh * xv);
-                if (inter) {
+                part = row_sum<CPR>(part);
+                if ((tid % CPR) == 0 && tid + 256 * k < NCH)
+                    yr[pk[k]] = from_f32<TIn>(part + Dh * xv[j][k]);
+                if (inter && tid + 256 * k < NCH) {
                     // written once and read only by a later rollback: stream past the caches
-                    TS *ip = inter + (rt * H + h) * PN + (int64_t)p * N + n0;
+                    TS *ip = inter + (rt * H + h) * PN + (int64_t)pk[k] * N + n0;
                     store8_nt(ip, st[k]);
                 }
             }
         }
-    }
+        t0 += TM;
+    } while (t0 < T);
     if (!inter && slot_ok) {
 #pragma unroll
-        for (int k = 0; k < KC; ++k) {
-            const int q = tid + 256 * k;
-            if (q < NCH) {
-                const int p = q / CPR;
-                if constexpr (sizeof(TS) == 2) {
-                    Vec16<TS>::store(cs + (int64_t)p * N + n0, st[k]);
-                } else {
-                    Vec16<TS>::store(cs + (int64_t)p * N + n0, st[k]);
-                    Vec16<TS>::store(cs + (int64_t)p * N + n0 + 4, st[k] + 4);
-                }
-            }
-        }
+        for (int k = 0; k < KC; ++k)
+            if (tid + 256 * k < NCH) store_run<TS, 8>(cs + (int64_t)pk[k] * N + n0, st[k]);
     }
 }
 
@@ -151,11 +220,18 @@ static void launch_ssu_t(const DecodeDims &d, void *cache, const int32_t *idx, c
                          const float *D, void *y, void *inter, hipStream_t st)
 {
     dim3 grid(d.H, d.R);
-    hipLaunchKernelGGL((state_update_kernel<TIn, TS, P, N>), grid, dim3(256), 0, st, d.T, d.H, d.G,
-                       d.num_slots, static_cast<TS *>(cache), idx, static_cast<const TIn *>(x),
-                       static_cast<const TIn *>(dt), A, static_cast<const TIn *>(B),
-                       static_cast<const TIn *>(C), D, static_cast<TIn *>(y),
-                       static_cast<TS *>(inter));
+#define SSD_SSU_LAUNCH(TM)                                                                        \
+    hipLaunchKernelGGL((state_update_kernel<TIn, TS, P, N, TM>), grid, dim3(256), 0, st, d.T,     \
+                       d.H, d.G, d.num_slots, static_cast<TS *>(cache), idx,                      \
+                       static_cast<const TIn *>(x), static_cast<const TIn *>(dt), A,              \
+                       static_cast<const TIn *>(B), static_cast<const TIn *>(C), D,               \
+                       static_cast<TIn *>(y), static_cast<TS *>(inter))
+    // tokens per load group: the whole request when it has up to 4 tokens
+    if (d.T <= 1) SSD_SSU_LAUNCH(1);
+    else if (d.T <= 2) SSD_SSU_LAUNCH(2);
+    else if (d.T <= 3) SSD_SSU_LAUNCH(3);
+    else SSD_SSU_LAUNCH(4);
+#undef SSD_SSU_LAUNCH
 }
 
 template <typename TIn, typename TS>
