@@ -947,8 +947,10 @@ __device__ __forceinline__ void load_cb_frags(const bf16 *CBc, int Q, int rt, in
                                               uint4 *f)
 {
     const bf16 *base = CBc + ((int64_t)rt * (Q >> 5) * 64 + lane) * 8;
+    // steps past nk load step nk - 1 again (never used): no branch around a load
+    const int last = nk > 0 ? nk - 1 : 0;
 #pragma unroll
-    for (int ks = 0; ks < K; ++ks) f[ks] = ks < nk ? ld16(base + (int64_t)ks * 512) : zero16();
+    for (int ks = 0; ks < K; ++ks) f[ks] = ld16(base + (int64_t)(ks < last ? ks : last) * 512);
 }
 
 // One 16-row tile of the chunk scan (rows i0 .. i0 + 15) for one wave; see the
@@ -957,9 +959,9 @@ __device__ __forceinline__ void load_cb_frags(const bf16 *CBc, int Q, int rt, in
 template <int Q, int K, int KN>
 __device__ __forceinline__ void scan_row_tile(
     int i0, int nk, const uint4 *cbf, bool exact, int len, int lane,
-    const bf16 *Cb, int G, const float *scum, const float *sdt, const bf16 *xs, const bf16 *hs,
-    bf16 *yw, const bf16 *xsrc, int H, float Dh, bf16 *yout, const bf16 *CBc, int nrt, int nnk,
-    uint4 *ncf, bool prefetch_next)
+    rsrc_t rc, uint32_t crow, const float *scum, const float *sdt, const bf16 *xs, const bf16 *hs,
+    bf16 *yw, rsrc_t rx, uint32_t xrow, int H, float Dh, bf16 *yout, const bf16 *CBc, int nrt,
+    int nnk, uint4 *ncf, bool prefetch_next)
 {
     constexpr int P = 64, N = 128, LDX = kFastLD, LDH = N + 8;
     if (nk == 0) {
@@ -973,11 +975,11 @@ __device__ __forceinline__ void scan_row_tile(
     uint4 cr[N / 32];                    // C rows of the state term (raw bf16 A operand)
 #pragma unroll
     for (int kk = 0; kk < N / 32; ++kk)
-        cr[kk] = i < len ? ld16(Cb + (int64_t)i * G * N + 32 * kk + 8 * kg) : zero16();
+        cr[kk] = buf_ld16(rc, (uint32_t)i * crow + 64 * kk + 16 * kg);   // zeros past len
     uint4 xe[2];                         // x of the D x term: row r16, p = 32 k + 8 kg + 0..7
 #pragma unroll
     for (int k = 0; k < 2; ++k)
-        xe[k] = i < len ? ld16(xsrc + (int64_t)i * H * P + 32 * k + 8 * kg) : zero16();
+        xe[k] = buf_ld16(rx, (uint32_t)i * xrow + 64 * k + 16 * kg);     // zeros past len
 
     f32x4 acc[P / 16];
 #pragma unroll
@@ -1103,40 +1105,45 @@ void chunk_scan_fast_kernel(
     const int nkA = rtA < ntiles ? (16 * rtA + 15) / 32 + 1 : 0;
     const int nkB = rtB < ntiles ? (16 * rtB + 15) / 32 + 1 : 0;
 
-    // stage cum, dt, the entering state and x' (or x in exact mode)
-    const bf16 *xsrc = x + ((int64_t)ci.start * H + h) * P;
+    // stage cum, dt, the entering state and x' (or x in exact mode). x and C come
+    // through buffer resources ending at the chunk's last row: rows past it read as
+    // zeros, with no branch around the loads (a branch would make the compiler wait
+    // on each load where the branches join)
+    const uint32_t xrow = (uint32_t)H * P * 2, crow = (uint32_t)G * N * 2;
+    const rsrc_t rx = make_rsrc(x + ((int64_t)ci.start * H + h) * P, (uint32_t)(len - 1) * xrow + P * 2);
+    const rsrc_t rc = make_rsrc(C + ((int64_t)ci.start * G + g) * N, (uint32_t)(len - 1) * crow + N * 2);
+    // requests in the order they are needed (the wait counter is in order): cum and
+    // dt, the entering state, x, then the CB fragments of the larger row tile B
+    // (tile A's follow later)
+    const float *cumrow = cum + ((int64_t)h * max_chunks + c) * Q;
+    const float *dtrow = dtc + ((int64_t)h * max_chunks + c) * Q;
+    const int iq = tid < Q ? tid : Q - 1;          // 2 Q threads: one position each
+    const float cmv = cumrow[iq], dtv = dtrow[iq];
+    __builtin_amdgcn_sched_barrier(0);   // (the scheduler would otherwise move them last)
+    const bf16 *hin = entering + ((int64_t)c * H + h) * P * N;
+    uint4 hr[kHVec];
+#pragma unroll
+    for (int k = 0; k < kHVec; ++k) {
+        const int u = tid + nthr * k;
+        hr[k] = ld16(hin + (u >> 4) * N + 8 * (u & 15));
+    }
+    __builtin_amdgcn_sched_barrier(0);
     uint4 xr[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {        // Q rows x 8 vectors over 2 Q threads
         const int u = tid + nthr * k;
-        const int t = u >> 3, c8 = u & 7;
-        xr[k] = t < len ? ld16(xsrc + (int64_t)t * H * P + 8 * c8) : zero16();
+        xr[k] = buf_ld16(rx, (uint32_t)(u >> 3) * xrow + 16 * (u & 7));
     }
-    {
-        const bf16 *hin = entering + ((int64_t)c * H + h) * P * N;
-        uint4 hr[kHVec];
-#pragma unroll
-        for (int k = 0; k < kHVec; ++k) {
-            const int u = tid + nthr * k;
-            hr[k] = ld16(hin + (u >> 4) * N + 8 * (u & 15));
-        }
-        const float *cumrow = cum + ((int64_t)h * max_chunks + c) * Q;
-        const float *dtrow = dtc + ((int64_t)h * max_chunks + c) * Q;
-        for (int i = tid; i < Q; i += nthr) {
-            scum[i] = cumrow[i] * kLog2e;
-            sdt[i] = dtrow[i];
-        }
-#pragma unroll
-        for (int k = 0; k < kHVec; ++k) {
-            const int u = tid + nthr * k;
-            st16(hs + (u >> 4) * LDH + 8 * (u & 15), hr[k]);
-        }
-    }
-    // CB fragments (split K order) of the larger row tile B, requested now so
-    // that they arrive during the staging barriers; tile A's follow later
     const bf16 *CBc = CB + ((int64_t)c * G + g) * Q * Q;
     uint4 cbf[kStepsB];
     load_cb_frags<kStepsB>(CBc, Q, rtB, lane, nkB, cbf);
+    scum[iq] = cmv * kLog2e;          // (threads past Q rewrite position Q - 1 with the
+    sdt[iq] = dtv;                     //  same values: no branch, so the loads stay first)
+#pragma unroll
+    for (int k = 0; k < kHVec; ++k) {
+        const int u = tid + nthr * k;
+        st16(hs + (u >> 4) * LDH + 8 * (u & 15), hr[k]);
+    }
     __syncthreads();
     // scaling factors of x: G_j = exp(R_k - cum_j) dt_j; exact mode when a span is too large
     bool big = false;
@@ -1170,17 +1177,16 @@ void chunk_scan_fast_kernel(
     __syncthreads();
 
     const float Dh = D ? D[h] : 0.0f;
-    const bf16 *Cb = C + ((int64_t)ci.start * G + g) * N;
     bf16 *yw = ys + wave * P * kScanLDR;
 
     // tile B first (larger); tile A's CB fragments are requested once B's are consumed
     uint4 caf[kStepsA];
-    scan_row_tile<Q, kStepsB, kStepsA>(16 * rtB, nkB, cbf, exact, len, lane, Cb, G, scum, sdt,
-                                       xs, hs, yw, xsrc, H, Dh,
+    scan_row_tile<Q, kStepsB, kStepsA>(16 * rtB, nkB, cbf, exact, len, lane, rc, crow, scum, sdt,
+                                       xs, hs, yw, rx, xrow, H, Dh,
                                        y + ((int64_t)ci.start * H + h) * P, CBc, rtA, nkA, caf,
                                        true);
-    scan_row_tile<Q, kStepsA, kStepsA>(16 * rtA, nkA, caf, exact, len, lane, Cb, G, scum, sdt,
-                                       xs, hs, yw, xsrc, H, Dh,
+    scan_row_tile<Q, kStepsA, kStepsA>(16 * rtA, nkA, caf, exact, len, lane, rc, crow, scum, sdt,
+                                       xs, hs, yw, rx, xrow, H, Dh,
                                        y + ((int64_t)ci.start * H + h) * P, CBc, 0, 0, caf, false);
 }
 
