@@ -103,10 +103,13 @@ __device__ __forceinline__ void cumsum_wave(int H, int Q, int max_chunks, int c,
     const int E = (Q + kWave - 1) / kWave;  // positions per lane (<= 4)
     const float Ah = A[h];
     float vals[4], loc[4], run = 0.0f;
+    // (loads at clamped positions, zeroed after: no branch between a load and its use)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int i = lane * E + e;
-        vals[e] = (e < E && i < ci.len) ? to_f32(dt[(int64_t)(ci.start + i) * H + h]) : 0.0f;
+        const int ic = i < ci.len ? i : ci.len - 1;
+        const float v = to_f32(dt[(int64_t)(ci.start + ic) * H + h]);
+        vals[e] = (e < E && i < ci.len) ? v : 0.0f;
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -373,13 +376,17 @@ __device__ __forceinline__ void bmm_rows(int G, int Q, int c, int g, int z, cons
     const int i0 = z * 16;
     if (ci.len <= 0 || i0 >= ci.len) return;
 
+    // rows past the chunk's end are loaded at the last row and zeroed after the
+    // load (no branch between a load and its use)
     typename M::frag cf[NK];       // C rows i0 .. i0 + 15 (B operand)
     const int i = i0 + r16;
+    const int ic = i < ci.len ? i : ci.len - 1;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
         const int n = kk * M::K + kg * M::KPL;
-        cf[kk] = (i < ci.len && n < N) ? M::load(C + ((int64_t)(ci.start + i) * G + g) * N + n)
-                                       : M::zero();
+        const int nc = n < N ? n : 0;
+        const typename M::frag f = M::load(C + ((int64_t)(ci.start + ic) * G + g) * N + nc);
+        cf[kk] = (i < ci.len && n < N) ? f : M::zero();
     }
     TIn *cbc = CB + ((int64_t)c * G + g) * Q * Q;
     // bf16 (fragment order): the 16 x 32 blocks holding the diagonal are written
@@ -394,12 +401,14 @@ __device__ __forceinline__ void bmm_rows(int G, int Q, int c, int g, int z, cons
             continue;
         }
         const int j = jt * 16 + r16;
+        const int jcl = j < ci.len ? j : ci.len - 1;
         typename M::frag bfr[NK];  // B rows j (A operand)
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
             const int n = kk * M::K + kg * M::KPL;
-            bfr[kk] = (j < ci.len && n < N)
-                ? M::load(B + ((int64_t)(ci.start + j) * G + g) * N + n) : M::zero();
+            const int nc = n < N ? n : 0;
+            const typename M::frag f = M::load(B + ((int64_t)(ci.start + jcl) * G + g) * N + nc);
+            bfr[kk] = (j < ci.len && n < N) ? f : M::zero();
         }
         f32x4 acc = zero4();
 #pragma unroll
