@@ -7,6 +7,8 @@
 // Notation: chunk c = (seq, start, len) from the metadata, head h, group
 // g = h / (H / G), local token index i in [0, len), cum = inclusive cumsum of
 // dt * A_h inside the chunk.
+#include <type_traits>
+
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -316,39 +318,55 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
     const bool read_init = slot_ok && (has_init != nullptr && has_init[s] != 0);
     TS *cslot = cache + ((int64_t)(slot_ok ? slot : 0) * H + h) * PN + e;
 
-    float hs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (read_init) load4<TS>(cslot, hs);
+    // every load below is unconditional (a branch between a load and its use makes
+    // the compiler wait on the load right there): the initial state is loaded from
+    // slot 0 when there is none and cleared bit-wise; batch entries past the
+    // sequence's last chunk reload that chunk and are not used
+    float hs[4];
+    load4<TS>(cslot, hs);
+    const uint32_t keep = read_init ? 0xffffffffu : 0u;
 
     int c0 = meta[s], c1 = meta[s + 1];
     c0 = c0 < max_chunks ? c0 : max_chunks;
     c1 = c1 < max_chunks ? c1 : max_chunks;
-    // chunks in batches of kBatch: every chunk state of a batch is loaded before
-    // the sequential recurrence over the batch runs (kBatch loads in flight)
-    constexpr int kBatch = 16;
-    for (int cb = c0; cb < c1; cb += kBatch) {
-        const int nb = c1 - cb < kBatch ? c1 - cb : kBatch;
-        float sc[kBatch][4], dec[kBatch];
+    // chunks in batches of 16, then 4, then 1: every chunk state of a batch is
+    // requested before the sequential recurrence over it runs, and a batch never
+    // reaches past the sequence's last chunk (so its loads need no guard)
+    bool masked = false;
+    auto batch = [&](int cb, auto kb) {
+        constexpr int K = decltype(kb)::value;
+        float sc[K][4], dec[K];
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-            if (k < nb) {
-                const int c = cb + k;
-                load4<float>(states + ((int64_t)c * H + h) * PN + e, sc[k]);
-                const int len = meta[(S + 1) + 3 * c + 2];
-                dec[k] = len > 0 ? __expf(cum[((int64_t)h * max_chunks + c) * Q + len - 1]) : 1.0f;
-            }
+        for (int k = 0; k < K; ++k) {
+            const int c = cb + k;
+            load4<float>(states + ((int64_t)c * H + h) * PN + e, sc[k]);
+            const int len = meta[(S + 1) + 3 * c + 2];
+            const float cl = cum[((int64_t)h * max_chunks + c) * Q + (len > 0 ? len - 1 : 0)];
+            dec[k] = len > 0 ? __expf(cl) : 1.0f;
+        }
+        if (!masked) {     // the initial state is used only now, after the batch was requested
+#pragma unroll
+            for (int q = 0; q < 4; ++q) hs[q] = __uint_as_float(__float_as_uint(hs[q]) & keep);
+            masked = true;
         }
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-            if (k < nb) {
-                const int64_t off = ((int64_t)(cb + k) * H + h) * PN + e;
-                // the chunk state at `off` was loaded above, before the entering
-                // state (which may share its memory) is stored
-                store4<TE>(entering + off, hs);
+        for (int k = 0; k < K; ++k) {
+            const int64_t off = ((int64_t)(cb + k) * H + h) * PN + e;
+            // the chunk state at `off` was loaded above, before the entering
+            // state (which may share its memory) is stored
+            store4<TE>(entering + off, hs);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) hs[q] = dec[k] * hs[q] + sc[k][q];
-                if (ckpt) store4<TS>(ckpt + off, hs);
-            }
+            for (int q = 0; q < 4; ++q) hs[q] = dec[k] * hs[q] + sc[k][q];
+            if (ckpt) store4<TS>(ckpt + off, hs);
         }
+    };
+    int cb = c0;
+    for (; cb + 16 <= c1; cb += 16) batch(cb, std::integral_constant<int, 16>());
+    for (; cb + 4 <= c1; cb += 4) batch(cb, std::integral_constant<int, 4>());
+    for (; cb < c1; ++cb) batch(cb, std::integral_constant<int, 1>());
+    if (!masked) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hs[q] = __uint_as_float(__float_as_uint(hs[q]) & keep);
     }
     if (slot_ok) store4<TS>(cslot, hs);
 }
