@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (for scaling HBM counters)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the other prefill shapes (used for the profiling runs, so that "
+                         "every dispatch of a kernel has the headline shape)")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summaries from rocprofv3 output of this script "
                          "(no GPU work)")
@@ -179,11 +182,11 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, cmds):
 
 PROFILE_COMMANDS = [
     "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof/trace -o c1 -- "
-    "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline",
+    "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline --headline-only",
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof/fetch -o run -- "
-    "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration",
+    "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --headline-only --copy-calibration",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof/write -o run -- "
-    "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration",
+    "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --headline-only --copy-calibration",
 ]
 
 
@@ -318,6 +321,53 @@ def main():
                            "traffic": load_traffic("selective_state_update"),
                            "bytes": ssu_bytes}}
 
+    # ------------------------------------------------------------------ other prefill shapes
+    # (context, not the headline): the cached short continuation and the mixed varlen
+    # batch with checkpoints - the whole combined call, and the step-wise state passing
+    # kernel on its own bytes (chunk states in, entering states, initial / final states
+    # and checkpoints)
+    others = {}
+    other_cfgs = () if args.headline_only else (("cached_continuation_32x32", sy.C2),
+                                                  ("mixed_varlen_8seq_ckpt", sy.C3))
+    for cname, ocfg in other_cfgs:
+        oin = sy.make_prefill(ocfg)
+        oT, oS, oH, oP, oN, oG, oQ = (ocfg.total_tokens, ocfg.num_seqs, ocfg.nheads, ocfg.headdim,
+                                      ocfg.d_state, ocfg.ngroups, ocfg.chunk_size)
+        op = ssd.make_problem(oT, oS, oH, oP, oN, oG, oQ, ocfg.num_slots, ocfg.in_dtype,
+                              ocfg.state_dtype)
+        ox, odt, oA, oB, oC, oD = (t.to(dev) for t in (oin.x, oin.dt, oin.A, oin.B, oin.C, oin.D))
+        ocu, oidx = oin.cu_seqlens.to(dev), oin.state_indices.to(dev)
+        ohi = oin.has_initial.to(dev) if oin.has_initial is not None else None
+        ocache = (torch.randn(ocfg.num_slots, oH, oP, oN, device=dev, generator=gen) * 0.03
+                  ).to(ocfg.state_dtype)
+        omc = ssd.max_chunks(op)
+        ock = (torch.empty(omc, oH, oP, oN, dtype=ocfg.state_dtype, device=dev)
+               if ocfg.checkpoints else None)
+        oy = torch.empty(oT, oH, oP, dtype=ocfg.in_dtype, device=dev)
+        ows = ssd.alloc_workspace(op, dev)
+        comb_us = avg_us(lambda: ssd.ssd_combined_varlen(op, ox, odt, oA, oB, oC, oD, ocu, ocache,
+                                                         oidx, ohi, oy, ock, ows, stream))
+        obuf = ssd.alloc_step_buffers(op, dev)
+        ssd.ssd_chunk_cumsum(op, odt, oA, ocu, obuf["chunk_meta"], obuf["dA_cumsum"],
+                             obuf["dt_chunk"], stream)
+        ssd.ssd_chunk_state(op, ox, oB, obuf["chunk_meta"], obuf["dA_cumsum"], obuf["dt_chunk"],
+                            obuf["chunk_states"], stream)
+        sp_us = avg_us(lambda: ssd.ssd_state_passing(op, obuf["chunk_states"], obuf["dA_cumsum"],
+                                                     obuf["chunk_meta"], ocache, oidx, ohi,
+                                                     obuf["entering"], ock, stream))
+        onc = int(np.sum(-(-np.diff(oin.cu_seqlens.numpy()) // oQ)))   # chunks, ceil per seq
+        es_o = 2 if ocfg.state_dtype == torch.bfloat16 else 4
+        s_init = int(oin.has_initial.sum()) if oin.has_initial is not None else 0
+        sp_bytes = prefill_bytes(oT, oS, oH, oP, oN, oG, oQ, onc, 2, es_o, s_init,
+                                 ocfg.checkpoints)["state_passing"]
+        others[cname] = {
+            "tokens": oT, "seqs": oS, "combined_us": round(comb_us, 3),
+            "tokens_per_s": round(oT / (comb_us * 1e-6), 1),
+            "state_passing_step": {"avg_us": round(sp_us, 3), "bytes": sp_bytes,
+                                   "GBps": round(sp_bytes / (sp_us * 1e-6) / 1e9, 1),
+                                   "frac": round(sp_bytes / (sp_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}}
+        del ox, odt, oB, oC, oy, ows, obuf, ocache, ock
+
     # achievable HBM bandwidth on this machine, for context: a plain 1 GiB device copy
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -376,6 +426,7 @@ def main():
         "hbm_copy_GBps": round(copy_gbps, 1),
         "kernels": kernels,
         "decode": decode,
+        "other_prefill_shapes": others,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

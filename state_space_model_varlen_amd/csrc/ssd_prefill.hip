@@ -678,17 +678,20 @@ __global__ __launch_bounds__(256) void chunk_state_fast_kernel(
 
     // issue every global load of the chunk first: x rows and B half-rows, 8 vectors of
     // 8 bf16 per row, Q rows each -> Q / 32 vectors of each per thread (<= 8)
+    // (buffer resources ending at the chunk's last row: rows past it read as zeros,
+    // with no branch between a load and its use)
     constexpr int kVec = Q / 32;          // vectors of each tile per thread
     uint4 xr[kVec], br[kVec];
-    const bf16 *xsrc = x + ((int64_t)ci.start * H + h) * P;
-    const bf16 *bsrc = B + ((int64_t)ci.start * G + g) * N + nh * NH;
+    const uint32_t xrow = (uint32_t)H * P * 2, brow = (uint32_t)G * N * 2;
+    const rsrc_t rx = make_rsrc(x + ((int64_t)ci.start * H + h) * P, (uint32_t)(len - 1) * xrow + P * 2);
+    const rsrc_t rb = make_rsrc(B + ((int64_t)ci.start * G + g) * N + nh * NH,
+                                (uint32_t)(len - 1) * brow + NH * 2);
 #pragma unroll
     for (int k = 0; k < kVec; ++k) {
         const int u = tid + 256 * k;
-        const int t = u >> 3, c8 = u & 7;
-        const bool ok = t < len;
-        xr[k] = ok ? ld16(xsrc + (int64_t)t * H * P + 8 * c8) : zero16();
-        br[k] = ok ? ld16(bsrc + (int64_t)t * G * N + 8 * c8) : zero16();
+        const uint32_t t = u >> 3, c8 = u & 7;
+        xr[k] = buf_ld16(rx, t * xrow + 16 * c8);
+        br[k] = buf_ld16(rb, t * brow + 16 * c8);
     }
     const float *cumrow = cum + ((int64_t)h * max_chunks + c) * Q;
     const float *dtrow = dtc + ((int64_t)h * max_chunks + c) * Q;
