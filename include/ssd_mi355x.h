@@ -130,6 +130,8 @@ size_t ssd_workspace_bytes(const ssd_problem *p);  /* for ssd_combined_varlen */
  *                 [0..S]            chunk_cu
  *                 [S+1+3c+0,1,2]    sequence, first token, token count of chunk c
  *                                   (-1, 0, 0 for c >= nc)
+ *                 [S+1+3mc+s]       cu_seqlens[s] clamped to [0, T], s = 0..S
+ *                                   (mc = ssd_max_chunks)
  *   dA_cumsum   out, float32 [H, max_chunks, Q]: inclusive cumsum of dt*A_h over
  *               the chunk's tokens; positions past the chunk's end hold its last value
  *   dt_chunk    out, float32 [H, max_chunks, Q]: dt per chunk position, 0 past the end

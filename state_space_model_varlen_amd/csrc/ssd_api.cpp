@@ -103,7 +103,7 @@ Workspace workspace_layout(const ssd_problem *p)
     const size_t H = p->nheads, P = p->headdim, N = p->d_state, G = p->ngroups, Q = p->chunk_size;
     Workspace w;
     w.meta = 0;
-    w.cum = w.meta + round_up(sizeof(int32_t) * ((size_t)p->num_seqs + 1 + 3 * mc));
+    w.cum = w.meta + round_up(sizeof(int32_t) * (2 * ((size_t)p->num_seqs + 1) + 3 * mc));
     w.dt = w.cum + round_up(sizeof(float) * H * mc * Q);
     w.cb = w.dt + round_up(sizeof(float) * H * mc * Q);
     const size_t ein = p->in_dtype == SSD_BF16 ? 2 : 4;
@@ -145,7 +145,7 @@ int64_t ssd_max_chunks(const ssd_problem *p)
 int64_t ssd_chunk_meta_count(const ssd_problem *p)
 {
     if (check_problem(p) != SSD_OK) return 0;
-    return (int64_t)p->num_seqs + 1 + 3 * ssd_max_chunks(p);
+    return 2 * ((int64_t)p->num_seqs + 1) + 3 * ssd_max_chunks(p);
 }
 
 size_t ssd_workspace_bytes(const ssd_problem *p)

@@ -252,6 +252,9 @@ __device__ __forceinline__ int xcd_logical_block(int pid, int nblocks) {
 // Chunk metadata as written by the cumsum kernel (int32):
 //   meta[0 .. S]               chunk_cu
 //   meta[S + 1 + 3c + {0,1,2}] sequence, first token, token count of chunk c
+//   meta[S + 1 + 3 mc + s]     cu_seqlens[s] clamped to [0, T], s = 0..S
+//                              (mc = max_chunks): sequence s spans tokens
+//                              [meta[..s], max(meta[..s], meta[..s + 1]))
 struct ChunkInfo {
     int seq, start, len;
 };

@@ -35,7 +35,8 @@ __device__ __forceinline__ int wave_inclusive_sum_int(int v, int lane) {
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
 // Block-wide: locate chunk c among the sequences of cu_seqlens. Writes
-// chunk_cu to meta[0..S] when `publish_cu`. Returns (seq, k) through shared
+// chunk_cu to meta[0..S] and the clamped cu_seqlens after the chunk triples
+// when `publish_cu`. Returns (seq, k) through shared
 // memory: chunk c is chunk k of sequence seq, seq = -1 when c >= nc.
 __device__ void find_chunk(int T, int S, int Q, int max_chunks, const int32_t *__restrict__ cu,
                            int c, bool publish_cu, int32_t *__restrict__ meta, int *s_found,
@@ -67,7 +68,10 @@ __device__ void find_chunk(int T, int S, int Q, int max_chunks, const int32_t *_
         }
         const int first = running + wave_off + incl - cnt;  // chunk_cu[s]
         if (s < S) {
-            if (publish_cu) meta[s] = first < max_chunks ? first : max_chunks;
+            if (publish_cu) {
+                meta[s] = first < max_chunks ? first : max_chunks;
+                meta[(S + 1) + 3 * max_chunks + s] = clampi(cu[s], 0, T);
+            }
             if (cnt > 0 && c >= first && c < first + cnt) {
                 s_found[0] = s;
                 s_found[1] = c - first;
@@ -75,7 +79,10 @@ __device__ void find_chunk(int T, int S, int Q, int max_chunks, const int32_t *_
         }
         running += tile_tot;
     }
-    if (publish_cu && tid == 0) meta[S] = running < max_chunks ? running : max_chunks;
+    if (publish_cu && tid == 0) {
+        meta[S] = running < max_chunks ? running : max_chunks;
+        meta[(S + 1) + 3 * max_chunks + S] = clampi(cu[S], 0, T);
+    }
     __syncthreads();
 }
 
@@ -750,9 +757,9 @@ __global__ __launch_bounds__(256) void chunk_state_fast_kernel(
 //   entering[c] = H;   H <- exp(cum_last) H + sum_t x_t (w_t B_t)^T,
 //   w_t = exp(cum_last - cum_t) dt_t,
 // and checkpoints / the final state are written from the same registers, so
-// chunk states never go to memory. The tiles of the next DEPTH chunks are in
-// flight to registers (buffer loads that return zeros past the chunk's end)
-// while chunk c is contracted; x is staged as loaded, B scaled by w_t.
+// chunk states never go to memory. The tiles of chunk c + 1 are in flight to
+// registers (buffer loads that return zeros past the chunk's end) while chunk
+// c is contracted; x is staged as loaded, B scaled by w_t.
 constexpr int kScanLDX = 80;   // x row pitch in LDS (bf16): conflict-free transpose reads
 constexpr int kScanNSL = 64;   // state columns per block
 constexpr int kScanLDB = kScanNSL + 16;
@@ -765,7 +772,7 @@ template <int Q> struct StateScanRegs {
     float cl;                                          // cum at the chunk's last token
 };
 
-template <int Q, int DEPTH, bool CKPT, typename TS>
+template <int Q, bool CKPT, typename TS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
 void state_scan_fast_kernel(
     int S, int H, int G, int max_chunks, int num_slots, const bf16 *__restrict__ x,
@@ -792,29 +799,30 @@ void state_scan_fast_kernel(
     // this lane's state elements: row 16 pw + r16, columns n0 + 32 nh + 16 j + 4 kg + 0..3
     const int64_t run = (int64_t)(16 * pw + r16) * N + n0 + 32 * nh + 4 * kg;
 
+    // every per-sequence value is requested before any is used (one memory
+    // latency): chunk range, token range, slot, has-initial flag
+    const int tokoff = (S + 1) + 3 * max_chunks;
     int c0 = meta[s], c1 = meta[s + 1];
+    const int first = meta[tokoff + s];
+    int end = meta[tokoff + s + 1];
+    const int slot = idx[s];
+    // (with no flag array, a byte of idx stands in and the flag is ignored)
+    const uint8_t hflag = (has_init != nullptr ? has_init : reinterpret_cast<const uint8_t *>(idx))[s];
+    __builtin_amdgcn_sched_barrier(0);
     c0 = c0 < max_chunks ? c0 : max_chunks;
     c1 = c1 < max_chunks ? c1 : max_chunks;
-    const int slot = idx[s];
+    c1 = c1 > c0 ? c1 : c0;
+    end = end > first ? end : first;
     const bool slot_ok = slot >= 0 && slot < num_slots;
-    const bool read_init = slot_ok && (has_init != nullptr && has_init[s] != 0);
     TS *cslot = cache + ((int64_t)(slot_ok ? slot : 0) * H + h) * PN + run;
 
-    f32x4 acc[2];
+    // the initial state is loaded whatever the flag says (slot 0 stands in for
+    // a bad slot) and selected once the first chunk's loads are also out
+    float iv[2][4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (read_init) load4<TS>(cslot + 16 * j, v);
-        acc[j][0] = v[0]; acc[j][1] = v[1]; acc[j][2] = v[2]; acc[j][3] = v[3];
-    }
+    for (int j = 0; j < 2; ++j) load4<TS>(cslot + 16 * j, iv[j]);
+    f32x4 acc[2];
 
-    // token range of the sequence: chunk c starts at first + (c - c0) Q
-    int first = 0, end = 0;
-    if (c0 < c1) {
-        first = chunk_info(meta, S, c0).start;
-        const ChunkInfo la = chunk_info(meta, S, c1 - 1);
-        end = la.start + la.len;
-    }
     // byte offsets inside a chunk's tiles (the same for every chunk)
     const uint32_t xrow = (uint32_t)H * P * 2, brow = (uint32_t)G * N * 2;
     uint32_t xo[Regs::kXV], bo[Regs::kBV], to[Regs::kBV];
@@ -830,16 +838,27 @@ void state_scan_fast_kernel(
         to[k] = u < Q * 8 ? (uint32_t)(u >> 3) * 4 : 0xfffffff0u;
     }
 
+    // Loads of chunk c's tiles through buffer resources that end at the chunk's
+    // last row: rows past it read as zero. Past the last chunk (and for a
+    // sequence with no chunk) every resource is empty and nothing is read.
     auto fetch = [&](Regs &R, int c) {
-        c = c < c1 ? c : c1 - 1;     // past the last chunk: the last one again (unused)
+        const bool any = c < c1;
+        c = c < c1 ? c : c1 - 1;
+        c = c > c0 ? c : c0;
         const int st = first + (c - c0) * Q;
-        const int len = end - st < Q ? end - st : Q;
-        const rsrc_t rx = make_rsrc(x + ((int64_t)st * H + h) * P, (uint32_t)(len - 1) * xrow + P * 2);
+        int len = end - st < Q ? end - st : Q;
+        len = any ? len : 0;
+        const rsrc_t rx = make_rsrc(x + ((int64_t)st * H + h) * P,
+                                    any ? (uint32_t)(len - 1) * xrow + P * 2 : 0u);
         const rsrc_t rb = make_rsrc(B + ((int64_t)st * G + g) * N + n0,
-                                    (uint32_t)(len - 1) * brow + NSL * 2);
+                                    any ? (uint32_t)(len - 1) * brow + NSL * 2 : 0u);
         const int64_t row = ((int64_t)h * max_chunks + c) * Q;
-        const rsrc_t rc = make_rsrc(cum + row, (uint32_t)len * 4);
-        const rsrc_t rd = make_rsrc(dtc + row, (uint32_t)len * 4);
+        const rsrc_t rc = make_rsrc(cum + row, any ? (uint32_t)len * 4 : 0u);
+        const rsrc_t rd = make_rsrc(dtc + row, any ? (uint32_t)len * 4 : 0u);
+        // (the cumsum at the chunk's last token first: a vector load, since a
+        // scalar one would share its wait counter with the LDS reads of the
+        // MFMA phase and stall them on global latency)
+        R.cl = buf_ldf(rc, (uint32_t)(len - 1) * 4);
 #pragma unroll
         for (int k = 0; k < Regs::kXV; ++k) R.x[k] = buf_ld16(rx, xo[k]);
 #pragma unroll
@@ -848,12 +867,13 @@ void state_scan_fast_kernel(
             R.cm[k] = buf_ldf(rc, to[k]);
             R.dt[k] = buf_ldf(rd, to[k]);
         }
-        R.cl = cum[row + len - 1];
     };
 
-    // one iteration: stage chunk c from R into LDS, refill R with chunk c + DEPTH,
-    // then fold chunk c into the running state
+    // one iteration: stage chunk c from R into LDS, refill R with chunk c + 1,
+    // then fold chunk c into the running state. An empty sequence makes one pass
+    // over zero tiles (it changes nothing) with its stores switched off.
     auto step = [&](Regs &R, int c) {
+        const bool live = c < c1;
         const int st = first + (c - c0) * Q;
         const int len = end - st < Q ? end - st : Q;
         __syncthreads();   // the previous chunk's MFMA reads of xs / bs are done
@@ -879,55 +899,70 @@ void state_scan_fast_kernel(
             }
         }
         const float decay = __expf(R.cl);
-        fetch(R, c + DEPTH);
+        fetch(R, c + 1);
         __syncthreads();
 
         const int64_t off = ((int64_t)c * H + h) * PN + run;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            float v[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
-            store4<bf16>(entering + off + 16 * j, v);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[j][e] *= decay;
-        }
-        const int nk = (len + 31) >> 5;
-        // (unrolled by 2 only: fully unrolled, every fragment is loaded ahead and
-        // the registers of the next chunks' tiles spill)
-#pragma unroll 2
-        for (int ks = 0; ks < nk; ++ks) {
-            const bf16x8 xf = mfma_frag_tr_split(xs, LDX, 32 * ks, 16 * pw, lane);
+        if (live) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const bf16x8 bf = mfma_frag_tr_split(bs, LDB, 32 * ks, 32 * nh + 16 * j, lane);
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf, xf, acc[j], 0, 0, 0);
+                float v[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+                store4<bf16>(entering + off + 16 * j, v);
             }
         }
-        if constexpr (CKPT) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                float w[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
-                store4<TS>(ckpt + off + 16 * j, w);
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[j][e] *= decay;
+        // K steps of 32 tokens, software-pipelined: the fragments of step ks + 1
+        // are requested before the MFMAs of step ks
+        const int nk = (len + 31) >> 5;
+        bf16x8 xf = mfma_frag_tr_split(xs, LDX, 0, 16 * pw, lane);
+        bf16x8 bf[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bf[j] = mfma_frag_tr_split(bs, LDB, 0, 32 * nh + 16 * j, lane);
+        for (int ks = 1; ks < nk; ++ks) {
+            const bf16x8 xn = mfma_frag_tr_split(xs, LDX, 32 * ks, 16 * pw, lane);
+            bf16x8 bn[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                bn[j] = mfma_frag_tr_split(bs, LDB, 32 * ks, 32 * nh + 16 * j, lane);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], xf, acc[j], 0, 0, 0);
+            xf = xn;
+            bf[0] = bn[0];
+            bf[1] = bn[1];
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], xf, acc[j], 0, 0, 0);
+        if constexpr (CKPT) {
+            if (live) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    float w[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+                    store4<TS>(ckpt + off + 16 * j, w);
+                }
             }
         }
     };
 
-    // DEPTH register sets in flight: chunk c + DEPTH is requested while chunk c is
-    // folded in. The main loop is unrolled over the sets (each stays in registers)
-    // and no branch separates a load from its use, so the compiler's wait counts
-    // stay exact; the last chunks are done one by one after it.
-    Regs R[DEPTH];
-    if (c0 < c1) {
+    // The first chunk's tiles are requested together with the initial state; the
+    // loop body runs at least once, so no branch separates these loads from their
+    // use and the compiler's wait counts stay exact.
+    Regs R;
+    fetch(R, c0);
+    __builtin_amdgcn_sched_barrier(0);
+    const bool read_init = slot_ok && has_init != nullptr && hflag != 0;
 #pragma unroll
-        for (int d = 0; d < DEPTH; ++d) fetch(R[d], c0 + d);
-    }
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[j][e] = read_init ? iv[j][e] : 0.0f;
     int c = c0;
-    for (; c + DEPTH <= c1; c += DEPTH) {
-#pragma unroll
-        for (int d = 0; d < DEPTH; ++d) step(R[d], c + d);
-    }
-#pragma unroll
-    for (int d = 0; d < DEPTH - 1; ++d)
-        if (c + d < c1) step(R[d], c + d);
+    do {
+        step(R, c);
+    } while (++c < c1);
 
     if (slot_ok) {
 #pragma unroll
@@ -1423,7 +1458,7 @@ void launch_state_passing(const PrefillDims &d, const float *states, const float
     }
 }
 
-template <int Q, int DEPTH, bool CKPT, typename TS>
+template <int Q, bool CKPT, typename TS>
 static void launch_state_scan_k(const PrefillDims &d, const void *x, const void *B,
                                 const int32_t *meta, const float *cum, const float *dtc,
                                 void *cache, const int32_t *idx, const uint8_t *has_init,
@@ -1431,10 +1466,10 @@ static void launch_state_scan_k(const PrefillDims &d, const void *x, const void 
 {
     const size_t smem = (size_t)Q * (kScanLDX + kScanLDB) * sizeof(bf16);
     static size_t raised = 0;
-    allow_lds(reinterpret_cast<const void *>(&state_scan_fast_kernel<Q, DEPTH, CKPT, TS>), smem,
+    allow_lds(reinterpret_cast<const void *>(&state_scan_fast_kernel<Q, CKPT, TS>), smem,
               raised);
     const unsigned nblk = (unsigned)((int64_t)d.S * d.H * (128 / kScanNSL));
-    hipLaunchKernelGGL((state_scan_fast_kernel<Q, DEPTH, CKPT, TS>), dim3(nblk), dim3(512), smem,
+    hipLaunchKernelGGL((state_scan_fast_kernel<Q, CKPT, TS>), dim3(nblk), dim3(512), smem,
                        st, d.S, d.H, d.G, d.max_chunks, d.num_slots, static_cast<const bf16 *>(x),
                        static_cast<const bf16 *>(B), meta, cum, dtc, static_cast<TS *>(cache), idx,
                        has_init, static_cast<bf16 *>(entering), static_cast<TS *>(ckpt));
@@ -1446,13 +1481,12 @@ static void launch_state_scan_q(const PrefillDims &d, const void *x, const void 
                                 void *cache, const int32_t *idx, const uint8_t *has_init,
                                 void *entering, void *ckpt, hipStream_t st)
 {
-    constexpr int DEPTH = 1;
     if (ckpt)
-        launch_state_scan_k<Q, DEPTH, true, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init,
-                                                entering, ckpt, st);
+        launch_state_scan_k<Q, true, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering,
+                                         ckpt, st);
     else
-        launch_state_scan_k<Q, DEPTH, false, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init,
-                                                 entering, ckpt, st);
+        launch_state_scan_k<Q, false, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering,
+                                          ckpt, st);
 }
 
 template <typename TS>
