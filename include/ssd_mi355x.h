@@ -277,6 +277,67 @@ int selective_state_update(const ssu_problem *p, void *state_cache, const int32_
 int ssd_state_commit(const ssu_problem *p, void *state_cache, const int32_t *state_indices,
                      const void *intermediate_states, const int32_t *num_accepted, void *stream);
 
+/*
+ * ReplaySSM MTP decode (vLLM PR #52928, sections "Summary" and "Design": each
+ * layer keeps a checkpoint state and a ring of the inputs per slot, the
+ * accepted length moves a shared cursor before the next forward, and the
+ * checkpoint is rewritten only when the next verify window would not fit;
+ * vLLM PR #55688, "Summary": pending history is materialised into the
+ * checkpoint before a state is published). No state per draft token is
+ * written: a rollback is a cursor move.
+ *
+ * Storage per slot s (caller-owned, ring_len = W entries, W >= 2 T):
+ *   ckpt     [num_slots,H,P,N] state_dtype   checkpoint state (the state cache)
+ *   ring_x   [num_slots,W,H,P] in_dtype      inputs of the tokens since the
+ *   ring_dt  [num_slots,W,H]   in_dtype      checkpoint, ring order
+ *   ring_B   [num_slots,W,G,N] in_dtype
+ *   cursor   [num_slots,2]     int32         (start, n): the n accepted tokens
+ *            not yet in the checkpoint sit at ring positions (start + i) mod W,
+ *            i = 0..n-1. A slot whose checkpoint was just written by a prefill
+ *            needs cursor (any start, 0). Values out of range are clamped
+ *            (start to [0, W), n to [0, W - T]).
+ * The current state of slot s is the checkpoint followed by those n tokens.
+ * Requests of one call must use distinct slots.
+ */
+
+/*
+ * Verify step: per request r (slot s = state_indices[r]) and head h, rebuild
+ * the current state from ckpt[s] and the n history tokens, then run the T new
+ * tokens in float32, writing y_t for each and appending their x, dt, B to the
+ * ring at positions (start + n + t) mod W. When n + T > W - T (the window
+ * after this one might not fit) the rebuilt state is first rounded into
+ * ckpt[s]. The cursor is only read.
+ *   x, y [R,T,H,P]; dt [R,T,H]; B, C [R,T,G,N] in_dtype; A, D [H] float32
+ *   (D may be NULL)
+ */
+int ssd_replay_update(const ssu_problem *p, int32_t ring_len, void *ckpt, void *ring_x,
+                      void *ring_dt, void *ring_B, const int32_t *cursor,
+                      const int32_t *state_indices, const void *x, const void *dt,
+                      const float *A, const void *B, const void *C, const float *D, void *y,
+                      void *stream);
+
+/*
+ * Cursor move after sampling: num_accepted[r] in [0, T) accepted draft tokens
+ * (the target token is always kept), so 1 + num_accepted[r] tokens of the
+ * last window join the history. With (start, n) the cursor the verify step
+ * read: if that step rewrote the checkpoint (n + T > W - T) the cursor becomes
+ * ((start + n) mod W, 1 + a), else (start, n + 1 + a). T is the window of that
+ * verify step (p->tokens_per_req). Out-of-range counts are clamped.
+ */
+int ssd_replay_advance(const ssu_problem *p, int32_t ring_len, int32_t *cursor,
+                       const int32_t *state_indices, const int32_t *num_accepted, void *stream);
+
+/*
+ * Materialise: for every request r, fold the history of slot state_indices[r]
+ * into its checkpoint (ckpt[s] = rounded current state) and set its cursor to
+ * ((start + n) mod W, 0). Two launches on the stream (the cursor is reset
+ * after every head has read it). p->tokens_per_req only bounds n (W - T).
+ */
+int ssd_replay_materialize(const ssu_problem *p, int32_t ring_len, void *ckpt,
+                           const void *ring_x, const void *ring_dt, const void *ring_B,
+                           int32_t *cursor, const int32_t *state_indices, const float *A,
+                           void *stream);
+
 #ifdef __cplusplus
 }
 #endif

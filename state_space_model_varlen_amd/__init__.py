@@ -68,6 +68,9 @@ _SIGS = {
     "ssd_combined_varlen": ([_pp] + [_vp] * 13 + [ctypes.c_size_t, _vp], ctypes.c_int),
     "selective_state_update": ([_up] + [_vp] * 11, ctypes.c_int),
     "ssd_state_commit": ([_up] + [_vp] * 5, ctypes.c_int),
+    "ssd_replay_update": ([_up, ctypes.c_int32] + [_vp] * 14, ctypes.c_int),
+    "ssd_replay_advance": ([_up, ctypes.c_int32] + [_vp] * 4, ctypes.c_int),
+    "ssd_replay_materialize": ([_up, ctypes.c_int32] + [_vp] * 8, ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -305,6 +308,55 @@ def ssd_state_commit(p: ssu_problem, state_cache, state_indices, intermediate_st
 
 
 # ---------------------------------------------------------------------------
+# ReplaySSM decode: checkpoint + input rings per slot (see include/ssd_mi355x.h)
+
+def _ring_ptrs(p: ssu_problem, W: int, ring_x, ring_dt, ring_B):
+    H, P, N, G = p.nheads, p.headdim, p.d_state, p.ngroups
+    ti = _TORCH[p.in_dtype]
+    return (_ptr(ring_x, "ring_x", ti, (p.num_slots, W, H, P)),
+            _ptr(ring_dt, "ring_dt", ti, (p.num_slots, W, H)),
+            _ptr(ring_B, "ring_B", ti, (p.num_slots, W, G, N)))
+
+
+def ssd_replay_update(p: ssu_problem, ring_len: int, ckpt, ring_x, ring_dt, ring_B, cursor,
+                      state_indices, x, dt, A, B, C, D, y, stream=None):
+    R, T, H, P, N, G = (p.num_reqs, p.tokens_per_req, p.nheads, p.headdim, p.d_state, p.ngroups)
+    ti, ts = _TORCH[p.in_dtype], _TORCH[p.state_dtype]
+    rc = _lib.ssd_replay_update(
+        ctypes.byref(p), int(ring_len), _ptr(ckpt, "ckpt", ts, (p.num_slots, H, P, N)),
+        *_ring_ptrs(p, ring_len, ring_x, ring_dt, ring_B),
+        _ptr(cursor, "cursor", torch.int32, (p.num_slots, 2)),
+        _ptr(state_indices, "state_indices", torch.int32, (R,)),
+        _ptr(x, "x", ti, (R, T, H, P)), _ptr(dt, "dt", ti, (R, T, H)),
+        _ptr(A, "A", torch.float32, (H,)), _ptr(B, "B", ti, (R, T, G, N)),
+        _ptr(C, "C", ti, (R, T, G, N)), _ptr(D, "D", torch.float32, (H,), optional=True),
+        _ptr(y, "y", ti, (R, T, H, P)), _stream(stream))
+    _check("ssd_replay_update", rc)
+
+
+def ssd_replay_advance(p: ssu_problem, ring_len: int, cursor, state_indices, num_accepted,
+                       stream=None):
+    rc = _lib.ssd_replay_advance(
+        ctypes.byref(p), int(ring_len), _ptr(cursor, "cursor", torch.int32, (p.num_slots, 2)),
+        _ptr(state_indices, "state_indices", torch.int32, (p.num_reqs,)),
+        _ptr(num_accepted, "num_accepted", torch.int32, (p.num_reqs,)), _stream(stream))
+    _check("ssd_replay_advance", rc)
+
+
+def ssd_replay_materialize(p: ssu_problem, ring_len: int, ckpt, ring_x, ring_dt, ring_B, cursor,
+                           state_indices, A, stream=None):
+    H, P, N = p.nheads, p.headdim, p.d_state
+    ts = _TORCH[p.state_dtype]
+    rc = _lib.ssd_replay_materialize(
+        ctypes.byref(p), int(ring_len), _ptr(ckpt, "ckpt", ts, (p.num_slots, H, P, N)),
+        *_ring_ptrs(p, ring_len, ring_x, ring_dt, ring_B),
+        _ptr(cursor, "cursor", torch.int32, (p.num_slots, 2)),
+        _ptr(state_indices, "state_indices", torch.int32, (p.num_reqs,)),
+        _ptr(A, "A", torch.float32, (H,)), _stream(stream))
+    _check("ssd_replay_materialize", rc)
+
+
+# ---------------------------------------------------------------------------
 # allocation helpers (torch plumbing; no arithmetic)
 
 def alloc_workspace(p: ssd_problem, device="cuda") -> torch.Tensor:
@@ -321,3 +373,13 @@ def alloc_step_buffers(p: ssd_problem, device="cuda") -> dict:
         chunk_states=torch.empty((mc, H, P, N), **f),
         entering=torch.empty((mc, H, P, N), dtype=_TORCH[p.in_dtype], device=device),
         CB=torch.empty((mc, G, Q, Q), dtype=_TORCH[p.in_dtype], device=device))
+
+
+def alloc_replay_rings(p: ssu_problem, ring_len: int, device="cuda") -> dict:
+    """Input rings and cursors of a ReplaySSM layer, zeroed (every history empty)."""
+    H, P, N, G, S = p.nheads, p.headdim, p.d_state, p.ngroups, p.num_slots
+    ti = _TORCH[p.in_dtype]
+    return dict(ring_x=torch.zeros((S, ring_len, H, P), dtype=ti, device=device),
+                ring_dt=torch.zeros((S, ring_len, H), dtype=ti, device=device),
+                ring_B=torch.zeros((S, ring_len, G, N), dtype=ti, device=device),
+                cursor=torch.zeros((S, 2), dtype=torch.int32, device=device))

@@ -313,4 +313,57 @@ int ssd_state_commit(const ssu_problem *p, void *state_cache, const int32_t *sta
     return launch_status();
 }
 
+static int check_replay(const ssu_problem *p, int32_t ring_len)
+{
+    int rc = check_ssu(p);
+    if (rc) return rc;
+    // the history (W - T entries) must hold a whole window: W >= 2 T
+    if (ring_len <= 0 || (int64_t)ring_len < 2 * (int64_t)p->tokens_per_req) return SSD_ERR_SHAPE;
+    return SSD_OK;
+}
+
+int ssd_replay_update(const ssu_problem *p, int32_t ring_len, void *ckpt, void *ring_x,
+                      void *ring_dt, void *ring_B, const int32_t *cursor,
+                      const int32_t *state_indices, const void *x, const void *dt,
+                      const float *A, const void *B, const void *C, const float *D, void *y,
+                      void *stream)
+{
+    int rc = check_replay(p, ring_len);
+    if (rc) return rc;
+    if (!ckpt || !ring_x || !ring_dt || !ring_B || !cursor || !state_indices || !x || !dt || !A ||
+        !B || !C || !y)
+        return SSD_ERR_NULL;
+    if (!aligned16(ckpt) || !aligned16(ring_x) || !aligned16(ring_B) || !aligned16(x) ||
+        !aligned16(B) || !aligned16(C))
+        return SSD_ERR_ALIGN;
+    ssd::launch_replay_update(dims_of(p), ring_len, ckpt, ring_x, ring_dt, ring_B, cursor,
+                              state_indices, x, dt, A, B, C, D, y, stream);
+    return launch_status();
+}
+
+int ssd_replay_advance(const ssu_problem *p, int32_t ring_len, int32_t *cursor,
+                       const int32_t *state_indices, const int32_t *num_accepted, void *stream)
+{
+    int rc = check_replay(p, ring_len);
+    if (rc) return rc;
+    if (!cursor || !state_indices || !num_accepted) return SSD_ERR_NULL;
+    ssd::launch_replay_advance(dims_of(p), ring_len, cursor, state_indices, num_accepted, stream);
+    return launch_status();
+}
+
+int ssd_replay_materialize(const ssu_problem *p, int32_t ring_len, void *ckpt,
+                           const void *ring_x, const void *ring_dt, const void *ring_B,
+                           int32_t *cursor, const int32_t *state_indices, const float *A,
+                           void *stream)
+{
+    int rc = check_replay(p, ring_len);
+    if (rc) return rc;
+    if (!ckpt || !ring_x || !ring_dt || !ring_B || !cursor || !state_indices || !A)
+        return SSD_ERR_NULL;
+    if (!aligned16(ckpt) || !aligned16(ring_x) || !aligned16(ring_B)) return SSD_ERR_ALIGN;
+    ssd::launch_replay_materialize(dims_of(p), ring_len, ckpt, ring_x, ring_dt, ring_B, cursor,
+                                   state_indices, A, stream);
+    return launch_status();
+}
+
 }  // extern "C"

@@ -53,4 +53,15 @@ void launch_state_update(const DecodeDims &d, void *cache, const int32_t *idx, c
 void launch_state_commit(const DecodeDims &d, void *cache, const int32_t *idx, const void *inter,
                          const int32_t *accepted, void *stream);
 
+// ReplaySSM decode: verify step, cursor move after sampling, materialisation.
+void launch_replay_update(const DecodeDims &d, int W, void *ckpt, void *rx, void *rdt, void *rB,
+                          const int32_t *cursor, const int32_t *idx, const void *x, const void *dt,
+                          const float *A, const void *B, const void *C, const float *D, void *y,
+                          void *stream);
+void launch_replay_advance(const DecodeDims &d, int W, int32_t *cursor, const int32_t *idx,
+                           const int32_t *accepted, void *stream);
+void launch_replay_materialize(const DecodeDims &d, int W, void *ckpt, const void *rx,
+                               const void *rdt, const void *rB, int32_t *cursor,
+                               const int32_t *idx, const float *A, void *stream);
+
 }  // namespace ssd

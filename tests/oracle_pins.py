@@ -19,6 +19,7 @@ import torch
 
 import oracle
 from oracle import chunked, dual
+from oracle import replay as oracle_replay
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -312,8 +313,58 @@ def pin_bf16_rounding(lib=None):
     np.testing.assert_array_equal(got, want)
 
 
+def pin_replay_matches_recurrence(lib=None, replay=None):
+    """ReplaySSM (checkpoint, input rings, cursor) against the plain recurrence over the
+    kept tokens. Storage in float64, so nothing is rounded: every window's y and the
+    materialised checkpoint must agree to 1e-12. The accepted pattern is fixed so the
+    checkpoint schedule and cursors can be worked by hand: T = 3, W = 9 (history
+    capacity L = 6), accepted drafts 2, 0, 1, 2, 2, 0, 1 give histories n = 0, 3, 4,
+    2, 5, 3, 4 at the verify steps, checkpoints rewritten at steps 2, 4, 6 (n + T > L)
+    and the cursor (4, 2) at the end, (6, 0) after materialising."""
+    rp = replay or oracle_replay
+    R, T, H, P, N, G, W = 3, 3, 4, 3, 5, 2, 9
+    g = np.random.default_rng(131)
+    idx = np.array([3, 0, 4], dtype=np.int64)
+    init = g.standard_normal((5, H, P, N)) * 0.3
+    layer = rp.ReplayLayer(torch.from_numpy(init), W, G, torch.float64)
+    A = -g.uniform(1.0, 4.0, H)
+    D = g.standard_normal(H)
+    pattern = [2, 0, 1, 2, 2, 0, 1]
+    want_ckpt_steps = {2, 4, 6}
+    kept = [[] for _ in range(R)]            # (x, dt, B, C) of every kept token
+    for step, a in enumerate(pattern):
+        x = g.standard_normal((R, T, H, P))
+        dt = g.uniform(1e-3, 0.4, (R, T, H))
+        B = g.standard_normal((R, T, G, N)) / math.sqrt(N)
+        C = g.standard_normal((R, T, G, N)) / math.sqrt(N)
+        before = layer.ckpt.clone()
+        y = rp.replay_update(layer, idx, *(torch.from_numpy(v) for v in (x, dt)),
+                             torch.from_numpy(A), torch.from_numpy(B), torch.from_numpy(C),
+                             torch.from_numpy(D))
+        changed = not torch.equal(before[idx], layer.ckpt[idx])
+        assert changed == (step in want_ckpt_steps), (step, changed)
+        for r in range(R):
+            seq = kept[r] + [(x[r, t], dt[r, t], B[r, t], C[r, t]) for t in range(T)]
+            xs, dts, Bs, Cs = (np.stack([e[i] for e in seq]) for i in range(4))
+            yr, _, _ = oracle.recurrence(xs, dts, A, Bs, Cs, D, [0, len(seq)], 8,
+                                         init=init[idx[r]][None], lib=lib)
+            np.testing.assert_allclose(y[r], yr[-T:], rtol=1e-12, atol=1e-13)
+            kept[r] += seq[len(kept[r]):len(kept[r]) + 1 + a]
+        rp.replay_advance(layer, idx, np.full(R, a), T)
+    assert all(tuple(layer.cursor[s]) == (4, 2) for s in idx)
+    rp.replay_materialize(layer, idx, torch.from_numpy(A))
+    assert all(tuple(layer.cursor[s]) == (6, 0) for s in idx)
+    for r in range(R):
+        xs, dts, Bs, Cs = (np.stack([e[i] for e in kept[r]]) for i in range(4))
+        _, fr, _ = oracle.recurrence(xs, dts, A, Bs, Cs, D, [0, len(kept[r])], 8,
+                                     init=init[idx[r]][None], lib=lib)
+        np.testing.assert_allclose(layer.ckpt[idx[r]].numpy(), fr[0], rtol=1e-12, atol=1e-13)
+    untouched = [1, 2]
+    np.testing.assert_array_equal(layer.ckpt[untouched].numpy(), init[untouched])
+
+
 ALL_PINS = [pin_hand_worked, pin_single_token_closed_form, pin_cumsum_reduction, pin_pure_decay,
             pin_skip_only, pin_linearity, pin_dual_form, pin_continued_prefill,
             pin_varlen_packing, pin_checkpoints_are_truncated_finals,
             pin_chunk_size_independence, pin_state_update_replay, pin_cache_semantics,
-            pin_bf16_rounding]
+            pin_bf16_rounding, pin_replay_matches_recurrence]

@@ -144,3 +144,31 @@ def test_binding_checks_shapes_before_the_library():
     x = torch.empty(10, 4, 16)   # CPU tensor: rejected by the binding
     with pytest.raises(ValueError):
         ssd.ssd_chunk_state(p, x, x, x, x, x, x)
+
+
+def test_replay_validation():
+    """ReplaySSM entry points: ring length at least two windows, NULL and alignment
+    checks on the host (nothing is launched in these cases)."""
+    lib = ssd._lib
+    ok = ctypes.c_void_p(256)
+    up = ssd.make_ssu_problem(2, 3, 8, 64, 128, 2, 4, torch.bfloat16, torch.bfloat16)
+    args = [ok] * 11 + [None, ok, None]  # ckpt .. C, D = NULL, y, stream
+    assert lib.ssd_replay_update(ctypes.byref(up), 5, *args) == 2   # W < 2 T
+    assert lib.ssd_replay_update(ctypes.byref(up), 0, *args) == 2
+    a = list(args)
+    a[0] = None                                                     # ckpt
+    assert lib.ssd_replay_update(ctypes.byref(up), 6, *a) == 1
+    a = list(args)
+    a[3] = None                                                     # ring_B
+    assert lib.ssd_replay_update(ctypes.byref(up), 6, *a) == 1
+    a = list(args)
+    a[1] = ctypes.c_void_p(264)                                     # ring_x misaligned
+    assert lib.ssd_replay_update(ctypes.byref(up), 6, *a) == 7
+    assert lib.ssd_replay_advance(ctypes.byref(up), 5, ok, ok, ok, None) == 2
+    assert lib.ssd_replay_advance(ctypes.byref(up), 6, ok, ok, None, None) == 1
+    assert lib.ssd_replay_materialize(ctypes.byref(up), 6, ok, ok, ok, ok, ok, ok, None,
+                                      None) == 1
+    assert lib.ssd_replay_materialize(ctypes.byref(up), 6, ctypes.c_void_p(8), ok, ok, ok, ok,
+                                      ok, ok, None) == 7
+    un = ssd.make_ssu_problem(2, 3, 8, 32, 128, 2, 4, torch.bfloat16, torch.bfloat16)
+    assert lib.ssd_replay_advance(ctypes.byref(un), 6, ok, ok, ok, None) == 4

@@ -110,3 +110,35 @@ def test_chunked_mutation_is_caught(mut, monkeypatch):
     monkeypatch.setattr(chunked, name, bad)
     with pytest.raises(AssertionError):
         oracle_pins.pin_chunk_size_independence()
+
+
+# Planted mistakes in the ReplaySSM state machine (oracle/replay.py): each edits one
+# line of a copy of the module, loaded under another name; the ReplaySSM pin must fail.
+import importlib.util  # noqa: E402
+
+REPLAY_SRC = os.path.join(os.path.dirname(oracle.__file__), "replay.py")
+REPLAY_MUTATIONS = [
+    ("target_token_not_kept", "layer.cursor[int(s)] = (start, n + 1 + int(a))",
+     "layer.cursor[int(s)] = (start, n + int(a))"),
+    ("window_overwrites_history", "pos = (start + n + t) % layer.W", "pos = (start + t) % layer.W"),
+    ("last_history_token_skipped", "    for i in range(n):\n", "    for i in range(n - 1):\n"),
+    ("checkpoint_one_step_late", "        if n + T > L:\n            layer.ckpt[s]",
+     "        if n + T > L + 1:\n            layer.ckpt[s]"),
+    ("cursor_not_moved_on_checkpoint", "layer.cursor[int(s)] = ((start + n) % layer.W, 1 + int(a))",
+     "layer.cursor[int(s)] = (start, n + 1 + int(a))"),
+]
+
+
+@pytest.mark.parametrize("mut", REPLAY_MUTATIONS, ids=lambda m: m[0])
+def test_replay_mutation_is_caught(mut, tmp_path):
+    name, old, new = mut
+    src = open(REPLAY_SRC).read()
+    assert src.count(old) == 1, f"mutation {name}: text not found once in oracle/replay.py"
+    src = src.replace(old, new).replace("from . import f64, round_to", "from oracle import f64, round_to")
+    path = tmp_path / f"replay_{name}.py"
+    path.write_text(src)
+    spec = importlib.util.spec_from_file_location(f"replay_{name}", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    with pytest.raises((AssertionError, IndexError)):
+        oracle_pins.pin_replay_matches_recurrence(replay=mod)
