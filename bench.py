@@ -321,6 +321,63 @@ def main():
                            "traffic": load_traffic("selective_state_update"),
                            "bytes": ssu_bytes}}
 
+    # ------------------------------------------------------------------ ReplaySSM decode
+    # The same MTP verify workload without stored draft states: checkpoint + input
+    # rings per slot (16 entries: up to 13 history tokens and one 3-token window).
+    # One step = verify + cursor move, over a seeded sequence of accepted counts,
+    # timed after enough steps that every request's history is in its steady cycle.
+    import dataclasses
+    W = 16
+    rings = ssd.alloc_replay_rings(up, W, dev)
+    rck = dcache.clone()
+    nsteps = 24
+    acc_seq = [sy.make_decode(dataclasses.replace(dcfg, seed=dcfg.seed + 1000 * k)).num_accepted
+               .to(dev) for k in range(nsteps)]
+    ry = torch.empty_like(dy)
+
+    def replay_step(k):
+        ssd.ssd_replay_update(up, W, rck, rings["ring_x"], rings["ring_dt"], rings["ring_B"],
+                              rings["cursor"], didx, dx, ddt, dA, dB, dC, dD, ry, stream)
+        ssd.ssd_replay_advance(up, W, rings["cursor"], didx, acc_seq[k], stream)
+
+    for k in range(nsteps):          # warm-up: histories reach their steady cycle
+        replay_step(k)
+    torch.cuda.synchronize()
+    ra, rb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(20_000_000)
+    ra.record(stream)
+    for k in range(nsteps):
+        replay_step(k)
+    rb.record(stream)
+    torch.cuda.synchronize()
+    replay_us = ra.elapsed_time(rb) * 1e3 / nsteps
+    # algorithmic bytes of the timed steps: the cursor rule replayed on the host
+    L = W - TT
+    hist = np.zeros(R, dtype=np.int64)
+    per_tok = (DH * DP + DH + DG * DN) * 2            # x, dt, B of one token (bf16)
+    state_b = DH * DP * DN * es
+    replay_bytes, hist_sum = 0, 0
+    for k in range(2 * nsteps):
+        ck = hist + TT > L
+        if k >= nsteps:
+            hist_sum += int(hist.sum())
+            replay_bytes += int(R * state_b + hist.sum() * per_tok
+                                + R * TT * (DH * DP + DH + 2 * DG * DN + DH * DP) * 2
+                                + R * TT * per_tok + ck.sum() * state_b)
+        a = acc_seq[k % nsteps].cpu().numpy()
+        hist = np.where(ck, 1 + a, hist + 1 + a)
+    replay_bytes //= nsteps
+    replay = {"workload": "mtp_verify_replayssm R=128 T=3 H=128 P=64 N=128 G=8 bf16, ring 16",
+              "metric": "decode updates/s", "value": round(R * TT / (replay_us * 1e-6), 1),
+              "unit": "updates/s", "avg_us_per_step": round(replay_us, 3),
+              "mean_history_tokens": round(hist_sum / (nsteps * R), 2),
+              "roofline": {"kernel": "replay_update + replay_advance", "bound": "hbm",
+                           "achieved": round(replay_bytes / (replay_us * 1e-6) / 1e9, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(replay_bytes / (replay_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                           "bytes": replay_bytes}}
+    del rings, rck
+
     # ------------------------------------------------------------------ other prefill shapes
     # (context, not the headline): the cached short continuation and the mixed varlen
     # batch with checkpoints - the whole combined call, and the step-wise state passing
@@ -426,6 +483,7 @@ def main():
         "hbm_copy_GBps": round(copy_gbps, 1),
         "kernels": kernels,
         "decode": decode,
+        "decode_replayssm": replay,
         "other_prefill_shapes": others,
         "cpu_baseline": cpu,
     }

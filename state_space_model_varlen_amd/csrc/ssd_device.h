@@ -97,6 +97,13 @@ template <> struct Mma<float> {
     __device__ __forceinline__ static frag load(const float *p) { return *p; }
 };
 
+// LDS writes of a wave made visible to the same wave's later reads.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ f32x4 zero4() {
     f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
     return z;

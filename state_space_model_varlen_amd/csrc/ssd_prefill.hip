@@ -996,12 +996,6 @@ void state_scan_fast_kernel(
 constexpr float kMaxSpan = 60.0f;    // natural-log units
 constexpr int kScanLDR = 20;         // p-major y tile pitch (bf16) of the epilogue
 
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 

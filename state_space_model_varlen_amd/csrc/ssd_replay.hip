@@ -203,6 +203,238 @@ __global__ __launch_bounds__(256) void replay_update_kernel(
     } while (t0 < T);
 }
 
+// Verify step for bf16 inputs and checkpoints, P = 64, N = 128, T <= 4 and
+// W <= 16 KT. Block (h, r) of 4 waves; wave w owns state rows p = 16 w .. + 15.
+// Taking the history and the window as one run of tokens k = 0 .. n + T - 1
+// (history first) with lambda_k = A sum_{k' <= k} dt_k', every output is the
+// dual (quadratic) form of the recurrence over that run:
+//   y_t = exp(lambda_{n+t}) (C_t . ckpt) + D x_t
+//         + sum_{k <= n+t} exp(lambda_{n+t} - lambda_k) dt_k (C_t . B_k) x_k.
+// C . ckpt and C . B are MFMA products (the checkpoint rows are read straight
+// from memory as operand fragments); the decay weights and the sums over at
+// most 16 KT tokens are a few scalars per lane. No state is built per token:
+// the state after the history is formed only when it becomes the checkpoint.
+template <int KT>
+__global__ __launch_bounds__(256) void replay_update_fast_kernel(
+    int T, int H, int G, int num_slots, int W, bf16 *ckpt, bf16 *ring_x, bf16 *ring_dt,
+    bf16 *ring_B, const int32_t *__restrict__ cursor, const int32_t *__restrict__ idx,
+    const bf16 *__restrict__ x, const bf16 *__restrict__ dt, const float *__restrict__ A,
+    const bf16 *__restrict__ B, const bf16 *__restrict__ C, const float *__restrict__ D,
+    bf16 *__restrict__ y)
+{
+    constexpr int P = 64, N = 128, NK = 16 * KT;   // token slots: history + window
+    __shared__ float s_dt[4][NK];                  // per wave: dt_k
+    __shared__ float s_lam[4][NK];                 // lambda_k
+    __shared__ float s_g[4][16][NK];               // decay-weighted C_t . B_k
+    __shared__ float s_y[4][16][16];               // C_t . ckpt, row p
+    __shared__ __attribute__((aligned(16))) bf16 s_b[4][NK][N];   // B_k (checkpoint rewrite)
+    const int h = blockIdx.x, r = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int g = h / (H / G);
+    const int L = W - T;
+
+    const int p = 16 * w + r16;
+    // ---- every load first, in dependency order (no branch between a load and
+    // its use): the window's C (A fragments, row t = r16; rows past T read as
+    // zero) needs nothing, the checkpoint and the cursor need the slot, the ring
+    // loads need the cursor
+    const rsrc_t rc = make_rsrc(C + ((int64_t)r * T * G + g) * N, (uint32_t)((T - 1) * G * N + N) * 2);
+    uint4 cf[4], kf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) cf[ks] = buf_ld16(rc, (uint32_t)(r16 * G * N + 32 * ks + 8 * kg) * 2);
+    const int slot = idx[r];
+    const bool slot_ok = slot >= 0 && slot < num_slots;
+    const int64_t cs = slot_ok ? slot : 0;
+    // (an invalid slot reads slot 0's cursor and checkpoint, both discarded)
+    const int cur0 = cursor[2 * cs], cur1 = cursor[2 * cs + 1];
+    const bf16 *ckrow = ckpt + ((cs * H + h) * P + p) * N;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kf[ks] = *reinterpret_cast<const uint4 *>(ckrow + 32 * ks + 8 * kg);
+    const float Ah = A[h];
+    const float Dh = D ? D[h] : 0.0f;
+    __builtin_amdgcn_sched_barrier(0);
+    const int start = clamp_int(cur0, 0, W - 1);
+    const int n = slot_ok ? clamp_int(cur1, 0, L) : 0;
+    const bool ck = slot_ok && n + T > L;
+    auto ring_pos = [&](int k) {
+        const int q = start + k;
+        return q < W ? q : q - W;
+    };
+    // B and dt of token k = 16 kt + r16: ring for k < n, window token k - n, zero after
+    uint4 bfr[KT][4];
+    bf16 dtraw[KT];
+    float dtk[KT];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+        const int k = 16 * kt + r16;
+        const bool hist = k < n;
+        const int tw = clamp_int(k - n, 0, T - 1);
+        const int64_t e = cs * W + ring_pos(hist ? k : 0);
+        const bf16 *bsrc = hist ? ring_B + (e * G + g) * N : B + (((int64_t)r * T + tw) * G + g) * N;
+        const bf16 *dsrc = hist ? ring_dt + e * H + h : dt + ((int64_t)r * T + tw) * H + h;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            bfr[kt][ks] = *reinterpret_cast<const uint4 *>(bsrc + 32 * ks + 8 * kg);
+        dtraw[kt] = *dsrc;
+    }
+    // x_k[p] for every token slot, and x_t[p] of this lane's window token t = kg
+    float xk[NK];
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+        const bool hist = k < n;
+        const int tw = clamp_int(k - n, 0, T - 1);
+        const bf16 *src = hist ? ring_x + ((cs * W + ring_pos(k)) * H + h) * P + p
+                               : x + (((int64_t)r * T + tw) * H + h) * P + p;
+        xk[k] = to_f32(*src);
+    }
+    const int tl = kg < T ? kg : T - 1;
+    const bf16 xtraw = x[(((int64_t)r * T + tl) * H + h) * P + p];
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- masks, then the MFMA products (C_t . ckpt)[t][p] and (C_t . B_k)[t][k]
+    const uint32_t kslot = slot_ok ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        kf[ks].x &= kslot; kf[ks].y &= kslot; kf[ks].z &= kslot; kf[ks].w &= kslot;
+    }
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+        const int k = 16 * kt + r16;
+        const uint32_t live = k < n + T ? 0xffffffffu : 0u;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            bfr[kt][ks].x &= live; bfr[kt][ks].y &= live; bfr[kt][ks].z &= live; bfr[kt][ks].w &= live;
+        }
+        dtk[kt] = k < n + T ? to_f32(dtraw[kt]) : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < NK; ++k) xk[k] = k < n + T ? xk[k] : 0.0f;
+    f32x4 ys = zero4(), cb[KT];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        ys = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cf[ks]),
+                                                     __builtin_bit_cast(bf16x8, kf[ks]), ys, 0, 0, 0);
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+        cb[kt] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            cb[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cf[ks]),
+                                                             __builtin_bit_cast(bf16x8, bfr[kt][ks]),
+                                                             cb[kt], 0, 0, 0);
+    }
+
+    // ---- lambda_k (a running sum over the token slots, read back from LDS)
+    float *sdt = s_dt[w], *slam = s_lam[w];
+    if (kg == 0) {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) sdt[16 * kt + r16] = dtk[kt];
+    }
+    wave_lds_sync();
+    float lk[KT];
+    {
+        float run = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+            run += Ah * sdt[k];
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+                if (k == 16 * kt + r16) lk[kt] = run;
+        }
+    }
+    if (kg == 0) {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) slam[16 * kt + r16] = lk[kt];
+    }
+    wave_lds_sync();
+    // weights G[t][k] = [k <= n + t] exp(lambda_{n+t} - lambda_k) dt_k CB[t][k], t = 4 kg + v
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int t = 4 * kg + v;
+        const float ln = slam[n + t < NK ? n + t : NK - 1];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+            const int k = 16 * kt + r16;
+            const float gv = __expf(ln - lk[kt]) * dtk[kt] * cb[kt][v];
+            s_g[w][t][k] = (t < T && k <= n + t) ? gv : 0.0f;
+        }
+        s_y[w][t][r16] = ys[v];
+    }
+    wave_lds_sync();
+
+    // ---- y_t[p], lane (p, t = kg)
+    if (kg < T) {
+        const int t = kg;
+        float acc = __expf(slam[n + t]) * s_y[w][t][r16];
+#pragma unroll
+        for (int k = 0; k < NK; ++k) acc += s_g[w][t][k] * xk[k];
+        acc += Dh * to_f32(xtraw);
+        y[(((int64_t)r * T + t) * H + h) * P + p] = from_f32<bf16>(acc);
+    }
+
+    // ---- the window's inputs join the ring (B by the group's first head, dt by wave 0)
+    if (slot_ok) {
+        if (kg < T) ring_x[((cs * W + ring_pos(n + kg)) * H + h) * P + p] = xtraw;
+        if (w == 0) {
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                const int k = 16 * kt + r16;
+                if (k >= n && k < n + T) {
+                    const int64_t e = cs * W + ring_pos(k);
+                    if (kg == 0) ring_dt[e * H + h] = dtraw[kt];
+                    if (h % (H / G) == 0) {
+#pragma unroll
+                        for (int ks = 0; ks < 4; ++ks)
+                            *reinterpret_cast<uint4 *>(ring_B + (e * G + g) * N + 32 * ks + 8 * kg) =
+                                bfr[kt][ks];
+                    }
+                }
+            }
+        }
+    }
+
+    // ---- checkpoint rewrite: the state after the history,
+    //   exp(lambda_{n-1}) ckpt + sum_{i<n} exp(lambda_{n-1} - lambda_i) dt_i x_i (x) B_i
+    if (ck) {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                *reinterpret_cast<uint4 *>(&s_b[w][16 * kt + r16][32 * ks + 8 * kg]) = bfr[kt][ks];
+        wave_lds_sync();
+        const float lh = n > 0 ? slam[n - 1] : 0.0f;
+        const float a0 = __expf(lh);
+        float st[4][8];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            Raw8<bf16> kr;
+            kr.w = kf[ks];
+            kr.widen(st[ks]);
+#pragma unroll
+            for (int v = 0; v < 8; ++v) st[ks][v] *= a0;
+        }
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            if (i < n) {
+                const float u = __expf(lh - slam[i]) * sdt[i] * xk[i];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    Raw8<bf16> br;
+                    br.w = *reinterpret_cast<const uint4 *>(&s_b[w][i][32 * ks + 8 * kg]);
+                    float b8[8];
+                    br.widen(b8);
+#pragma unroll
+                    for (int v = 0; v < 8; ++v) st[ks][v] += u * b8[v];
+                }
+            }
+        }
+        bf16 *dst = ckpt + ((cs * H + h) * P + p) * N;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) store_run<bf16, 8>(dst + 32 * ks + 8 * kg, st[ks]);
+    }
+}
+
 // Materialise: ckpt[s] = checkpoint followed by the history. Block (h, r).
 template <typename TIn, typename TS, int P, int N>
 __global__ __launch_bounds__(256) void replay_materialize_kernel(
@@ -350,8 +582,21 @@ void launch_replay_update(const DecodeDims &d, int W, void *ckpt, void *rx, void
                           void *stream)
 {
     if (d.R <= 0 || d.T <= 0) return;
-    dispatch<UpdateOp>(d, W, ckpt, rx, rdt, rB, cursor, idx, x, dt, A, B, C, D, y,
-                       reinterpret_cast<hipStream_t>(stream));
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (d.in_bf16 && d.state_bf16 && d.P == 64 && d.N == 128 && d.T <= 4 && W <= 32) {
+#define SSD_REPLAY_FAST(KT)                                                                       \
+    hipLaunchKernelGGL((replay_update_fast_kernel<KT>), dim3(d.H, d.R), dim3(256), 0, st, d.T,    \
+                       d.H, d.G, d.num_slots, W, static_cast<bf16 *>(ckpt), static_cast<bf16 *>(rx), \
+                       static_cast<bf16 *>(rdt), static_cast<bf16 *>(rB), cursor, idx,            \
+                       static_cast<const bf16 *>(x), static_cast<const bf16 *>(dt), A,            \
+                       static_cast<const bf16 *>(B), static_cast<const bf16 *>(C), D,             \
+                       static_cast<bf16 *>(y))
+        if (W <= 16) SSD_REPLAY_FAST(1);
+        else SSD_REPLAY_FAST(2);
+#undef SSD_REPLAY_FAST
+        return;
+    }
+    dispatch<UpdateOp>(d, W, ckpt, rx, rdt, rB, cursor, idx, x, dt, A, B, C, D, y, st);
 }
 
 void launch_replay_advance(const DecodeDims &d, int W, int32_t *cursor, const int32_t *idx,

@@ -87,6 +87,9 @@ CASES = [
     (3, 2, 4, 16, 16, 1, 5, F32, F32),
     (5, 4, 4, 64, 16, 2, 8, BF16, F32),     # W = 2 T: a checkpoint at every other step
     (2, 1, 6, 16, 128, 3, 4, F32, BF16),    # plain decode (no drafts)
+    (3, 4, 8, 64, 128, 2, 20, BF16, BF16),  # bf16 fast path with 32 token slots
+    (4, 4, 4, 64, 128, 4, 8, BF16, BF16),   # bf16 fast path, W = 2 T
+    (3, 2, 8, 64, 128, 8, 40, BF16, BF16),  # bf16, ring longer than the fast path takes
 ]
 
 
