@@ -108,6 +108,20 @@ typedef struct {
     int32_t state_dtype;    /* ssd_dtype of the state cache and the intermediate states */
 } ssu_problem;
 
+/*
+ * The layer's step-size preprocessing, fused into the kernels that read dt:
+ *   dt = min(max(softplus(dt_raw + dt_bias[h]), dt_min), dt_max)
+ * in float32, softplus(v) = log(1 + exp(v)) (v itself above 20). The step
+ * size is defined this way in the workload of vLLM PR #52928 ("Summary": the
+ * same kernels with the model's input conventions) and the pages' test
+ * inputs; dt_raw is then the pre-activation value in in_dtype.
+ */
+typedef struct {
+    const float *dt_bias; /* [H] float32 on the device, or NULL (no bias) */
+    float dt_min;         /* lower clamp (0 for none) */
+    float dt_max;         /* upper clamp (a huge value for none); dt_min <= dt_max */
+} ssd_dt_transform;
+
 /* SSD_ABI_VERSION of the built library. */
 int ssd_abi_version(void);
 
@@ -276,6 +290,57 @@ int selective_state_update(const ssu_problem *p, void *state_cache, const int32_
  */
 int ssd_state_commit(const ssu_problem *p, void *state_cache, const int32_t *state_indices,
                      const void *intermediate_states, const int32_t *num_accepted, void *stream);
+
+/*
+ * Step 1 with the dt preprocessing: as ssd_chunk_cumsum with dt_raw in place
+ * of dt; dt_chunk receives the preprocessed float32 step sizes, so steps 2-5
+ * are unchanged. dt_transform must not be NULL.
+ */
+int ssd_chunk_cumsum_dt(const ssd_problem *p, const ssd_dt_transform *dt_transform,
+                        const void *dt_raw, const float *A, const int32_t *cu_seqlens,
+                        int32_t *chunk_meta, float *dA_cumsum, float *dt_chunk, void *stream);
+
+/*
+ * ssd_combined_varlen with the dt preprocessing applied in step 1.
+ */
+int ssd_combined_varlen_dt(const ssd_problem *p, const ssd_dt_transform *dt_transform,
+                           const void *x, const void *dt_raw, const float *A, const void *B,
+                           const void *C, const float *D, const int32_t *cu_seqlens,
+                           void *state_cache, const int32_t *state_indices,
+                           const uint8_t *has_initial_state, void *y, void *checkpoints,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Packed-varlen MTP verify (vLLM PR #52928, section "Summary": variable-length
+ * batches use the packed cu_seqlens interface) with optional dt preprocessing.
+ * Request r owns tokens cu_seqlens[r] .. cu_seqlens[r+1]-1 of the packed
+ * arrays (any count, 0 included: a request with no token changes nothing);
+ * otherwise as selective_state_update, with intermediate_states indexed by
+ * packed token.
+ *   total_tokens     rows of the packed arrays (T_tot)
+ *   cu_seqlens       [R+1] int32 on the device, non-decreasing (values are
+ *                    clamped to [0, T_tot] on the device)
+ *   x, y [T_tot,H,P]; dt [T_tot,H]; B, C [T_tot,G,N] in_dtype
+ *   intermediate_states [T_tot,H,P,N] state_dtype or NULL
+ *   dt_transform     NULL: dt as given; else dt is dt_raw, preprocessed
+ * p->tokens_per_req is a hint only (the most tokens of a request; >= 1).
+ */
+int selective_state_update_varlen(const ssu_problem *p, int32_t total_tokens,
+                                  const int32_t *cu_seqlens,
+                                  const ssd_dt_transform *dt_transform, void *state_cache,
+                                  const int32_t *state_indices, const void *x, const void *dt,
+                                  const float *A, const void *B, const void *C, const float *D,
+                                  void *y, void *intermediate_states, void *stream);
+
+/*
+ * Rollback after a packed-varlen verify: for every request r with
+ * 0 <= num_accepted[r] < (its token count), copy
+ * intermediate_states[cu_seqlens[r] + num_accepted[r]] into its slot.
+ */
+int ssd_state_commit_varlen(const ssu_problem *p, int32_t total_tokens,
+                            const int32_t *cu_seqlens, void *state_cache,
+                            const int32_t *state_indices, const void *intermediate_states,
+                            const int32_t *num_accepted, void *stream);
 
 /*
  * ReplaySSM MTP decode (vLLM PR #52928, sections "Summary" and "Design": each

@@ -192,6 +192,47 @@ def state_update(cache: torch.Tensor, state_indices, x, dt, A, B, C, D, keep_sta
     return dict(y=y, states=states, final=final, cache=after)
 
 
+def dt_preprocess(dt_raw, dt_bias, dt_min: float, dt_max: float) -> np.ndarray:
+    """The layer's step-size preprocessing in float64 (the step size of the pages'
+    workload, vLLM PR #52928 "Summary"): clamp(softplus(dt_raw + dt_bias_h),
+    dt_min, dt_max), softplus(v) = log(1 + exp(v)), taken as v itself above 20
+    (the kernels' convention). dt_raw [..., H]; dt_bias [H] or None."""
+    v = f64(dt_raw)
+    if dt_bias is not None:
+        v = v + f64(dt_bias)
+    sp = np.where(v > 20.0, v, np.log1p(np.exp(np.minimum(v, 20.0))))
+    return np.minimum(np.maximum(sp, float(dt_min)), float(dt_max))
+
+
+def state_update_varlen(cache: torch.Tensor, state_indices, cu_seqlens, x, dt, A, B, C, D,
+                        keep_states: bool, lib=None):
+    """Packed-varlen verify: request r owns packed tokens cu[r] .. cu[r+1]-1 and
+    continues from cache[state_indices[r]]; each request is the state update above
+    over its own tokens (a request with no token changes nothing).
+
+    x [Tt,H,P], dt [Tt,H], B/C [Tt,G,N]. Returns dict(y [Tt,H,P], states
+    [Tt,H,P,N] or None, cache after the call)."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    x, dt, B, C = f64(x), f64(dt), f64(B), f64(C)
+    Tt, H, P = x.shape
+    N = B.shape[2]
+    y = np.zeros((Tt, H, P))
+    states = np.zeros((Tt, H, P, N)) if keep_states else None
+    after = cache.clone()
+    for r, slot in enumerate(np.asarray(state_indices, dtype=np.int64)):
+        a, b = int(cu[r]), int(cu[r + 1])
+        if b <= a:
+            continue
+        out = state_update(cache, [slot], x[None, a:b], dt[None, a:b], A, B[None, a:b],
+                           C[None, a:b], D, keep_states, lib=lib)
+        y[a:b] = out["y"][0]
+        if keep_states:
+            states[a:b] = out["states"][0]
+        else:
+            after[int(slot)] = out["cache"][int(slot)]
+    return dict(y=y, states=states, cache=after)
+
+
 def commit(cache: torch.Tensor, state_indices, replay: torch.Tensor, num_accepted) -> torch.Tensor:
     """Rollback to the accepted count: cache[idx[r]] = replay[r, a_r] (a copy)."""
     after = cache.clone()

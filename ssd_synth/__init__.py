@@ -134,15 +134,16 @@ def layer_params(seed: int, nheads: int):
 
 
 def token_block(g: np.random.Generator, ntok: int, nheads: int, headdim: int, ngroups: int,
-                d_state: int, dt_bias: np.ndarray):
-    """x [T,H,P], dt [T,H], B [T,G,N], C [T,G,N] in float64, drawn in this order."""
+                d_state: int, dt_bias: np.ndarray, with_raw: bool = False):
+    """x [T,H,P], dt [T,H], B [T,G,N], C [T,G,N] in float64, drawn in this order;
+    with_raw also returns z [T,H], the pre-activation draw behind dt."""
     x = g.standard_normal((ntok, nheads, headdim))
     z = g.standard_normal((ntok, nheads))
     dt = np.clip(_softplus(z + dt_bias[None, :]), DT_MIN, DT_MAX)
     scale = 1.0 / math.sqrt(d_state)
     B = g.standard_normal((ntok, ngroups, d_state)) * scale
     C = g.standard_normal((ntok, ngroups, d_state)) * scale
-    return x, dt, B, C
+    return (x, dt, B, C, z) if with_raw else (x, dt, B, C)
 
 
 @dataclasses.dataclass
@@ -158,6 +159,7 @@ class PrefillInputs:
     state_indices: torch.Tensor  # [S] int32
     has_initial: Optional[torch.Tensor]  # [S] uint8 or None
     dt_bias: np.ndarray = None
+    dt_raw: torch.Tensor = None  # [T,H] in_dtype: z, the pre-activation draw behind dt
 
     def prefix_tokens(self, s: int):
         """(x, dt, B, C) of sequence s's seeded prefix (in_dtype), or None when the
@@ -177,7 +179,7 @@ def make_prefill(cfg: PrefillConfig, seqlens: Optional[Sequence[int]] = None) ->
     H, P, N, G = cfg.nheads, cfg.headdim, cfg.d_state, cfg.ngroups
     T = int(sum(lens))
     A, dt_bias, D = layer_params(cfg.seed, H)
-    x, dt, B, C = token_block(_rng(cfg.seed, 1), T, H, P, G, N, dt_bias)
+    x, dt, B, C, z = token_block(_rng(cfg.seed, 1), T, H, P, G, N, dt_bias, with_raw=True)
     cu = np.zeros(len(lens) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(lens)
     perm = _rng(cfg.seed, 2).permutation(cfg.num_slots).astype(np.int32)
@@ -192,7 +194,7 @@ def make_prefill(cfg: PrefillConfig, seqlens: Optional[Sequence[int]] = None) ->
         A=to_dtype(A, torch.float32), B=to_dtype(B, cfg.in_dtype), C=to_dtype(C, cfg.in_dtype),
         D=to_dtype(D, torch.float32),
         cu_seqlens=torch.from_numpy(cu), state_indices=torch.from_numpy(idx.copy()),
-        has_initial=has_init, dt_bias=dt_bias)
+        has_initial=has_init, dt_bias=dt_bias, dt_raw=to_dtype(z, cfg.in_dtype))
 
 
 @dataclasses.dataclass
@@ -207,6 +209,7 @@ class DecodeInputs:
     state_indices: torch.Tensor  # [R] int32
     num_accepted: torch.Tensor   # [R] int32 in [0, T)
     dt_bias: np.ndarray = None
+    dt_raw: torch.Tensor = None  # [R,T,H] in_dtype: z, the pre-activation draw behind dt
 
     def prefix_tokens(self, r: int):
         """(x [L,H,P], dt [L,H], B [L,G,N], C [L,G,N]) of request r's seeded prefix."""
@@ -220,7 +223,7 @@ def make_decode(cfg: DecodeConfig, num_reqs: Optional[int] = None) -> DecodeInpu
     R = cfg.num_reqs if num_reqs is None else int(num_reqs)
     T, H, P, N, G = cfg.tokens_per_req, cfg.nheads, cfg.headdim, cfg.d_state, cfg.ngroups
     A, dt_bias, D = layer_params(cfg.seed, H)
-    x, dt, B, C = token_block(_rng(cfg.seed, 1), R * T, H, P, G, N, dt_bias)
+    x, dt, B, C, z = token_block(_rng(cfg.seed, 1), R * T, H, P, G, N, dt_bias, with_raw=True)
     perm = _rng(cfg.seed, 2).permutation(cfg.num_slots).astype(np.int32)
     acc = _rng(cfg.seed, 4).integers(0, T, size=R).astype(np.int32)
     return DecodeInputs(
@@ -232,7 +235,8 @@ def make_decode(cfg: DecodeConfig, num_reqs: Optional[int] = None) -> DecodeInpu
         C=to_dtype(C.reshape(R, T, G, N), cfg.in_dtype),
         D=to_dtype(D, torch.float32),
         state_indices=torch.from_numpy(perm[:R].copy()),
-        num_accepted=torch.from_numpy(acc), dt_bias=dt_bias)
+        num_accepted=torch.from_numpy(acc), dt_bias=dt_bias,
+        dt_raw=to_dtype(z.reshape(R, T, H), cfg.in_dtype))
 
 
 def random_problem(seed: int, seqlens: Sequence[int], nheads: int, headdim: int, d_state: int,

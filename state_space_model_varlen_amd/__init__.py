@@ -50,9 +50,15 @@ class ssu_problem(ctypes.Structure):
         "in_dtype", "state_dtype")]
 
 
+class ssd_dt_transform(ctypes.Structure):
+    _fields_ = [("dt_bias", ctypes.c_void_p), ("dt_min", ctypes.c_float),
+                ("dt_max", ctypes.c_float)]
+
+
 _vp = ctypes.c_void_p
 _pp = ctypes.POINTER(ssd_problem)
 _up = ctypes.POINTER(ssu_problem)
+_tp = ctypes.POINTER(ssd_dt_transform)
 _SIGS = {
     "ssd_abi_version": ([], ctypes.c_int),
     "ssd_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -68,6 +74,10 @@ _SIGS = {
     "ssd_combined_varlen": ([_pp] + [_vp] * 13 + [ctypes.c_size_t, _vp], ctypes.c_int),
     "selective_state_update": ([_up] + [_vp] * 11, ctypes.c_int),
     "ssd_state_commit": ([_up] + [_vp] * 5, ctypes.c_int),
+    "ssd_chunk_cumsum_dt": ([_pp, _tp] + [_vp] * 7, ctypes.c_int),
+    "ssd_combined_varlen_dt": ([_pp, _tp] + [_vp] * 13 + [ctypes.c_size_t, _vp], ctypes.c_int),
+    "selective_state_update_varlen": ([_up, ctypes.c_int32, _vp, _tp] + [_vp] * 11, ctypes.c_int),
+    "ssd_state_commit_varlen": ([_up, ctypes.c_int32] + [_vp] * 6, ctypes.c_int),
     "ssd_replay_update": ([_up, ctypes.c_int32] + [_vp] * 14, ctypes.c_int),
     "ssd_replay_advance": ([_up, ctypes.c_int32] + [_vp] * 4, ctypes.c_int),
     "ssd_replay_materialize": ([_up, ctypes.c_int32] + [_vp] * 8, ctypes.c_int),
@@ -305,6 +315,91 @@ def ssd_state_commit(p: ssu_problem, state_cache, state_indices, intermediate_st
         _ptr(intermediate_states, "intermediate_states", ts, (R, T, H, P, N)),
         _ptr(num_accepted, "num_accepted", torch.int32, (R,)), _stream(stream))
     _check("ssd_state_commit", rc)
+
+
+# ---------------------------------------------------------------------------
+# dt preprocessing fused into the kernels, packed-varlen MTP verify
+
+def make_dt_transform(dt_bias, dt_min: float, dt_max: float) -> ssd_dt_transform:
+    """dt = clamp(softplus(dt_raw + dt_bias[h]), dt_min, dt_max). dt_bias: [H] float32
+    GPU tensor or None; the returned struct holds a reference to it, so the device
+    memory stays valid as long as the struct is alive."""
+    t = ssd_dt_transform()
+    t.dt_bias = None if dt_bias is None else _ptr(dt_bias, "dt_bias", torch.float32)
+    t.dt_min, t.dt_max = float(dt_min), float(dt_max)
+    t._dt_bias_tensor = dt_bias
+    return t
+
+
+def ssd_chunk_cumsum_dt(p: ssd_problem, dt_transform: ssd_dt_transform, dt_raw, A, cu_seqlens,
+                        chunk_meta, dA_cumsum, dt_chunk, stream=None):
+    T, S, H, P, N, G, Q, mc = _dims(p)
+    ti = _TORCH[p.in_dtype]
+    rc = _lib.ssd_chunk_cumsum_dt(
+        ctypes.byref(p), ctypes.byref(dt_transform), _ptr(dt_raw, "dt_raw", ti, (T, H)),
+        _ptr(A, "A", torch.float32, (H,)), _ptr(cu_seqlens, "cu_seqlens", torch.int32, (S + 1,)),
+        _ptr(chunk_meta, "chunk_meta", torch.int32, (chunk_meta_count(p),)),
+        _ptr(dA_cumsum, "dA_cumsum", torch.float32, (H, mc, Q)),
+        _ptr(dt_chunk, "dt_chunk", torch.float32, (H, mc, Q)), _stream(stream))
+    _check("ssd_chunk_cumsum_dt", rc)
+
+
+def ssd_combined_varlen_dt(p: ssd_problem, dt_transform: ssd_dt_transform, x, dt_raw, A, B, C, D,
+                           cu_seqlens, state_cache, state_indices, has_initial_state, y,
+                           checkpoints, workspace, stream=None):
+    T, S, H, P, N, G, Q, mc = _dims(p)
+    ti, ts = _TORCH[p.in_dtype], _TORCH[p.state_dtype]
+    if workspace is None or workspace.dtype != torch.uint8 or workspace.dim() != 1:
+        raise ValueError("workspace must be a 1-D uint8 GPU tensor")
+    rc = _lib.ssd_combined_varlen_dt(
+        ctypes.byref(p), ctypes.byref(dt_transform), _ptr(x, "x", ti, (T, H, P)),
+        _ptr(dt_raw, "dt_raw", ti, (T, H)), _ptr(A, "A", torch.float32, (H,)),
+        _ptr(B, "B", ti, (T, G, N)), _ptr(C, "C", ti, (T, G, N)),
+        _ptr(D, "D", torch.float32, (H,), optional=True),
+        _ptr(cu_seqlens, "cu_seqlens", torch.int32, (S + 1,)),
+        _ptr(state_cache, "state_cache", ts, (p.num_slots, H, P, N)),
+        _ptr(state_indices, "state_indices", torch.int32, (S,)),
+        _ptr(has_initial_state, "has_initial_state", torch.uint8, (S,), optional=True),
+        _ptr(y, "y", ti, (T, H, P)),
+        _ptr(checkpoints, "checkpoints", ts, (mc, H, P, N), optional=True),
+        _ptr(workspace, "workspace", torch.uint8), ctypes.c_size_t(workspace.numel()),
+        _stream(stream))
+    _check("ssd_combined_varlen_dt", rc)
+
+
+def selective_state_update_varlen(p: ssu_problem, cu_seqlens, state_cache, state_indices, x, dt,
+                                  A, B, C, D, y, intermediate_states=None, dt_transform=None,
+                                  stream=None):
+    """Packed-varlen verify: x [T_tot,H,P] etc., request r owning rows cu[r] .. cu[r+1]-1."""
+    R, H, P, N, G = p.num_reqs, p.nheads, p.headdim, p.d_state, p.ngroups
+    ti, ts = _TORCH[p.in_dtype], _TORCH[p.state_dtype]
+    Tt = int(x.shape[0])
+    rc = _lib.selective_state_update_varlen(
+        ctypes.byref(p), Tt, _ptr(cu_seqlens, "cu_seqlens", torch.int32, (R + 1,)),
+        None if dt_transform is None else ctypes.byref(dt_transform),
+        _ptr(state_cache, "state_cache", ts, (p.num_slots, H, P, N)),
+        _ptr(state_indices, "state_indices", torch.int32, (R,)),
+        _ptr(x, "x", ti, (Tt, H, P)), _ptr(dt, "dt", ti, (Tt, H)),
+        _ptr(A, "A", torch.float32, (H,)), _ptr(B, "B", ti, (Tt, G, N)),
+        _ptr(C, "C", ti, (Tt, G, N)), _ptr(D, "D", torch.float32, (H,), optional=True),
+        _ptr(y, "y", ti, (Tt, H, P)),
+        _ptr(intermediate_states, "intermediate_states", ts, (Tt, H, P, N), optional=True),
+        _stream(stream))
+    _check("selective_state_update_varlen", rc)
+
+
+def ssd_state_commit_varlen(p: ssu_problem, cu_seqlens, state_cache, state_indices,
+                            intermediate_states, num_accepted, stream=None):
+    R, H, P, N = p.num_reqs, p.nheads, p.headdim, p.d_state
+    ts = _TORCH[p.state_dtype]
+    Tt = int(intermediate_states.shape[0])
+    rc = _lib.ssd_state_commit_varlen(
+        ctypes.byref(p), Tt, _ptr(cu_seqlens, "cu_seqlens", torch.int32, (R + 1,)),
+        _ptr(state_cache, "state_cache", ts, (p.num_slots, H, P, N)),
+        _ptr(state_indices, "state_indices", torch.int32, (R,)),
+        _ptr(intermediate_states, "intermediate_states", ts, (Tt, H, P, N)),
+        _ptr(num_accepted, "num_accepted", torch.int32, (R,)), _stream(stream))
+    _check("ssd_state_commit_varlen", rc)
 
 
 # ---------------------------------------------------------------------------

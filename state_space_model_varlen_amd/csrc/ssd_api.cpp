@@ -84,6 +84,18 @@ ssd::DecodeDims dims_of(const ssu_problem *p)
     return d;
 }
 
+// Host copy of the dt preprocessing parameters (NULL transform: rejected).
+int dt_tf_of(const ssd_dt_transform *t, ssd::DtTf *out)
+{
+    if (!t) return SSD_ERR_NULL;
+    if (!(t->dt_min <= t->dt_max)) return SSD_ERR_SHAPE;   // (NaN bounds fail too)
+    out->bias = t->dt_bias;
+    out->lo = t->dt_min;
+    out->hi = t->dt_max;
+    out->on = 1;
+    return SSD_OK;
+}
+
 int launch_status()
 {
     const hipError_t e = hipGetLastError();
@@ -166,6 +178,22 @@ int ssd_chunk_cumsum(const ssd_problem *p, const void *dt, const float *A,
     return launch_status();
 }
 
+int ssd_chunk_cumsum_dt(const ssd_problem *p, const ssd_dt_transform *dt_transform,
+                        const void *dt_raw, const float *A, const int32_t *cu_seqlens,
+                        int32_t *chunk_meta, float *dA_cumsum, float *dt_chunk, void *stream)
+{
+    int rc = check_problem(p);
+    if (rc) return rc;
+    ssd::DtTf tf;
+    rc = dt_tf_of(dt_transform, &tf);
+    if (rc) return rc;
+    if (!dt_raw || !A || !cu_seqlens || !chunk_meta || !dA_cumsum || !dt_chunk) return SSD_ERR_NULL;
+    if (!aligned16(dA_cumsum) || !aligned16(dt_chunk)) return SSD_ERR_ALIGN;
+    ssd::launch_chunk_cumsum(dims_of(p), dt_raw, A, cu_seqlens, chunk_meta, dA_cumsum, dt_chunk,
+                             stream, tf);
+    return launch_status();
+}
+
 int ssd_chunk_state(const ssd_problem *p, const void *x, const void *B,
                     const int32_t *chunk_meta, const float *dA_cumsum, const float *dt_chunk,
                     float *chunk_states, void *stream)
@@ -245,11 +273,11 @@ int ssd_chunk_scan(const ssd_problem *p, const void *x, const void *C, const flo
     return launch_status();
 }
 
-int ssd_combined_varlen(const ssd_problem *p, const void *x, const void *dt, const float *A,
-                        const void *B, const void *C, const float *D, const int32_t *cu_seqlens,
-                        void *state_cache, const int32_t *state_indices,
-                        const uint8_t *has_initial_state, void *y, void *checkpoints,
-                        void *workspace, size_t workspace_bytes, void *stream)
+static int combined(const ssd_problem *p, const ssd::DtTf &tf, const void *x, const void *dt,
+                    const float *A, const void *B, const void *C, const float *D,
+                    const int32_t *cu_seqlens, void *state_cache, const int32_t *state_indices,
+                    const uint8_t *has_initial_state, void *y, void *checkpoints, void *workspace,
+                    size_t workspace_bytes, void *stream)
 {
     int rc = check_problem(p);
     if (rc) return rc;
@@ -272,7 +300,7 @@ int ssd_combined_varlen(const ssd_problem *p, const void *x, const void *dt, con
     float *states = reinterpret_cast<float *>(base + w.states);
     void *entering = base + w.entering;
 
-    ssd::launch_chunk_prep(d, dt, A, cu_seqlens, meta, cum, dtc, B, C, cb, stream);
+    ssd::launch_chunk_prep(d, dt, A, cu_seqlens, meta, cum, dtc, B, C, cb, stream, tf);
     if (ssd::fused_state_path(d)) {
         ssd::launch_state_scan(d, x, B, meta, cum, dtc, state_cache, state_indices,
                                has_initial_state, entering, checkpoints, stream);
@@ -283,6 +311,30 @@ int ssd_combined_varlen(const ssd_problem *p, const void *x, const void *dt, con
     }
     ssd::launch_chunk_scan(d, x, C, D, meta, cum, dtc, cb, entering, y, stream);
     return launch_status();
+}
+
+int ssd_combined_varlen(const ssd_problem *p, const void *x, const void *dt, const float *A,
+                        const void *B, const void *C, const float *D, const int32_t *cu_seqlens,
+                        void *state_cache, const int32_t *state_indices,
+                        const uint8_t *has_initial_state, void *y, void *checkpoints,
+                        void *workspace, size_t workspace_bytes, void *stream)
+{
+    return combined(p, ssd::DtTf(), x, dt, A, B, C, D, cu_seqlens, state_cache, state_indices,
+                    has_initial_state, y, checkpoints, workspace, workspace_bytes, stream);
+}
+
+int ssd_combined_varlen_dt(const ssd_problem *p, const ssd_dt_transform *dt_transform,
+                           const void *x, const void *dt_raw, const float *A, const void *B,
+                           const void *C, const float *D, const int32_t *cu_seqlens,
+                           void *state_cache, const int32_t *state_indices,
+                           const uint8_t *has_initial_state, void *y, void *checkpoints,
+                           void *workspace, size_t workspace_bytes, void *stream)
+{
+    ssd::DtTf tf;
+    const int rc = dt_tf_of(dt_transform, &tf);
+    if (rc) return rc;
+    return combined(p, tf, x, dt_raw, A, B, C, D, cu_seqlens, state_cache, state_indices,
+                    has_initial_state, y, checkpoints, workspace, workspace_bytes, stream);
 }
 
 int selective_state_update(const ssu_problem *p, void *state_cache, const int32_t *state_indices,
@@ -310,6 +362,49 @@ int ssd_state_commit(const ssu_problem *p, void *state_cache, const int32_t *sta
     if (!aligned16(state_cache) || !aligned16(intermediate_states)) return SSD_ERR_ALIGN;
     ssd::launch_state_commit(dims_of(p), state_cache, state_indices, intermediate_states,
                              num_accepted, stream);
+    return launch_status();
+}
+
+int selective_state_update_varlen(const ssu_problem *p, int32_t total_tokens,
+                                  const int32_t *cu_seqlens,
+                                  const ssd_dt_transform *dt_transform, void *state_cache,
+                                  const int32_t *state_indices, const void *x, const void *dt,
+                                  const float *A, const void *B, const void *C, const float *D,
+                                  void *y, void *intermediate_states, void *stream)
+{
+    int rc = check_ssu(p);
+    if (rc) return rc;
+    if (p->tokens_per_req < 1 || total_tokens < 0) return SSD_ERR_SHAPE;
+    ssd::DtTf tf;
+    if (dt_transform) {
+        rc = dt_tf_of(dt_transform, &tf);
+        if (rc) return rc;
+    }
+    if (!cu_seqlens || !state_cache || !state_indices || !x || !dt || !A || !B || !C || !y)
+        return SSD_ERR_NULL;
+    if (!aligned16(state_cache) || !aligned16(B) || !aligned16(C) ||
+        !aligned16(intermediate_states))
+        return SSD_ERR_ALIGN;
+    if (total_tokens == 0) return SSD_OK;
+    ssd::launch_state_update(dims_of(p), state_cache, state_indices, x, dt, A, B, C, D, y,
+                             intermediate_states, stream, cu_seqlens, total_tokens, tf);
+    return launch_status();
+}
+
+int ssd_state_commit_varlen(const ssu_problem *p, int32_t total_tokens,
+                            const int32_t *cu_seqlens, void *state_cache,
+                            const int32_t *state_indices, const void *intermediate_states,
+                            const int32_t *num_accepted, void *stream)
+{
+    int rc = check_ssu(p);
+    if (rc) return rc;
+    if (p->tokens_per_req < 1 || total_tokens < 0) return SSD_ERR_SHAPE;
+    if (!cu_seqlens || !state_cache || !state_indices || !intermediate_states || !num_accepted)
+        return SSD_ERR_NULL;
+    if (!aligned16(state_cache) || !aligned16(intermediate_states)) return SSD_ERR_ALIGN;
+    if (total_tokens == 0) return SSD_OK;
+    ssd::launch_state_commit(dims_of(p), state_cache, state_indices, intermediate_states,
+                             num_accepted, stream, cu_seqlens, total_tokens);
     return launch_status();
 }
 

@@ -28,7 +28,8 @@ __global__ __launch_bounds__(256) void state_update_kernel(
     int T, int H, int G, int num_slots, TS *cache, const int32_t *__restrict__ idx,
     const TIn *__restrict__ x, const TIn *__restrict__ dt, const float *__restrict__ A,
     const TIn *__restrict__ B, const TIn *__restrict__ C, const float *__restrict__ D,
-    TIn *__restrict__ y, TS *__restrict__ inter)
+    TIn *__restrict__ y, TS *__restrict__ inter, const int32_t *__restrict__ cu, int Ttot,
+    DtTf tf)
 {
     constexpr int CPR = N / 8;                       // chunks per state row
     constexpr int NCH = P * N / 8;                   // chunks per (request, head)
@@ -39,6 +40,16 @@ __global__ __launch_bounds__(256) void state_update_kernel(
     const int g = h / (H / G);
     const int n0 = (tid % CPR) * 8;
 
+    // tokens of request r: tb .. tb + Tr - 1 of the packed rows
+    int tb = r * T, Tr = T;
+    if (cu) {
+        int a = cu[r], b = cu[r + 1];
+        a = a < 0 ? 0 : (a > Ttot ? Ttot : a);
+        b = b < 0 ? 0 : (b > Ttot ? Ttot : b);
+        tb = a;
+        Tr = b > a ? b - a : 0;
+    }
+    if (Tr == 0) return;   // no token: nothing changes
     const int slot = idx[r];
     const bool slot_ok = slot >= 0 && slot < num_slots;
     const int64_t PN = (int64_t)P * N;
@@ -53,15 +64,16 @@ __global__ __launch_bounds__(256) void state_update_kernel(
     }
     const float Ah = A[h];
     const float Dh = D ? D[h] : 0.0f;
+    const float bh = tf.bias ? tf.bias[h] : 0.0f;
     float dtv[TM], xv[TM][KC];
     Raw8<TIn> braw[TM], craw[TM];
-    // requests dt, x, B, C of tokens t0 .. t0 + TM - 1 (clamped to T - 1)
+    // requests dt, x, B, C of tokens t0 .. t0 + TM - 1 (clamped to Tr - 1)
     auto load_group = [&](int t0) {
 #pragma unroll
         for (int j = 0; j < TM; ++j) {
-            const int t = t0 + j < T ? t0 + j : T - 1;
-            const int64_t rt = (int64_t)r * T + t;
-            dtv[j] = to_f32(dt[rt * H + h]);
+            const int t = t0 + j < Tr ? t0 + j : Tr - 1;
+            const int64_t rt = (int64_t)tb + t;
+            dtv[j] = dt_apply(tf, to_f32(dt[rt * H + h]), bh);
             braw[j].load(B + (rt * G + g) * N + n0);
             craw[j].load(C + (rt * G + g) * N + n0);
 #pragma unroll
@@ -86,15 +98,15 @@ __global__ __launch_bounds__(256) void state_update_kernel(
         }
     }
 
-    // (T >= 1: the launcher enqueues nothing for T = 0, so the first group always
-    // runs and its loads are not sunk past a loop-entry test)
+    // (Tr >= 1, so the first group always runs and its loads are not sunk past a
+    // loop-entry test)
     int t0 = 0;
     do {
         if (t0 > 0) load_group(t0);
 #pragma unroll
         for (int j = 0; j < TM; ++j) {
-            if (t0 + j >= T) break;
-            const int64_t rt = (int64_t)r * T + t0 + j;
+            if (t0 + j >= Tr) break;
+            const int64_t rt = (int64_t)tb + t0 + j;
             const float decay = __expf(dtv[j] * Ah);
             float b8[8], c8[8];
             braw[j].widen(b8);
@@ -120,7 +132,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(
             }
         }
         t0 += TM;
-    } while (t0 < T);
+    } while (t0 < Tr);
     if (!inter && slot_ok) {
 #pragma unroll
         for (int k = 0; k < KC; ++k)
@@ -128,27 +140,38 @@ __global__ __launch_bounds__(256) void state_update_kernel(
     }
 }
 
-// Rollback commit: cache[idx[r]] = inter[r, accepted[r]], 16 bytes per thread.
+// Rollback commit: cache[idx[r]] = inter[token a of request r], 16 bytes per
+// thread (request r's tokens: r T .., or cu[r] .. cu[r+1]-1 when packed).
 template <typename TS>
 __global__ __launch_bounds__(256) void state_commit_kernel(int T, int64_t HPN, int num_slots,
                                                            TS *cache, const int32_t *__restrict__ idx,
                                                            const TS *__restrict__ inter,
-                                                           const int32_t *__restrict__ accepted)
+                                                           const int32_t *__restrict__ accepted,
+                                                           const int32_t *__restrict__ cu, int Ttot)
 {
     constexpr int VE = 16 / sizeof(TS);
     const int r = blockIdx.y;
     const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * VE;
+    int tb = r * T, Tr = T;
+    if (cu) {
+        int a0 = cu[r], b0 = cu[r + 1];
+        a0 = a0 < 0 ? 0 : (a0 > Ttot ? Ttot : a0);
+        b0 = b0 < 0 ? 0 : (b0 > Ttot ? Ttot : b0);
+        tb = a0;
+        Tr = b0 > a0 ? b0 - a0 : 0;
+    }
     const int a = accepted[r];
     const int slot = idx[r];
-    if (e >= HPN || a < 0 || a >= T || slot < 0 || slot >= num_slots) return;
-    const uint4 v = *reinterpret_cast<const uint4 *>(inter + ((int64_t)r * T + a) * HPN + e);
+    if (e >= HPN || a < 0 || a >= Tr || slot < 0 || slot >= num_slots) return;
+    const uint4 v = *reinterpret_cast<const uint4 *>(inter + ((int64_t)tb + a) * HPN + e);
     *reinterpret_cast<uint4 *>(cache + (int64_t)slot * HPN + e) = v;
 }
 
 template <typename TIn, typename TS, int P, int N>
 static void launch_ssu_t(const DecodeDims &d, void *cache, const int32_t *idx, const void *x,
                          const void *dt, const float *A, const void *B, const void *C,
-                         const float *D, void *y, void *inter, hipStream_t st)
+                         const float *D, void *y, void *inter, hipStream_t st, const int32_t *cu,
+                         int Ttot, const DtTf &tf)
 {
     dim3 grid(d.H, d.R);
 #define SSD_SSU_LAUNCH(TM)                                                                        \
@@ -156,7 +179,7 @@ static void launch_ssu_t(const DecodeDims &d, void *cache, const int32_t *idx, c
                        d.H, d.G, d.num_slots, static_cast<TS *>(cache), idx,                      \
                        static_cast<const TIn *>(x), static_cast<const TIn *>(dt), A,              \
                        static_cast<const TIn *>(B), static_cast<const TIn *>(C), D,               \
-                       static_cast<TIn *>(y), static_cast<TS *>(inter))
+                       static_cast<TIn *>(y), static_cast<TS *>(inter), cu, Ttot, tf)
     // tokens per load group: the whole request when it has up to 4 tokens
     if (d.T <= 1) SSD_SSU_LAUNCH(1);
     else if (d.T <= 2) SSD_SSU_LAUNCH(2);
@@ -168,33 +191,37 @@ static void launch_ssu_t(const DecodeDims &d, void *cache, const int32_t *idx, c
 template <typename TIn, typename TS>
 static void launch_ssu_pn(const DecodeDims &d, void *cache, const int32_t *idx, const void *x,
                           const void *dt, const float *A, const void *B, const void *C,
-                          const float *D, void *y, void *inter, hipStream_t st)
+                          const float *D, void *y, void *inter, hipStream_t st, const int32_t *cu,
+                          int Ttot, const DtTf &tf)
 {
-    if (d.P == 64 && d.N == 128) launch_ssu_t<TIn, TS, 64, 128>(d, cache, idx, x, dt, A, B, C, D, y, inter, st);
-    else if (d.P == 64 && d.N == 16) launch_ssu_t<TIn, TS, 64, 16>(d, cache, idx, x, dt, A, B, C, D, y, inter, st);
-    else if (d.P == 16 && d.N == 128) launch_ssu_t<TIn, TS, 16, 128>(d, cache, idx, x, dt, A, B, C, D, y, inter, st);
-    else launch_ssu_t<TIn, TS, 16, 16>(d, cache, idx, x, dt, A, B, C, D, y, inter, st);
+    if (d.P == 64 && d.N == 128) launch_ssu_t<TIn, TS, 64, 128>(d, cache, idx, x, dt, A, B, C, D, y, inter, st, cu, Ttot, tf);
+    else if (d.P == 64 && d.N == 16) launch_ssu_t<TIn, TS, 64, 16>(d, cache, idx, x, dt, A, B, C, D, y, inter, st, cu, Ttot, tf);
+    else if (d.P == 16 && d.N == 128) launch_ssu_t<TIn, TS, 16, 128>(d, cache, idx, x, dt, A, B, C, D, y, inter, st, cu, Ttot, tf);
+    else launch_ssu_t<TIn, TS, 16, 16>(d, cache, idx, x, dt, A, B, C, D, y, inter, st, cu, Ttot, tf);
 }
 
 void launch_state_update(const DecodeDims &d, void *cache, const int32_t *idx, const void *x,
                          const void *dt, const float *A, const void *B, const void *C,
-                         const float *D, void *y, void *inter, void *stream)
+                         const float *D, void *y, void *inter, void *stream, const int32_t *cu,
+                         int Ttot, const DtTf &tf)
 {
     if (d.R <= 0 || d.T <= 0) return;
+    if (!cu) Ttot = d.R * d.T;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (d.in_bf16) {
-        if (d.state_bf16) launch_ssu_pn<bf16, bf16>(d, cache, idx, x, dt, A, B, C, D, y, inter, st);
-        else launch_ssu_pn<bf16, float>(d, cache, idx, x, dt, A, B, C, D, y, inter, st);
+        if (d.state_bf16) launch_ssu_pn<bf16, bf16>(d, cache, idx, x, dt, A, B, C, D, y, inter, st, cu, Ttot, tf);
+        else launch_ssu_pn<bf16, float>(d, cache, idx, x, dt, A, B, C, D, y, inter, st, cu, Ttot, tf);
     } else {
-        if (d.state_bf16) launch_ssu_pn<float, bf16>(d, cache, idx, x, dt, A, B, C, D, y, inter, st);
-        else launch_ssu_pn<float, float>(d, cache, idx, x, dt, A, B, C, D, y, inter, st);
+        if (d.state_bf16) launch_ssu_pn<float, bf16>(d, cache, idx, x, dt, A, B, C, D, y, inter, st, cu, Ttot, tf);
+        else launch_ssu_pn<float, float>(d, cache, idx, x, dt, A, B, C, D, y, inter, st, cu, Ttot, tf);
     }
 }
 
 void launch_state_commit(const DecodeDims &d, void *cache, const int32_t *idx, const void *inter,
-                         const int32_t *accepted, void *stream)
+                         const int32_t *accepted, void *stream, const int32_t *cu, int Ttot)
 {
     if (d.R <= 0 || d.T <= 0) return;
+    if (!cu) Ttot = d.R * d.T;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const int64_t HPN = (int64_t)d.H * d.P * d.N;
     const int VE = d.state_bf16 ? 8 : 4;
@@ -202,11 +229,11 @@ void launch_state_commit(const DecodeDims &d, void *cache, const int32_t *idx, c
     if (d.state_bf16)
         hipLaunchKernelGGL(state_commit_kernel<bf16>, grid, dim3(256), 0, st, d.T, HPN, d.num_slots,
                            static_cast<bf16 *>(cache), idx, static_cast<const bf16 *>(inter),
-                           accepted);
+                           accepted, cu, Ttot);
     else
         hipLaunchKernelGGL(state_commit_kernel<float>, grid, dim3(256), 0, st, d.T, HPN, d.num_slots,
                            static_cast<float *>(cache), idx, static_cast<const float *>(inter),
-                           accepted);
+                           accepted, cu, Ttot);
 }
 
 }  // namespace ssd

@@ -2,6 +2,8 @@
 // (gfx950 / CDNA4, wave64).
 #pragma once
 
+#include "ssd_launch.h"
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -96,6 +98,14 @@ template <> struct Mma<float> {
     __device__ __forceinline__ static frag zero() { return 0.0f; }
     __device__ __forceinline__ static frag load(const float *p) { return *p; }
 };
+
+// Step-size preprocessing (see DtTf): softplus(v) = log(1 + exp(v)), v itself
+// above 20, then the clamp; `bias` is bias[h], read once by the caller.
+__device__ __forceinline__ float dt_apply(const DtTf &tf, float raw, float bias) {
+    const float v = raw + bias;
+    const float sp = v > 20.0f ? v : log1pf(__expf(v));
+    return tf.on ? fminf(fmaxf(sp, tf.lo), tf.hi) : raw;
+}
 
 // LDS writes of a wave made visible to the same wave's later reads.
 __device__ __forceinline__ void wave_lds_sync() {

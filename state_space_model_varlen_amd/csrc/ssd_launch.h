@@ -8,6 +8,14 @@
 
 namespace ssd {
 
+// The layer's step-size preprocessing, applied where dt is read:
+// dt = min(max(softplus(dt_raw + bias[h]), lo), hi) when `on`.
+struct DtTf {
+    const float *bias = nullptr;
+    float lo = 0.0f, hi = 0.0f;
+    int on = 0;
+};
+
 struct PrefillDims {
     int T, S, H, P, N, G, Q;
     int max_chunks;
@@ -24,11 +32,12 @@ struct DecodeDims {
 };
 
 void launch_chunk_cumsum(const PrefillDims &d, const void *dt, const float *A, const int32_t *cu,
-                         int32_t *meta, float *cum, float *dto, void *stream);
+                         int32_t *meta, float *cum, float *dto, void *stream,
+                         const DtTf &tf = DtTf());
 // Steps 1 and 4 (cumsum with chunk metadata, and CB) in one launch.
 void launch_chunk_prep(const PrefillDims &d, const void *dt, const float *A, const int32_t *cu,
                        int32_t *meta, float *cum, float *dto, const void *B, const void *C,
-                       void *CB, void *stream);
+                       void *CB, void *stream, const DtTf &tf = DtTf());
 void launch_chunk_state(const PrefillDims &d, const void *x, const void *B, const int32_t *meta,
                         const float *cum, const float *dtc, float *states, void *stream);
 void launch_state_passing(const PrefillDims &d, const float *states, const float *cum,
@@ -47,11 +56,15 @@ void launch_chunk_scan(const PrefillDims &d, const void *x, const void *C, const
                        const int32_t *meta, const float *cum, const float *dtc, const void *CB,
                        const void *entering, void *y, void *stream);
 
+// cu (optional): packed-varlen requests, request r owning tokens cu[r] .. cu[r+1]-1
+// of Ttot packed rows; without it request r owns tokens r T .. r T + T - 1.
 void launch_state_update(const DecodeDims &d, void *cache, const int32_t *idx, const void *x,
                          const void *dt, const float *A, const void *B, const void *C,
-                         const float *D, void *y, void *inter, void *stream);
+                         const float *D, void *y, void *inter, void *stream,
+                         const int32_t *cu = nullptr, int Ttot = 0, const DtTf &tf = DtTf());
 void launch_state_commit(const DecodeDims &d, void *cache, const int32_t *idx, const void *inter,
-                         const int32_t *accepted, void *stream);
+                         const int32_t *accepted, void *stream, const int32_t *cu = nullptr,
+                         int Ttot = 0);
 
 // ReplaySSM decode: verify step, cursor move after sampling, materialisation.
 void launch_replay_update(const DecodeDims &d, int W, void *ckpt, void *rx, void *rdt, void *rB,

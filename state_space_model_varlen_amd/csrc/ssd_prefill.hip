@@ -107,17 +107,19 @@ template <typename TIn>
 __device__ __forceinline__ void cumsum_wave(int H, int Q, int max_chunks, int c, int h,
                                             const ChunkInfo &ci, int lane,
                                             const TIn *__restrict__ dt, const float *__restrict__ A,
-                                            float *__restrict__ cum_out, float *__restrict__ dt_out)
+                                            float *__restrict__ cum_out, float *__restrict__ dt_out,
+                                            const DtTf &tf)
 {
     const int E = (Q + kWave - 1) / kWave;  // positions per lane (<= 4)
     const float Ah = A[h];
+    const float bh = tf.bias ? tf.bias[h] : 0.0f;
     float vals[4], loc[4], run = 0.0f;
     // (loads at clamped positions, zeroed after: no branch between a load and its use)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int i = lane * E + e;
         const int ic = i < ci.len ? i : ci.len - 1;
-        const float v = to_f32(dt[(int64_t)(ci.start + ic) * H + h]);
+        const float v = dt_apply(tf, to_f32(dt[(int64_t)(ci.start + ic) * H + h]), bh);
         vals[e] = (e < E && i < ci.len) ? v : 0.0f;
     }
 #pragma unroll
@@ -151,7 +153,7 @@ template <typename TIn>
 __global__ __launch_bounds__(256) void chunk_cumsum_kernel(
     int T, int S, int H, int Q, int max_chunks, const TIn *__restrict__ dt,
     const float *__restrict__ A, const int32_t *__restrict__ cu, int32_t *__restrict__ meta,
-    float *__restrict__ cum_out, float *__restrict__ dt_out)
+    float *__restrict__ cum_out, float *__restrict__ dt_out, DtTf tf)
 {
     __shared__ int s_wave_tot[4];
     __shared__ int s_found[2];
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(
     if (publish && threadIdx.x == 0) publish_chunk(S, c, ci, meta);
     const int h = blockIdx.y * kCumsumHeadsPerBlock + wave;
     if (ci.len <= 0 || h >= H) return;
-    cumsum_wave<TIn>(H, Q, max_chunks, c, h, ci, lane, dt, A, cum_out, dt_out);
+    cumsum_wave<TIn>(H, Q, max_chunks, c, h, ci, lane, dt, A, cum_out, dt_out, tf);
 }
 
 // ===========================================================================
@@ -472,7 +474,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     int T, int S, int H, int G, int Q, int max_chunks, const TIn *__restrict__ dt,
     const float *__restrict__ A, const int32_t *__restrict__ cu, int32_t *__restrict__ meta,
     float *__restrict__ cum_out, float *__restrict__ dt_out, const TIn *__restrict__ B,
-    const TIn *__restrict__ C, TIn *__restrict__ CB)
+    const TIn *__restrict__ C, TIn *__restrict__ CB, DtTf tf)
 {
     __shared__ int s_wave_tot[4];
     __shared__ int s_found[2];
@@ -485,7 +487,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
         if (publish && threadIdx.x == 0) publish_chunk(S, c, ci, meta);
         const int h = blockIdx.y * kCumsumHeadsPerBlock + (threadIdx.x >> 6);
         if (ci.len <= 0 || h >= H) return;
-        cumsum_wave<TIn>(H, Q, max_chunks, c, h, ci, threadIdx.x & 63, dt, A, cum_out, dt_out);
+        cumsum_wave<TIn>(H, Q, max_chunks, c, h, ci, threadIdx.x & 63, dt, A, cum_out, dt_out,
+                         tf);
     } else {
         const int y = blockIdx.y - HB, tiles = Q / 16;
         bmm_rows<TIn, N>(G, Q, c, y / tiles, y % tiles, ci, B, C, CB);
@@ -1268,47 +1271,47 @@ static void allow_lds(const void *fn, size_t bytes, size_t &raised_to)
 
 template <typename TIn>
 static void launch_cumsum_t(const PrefillDims &d, const void *dt, const float *A, const int32_t *cu,
-                            int32_t *meta, float *cum, float *dto, hipStream_t st)
+                            int32_t *meta, float *cum, float *dto, hipStream_t st, const DtTf &tf)
 {
     dim3 grid(d.max_chunks, (d.H + kCumsumHeadsPerBlock - 1) / kCumsumHeadsPerBlock);
     hipLaunchKernelGGL(chunk_cumsum_kernel<TIn>, grid, dim3(256), 0, st, d.T, d.S, d.H, d.Q,
-                       d.max_chunks, static_cast<const TIn *>(dt), A, cu, meta, cum, dto);
+                       d.max_chunks, static_cast<const TIn *>(dt), A, cu, meta, cum, dto, tf);
 }
 
 template <typename TIn, int N>
 static void launch_prep_t(const PrefillDims &d, const void *dt, const float *A, const int32_t *cu,
                           int32_t *meta, float *cum, float *dto, const void *B, const void *C,
-                          void *CB, hipStream_t st)
+                          void *CB, hipStream_t st, const DtTf &tf)
 {
     const int HB = (d.H + kCumsumHeadsPerBlock - 1) / kCumsumHeadsPerBlock;
     dim3 grid(d.max_chunks, HB + d.G * (d.Q / 16));
     hipLaunchKernelGGL((chunk_prep_kernel<TIn, N>), grid, dim3(256), 0, st, d.T, d.S, d.H, d.G, d.Q,
                        d.max_chunks, static_cast<const TIn *>(dt), A, cu, meta, cum, dto,
                        static_cast<const TIn *>(B), static_cast<const TIn *>(C),
-                       static_cast<TIn *>(CB));
+                       static_cast<TIn *>(CB), tf);
 }
 
 void launch_chunk_prep(const PrefillDims &d, const void *dt, const float *A, const int32_t *cu,
                        int32_t *meta, float *cum, float *dto, const void *B, const void *C,
-                       void *CB, void *stream)
+                       void *CB, void *stream, const DtTf &tf)
 {
     if (d.max_chunks <= 0) return;
     hipStream_t st = as_stream(stream);
     if (d.in_bf16) {
-        if (d.N == 128) launch_prep_t<bf16, 128>(d, dt, A, cu, meta, cum, dto, B, C, CB, st);
-        else launch_prep_t<bf16, 16>(d, dt, A, cu, meta, cum, dto, B, C, CB, st);
+        if (d.N == 128) launch_prep_t<bf16, 128>(d, dt, A, cu, meta, cum, dto, B, C, CB, st, tf);
+        else launch_prep_t<bf16, 16>(d, dt, A, cu, meta, cum, dto, B, C, CB, st, tf);
     } else {
-        if (d.N == 128) launch_prep_t<float, 128>(d, dt, A, cu, meta, cum, dto, B, C, CB, st);
-        else launch_prep_t<float, 16>(d, dt, A, cu, meta, cum, dto, B, C, CB, st);
+        if (d.N == 128) launch_prep_t<float, 128>(d, dt, A, cu, meta, cum, dto, B, C, CB, st, tf);
+        else launch_prep_t<float, 16>(d, dt, A, cu, meta, cum, dto, B, C, CB, st, tf);
     }
 }
 
 void launch_chunk_cumsum(const PrefillDims &d, const void *dt, const float *A, const int32_t *cu,
-                         int32_t *meta, float *cum, float *dto, void *stream)
+                         int32_t *meta, float *cum, float *dto, void *stream, const DtTf &tf)
 {
     if (d.max_chunks <= 0) return;
-    if (d.in_bf16) launch_cumsum_t<bf16>(d, dt, A, cu, meta, cum, dto, as_stream(stream));
-    else launch_cumsum_t<float>(d, dt, A, cu, meta, cum, dto, as_stream(stream));
+    if (d.in_bf16) launch_cumsum_t<bf16>(d, dt, A, cu, meta, cum, dto, as_stream(stream), tf);
+    else launch_cumsum_t<float>(d, dt, A, cu, meta, cum, dto, as_stream(stream), tf);
 }
 
 template <typename TIn, int P, int N>

@@ -363,8 +363,59 @@ def pin_replay_matches_recurrence(lib=None, replay=None):
     np.testing.assert_array_equal(layer.ckpt[untouched].numpy(), init[untouched])
 
 
+def pin_dt_preprocess(lib=None, dtp=None):
+    """The step-size preprocessing: softplus(0) = log 2, softplus(v) - softplus(-v) = v,
+    agreement with torch's float64 softplus (threshold 20), the clamp, and the bias
+    taken per head (last axis)."""
+    f = dtp or oracle.dt_preprocess
+    big = 1e30
+    np.testing.assert_allclose(f(np.zeros(3), None, 0.0, big), np.full(3, math.log(2.0)),
+                               rtol=0, atol=1e-15)
+    v = np.linspace(-19.0, 19.0, 77)
+    np.testing.assert_allclose(f(v, None, 0.0, big) - f(-v, None, 0.0, big), v, rtol=0,
+                               atol=1e-12)
+    g = np.random.default_rng(141)
+    raw = g.standard_normal((5, 4)) * 8.0
+    bias = g.uniform(-3.0, 3.0, 4)
+    want = torch.nn.functional.softplus(torch.from_numpy(raw + bias)).numpy()
+    np.testing.assert_allclose(f(raw, bias, 0.0, big), want, rtol=1e-14, atol=1e-300)
+    lo, hi = 1e-3, 0.1
+    got = f(raw, bias, lo, hi)
+    np.testing.assert_allclose(got, np.clip(want, lo, hi), rtol=1e-14, atol=0)
+    assert got.min() >= lo and got.max() <= hi
+    np.testing.assert_allclose(f(np.array([25.0]), None, 0.0, big), [25.0], rtol=0, atol=0)
+
+
+def pin_varlen_update_is_prefill(lib=None):
+    """The packed-varlen state update against the prefill recurrence over the same
+    packed batch (every request starting from its slot): y equal; the state after
+    every token equal to prefill checkpoints with chunk size 1; the written cache
+    equal to prefill's write-back. Counts include an empty request."""
+    counts = [3, 0, 1, 4, 2]
+    R, H, P, N, G = len(counts), 4, 3, 5, 2
+    Tt = sum(counts)
+    x, dt, A, B, C, D = _rand(151, Tt, H, P, N, G)
+    cu = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    cache = torch.from_numpy(np.random.default_rng(152).standard_normal((7, H, P, N)))
+    idx = np.array([5, 1, 0, 6, 2], dtype=np.int32)
+    keep = oracle.state_update_varlen(cache, idx, cu, x, dt, A, B, C, D, True, lib=lib)
+    plain = oracle.state_update_varlen(cache, idx, cu, x, dt, A, B, C, D, False, lib=lib)
+    init = cache[torch.from_numpy(idx.astype(np.int64))].numpy()
+    yp, fp, ck = oracle.recurrence(x, dt, A, B, C, D, cu, 1, init=init,
+                                   has_init=np.ones(R, np.uint8), checkpoints=True, lib=lib)
+    np.testing.assert_allclose(keep["y"], yp, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(plain["y"], yp, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(keep["states"], ck, rtol=1e-12, atol=1e-14)
+    assert torch.equal(keep["cache"], cache)
+    for r in range(R):
+        np.testing.assert_allclose(plain["cache"][idx[r]].numpy(), fp[r], rtol=1e-12, atol=1e-14)
+    untouched = [3, 4]
+    assert torch.equal(plain["cache"][untouched], cache[untouched])
+
+
 ALL_PINS = [pin_hand_worked, pin_single_token_closed_form, pin_cumsum_reduction, pin_pure_decay,
             pin_skip_only, pin_linearity, pin_dual_form, pin_continued_prefill,
             pin_varlen_packing, pin_checkpoints_are_truncated_finals,
             pin_chunk_size_independence, pin_state_update_replay, pin_cache_semantics,
-            pin_bf16_rounding, pin_replay_matches_recurrence]
+            pin_bf16_rounding, pin_replay_matches_recurrence, pin_dt_preprocess,
+            pin_varlen_update_is_prefill]

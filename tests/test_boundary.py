@@ -172,3 +172,30 @@ def test_replay_validation():
                                       ok, ok, None) == 7
     un = ssd.make_ssu_problem(2, 3, 8, 32, 128, 2, 4, torch.bfloat16, torch.bfloat16)
     assert lib.ssd_replay_advance(ctypes.byref(un), 6, ok, ok, ok, None) == 4
+
+
+def test_dt_transform_and_varlen_validation():
+    """NULL transform, inverted clamp, bad token counts and NULL arrays are refused
+    on the host."""
+    lib = ssd._lib
+    ok = ctypes.c_void_p(256)
+    p = P()
+    good = ssd.ssd_dt_transform(None, 1e-3, 0.1)
+    bad = ssd.ssd_dt_transform(None, 0.5, 0.1)
+    assert lib.ssd_chunk_cumsum_dt(ctypes.byref(p), None, *([ok] * 6), None) == 1
+    assert lib.ssd_chunk_cumsum_dt(ctypes.byref(p), ctypes.byref(bad), *([ok] * 6), None) == 2
+    assert lib.ssd_chunk_cumsum_dt(ctypes.byref(p), ctypes.byref(good), None, *([ok] * 5),
+                                   None) == 1
+    assert lib.ssd_combined_varlen_dt(ctypes.byref(p), None, *([ok] * 13),
+                                      ctypes.c_size_t(1 << 30), None) == 1
+    up = ssd.make_ssu_problem(2, 3, 8, 64, 128, 2, 4, torch.bfloat16, torch.bfloat16)
+    args = [ok] * 7 + [None, ok, None]     # cache .. C, D = NULL, y, inter = NULL
+    f = lib.selective_state_update_varlen
+    assert f(ctypes.byref(up), -1, ok, None, *args, None) == 2
+    assert f(ctypes.byref(up), 6, None, None, *args, None) == 1
+    assert f(ctypes.byref(up), 6, ok, ctypes.byref(bad), *args, None) == 2
+    zero = ssd.make_ssu_problem(2, 0, 8, 64, 128, 2, 4, torch.bfloat16, torch.bfloat16)
+    assert f(ctypes.byref(zero), 6, ok, None, *args, None) == 2
+    g = lib.ssd_state_commit_varlen
+    assert g(ctypes.byref(up), 6, None, ok, ok, ok, ok, None) == 1
+    assert g(ctypes.byref(up), 6, ok, ok, ok, ctypes.c_void_p(264), ok, None) == 7

@@ -142,3 +142,25 @@ def test_replay_mutation_is_caught(mut, tmp_path):
     spec.loader.exec_module(mod)
     with pytest.raises((AssertionError, IndexError)):
         oracle_pins.pin_replay_matches_recurrence(replay=mod)
+
+
+# Planted mistakes in the step-size preprocessing, passed to its pin directly.
+def _dtp_no_bias(dt_raw, dt_bias, lo, hi):
+    return oracle.dt_preprocess(dt_raw, None, lo, hi)
+
+
+def _dtp_exp_not_softplus(dt_raw, dt_bias, lo, hi):
+    v = oracle.f64(dt_raw) + (0.0 if dt_bias is None else oracle.f64(dt_bias))
+    return np.clip(np.exp(np.minimum(v, 20.0)), lo, hi)
+
+
+def _dtp_clamp_before_softplus(dt_raw, dt_bias, lo, hi):
+    v = oracle.f64(dt_raw) + (0.0 if dt_bias is None else oracle.f64(dt_bias))
+    return np.log1p(np.exp(np.clip(v, lo, hi)))
+
+
+@pytest.mark.parametrize("bad", [_dtp_no_bias, _dtp_exp_not_softplus, _dtp_clamp_before_softplus],
+                         ids=lambda f: f.__name__)
+def test_dt_preprocess_mutation_is_caught(bad):
+    with pytest.raises(AssertionError):
+        oracle_pins.pin_dt_preprocess(dtp=bad)
