@@ -146,6 +146,7 @@ size_t ssd_workspace_bytes(const ssd_problem *p);  /* for ssd_combined_varlen */
  *                                   (-1, 0, 0 for c >= nc)
  *                 [S+1+3mc+s]       cu_seqlens[s] clamped to [0, T], s = 0..S
  *                                   (mc = ssd_max_chunks)
+ *                 [2S+2+3mc+s]      tokens in sequence s's first chunk, s < S
  *   dA_cumsum   out, float32 [H, max_chunks, Q]: inclusive cumsum of dt*A_h over
  *               the chunk's tokens; positions past the chunk's end hold its last value
  *   dt_chunk    out, float32 [H, max_chunks, Q]: dt per chunk position, 0 past the end
@@ -309,6 +310,29 @@ int ssd_combined_varlen_dt(const ssd_problem *p, const ssd_dt_transform *dt_tran
                            void *state_cache, const int32_t *state_indices,
                            const uint8_t *has_initial_state, void *y, void *checkpoints,
                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Align-mode prefill (vLLM PR #55688, "Summary": prefix caching in the align
+ * cache mode; checkpoints serve prefix reuse, vLLM PR #61501 "Changes"): sequence s
+ * continues after prefix_lens[s] cached tokens, and chunk boundaries fall on
+ * absolute token positions that are multiples of Q, so its first chunk holds
+ * Q - (prefix_lens[s] mod Q) tokens (Q when that is 0) and every checkpoint
+ * is the state at an absolute multiple of Q (or the sequence's end). Results
+ * are those of ssd_combined_varlen otherwise; y and the final states do not
+ * depend on where chunks are cut.
+ *   prefix_lens   [S] int32 on the device (negative values count as 0)
+ *   checkpoints   [ssd_max_chunks_aligned(p),H,P,N] state_dtype or NULL; row
+ *                 chunk_cu[s] + k holds the exit state of sequence s's chunk k
+ *   workspace     at least ssd_workspace_bytes_aligned(p) bytes
+ */
+int64_t ssd_max_chunks_aligned(const ssd_problem *p);   /* T/Q + 2 S */
+size_t ssd_workspace_bytes_aligned(const ssd_problem *p);
+int ssd_combined_varlen_aligned(const ssd_problem *p, const int32_t *prefix_lens, const void *x,
+                                const void *dt, const float *A, const void *B, const void *C,
+                                const float *D, const int32_t *cu_seqlens, void *state_cache,
+                                const int32_t *state_indices, const uint8_t *has_initial_state,
+                                void *y, void *checkpoints, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /*
  * Packed-varlen MTP verify (vLLM PR #52928, section "Summary": variable-length

@@ -160,6 +160,43 @@ def prefill(x, dt, A, B, C, D, cu_seqlens, state_indices, has_initial, cache: to
     return dict(y=y, final=final, ckpt=ckpt, cache=after)
 
 
+def aligned_chunks(L: int, Q: int, prefix_len: int):
+    """(offset, length) of each chunk of an L-token sequence that follows
+    prefix_len cached tokens, cut at absolute token positions that are multiples
+    of Q (align mode, vLLM PR #55688 "Summary"): the first chunk runs to the next
+    multiple of Q, the others are Q long, the last may be partial."""
+    o = prefix_len % Q if prefix_len > 0 else 0
+    first = Q - o if o else Q
+    out, pos = [], 0
+    while pos < L:
+        ln = min(first if pos == 0 else Q, L - pos)
+        out.append((pos, ln))
+        pos += ln
+    return out
+
+
+def prefill_aligned(x, dt, A, B, C, D, cu_seqlens, state_indices, has_initial,
+                    cache: torch.Tensor, chunk_size: int, prefix_lens, lib=None):
+    """Align-mode prefill: as ``prefill``, with the checkpoint of every chunk cut by
+    ``aligned_chunks`` (the state after the chunk's last token), in packed chunk
+    order. The states come from the recurrence run with a checkpoint after every
+    token (chunk size 1)."""
+    out = prefill(x, dt, A, B, C, D, cu_seqlens, state_indices, has_initial, cache,
+                  chunk_size, lib=lib)
+    per_token = prefill(x, dt, A, B, C, D, cu_seqlens, state_indices, has_initial, cache, 1,
+                        checkpoints=True, lib=lib)["ckpt"]
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    rows, base = [], 0
+    for s in range(len(cu) - 1):
+        L = max(int(cu[s + 1] - cu[s]), 0)
+        for off, ln in aligned_chunks(L, chunk_size, int(prefix_lens[s])):
+            rows.append(per_token[base + off + ln - 1])
+        base += L
+    shape = (0,) + tuple(per_token.shape[1:])
+    out["ckpt"] = np.stack(rows) if rows else np.zeros(shape)
+    return out
+
+
 def state_update(cache: torch.Tensor, state_indices, x, dt, A, B, C, D, keep_states: bool,
                  nthreads: int = 0, lib=None):
     """Decode / MTP verify: per request, continue from cache[state_indices[r]].

@@ -74,6 +74,9 @@ _SIGS = {
     "ssd_combined_varlen": ([_pp] + [_vp] * 13 + [ctypes.c_size_t, _vp], ctypes.c_int),
     "selective_state_update": ([_up] + [_vp] * 11, ctypes.c_int),
     "ssd_state_commit": ([_up] + [_vp] * 5, ctypes.c_int),
+    "ssd_max_chunks_aligned": ([_pp], ctypes.c_int64),
+    "ssd_workspace_bytes_aligned": ([_pp], ctypes.c_size_t),
+    "ssd_combined_varlen_aligned": ([_pp] + [_vp] * 14 + [ctypes.c_size_t, _vp], ctypes.c_int),
     "ssd_chunk_cumsum_dt": ([_pp, _tp] + [_vp] * 7, ctypes.c_int),
     "ssd_combined_varlen_dt": ([_pp, _tp] + [_vp] * 13 + [ctypes.c_size_t, _vp], ctypes.c_int),
     "selective_state_update_varlen": ([_up, ctypes.c_int32, _vp, _tp] + [_vp] * 11, ctypes.c_int),
@@ -315,6 +318,42 @@ def ssd_state_commit(p: ssu_problem, state_cache, state_indices, intermediate_st
         _ptr(intermediate_states, "intermediate_states", ts, (R, T, H, P, N)),
         _ptr(num_accepted, "num_accepted", torch.int32, (R,)), _stream(stream))
     _check("ssd_state_commit", rc)
+
+
+# ---------------------------------------------------------------------------
+# align-mode prefill: chunk boundaries at absolute multiples of the chunk size
+
+def max_chunks_aligned(p: ssd_problem) -> int:
+    return int(_lib.ssd_max_chunks_aligned(ctypes.byref(p)))
+
+
+def alloc_workspace_aligned(p: ssd_problem, device="cuda") -> torch.Tensor:
+    n = int(_lib.ssd_workspace_bytes_aligned(ctypes.byref(p)))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def ssd_combined_varlen_aligned(p: ssd_problem, prefix_lens, x, dt, A, B, C, D, cu_seqlens,
+                                state_cache, state_indices, has_initial_state, y, checkpoints,
+                                workspace, stream=None):
+    T, S, H, P, N, G, Q, _ = _dims(p)
+    mc = max_chunks_aligned(p)
+    ti, ts = _TORCH[p.in_dtype], _TORCH[p.state_dtype]
+    if workspace is None or workspace.dtype != torch.uint8 or workspace.dim() != 1:
+        raise ValueError("workspace must be a 1-D uint8 GPU tensor")
+    rc = _lib.ssd_combined_varlen_aligned(
+        ctypes.byref(p), _ptr(prefix_lens, "prefix_lens", torch.int32, (S,)),
+        _ptr(x, "x", ti, (T, H, P)), _ptr(dt, "dt", ti, (T, H)),
+        _ptr(A, "A", torch.float32, (H,)), _ptr(B, "B", ti, (T, G, N)),
+        _ptr(C, "C", ti, (T, G, N)), _ptr(D, "D", torch.float32, (H,), optional=True),
+        _ptr(cu_seqlens, "cu_seqlens", torch.int32, (S + 1,)),
+        _ptr(state_cache, "state_cache", ts, (p.num_slots, H, P, N)),
+        _ptr(state_indices, "state_indices", torch.int32, (S,)),
+        _ptr(has_initial_state, "has_initial_state", torch.uint8, (S,), optional=True),
+        _ptr(y, "y", ti, (T, H, P)),
+        _ptr(checkpoints, "checkpoints", ts, (mc, H, P, N), optional=True),
+        _ptr(workspace, "workspace", torch.uint8), ctypes.c_size_t(workspace.numel()),
+        _stream(stream))
+    _check("ssd_combined_varlen_aligned", rc)
 
 
 # ---------------------------------------------------------------------------

@@ -52,7 +52,14 @@ int check_ssu(const ssu_problem *p)
     return SSD_OK;
 }
 
-ssd::PrefillDims dims_of(const ssd_problem *p)
+// Upper bound on the chunks of a batch: T / Q + S (each sequence adds at most
+// one partial chunk), T / Q + 2 S in align mode (a partial chunk at each end).
+int64_t max_chunks_of(const ssd_problem *p, bool aligned)
+{
+    return (int64_t)p->total_tokens / p->chunk_size + (aligned ? 2 : 1) * (int64_t)p->num_seqs;
+}
+
+ssd::PrefillDims dims_of(const ssd_problem *p, bool aligned = false)
 {
     ssd::PrefillDims d;
     d.T = p->total_tokens;
@@ -62,7 +69,7 @@ ssd::PrefillDims dims_of(const ssd_problem *p)
     d.N = p->d_state;
     d.G = p->ngroups;
     d.Q = p->chunk_size;
-    d.max_chunks = (int)((int64_t)p->total_tokens / p->chunk_size + p->num_seqs);
+    d.max_chunks = (int)max_chunks_of(p, aligned);
     d.num_slots = p->num_slots;
     d.in_bf16 = p->in_dtype == SSD_BF16;
     d.state_bf16 = p->state_dtype == SSD_BF16;
@@ -109,13 +116,13 @@ struct Workspace {
     size_t meta, cum, dt, cb, states, entering, total;
 };
 
-Workspace workspace_layout(const ssd_problem *p)
+Workspace workspace_layout(const ssd_problem *p, bool aligned = false)
 {
-    const size_t mc = (size_t)((int64_t)p->total_tokens / p->chunk_size + p->num_seqs);
+    const size_t mc = (size_t)max_chunks_of(p, aligned);
     const size_t H = p->nheads, P = p->headdim, N = p->d_state, G = p->ngroups, Q = p->chunk_size;
     Workspace w;
     w.meta = 0;
-    w.cum = w.meta + round_up(sizeof(int32_t) * (2 * ((size_t)p->num_seqs + 1) + 3 * mc));
+    w.cum = w.meta + round_up(sizeof(int32_t) * (3 * (size_t)p->num_seqs + 2 + 3 * mc));
     w.dt = w.cum + round_up(sizeof(float) * H * mc * Q);
     w.cb = w.dt + round_up(sizeof(float) * H * mc * Q);
     const size_t ein = p->in_dtype == SSD_BF16 ? 2 : 4;
@@ -157,7 +164,7 @@ int64_t ssd_max_chunks(const ssd_problem *p)
 int64_t ssd_chunk_meta_count(const ssd_problem *p)
 {
     if (check_problem(p) != SSD_OK) return 0;
-    return 2 * ((int64_t)p->num_seqs + 1) + 3 * ssd_max_chunks(p);
+    return 3 * (int64_t)p->num_seqs + 2 + 3 * ssd_max_chunks(p);
 }
 
 size_t ssd_workspace_bytes(const ssd_problem *p)
@@ -277,8 +284,9 @@ static int combined(const ssd_problem *p, const ssd::DtTf &tf, const void *x, co
                     const float *A, const void *B, const void *C, const float *D,
                     const int32_t *cu_seqlens, void *state_cache, const int32_t *state_indices,
                     const uint8_t *has_initial_state, void *y, void *checkpoints, void *workspace,
-                    size_t workspace_bytes, void *stream)
+                    size_t workspace_bytes, void *stream, const int32_t *prefix = nullptr)
 {
+    const bool aligned = prefix != nullptr;
     int rc = check_problem(p);
     if (rc) return rc;
     if (!x || !dt || !A || !B || !C || !cu_seqlens || !state_cache || !state_indices || !y ||
@@ -288,10 +296,11 @@ static int combined(const ssd_problem *p, const ssd::DtTf &tf, const void *x, co
         !aligned16(state_cache) || !aligned16(checkpoints) ||
         (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return SSD_ERR_ALIGN;
-    const Workspace w = workspace_layout(p);
+    const Workspace w = workspace_layout(p, aligned);
     if (workspace_bytes < w.total) return SSD_ERR_WORKSPACE;
 
-    const ssd::PrefillDims d = dims_of(p);
+    ssd::PrefillDims d = dims_of(p, aligned);
+    d.prefix = prefix;
     char *base = static_cast<char *>(workspace);
     int32_t *meta = reinterpret_cast<int32_t *>(base + w.meta);
     float *cum = reinterpret_cast<float *>(base + w.cum);
@@ -321,6 +330,31 @@ int ssd_combined_varlen(const ssd_problem *p, const void *x, const void *dt, con
 {
     return combined(p, ssd::DtTf(), x, dt, A, B, C, D, cu_seqlens, state_cache, state_indices,
                     has_initial_state, y, checkpoints, workspace, workspace_bytes, stream);
+}
+
+int64_t ssd_max_chunks_aligned(const ssd_problem *p)
+{
+    if (check_problem(p) != SSD_OK) return 0;
+    return max_chunks_of(p, true);
+}
+
+size_t ssd_workspace_bytes_aligned(const ssd_problem *p)
+{
+    if (check_problem(p) != SSD_OK) return 0;
+    return workspace_layout(p, true).total;
+}
+
+int ssd_combined_varlen_aligned(const ssd_problem *p, const int32_t *prefix_lens, const void *x,
+                                const void *dt, const float *A, const void *B, const void *C,
+                                const float *D, const int32_t *cu_seqlens, void *state_cache,
+                                const int32_t *state_indices, const uint8_t *has_initial_state,
+                                void *y, void *checkpoints, void *workspace,
+                                size_t workspace_bytes, void *stream)
+{
+    if (!prefix_lens) return SSD_ERR_NULL;
+    return combined(p, ssd::DtTf(), x, dt, A, B, C, D, cu_seqlens, state_cache, state_indices,
+                    has_initial_state, y, checkpoints, workspace, workspace_bytes, stream,
+                    prefix_lens);
 }
 
 int ssd_combined_varlen_dt(const ssd_problem *p, const ssd_dt_transform *dt_transform,

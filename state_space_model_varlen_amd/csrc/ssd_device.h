@@ -272,6 +272,8 @@ __device__ __forceinline__ int xcd_logical_block(int pid, int nblocks) {
 //   meta[S + 1 + 3 mc + s]     cu_seqlens[s] clamped to [0, T], s = 0..S
 //                              (mc = max_chunks): sequence s spans tokens
 //                              [meta[..s], max(meta[..s], meta[..s + 1]))
+//   meta[2 (S + 1) + 3 mc + s] tokens in the first chunk of sequence s (Q, or
+//                              fewer in align mode), s = 0..S-1
 struct ChunkInfo {
     int seq, start, len;
 };

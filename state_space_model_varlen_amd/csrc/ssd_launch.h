@@ -22,6 +22,9 @@ struct PrefillDims {
     int num_slots;
     bool in_bf16;
     bool state_bf16;
+    // align mode: prefix[s] tokens precede sequence s, chunk boundaries fall on
+    // absolute multiples of Q (nullptr: chunks start at each sequence's start)
+    const int32_t *prefix = nullptr;
 };
 
 struct DecodeDims {

@@ -34,28 +34,41 @@ __device__ __forceinline__ int wave_inclusive_sum_int(int v, int lane) {
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+// Length of a sequence's first chunk: Q, or with `prefix` (align mode) the
+// distance from the sequence's first token to the next absolute multiple of Q
+// when prefix[s] tokens precede it.
+__device__ __forceinline__ int first_chunk_len(int Q, const int32_t *__restrict__ prefix, int s)
+{
+    const int pl = prefix ? prefix[s] : 0;
+    const int o = pl > 0 ? pl % Q : 0;
+    return o > 0 ? Q - o : Q;
+}
+
 // Block-wide: locate chunk c among the sequences of cu_seqlens. Writes
-// chunk_cu to meta[0..S] and the clamped cu_seqlens after the chunk triples
-// when `publish_cu`. Returns (seq, k) through shared
-// memory: chunk c is chunk k of sequence seq, seq = -1 when c >= nc.
+// chunk_cu to meta[0..S], the clamped cu_seqlens after the chunk triples and
+// the first-chunk lengths after those when `publish_cu`. Returns (seq, k, f)
+// through shared memory: chunk c is chunk k of sequence seq, whose first
+// chunk has f tokens; seq = -1 when c >= nc.
 __device__ void find_chunk(int T, int S, int Q, int max_chunks, const int32_t *__restrict__ cu,
-                           int c, bool publish_cu, int32_t *__restrict__ meta, int *s_found,
-                           int *s_wave_tot)
+                           const int32_t *__restrict__ prefix, int c, bool publish_cu,
+                           int32_t *__restrict__ meta, int *s_found, int *s_wave_tot)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (tid == 0) {
         s_found[0] = -1;
         s_found[1] = 0;
+        s_found[2] = Q;
     }
     int running = 0;
     for (int base = 0; base < S; base += 256) {
         __syncthreads();
         const int s = base + tid;
-        int cnt = 0;
+        int cnt = 0, f = Q;
         if (s < S) {
             const int a = clampi(cu[s], 0, T), b = clampi(cu[s + 1], 0, T);
             const int L = b > a ? b - a : 0;
-            cnt = (L + Q - 1) / Q;
+            f = first_chunk_len(Q, prefix, s);
+            cnt = L == 0 ? 0 : (L <= f ? 1 : 1 + (L - f + Q - 1) / Q);
         }
         const int incl = wave_inclusive_sum_int(cnt, lane);
         if (lane == 63) s_wave_tot[wave] = incl;
@@ -71,10 +84,12 @@ __device__ void find_chunk(int T, int S, int Q, int max_chunks, const int32_t *_
             if (publish_cu) {
                 meta[s] = first < max_chunks ? first : max_chunks;
                 meta[(S + 1) + 3 * max_chunks + s] = clampi(cu[s], 0, T);
+                meta[2 * (S + 1) + 3 * max_chunks + s] = f;
             }
             if (cnt > 0 && c >= first && c < first + cnt) {
                 s_found[0] = s;
                 s_found[1] = c - first;
+                s_found[2] = f;
             }
         }
         running += tile_tot;
@@ -96,8 +111,10 @@ __device__ __forceinline__ ChunkInfo found_chunk(int T, int Q, const int32_t *__
     ci.len = 0;
     if (ci.seq >= 0) {
         const int a = clampi(cu[ci.seq], 0, T), b = clampi(cu[ci.seq + 1], 0, T);
-        ci.start = a + s_found[1] * Q;
-        ci.len = b - ci.start < Q ? b - ci.start : Q;
+        const int k = s_found[1], f = s_found[2];
+        ci.start = a + (k == 0 ? 0 : f + (k - 1) * Q);
+        const int cap = k == 0 ? f : Q;
+        ci.len = b - ci.start < cap ? b - ci.start : cap;
     }
     return ci;
 }
@@ -153,14 +170,16 @@ template <typename TIn>
 __global__ __launch_bounds__(256) void chunk_cumsum_kernel(
     int T, int S, int H, int Q, int max_chunks, const TIn *__restrict__ dt,
     const float *__restrict__ A, const int32_t *__restrict__ cu, int32_t *__restrict__ meta,
-    float *__restrict__ cum_out, float *__restrict__ dt_out, DtTf tf)
+    float *__restrict__ cum_out, float *__restrict__ dt_out, DtTf tf,
+    const int32_t *__restrict__ prefix)
 {
     __shared__ int s_wave_tot[4];
-    __shared__ int s_found[2];
+    __shared__ int s_found[3];
     const int c = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const bool publish = blockIdx.y == 0;
-    find_chunk(T, S, Q, max_chunks, cu, c, publish && blockIdx.x == 0, meta, s_found, s_wave_tot);
+    find_chunk(T, S, Q, max_chunks, cu, prefix, c, publish && blockIdx.x == 0, meta, s_found,
+               s_wave_tot);
     const ChunkInfo ci = found_chunk(T, Q, cu, s_found);
     if (publish && threadIdx.x == 0) publish_chunk(S, c, ci, meta);
     const int h = blockIdx.y * kCumsumHeadsPerBlock + wave;
@@ -474,14 +493,15 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     int T, int S, int H, int G, int Q, int max_chunks, const TIn *__restrict__ dt,
     const float *__restrict__ A, const int32_t *__restrict__ cu, int32_t *__restrict__ meta,
     float *__restrict__ cum_out, float *__restrict__ dt_out, const TIn *__restrict__ B,
-    const TIn *__restrict__ C, TIn *__restrict__ CB, DtTf tf)
+    const TIn *__restrict__ C, TIn *__restrict__ CB, DtTf tf, const int32_t *__restrict__ prefix)
 {
     __shared__ int s_wave_tot[4];
-    __shared__ int s_found[2];
+    __shared__ int s_found[3];
     const int c = blockIdx.x;
     const int HB = (H + kCumsumHeadsPerBlock - 1) / kCumsumHeadsPerBlock;
     const bool publish = blockIdx.y == 0;
-    find_chunk(T, S, Q, max_chunks, cu, c, publish && blockIdx.x == 0, meta, s_found, s_wave_tot);
+    find_chunk(T, S, Q, max_chunks, cu, prefix, c, publish && blockIdx.x == 0, meta, s_found,
+               s_wave_tot);
     const ChunkInfo ci = found_chunk(T, Q, cu, s_found);
     if ((int)blockIdx.y < HB) {
         if (publish && threadIdx.x == 0) publish_chunk(S, c, ci, meta);
@@ -808,6 +828,7 @@ void state_scan_fast_kernel(
     int c0 = meta[s], c1 = meta[s + 1];
     const int first = meta[tokoff + s];
     int end = meta[tokoff + s + 1];
+    int fcl = meta[tokoff + (S + 1) + s];   // length of the first chunk (Q unless aligned)
     const int slot = idx[s];
     // (with no flag array, a byte of idx stands in and the flag is ignored)
     const uint8_t hflag = (has_init != nullptr ? has_init : reinterpret_cast<const uint8_t *>(idx))[s];
@@ -816,6 +837,10 @@ void state_scan_fast_kernel(
     c1 = c1 < max_chunks ? c1 : max_chunks;
     c1 = c1 > c0 ? c1 : c0;
     end = end > first ? end : first;
+    fcl = fcl < 1 ? 1 : (fcl > Q ? Q : fcl);
+    // chunk c of the sequence: tokens first + off(c) .., at most cap(c) of them
+    auto chunk_off = [&](int c) { return c == c0 ? 0 : fcl + (c - c0 - 1) * Q; };
+    auto chunk_cap = [&](int c) { return c == c0 ? fcl : Q; };
     const bool slot_ok = slot >= 0 && slot < num_slots;
     TS *cslot = cache + ((int64_t)(slot_ok ? slot : 0) * H + h) * PN + run;
 
@@ -848,8 +873,8 @@ void state_scan_fast_kernel(
         const bool any = c < c1;
         c = c < c1 ? c : c1 - 1;
         c = c > c0 ? c : c0;
-        const int st = first + (c - c0) * Q;
-        int len = end - st < Q ? end - st : Q;
+        const int st = first + chunk_off(c);
+        int len = end - st < chunk_cap(c) ? end - st : chunk_cap(c);
         len = any ? len : 0;
         const rsrc_t rx = make_rsrc(x + ((int64_t)st * H + h) * P,
                                     any ? (uint32_t)(len - 1) * xrow + P * 2 : 0u);
@@ -877,8 +902,8 @@ void state_scan_fast_kernel(
     // over zero tiles (it changes nothing) with its stores switched off.
     auto step = [&](Regs &R, int c) {
         const bool live = c < c1;
-        const int st = first + (c - c0) * Q;
-        const int len = end - st < Q ? end - st : Q;
+        const int st = first + chunk_off(c);
+        const int len = end - st < chunk_cap(c) ? end - st : chunk_cap(c);
         __syncthreads();   // the previous chunk's MFMA reads of xs / bs are done
 #pragma unroll
         for (int k = 0; k < Regs::kXV; ++k) {
@@ -1275,7 +1300,8 @@ static void launch_cumsum_t(const PrefillDims &d, const void *dt, const float *A
 {
     dim3 grid(d.max_chunks, (d.H + kCumsumHeadsPerBlock - 1) / kCumsumHeadsPerBlock);
     hipLaunchKernelGGL(chunk_cumsum_kernel<TIn>, grid, dim3(256), 0, st, d.T, d.S, d.H, d.Q,
-                       d.max_chunks, static_cast<const TIn *>(dt), A, cu, meta, cum, dto, tf);
+                       d.max_chunks, static_cast<const TIn *>(dt), A, cu, meta, cum, dto, tf,
+                       d.prefix);
 }
 
 template <typename TIn, int N>
@@ -1288,7 +1314,7 @@ static void launch_prep_t(const PrefillDims &d, const void *dt, const float *A, 
     hipLaunchKernelGGL((chunk_prep_kernel<TIn, N>), grid, dim3(256), 0, st, d.T, d.S, d.H, d.G, d.Q,
                        d.max_chunks, static_cast<const TIn *>(dt), A, cu, meta, cum, dto,
                        static_cast<const TIn *>(B), static_cast<const TIn *>(C),
-                       static_cast<TIn *>(CB), tf);
+                       static_cast<TIn *>(CB), tf, d.prefix);
 }
 
 void launch_chunk_prep(const PrefillDims &d, const void *dt, const float *A, const int32_t *cu,

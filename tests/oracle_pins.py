@@ -413,9 +413,59 @@ def pin_varlen_update_is_prefill(lib=None):
     assert torch.equal(plain["cache"][untouched], cache[untouched])
 
 
+def pin_aligned_checkpoints(lib=None):
+    """Align mode: chunk cuts worked by hand; a prefix that is a multiple of Q gives
+    the plain checkpoints; every aligned checkpoint equals the final state of the
+    prefill truncated at that absolute position (separate recurrence calls); and a
+    suffix prefill after a cached prefix reproduces the whole sequence's plain
+    checkpoints at the same absolute positions."""
+    assert oracle.aligned_chunks(10, 4, 6) == [(0, 2), (2, 4), (6, 4)]
+    assert oracle.aligned_chunks(3, 4, 6) == [(0, 2), (2, 1)]
+    assert oracle.aligned_chunks(1, 4, 7) == [(0, 1)]
+    assert oracle.aligned_chunks(9, 4, 8) == [(0, 4), (4, 4), (8, 1)]
+    assert oracle.aligned_chunks(0, 4, 3) == []
+    assert oracle.aligned_chunks(10, 4, 5) == [(0, 3), (3, 4), (7, 3)]
+    assert oracle.aligned_chunks(6, 8, 3) == [(0, 5), (5, 1)]
+    assert oracle.aligned_chunks(5, 8, 21) == [(0, 3), (3, 2)]
+    lens, Q = [10, 3, 0, 7], 4
+    T, H, P, N, G = sum(lens), 2, 2, 3, 1
+    x, dt, A, B, C, D = _rand(161, T, H, P, N, G)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cache = torch.from_numpy(np.random.default_rng(162).standard_normal((6, H, P, N)))
+    idx = np.array([4, 0, 2, 5], dtype=np.int32)
+    hi = np.array([1, 0, 1, 1], dtype=np.uint8)
+    plain = oracle.prefill(x, dt, A, B, C, D, cu, idx, hi, cache, Q, checkpoints=True, lib=lib)
+    same = oracle.prefill_aligned(x, dt, A, B, C, D, cu, idx, hi, cache, Q, [0, 8, 4, 12],
+                                  lib=lib)
+    np.testing.assert_allclose(same["ckpt"], plain["ckpt"], rtol=1e-12, atol=1e-14)
+    prefix = [6, 1, 5, 13]
+    al = oracle.prefill_aligned(x, dt, A, B, C, D, cu, idx, hi, cache, Q, prefix, lib=lib)
+    np.testing.assert_allclose(al["y"], plain["y"], rtol=1e-12, atol=1e-14)
+    row = 0
+    for s in range(len(lens)):
+        a = int(cu[s])
+        init = cache[int(idx[s])].numpy()[None] if hi[s] else None
+        for off, ln in oracle.aligned_chunks(lens[s], Q, prefix[s]):
+            e = off + ln
+            _, f, _ = oracle.recurrence(x[a:a + e], dt[a:a + e], A, B[a:a + e], C[a:a + e], D,
+                                        [0, e], Q, init=init, lib=lib)
+            np.testing.assert_allclose(al["ckpt"][row], f[0], rtol=1e-12, atol=1e-14)
+            row += 1
+    assert row == len(al["ckpt"])
+    # a 16-token sequence cut after 6 cached tokens: the 10-token suffix's aligned
+    # checkpoints are the whole sequence's plain ones at absolute positions 8, 12, 16
+    x1, dt1, A1, B1, C1, D1 = _rand(163, 16, H, P, N, G)
+    whole = oracle.recurrence(x1, dt1, A1, B1, C1, D1, [0, 16], Q, checkpoints=True, lib=lib)[2]
+    _, f6, _ = oracle.recurrence(x1[:6], dt1[:6], A1, B1[:6], C1[:6], D1, [0, 6], Q, lib=lib)
+    c1 = torch.from_numpy(f6)
+    suf = oracle.prefill_aligned(x1[6:], dt1[6:], A1, B1[6:], C1[6:], D1, [0, 10], [0], [1], c1,
+                                 Q, [6], lib=lib)
+    np.testing.assert_allclose(suf["ckpt"], whole[1:], rtol=1e-12, atol=1e-14)
+
+
 ALL_PINS = [pin_hand_worked, pin_single_token_closed_form, pin_cumsum_reduction, pin_pure_decay,
             pin_skip_only, pin_linearity, pin_dual_form, pin_continued_prefill,
             pin_varlen_packing, pin_checkpoints_are_truncated_finals,
             pin_chunk_size_independence, pin_state_update_replay, pin_cache_semantics,
             pin_bf16_rounding, pin_replay_matches_recurrence, pin_dt_preprocess,
-            pin_varlen_update_is_prefill]
+            pin_varlen_update_is_prefill, pin_aligned_checkpoints]

@@ -46,11 +46,12 @@ def P(**kw):
 def test_sizes():
     p = P()
     assert ssd.max_chunks(p) == 256 // 64 + 1
-    assert ssd.chunk_meta_count(p) == 2 * 2 + 3 * 5   # chunk_cu, chunk triples, clamped cu
+    # chunk_cu, chunk triples, clamped cu, first-chunk lengths
+    assert ssd.chunk_meta_count(p) == 2 + 3 * 5 + 2 + 1
     ws = ssd.workspace_bytes(p)
     # meta, cumsum, dt, CB and chunk states, each rounded up to 256 bytes
     r = lambda v: (v + 255) // 256 * 256
-    want = (r(4 * 19) + 2 * r(4 * 4 * 5 * 64) + r(4 * 5 * 1 * 64 * 64) + r(4 * 5 * 4 * 16 * 16)
+    want = (r(4 * 20) + 2 * r(4 * 4 * 5 * 64) + r(4 * 5 * 1 * 64 * 64) + r(4 * 5 * 4 * 16 * 16)
             + r(4 * 5 * 4 * 16 * 16))   # fp32 inputs: CB and entering states in fp32
     assert ws == want
     big = P(total_tokens=4096, nheads=80, headdim=64, d_state=128, chunk_size=256,
@@ -58,7 +59,7 @@ def test_sizes():
     assert ssd.max_chunks(big) == 17
     # bf16 inputs, headdim 64, d_state 128: the fused state kernel needs no chunk states
     mc, H, Q = 17, 80, 256
-    want_big = (r(4 * (4 + 3 * mc)) + 2 * r(4 * H * mc * Q) + r(2 * mc * 1 * Q * Q)
+    want_big = (r(4 * (5 + 3 * mc)) + 2 * r(4 * H * mc * Q) + r(2 * mc * 1 * Q * Q)
                 + r(2 * mc * H * 64 * 128))
     assert ssd.workspace_bytes(big) == want_big
 

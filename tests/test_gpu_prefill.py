@@ -97,7 +97,9 @@ def test_steps_match_chunked_oracle(case):
     gm = buf["chunk_meta"].cpu().numpy()
     assert gm[: S + 1].tolist() == meta["chunk_cu"].tolist()
     trip = gm[S + 1: S + 1 + 3 * mc].reshape(mc, 3)
-    assert gm[S + 1 + 3 * mc:].tolist() == np.clip(inp.cu_seqlens.numpy(), 0, T).tolist()
+    assert gm[S + 1 + 3 * mc: 2 * S + 2 + 3 * mc].tolist() == \
+        np.clip(inp.cu_seqlens.numpy(), 0, T).tolist()
+    assert (gm[2 * S + 2 + 3 * mc:] == Q).all()   # first chunks are whole outside align mode
     assert trip[:nc, 0].tolist() == meta["seq"].tolist()
     assert trip[:nc, 1].tolist() == meta["start"].tolist()
     assert trip[:nc, 2].tolist() == meta["len"].tolist()

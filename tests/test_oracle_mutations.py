@@ -164,3 +164,27 @@ def _dtp_clamp_before_softplus(dt_raw, dt_bias, lo, hi):
 def test_dt_preprocess_mutation_is_caught(bad):
     with pytest.raises(AssertionError):
         oracle_pins.pin_dt_preprocess(dtp=bad)
+
+
+# Planted mistakes in the align-mode chunk cuts, swapped in with monkeypatch.
+def _cuts_first_is_remainder(L, Q, prefix_len):
+    o = prefix_len % Q if prefix_len > 0 else 0
+    first = o if o else Q
+    out, pos = [], 0
+    while pos < L:
+        ln = min(first if pos == 0 else Q, L - pos)
+        out.append((pos, ln))
+        pos += ln
+    return out
+
+
+def _cuts_ignore_prefix(L, Q, prefix_len):
+    return [(pos, min(Q, L - pos)) for pos in range(0, L, Q)]
+
+
+@pytest.mark.parametrize("bad", [_cuts_first_is_remainder, _cuts_ignore_prefix],
+                         ids=lambda f: f.__name__)
+def test_aligned_cut_mutation_is_caught(bad, monkeypatch):
+    monkeypatch.setattr(oracle, "aligned_chunks", bad)
+    with pytest.raises(AssertionError):
+        oracle_pins.pin_aligned_checkpoints()
