@@ -79,7 +79,9 @@ enum ssd_status {
     SSD_ERR_ALIGN = 7        /* an array pointer is not 16-byte aligned */
 };
 
-typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+/* SSD_F16 is a state dtype only (state caches, checkpoints, per-token and
+ * ReplaySSM states); inputs are SSD_F32 or SSD_BF16. */
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1, SSD_F16 = 2 } ssd_dtype;
 
 /* One packed varlen prefill (host struct). */
 typedef struct {
@@ -121,6 +123,34 @@ typedef struct {
     float dt_min;         /* lower clamp (0 for none) */
     float dt_max;         /* upper clamp (a huge value for none); dt_min <= dt_max */
 } ssd_dt_transform;
+
+/*
+ * Options of the _ex entry points (every field may be NULL / 0):
+ *   dt_transform  the step-size preprocessing above
+ *   prefix_lens   [S] int32 on the device: align mode (see
+ *                 ssd_combined_varlen_aligned); prefill only
+ *   sr_seed       stochastic rounding of fp16 state stores (vLLM PR #61501,
+ *                 "Test plan": a float16 SSM cache with stochastic rounding
+ *                 and a configurable number of Philox rounds; "Changes": one
+ *                 seed per step read from a device buffer). Points to one
+ *                 uint64 on the device, read by the kernels, so a caller can
+ *                 refresh it per step without host synchronisation. Requires
+ *                 state_dtype SSD_F16. NULL: round to nearest even.
+ *   sr_rounds     Philox4x32 rounds, 1..16 (e.g. 5 or 10)
+ * Rounding: x becomes the fp16 value above or below it in magnitude, the
+ * farther one with probability (|x| - |lo|) / (|hi| - |lo|), drawn as
+ * (w >> 8) / 2^24 from a 32-bit word w (non-finite values and |x| > 65504
+ * round to nearest even). Element e of a destination array of kind k takes
+ * word e mod 4 of Philox4x32-R(counter = (e/4 low, e/4 high, k, 0), key =
+ * seed); kinds: 0 final states, 1 checkpoints, 2 per-token states,
+ * 3 ReplaySSM checkpoints. e is the flat element index in that array.
+ */
+typedef struct {
+    const ssd_dt_transform *dt_transform;
+    const int32_t *prefix_lens;
+    const uint64_t *sr_seed;
+    int32_t sr_rounds;
+} ssd_options;
 
 /* SSD_ABI_VERSION of the built library. */
 int ssd_abi_version(void);
@@ -367,6 +397,38 @@ int ssd_state_commit_varlen(const ssu_problem *p, int32_t total_tokens,
                             const int32_t *num_accepted, void *stream);
 
 /*
+ * ssd_combined_varlen with options (dt preprocessing, align mode, stochastic
+ * rounding of fp16 final states and checkpoints); the workspace must hold
+ * ssd_workspace_bytes_aligned(p) bytes when prefix_lens is set.
+ */
+int ssd_combined_varlen_ex(const ssd_problem *p, const ssd_options *opt, const void *x,
+                           const void *dt, const float *A, const void *B, const void *C,
+                           const float *D, const int32_t *cu_seqlens, void *state_cache,
+                           const int32_t *state_indices, const uint8_t *has_initial_state,
+                           void *y, void *checkpoints, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/*
+ * selective_state_update with options (dt preprocessing, stochastic rounding
+ * of fp16 stores); with cu_seqlens non-NULL it is the packed-varlen form over
+ * total_tokens rows (see selective_state_update_varlen), else the uniform form
+ * (total_tokens unused). opt->prefix_lens is ignored.
+ */
+int selective_state_update_ex(const ssu_problem *p, const ssd_options *opt, int32_t total_tokens,
+                              const int32_t *cu_seqlens, void *state_cache,
+                              const int32_t *state_indices, const void *x, const void *dt,
+                              const float *A, const void *B, const void *C, const float *D,
+                              void *y, void *intermediate_states, void *stream);
+
+/*
+ * fp32 -> fp16 of n values with the rounding of the state stores (stream
+ * `kind`, element e = index in the array; sr_seed NULL: nearest even). For
+ * converting states between caches, and for checking the rounding itself.
+ */
+int ssd_round_f16(const float *in, void *out, int64_t n, const uint64_t *sr_seed,
+                  int32_t sr_rounds, int32_t kind, void *stream);
+
+/*
  * ReplaySSM MTP decode (vLLM PR #52928, sections "Summary" and "Design": each
  * layer keeps a checkpoint state and a ring of the inputs per slot, the
  * accepted length moves a shared cursor before the next forward, and the
@@ -413,6 +475,18 @@ int ssd_replay_update(const ssu_problem *p, int32_t ring_len, void *ckpt, void *
  * ((start + n) mod W, 1 + a), else (start, n + 1 + a). T is the window of that
  * verify step (p->tokens_per_req). Out-of-range counts are clamped.
  */
+/* ssd_replay_update / ssd_replay_materialize with stochastic rounding of fp16
+ * checkpoints (opt->sr_seed; dt_transform and prefix_lens are not supported). */
+int ssd_replay_update_ex(const ssu_problem *p, const ssd_options *opt, int32_t ring_len,
+                         void *ckpt, void *ring_x, void *ring_dt, void *ring_B,
+                         const int32_t *cursor, const int32_t *state_indices, const void *x,
+                         const void *dt, const float *A, const void *B, const void *C,
+                         const float *D, void *y, void *stream);
+int ssd_replay_materialize_ex(const ssu_problem *p, const ssd_options *opt, int32_t ring_len,
+                              void *ckpt, const void *ring_x, const void *ring_dt,
+                              const void *ring_B, int32_t *cursor, const int32_t *state_indices,
+                              const float *A, void *stream);
+
 int ssd_replay_advance(const ssu_problem *p, int32_t ring_len, int32_t *cursor,
                        const int32_t *state_indices, const int32_t *num_accepted, void *stream);
 

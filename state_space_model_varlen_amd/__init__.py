@@ -33,9 +33,9 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 SSD_OK = 0
-F32, BF16 = 0, 1
-_DT = {torch.float32: F32, torch.bfloat16: BF16}
-_TORCH = {F32: torch.float32, BF16: torch.bfloat16}
+F32, BF16, F16 = 0, 1, 2
+_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+_TORCH = {F32: torch.float32, BF16: torch.bfloat16, F16: torch.float16}
 
 
 class ssd_problem(ctypes.Structure):
@@ -53,6 +53,11 @@ class ssu_problem(ctypes.Structure):
 class ssd_dt_transform(ctypes.Structure):
     _fields_ = [("dt_bias", ctypes.c_void_p), ("dt_min", ctypes.c_float),
                 ("dt_max", ctypes.c_float)]
+
+
+class ssd_options(ctypes.Structure):
+    _fields_ = [("dt_transform", ctypes.c_void_p), ("prefix_lens", ctypes.c_void_p),
+                ("sr_seed", ctypes.c_void_p), ("sr_rounds", ctypes.c_int32)]
 
 
 _vp = ctypes.c_void_p
@@ -78,6 +83,16 @@ _SIGS = {
     "ssd_workspace_bytes_aligned": ([_pp], ctypes.c_size_t),
     "ssd_combined_varlen_aligned": ([_pp] + [_vp] * 14 + [ctypes.c_size_t, _vp], ctypes.c_int),
     "ssd_chunk_cumsum_dt": ([_pp, _tp] + [_vp] * 7, ctypes.c_int),
+    "ssd_combined_varlen_ex": ([_pp, ctypes.POINTER(ssd_options)] + [_vp] * 13
+                               + [ctypes.c_size_t, _vp], ctypes.c_int),
+    "selective_state_update_ex": ([_up, ctypes.POINTER(ssd_options), ctypes.c_int32]
+                                  + [_vp] * 12, ctypes.c_int),
+    "ssd_round_f16": ([_vp, _vp, ctypes.c_int64, _vp, ctypes.c_int32, ctypes.c_int32, _vp],
+                      ctypes.c_int),
+    "ssd_replay_update_ex": ([_up, ctypes.POINTER(ssd_options), ctypes.c_int32] + [_vp] * 14,
+                             ctypes.c_int),
+    "ssd_replay_materialize_ex": ([_up, ctypes.POINTER(ssd_options), ctypes.c_int32] + [_vp] * 8,
+                                  ctypes.c_int),
     "ssd_combined_varlen_dt": ([_pp, _tp] + [_vp] * 13 + [ctypes.c_size_t, _vp], ctypes.c_int),
     "selective_state_update_varlen": ([_up, ctypes.c_int32, _vp, _tp] + [_vp] * 11, ctypes.c_int),
     "ssd_state_commit_varlen": ([_up, ctypes.c_int32] + [_vp] * 6, ctypes.c_int),
@@ -439,6 +454,111 @@ def ssd_state_commit_varlen(p: ssu_problem, cu_seqlens, state_cache, state_indic
         _ptr(intermediate_states, "intermediate_states", ts, (Tt, H, P, N)),
         _ptr(num_accepted, "num_accepted", torch.int32, (R,)), _stream(stream))
     _check("ssd_state_commit_varlen", rc)
+
+
+# ---------------------------------------------------------------------------
+# options: dt preprocessing, align mode, stochastic rounding of fp16 states
+
+def make_options(dt_transform=None, prefix_lens=None, sr_seed=None, sr_rounds: int = 10):
+    """ssd_options; sr_seed: a 1-element int64 GPU tensor (read by the kernels, so it can
+    be refreshed per step). The struct keeps references to the tensors it points at."""
+    o = ssd_options()
+    o.dt_transform = None if dt_transform is None else ctypes.addressof(dt_transform)
+    o.prefix_lens = None if prefix_lens is None else _ptr(prefix_lens, "prefix_lens", torch.int32)
+    o.sr_seed = None if sr_seed is None else _ptr(sr_seed, "sr_seed", torch.int64, (1,))
+    o.sr_rounds = int(sr_rounds) if sr_seed is not None else 0
+    o._refs = (dt_transform, prefix_lens, sr_seed)
+    return o
+
+
+def ssd_combined_varlen_ex(p: ssd_problem, options: ssd_options, x, dt, A, B, C, D, cu_seqlens,
+                           state_cache, state_indices, has_initial_state, y, checkpoints,
+                           workspace, stream=None):
+    T, S, H, P, N, G, Q, mc = _dims(p)
+    if options.prefix_lens:
+        mc = max_chunks_aligned(p)
+    ti, ts = _TORCH[p.in_dtype], _TORCH[p.state_dtype]
+    if workspace is None or workspace.dtype != torch.uint8 or workspace.dim() != 1:
+        raise ValueError("workspace must be a 1-D uint8 GPU tensor")
+    rc = _lib.ssd_combined_varlen_ex(
+        ctypes.byref(p), ctypes.byref(options), _ptr(x, "x", ti, (T, H, P)),
+        _ptr(dt, "dt", ti, (T, H)), _ptr(A, "A", torch.float32, (H,)),
+        _ptr(B, "B", ti, (T, G, N)), _ptr(C, "C", ti, (T, G, N)),
+        _ptr(D, "D", torch.float32, (H,), optional=True),
+        _ptr(cu_seqlens, "cu_seqlens", torch.int32, (S + 1,)),
+        _ptr(state_cache, "state_cache", ts, (p.num_slots, H, P, N)),
+        _ptr(state_indices, "state_indices", torch.int32, (S,)),
+        _ptr(has_initial_state, "has_initial_state", torch.uint8, (S,), optional=True),
+        _ptr(y, "y", ti, (T, H, P)),
+        _ptr(checkpoints, "checkpoints", ts, (mc, H, P, N), optional=True),
+        _ptr(workspace, "workspace", torch.uint8), ctypes.c_size_t(workspace.numel()),
+        _stream(stream))
+    _check("ssd_combined_varlen_ex", rc)
+
+
+def selective_state_update_ex(p: ssu_problem, options: ssd_options, state_cache, state_indices,
+                              x, dt, A, B, C, D, y, intermediate_states=None, cu_seqlens=None,
+                              stream=None):
+    """Uniform (x [R,T,H,P] ...) or, with cu_seqlens, packed-varlen (x [T_tot,H,P] ...)."""
+    R, T, H, P, N, G = (p.num_reqs, p.tokens_per_req, p.nheads, p.headdim, p.d_state, p.ngroups)
+    ti, ts = _TORCH[p.in_dtype], _TORCH[p.state_dtype]
+    lead = (R, T) if cu_seqlens is None else (int(x.shape[0]),)
+    Tt = R * T if cu_seqlens is None else int(x.shape[0])
+    rc = _lib.selective_state_update_ex(
+        ctypes.byref(p), ctypes.byref(options), Tt,
+        None if cu_seqlens is None else _ptr(cu_seqlens, "cu_seqlens", torch.int32, (R + 1,)),
+        _ptr(state_cache, "state_cache", ts, (p.num_slots, H, P, N)),
+        _ptr(state_indices, "state_indices", torch.int32, (R,)),
+        _ptr(x, "x", ti, lead + (H, P)), _ptr(dt, "dt", ti, lead + (H,)),
+        _ptr(A, "A", torch.float32, (H,)), _ptr(B, "B", ti, lead + (G, N)),
+        _ptr(C, "C", ti, lead + (G, N)), _ptr(D, "D", torch.float32, (H,), optional=True),
+        _ptr(y, "y", ti, lead + (H, P)),
+        _ptr(intermediate_states, "intermediate_states", ts, lead + (H, P, N), optional=True),
+        _stream(stream))
+    _check("selective_state_update_ex", rc)
+
+
+def ssd_round_f16(x, out, sr_seed=None, sr_rounds: int = 10, kind: int = 0, stream=None):
+    """out (float16) = x (float32) rounded as the fp16 state stores are."""
+    if x.numel() != out.numel() or out.dtype != torch.float16:
+        raise ValueError("out must be a float16 tensor with as many elements as x")
+    rc = _lib.ssd_round_f16(_ptr(x, "x", torch.float32), _ptr(out, "out", torch.float16),
+                            int(x.numel()),
+                            None if sr_seed is None else _ptr(sr_seed, "sr_seed", torch.int64, (1,)),
+                            int(sr_rounds), int(kind), _stream(stream))
+    _check("ssd_round_f16", rc)
+
+
+def ssd_replay_update_ex(p: ssu_problem, options: ssd_options, ring_len: int, ckpt, ring_x,
+                         ring_dt, ring_B, cursor, state_indices, x, dt, A, B, C, D, y,
+                         stream=None):
+    R, T, H, P, N, G = (p.num_reqs, p.tokens_per_req, p.nheads, p.headdim, p.d_state, p.ngroups)
+    ti, ts = _TORCH[p.in_dtype], _TORCH[p.state_dtype]
+    rc = _lib.ssd_replay_update_ex(
+        ctypes.byref(p), ctypes.byref(options), int(ring_len),
+        _ptr(ckpt, "ckpt", ts, (p.num_slots, H, P, N)),
+        *_ring_ptrs(p, ring_len, ring_x, ring_dt, ring_B),
+        _ptr(cursor, "cursor", torch.int32, (p.num_slots, 2)),
+        _ptr(state_indices, "state_indices", torch.int32, (R,)),
+        _ptr(x, "x", ti, (R, T, H, P)), _ptr(dt, "dt", ti, (R, T, H)),
+        _ptr(A, "A", torch.float32, (H,)), _ptr(B, "B", ti, (R, T, G, N)),
+        _ptr(C, "C", ti, (R, T, G, N)), _ptr(D, "D", torch.float32, (H,), optional=True),
+        _ptr(y, "y", ti, (R, T, H, P)), _stream(stream))
+    _check("ssd_replay_update_ex", rc)
+
+
+def ssd_replay_materialize_ex(p: ssu_problem, options: ssd_options, ring_len: int, ckpt, ring_x,
+                              ring_dt, ring_B, cursor, state_indices, A, stream=None):
+    H, P, N = p.nheads, p.headdim, p.d_state
+    ts = _TORCH[p.state_dtype]
+    rc = _lib.ssd_replay_materialize_ex(
+        ctypes.byref(p), ctypes.byref(options), int(ring_len),
+        _ptr(ckpt, "ckpt", ts, (p.num_slots, H, P, N)),
+        *_ring_ptrs(p, ring_len, ring_x, ring_dt, ring_B),
+        _ptr(cursor, "cursor", torch.int32, (p.num_slots, 2)),
+        _ptr(state_indices, "state_indices", torch.int32, (p.num_reqs,)),
+        _ptr(A, "A", torch.float32, (H,)), _stream(stream))
+    _check("ssd_replay_materialize_ex", rc)
 
 
 # ---------------------------------------------------------------------------

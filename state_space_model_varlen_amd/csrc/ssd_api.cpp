@@ -13,6 +13,8 @@ namespace {
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool dtype_ok(int32_t d) { return d == SSD_F32 || d == SSD_BF16; }
+// states may also be fp16
+bool state_dtype_ok(int32_t d) { return dtype_ok(d) || d == SSD_F16; }
 
 bool gpu_shape_ok(int P, int N) { return (P == 16 || P == 64) && (N == 16 || N == 128); }
 
@@ -27,7 +29,7 @@ int check_problem(const ssd_problem *p)
         return SSD_ERR_SHAPE;
     if (p->nheads % p->ngroups != 0) return SSD_ERR_SHAPE;
     if (p->num_seqs > 0 && p->num_slots <= 0) return SSD_ERR_SHAPE;
-    if (!dtype_ok(p->in_dtype) || !dtype_ok(p->state_dtype)) return SSD_ERR_DTYPE;
+    if (!dtype_ok(p->in_dtype) || !state_dtype_ok(p->state_dtype)) return SSD_ERR_DTYPE;
     if (!gpu_shape_ok(p->headdim, p->d_state) || !chunk_ok(p->chunk_size)) return SSD_ERR_UNSUPPORTED;
     // grid limits: chunks and heads index grid dimensions
     const int64_t mc = (int64_t)p->total_tokens / p->chunk_size + p->num_seqs;
@@ -46,7 +48,7 @@ int check_ssu(const ssu_problem *p)
         return SSD_ERR_SHAPE;
     if (p->nheads % p->ngroups != 0) return SSD_ERR_SHAPE;
     if (p->num_reqs > 0 && p->num_slots <= 0) return SSD_ERR_SHAPE;
-    if (!dtype_ok(p->in_dtype) || !dtype_ok(p->state_dtype)) return SSD_ERR_DTYPE;
+    if (!dtype_ok(p->in_dtype) || !state_dtype_ok(p->state_dtype)) return SSD_ERR_DTYPE;
     if (!gpu_shape_ok(p->headdim, p->d_state)) return SSD_ERR_UNSUPPORTED;
     if (p->nheads > 0x7fffffff / 2 || p->num_reqs > 65535) return SSD_ERR_UNSUPPORTED;
     return SSD_OK;
@@ -73,6 +75,7 @@ ssd::PrefillDims dims_of(const ssd_problem *p, bool aligned = false)
     d.num_slots = p->num_slots;
     d.in_bf16 = p->in_dtype == SSD_BF16;
     d.state_bf16 = p->state_dtype == SSD_BF16;
+    d.state_f16 = p->state_dtype == SSD_F16;
     return d;
 }
 
@@ -88,6 +91,7 @@ ssd::DecodeDims dims_of(const ssu_problem *p)
     d.num_slots = p->num_slots;
     d.in_bf16 = p->in_dtype == SSD_BF16;
     d.state_bf16 = p->state_dtype == SSD_BF16;
+    d.state_f16 = p->state_dtype == SSD_F16;
     return d;
 }
 
@@ -284,7 +288,8 @@ static int combined(const ssd_problem *p, const ssd::DtTf &tf, const void *x, co
                     const float *A, const void *B, const void *C, const float *D,
                     const int32_t *cu_seqlens, void *state_cache, const int32_t *state_indices,
                     const uint8_t *has_initial_state, void *y, void *checkpoints, void *workspace,
-                    size_t workspace_bytes, void *stream, const int32_t *prefix = nullptr)
+                    size_t workspace_bytes, void *stream, const int32_t *prefix = nullptr,
+                    const ssd::SrCtx &sr = ssd::SrCtx())
 {
     const bool aligned = prefix != nullptr;
     int rc = check_problem(p);
@@ -301,6 +306,7 @@ static int combined(const ssd_problem *p, const ssd::DtTf &tf, const void *x, co
 
     ssd::PrefillDims d = dims_of(p, aligned);
     d.prefix = prefix;
+    d.sr = sr;
     char *base = static_cast<char *>(workspace);
     int32_t *meta = reinterpret_cast<int32_t *>(base + w.meta);
     float *cum = reinterpret_cast<float *>(base + w.cum);
@@ -330,6 +336,39 @@ int ssd_combined_varlen(const ssd_problem *p, const void *x, const void *dt, con
 {
     return combined(p, ssd::DtTf(), x, dt, A, B, C, D, cu_seqlens, state_cache, state_indices,
                     has_initial_state, y, checkpoints, workspace, workspace_bytes, stream);
+}
+
+// Stochastic rounding parameters of an options struct (fp16 states only).
+static int sr_of(const ssd_options *o, int32_t state_dtype, ssd::SrCtx *sr)
+{
+    if (!o || !o->sr_seed) return SSD_OK;
+    if (state_dtype != SSD_F16) return SSD_ERR_UNSUPPORTED;
+    if (o->sr_rounds < 1 || o->sr_rounds > 16) return SSD_ERR_SHAPE;
+    sr->seed = o->sr_seed;
+    sr->rounds = o->sr_rounds;
+    return SSD_OK;
+}
+
+int ssd_combined_varlen_ex(const ssd_problem *p, const ssd_options *opt, const void *x,
+                           const void *dt, const float *A, const void *B, const void *C,
+                           const float *D, const int32_t *cu_seqlens, void *state_cache,
+                           const int32_t *state_indices, const uint8_t *has_initial_state,
+                           void *y, void *checkpoints, void *workspace, size_t workspace_bytes,
+                           void *stream)
+{
+    int rc = check_problem(p);
+    if (rc) return rc;
+    ssd::DtTf tf;
+    ssd::SrCtx sr;
+    if (opt && opt->dt_transform) {
+        rc = dt_tf_of(opt->dt_transform, &tf);
+        if (rc) return rc;
+    }
+    rc = sr_of(opt, p->state_dtype, &sr);
+    if (rc) return rc;
+    return combined(p, tf, x, dt, A, B, C, D, cu_seqlens, state_cache, state_indices,
+                    has_initial_state, y, checkpoints, workspace, workspace_bytes, stream,
+                    opt ? opt->prefix_lens : nullptr, sr);
 }
 
 int64_t ssd_max_chunks_aligned(const ssd_problem *p)
@@ -425,6 +464,55 @@ int selective_state_update_varlen(const ssu_problem *p, int32_t total_tokens,
     return launch_status();
 }
 
+int selective_state_update_ex(const ssu_problem *p, const ssd_options *opt, int32_t total_tokens,
+                              const int32_t *cu_seqlens, void *state_cache,
+                              const int32_t *state_indices, const void *x, const void *dt,
+                              const float *A, const void *B, const void *C, const float *D,
+                              void *y, void *intermediate_states, void *stream)
+{
+    int rc = check_ssu(p);
+    if (rc) return rc;
+    if (p->tokens_per_req < 1 && cu_seqlens) return SSD_ERR_SHAPE;
+    if (total_tokens < 0) return SSD_ERR_SHAPE;
+    ssd::DtTf tf;
+    ssd::SrCtx sr;
+    if (opt && opt->dt_transform) {
+        rc = dt_tf_of(opt->dt_transform, &tf);
+        if (rc) return rc;
+    }
+    rc = sr_of(opt, p->state_dtype, &sr);
+    if (rc) return rc;
+    if (!state_cache || !state_indices || !x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL;
+    if (!aligned16(state_cache) || !aligned16(B) || !aligned16(C) ||
+        !aligned16(intermediate_states))
+        return SSD_ERR_ALIGN;
+    ssd::DecodeDims d = dims_of(p);
+    d.sr = sr;
+    if (cu_seqlens) {
+        if (total_tokens == 0) return SSD_OK;
+        ssd::launch_state_update(d, state_cache, state_indices, x, dt, A, B, C, D, y,
+                                 intermediate_states, stream, cu_seqlens, total_tokens, tf);
+    } else {
+        ssd::launch_state_update(d, state_cache, state_indices, x, dt, A, B, C, D, y,
+                                 intermediate_states, stream, nullptr, 0, tf);
+    }
+    return launch_status();
+}
+
+int ssd_round_f16(const float *in, void *out, int64_t n, const uint64_t *sr_seed,
+                  int32_t sr_rounds, int32_t kind, void *stream)
+{
+    if (n < 0) return SSD_ERR_SHAPE;
+    if (n == 0) return SSD_OK;
+    if (!in || !out) return SSD_ERR_NULL;
+    if (sr_seed && (sr_rounds < 1 || sr_rounds > 16)) return SSD_ERR_SHAPE;
+    ssd::SrCtx sr;
+    sr.seed = sr_seed;
+    sr.rounds = sr_seed ? sr_rounds : 0;
+    ssd::launch_round_f16(in, out, n, sr, kind, stream);
+    return launch_status();
+}
+
 int ssd_state_commit_varlen(const ssu_problem *p, int32_t total_tokens,
                             const int32_t *cu_seqlens, void *state_cache,
                             const int32_t *state_indices, const void *intermediate_states,
@@ -467,6 +555,52 @@ int ssd_replay_update(const ssu_problem *p, int32_t ring_len, void *ckpt, void *
         return SSD_ERR_ALIGN;
     ssd::launch_replay_update(dims_of(p), ring_len, ckpt, ring_x, ring_dt, ring_B, cursor,
                               state_indices, x, dt, A, B, C, D, y, stream);
+    return launch_status();
+}
+
+int ssd_replay_update_ex(const ssu_problem *p, const ssd_options *opt, int32_t ring_len,
+                         void *ckpt, void *ring_x, void *ring_dt, void *ring_B,
+                         const int32_t *cursor, const int32_t *state_indices, const void *x,
+                         const void *dt, const float *A, const void *B, const void *C,
+                         const float *D, void *y, void *stream)
+{
+    int rc = check_replay(p, ring_len);
+    if (rc) return rc;
+    if (opt && (opt->dt_transform || opt->prefix_lens)) return SSD_ERR_UNSUPPORTED;
+    ssd::SrCtx sr;
+    rc = sr_of(opt, p->state_dtype, &sr);
+    if (rc) return rc;
+    if (!ckpt || !ring_x || !ring_dt || !ring_B || !cursor || !state_indices || !x || !dt || !A ||
+        !B || !C || !y)
+        return SSD_ERR_NULL;
+    if (!aligned16(ckpt) || !aligned16(ring_x) || !aligned16(ring_B) || !aligned16(x) ||
+        !aligned16(B) || !aligned16(C))
+        return SSD_ERR_ALIGN;
+    ssd::DecodeDims d = dims_of(p);
+    d.sr = sr;
+    ssd::launch_replay_update(d, ring_len, ckpt, ring_x, ring_dt, ring_B, cursor, state_indices,
+                              x, dt, A, B, C, D, y, stream);
+    return launch_status();
+}
+
+int ssd_replay_materialize_ex(const ssu_problem *p, const ssd_options *opt, int32_t ring_len,
+                              void *ckpt, const void *ring_x, const void *ring_dt,
+                              const void *ring_B, int32_t *cursor, const int32_t *state_indices,
+                              const float *A, void *stream)
+{
+    int rc = check_replay(p, ring_len);
+    if (rc) return rc;
+    if (opt && (opt->dt_transform || opt->prefix_lens)) return SSD_ERR_UNSUPPORTED;
+    ssd::SrCtx sr;
+    rc = sr_of(opt, p->state_dtype, &sr);
+    if (rc) return rc;
+    if (!ckpt || !ring_x || !ring_dt || !ring_B || !cursor || !state_indices || !A)
+        return SSD_ERR_NULL;
+    if (!aligned16(ckpt) || !aligned16(ring_x) || !aligned16(ring_B)) return SSD_ERR_ALIGN;
+    ssd::DecodeDims d = dims_of(p);
+    d.sr = sr;
+    ssd::launch_replay_materialize(d, ring_len, ckpt, ring_x, ring_dt, ring_B, cursor,
+                                   state_indices, A, stream);
     return launch_status();
 }
 

@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(
     const TIn *__restrict__ x, const TIn *__restrict__ dt, const float *__restrict__ A,
     const TIn *__restrict__ B, const TIn *__restrict__ C, const float *__restrict__ D,
     TIn *__restrict__ y, TS *__restrict__ inter, const int32_t *__restrict__ cu, int Ttot,
-    DtTf tf)
+    DtTf tf, SrCtx sr)
 {
     constexpr int CPR = N / 8;                       // chunks per state row
     constexpr int NCH = P * N / 8;                   // chunks per (request, head)
@@ -65,6 +65,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(
     const float Ah = A[h];
     const float Dh = D ? D[h] : 0.0f;
     const float bh = tf.bias ? tf.bias[h] : 0.0f;
+    const SrKey srk = sr_key(sr, cache);
     float dtv[TM], xv[TM][KC];
     Raw8<TIn> braw[TM], craw[TM];
     // requests dt, x, B, C of tokens t0 .. t0 + TM - 1 (clamped to Tr - 1)
@@ -126,17 +127,23 @@ __global__ __launch_bounds__(256) void state_update_kernel(
                     yr[pk[k]] = from_f32<TIn>(part + Dh * xv[j][k]);
                 if (inter && tid + 256 * k < NCH) {
                     // written once and read only by a later rollback: stream past the caches
-                    TS *ip = inter + (rt * H + h) * PN + (int64_t)pk[k] * N + n0;
-                    store8_nt(ip, st[k]);
+                    const int64_t io = (rt * H + h) * PN + (int64_t)pk[k] * N + n0;
+                    if (std::is_same<TS, f16>::value && srk.rounds > 0)
+                        put_run<TS, 8>(inter + io, st[k], srk, (uint64_t)io, kSrStates);
+                    else
+                        store8_nt(inter + io, st[k]);
                 }
             }
         }
         t0 += TM;
     } while (t0 < Tr);
     if (!inter && slot_ok) {
+        const int64_t so = (int64_t)slot * H * PN + (int64_t)h * PN;
 #pragma unroll
         for (int k = 0; k < KC; ++k)
-            if (tid + 256 * k < NCH) store_run<TS, 8>(cs + (int64_t)pk[k] * N + n0, st[k]);
+            if (tid + 256 * k < NCH)
+                put_run<TS, 8>(cs + (int64_t)pk[k] * N + n0, st[k], srk,
+                               (uint64_t)(so + (int64_t)pk[k] * N + n0), kSrFinal);
     }
 }
 
@@ -179,7 +186,7 @@ static void launch_ssu_t(const DecodeDims &d, void *cache, const int32_t *idx, c
                        d.H, d.G, d.num_slots, static_cast<TS *>(cache), idx,                      \
                        static_cast<const TIn *>(x), static_cast<const TIn *>(dt), A,              \
                        static_cast<const TIn *>(B), static_cast<const TIn *>(C), D,               \
-                       static_cast<TIn *>(y), static_cast<TS *>(inter), cu, Ttot, tf)
+                       static_cast<TIn *>(y), static_cast<TS *>(inter), cu, Ttot, tf, d.sr)
     // tokens per load group: the whole request when it has up to 4 tokens
     if (d.T <= 1) SSD_SSU_LAUNCH(1);
     else if (d.T <= 2) SSD_SSU_LAUNCH(2);
@@ -209,10 +216,12 @@ void launch_state_update(const DecodeDims &d, void *cache, const int32_t *idx, c
     if (!cu) Ttot = d.R * d.T;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (d.in_bf16) {
-        if (d.state_bf16) launch_ssu_pn<bf16, bf16>(d, cache, idx, x, dt, A, B, C, D, y, inter, st, cu, Ttot, tf);
+        if (d.state_f16) launch_ssu_pn<bf16, f16>(d, cache, idx, x, dt, A, B, C, D, y, inter, st, cu, Ttot, tf);
+        else if (d.state_bf16) launch_ssu_pn<bf16, bf16>(d, cache, idx, x, dt, A, B, C, D, y, inter, st, cu, Ttot, tf);
         else launch_ssu_pn<bf16, float>(d, cache, idx, x, dt, A, B, C, D, y, inter, st, cu, Ttot, tf);
     } else {
-        if (d.state_bf16) launch_ssu_pn<float, bf16>(d, cache, idx, x, dt, A, B, C, D, y, inter, st, cu, Ttot, tf);
+        if (d.state_f16) launch_ssu_pn<float, f16>(d, cache, idx, x, dt, A, B, C, D, y, inter, st, cu, Ttot, tf);
+        else if (d.state_bf16) launch_ssu_pn<float, bf16>(d, cache, idx, x, dt, A, B, C, D, y, inter, st, cu, Ttot, tf);
         else launch_ssu_pn<float, float>(d, cache, idx, x, dt, A, B, C, D, y, inter, st, cu, Ttot, tf);
     }
 }
@@ -224,9 +233,11 @@ void launch_state_commit(const DecodeDims &d, void *cache, const int32_t *idx, c
     if (!cu) Ttot = d.R * d.T;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const int64_t HPN = (int64_t)d.H * d.P * d.N;
-    const int VE = d.state_bf16 ? 8 : 4;
+    // (a copy: fp16 moves as the 2-byte bf16 instantiation does)
+    const bool two = d.state_bf16 || d.state_f16;
+    const int VE = two ? 8 : 4;
     dim3 grid((unsigned)((HPN / VE + 255) / 256), d.R);
-    if (d.state_bf16)
+    if (two)
         hipLaunchKernelGGL(state_commit_kernel<bf16>, grid, dim3(256), 0, st, d.T, HPN, d.num_slots,
                            static_cast<bf16 *>(cache), idx, static_cast<const bf16 *>(inter),
                            accepted, cu, Ttot);
@@ -234,6 +245,38 @@ void launch_state_commit(const DecodeDims &d, void *cache, const int32_t *idx, c
         hipLaunchKernelGGL(state_commit_kernel<float>, grid, dim3(256), 0, st, d.T, HPN, d.num_slots,
                            static_cast<float *>(cache), idx, static_cast<const float *>(inter),
                            accepted, cu, Ttot);
+}
+
+// fp32 -> fp16 of n values with the state stores' rounding (element e of
+// stream `kind`), 4 values per thread.
+__global__ __launch_bounds__(256) void round_f16_kernel(const float *__restrict__ in,
+                                                        f16 *__restrict__ out, int64_t n, SrCtx sr,
+                                                        int kind)
+{
+    const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e0 >= n) return;
+    const SrKey srk = sr_key(sr, in);
+    if (e0 + 4 <= n && (reinterpret_cast<uintptr_t>(out + e0) & 7u) == 0) {
+        const float v[4] = {in[e0], in[e0 + 1], in[e0 + 2], in[e0 + 3]};
+        put4<f16>(out + e0, v, srk, (uint64_t)e0, (uint32_t)kind);
+        return;
+    }
+    const uint64_t blk = (uint64_t)e0 >> 2;
+    const uint4 w = philox4x32(make_uint4((uint32_t)blk, (uint32_t)(blk >> 32), (uint32_t)kind, 0u),
+                               srk.k0, srk.k1, srk.rounds);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    for (int j = 0; j < 4 && e0 + j < n; ++j)
+        out[e0 + j] = srk.rounds > 0 ? sr_f16(in[e0 + j], ws[j]) : static_cast<f16>(in[e0 + j]);
+}
+
+void launch_round_f16(const float *in, void *out, int64_t n, const SrCtx &sr, int kind,
+                      void *stream)
+{
+    if (n <= 0) return;
+    const int64_t groups = (n + 3) / 4;
+    hipLaunchKernelGGL(round_f16_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), in, static_cast<f16 *>(out), n, sr,
+                       kind);
 }
 
 }  // namespace ssd

@@ -5,11 +5,13 @@
 #include "ssd_launch.h"
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 namespace ssd {
 
 typedef __bf16 bf16;
+typedef _Float16 f16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -23,6 +25,8 @@ __device__ __forceinline__ float to_f32(bf16 v) { return static_cast<float>(v); 
 template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return static_cast<bf16>(v); }
+__device__ __forceinline__ float to_f32(f16 v) { return static_cast<float>(v); }
+template <> __device__ __forceinline__ f16 from_f32<f16>(float v) { return static_cast<f16>(v); }
 
 // ---------------------------------------------------------------------------
 // 16-byte vector loads / stores of 8 bf16 or 4 float.
@@ -43,6 +47,21 @@ template <> struct Vec16<bf16> {
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = static_cast<bf16>(in[i]);
         *reinterpret_cast<bf16x8 *>(p) = v;
+    }
+};
+template <> struct Vec16<f16> {
+    static constexpr int kElems = 8;
+    typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+    __device__ __forceinline__ static void load(const f16 *p, float *out) {
+        const f16x8 v = *reinterpret_cast<const f16x8 *>(p);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out[i] = static_cast<float>(v[i]);
+    }
+    __device__ __forceinline__ static void store(f16 *p, const float *in) {
+        f16x8 v;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = static_cast<f16>(in[i]);
+        *reinterpret_cast<f16x8 *>(p) = v;
     }
 };
 template <> struct Vec16<float> {
@@ -150,6 +169,11 @@ template <> __device__ __forceinline__ void load4<bf16>(const bf16 *p, float *v)
     v[2] = __uint_as_float(q.y << 16);
     v[3] = __uint_as_float(q.y & 0xffff0000u);
 }
+template <> __device__ __forceinline__ void load4<f16>(const f16 *p, float *v) {
+    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+    const f16x4 q = *reinterpret_cast<const f16x4 *>(p);
+    v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3];
+}
 template <typename T> __device__ __forceinline__ void store4(T *p, const float *v);
 template <> __device__ __forceinline__ void store4<float>(float *p, const float *v) {
     *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
@@ -162,6 +186,103 @@ template <> __device__ __forceinline__ void store4<bf16>(bf16 *p, const float *v
     q[2] = static_cast<bf16>(v[2]);
     q[3] = static_cast<bf16>(v[3]);
     *reinterpret_cast<bf16x4 *>(p) = q;
+}
+
+template <> __device__ __forceinline__ void store4<f16>(f16 *p, const float *v) {
+    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+    f16x4 q;
+    q[0] = static_cast<f16>(v[0]);
+    q[1] = static_cast<f16>(v[1]);
+    q[2] = static_cast<f16>(v[2]);
+    q[3] = static_cast<f16>(v[3]);
+    *reinterpret_cast<f16x4 *>(p) = q;
+}
+
+// ---------------------------------------------------------------------------
+// Stochastic rounding of fp16 state stores.
+//
+// Philox4x32 with R rounds (Salmon, Moraes, Dror, Shaw, "Parallel random
+// numbers: as easy as 1, 2, 3", SC 2011): per round two 32 x 32 -> 64-bit
+// products of counter words with fixed multipliers, the high halves mixed with
+// the other counter words and the key, the key bumped by two Weyl constants
+// between rounds. Element e of a destination array of kind k takes word e % 4
+// of Philox(counter = (e / 4 low, e / 4 high, k, 0), key = seed).
+__device__ __forceinline__ uint4 philox4x32(uint4 c, uint32_t k0, uint32_t k1, int rounds)
+{
+    for (int r = 0; r < rounds; ++r) {
+        if (r) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint32_t hi0 = __umulhi(0xD2511F53u, c.x), lo0 = 0xD2511F53u * c.x;
+        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z), lo1 = 0xCD9E8D57u * c.z;
+        c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    }
+    return c;
+}
+
+// x rounded to one of the two fp16 values bracketing it: the one away from zero
+// with probability (|x| - |lo|) / (|hi| - |lo|) (exact in float32: a difference of
+// nearby floats over a power of two), drawn as (w >> 8) / 2^24 < probability.
+// Non-finite values and |x| > 65504 round to nearest even.
+__device__ __forceinline__ f16 sr_f16(float x, uint32_t w)
+{
+    const float a = fabsf(x);
+    const f16 rne = static_cast<f16>(x);
+    if (!(a <= 65504.0f)) return rne;
+    const uint16_t bits = __builtin_bit_cast(uint16_t, rne);
+    const uint16_t lob = fabsf(static_cast<float>(rne)) > a ? (uint16_t)(bits - 1) : bits;
+    const float l = fabsf(static_cast<float>(__builtin_bit_cast(f16, lob)));
+    const float h = fabsf(static_cast<float>(__builtin_bit_cast(f16, (uint16_t)(lob + 1))));
+    const float prob = (a - l) / (h - l);
+    const float u = static_cast<float>(w >> 8) * 0x1p-24f;
+    return __builtin_bit_cast(f16, (a != l && u < prob) ? (uint16_t)(lob + 1) : lob);
+}
+
+// Philox streams of the state arrays a kernel writes
+constexpr uint32_t kSrFinal = 0, kSrCkpt = 1, kSrStates = 2, kSrReplay = 3;
+
+// The key of one kernel's stores (seed read once); rounds = 0: nearest even.
+struct SrKey {
+    uint32_t k0 = 0, k1 = 0;
+    int rounds = 0;
+};
+// `standin`: any 8 readable bytes, loaded instead of the seed when there is none
+// (so no branch separates the load from its use)
+__device__ __forceinline__ SrKey sr_key(const SrCtx &c, const void *standin)
+{
+    const uint64_t s = *(c.seed ? c.seed : reinterpret_cast<const uint64_t *>(standin));
+    SrKey k;
+    k.k0 = (uint32_t)s;
+    k.k1 = (uint32_t)(s >> 32);
+    k.rounds = c.seed ? c.rounds : 0;
+    return k;
+}
+
+// 4 consecutive state values to storage; e = flat index of the first one in the
+// destination array (a multiple of 4), kind = its stream. Only fp16 stores round
+// stochastically.
+template <typename T>
+__device__ __forceinline__ void put4(T *p, const float *v, const SrKey &, uint64_t, uint32_t) {
+    store4<T>(p, v);
+}
+template <>
+__device__ __forceinline__ void put4<f16>(f16 *p, const float *v, const SrKey &k, uint64_t e,
+                                          uint32_t kind) {
+    if (k.rounds == 0) {
+        store4<f16>(p, v);
+        return;
+    }
+    const uint64_t blk = e >> 2;
+    const uint4 w = philox4x32(make_uint4((uint32_t)blk, (uint32_t)(blk >> 32), kind, 0u), k.k0,
+                               k.k1, k.rounds);
+    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+    f16x4 q;
+    q[0] = sr_f16(v[0], w.x);
+    q[1] = sr_f16(v[1], w.y);
+    q[2] = sr_f16(v[2], w.z);
+    q[3] = sr_f16(v[3], w.w);
+    *reinterpret_cast<f16x4 *>(p) = q;
 }
 
 // ---------------------------------------------------------------------------
@@ -221,6 +342,18 @@ template <typename T, int M> __device__ __forceinline__ void store_run(T *p, con
     static_assert(M % E == 0, "whole 16-byte vectors only");
 #pragma unroll
     for (int i = 0; i < M / E; ++i) Vec16<T>::store(p + E * i, v + E * i);
+}
+// M consecutive state values (M a multiple of 4, e as for put4)
+template <typename T, int M>
+__device__ __forceinline__ void put_run(T *p, const float *v, const SrKey &k, uint64_t e,
+                                        uint32_t kind) {
+    if constexpr (std::is_same<T, f16>::value) {
+        static_assert(M % 4 == 0, "runs of 4");
+#pragma unroll
+        for (int i = 0; i < M / 4; ++i) put4<f16>(p + 4 * i, v + 4 * i, k, e + 4 * i, kind);
+    } else {
+        store_run<T, M>(p, v);
+    }
 }
 
 // ---------------------------------------------------------------------------

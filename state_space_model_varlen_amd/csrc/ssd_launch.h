@@ -16,12 +16,21 @@ struct DtTf {
     int on = 0;
 };
 
+// Stochastic rounding of fp16 state stores: the seed is read on the device
+// (one word per step), `rounds` Philox rounds; no seed: round to nearest even.
+struct SrCtx {
+    const uint64_t *seed = nullptr;
+    int rounds = 0;
+};
+
 struct PrefillDims {
     int T, S, H, P, N, G, Q;
     int max_chunks;
     int num_slots;
     bool in_bf16;
     bool state_bf16;
+    bool state_f16 = false;   // fp16 state cache and checkpoints
+    SrCtx sr;
     // align mode: prefix[s] tokens precede sequence s, chunk boundaries fall on
     // absolute multiples of Q (nullptr: chunks start at each sequence's start)
     const int32_t *prefix = nullptr;
@@ -32,7 +41,14 @@ struct DecodeDims {
     int num_slots;
     bool in_bf16;
     bool state_bf16;
+    bool state_f16 = false;   // fp16 state cache and per-token states
+    SrCtx sr;
 };
+
+// fp32 -> fp16 with the library's stochastic rounding (kind: Philox stream of
+// the destination array), or round to nearest even without a seed.
+void launch_round_f16(const float *in, void *out, int64_t n, const SrCtx &sr, int kind,
+                      void *stream);
 
 void launch_chunk_cumsum(const PrefillDims &d, const void *dt, const float *A, const int32_t *cu,
                          int32_t *meta, float *cum, float *dto, void *stream,

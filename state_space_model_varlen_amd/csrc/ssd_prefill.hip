@@ -331,7 +331,7 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
     int S, int H, int PN, int Q, int max_chunks, int num_slots, const float *states,
     const float *__restrict__ cum, const int32_t *__restrict__ meta, TS *cache,
     const int32_t *__restrict__ idx, const uint8_t *__restrict__ has_init, TE *entering,
-    TS *__restrict__ ckpt)
+    TS *__restrict__ ckpt, SrCtx sr)
 {
     const int EB = (PN + 1023) / 1024;
     const int b = blockIdx.x;
@@ -353,6 +353,7 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
     float hs[4];
     load4<TS>(cslot, hs);
     const uint32_t keep = read_init ? 0xffffffffu : 0u;
+    const SrKey srk = sr_key(sr, meta);
 
     int c0 = meta[s], c1 = meta[s + 1];
     c0 = c0 < max_chunks ? c0 : max_chunks;
@@ -385,7 +386,7 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
             store4<TE>(entering + off, hs);
 #pragma unroll
             for (int q = 0; q < 4; ++q) hs[q] = dec[k] * hs[q] + sc[k][q];
-            if (ckpt) store4<TS>(ckpt + off, hs);
+            if (ckpt) put4<TS>(ckpt + off, hs, srk, (uint64_t)off, kSrCkpt);
         }
     };
     int cb = c0;
@@ -396,7 +397,7 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
 #pragma unroll
         for (int q = 0; q < 4; ++q) hs[q] = __uint_as_float(__float_as_uint(hs[q]) & keep);
     }
-    if (slot_ok) store4<TS>(cslot, hs);
+    if (slot_ok) put4<TS>(cslot, hs, srk, (uint64_t)(((int64_t)slot * H + h) * PN + e), kSrFinal);
 }
 
 // ===========================================================================
@@ -801,7 +802,8 @@ void state_scan_fast_kernel(
     int S, int H, int G, int max_chunks, int num_slots, const bf16 *__restrict__ x,
     const bf16 *__restrict__ B, const int32_t *__restrict__ meta, const float *__restrict__ cum,
     const float *__restrict__ dtc, TS *cache, const int32_t *__restrict__ idx,
-    const uint8_t *__restrict__ has_init, bf16 *__restrict__ entering, TS *__restrict__ ckpt)
+    const uint8_t *__restrict__ has_init, bf16 *__restrict__ entering, TS *__restrict__ ckpt,
+    SrCtx sr)
 {
     constexpr int P = 64, N = 128, NSL = kScanNSL, NS = N / NSL;
     constexpr int LDX = kScanLDX, LDB = kScanLDB;
@@ -832,6 +834,7 @@ void state_scan_fast_kernel(
     const int slot = idx[s];
     // (with no flag array, a byte of idx stands in and the flag is ignored)
     const uint8_t hflag = (has_init != nullptr ? has_init : reinterpret_cast<const uint8_t *>(idx))[s];
+    const SrKey srk = sr_key(sr, meta);
     __builtin_amdgcn_sched_barrier(0);
     c0 = c0 < max_chunks ? c0 : max_chunks;
     c1 = c1 < max_chunks ? c1 : max_chunks;
@@ -970,7 +973,7 @@ void state_scan_fast_kernel(
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     float w[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
-                    store4<TS>(ckpt + off + 16 * j, w);
+                    put4<TS>(ckpt + off + 16 * j, w, srk, (uint64_t)(off + 16 * j), kSrCkpt);
                 }
             }
         }
@@ -993,10 +996,11 @@ void state_scan_fast_kernel(
     } while (++c < c1);
 
     if (slot_ok) {
+        const int64_t fo = ((int64_t)slot * H + h) * PN + run;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             float v[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
-            store4<TS>(cslot + 16 * j, v);
+            put4<TS>(cslot + 16 * j, v, srk, (uint64_t)(fo + 16 * j), kSrFinal);
         }
     }
 }
@@ -1463,7 +1467,7 @@ static void launch_sp_t(const PrefillDims &d, const float *states, const float *
     dim3 grid((unsigned)((int64_t)d.S * d.H * EB));
     hipLaunchKernelGGL((state_passing_kernel<TS, TE>), grid, dim3(256), 0, st, d.S, d.H, PN, d.Q,
                        d.max_chunks, d.num_slots, states, cum, meta, static_cast<TS *>(cache), idx,
-                       has_init, static_cast<TE *>(entering), static_cast<TS *>(ckpt));
+                       has_init, static_cast<TE *>(entering), static_cast<TS *>(ckpt), d.sr);
 }
 
 void launch_state_passing(const PrefillDims &d, const float *states, const float *cum,
@@ -1472,7 +1476,10 @@ void launch_state_passing(const PrefillDims &d, const float *states, const float
 {
     if (d.S <= 0) return;
     hipStream_t st = as_stream(stream);
-    if (d.state_bf16) {
+    if (d.state_f16) {
+        if (d.in_bf16) launch_sp_t<f16, bf16>(d, states, cum, meta, cache, idx, has_init, entering, ckpt, st);
+        else launch_sp_t<f16, float>(d, states, cum, meta, cache, idx, has_init, entering, ckpt, st);
+    } else if (d.state_bf16) {
         if (d.in_bf16) launch_sp_t<bf16, bf16>(d, states, cum, meta, cache, idx, has_init, entering, ckpt, st);
         else launch_sp_t<bf16, float>(d, states, cum, meta, cache, idx, has_init, entering, ckpt, st);
     } else {
@@ -1495,7 +1502,7 @@ static void launch_state_scan_k(const PrefillDims &d, const void *x, const void 
     hipLaunchKernelGGL((state_scan_fast_kernel<Q, CKPT, TS>), dim3(nblk), dim3(512), smem,
                        st, d.S, d.H, d.G, d.max_chunks, d.num_slots, static_cast<const bf16 *>(x),
                        static_cast<const bf16 *>(B), meta, cum, dtc, static_cast<TS *>(cache), idx,
-                       has_init, static_cast<bf16 *>(entering), static_cast<TS *>(ckpt));
+                       has_init, static_cast<bf16 *>(entering), static_cast<TS *>(ckpt), d.sr);
 }
 
 template <int Q, typename TS>
@@ -1534,7 +1541,9 @@ void launch_state_scan(const PrefillDims &d, const void *x, const void *B, const
 {
     if (d.S <= 0) return;
     hipStream_t st = as_stream(stream);
-    if (d.state_bf16)
+    if (d.state_f16)
+        launch_state_scan_t<f16>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, st);
+    else if (d.state_bf16)
         launch_state_scan_t<bf16>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, st);
     else
         launch_state_scan_t<float>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, st);

@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256) void replay_update_kernel(
     int T, int H, int G, int num_slots, int W, TS *ckpt, TIn *ring_x, TIn *ring_dt, TIn *ring_B,
     const int32_t *__restrict__ cursor, const int32_t *__restrict__ idx, const TIn *__restrict__ x,
     const TIn *__restrict__ dt, const float *__restrict__ A, const TIn *__restrict__ B,
-    const TIn *__restrict__ C, const float *__restrict__ D, TIn *__restrict__ y)
+    const TIn *__restrict__ C, const float *__restrict__ D, TIn *__restrict__ y, SrCtx sr)
 {
     typedef ChunkMap<P, N> M;
     constexpr int CPR = M::CPR, NCH = M::NCH, KC = M::KC;
@@ -115,12 +115,13 @@ __global__ __launch_bounds__(256) void replay_update_kernel(
     }
     const float Ah = A[h];
     const float Dh = D ? D[h] : 0.0f;
+    const SrKey srk = sr_key(sr, ckpt);
 
     // checkpoint (an invalid slot reads slot 0 and is cleared bit-wise), then the history
     const uint32_t keep = slot_ok ? 0xffffffffu : 0u;
-    Raw8<TS> sr[KC];
+    Raw8<TS> cr[KC];
 #pragma unroll
-    for (int k = 0; k < KC; ++k) sr[k].load(ck + (int64_t)pk[k] * N + n0);
+    for (int k = 0; k < KC; ++k) cr[k].load(ck + (int64_t)pk[k] * N + n0);
     float st[KC][8];
 #pragma unroll
     for (int k = 0; k < KC; ++k)
@@ -131,9 +132,9 @@ __global__ __launch_bounds__(256) void replay_update_kernel(
     const float a0 = __expf(Ah * S);
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
-        sr[k].mask(keep);
+        cr[k].mask(keep);
         float s8[8];
-        sr[k].widen(s8);
+        cr[k].widen(s8);
 #pragma unroll
         for (int v = 0; v < 8; ++v) st[k][v] += a0 * s8[v];
     }
@@ -141,7 +142,9 @@ __global__ __launch_bounds__(256) void replay_update_kernel(
     if (slot_ok && n + T > L) {
 #pragma unroll
         for (int k = 0; k < KC; ++k)
-            if (tid + 256 * k < NCH) store_run<TS, 8>(ck + (int64_t)pk[k] * N + n0, st[k]);
+            if (tid + 256 * k < NCH)
+                put_run<TS, 8>(ck + (int64_t)pk[k] * N + n0, st[k], srk,
+                               (uint64_t)((cs * H + h) * PN + (int64_t)pk[k] * N + n0), kSrReplay);
     }
 
     // the window: T tokens, TM at a time, y for each; inputs appended to the ring
@@ -441,7 +444,7 @@ __global__ __launch_bounds__(256) void replay_materialize_kernel(
     int L, int H, int G, int num_slots, int W, TS *ckpt, const TIn *__restrict__ ring_x,
     const TIn *__restrict__ ring_dt, const TIn *__restrict__ ring_B,
     const int32_t *__restrict__ cursor, const int32_t *__restrict__ idx,
-    const float *__restrict__ A)
+    const float *__restrict__ A, SrCtx sr)
 {
     typedef ChunkMap<P, N> M;
     constexpr int CPR = M::CPR, NCH = M::NCH, KC = M::KC;
@@ -463,9 +466,10 @@ __global__ __launch_bounds__(256) void replay_materialize_kernel(
         pk[k] = (q < NCH ? q : NCH - 1) / CPR;
     }
     const float Ah = A[h];
-    Raw8<TS> sr[KC];
+    const SrKey srk = sr_key(sr, ckpt);
+    Raw8<TS> cr[KC];
 #pragma unroll
-    for (int k = 0; k < KC; ++k) sr[k].load(ck + (int64_t)pk[k] * N + n0);
+    for (int k = 0; k < KC; ++k) cr[k].load(ck + (int64_t)pk[k] * N + n0);
     float st[KC][8];
 #pragma unroll
     for (int k = 0; k < KC; ++k)
@@ -477,10 +481,12 @@ __global__ __launch_bounds__(256) void replay_materialize_kernel(
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
         float s8[8];
-        sr[k].widen(s8);
+        cr[k].widen(s8);
 #pragma unroll
         for (int v = 0; v < 8; ++v) st[k][v] += a0 * s8[v];
-        if (tid + 256 * k < NCH) store_run<TS, 8>(ck + (int64_t)pk[k] * N + n0, st[k]);
+        if (tid + 256 * k < NCH)
+            put_run<TS, 8>(ck + (int64_t)pk[k] * N + n0, st[k], srk,
+                           (uint64_t)((cs * H + h) * PN + (int64_t)pk[k] * N + n0), kSrReplay);
     }
 }
 
@@ -527,7 +533,7 @@ void launch_update_t(const DecodeDims &d, int W, void *ckpt, void *rx, void *rdt
                        static_cast<TIn *>(rdt), static_cast<TIn *>(rB), cursor, idx,              \
                        static_cast<const TIn *>(x), static_cast<const TIn *>(dt), A,              \
                        static_cast<const TIn *>(B), static_cast<const TIn *>(C), D,               \
-                       static_cast<TIn *>(y))
+                       static_cast<TIn *>(y), d.sr)
     if (d.T <= 1) SSD_REPLAY_LAUNCH(1);
     else if (d.T <= 2) SSD_REPLAY_LAUNCH(2);
     else if (d.T <= 3) SSD_REPLAY_LAUNCH(3);
@@ -543,7 +549,7 @@ void launch_materialize_t(const DecodeDims &d, int W, void *ckpt, const void *rx
     hipLaunchKernelGGL((replay_materialize_kernel<TIn, TS, P, N>), dim3(d.H, d.R), dim3(256), 0,
                        st, W - d.T, d.H, d.G, d.num_slots, W, static_cast<TS *>(ckpt),
                        static_cast<const TIn *>(rx), static_cast<const TIn *>(rdt),
-                       static_cast<const TIn *>(rB), cursor, idx, A);
+                       static_cast<const TIn *>(rB), cursor, idx, A, d.sr);
 }
 
 // dispatch on (in dtype, state dtype, P, N) for the shapes the GPU path supports
@@ -559,10 +565,12 @@ void dispatch(const DecodeDims &d, Args &&...args)
         else Op<TIn, TS, 16, 16>::run(d, args...);
     };
     if (d.in_bf16) {
-        if (d.state_bf16) pn(bf16(), bf16());
+        if (d.state_f16) pn(bf16(), f16());
+        else if (d.state_bf16) pn(bf16(), bf16());
         else pn(bf16(), float());
     } else {
-        if (d.state_bf16) pn(float(), bf16());
+        if (d.state_f16) pn(float(), f16());
+        else if (d.state_bf16) pn(float(), bf16());
         else pn(float(), float());
     }
 }

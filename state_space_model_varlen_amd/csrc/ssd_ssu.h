@@ -16,6 +16,13 @@ __device__ __forceinline__ void store8_nt(bf16 *p, const float *v) {
     for (int i = 0; i < 8; ++i) q[i] = static_cast<bf16>(v[i]);
     __builtin_nontemporal_store(__builtin_bit_cast(u32x4, q), reinterpret_cast<u32x4 *>(p));
 }
+__device__ __forceinline__ void store8_nt(f16 *p, const float *v) {
+    typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+    f16x8 q;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = static_cast<f16>(v[i]);
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, q), reinterpret_cast<u32x4 *>(p));
+}
 __device__ __forceinline__ void store8_nt(float *p, const float *v) {
     const f32x4 lo = {v[0], v[1], v[2], v[3]}, hi = {v[4], v[5], v[6], v[7]};
     __builtin_nontemporal_store(lo, reinterpret_cast<f32x4 *>(p));
@@ -37,6 +44,18 @@ template <> struct Raw8<bf16> {
             f[2 * i] = __uint_as_float(u[i] << 16);
             f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
         }
+    }
+};
+template <> struct Raw8<f16> {
+    uint4 w;
+    __device__ __forceinline__ void load(const f16 *p) { w = *reinterpret_cast<const uint4 *>(p); }
+    __device__ __forceinline__ void mask(uint32_t m) { w.x &= m; w.y &= m; w.z &= m; w.w &= m; }
+    __device__ __forceinline__ void store(f16 *p) const { *reinterpret_cast<uint4 *>(p) = w; }
+    __device__ __forceinline__ void widen(float *f) const {
+        typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+        const f16x8 q = __builtin_bit_cast(f16x8, w);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = static_cast<float>(q[i]);
     }
 };
 template <> struct Raw8<float> {

@@ -20,6 +20,7 @@ import torch
 import oracle
 from oracle import chunked, dual
 from oracle import replay as oracle_replay
+from oracle import rounding as oracle_rounding
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -463,9 +464,73 @@ def pin_aligned_checkpoints(lib=None):
     np.testing.assert_allclose(suf["ckpt"], whole[1:], rtol=1e-12, atol=1e-14)
 
 
+def pin_philox_known_answers(lib=None, rnd=None):
+    """Philox4x32-10 against the generator's published known-answer vectors
+    (tests/golden), and the per-element word layout of the state stores."""
+    r = rnd or oracle_rounding
+    with open(os.path.join(GOLDEN, "philox4x32_10_kat.json")) as f:
+        cases = json.load(f)["cases"]
+    for cs in cases:
+        ctr = np.array([int(v, 16) for v in cs["counter"]], dtype=np.uint32)
+        key = np.array([int(v, 16) for v in cs["key"]], dtype=np.uint32)
+        got = r.philox4x32(ctr, key, 10)
+        assert [int(v) for v in got] == [int(v, 16) for v in cs["out"]], cs
+    # element e of stream k takes word e % 4 of the block e // 4
+    seed, kind = 0x0123456789ABCDEF, 3
+    w = r.words_for(11, seed, kind, 7, first=(1 << 34) + 2)
+    for j, e in enumerate(range((1 << 34) + 2, (1 << 34) + 13)):
+        blk = e // 4
+        ctr = np.array([blk & 0xFFFFFFFF, blk >> 32, kind, 0], dtype=np.uint32)
+        key = np.array([seed & 0xFFFFFFFF, seed >> 32], dtype=np.uint32)
+        assert int(w[j]) == int(r.philox4x32(ctr, key, 7)[e % 4])
+
+
+def pin_stochastic_rounding(lib=None, rnd=None):
+    """fp32 -> fp16 stochastic rounding: the two candidates are the fp16 values
+    bracketing x (found by brute force over every finite fp16 value), the draw
+    u = (w >> 8) / 2^24 goes up exactly when u < (|x| - |lo|) / (|hi| - |lo|),
+    representable and special values pass unchanged or round to nearest, and the
+    mean over random words is x."""
+    r = rnd or oracle_rounding
+    allh = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    fin = np.unique(allh[np.isfinite(allh)].astype(np.float32))
+    g = np.random.default_rng(171)
+    x = np.concatenate([g.standard_normal(400) * 0.03, g.standard_normal(200) * 30.0,
+                        g.uniform(-6e-5, 6e-5, 200), g.uniform(-3e-7, 3e-7, 50)]
+                       ).astype(np.float32)
+    exact = np.isin(x, fin)
+    i = np.searchsorted(fin, np.abs(x), side="right") - 1      # largest magnitude <= |x|
+    lo_mag, hi_mag = fin[i], fin[np.minimum(i + 1, len(fin) - 1)]
+    sign = np.where(x < 0, -1.0, 1.0).astype(np.float32)
+    up = r.stochastic_round_f16(x, np.zeros(len(x), np.uint32)).astype(np.float32)
+    down = r.stochastic_round_f16(x, np.full(len(x), 0xFFFFFFFF, np.uint32)).astype(np.float32)
+    np.testing.assert_array_equal(down, sign * lo_mag)
+    np.testing.assert_array_equal(up[~exact], (sign * hi_mag)[~exact])
+    np.testing.assert_array_equal(up[exact], x[exact])
+    # the threshold: x half way between neighbours goes up for u just below 1/2 only
+    half = np.float32(1.0 + 2.0 ** -11)                          # fp16 ulp at 1 is 2^-10
+    w_lo = np.array([(2 ** 23 - 1) << 8], np.uint32)
+    w_hi = np.array([(2 ** 23) << 8], np.uint32)
+    assert float(r.stochastic_round_f16(np.array([half]), w_lo)[0]) == 1.0 + 2.0 ** -10
+    assert float(r.stochastic_round_f16(np.array([half]), w_hi)[0]) == 1.0
+    assert float(r.stochastic_round_f16(np.array([-half]), w_lo)[0]) == -(1.0 + 2.0 ** -10)
+    # specials: nearest even
+    sp = np.array([np.inf, -np.inf, 70000.0, 65510.0, 0.0], np.float32)
+    got = r.stochastic_round_f16(sp, np.zeros(5, np.uint32)).astype(np.float32)
+    np.testing.assert_array_equal(got, [np.inf, -np.inf, np.inf, 65504.0, 0.0])
+    assert np.isnan(r.stochastic_round_f16(np.array([np.nan], np.float32), [0])[0])
+    # unbiased: 4096 random words per value
+    xs = np.repeat(x[:64], 4096)
+    ws = g.integers(0, 2 ** 32, size=len(xs), dtype=np.uint64).astype(np.uint32)
+    mean = r.stochastic_round_f16(xs, ws).astype(np.float64).reshape(64, 4096).mean(axis=1)
+    ulp = (hi_mag - lo_mag)[:64].astype(np.float64)
+    assert np.all(np.abs(mean - x[:64]) <= 6 * 0.5 * ulp / 64.0 + 1e-12)
+
+
 ALL_PINS = [pin_hand_worked, pin_single_token_closed_form, pin_cumsum_reduction, pin_pure_decay,
             pin_skip_only, pin_linearity, pin_dual_form, pin_continued_prefill,
             pin_varlen_packing, pin_checkpoints_are_truncated_finals,
             pin_chunk_size_independence, pin_state_update_replay, pin_cache_semantics,
             pin_bf16_rounding, pin_replay_matches_recurrence, pin_dt_preprocess,
-            pin_varlen_update_is_prefill, pin_aligned_checkpoints]
+            pin_varlen_update_is_prefill, pin_aligned_checkpoints, pin_philox_known_answers,
+            pin_stochastic_rounding]

@@ -200,3 +200,38 @@ def test_dt_transform_and_varlen_validation():
     g = lib.ssd_state_commit_varlen
     assert g(ctypes.byref(up), 6, None, ok, ok, ok, ok, None) == 1
     assert g(ctypes.byref(up), 6, ok, ok, ok, ctypes.c_void_p(264), ok, None) == 7
+
+
+def test_fp16_state_and_options_validation():
+    """fp16 is a state dtype only; stochastic rounding needs an fp16 state and 1..16
+    Philox rounds; NULL arrays are refused (nothing is launched in these cases)."""
+    lib = ssd._lib
+    ok = ctypes.c_void_p(256)
+    seed = ctypes.c_void_p(512)
+    p16 = P(state_dtype=torch.float16)
+    assert ssd.workspace_bytes(p16) > 0
+    bad_in = P()
+    bad_in.in_dtype = 2
+    assert ssd.workspace_bytes(bad_in) == 0
+    opt = ssd.ssd_options(None, None, seed.value, 10)
+    pf32 = P()
+    assert lib.ssd_combined_varlen_ex(ctypes.byref(pf32), ctypes.byref(opt), *([ok] * 13),
+                                      ctypes.c_size_t(1 << 30), None) == 4
+    opt0 = ssd.ssd_options(None, None, seed.value, 0)
+    assert lib.ssd_combined_varlen_ex(ctypes.byref(p16), ctypes.byref(opt0), *([ok] * 13),
+                                      ctypes.c_size_t(1 << 30), None) == 2
+    a = [ok] * 13
+    a[0] = None
+    assert lib.ssd_combined_varlen_ex(ctypes.byref(p16), ctypes.byref(opt), *a,
+                                      ctypes.c_size_t(1 << 30), None) == 1
+    up = ssd.make_ssu_problem(2, 3, 8, 64, 128, 2, 4, torch.bfloat16, torch.float16)
+    args = [ok] * 7 + [None, None, None]     # cache .. C, D, y = NULL, inter
+    assert lib.selective_state_update_ex(ctypes.byref(up), ctypes.byref(opt), 6, None, *args,
+                                         None) == 1
+    assert lib.ssd_round_f16(None, ok, 8, None, 10, 0, None) == 1
+    assert lib.ssd_round_f16(ok, ok, -1, None, 10, 0, None) == 2
+    assert lib.ssd_round_f16(ok, ok, 8, seed, 17, 0, None) == 2
+    assert lib.ssd_round_f16(ok, ok, 0, None, 10, 0, None) == 0     # nothing to do
+    ub = ssd.make_ssu_problem(2, 3, 8, 64, 128, 2, 4, torch.bfloat16, torch.bfloat16)
+    assert lib.ssd_replay_update_ex(ctypes.byref(ub), ctypes.byref(opt), 6,
+                                    *([ok] * 11), None, ok, None) == 4

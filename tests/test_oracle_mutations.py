@@ -188,3 +188,36 @@ def test_aligned_cut_mutation_is_caught(bad, monkeypatch):
     monkeypatch.setattr(oracle, "aligned_chunks", bad)
     with pytest.raises(AssertionError):
         oracle_pins.pin_aligned_checkpoints()
+
+
+# Planted mistakes in the generator and the rounding (copies of oracle/rounding.py).
+ROUNDING_SRC = os.path.join(os.path.dirname(oracle.__file__), "rounding.py")
+ROUNDING_MUTATIONS = [
+    ("wrong_multiplier", "M0, M1 = 0xD2511F53, 0xCD9E8D57", "M0, M1 = 0xD2511F55, 0xCD9E8D57"),
+    ("key_not_bumped", "            k0 = (k0 + W0) & MASK\n", "            k0 = k0\n"),
+    ("words_swapped", "c = [hi1 ^ c[1] ^ k0, lo1, hi0 ^ c[3] ^ k1, lo0]",
+     "c = [hi0 ^ c[1] ^ k0, lo1, hi1 ^ c[3] ^ k1, lo0]"),
+    ("rounds_up_at_equality", "out = np.where(u < prob, hi, lo)", "out = np.where(u <= prob, hi, lo)"),
+    ("rounds_toward_the_nearer", "out = np.where(u < prob, hi, lo)",
+     "out = np.where(u < 1 - prob, hi, lo)"),
+    ("stream_ignored", "np.full_like(blk, kind)", "np.zeros_like(blk)"),
+]
+
+
+@pytest.mark.parametrize("mut", ROUNDING_MUTATIONS, ids=lambda m: m[0])
+def test_rounding_mutation_is_caught(mut, tmp_path):
+    name, old, new = mut
+    src = open(ROUNDING_SRC).read()
+    assert src.count(old) == 1, f"mutation {name}: text not found once in oracle/rounding.py"
+    path = tmp_path / f"rounding_{name}.py"
+    path.write_text(src.replace(old, new))
+    spec = importlib.util.spec_from_file_location(f"rounding_{name}", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    caught = False
+    for pin in (oracle_pins.pin_philox_known_answers, oracle_pins.pin_stochastic_rounding):
+        try:
+            pin(rnd=mod)
+        except AssertionError:
+            caught = True
+    assert caught, f"no pin catches the planted mistake '{name}'"
