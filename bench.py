@@ -38,8 +38,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, published
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # (200 timed steps of ~0.09 ms: long enough that the clocks have settled, as in a
+    # serving loop; shorter runs read the clock ramp)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (for scaling HBM counters)")
@@ -76,13 +78,17 @@ def prefill_bytes(T, S, H, P, N, G, Q, nc, ex, es, s_init, checkpoints):
 
 
 # kernel name fragment (as rocprofv3 prints it) -> (name used here, source files it is built from)
+_PRE = ["ssd_prefill.hip", "ssd_device.h", "ssd_launch.h"]
+_DEC = ["ssd_decode.hip", "ssd_device.h", "ssd_launch.h", "ssd_ssu.h"]
 KERNELS = {
-    "chunk_prep_kernel": ("chunk_prep", ["ssd_prefill.hip", "ssd_device.h"]),
-    "chunk_cumsum_kernel": ("chunk_cumsum", ["ssd_prefill.hip", "ssd_device.h"]),
-    "bmm_kernel": ("bmm_chunk", ["ssd_prefill.hip", "ssd_device.h"]),
-    "state_scan_fast_kernel": ("chunk_state_passing", ["ssd_prefill.hip", "ssd_device.h"]),
-    "chunk_scan_fast_kernel": ("chunk_scan", ["ssd_prefill.hip", "ssd_device.h"]),
-    "state_update_kernel": ("selective_state_update", ["ssd_decode.hip", "ssd_device.h"]),
+    "chunk_prep_kernel": ("chunk_prep", _PRE),
+    "chunk_cumsum_kernel": ("chunk_cumsum", _PRE),
+    "bmm_kernel": ("bmm_chunk", _PRE),
+    "state_scan_fast_kernel": ("chunk_state_passing", _PRE),
+    "chunk_scan_fast_kernel": ("chunk_scan", _PRE),
+    "state_update_kernel": ("selective_state_update", _DEC),
+    "replay_update_fast_kernel": ("replay_update", ["ssd_replay.hip", "ssd_device.h",
+                                                    "ssd_launch.h", "ssd_ssu.h"]),
 }
 CSRC = os.path.join("state_space_model_varlen_amd", "csrc")
 CALIBRATION_BYTES = 256 << 20   # the --copy-calibration copy
@@ -367,6 +373,9 @@ def main():
         a = acc_seq[k % nsteps].cpu().numpy()
         hist = np.where(ck, 1 + a, hist + 1 + a)
     replay_bytes //= nsteps
+    replay_kernel_us = avg_us(lambda: ssd.ssd_replay_update(
+        up, W, rck, rings["ring_x"], rings["ring_dt"], rings["ring_B"], rings["cursor"], didx,
+        dx, ddt, dA, dB, dC, dD, ry, stream))
     replay = {"workload": "mtp_verify_replayssm R=128 T=3 H=128 P=64 N=128 G=8 bf16, ring 16",
               "metric": "decode updates/s", "value": round(R * TT / (replay_us * 1e-6), 1),
               "unit": "updates/s", "avg_us_per_step": round(replay_us, 3),
@@ -375,8 +384,53 @@ def main():
                            "achieved": round(replay_bytes / (replay_us * 1e-6) / 1e9, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(replay_bytes / (replay_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                           "bytes": replay_bytes}}
+                           "bytes": replay_bytes,
+                           "traffic": load_traffic("replay_update")},
+              "verify_kernel_us_at_end_state": round(replay_kernel_us, 3)}
     del rings, rck
+
+    # ------------------------------------------------------------------ steps either side
+    # (context): the layer's dt preprocessing fused into the c1 call, the MTP verify as a
+    # packed varlen batch (1-3 tokens per request), and fp16 states with Philox
+    # stochastic rounding (the c4 verify with per-token states, 5 rounds)
+    extras = {}
+    if not args.headline_only:
+        bias = torch.from_numpy(inp.dt_bias).float().to(dev)
+        tf = ssd.make_dt_transform(bias, sy.DT_MIN, sy.DT_MAX)
+        raw = inp.dt_raw.to(dev)
+        fused_us = avg_us(lambda: ssd.ssd_combined_varlen_dt(p, tf, x, raw, A, B, C, D, cu, cache,
+                                                             idx, None, y, None, ws, stream))
+        extras["prefill_dt_fused_c1"] = {"combined_us": round(fused_us, 3),
+                                         "tokens_per_s": round(T / (fused_us * 1e-6), 1)}
+        counts = torch.from_numpy(np.random.default_rng(5).integers(1, TT + 1, size=R)
+                                  .astype(np.int32))
+        vcu = torch.zeros(R + 1, dtype=torch.int32)
+        vcu[1:] = torch.cumsum(counts, 0)
+        Tt = int(vcu[-1])
+        flat = lambda t: t.reshape(-1, *t.shape[2:])[:Tt].contiguous()
+        vx, vdt, vB, vC = flat(dx), flat(ddt), flat(dB), flat(dC)
+        vy = torch.empty(Tt, DH, DP, dtype=dcfg.in_dtype, device=dev)
+        vinter = torch.empty(Tt, DH, DP, DN, dtype=dcfg.state_dtype, device=dev)
+        vcu = vcu.to(dev)
+        var_us = avg_us(lambda: ssd.selective_state_update_varlen(up, vcu, dcache, didx, vx, vdt,
+                                                                  dA, vB, vC, dD, vy, vinter,
+                                                                  stream=stream))
+        extras["decode_varlen_mtp"] = {"tokens": Tt, "avg_us": round(var_us, 3),
+                                       "updates_per_s": round(Tt / (var_us * 1e-6), 1)}
+        del vinter
+        up16 = ssd.make_ssu_problem(R, TT, DH, DP, DN, DG, dcfg.num_slots, dcfg.in_dtype,
+                                    torch.float16)
+        c16 = dcache.to(torch.float16)
+        i16 = torch.empty(R, TT, DH, DP, DN, dtype=torch.float16, device=dev)
+        seed = torch.tensor([12345], dtype=torch.int64, device=dev)
+        for name, opt in (("fp16_nearest", ssd.make_options()),
+                          ("fp16_stochastic_philox5", ssd.make_options(sr_seed=seed, sr_rounds=5))):
+            us16 = avg_us(lambda: ssd.selective_state_update_ex(up16, opt, c16, didx, dx, ddt, dA,
+                                                                dB, dC, dD, dy, i16,
+                                                                stream=stream))
+            extras[f"decode_{name}"] = {"avg_us": round(us16, 3),
+                                        "updates_per_s": round(R * TT / (us16 * 1e-6), 1)}
+        del c16, i16
 
     # ------------------------------------------------------------------ other prefill shapes
     # (context, not the headline): the cached short continuation and the mixed varlen
@@ -423,6 +477,17 @@ def main():
             "state_passing_step": {"avg_us": round(sp_us, 3), "bytes": sp_bytes,
                                    "GBps": round(sp_bytes / (sp_us * 1e-6) / 1e9, 1),
                                    "frac": round(sp_bytes / (sp_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}}
+        if cname == "mixed_varlen_8seq_ckpt":
+            # the same batch in align mode: odd sequences follow 4224 cached tokens
+            pre = torch.tensor([ocfg.prefix_len if int(oin.has_initial[s]) else 0
+                                for s in range(oS)], dtype=torch.int32, device=dev)
+            ack = torch.empty(ssd.max_chunks_aligned(op), oH, oP, oN, dtype=ocfg.state_dtype,
+                              device=dev)
+            aws = ssd.alloc_workspace_aligned(op, dev)
+            al_us = avg_us(lambda: ssd.ssd_combined_varlen_aligned(
+                op, pre, ox, odt, oA, oB, oC, oD, ocu, ocache, oidx, ohi, oy, ack, aws, stream))
+            others[cname]["aligned_combined_us"] = round(al_us, 3)
+            del ack, aws
         del ox, odt, oB, oC, oy, ows, obuf, ocache, ock
 
     # achievable HBM bandwidth on this machine, for context: a plain 1 GiB device copy
@@ -485,6 +550,7 @@ def main():
         "decode": decode,
         "decode_replayssm": replay,
         "other_prefill_shapes": others,
+        "steps_either_side": extras,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

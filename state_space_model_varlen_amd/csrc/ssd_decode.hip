@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(
         for (int j = 0; j < TM; ++j) {
             const int t = t0 + j < Tr ? t0 + j : Tr - 1;
             const int64_t rt = (int64_t)tb + t;
-            dtv[j] = dt_apply(tf, to_f32(dt[rt * H + h]), bh);
+            dtv[j] = to_f32(dt[rt * H + h]);
             braw[j].load(B + (rt * G + g) * N + n0);
             craw[j].load(C + (rt * G + g) * N + n0);
 #pragma unroll
@@ -104,6 +104,10 @@ __global__ __launch_bounds__(256) void state_update_kernel(
     int t0 = 0;
     do {
         if (t0 > 0) load_group(t0);
+        if (tf.on) {
+#pragma unroll
+            for (int j = 0; j < TM; ++j) dtv[j] = dt_transform(tf, dtv[j], bh);
+        }
 #pragma unroll
         for (int j = 0; j < TM; ++j) {
             if (t0 + j >= Tr) break;

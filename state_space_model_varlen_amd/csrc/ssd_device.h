@@ -119,11 +119,13 @@ template <> struct Mma<float> {
 };
 
 // Step-size preprocessing (see DtTf): softplus(v) = log(1 + exp(v)), v itself
-// above 20, then the clamp; `bias` is bias[h], read once by the caller.
-__device__ __forceinline__ float dt_apply(const DtTf &tf, float raw, float bias) {
+// above 20, then the clamp; `bias` is bias[h], read once by the caller. Callers
+// test tf.on once per group of already-loaded values (a branch right after a
+// load would make the compiler wait on that load there).
+__device__ __forceinline__ float dt_transform(const DtTf &tf, float raw, float bias) {
     const float v = raw + bias;
     const float sp = v > 20.0f ? v : log1pf(__expf(v));
-    return tf.on ? fminf(fmaxf(sp, tf.lo), tf.hi) : raw;
+    return fminf(fmaxf(sp, tf.lo), tf.hi);
 }
 
 // LDS writes of a wave made visible to the same wave's later reads.

@@ -136,8 +136,16 @@ __device__ __forceinline__ void cumsum_wave(int H, int Q, int max_chunks, int c,
     for (int e = 0; e < 4; ++e) {
         const int i = lane * E + e;
         const int ic = i < ci.len ? i : ci.len - 1;
-        const float v = dt_apply(tf, to_f32(dt[(int64_t)(ci.start + ic) * H + h]), bh);
-        vals[e] = (e < E && i < ci.len) ? v : 0.0f;
+        vals[e] = to_f32(dt[(int64_t)(ci.start + ic) * H + h]);
+    }
+    if (tf.on) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vals[e] = dt_transform(tf, vals[e], bh);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int i = lane * E + e;
+        vals[e] = (e < E && i < ci.len) ? vals[e] : 0.0f;
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
