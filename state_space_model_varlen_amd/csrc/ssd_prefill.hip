@@ -1026,7 +1026,10 @@ void state_scan_fast_kernel(
 // of eight. Within a block both factors stay in [exp(-span), exp(span)], span
 // = |cum| change over the block; a block whose span exceeds kMaxSpan (where
 // float32/bf16 range could be lost) is computed with the exact per-element
-// exponentials on unscaled x instead.
+// exponentials on unscaled x instead. When the whole chunk's span fits, one
+// reference serves every block (R = cum at the chunk's end): x' carries
+// exp(R - cum_j) dt_j, A is CB exactly as stored (no arithmetic per K step),
+// and each output row is scaled once by exp(cum_i - R) after the loop.
 //   acc  = sum_j A_ij x'_j,   A_ij = CB[i,j] exp(cum_i - R_k) [j <= i]    (MFMA)
 //   acc += (exp(cum_i) C_i) . H_in^T                                        (MFMA)
 //   y_i  = acc + D_h x_i
@@ -1057,7 +1060,7 @@ __device__ __forceinline__ void load_cb_frags(const bf16 *CBc, int Q, int rt, in
 // (row tile nrt, nnk steps) are requested after this tile's intra-chunk loop.
 template <int Q, int K, int KN>
 __device__ __forceinline__ void scan_row_tile(
-    int i0, int nk, const uint4 *cbf, bool exact, int len, int lane,
+    int i0, int nk, const uint4 *cbf, bool exact, bool single, float rs, int len, int lane,
     rsrc_t rc, uint32_t crow, const float *scum, const float *sdt, const bf16 *xs, const bf16 *hs,
     bf16 *yw, rsrc_t rx, uint32_t xrow, int H, float Dh, bf16 *yout, const bf16 *CBc, int nrt,
     int nnk, uint4 *ncf, bool prefetch_next)
@@ -1092,7 +1095,11 @@ __device__ __forceinline__ void scan_row_tile(
                                   bf16_hi(cbf[ks].y), bf16_lo(cbf[ks].z), bf16_hi(cbf[ks].z),
                                   bf16_lo(cbf[ks].w), bf16_hi(cbf[ks].w)};
             bf16x8 af;
-            if (!exact) {
+            if (single) {
+                // whole-chunk reference: x' carries exp(R - cum_j) dt_j, the row factor
+                // exp(cum_i - R) comes after the loop, so A is CB as stored
+                af = __builtin_bit_cast(bf16x8, cbf[ks]);
+            } else if (!exact) {
                 // CB is zero above the diagonal (see bmm), and e is finite: no mask
                 const float e = __builtin_amdgcn_exp2f(ci2 - scum[j0 + 31 < Q ? j0 + 31 : Q - 1]);
 #pragma unroll
@@ -1132,6 +1139,14 @@ __device__ __forceinline__ void scan_row_tile(
     float erow[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) erow[v] = __builtin_amdgcn_exp2f(scum[i0 + 4 * kg + v]);
+    if (single) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float f = __builtin_amdgcn_exp2f(scum[i0 + 4 * kg + v] - rs);
+#pragma unroll
+            for (int pt = 0; pt < P / 16; ++pt) acc[pt][v] *= f;
+        }
+    }
 #pragma unroll
     for (int pt = 0; pt < P / 16; ++pt)
 #pragma unroll
@@ -1253,13 +1268,18 @@ void chunk_scan_fast_kernel(
         big |= fabsf(rk - scum[t]) > kMaxSpan * kLog2e;
     }
     const bool exact = __syncthreads_or(big) != 0;
+    // whole-chunk reference when the chunk's decay span fits (every factor in
+    // [exp(-span), exp(span)]): R = cum at the chunk's end (positions past it hold it)
+    const float rs = scum[Q - 1];
+    const bool single = !exact && scum[0] - rs <= kMaxSpan * kLog2e;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int u = tid + nthr * k;
         const int t = u >> 3, c8 = u & 7;
         uint4 v = xr[k];
         if (!exact) {
-            const float gt = __builtin_amdgcn_exp2f(scum[(t | 31) < Q ? (t | 31) : Q - 1] - scum[t]) *
+            const float rk = single ? rs : scum[(t | 31) < Q ? (t | 31) : Q - 1];
+            const float gt = __builtin_amdgcn_exp2f(rk - scum[t]) *
                              sdt[t];
             float f[8];
             const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
@@ -1280,11 +1300,13 @@ void chunk_scan_fast_kernel(
 
     // tile B first (larger); tile A's CB fragments are requested once B's are consumed
     uint4 caf[kStepsA];
-    scan_row_tile<Q, kStepsB, kStepsA>(16 * rtB, nkB, cbf, exact, len, lane, rc, crow, scum, sdt,
+    scan_row_tile<Q, kStepsB, kStepsA>(16 * rtB, nkB, cbf, exact, single, rs, len, lane, rc, crow,
+                                       scum, sdt,
                                        xs, hs, yw, rx, xrow, H, Dh,
                                        y + ((int64_t)ci.start * H + h) * P, CBc, rtA, nkA, caf,
                                        true);
-    scan_row_tile<Q, kStepsA, kStepsA>(16 * rtA, nkA, caf, exact, len, lane, rc, crow, scum, sdt,
+    scan_row_tile<Q, kStepsA, kStepsA>(16 * rtA, nkA, caf, exact, single, rs, len, lane, rc, crow,
+                                       scum, sdt,
                                        xs, hs, yw, rx, xrow, H, Dh,
                                        y + ((int64_t)ci.start * H + h) * P, CBc, 0, 0, caf, false);
 }

@@ -385,3 +385,32 @@ def test_c2_cached_short_continuation_full():
 
 def test_c3_mixed_varlen_full():
     _sampled_continuation(sy.C3, seqs=list(range(8)), heads=[0, 9, 36, 63], checkpoints=True)
+
+
+@pytest.mark.parametrize("dt_scale", [1.0, 12.0, 40.0], ids=["whole_chunk", "per_block", "exact"])
+def test_decay_span_modes(dt_scale):
+    """The bf16 chunk scan picks its decay reference by span: the whole chunk (span
+    <= 60 over the chunk), 32-token blocks (span <= 60 per block) or per element.
+    The workload's dt reaches only the first two; scaled step sizes reach all
+    three (every sequence here has full chunks, ragged tails and a cached state).
+    (Far larger steps make a chunk's cumulative decay so large in magnitude that
+    differences of its float32 prefix sums lose accuracy, as in any chunked scan
+    built on cumsum differences; dt x 40 keeps it below about 3e4.)"""
+    lens, H, P, N, G, Q = (600, 257, 31), 8, 64, 128, 2, 256
+    S = len(lens)
+    inp = sy.random_problem(900 + int(dt_scale), lens, H, P, N, G, Q, BF16, F32,
+                            num_slots=2 * S, has_initial=[True] * S)
+    inp.dt = (inp.dt.float() * dt_scale).to(BF16)
+    cache = _cache_with_states(inp, 2 * S, F32)
+    y, after, ckpt = gpu_prefill(inp, cache, Q, checkpoints=True)
+    ref = oracle.prefill(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.cu_seqlens,
+                         inp.state_indices, inp.has_initial, cache, Q, checkpoints=True)
+    assert_close(y, ref["y"], BF16, f"y (dt x {dt_scale})", normalised=False)
+    used = inp.state_indices.long()
+    assert_close(after[used], ref["final"], BF16, "final states")
+    nc = len(ref["ckpt"])
+    assert_close(ckpt[:nc], ref["ckpt"], BF16, "checkpoints")
+    yd, _, _ = gpu_prefill(inp, cache, Q, D=False)
+    refd = oracle.prefill(inp.x, inp.dt, inp.A, inp.B, inp.C, None, inp.cu_seqlens,
+                          inp.state_indices, inp.has_initial, cache, Q)
+    assert_close(yd, refd["y"], BF16, f"y without D (dt x {dt_scale})")
