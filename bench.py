@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Throughput of the MI355X SSD varlen prefill scan (and the MTP state update).
 
-One step = one ssd_combined_varlen call (three launches: chunk cumsum with bmm,
-chunk state with state passing, chunk scan) over the single-sequence Mamba2 layer prefill:
+One step = one ssd_combined_varlen call (chunk cumsum with bmm; chunk state with
+state passing, here cut into 3 parallel segments per head and chained by a carry
+step; chunk scan) over the single-sequence Mamba2 layer prefill:
 L = 4096 tokens, 80 heads, headdim 64, d_state 128, 1 group, chunk 256, bf16
 x/B/C/dt, fp32 A/D/state. Inputs are seeded synthetic draws, resident in HBM
 before the timed region. `value` = tokens / s of that call (one layer).
@@ -85,6 +86,7 @@ KERNELS = {
     "chunk_cumsum_kernel": ("chunk_cumsum", _PRE),
     "bmm_kernel": ("bmm_chunk", _PRE),
     "state_scan_fast_kernel": ("chunk_state_passing", _PRE),
+    "state_carry_kernel": ("state_carry", _PRE),
     "chunk_scan_fast_kernel": ("chunk_scan", _PRE),
     "state_update_kernel": ("selective_state_update", _DEC),
     "replay_update_fast_kernel": ("replay_update", ["ssd_replay.hip", "ssd_device.h",
@@ -127,12 +129,22 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, cmds):
     dispatch) are scaled by what the same counter reads for the 256 MiB
     calibration copy (the last copy dispatch of the run)."""
     import csv
+    import re
 
     def short(name):
+        """Report name of a kernel; the variants of the segmented state pass that
+        the combined call runs for this layer get their own rows."""
         for frag, (nm, _) in KERNELS.items():
             if frag in name:
-                return nm
+                m = re.search(r"state_scan_fast_kernelILi\d+ELb[01]ELb1E", name) or \
+                    re.search(r"chunk_scan_fast_kernelILi\d+ELb1E", name)
+                return nm + "_segmented" if m else nm
         return None
+
+    def sources(nm):
+        base = nm[:-len("_segmented")] if nm.endswith("_segmented") else nm
+        return [os.path.join(CSRC, p) for p in next(v[1] for v in KERNELS.values()
+                                                    if v[0] == base)]
 
     stats = list(csv.DictReader(open(os.path.join(trace_dir, "c1_kernel_stats.csv"))))
     counters = {}
@@ -153,7 +165,11 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, cmds):
              "", "Command (MI355X, one GPU, from the repository root):", "```", cmds[0], "```",
              "Source: `c1_kernel_stats.csv` written by that command (rocprofv3 `--stats`). "
              "Prefill kernels run inside ssd_combined_varlen (warm-up + timed steps) and alone "
-             "(per-kernel timing); torch kernels (input casts, copies) omitted.", "",
+             "(per-kernel timing, the step-wise entry points); torch kernels (input casts, "
+             "copies) omitted. For this layer (one sequence, 80 heads) the combined call cuts "
+             "each head's chunk chain into 3 segments: its state pass, carry step and chunk "
+             "scan are the `_segmented` / `state_carry` rows; the step-wise entry points run "
+             "the unsegmented kernels (the plain rows).", "",
              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     for r in stats:
         nm = short(r["Name"])
@@ -174,7 +190,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, cmds):
         f, w = counters["FETCH_SIZE"][nm], counters["WRITE_SIZE"][nm]
         fb, wb = f * 1024 * scale["FETCH_SIZE"], w * 1024 * scale["WRITE_SIZE"]
         lines.append(f"| {nm} | {f:.1f} | {w:.1f} | {fb + wb:.0f} |")
-        srcs = [os.path.join(CSRC, p) for p in next(v[1] for v in KERNELS.values() if v[0] == nm)]
+        srcs = sources(nm)
         with open(os.path.join(ROOT, "profiles", f"traffic_{nm}.json"), "w") as fh:
             json.dump({"kernel": nm, "sources": srcs, "source_sha": source_sha(srcs),
                        "fetch_bytes": round(fb), "write_bytes": round(wb),

@@ -118,6 +118,10 @@ size_t round_up(size_t v) { return (v + 255) & ~(size_t)255; }
 // Workspace of ssd_combined_varlen, 256-byte aligned pieces in this order.
 struct Workspace {
     size_t meta, cum, dt, cb, states, entering, total;
+    // segmented state passing (nseg > 1): per-segment final states, starting
+    // states, decays, and per-chunk decay / segment index
+    int nseg;
+    size_t seg_fin, seg_carry, seg_L, seg_F, seg_I;
 };
 
 Workspace workspace_layout(const ssd_problem *p, bool aligned = false)
@@ -134,7 +138,15 @@ Workspace workspace_layout(const ssd_problem *p, bool aligned = false)
     // the fused state kernel keeps chunk states in registers: no buffer for them
     const size_t nstates = ssd::fused_state_path(dims_of(p)) ? 0 : mc * H * P * N;
     w.entering = w.states + round_up(sizeof(float) * nstates);
-    w.total = w.entering + round_up(ein * mc * H * P * N);
+    w.seg_fin = w.entering + round_up(ein * mc * H * P * N);
+    w.nseg = ssd::state_segments(dims_of(p, aligned));
+    const size_t nsb = w.nseg > 1 ? (size_t)p->num_seqs * w.nseg : 0;
+    const size_t nsc = w.nseg > 1 ? mc : 0;
+    w.seg_carry = w.seg_fin + round_up(sizeof(float) * nsb * H * P * N);
+    w.seg_L = w.seg_carry + round_up(2 * nsb * H * P * N);
+    w.seg_F = w.seg_L + round_up(sizeof(float) * nsb * H);
+    w.seg_I = w.seg_F + round_up(sizeof(float) * nsc * H);
+    w.total = w.seg_I + round_up(sizeof(int32_t) * nsc);
     return w;
 }
 
@@ -316,15 +328,26 @@ static int combined(const ssd_problem *p, const ssd::DtTf &tf, const void *x, co
     void *entering = base + w.entering;
 
     ssd::launch_chunk_prep(d, dt, A, cu_seqlens, meta, cum, dtc, B, C, cb, stream, tf);
+    // segmented state passing when the state kernel alone would leave CUs idle
+    // (not with checkpoints, which need every chunk's true state in that kernel)
+    ssd::SegBufs seg;
+    if (w.nseg > 1 && !checkpoints) {
+        seg.nseg = w.nseg;
+        seg.fin = reinterpret_cast<float *>(base + w.seg_fin);
+        seg.carry = base + w.seg_carry;
+        seg.L = reinterpret_cast<float *>(base + w.seg_L);
+        seg.F = reinterpret_cast<float *>(base + w.seg_F);
+        seg.I = reinterpret_cast<int32_t *>(base + w.seg_I);
+    }
     if (ssd::fused_state_path(d)) {
         ssd::launch_state_scan(d, x, B, meta, cum, dtc, state_cache, state_indices,
-                               has_initial_state, entering, checkpoints, stream);
+                               has_initial_state, entering, checkpoints, stream, &seg);
     } else {
         ssd::launch_chunk_state(d, x, B, meta, cum, dtc, states, stream);
         ssd::launch_state_passing(d, states, cum, meta, state_cache, state_indices,
                                   has_initial_state, entering, checkpoints, stream);
     }
-    ssd::launch_chunk_scan(d, x, C, D, meta, cum, dtc, cb, entering, y, stream);
+    ssd::launch_chunk_scan(d, x, C, D, meta, cum, dtc, cb, entering, y, stream, &seg);
     return launch_status();
 }
 

@@ -374,6 +374,21 @@ __device__ __forceinline__ uint4 buf_ld16(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ float buf_ldf(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }
+// 8-byte store; one at or past the resource's size is dropped
+__device__ __forceinline__ void buf_st8(rsrc_t r, uint32_t off, uint2 v) {
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i, v), r, (int)off, 0, 0);
+}
+// four floats as bf16 (round to nearest even), in one 8-byte word
+__device__ __forceinline__ uint2 pack_bf16x4(const float *v) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 q;
+    q[0] = static_cast<bf16>(v[0]);
+    q[1] = static_cast<bf16>(v[1]);
+    q[2] = static_cast<bf16>(v[2]);
+    q[3] = static_cast<bf16>(v[3]);
+    return __builtin_bit_cast(uint2, q);
+}
 
 // ---------------------------------------------------------------------------
 // CB in MFMA fragment order (bf16 inputs). For row tile rt = i / 16 and K block

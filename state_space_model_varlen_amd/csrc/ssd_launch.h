@@ -66,14 +66,34 @@ void launch_state_passing(const PrefillDims &d, const float *states, const float
 // d_state 128 only: fused_state_path()); writes what state passing writes and
 // needs no chunk-state buffer.
 bool fused_state_path(const PrefillDims &d);
+
+// Segmented state passing (fused path, no checkpoints): each sequence's chunk
+// chain is cut into up to `nseg` segments that run in parallel, each from a zero
+// state (the first from the cached one). A segment leaves its local final state
+// (fin, float32 [S nseg][H][P][N]) and total log decay (L, [S nseg][H]); for
+// every chunk, the log decay from its segment's start (F, [H][max_chunks]) and
+// the segment's global index s nseg + b (I, [max_chunks], -1 in a first
+// segment). The carry step then chains the segments into each one's true
+// starting state (carry, bf16 [S nseg][H][P][N]) and writes the final states;
+// the chunk scan adds exp(F) carry to the local entering states.
+struct SegBufs {
+    int nseg = 1;
+    float *fin = nullptr, *L = nullptr, *F = nullptr;
+    int32_t *I = nullptr;
+    void *carry = nullptr;
+};
+// Segments the combined call uses for these dimensions (1: unsegmented).
+int state_segments(const PrefillDims &d);
 void launch_state_scan(const PrefillDims &d, const void *x, const void *B, const int32_t *meta,
                        const float *cum, const float *dtc, void *cache, const int32_t *idx,
-                       const uint8_t *has_init, void *entering, void *ckpt, void *stream);
+                       const uint8_t *has_init, void *entering, void *ckpt, void *stream,
+                       const SegBufs *seg = nullptr);
 void launch_bmm(const PrefillDims &d, const void *B, const void *C, const int32_t *meta, void *CB,
                 void *stream);
 void launch_chunk_scan(const PrefillDims &d, const void *x, const void *C, const float *D,
                        const int32_t *meta, const float *cum, const float *dtc, const void *CB,
-                       const void *entering, void *y, void *stream);
+                       const void *entering, void *y, void *stream,
+                       const SegBufs *seg = nullptr);
 
 // cu (optional): packed-varlen requests, request r owning tokens cu[r] .. cu[r+1]-1
 // of Ttot packed rows; without it request r owns tokens r T .. r T + T - 1.

@@ -804,14 +804,15 @@ template <int Q> struct StateScanRegs {
     float cl;                                          // cum at the chunk's last token
 };
 
-template <int Q, bool CKPT, typename TS>
+template <int Q, bool CKPT, bool SEG, typename TS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
 void state_scan_fast_kernel(
     int S, int H, int G, int max_chunks, int num_slots, const bf16 *__restrict__ x,
     const bf16 *__restrict__ B, const int32_t *__restrict__ meta, const float *__restrict__ cum,
     const float *__restrict__ dtc, TS *cache, const int32_t *__restrict__ idx,
     const uint8_t *__restrict__ has_init, bf16 *__restrict__ entering, TS *__restrict__ ckpt,
-    SrCtx sr)
+    SrCtx sr, int nseg, float *__restrict__ seg_fin, float *__restrict__ seg_L,
+    float *__restrict__ seg_F, int32_t *__restrict__ seg_I)
 {
     constexpr int P = 64, N = 128, NSL = kScanNSL, NS = N / NSL;
     constexpr int LDX = kScanLDX, LDB = kScanLDB;
@@ -820,9 +821,13 @@ void state_scan_fast_kernel(
     bf16 *xs = reinterpret_cast<bf16 *>(smem);   // [Q][LDX]  x_t
     bf16 *bs = xs + Q * LDX;                     // [Q][LDB]  w_t B_t (slice columns)
 
-    const int nblk = S * H * NS;
+    // logical order (segment of sequence, head, column slice): the heads that
+    // share a B group sit side by side on one XCD
+    const int nsg = SEG ? nseg : 1;
+    const int nblk = S * nsg * H * NS;
     const int lb = xcd_logical_block(blockIdx.x, nblk);
-    const int q = lb % NS, h = (lb / NS) % H, s = lb / (NS * H);
+    const int q = lb % NS, h = (lb / NS) % H, sb = lb / (NS * H);
+    const int s = sb / nsg, b = sb - s * nsg;
     const int g = h / (H / G);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, kg = lane >> 4;
@@ -849,6 +854,16 @@ void state_scan_fast_kernel(
     c1 = c1 > c0 ? c1 : c0;
     end = end > first ? end : first;
     fcl = fcl < 1 ? 1 : (fcl > Q ? Q : fcl);
+    // this block's chunks lo .. hi - 1: all of the sequence's, or segment b of
+    // min(nseg, chunks) near-equal segments (a sequence with no chunk has one)
+    int lo = c0, hi = c1;
+    if constexpr (SEG) {
+        const int n = c1 - c0;
+        const int ns = n < nsg ? (n > 1 ? n : 1) : nsg;
+        if (b >= ns) return;   // (uniform over the block, before any barrier)
+        lo = c0 + b * n / ns;
+        hi = c0 + (b + 1) * n / ns;
+    }
     // chunk c of the sequence: tokens first + off(c) .., at most cap(c) of them
     auto chunk_off = [&](int c) { return c == c0 ? 0 : fcl + (c - c0 - 1) * Q; };
     auto chunk_cap = [&](int c) { return c == c0 ? fcl : Q; };
@@ -881,9 +896,9 @@ void state_scan_fast_kernel(
     // last row: rows past it read as zero. Past the last chunk (and for a
     // sequence with no chunk) every resource is empty and nothing is read.
     auto fetch = [&](Regs &R, int c) {
-        const bool any = c < c1;
-        c = c < c1 ? c : c1 - 1;
-        c = c > c0 ? c : c0;
+        const bool any = c < hi;
+        c = c < hi ? c : hi - 1;
+        c = c > lo ? c : lo;
         const int st = first + chunk_off(c);
         int len = end - st < chunk_cap(c) ? end - st : chunk_cap(c);
         len = any ? len : 0;
@@ -911,8 +926,9 @@ void state_scan_fast_kernel(
     // one iteration: stage chunk c from R into LDS, refill R with chunk c + 1,
     // then fold chunk c into the running state. An empty sequence makes one pass
     // over zero tiles (it changes nothing) with its stores switched off.
+    float F = 0.0f;   // log decay from the block's first chunk to chunk c
     auto step = [&](Regs &R, int c) {
-        const bool live = c < c1;
+        const bool live = c < hi;
         const int st = first + chunk_off(c);
         const int len = end - st < chunk_cap(c) ? end - st : chunk_cap(c);
         __syncthreads();   // the previous chunk's MFMA reads of xs / bs are done
@@ -938,6 +954,13 @@ void state_scan_fast_kernel(
             }
         }
         const float decay = __expf(R.cl);
+        if constexpr (SEG) {
+            if (live && q == 0 && tid == 0) {
+                seg_F[(int64_t)h * max_chunks + c] = F;
+                if (h == 0) seg_I[c] = b > 0 ? sb : -1;
+            }
+            F += R.cl;
+        }
         fetch(R, c + 1);
         __syncthreads();
 
@@ -991,25 +1014,97 @@ void state_scan_fast_kernel(
     // loop body runs at least once, so no branch separates these loads from their
     // use and the compiler's wait counts stay exact.
     Regs R;
-    fetch(R, c0);
+    fetch(R, lo);
     __builtin_amdgcn_sched_barrier(0);
-    const bool read_init = slot_ok && has_init != nullptr && hflag != 0;
+    const bool read_init = slot_ok && has_init != nullptr && hflag != 0 && b == 0;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[j][e] = read_init ? iv[j][e] : 0.0f;
-    int c = c0;
+    int c = lo;
     do {
         step(R, c);
-    } while (++c < c1);
+    } while (++c < hi);
 
-    if (slot_ok) {
+    if constexpr (SEG) {
+        // the segment's local final state and total decay, for the carry step
+        if (q == 0 && tid == 0) seg_L[(int64_t)sb * H + h] = F;
+        float *fin = seg_fin + ((int64_t)sb * H + h) * PN + run;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            float v[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+            store4<float>(fin + 16 * j, v);
+        }
+    } else if (slot_ok) {
         const int64_t fo = ((int64_t)slot * H + h) * PN + run;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             float v[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
             put4<TS>(cslot + 16 * j, v, srk, (uint64_t)(fo + 16 * j), kSrFinal);
         }
+    }
+}
+
+// Carry step of segmented state passing. A segment's chunk chain is linear in
+// its starting state, so with h_b the true state entering segment b, fin_b the
+// segment's final state from a zero start (the first segment's from the cached
+// one) and L_b its total log decay:
+//     h_1 = fin_0,   h_{b+1} = exp(L_b) h_b + fin_b,   final = h_ns.
+// Grid: S * H * (P N / 1024) blocks of 256 threads, 4 consecutive state
+// elements per thread; h_b (b >= 1) is kept in bf16 for the chunk scan, the
+// final state goes to the cache slot as the unsegmented path writes it.
+constexpr int kMaxSeg = 8;
+
+template <typename TS>
+__global__ __launch_bounds__(256) void state_carry_kernel(
+    int S, int H, int PN, int nseg, int max_chunks, int num_slots,
+    const int32_t *__restrict__ meta, const float *__restrict__ seg_fin,
+    const float *__restrict__ seg_L, bf16 *__restrict__ carry, TS *cache,
+    const int32_t *__restrict__ idx, SrCtx sr)
+{
+    const int per = PN / 1024;
+    const int e0 = (blockIdx.x % per) * 1024 + 4 * threadIdx.x;
+    const int h = (blockIdx.x / per) % H, s = blockIdx.x / (per * H);
+    int c0 = meta[s], c1 = meta[s + 1];
+    const int slot = idx[s];
+    const SrKey srk = sr_key(sr, meta);
+    c0 = c0 < max_chunks ? c0 : max_chunks;
+    c1 = c1 < max_chunks ? c1 : max_chunks;
+    const int n = c1 > c0 ? c1 - c0 : 0;
+    const int ns = n < nseg ? (n > 1 ? n : 1) : nseg;
+    // Every segment's values are requested before the chain starts, through
+    // buffer resources that end at the sequence's last segment: entries past it
+    // read as zero (no decay, nothing added) and stores there are dropped, so the
+    // chain has no branch and one wait covers all the loads.
+    const int64_t sq = (int64_t)s * nseg * H;
+    const rsrc_t rf = make_rsrc(seg_fin + sq * PN, (uint32_t)((int64_t)ns * H * PN * 4));
+    const rsrc_t rl = make_rsrc(seg_L + sq, (uint32_t)(ns * H * 4));
+    const rsrc_t rc = make_rsrc(carry + sq * PN, (uint32_t)((int64_t)ns * H * PN * 2));
+    float fin[kMaxSeg][4], L[kMaxSeg];
+#pragma unroll
+    for (int b = 0; b < kMaxSeg; ++b) {
+        const uint32_t eo = (uint32_t)((b * H + h) * PN + e0);
+        const uint4 w = buf_ld16(rf, eo * 4);
+        fin[b][0] = __uint_as_float(w.x);
+        fin[b][1] = __uint_as_float(w.y);
+        fin[b][2] = __uint_as_float(w.z);
+        fin[b][3] = __uint_as_float(w.w);
+        L[b] = buf_ldf(rl, (uint32_t)(b * H + h) * 4);
+    }
+    float v[4] = {fin[0][0], fin[0][1], fin[0][2], fin[0][3]};
+#pragma unroll
+    for (int b = 1; b < kMaxSeg; ++b) {
+        buf_st8(rc, (uint32_t)((b * H + h) * PN + e0) * 2, pack_bf16x4(v));
+        const float d = __expf(L[b]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = d * v[i] + fin[b][i];
+    }
+    // (the chain completes here, not inside the branch below, which would put
+    // the last segment's loads after it)
+    asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
+    if (slot >= 0 && slot < num_slots) {
+        const int64_t fo = ((int64_t)slot * H + h) * PN + e0;
+        put4<TS>(cache + fo, v, srk, (uint64_t)fo, kSrFinal);
     }
 }
 
@@ -1184,13 +1279,14 @@ __device__ __forceinline__ void scan_row_tile(
     wave_lds_sync();
 }
 
-template <int Q>
+template <int Q, bool SEG>
 __global__ __launch_bounds__(2 * Q) __attribute__((amdgpu_waves_per_eu(4)))
 void chunk_scan_fast_kernel(
     int S, int H, int G, int max_chunks, const bf16 *__restrict__ x,
     const bf16 *__restrict__ C, const float *__restrict__ D, const int32_t *__restrict__ meta,
     const float *__restrict__ cum, const float *__restrict__ dtc, const bf16 *__restrict__ CB,
-    const bf16 *__restrict__ entering, bf16 *__restrict__ y)
+    const bf16 *__restrict__ entering, bf16 *__restrict__ y, const int32_t *__restrict__ seg_I,
+    const float *__restrict__ seg_F, const bf16 *__restrict__ carry)
 {
     constexpr int P = 64, N = 128, LDX = kFastLD, LDH = N + 8;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -1204,6 +1300,14 @@ void chunk_scan_fast_kernel(
     const int lb = xcd_logical_block(blockIdx.x, nblk);
     const int h = lb % H, c = lb / H;
     const ChunkInfo ci = chunk_info(meta, S, c);
+    // segmented state passing: the entering state is the stored local one plus
+    // exp(F) times the segment's starting state (none in a first segment)
+    int sid = -1;
+    float sF = 0.0f;
+    if constexpr (SEG) {
+        sid = seg_I[c];
+        sF = seg_F[(int64_t)h * max_chunks + c];
+    }
     if (ci.len <= 0) return;
     const int g = h / (H / G);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1241,6 +1345,17 @@ void chunk_scan_fast_kernel(
         const int u = tid + nthr * k;
         hr[k] = ld16(hin + (u >> 4) * N + 8 * (u & 15));
     }
+    uint4 hc[kHVec];
+    if constexpr (SEG) {
+        const bool has = sid >= 0;
+        const rsrc_t rh = make_rsrc(carry + ((int64_t)(has ? sid : 0) * H + h) * P * N,
+                                    has ? (uint32_t)(P * N * 2) : 0u);
+#pragma unroll
+        for (int k = 0; k < kHVec; ++k) {
+            const int u = tid + nthr * k;
+            hc[k] = buf_ld16(rh, (uint32_t)((u >> 4) * N + 8 * (u & 15)) * 2);
+        }
+    }
     __builtin_amdgcn_sched_barrier(0);
     uint4 xr[4];
 #pragma unroll
@@ -1256,7 +1371,21 @@ void chunk_scan_fast_kernel(
 #pragma unroll
     for (int k = 0; k < kHVec; ++k) {
         const int u = tid + nthr * k;
-        st16(hs + (u >> 4) * LDH + 8 * (u & 15), hr[k]);
+        bf16 *dst = hs + (u >> 4) * LDH + 8 * (u & 15);
+        if constexpr (SEG) {
+            const float ef = sid >= 0 ? __expf(sF) : 0.0f;
+            const uint32_t a4[4] = {hr[k].x, hr[k].y, hr[k].z, hr[k].w};
+            const uint32_t c4[4] = {hc[k].x, hc[k].y, hc[k].z, hc[k].w};
+            float f[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f[2 * i] = bf16_lo(a4[i]) + ef * bf16_lo(c4[i]);
+                f[2 * i + 1] = bf16_hi(a4[i]) + ef * bf16_hi(c4[i]);
+            }
+            Vec16<bf16>::store(dst, f);
+        } else {
+            st16(dst, hr[k]);
+        }
     }
     __syncthreads();
     // scaling factors of x: G_j = exp(R_k - cum_j) dt_j; exact mode when a span is too large
@@ -1430,21 +1559,35 @@ static void launch_state_fast(const PrefillDims &d, const void *x, const void *B
                        meta, cum, dtc, states);
 }
 
-template <int Q>
-static void launch_scan_fast(const PrefillDims &d, const void *x, const void *C, const float *D,
-                             const int32_t *meta, const float *cum, const float *dtc,
-                             const void *CB, const void *entering, void *y, hipStream_t st)
+template <int Q, bool SEG>
+static void launch_scan_fast_s(const PrefillDims &d, const void *x, const void *C, const float *D,
+                               const int32_t *meta, const float *cum, const float *dtc,
+                               const void *CB, const void *entering, void *y, const SegBufs &seg,
+                               hipStream_t st)
 {
     const size_t smem = (size_t)Q * (kFastLD * sizeof(bf16) + 2 * sizeof(float)) +
                         (size_t)64 * (128 + 8) * sizeof(bf16) +
                         (size_t)(Q / 32) * 64 * kScanLDR * sizeof(bf16);
     static size_t raised = 0;
-    allow_lds(reinterpret_cast<const void *>(&chunk_scan_fast_kernel<Q>), smem, raised);
+    allow_lds(reinterpret_cast<const void *>(&chunk_scan_fast_kernel<Q, SEG>), smem, raised);
     const unsigned nblk = (unsigned)((int64_t)d.max_chunks * d.H);
-    hipLaunchKernelGGL(chunk_scan_fast_kernel<Q>, dim3(nblk), dim3(2 * Q), smem, st, d.S, d.H, d.G,
-                       d.max_chunks, static_cast<const bf16 *>(x), static_cast<const bf16 *>(C), D,
-                       meta, cum, dtc, static_cast<const bf16 *>(CB),
-                       static_cast<const bf16 *>(entering), static_cast<bf16 *>(y));
+    hipLaunchKernelGGL((chunk_scan_fast_kernel<Q, SEG>), dim3(nblk), dim3(2 * Q), smem, st, d.S,
+                       d.H, d.G, d.max_chunks, static_cast<const bf16 *>(x),
+                       static_cast<const bf16 *>(C), D, meta, cum, dtc,
+                       static_cast<const bf16 *>(CB), static_cast<const bf16 *>(entering),
+                       static_cast<bf16 *>(y), seg.I, seg.F, static_cast<const bf16 *>(seg.carry));
+}
+
+template <int Q>
+static void launch_scan_fast(const PrefillDims &d, const void *x, const void *C, const float *D,
+                             const int32_t *meta, const float *cum, const float *dtc,
+                             const void *CB, const void *entering, void *y, const SegBufs *seg,
+                             hipStream_t st)
+{
+    if (seg && seg->nseg > 1)
+        launch_scan_fast_s<Q, true>(d, x, C, D, meta, cum, dtc, CB, entering, y, *seg, st);
+    else
+        launch_scan_fast_s<Q, false>(d, x, C, D, meta, cum, dtc, CB, entering, y, SegBufs(), st);
 }
 
 #define SSD_DISPATCH_PN(d, FN, TIN, ...)                                 \
@@ -1518,79 +1661,106 @@ void launch_state_passing(const PrefillDims &d, const float *states, const float
     }
 }
 
-template <int Q, bool CKPT, typename TS>
+template <int Q, bool CKPT, bool SEG, typename TS>
 static void launch_state_scan_k(const PrefillDims &d, const void *x, const void *B,
                                 const int32_t *meta, const float *cum, const float *dtc,
                                 void *cache, const int32_t *idx, const uint8_t *has_init,
-                                void *entering, void *ckpt, hipStream_t st)
+                                void *entering, void *ckpt, const SegBufs &seg, hipStream_t st)
 {
     const size_t smem = (size_t)Q * (kScanLDX + kScanLDB) * sizeof(bf16);
     static size_t raised = 0;
-    allow_lds(reinterpret_cast<const void *>(&state_scan_fast_kernel<Q, CKPT, TS>), smem,
+    allow_lds(reinterpret_cast<const void *>(&state_scan_fast_kernel<Q, CKPT, SEG, TS>), smem,
               raised);
-    const unsigned nblk = (unsigned)((int64_t)d.S * d.H * (128 / kScanNSL));
-    hipLaunchKernelGGL((state_scan_fast_kernel<Q, CKPT, TS>), dim3(nblk), dim3(512), smem,
+    const int nseg = SEG ? seg.nseg : 1;
+    const unsigned nblk = (unsigned)((int64_t)d.S * nseg * d.H * (128 / kScanNSL));
+    hipLaunchKernelGGL((state_scan_fast_kernel<Q, CKPT, SEG, TS>), dim3(nblk), dim3(512), smem,
                        st, d.S, d.H, d.G, d.max_chunks, d.num_slots, static_cast<const bf16 *>(x),
                        static_cast<const bf16 *>(B), meta, cum, dtc, static_cast<TS *>(cache), idx,
-                       has_init, static_cast<bf16 *>(entering), static_cast<TS *>(ckpt), d.sr);
+                       has_init, static_cast<bf16 *>(entering), static_cast<TS *>(ckpt), d.sr,
+                       nseg, seg.fin, seg.L, seg.F, seg.I);
+    if constexpr (SEG) {
+        const int PN = 64 * 128;
+        const unsigned ncar = (unsigned)((int64_t)d.S * d.H * (PN / 1024));
+        hipLaunchKernelGGL(state_carry_kernel<TS>, dim3(ncar), dim3(256), 0, st, d.S, d.H, PN,
+                           nseg, d.max_chunks, d.num_slots, meta, seg.fin, seg.L,
+                           static_cast<bf16 *>(seg.carry), static_cast<TS *>(cache), idx, d.sr);
+    }
 }
 
 template <int Q, typename TS>
 static void launch_state_scan_q(const PrefillDims &d, const void *x, const void *B,
                                 const int32_t *meta, const float *cum, const float *dtc,
                                 void *cache, const int32_t *idx, const uint8_t *has_init,
-                                void *entering, void *ckpt, hipStream_t st)
+                                void *entering, void *ckpt, const SegBufs *seg, hipStream_t st)
 {
     if (ckpt)
-        launch_state_scan_k<Q, true, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering,
-                                         ckpt, st);
+        launch_state_scan_k<Q, true, false, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init,
+                                                entering, ckpt, SegBufs(), st);
+    else if (seg && seg->nseg > 1)
+        launch_state_scan_k<Q, false, true, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init,
+                                                entering, ckpt, *seg, st);
     else
-        launch_state_scan_k<Q, false, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering,
-                                          ckpt, st);
+        launch_state_scan_k<Q, false, false, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init,
+                                                 entering, ckpt, SegBufs(), st);
 }
 
 template <typename TS>
 static void launch_state_scan_t(const PrefillDims &d, const void *x, const void *B,
                                 const int32_t *meta, const float *cum, const float *dtc,
                                 void *cache, const int32_t *idx, const uint8_t *has_init,
-                                void *entering, void *ckpt, hipStream_t st)
+                                void *entering, void *ckpt, const SegBufs *seg, hipStream_t st)
 {
     switch (d.Q) {
-    case 32: launch_state_scan_q<32, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, st); break;
-    case 64: launch_state_scan_q<64, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, st); break;
-    case 128: launch_state_scan_q<128, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, st); break;
-    default: launch_state_scan_q<256, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, st); break;
+    case 32: launch_state_scan_q<32, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, seg, st); break;
+    case 64: launch_state_scan_q<64, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, seg, st); break;
+    case 128: launch_state_scan_q<128, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, seg, st); break;
+    default: launch_state_scan_q<256, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, seg, st); break;
     }
 }
 
 bool fused_state_path(const PrefillDims &d) { return use_fast(d); }
 
+// Segments per sequence: enough (state scan) blocks to give every CU about two,
+// at most kMaxSeg, never more than the chunks there can be.
+constexpr int64_t kSegBlocks = 512;
+
+int state_segments(const PrefillDims &d)
+{
+    if (!use_fast(d) || d.S <= 0 || d.max_chunks < 2) return 1;
+    const int64_t base = (int64_t)d.S * d.H * (128 / kScanNSL);
+    int64_t n = kSegBlocks / base;
+    n = n < kMaxSeg ? n : kMaxSeg;
+    n = n < d.max_chunks ? n : d.max_chunks;
+    return n > 1 ? (int)n : 1;
+}
+
 void launch_state_scan(const PrefillDims &d, const void *x, const void *B, const int32_t *meta,
                        const float *cum, const float *dtc, void *cache, const int32_t *idx,
-                       const uint8_t *has_init, void *entering, void *ckpt, void *stream)
+                       const uint8_t *has_init, void *entering, void *ckpt, void *stream,
+                       const SegBufs *seg)
 {
     if (d.S <= 0) return;
     hipStream_t st = as_stream(stream);
     if (d.state_f16)
-        launch_state_scan_t<f16>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, st);
+        launch_state_scan_t<f16>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, seg, st);
     else if (d.state_bf16)
-        launch_state_scan_t<bf16>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, st);
+        launch_state_scan_t<bf16>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, seg, st);
     else
-        launch_state_scan_t<float>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, st);
+        launch_state_scan_t<float>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, seg, st);
 }
 
 void launch_chunk_scan(const PrefillDims &d, const void *x, const void *C, const float *D,
                        const int32_t *meta, const float *cum, const float *dtc, const void *CB,
-                       const void *entering, void *y, void *stream)
+                       const void *entering, void *y, void *stream, const SegBufs *seg)
 {
     if (d.max_chunks <= 0) return;
     hipStream_t st = as_stream(stream);
     if (use_fast(d)) {
         switch (d.Q) {
-        case 32: launch_scan_fast<32>(d, x, C, D, meta, cum, dtc, CB, entering, y, st); break;
-        case 64: launch_scan_fast<64>(d, x, C, D, meta, cum, dtc, CB, entering, y, st); break;
-        case 128: launch_scan_fast<128>(d, x, C, D, meta, cum, dtc, CB, entering, y, st); break;
-        default: launch_scan_fast<256>(d, x, C, D, meta, cum, dtc, CB, entering, y, st); break;
+        case 32: launch_scan_fast<32>(d, x, C, D, meta, cum, dtc, CB, entering, y, seg, st); break;
+        case 64: launch_scan_fast<64>(d, x, C, D, meta, cum, dtc, CB, entering, y, seg, st); break;
+        case 128: launch_scan_fast<128>(d, x, C, D, meta, cum, dtc, CB, entering, y, seg, st); break;
+        default: launch_scan_fast<256>(d, x, C, D, meta, cum, dtc, CB, entering, y, seg, st); break;
         }
         return;
     }

@@ -59,9 +59,21 @@ def test_sizes():
     assert ssd.max_chunks(big) == 17
     # bf16 inputs, headdim 64, d_state 128: the fused state kernel needs no chunk states
     mc, H, Q = 17, 80, 256
+    # one sequence over 80 heads x 2 column slices: 160 state blocks, so the chunk
+    # chain is cut into 512 // 160 = 3 segments with their own buffers (final
+    # states fp32, starting states bf16, decays, per-chunk decay and segment index)
+    ns = 3
     want_big = (r(4 * (5 + 3 * mc)) + 2 * r(4 * H * mc * Q) + r(2 * mc * 1 * Q * Q)
-                + r(2 * mc * H * 64 * 128))
+                + r(2 * mc * H * 64 * 128)
+                + r(4 * ns * H * 64 * 128) + r(2 * ns * H * 64 * 128) + r(4 * ns * H)
+                + r(4 * mc * H) + r(4 * mc))
     assert ssd.workspace_bytes(big) == want_big
+    # 32 sequences x 64 heads fill the chip: no segments
+    many = P(total_tokens=1024, num_seqs=32, nheads=64, headdim=64, d_state=128,
+             chunk_size=256, ngroups=8, in_dtype=torch.bfloat16)
+    mc = 1024 // 256 + 32
+    assert ssd.workspace_bytes(many) == (r(4 * (3 * 32 + 2 + 3 * mc)) + 2 * r(4 * 64 * mc * 256)
+                                         + r(2 * mc * 8 * 256 * 256) + r(2 * mc * 64 * 64 * 128))
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -148,6 +148,21 @@ def test_prefill_bf16_fused_path_fp16_cache():
     assert torch.equal(ck2.view(torch.int16), ck.view(torch.int16))
 
 
+def test_prefill_bf16_segmented_fp16_cache():
+    """Without checkpoints a short batch takes the segmented state path: the final
+    fp16 states are written (stochastically rounded) by the carry step."""
+    Q = 128
+    inp, cache = _problem((1500, 3, 900), 4, 64, 128, 2, Q, BF16, 814)
+    y, after, _ = _prefill(inp, cache, Q, seed=7, rounds=5, ck=False)
+    ref = oracle.prefill(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.cu_seqlens,
+                         inp.state_indices, inp.has_initial, cache, Q)
+    assert_close(y, ref["y"], BF16, "y", normalised=False)
+    used = inp.state_indices.long()
+    assert_close(after[used], ref["final"], BF16, "final states")
+    _, after2, _ = _prefill(inp, cache, Q, seed=7, rounds=5, ck=False)
+    assert torch.equal(after2.view(torch.int16), after.view(torch.int16))
+
+
 @pytest.mark.parametrize("keep", [True, False])
 def test_decode_fp16_states(keep):
     ssd = _ssd()

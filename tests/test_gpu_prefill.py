@@ -206,7 +206,9 @@ def test_deterministic_and_inputs_untouched():
 
 def test_packing_is_bitwise_invariant():
     """A packed batch gives the same bits as each sequence run alone: chunks
-    start at every sequence's first token, so the work per sequence is identical."""
+    start at every sequence's first token, so the work per sequence is identical.
+    (A sequence's chain is cut into min(segment limit, its chunks) segments; here
+    no sequence has more chunks than the limit of either run, so the cuts agree.)"""
     lens, H, P, N, G, Q = (300, 17, 513, 64), 4, 64, 128, 2, 128
     S = len(lens)
     inp = sy.random_problem(9, lens, H, P, N, G, Q, BF16, F32, num_slots=S,
@@ -414,3 +416,63 @@ def test_decay_span_modes(dt_scale):
     refd = oracle.prefill(inp.x, inp.dt, inp.A, inp.B, inp.C, None, inp.cu_seqlens,
                           inp.state_indices, inp.has_initial, cache, Q)
     assert_close(yd, refd["y"], BF16, f"y without D (dt x {dt_scale})")
+
+
+SEG_CASES = [
+    # seqlens, H, Q, state dtype, has_initial: short batches of long sequences, where
+    # the state kernel cuts each chunk chain into segments chained by the carry step
+    ((2000, 0, 700, 64, 1), 8, 64, F32, [True, True, False, True, True]),
+    ((4096,), 2, 256, BF16, [True]),
+    ((300, 5000), 4, 128, F32, [False, True]),
+    ((1537, 2049), 8, 32, BF16, [True, False]),
+]
+
+
+@pytest.mark.parametrize("case", SEG_CASES, ids=lambda c: f"S{len(c[0])}_H{c[1]}_Q{c[2]}_"
+                         f"{str(c[3])[6:]}")
+def test_segmented_state_passing(case):
+    """Few (sequence, head) pairs: the combined call runs each sequence's chunk chain
+    as up to eight parallel segments and chains their states afterwards. Sequences
+    with more chunks than segments, fewer chunks than segments, one chunk, one
+    token and none; with and without cached states. The step-wise state kernel
+    (one block walks the whole chain) gives the same final states."""
+    lens, H, Q, ts, hi = case
+    P, N, G = 64, 128, 2
+    S = len(lens)
+    inp = sy.random_problem(950 + SEG_CASES.index(case), lens, H, P, N, G, Q, BF16, ts,
+                            num_slots=2 * S + 1, has_initial=hi)
+    cache = _cache_with_states(inp, 2 * S + 1, ts)
+    ssd = _ssd()
+    T = sum(lens)
+    p = ssd.make_problem(T, S, H, P, N, G, Q, 2 * S + 1, BF16, ts)
+    # the workspace holds segment buffers exactly when segments are used
+    mc = ssd.max_chunks(p)
+    r = lambda v: (v + 255) // 256 * 256
+    plain = (r(4 * (3 * S + 2 + 3 * mc)) + 2 * r(4 * H * mc * Q) + r(2 * mc * G * Q * Q)
+             + r(2 * mc * H * P * N))
+    assert ssd.workspace_bytes(p) > plain
+    y, after, _ = gpu_prefill(inp, cache, Q)
+    ref = oracle.prefill(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.cu_seqlens,
+                         inp.state_indices, inp.has_initial, cache, Q)
+    assert_close(y, ref["y"], BF16, "y", normalised=False)
+    used = inp.state_indices.long()
+    assert_close(after[used], ref["final"], looser(BF16, ts), "final states")
+    others = [k for k in range(cache.shape[0]) if k not in set(used.tolist())]
+    bits = torch.int16 if ts == BF16 else torch.int32
+    assert torch.equal(after[others].view(bits), cache[others].view(bits))
+    yd, _, _ = gpu_prefill(inp, cache, Q, D=False)
+    refd = oracle.prefill(inp.x, inp.dt, inp.A, inp.B, inp.C, None, inp.cu_seqlens,
+                          inp.state_indices, inp.has_initial, cache, Q)
+    assert_close(yd, refd["y"], BF16, "y without D")
+    # step-wise: cumsum, then the unsegmented state kernel
+    buf = ssd.alloc_step_buffers(p, DEV)
+    g_cache = cache.to(DEV)
+    ssd.ssd_chunk_cumsum(p, inp.dt.to(DEV), inp.A.to(DEV), inp.cu_seqlens.to(DEV),
+                         buf["chunk_meta"], buf["dA_cumsum"], buf["dt_chunk"])
+    ssd.ssd_chunk_state_passing(p, inp.x.to(DEV), inp.B.to(DEV), buf["chunk_meta"],
+                                buf["dA_cumsum"], buf["dt_chunk"], g_cache,
+                                inp.state_indices.to(DEV), inp.has_initial.to(DEV),
+                                buf["entering"], None)
+    torch.cuda.synchronize()
+    assert_close(g_cache.cpu()[used], to64(after[used]), looser(BF16, ts),
+                 "segmented vs unsegmented final states")
