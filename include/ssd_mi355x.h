@@ -279,7 +279,12 @@ int ssd_chunk_scan(const ssd_problem *p, const void *x, const void *C, const flo
  * Semantics are those of the five steps composed: every initial state is
  * read as it was before the call even though the call overwrites the slot.
  * For bf16 inputs with headdim 64 and d_state 128, steps 2 and 3 run as
- * ssd_chunk_state_passing (and the workspace holds no chunk states).
+ * ssd_chunk_state_passing (and the workspace holds no chunk states). When
+ * such a call has no checkpoints and few (sequence, head) pairs, each
+ * sequence's chunk chain is cut into segments that run in parallel and are
+ * chained afterwards (the recurrence is linear in its starting state); the
+ * workspace then also holds the segments' states. Results agree with the
+ * unsegmented path within rounding, not bit for bit.
  *   workspace        device buffer of at least ssd_workspace_bytes(p) bytes,
  *                    256-byte aligned; its contents on entry do not matter
  *   checkpoints      [max_chunks,H,P,N] state_dtype or NULL
