@@ -327,7 +327,6 @@ static int combined(const ssd_problem *p, const ssd::DtTf &tf, const void *x, co
     float *states = reinterpret_cast<float *>(base + w.states);
     void *entering = base + w.entering;
 
-    ssd::launch_chunk_prep(d, dt, A, cu_seqlens, meta, cum, dtc, B, C, cb, stream, tf);
     // segmented state passing when the state kernel alone would leave CUs idle
     // (not with checkpoints, which need every chunk's true state in that kernel)
     ssd::SegBufs seg;
@@ -338,7 +337,14 @@ static int combined(const ssd_problem *p, const ssd::DtTf &tf, const void *x, co
         seg.L = reinterpret_cast<float *>(base + w.seg_L);
         seg.F = reinterpret_cast<float *>(base + w.seg_F);
         seg.I = reinterpret_cast<int32_t *>(base + w.seg_I);
+        seg.C = C;
+        seg.CB = cb;
     }
+    // steps 1 and 4 in one launch, or (segmented) step 4 beside the carry step
+    if (seg.nseg > 1)
+        ssd::launch_chunk_cumsum(d, dt, A, cu_seqlens, meta, cum, dtc, stream, tf);
+    else
+        ssd::launch_chunk_prep(d, dt, A, cu_seqlens, meta, cum, dtc, B, C, cb, stream, tf);
     if (ssd::fused_state_path(d)) {
         ssd::launch_state_scan(d, x, B, meta, cum, dtc, state_cache, state_indices,
                                has_initial_state, entering, checkpoints, stream, &seg);

@@ -76,11 +76,15 @@ bool fused_state_path(const PrefillDims &d);
 // segment). The carry step then chains the segments into each one's true
 // starting state (carry, bf16 [S nseg][H][P][N]) and writes the final states;
 // the chunk scan adds exp(F) carry to the local entering states.
+// With C and CB set, the carry launch also computes CB (step 4), so that the
+// call runs step 1 alone (launch_chunk_cumsum) instead of launch_chunk_prep.
 struct SegBufs {
     int nseg = 1;
     float *fin = nullptr, *L = nullptr, *F = nullptr;
     int32_t *I = nullptr;
     void *carry = nullptr;
+    const void *C = nullptr;
+    void *CB = nullptr;
 };
 // Segments the combined call uses for these dimensions (1: unsegmented).
 int state_segments(const PrefillDims &d);

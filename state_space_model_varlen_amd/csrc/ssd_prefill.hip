@@ -1055,16 +1055,27 @@ void state_scan_fast_kernel(
 // final state goes to the cache slot as the unsegmented path writes it.
 constexpr int kMaxSeg = 8;
 
+//
+// The same launch computes CB (step 4, which only the chunk scan reads) in its
+// first nbmm blocks, one CB row tile each, beside the carry blocks.
 template <typename TS>
 __global__ __launch_bounds__(256) void state_carry_kernel(
     int S, int H, int PN, int nseg, int max_chunks, int num_slots,
     const int32_t *__restrict__ meta, const float *__restrict__ seg_fin,
     const float *__restrict__ seg_L, bf16 *__restrict__ carry, TS *cache,
-    const int32_t *__restrict__ idx, SrCtx sr)
+    const int32_t *__restrict__ idx, SrCtx sr, int nbmm, int G, int Q,
+    const bf16 *__restrict__ B, const bf16 *__restrict__ C, bf16 *__restrict__ CB)
 {
+    if ((int)blockIdx.x < nbmm) {
+        const int tiles = Q / 16, y = blockIdx.x;
+        const int c = y / (G * tiles), g = (y / tiles) % G, z = y % tiles;
+        bmm_rows<bf16, 128>(G, Q, c, g, z, chunk_info(meta, S, c), B, C, CB);
+        return;
+    }
+    const int bx = blockIdx.x - nbmm;
     const int per = PN / 1024;
-    const int e0 = (blockIdx.x % per) * 1024 + 4 * threadIdx.x;
-    const int h = (blockIdx.x / per) % H, s = blockIdx.x / (per * H);
+    const int e0 = (bx % per) * 1024 + 4 * threadIdx.x;
+    const int h = (bx / per) % H, s = bx / (per * H);
     int c0 = meta[s], c1 = meta[s + 1];
     const int slot = idx[s];
     const SrKey srk = sr_key(sr, meta);
@@ -1680,10 +1691,13 @@ static void launch_state_scan_k(const PrefillDims &d, const void *x, const void 
                        nseg, seg.fin, seg.L, seg.F, seg.I);
     if constexpr (SEG) {
         const int PN = 64 * 128;
-        const unsigned ncar = (unsigned)((int64_t)d.S * d.H * (PN / 1024));
-        hipLaunchKernelGGL(state_carry_kernel<TS>, dim3(ncar), dim3(256), 0, st, d.S, d.H, PN,
-                           nseg, d.max_chunks, d.num_slots, meta, seg.fin, seg.L,
-                           static_cast<bf16 *>(seg.carry), static_cast<TS *>(cache), idx, d.sr);
+        const int ncar = d.S * d.H * (PN / 1024);
+        const int nbmm = seg.CB ? d.max_chunks * d.G * (d.Q / 16) : 0;
+        hipLaunchKernelGGL(state_carry_kernel<TS>, dim3((unsigned)(nbmm + ncar)), dim3(256), 0, st,
+                           d.S, d.H, PN, nseg, d.max_chunks, d.num_slots, meta, seg.fin, seg.L,
+                           static_cast<bf16 *>(seg.carry), static_cast<TS *>(cache), idx, d.sr,
+                           nbmm, d.G, d.Q, static_cast<const bf16 *>(B),
+                           static_cast<const bf16 *>(seg.C), static_cast<bf16 *>(seg.CB));
     }
 }
 
