@@ -1327,7 +1327,7 @@ void chunk_scan_fast_kernel(
     const bf16 *__restrict__ C, const float *__restrict__ D, const int32_t *__restrict__ meta,
     const float *__restrict__ cum, const float *__restrict__ dtc, const bf16 *__restrict__ CB,
     const bf16 *__restrict__ entering, bf16 *__restrict__ y, const int32_t *__restrict__ seg_I,
-    const float *__restrict__ seg_F, const bf16 *__restrict__ carry)
+    const float *__restrict__ seg_F, const bf16 *__restrict__ carry, int by_chunk)
 {
     constexpr int P = 64, N = 128, LDX = kScanXLD, LDH = N + 8;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -1337,9 +1337,23 @@ void chunk_scan_fast_kernel(
     float *scum = reinterpret_cast<float *>(ys + (Q / 32) * P * kScanLDR);  // [Q] cum * log2(e)
     float *sdt = scum + Q;                                     // [Q]
 
-    const int nblk = max_chunks * H;
-    const int lb = xcd_logical_block(blockIdx.x, nblk);
-    const int h = lb % H, c = lb / H;
+    // Unit (chunk c, head h). With by_chunk, XCD x takes the chunks c = x mod 8,
+    // all heads of each: every XCD gets the same number of real chunks whatever
+    // the padding of max_chunks (the grid is padded to whole rounds of 8 chunks;
+    // the padding blocks leave at once). Otherwise each XCD takes one contiguous
+    // range of units in order c H + h. Either way the heads of a chunk share its
+    // C and CB in one L2.
+    int h, c;
+    if (by_chunk) {
+        const int slot = blockIdx.x / kXcds, m = slot / H;
+        h = slot - m * H;
+        c = (int)(blockIdx.x % kXcds) + kXcds * m;
+        if (c >= max_chunks) return;
+    } else {
+        const int lb = xcd_logical_block(blockIdx.x, max_chunks * H);
+        h = lb % H;
+        c = lb / H;
+    }
     const ChunkInfo ci = chunk_info(meta, S, c);
     // segmented state passing: the entering state is the stored local one plus
     // exp(F) times the segment's starting state (none in a first segment)
@@ -1611,12 +1625,17 @@ static void launch_scan_fast_s(const PrefillDims &d, const void *x, const void *
                         (size_t)(Q / 32) * 64 * kScanLDR * sizeof(bf16);
     static size_t raised = 0;
     allow_lds(reinterpret_cast<const void *>(&chunk_scan_fast_kernel<Q, SEG>), smem, raised);
-    const unsigned nblk = (unsigned)((int64_t)d.max_chunks * d.H);
+    // chunk-interleaved XCD order once there are at least two chunks per XCD
+    const int by_chunk = d.max_chunks >= 2 * kXcds;
+    const int64_t rounds = ((int64_t)d.max_chunks + kXcds - 1) / kXcds;
+    const unsigned nblk = (unsigned)(by_chunk ? rounds * kXcds * d.H
+                                              : (int64_t)d.max_chunks * d.H);
     hipLaunchKernelGGL((chunk_scan_fast_kernel<Q, SEG>), dim3(nblk), dim3(2 * Q), smem, st, d.S,
                        d.H, d.G, d.max_chunks, static_cast<const bf16 *>(x),
                        static_cast<const bf16 *>(C), D, meta, cum, dtc,
                        static_cast<const bf16 *>(CB), static_cast<const bf16 *>(entering),
-                       static_cast<bf16 *>(y), seg.I, seg.F, static_cast<const bf16 *>(seg.carry));
+                       static_cast<bf16 *>(y), seg.I, seg.F, static_cast<const bf16 *>(seg.carry),
+                       by_chunk);
 }
 
 template <int Q>
