@@ -850,12 +850,14 @@ void state_scan_fast_kernel(
     bf16 *xs = reinterpret_cast<bf16 *>(smem);   // [Q][LDX]  x_t
     bf16 *bs = xs + Q * LDX;                     // [Q][LDB]  w_t B_t (slice columns)
 
-    // logical order (segment of sequence, head, column slice): the heads that
-    // share a B group sit side by side on one XCD
+    // logical order (head, segment of sequence, column slice): each XCD takes a
+    // contiguous range of heads with every sequence of the batch, so a batch of
+    // long and short sequences gives every XCD the same chain lengths, and the
+    // heads that share a B group sit side by side on one XCD
     const int nsg = SEG ? nseg : 1;
     const int nblk = S * nsg * H * NS;
     const int lb = xcd_logical_block(blockIdx.x, nblk);
-    const int q = lb % NS, h = (lb / NS) % H, sb = lb / (NS * H);
+    const int q = lb % NS, sb = (lb / NS) % (S * nsg), h = lb / (NS * S * nsg);
     const int s = sb / nsg, b = sb - s * nsg;
     const int g = h / (H / G);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1337,17 +1339,20 @@ void chunk_scan_fast_kernel(
     float *scum = reinterpret_cast<float *>(ys + (Q / 32) * P * kScanLDR);  // [Q] cum * log2(e)
     float *sdt = scum + Q;                                     // [Q]
 
-    // Unit (chunk c, head h). With by_chunk, XCD x takes the chunks c = x mod 8,
-    // all heads of each: every XCD gets the same number of real chunks whatever
-    // the padding of max_chunks (the grid is padded to whole rounds of 8 chunks;
-    // the padding blocks leave at once). Otherwise each XCD takes one contiguous
-    // range of units in order c H + h. Either way the heads of a chunk share its
-    // C and CB in one L2.
+    // Unit (chunk c, head h). With by_chunk, the (chunk, group) pairs u = c G + g
+    // are dealt to the XCDs as u mod 8, each with all heads of its group: every
+    // XCD gets the same share of real chunks, whatever the padding of max_chunks
+    // and however the chunk lengths vary along the batch (the grid is padded to
+    // whole rounds of 8 pairs; the padding blocks leave at once). Otherwise each
+    // XCD takes one contiguous range of units in order c H + h. Either way the
+    // heads that read one (chunk, group)'s C and CB share an L2.
     int h, c;
     if (by_chunk) {
-        const int slot = blockIdx.x / kXcds, m = slot / H;
-        h = slot - m * H;
-        c = (int)(blockIdx.x % kXcds) + kXcds * m;
+        const int hpg = H / G;
+        const int slot = blockIdx.x / kXcds, m = slot / hpg;
+        const int u = (int)(blockIdx.x % kXcds) + kXcds * m;
+        c = u / G;
+        h = (u - c * G) * hpg + (slot - m * hpg);
         if (c >= max_chunks) return;
     } else {
         const int lb = xcd_logical_block(blockIdx.x, max_chunks * H);
@@ -1625,10 +1630,11 @@ static void launch_scan_fast_s(const PrefillDims &d, const void *x, const void *
                         (size_t)(Q / 32) * 64 * kScanLDR * sizeof(bf16);
     static size_t raised = 0;
     allow_lds(reinterpret_cast<const void *>(&chunk_scan_fast_kernel<Q, SEG>), smem, raised);
-    // chunk-interleaved XCD order once there are at least two chunks per XCD
-    const int by_chunk = d.max_chunks >= 2 * kXcds;
-    const int64_t rounds = ((int64_t)d.max_chunks + kXcds - 1) / kXcds;
-    const unsigned nblk = (unsigned)(by_chunk ? rounds * kXcds * d.H
+    // (chunk, group)-interleaved XCD order once there are at least two pairs per XCD
+    const int64_t pairs = (int64_t)d.max_chunks * d.G;
+    const int by_chunk = pairs >= 2 * kXcds;
+    const int64_t rounds = (pairs + kXcds - 1) / kXcds;
+    const unsigned nblk = (unsigned)(by_chunk ? rounds * kXcds * (d.H / d.G)
                                               : (int64_t)d.max_chunks * d.H);
     hipLaunchKernelGGL((chunk_scan_fast_kernel<Q, SEG>), dim3(nblk), dim3(2 * Q), smem, st, d.S,
                        d.H, d.G, d.max_chunks, static_cast<const bf16 *>(x),
