@@ -308,7 +308,11 @@ def main():
         us = avg_us(fn)
         kernels[name] = {"avg_us": round(us, 3), "bytes": nb[name],
                          "GBps": round(nb[name] / (us * 1e-6) / 1e9, 1)}
-    dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    # the roofline is reported for the chunk scan: the largest kernel of the timed call
+    # (the call cuts this layer's state pass into segments, which the step-wise
+    # chunk_state_passing entry point timed above does not, so that entry point's
+    # time is not the time the state pass takes inside the call)
+    dom = "chunk_scan"
     dk = kernels[dom]
     traffic = load_traffic(dom)
     roofline = {"kernel": dom, "bound": "hbm", "achieved": dk["GBps"], "peak": HBM_PEAK_GBS,

@@ -448,65 +448,36 @@ __device__ __forceinline__ void bmm_rows(int G, int Q, int c, int g, int z, cons
     // whole, zero above the diagonal, so that chunk scan needs no causal mask
     const int jd = i0 / 16;
     const int jmax = sizeof(TIn) == 2 && (jd & 1) == 0 ? jd + 1 : jd;
-    // lane holds CB^T[16 jt + 4 kg + v][i] = CB[i][16 jt + 4 kg + v], v = 0..3
-    // after the MFMAs: 4 consecutive elements in either layout (row-major for
-    // float32 inputs, MFMA fragment order for bf16 inputs)
-    auto store_tile = [&](int jt, f32x4 acc) {
+    for (int jt = wave; jt <= jmax; jt += 4) {
         const int jc = jt * 16 + 4 * kg;
-        float v4[4] = {acc[0], acc[1], acc[2], acc[3]};
+        if (jt > jd) {
+            const float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            store4<TIn>(cbc + cb_frag_offset(Q, i, jc), z);
+            continue;
+        }
+        const int j = jt * 16 + r16;
+        const int jcl = j < ci.len ? j : ci.len - 1;
+        typename M::frag bfr[NK];  // B rows j (A operand)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) v4[v] = jt <= jd && jc + v <= i ? v4[v] : 0.0f;
+        for (int kk = 0; kk < NK; ++kk) {
+            const int n = kk * M::K + kg * M::KPL;
+            const int nc = n < N ? n : 0;
+            const typename M::frag f = M::load(B + ((int64_t)(ci.start + jcl) * G + g) * N + nc);
+            bfr[kk] = (j < ci.len && n < N) ? f : M::zero();
+        }
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) acc = M::run(bfr[kk], cf[kk], acc);
+        // lane holds CB^T[16 jt + 4 kg + v][i] = CB[i][16 jt + 4 kg + v], v = 0..3:
+        // 4 consecutive elements in either layout (row-major for float32 inputs,
+        // MFMA fragment order for bf16 inputs)
+        float v4[4] = {acc[0], acc[1], acc[2], acc[3]};
+        if (jt == jd) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) v4[v] = jc + v <= i ? v4[v] : 0.0f;
+        }
         if constexpr (sizeof(TIn) == 2) store4<TIn>(cbc + cb_frag_offset(Q, i, jc), v4);
         else store4<TIn>(cbc + (int64_t)i * Q + jc, v4);
-    };
-    if constexpr (sizeof(TIn) == 2) {
-        // the wave's column tiles jt = wave + 4 it (Q / 16 <= 16 tiles): every
-        // B-row load is issued before the first MFMA, rows clamped into the
-        // chunk and zeroed where the values are used (a tile past the diagonal
-        // reloads the diagonal tile's rows and stores zeros)
-        constexpr int kIt = 4;
-        typename M::frag bfr[kIt][NK];
-#pragma unroll
-        for (int it = 0; it < kIt; ++it) {
-            const int jt = wave + 4 * it < jd ? wave + 4 * it : jd;
-            const int j = jt * 16 + r16;
-            const int jcl = j < ci.len ? j : ci.len - 1;
-#pragma unroll
-            for (int kk = 0; kk < NK; ++kk) {
-                const int n = kk * M::K + kg * M::KPL;
-                bfr[it][kk] = M::load(B + ((int64_t)(ci.start + jcl) * G + g) * N + (n < N ? n : 0));
-            }
-        }
-#pragma unroll
-        for (int it = 0; it < kIt; ++it) {
-            const int jt = wave + 4 * it;
-            if (jt > jmax) break;
-            const bool jok = jt * 16 + r16 < ci.len;
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int kk = 0; kk < NK; ++kk) {
-                const bool ok = jok && kk * M::K + kg * M::KPL < N;
-                acc = M::run(ok ? bfr[it][kk] : M::zero(), cf[kk], acc);
-            }
-            store_tile(jt, acc);
-        }
-    } else {
-        for (int jt = wave; jt <= jmax; jt += 4) {
-            const int j = jt * 16 + r16;
-            const int jcl = j < ci.len ? j : ci.len - 1;
-            typename M::frag bfr[NK];  // B rows j (A operand)
-#pragma unroll
-            for (int kk = 0; kk < NK; ++kk) {
-                const int n = kk * M::K + kg * M::KPL;
-                const int nc = n < N ? n : 0;
-                const typename M::frag f = M::load(B + ((int64_t)(ci.start + jcl) * G + g) * N + nc);
-                bfr[kk] = (j < ci.len && n < N) ? f : M::zero();
-            }
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int kk = 0; kk < NK; ++kk) acc = M::run(bfr[kk], cf[kk], acc);
-            store_tile(jt, acc);
-        }
     }
 }
 

@@ -90,6 +90,7 @@ CASES = [
     (3, 4, 8, 64, 128, 2, 20, BF16, BF16),  # bf16 fast path with 32 token slots
     (4, 4, 4, 64, 128, 4, 8, BF16, BF16),   # bf16 fast path, W = 2 T
     (3, 2, 8, 64, 128, 8, 40, BF16, BF16),  # bf16, ring longer than the fast path takes
+    (3, 3, 12, 64, 128, 2, 12, BF16, BF16),  # bf16 fast path, 6 heads per group (2 per block)
 ]
 
 
