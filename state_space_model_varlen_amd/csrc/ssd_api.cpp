@@ -340,11 +340,16 @@ static int combined(const ssd_problem *p, const ssd::DtTf &tf, const void *x, co
         seg.C = C;
         seg.CB = cb;
     }
-    // steps 1 and 4 in one launch, or (segmented) step 4 beside the carry step
-    if (seg.nseg > 1)
+    // steps 1 and 4 in one launch; or (segmented) step 4 beside the carry step;
+    // or, with many (chunk, group) pairs, step 4 one pair per block after step 1
+    if (seg.nseg > 1) {
         ssd::launch_chunk_cumsum(d, dt, A, cu_seqlens, meta, cum, dtc, stream, tf);
-    else
+    } else if (ssd::cb_by_pair(d)) {
+        ssd::launch_chunk_cumsum(d, dt, A, cu_seqlens, meta, cum, dtc, stream, tf);
+        ssd::launch_bmm(d, B, C, meta, cb, stream);
+    } else {
         ssd::launch_chunk_prep(d, dt, A, cu_seqlens, meta, cum, dtc, B, C, cb, stream, tf);
+    }
     if (ssd::fused_state_path(d)) {
         ssd::launch_state_scan(d, x, B, meta, cum, dtc, state_cache, state_indices,
                                has_initial_state, entering, checkpoints, stream, &seg);

@@ -94,6 +94,10 @@ void launch_state_scan(const PrefillDims &d, const void *x, const void *B, const
                        const SegBufs *seg = nullptr);
 void launch_bmm(const PrefillDims &d, const void *B, const void *C, const int32_t *meta, void *CB,
                 void *stream);
+// Whether launch_bmm computes CB with one block per (chunk, group) pair (bf16,
+// d_state 128, enough pairs to fill the chip); the combined call then runs step
+// 1 alone and launch_bmm after it, instead of launch_chunk_prep.
+bool cb_by_pair(const PrefillDims &d);
 void launch_chunk_scan(const PrefillDims &d, const void *x, const void *C, const float *D,
                        const int32_t *meta, const float *cum, const float *dtc, const void *CB,
                        const void *entering, void *y, void *stream,

@@ -492,6 +492,90 @@ __global__ __launch_bounds__(256) void bmm_kernel(int S, int G, int Q, int max_c
     bmm_rows<TIn, N>(G, Q, c, blockIdx.y, blockIdx.z, chunk_info(meta, S, c), B, C, CB);
 }
 
+// CB for one (chunk, group) pair per block (bf16, d_state 128), for batches
+// with enough pairs to fill the chip. The chunk's B rows are staged in LDS once
+// and every row tile of the pair reads its A operands there, where the row-tile
+// blocks of bmm_kernel each fetch them again from L2 (at Q = 256 that is 136
+// column tiles of 4 KiB per pair instead of 64 KiB). Same products, layout and
+// zeros as bmm_rows. Block of 2 Q threads (Q / 32 waves); wave w takes row
+// tiles w and Q / 16 - 1 - w, so the causal work is balanced.
+constexpr int kCbLDB = 136;       // B row pitch in LDS (bf16): 68 dwords, conflict-free b128 reads
+constexpr int kCbPairMin = 128;   // pairs from which the per-pair kernel is used
+
+template <int Q>
+__global__ __launch_bounds__(2 * Q) void bmm_pair_kernel(int S, int G,
+                                                         const bf16 *__restrict__ B,
+                                                         const bf16 *__restrict__ C,
+                                                         const int32_t *__restrict__ meta,
+                                                         bf16 *__restrict__ CB)
+{
+    constexpr int N = 128, NT = 2 * Q, KV = Q * (N / 8) / NT;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    bf16 *bs = reinterpret_cast<bf16 *>(smem);   // [Q][kCbLDB]
+    const int c = blockIdx.x / G, g = blockIdx.x - c * G;
+    const ChunkInfo ci = chunk_info(meta, S, c);
+    if (ci.len <= 0) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int len = ci.len;
+    // B and C rows through buffer resources ending at the chunk's last row
+    // (rows past it read as zero, with no branch around the loads)
+    const uint32_t brow = (uint32_t)G * N * 2;
+    const rsrc_t rb = make_rsrc(B + ((int64_t)ci.start * G + g) * N, (uint32_t)(len - 1) * brow + N * 2);
+    const rsrc_t rc = make_rsrc(C + ((int64_t)ci.start * G + g) * N, (uint32_t)(len - 1) * brow + N * 2);
+    uint4 bv[KV];
+#pragma unroll
+    for (int k = 0; k < KV; ++k) {
+        const int u = tid + NT * k;
+        bv[k] = buf_ld16(rb, (uint32_t)(u >> 4) * brow + 16 * (u & 15));
+    }
+    // C rows i = 16 rt + r16 of the wave's two row tiles: B operand fragments
+    const int rt[2] = {Q / 16 - 1 - wave, wave};
+    uint4 cf[2][4];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            cf[a][kk] = buf_ld16(rc, (uint32_t)(16 * rt[a] + r16) * brow + 64 * kk + 16 * kg);
+#pragma unroll
+    for (int k = 0; k < KV; ++k) {
+        const int u = tid + NT * k;
+        *reinterpret_cast<uint4 *>(bs + (u >> 4) * kCbLDB + 8 * (u & 15)) = bv[k];
+    }
+    __syncthreads();
+    bf16 *cbc = CB + ((int64_t)c * G + g) * Q * Q;
+    const int ntiles = (len + 15) / 16;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        const int z = rt[a];
+        if (z >= ntiles) continue;
+        const int i = 16 * z + r16;
+        // the 16 x 32 blocks holding the diagonal are written whole, zero above it
+        const int jmax = (z & 1) == 0 ? z + 1 : z;
+        for (int jt = 0; jt <= jmax; ++jt) {
+            const int jc = jt * 16 + 4 * kg;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const bf16x8 af =
+                    *reinterpret_cast<const bf16x8 *>(bs + (16 * jt + r16) * kCbLDB + 32 * kk + 8 * kg);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8, cf[a][kk]),
+                                                              acc, 0, 0, 0);
+            }
+            // lane holds CB[i][16 jt + 4 kg + v], v = 0..3
+            float v4[4] = {acc[0], acc[1], acc[2], acc[3]};
+#pragma unroll
+            for (int v = 0; v < 4; ++v) v4[v] = jt <= z && jc + v <= i ? v4[v] : 0.0f;
+            store4<bf16>(cbc + cb_frag_offset(Q, i, jc), v4);
+        }
+    }
+}
+
+bool cb_by_pair(const PrefillDims &d)
+{
+    return d.in_bf16 && d.N == 128 && (int64_t)d.max_chunks * d.G >= kCbPairMin;
+}
+
 // Steps 1 and 4 in one launch (the combined call): grid (max_chunks, HB + G Q / 16),
 // HB = ceil(H / 4). Blocks with blockIdx.y < HB are cumsum blocks (four heads,
 // metadata published by blockIdx.y == 0), the others compute one CB row tile.
@@ -1653,11 +1737,32 @@ void launch_chunk_state(const PrefillDims &d, const void *x, const void *B, cons
     else SSD_DISPATCH_PN(d, launch_state_t, float, d, x, B, meta, cum, dtc, states, st);
 }
 
+template <int Q>
+static void launch_bmm_pair(const PrefillDims &d, const void *B, const void *C, const int32_t *meta,
+                            void *CB, hipStream_t st)
+{
+    const size_t smem = (size_t)Q * kCbLDB * sizeof(bf16);
+    static size_t raised = 0;
+    allow_lds(reinterpret_cast<const void *>(&bmm_pair_kernel<Q>), smem, raised);
+    hipLaunchKernelGGL(bmm_pair_kernel<Q>, dim3((unsigned)((int64_t)d.max_chunks * d.G)),
+                       dim3(2 * Q), smem, st, d.S, d.G, static_cast<const bf16 *>(B),
+                       static_cast<const bf16 *>(C), meta, static_cast<bf16 *>(CB));
+}
+
 void launch_bmm(const PrefillDims &d, const void *B, const void *C, const int32_t *meta, void *CB,
                 void *stream)
 {
     if (d.max_chunks <= 0) return;
     hipStream_t st = as_stream(stream);
+    if (cb_by_pair(d)) {
+        switch (d.Q) {
+            case 32: launch_bmm_pair<32>(d, B, C, meta, CB, st); break;
+            case 64: launch_bmm_pair<64>(d, B, C, meta, CB, st); break;
+            case 128: launch_bmm_pair<128>(d, B, C, meta, CB, st); break;
+            default: launch_bmm_pair<256>(d, B, C, meta, CB, st); break;
+        }
+        return;
+    }
     if (d.in_bf16) {
         if (d.N == 128) launch_bmm_t<bf16, 128>(d, B, C, meta, CB, st);
         else launch_bmm_t<bf16, 16>(d, B, C, meta, CB, st);

@@ -52,6 +52,8 @@ STEP_CASES = [
     ((129, 64), 2, 16, 128, 1, 64, BF16, F32),
     ((77, 200), 2, 64, 16, 2, 64, BF16, BF16),
     ((90, 33), 2, 64, 128, 2, 64, F32, F32),
+    # 23 chunk slots x 8 groups: CB with one block per (chunk, group) pair
+    ((300, 5, 213, 0, 64), 8, 64, 128, 8, 32, BF16, BF16),
 ]
 
 
