@@ -145,6 +145,10 @@ E2E_CASES = [
     ((1000,), 2, 64, 128, 1, 256, BF16, F32, False),
     ((150, 90), 4, 16, 128, 2, 32, BF16, BF16, True),
     ((90, 150), 4, 64, 16, 4, 64, F32, BF16, True),
+    # at least 128 (chunk, group) pairs: CB one block per pair, chunk scan dealing
+    # pairs over the XCDs (one head per group)
+    ((400, 77, 130), 16, 64, 128, 16, 64, BF16, F32, True),
+    ((700, 260, 5, 90), 16, 64, 128, 16, 128, BF16, BF16, False),
 ]
 
 
