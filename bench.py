@@ -49,6 +49,12 @@ def parse():
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the other prefill shapes (used for the profiling runs, so that "
                          "every dispatch of a kernel has the headline shape)")
+    ap.add_argument("--shape", choices=("cached_continuation_32x32", "mixed_varlen_8seq_ckpt"),
+                    help="time only the combined call on this other prefill shape (for a kernel "
+                         "trace of that shape); prints one JSON line for it")
+    ap.add_argument("--summarize-shape-trace", nargs=2, metavar=("TRACE_DIR", "SHAPE"),
+                    help="write profiles/kernel_trace_prefill_<SHAPE>.md from the rocprofv3 "
+                         "kernel trace of `--shape SHAPE` (no GPU work)")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summaries from rocprofv3 output of this script "
                          "(no GPU work)")
@@ -202,6 +208,78 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, cmds):
     print("\n".join(lines))
 
 
+def shape_only(args, sy, ssd, torch):
+    """The combined call alone on one of the other prefill shapes: W warm-up and K
+    timed calls, HIP events on the call's stream. Used for the kernel trace of that
+    shape (prints its time per call and tokens/s)."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    ocfg = {"cached_continuation_32x32": sy.C2, "mixed_varlen_8seq_ckpt": sy.C3}[args.shape]
+    oin = sy.make_prefill(ocfg)
+    oT, oS, oH, oP, oN, oG, oQ = (ocfg.total_tokens, ocfg.num_seqs, ocfg.nheads, ocfg.headdim,
+                                  ocfg.d_state, ocfg.ngroups, ocfg.chunk_size)
+    op = ssd.make_problem(oT, oS, oH, oP, oN, oG, oQ, ocfg.num_slots, ocfg.in_dtype,
+                          ocfg.state_dtype)
+    ox, odt, oA, oB, oC, oD = (t.to(dev) for t in (oin.x, oin.dt, oin.A, oin.B, oin.C, oin.D))
+    ocu, oidx = oin.cu_seqlens.to(dev), oin.state_indices.to(dev)
+    ohi = oin.has_initial.to(dev) if oin.has_initial is not None else None
+    gen = torch.Generator(device=dev).manual_seed(4)
+    ocache = (torch.randn(ocfg.num_slots, oH, oP, oN, device=dev, generator=gen) * 0.03
+              ).to(ocfg.state_dtype)
+    ock = (torch.empty(ssd.max_chunks(op), oH, oP, oN, dtype=ocfg.state_dtype, device=dev)
+           if ocfg.checkpoints else None)
+    oy = torch.empty(oT, oH, oP, dtype=ocfg.in_dtype, device=dev)
+    ows = ssd.alloc_workspace(op, dev)
+
+    def call():
+        ssd.ssd_combined_varlen(op, ox, odt, oA, oB, oC, oD, ocu, ocache, oidx, ohi, oy, ock, ows,
+                                stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(20_000_000)
+    a.record(stream)
+    for _ in range(args.steps):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / args.steps
+    print(json.dumps({"shape": args.shape, "tokens": oT, "seqs": oS, "combined_us": round(us, 3),
+                      "tokens_per_s": round(oT / (us * 1e-6), 1), "steps": args.steps,
+                      "warmup": args.warmup}), flush=True)
+
+
+def shape_trace_command(shape):
+    return ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof/" + shape +
+            " -o run -- python3 bench.py --shape " + shape + " --steps 200 --warmup 50")
+
+
+def summarize_shape_trace(trace_dir, shape):
+    """profiles/kernel_trace_prefill_<shape>.md from the kernel statistics of
+    shape_trace_command(shape) (the library's kernels only)."""
+    import csv
+    stats = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
+    lines = [f"# Kernel trace: SSD prefill, {shape} (the combined call alone)", "",
+             "Command (MI355X, one GPU, from the repository root):", "```",
+             shape_trace_command(shape), "```",
+             "Source: `run_kernel_stats.csv` written by that command (rocprofv3 `--stats`): "
+             "50 warm-up and 200 timed calls of ssd_combined_varlen; torch kernels (input "
+             "generation, casts) omitted.", "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in stats:
+        if "ssd" not in r["Name"]:
+            continue
+        lines.append(f"| `{r['Name'][:70]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    out = os.path.join(ROOT, "profiles", f"kernel_trace_prefill_{shape}.md")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 PROFILE_COMMANDS = [
     "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof/trace -o c1 -- "
     "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline --headline-only",
@@ -217,6 +295,9 @@ def main():
     if args.summarize_profiles:
         summarize_profiles(*args.summarize_profiles, PROFILE_COMMANDS)
         return
+    if args.summarize_shape_trace:
+        summarize_shape_trace(*args.summarize_shape_trace)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} (WORLD_SIZE={world}) is not "
@@ -229,6 +310,10 @@ def main():
 
     import ssd_synth as sy
     import state_space_model_varlen_amd as ssd
+
+    if args.shape:
+        shape_only(args, sy, ssd, torch)
+        return
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
