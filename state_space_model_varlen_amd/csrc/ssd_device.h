@@ -216,8 +216,10 @@ __device__ __forceinline__ uint4 philox4x32(uint4 c, uint32_t k0, uint32_t k1, i
             k0 += 0x9E3779B9u;
             k1 += 0xBB67AE85u;
         }
-        const uint32_t hi0 = __umulhi(0xD2511F53u, c.x), lo0 = 0xD2511F53u * c.x;
-        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z), lo1 = 0xCD9E8D57u * c.z;
+        // (one 32 x 32 -> 64-bit product each: both halves from one multiply)
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c.x, p1 = (uint64_t)0xCD9E8D57u * c.z;
+        const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
         c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
     }
     return c;
@@ -236,9 +238,11 @@ __device__ __forceinline__ f16 sr_f16(float x, uint32_t w)
     const uint16_t lob = fabsf(static_cast<float>(rne)) > a ? (uint16_t)(bits - 1) : bits;
     const float l = fabsf(static_cast<float>(__builtin_bit_cast(f16, lob)));
     const float h = fabsf(static_cast<float>(__builtin_bit_cast(f16, (uint16_t)(lob + 1))));
-    const float prob = (a - l) / (h - l);
+    // u < (a - l) / (h - l), taken as u (h - l) < a - l: h - l is a power of two
+    // (the fp16 spacing below h) and a - l is exact, so both sides are exact and
+    // the test is the same as with the quotient, without a division
     const float u = static_cast<float>(w >> 8) * 0x1p-24f;
-    return __builtin_bit_cast(f16, (a != l && u < prob) ? (uint16_t)(lob + 1) : lob);
+    return __builtin_bit_cast(f16, (a != l && u * (h - l) < a - l) ? (uint16_t)(lob + 1) : lob);
 }
 
 // Philox streams of the state arrays a kernel writes
