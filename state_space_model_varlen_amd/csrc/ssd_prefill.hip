@@ -46,9 +46,10 @@ __device__ __forceinline__ int first_chunk_len(int Q, const int32_t *__restrict_
 
 // Block-wide: locate chunk c among the sequences of cu_seqlens. Writes
 // chunk_cu to meta[0..S], the clamped cu_seqlens after the chunk triples and
-// the first-chunk lengths after those when `publish_cu`. Returns (seq, k, f)
-// through shared memory: chunk c is chunk k of sequence seq, whose first
-// chunk has f tokens; seq = -1 when c >= nc.
+// the first-chunk lengths after those when `publish_cu`. Returns (seq, k, f,
+// a, b) through shared memory: chunk c is chunk k of sequence seq, whose first
+// chunk has f tokens and whose clamped token range is [a, b); seq = -1 when
+// c >= nc.
 __device__ void find_chunk(int T, int S, int Q, int max_chunks, const int32_t *__restrict__ cu,
                            const int32_t *__restrict__ prefix, int c, bool publish_cu,
                            int32_t *__restrict__ meta, int *s_found, int *s_wave_tot)
@@ -63,9 +64,10 @@ __device__ void find_chunk(int T, int S, int Q, int max_chunks, const int32_t *_
     for (int base = 0; base < S; base += 256) {
         __syncthreads();
         const int s = base + tid;
-        int cnt = 0, f = Q;
+        int cnt = 0, f = Q, a = 0, b = 0;
         if (s < S) {
-            const int a = clampi(cu[s], 0, T), b = clampi(cu[s + 1], 0, T);
+            a = clampi(cu[s], 0, T);
+            b = clampi(cu[s + 1], 0, T);
             const int L = b > a ? b - a : 0;
             f = first_chunk_len(Q, prefix, s);
             cnt = L == 0 ? 0 : (L <= f ? 1 : 1 + (L - f + Q - 1) / Q);
@@ -90,6 +92,8 @@ __device__ void find_chunk(int T, int S, int Q, int max_chunks, const int32_t *_
                 s_found[0] = s;
                 s_found[1] = c - first;
                 s_found[2] = f;
+                s_found[3] = a;     // the sequence's clamped token range, so that
+                s_found[4] = b;     // found_chunk need not load it again
             }
         }
         running += tile_tot;
@@ -101,16 +105,15 @@ __device__ void find_chunk(int T, int S, int Q, int max_chunks, const int32_t *_
     __syncthreads();
 }
 
-// Chunk (seq, start, len) of chunk c after find_chunk, from cu_seqlens.
-__device__ __forceinline__ ChunkInfo found_chunk(int T, int Q, const int32_t *__restrict__ cu,
-                                                 const int *s_found)
+// Chunk (seq, start, len) of chunk c after find_chunk (from what it kept of cu_seqlens).
+__device__ __forceinline__ ChunkInfo found_chunk(int Q, const int *s_found)
 {
     ChunkInfo ci;
     ci.seq = s_found[0];
     ci.start = 0;
     ci.len = 0;
     if (ci.seq >= 0) {
-        const int a = clampi(cu[ci.seq], 0, T), b = clampi(cu[ci.seq + 1], 0, T);
+        const int a = s_found[3], b = s_found[4];
         const int k = s_found[1], f = s_found[2];
         ci.start = a + (k == 0 ? 0 : f + (k - 1) * Q);
         const int cap = k == 0 ? f : Q;
@@ -182,13 +185,13 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(
     const int32_t *__restrict__ prefix)
 {
     __shared__ int s_wave_tot[4];
-    __shared__ int s_found[3];
+    __shared__ int s_found[5];
     const int c = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const bool publish = blockIdx.y == 0;
     find_chunk(T, S, Q, max_chunks, cu, prefix, c, publish && blockIdx.x == 0, meta, s_found,
                s_wave_tot);
-    const ChunkInfo ci = found_chunk(T, Q, cu, s_found);
+    const ChunkInfo ci = found_chunk(Q, s_found);
     if (publish && threadIdx.x == 0) publish_chunk(S, c, ci, meta);
     const int h = blockIdx.y * kCumsumHeadsPerBlock + wave;
     if (ci.len <= 0 || h >= H) return;
@@ -589,13 +592,13 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     const TIn *__restrict__ C, TIn *__restrict__ CB, DtTf tf, const int32_t *__restrict__ prefix)
 {
     __shared__ int s_wave_tot[4];
-    __shared__ int s_found[3];
+    __shared__ int s_found[5];
     const int c = blockIdx.x;
     const int HB = (H + kCumsumHeadsPerBlock - 1) / kCumsumHeadsPerBlock;
     const bool publish = blockIdx.y == 0;
     find_chunk(T, S, Q, max_chunks, cu, prefix, c, publish && blockIdx.x == 0, meta, s_found,
                s_wave_tot);
-    const ChunkInfo ci = found_chunk(T, Q, cu, s_found);
+    const ChunkInfo ci = found_chunk(Q, s_found);
     if ((int)blockIdx.y < HB) {
         if (publish && threadIdx.x == 0) publish_chunk(S, c, ci, meta);
         const int h = blockIdx.y * kCumsumHeadsPerBlock + (threadIdx.x >> 6);
@@ -762,10 +765,11 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
 //
 // Tiles are staged in LDS row-major - token rows, 16-byte copies straight
 // from HBM - and MFMA operands that need the token index contiguous per lane
-// are read with the LDS transpose read (mfma_frag_tr). Rows are padded by 16
-// bytes (LD = 72 elements = 36 dwords), which puts the four rows one 16-lane
-// group reads in disjoint bank ranges. Blocks are put in XCD-aware order so
-// the heads sharing a chunk's B, C and CB run on one L2.
+// are read with the LDS transpose read (mfma_frag_tr). Rows are padded: 72
+// elements (36 dwords) in chunk_state, which puts the four rows one 16-lane
+// group reads in disjoint bank ranges; 80 elements (40 dwords) in the fused
+// state kernel and the chunk scan, with no overlap at all. Blocks are put in
+// XCD-aware order so the heads sharing a chunk's B, C and CB run on one L2.
 constexpr int kFastLD = 72;   // row pitch of token-major tiles (64 bf16 + 8 pad)
 constexpr float kLog2e = 1.4426950408889634f;
 
