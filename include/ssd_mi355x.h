@@ -273,8 +273,8 @@ int ssd_chunk_scan(const ssd_problem *p, const void *x, const void *C, const flo
 
 /*
  * The whole prefill: steps 1-5 enqueued on one stream with no host
- * synchronisation (steps 1 and 4 share one launch), intermediates in the
- * caller's workspace (vLLM PR #61501,
+ * synchronisation (three or four launches; how the steps are grouped depends
+ * on the shapes), intermediates in the caller's workspace (vLLM PR #61501,
  * sections "Details" and "Claims"; vLLM PR #62922, section "Details").
  * Semantics are those of the five steps composed: every initial state is
  * read as it was before the call even though the call overwrites the slot.
