@@ -351,6 +351,26 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = T * args.steps / elapsed
 
+    # the same call with the last-level cache (256 MB on MI355X) flushed before each
+    # call by a 512 MiB device write, each call timed alone: how much of the warm
+    # figure comes from inputs still cached from the previous call (context only)
+    cold = None
+    if not args.headline_only:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        ca_, cb_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        times = []
+        for _ in range(max(args.steps // 4, 5)):
+            flush.fill_(1)
+            ca_.record(stream)
+            step()
+            cb_.record(stream)
+            torch.cuda.synchronize()
+            times.append(ca_.elapsed_time(cb_) * 1e3)
+        del flush
+        cold_us = float(np.median(times))
+        cold = {"us_per_step": round(cold_us, 2), "tokens_per_s": round(T / (cold_us * 1e-6), 1),
+                "calls": len(times), "flush_bytes": 512 << 20}
+
     # ------------------------------------------------------------------ per-kernel timing
     nc = int(np.ceil(T / Q))
     buf = ssd.alloc_step_buffers(p, dev)
@@ -653,6 +673,7 @@ def main():
                    "ngroups": G, "chunk_size": Q, "inputs": "bf16 x/B/C/dt, fp32 A/D/state",
                    "parallelism": "single GPU"},
         "roofline": roofline,
+        "cold_cache": cold,
         "hbm_copy_GBps": round(copy_gbps, 1),
         "kernels": kernels,
         "decode": decode,
