@@ -337,78 +337,98 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(
 // Sequential over the sequence's chunks in float32 registers; bandwidth-bound.
 // The entering states are stored in the dtype chunk scan feeds its MFMA
 // (TE = input dtype), the checkpoints and the final state in the cache dtype.
-template <typename TS, typename TE>
+template <typename TS, typename TE, int EG>
 __global__ __launch_bounds__(256) void state_passing_kernel(
     int S, int H, int PN, int Q, int max_chunks, int num_slots, const float *states,
     const float *__restrict__ cum, const int32_t *__restrict__ meta, TS *cache,
     const int32_t *__restrict__ idx, const uint8_t *__restrict__ has_init, TE *entering,
     TS *__restrict__ ckpt, SrCtx sr)
 {
-    const int EB = (PN + 1023) / 1024;
+    // a block covers 1024 EG consecutive state elements of one (sequence, head):
+    // group g of a thread is elements e0 + 1024 g .. + 3 (PN is a multiple of
+    // 1024 EG whenever EG > 1)
+    const int EB = (PN + 1024 * EG - 1) / (1024 * EG);
     const int b = blockIdx.x;
     const int eb = b % EB;
     const int h = (b / EB) % H;
     const int s = b / (EB * H);
-    const int e = (eb * 256 + threadIdx.x) * 4;
-    if (s >= S || e >= PN) return;
+    const int e0 = eb * 1024 * EG + threadIdx.x * 4;
+    if (s >= S || e0 >= PN) return;
 
     const int slot = idx[s];
     const bool slot_ok = slot >= 0 && slot < num_slots;
     const bool read_init = slot_ok && (has_init != nullptr && has_init[s] != 0);
-    TS *cslot = cache + ((int64_t)(slot_ok ? slot : 0) * H + h) * PN + e;
+    TS *cslot = cache + ((int64_t)(slot_ok ? slot : 0) * H + h) * PN + e0;
 
     // every load below is unconditional (a branch between a load and its use makes
     // the compiler wait on the load right there): the initial state is loaded from
     // slot 0 when there is none and cleared bit-wise; batch entries past the
     // sequence's last chunk reload that chunk and are not used
-    float hs[4];
-    load4<TS>(cslot, hs);
+    float hs[EG][4];
+#pragma unroll
+    for (int g = 0; g < EG; ++g) load4<TS>(cslot + 1024 * g, hs[g]);
     const uint32_t keep = read_init ? 0xffffffffu : 0u;
     const SrKey srk = sr_key(sr, meta);
 
     int c0 = meta[s], c1 = meta[s + 1];
     c0 = c0 < max_chunks ? c0 : max_chunks;
     c1 = c1 < max_chunks ? c1 : max_chunks;
-    // chunks in batches of 16, then 4, then 1: every chunk state of a batch is
-    // requested before the sequential recurrence over it runs, and a batch never
-    // reaches past the sequence's last chunk (so its loads need no guard)
+    // chunks in batches (16, 4 and 1 with one element group per thread; 4 and 1
+    // with four): every chunk state of a batch is requested before the sequential
+    // recurrence over it runs, and a batch never reaches past the sequence's last
+    // chunk (so its loads need no guard)
     bool masked = false;
     auto batch = [&](int cb, auto kb) {
         constexpr int K = decltype(kb)::value;
-        float sc[K][4], dec[K];
+        float sc[K][EG][4], dec[K];
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int c = cb + k;
-            load4<float>(states + ((int64_t)c * H + h) * PN + e, sc[k]);
+#pragma unroll
+            for (int g = 0; g < EG; ++g)
+                load4<float>(states + ((int64_t)c * H + h) * PN + e0 + 1024 * g, sc[k][g]);
             const int len = meta[(S + 1) + 3 * c + 2];
             const float cl = cum[((int64_t)h * max_chunks + c) * Q + (len > 0 ? len - 1 : 0)];
             dec[k] = len > 0 ? __expf(cl) : 1.0f;
         }
         if (!masked) {     // the initial state is used only now, after the batch was requested
 #pragma unroll
-            for (int q = 0; q < 4; ++q) hs[q] = __uint_as_float(__float_as_uint(hs[q]) & keep);
+            for (int g = 0; g < EG; ++g)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) hs[g][q] = __uint_as_float(__float_as_uint(hs[g][q]) & keep);
             masked = true;
         }
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            const int64_t off = ((int64_t)(cb + k) * H + h) * PN + e;
-            // the chunk state at `off` was loaded above, before the entering
-            // state (which may share its memory) is stored
-            store4<TE>(entering + off, hs);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) hs[q] = dec[k] * hs[q] + sc[k][q];
-            if (ckpt) put4<TS>(ckpt + off, hs, srk, (uint64_t)off, kSrCkpt);
+            for (int g = 0; g < EG; ++g) {
+                const int64_t off = ((int64_t)(cb + k) * H + h) * PN + e0 + 1024 * g;
+                // the chunk state at `off` was loaded above, before the entering
+                // state (which may share its memory) is stored
+                store4<TE>(entering + off, hs[g]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) hs[g][q] = dec[k] * hs[g][q] + sc[k][g][q];
+                if (ckpt) put4<TS>(ckpt + off, hs[g], srk, (uint64_t)off, kSrCkpt);
+            }
         }
     };
     int cb = c0;
-    for (; cb + 16 <= c1; cb += 16) batch(cb, std::integral_constant<int, 16>());
+    if constexpr (EG == 1)
+        for (; cb + 16 <= c1; cb += 16) batch(cb, std::integral_constant<int, 16>());
     for (; cb + 4 <= c1; cb += 4) batch(cb, std::integral_constant<int, 4>());
     for (; cb < c1; ++cb) batch(cb, std::integral_constant<int, 1>());
     if (!masked) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) hs[q] = __uint_as_float(__float_as_uint(hs[q]) & keep);
+        for (int g = 0; g < EG; ++g)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) hs[g][q] = __uint_as_float(__float_as_uint(hs[g][q]) & keep);
     }
-    if (slot_ok) put4<TS>(cslot, hs, srk, (uint64_t)(((int64_t)slot * H + h) * PN + e), kSrFinal);
+    if (slot_ok) {
+#pragma unroll
+        for (int g = 0; g < EG; ++g)
+            put4<TS>(cslot + 1024 * g, hs[g], srk,
+                     (uint64_t)(((int64_t)slot * H + h) * PN + e0 + 1024 * g), kSrFinal);
+    }
 }
 
 // ===========================================================================
@@ -1776,17 +1796,29 @@ void launch_bmm(const PrefillDims &d, const void *B, const void *C, const int32_
     }
 }
 
+constexpr int64_t kSpMinBlocks = 1024;   // four blocks per CU
+
 template <typename TS, typename TE>
 static void launch_sp_t(const PrefillDims &d, const float *states, const float *cum,
                         const int32_t *meta, void *cache, const int32_t *idx,
                         const uint8_t *has_init, void *entering, void *ckpt, hipStream_t st)
 {
     const int PN = d.P * d.N;
+    // four element groups per thread (more bytes in flight per sequence-chain
+    // latency) when the state splits evenly and there are still enough blocks
+    const int64_t blocks4 = (int64_t)d.S * d.H * (PN / 4096);
+    if (PN % 4096 == 0 && blocks4 >= kSpMinBlocks) {
+        hipLaunchKernelGGL((state_passing_kernel<TS, TE, 4>), dim3((unsigned)blocks4), dim3(256), 0,
+                           st, d.S, d.H, PN, d.Q, d.max_chunks, d.num_slots, states, cum, meta,
+                           static_cast<TS *>(cache), idx, has_init, static_cast<TE *>(entering),
+                           static_cast<TS *>(ckpt), d.sr);
+        return;
+    }
     const int EB = (PN + 1023) / 1024;
     dim3 grid((unsigned)((int64_t)d.S * d.H * EB));
-    hipLaunchKernelGGL((state_passing_kernel<TS, TE>), grid, dim3(256), 0, st, d.S, d.H, PN, d.Q,
-                       d.max_chunks, d.num_slots, states, cum, meta, static_cast<TS *>(cache), idx,
-                       has_init, static_cast<TE *>(entering), static_cast<TS *>(ckpt), d.sr);
+    hipLaunchKernelGGL((state_passing_kernel<TS, TE, 1>), grid, dim3(256), 0, st, d.S, d.H, PN,
+                       d.Q, d.max_chunks, d.num_slots, states, cum, meta, static_cast<TS *>(cache),
+                       idx, has_init, static_cast<TE *>(entering), static_cast<TS *>(ckpt), d.sr);
 }
 
 void launch_state_passing(const PrefillDims &d, const float *states, const float *cum,

@@ -54,6 +54,8 @@ STEP_CASES = [
     ((90, 33), 2, 64, 128, 2, 64, F32, F32),
     # 23 chunk slots x 8 groups: CB with one block per (chunk, group) pair
     ((300, 5, 213, 0, 64), 8, 64, 128, 8, 32, BF16, BF16),
+    # 64 sequences x 8 heads: state passing with four element groups per thread
+    (tuple((7 * i) % 70 + 1 for i in range(63)) + (130,), 8, 64, 128, 2, 64, BF16, F32),
 ]
 
 
