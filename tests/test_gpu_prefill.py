@@ -433,6 +433,8 @@ SEG_CASES = [
     ((4096,), 2, 256, BF16, [True]),
     ((300, 5000), 4, 128, F32, [False, True]),
     ((1537, 2049), 8, 32, BF16, [True, False]),
+    # one 65536-token sequence: 256 chunks in eight segments of 32
+    ((65536,), 2, 256, BF16, [True]),
 ]
 
 
