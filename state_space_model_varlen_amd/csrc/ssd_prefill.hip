@@ -1155,6 +1155,282 @@ void state_scan_fast_kernel(
     }
 }
 
+// The fused state kernel for batches of short sequences (no segments):
+// persistent blocks, each walking several (sequence, head, slice) items in the
+// same head-major order, with the one-chunk-ahead prefetch crossing item
+// boundaries. While an item's last chunk is folded in, the next item's initial
+// state and first tiles are in flight, and its metadata was requested one item
+// earlier, through vector loads (a scalar load in the loop would share its wait
+// counter with the MFMA phase's LDS reads). What the single-item kernel pays
+// per block - metadata, then the state and tiles, then the stores - is paid
+// once per block instead of once per item. Same arithmetic, same outputs.
+template <int Q, bool CKPT, typename TS>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
+void state_scan_multi_kernel(
+    int S, int H, int G, int max_chunks, int num_slots, const bf16 *__restrict__ x,
+    const bf16 *__restrict__ B, const int32_t *__restrict__ meta, const float *__restrict__ cum,
+    const float *__restrict__ dtc, TS *cache, const int32_t *__restrict__ idx,
+    const uint8_t *__restrict__ has_init, bf16 *__restrict__ entering, TS *__restrict__ ckpt,
+    SrCtx sr)
+{
+    constexpr int P = 64, N = 128, NSL = kScanNSL, NS = N / NSL;
+    constexpr int LDX = kScanLDX, LDB = kScanLDB;
+    typedef StateScanRegs<Q> Regs;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    bf16 *xs = reinterpret_cast<bf16 *>(smem);   // [Q][LDX]  x_t
+    bf16 *bs = xs + Q * LDX;                     // [Q][LDB]  w_t B_t (slice columns)
+
+    // items in logical order (h S + s) NS + q; XCD x owns one contiguous range of
+    // them and its blocks walk that range with a stride of their count
+    const int nitems = S * H * NS;
+    const int xcd = blockIdx.x % kXcds, bslot = blockIdx.x / kXcds;
+    const int nbx = ((int)gridDim.x - xcd + kXcds - 1) / kXcds;
+    const int qx = nitems / kXcds, rx_ = nitems % kXcds;
+    const int ibase = xcd < rx_ ? xcd * (qx + 1) : rx_ * (qx + 1) + (xcd - rx_) * qx;
+    const int icnt = qx + (xcd < rx_ ? 1 : 0);
+    const int nmine = bslot < icnt ? (icnt - bslot + nbx - 1) / nbx : 0;
+    if (nmine == 0) return;   // (uniform over the block, before any barrier)
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int pw = wave & 3, nh = wave >> 2;
+    const int PN = P * N;
+    // this lane's state elements: row 16 pw + r16, columns n0 + 32 nh + 16 j + 4 kg + 0..3
+    const int64_t run0 = (int64_t)(16 * pw + r16) * N + 32 * nh + 4 * kg;
+    const int tokoff = (S + 1) + 3 * max_chunks;
+    const SrKey srk = sr_key(sr, meta);
+
+    // an item's metadata as raw vector loads (clamped to the block's last item)
+    const rsrc_t rmeta = make_rsrc(meta, (uint32_t)(2 * (S + 1) + 3 * max_chunks + S) * 4u);
+    const rsrc_t ridx = make_rsrc(idx, (uint32_t)S * 4u);
+    const rsrc_t rflag = make_rsrc(has_init, has_init != nullptr ? (uint32_t)S : 0u);
+    struct MetaRaw {
+        float c0, c1, first, end, fcl, slot;
+        uint32_t flag;
+    };
+    auto item_id = [&](int k) { return ibase + bslot + (k < nmine ? k : nmine - 1) * nbx; };
+    auto meta_load = [&](MetaRaw &m, int k) {
+        const int s = (item_id(k) / NS) % S;
+        m.c0 = buf_ldf(rmeta, (uint32_t)s * 4);
+        m.c1 = buf_ldf(rmeta, (uint32_t)(s + 1) * 4);
+        m.first = buf_ldf(rmeta, (uint32_t)(tokoff + s) * 4);
+        m.end = buf_ldf(rmeta, (uint32_t)(tokoff + s + 1) * 4);
+        m.fcl = buf_ldf(rmeta, (uint32_t)(tokoff + S + 1 + s) * 4);
+        m.slot = buf_ldf(ridx, (uint32_t)s * 4);
+        m.flag = __builtin_amdgcn_raw_buffer_load_b8(rflag, (int)s, 0, 0);
+    };
+    struct Item {
+        int h, g, n0, lo, hi, first, end, fcl;
+        int64_t run;
+        bool slot_ok, read_init;
+        int slot;
+    };
+    auto rfl = [](float v) { return __builtin_amdgcn_readfirstlane(__float_as_int(v)); };
+    auto make_item = [&](const MetaRaw &m, int k) {
+        Item it;
+        const int lb = item_id(k);
+        it.h = lb / (NS * S);
+        it.g = it.h / (H / G);
+        it.n0 = (lb % NS) * NSL;
+        it.run = run0 + it.n0;
+        int c0 = rfl(m.c0), c1 = rfl(m.c1);
+        c0 = c0 < max_chunks ? c0 : max_chunks;
+        c1 = c1 < max_chunks ? c1 : max_chunks;
+        it.lo = c0;
+        it.hi = c1 > c0 ? c1 : c0;
+        it.first = rfl(m.first);
+        const int end = rfl(m.end);
+        it.end = end > it.first ? end : it.first;
+        const int fcl = rfl(m.fcl);
+        it.fcl = fcl < 1 ? 1 : (fcl > Q ? Q : fcl);
+        it.slot = rfl(m.slot);
+        it.slot_ok = it.slot >= 0 && it.slot < num_slots;
+        it.read_init = it.slot_ok && has_init != nullptr &&
+                       __builtin_amdgcn_readfirstlane((int)m.flag) != 0;
+        return it;
+    };
+    auto chunk_off = [](const Item &it, int c) { return c == it.lo ? 0 : it.fcl + (c - it.lo - 1) * Q; };
+    auto chunk_cap = [](const Item &it, int c) { return c == it.lo ? it.fcl : Q; };
+    auto chunk_len = [&](const Item &it, int c) {
+        const int st = it.first + chunk_off(it, c);
+        const int cap = chunk_cap(it, c);
+        return it.end - st < cap ? it.end - st : cap;
+    };
+
+    // byte offsets inside a chunk's tiles (the same for every chunk)
+    const uint32_t xrow = (uint32_t)H * P * 2, brow = (uint32_t)G * N * 2;
+    uint32_t xo[Regs::kXV], bo[Regs::kBV], to[Regs::kBV];
+#pragma unroll
+    for (int k = 0; k < Regs::kXV; ++k) {
+        const int u = tid + 512 * k;
+        xo[k] = u < Q * 8 ? (uint32_t)(u >> 3) * xrow + 16 * (u & 7) : 0xfffffff0u;
+    }
+#pragma unroll
+    for (int k = 0; k < Regs::kBV; ++k) {
+        const int u = tid + 512 * k;
+        bo[k] = u < Q * 8 ? (uint32_t)(u >> 3) * brow + 16 * (u & 7) : 0xfffffff0u;
+        to[k] = u < Q * 8 ? (uint32_t)(u >> 3) * 4 : 0xfffffff0u;
+    }
+    // chunk c of item `it` through buffer resources ending at the chunk's last row
+    // (rows past it read as zero); c outside the item's chunks reads nothing
+    auto fetch = [&](Regs &R, const Item &it, int c) {
+        const bool any = c < it.hi;
+        c = c < it.hi ? c : it.hi - 1;
+        c = c > it.lo ? c : it.lo;
+        const int st = it.first + chunk_off(it, c);
+        int len = chunk_len(it, c);
+        len = any ? len : 0;
+        const rsrc_t rx = make_rsrc(x + ((int64_t)st * H + it.h) * P,
+                                    any ? (uint32_t)(len - 1) * xrow + P * 2 : 0u);
+        const rsrc_t rb = make_rsrc(B + ((int64_t)st * G + it.g) * N + it.n0,
+                                    any ? (uint32_t)(len - 1) * brow + NSL * 2 : 0u);
+        const int64_t row = ((int64_t)it.h * max_chunks + c) * Q;
+        const rsrc_t rc = make_rsrc(cum + row, any ? (uint32_t)len * 4 : 0u);
+        const rsrc_t rd = make_rsrc(dtc + row, any ? (uint32_t)len * 4 : 0u);
+        R.cl = buf_ldf(rc, (uint32_t)(len - 1) * 4);
+#pragma unroll
+        for (int k = 0; k < Regs::kXV; ++k) R.x[k] = buf_ld16(rx, xo[k]);
+#pragma unroll
+        for (int k = 0; k < Regs::kBV; ++k) {
+            R.b[k] = buf_ld16(rb, bo[k]);
+            R.cm[k] = buf_ldf(rc, to[k]);
+            R.dt[k] = buf_ldf(rd, to[k]);
+        }
+    };
+    // an item's initial state (slot 0 stands in for a bad slot; selected later)
+    auto init_load = [&](float (&iv)[2][4], const Item &it) {
+        const TS *cs = cache + ((int64_t)(it.slot_ok ? it.slot : 0) * H + it.h) * PN + it.run;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) load4<TS>(cs + 16 * j, iv[j]);
+    };
+
+    MetaRaw mnext, mnext2;
+    meta_load(mnext, 0);
+    Item cur = make_item(mnext, 0);
+    meta_load(mnext, 1);
+    float iv[2][4];
+    init_load(iv, cur);
+    Regs R;
+    fetch(R, cur, cur.lo);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 acc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[j][e] = cur.read_init ? iv[j][e] : 0.0f;
+
+    for (int k = 0; k < nmine; ++k) {
+        const bool have_next = k + 1 < nmine;
+        const Item nxt = make_item(mnext, k + 1);   // (the last item again when there is none)
+        // an empty sequence makes one pass over zero tiles with its stores off
+        const int cend = cur.hi > cur.lo ? cur.hi : cur.lo + 1;
+        for (int c = cur.lo; c < cend; ++c) {
+            const bool live = c < cur.hi;
+            const int len = chunk_len(cur, c);
+            // rows the MFMA phase reads: whole 32-token K steps, at least one (it
+            // always runs the first, also for an empty item); rows past them are
+            // left as they are (items here are mostly short)
+            const int rows = len > 32 ? ((len + 31) >> 5) << 5 : 32;
+            __syncthreads();   // the previous chunk's MFMA reads of xs / bs are done
+#pragma unroll
+            for (int kx = 0; kx < Regs::kXV; ++kx) {
+                const int u = tid + 512 * kx;
+                if (u < Q * 8 && (u >> 3) < rows) st16(xs + (u >> 3) * LDX + 8 * (u & 7), R.x[kx]);
+            }
+#pragma unroll
+            for (int kb = 0; kb < Regs::kBV; ++kb) {
+                const int u = tid + 512 * kb;
+                if (u < Q * 8 && (u >> 3) < rows) {
+                    const int t = u >> 3;
+                    const float w = t < len ? __expf(R.cl - R.cm[kb]) * R.dt[kb] : 0.0f;
+                    const uint32_t w4[4] = {R.b[kb].x, R.b[kb].y, R.b[kb].z, R.b[kb].w};
+                    float f[8];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        f[2 * i] = __uint_as_float(w4[i] << 16) * w;
+                        f[2 * i + 1] = __uint_as_float(w4[i] & 0xffff0000u) * w;
+                    }
+                    Vec16<bf16>::store(bs + t * LDB + 8 * (u & 7), f);
+                }
+            }
+            const float decay = __expf(R.cl);
+            // the next chunk: this item's, or after its last the next item's first,
+            // together with that item's initial state (one code path, no branch
+            // around the loads)
+            const bool last = c + 1 >= cend;
+            const Item &tgt = last ? nxt : cur;
+            float ivn[2][4];
+            init_load(ivn, tgt);
+            fetch(R, tgt, last ? nxt.lo : c + 1);
+            // the metadata of the item after the next, requested after the tiles so
+            // that staging the next chunk does not wait for it
+            meta_load(mnext2, k + 2);
+            __syncthreads();
+
+            const int64_t off = ((int64_t)c * H + cur.h) * PN + cur.run;
+            if (live) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    float v[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+                    store4<bf16>(entering + off + 16 * j, v);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[j][e] *= decay;
+            const int nk = (len + 31) >> 5;
+            bf16x8 xf = mfma_frag_tr_split(xs, LDX, 0, 16 * pw, lane);
+            bf16x8 bf[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) bf[j] = mfma_frag_tr_split(bs, LDB, 0, 32 * nh + 16 * j, lane);
+            for (int ks = 1; ks < nk; ++ks) {
+                const bf16x8 xn = mfma_frag_tr_split(xs, LDX, 32 * ks, 16 * pw, lane);
+                bf16x8 bn[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    bn[j] = mfma_frag_tr_split(bs, LDB, 32 * ks, 32 * nh + 16 * j, lane);
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], xf, acc[j], 0, 0, 0);
+                xf = xn;
+                bf[0] = bn[0];
+                bf[1] = bn[1];
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], xf, acc[j], 0, 0, 0);
+            if constexpr (CKPT) {
+                if (live) {
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        float w[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+                        put4<TS>(ckpt + off + 16 * j, w, srk, (uint64_t)(off + 16 * j), kSrCkpt);
+                    }
+                }
+            }
+            if (last) {
+                // the item's final state, then the next item's initial state
+                if (cur.slot_ok) {
+                    const int64_t fo = ((int64_t)cur.slot * H + cur.h) * PN + cur.run;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        float v[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+                        put4<TS>(cache + fo + 16 * j, v, srk, (uint64_t)(fo + 16 * j), kSrFinal);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[j][e] = nxt.read_init ? ivn[j][e] : 0.0f;
+            }
+        }
+        if (!have_next) break;
+        cur = nxt;
+        mnext = mnext2;
+    }
+}
+
 // Carry step of segmented state passing. A segment's chunk chain is linear in
 // its starting state, so with h_b the true state entering segment b, fin_b the
 // segment's final state from a zero start (the first segment's from the cached
@@ -1540,11 +1816,15 @@ void chunk_scan_fast_kernel(
     // [exp(-span), exp(span)]): R = cum at the chunk's end (positions past it hold it)
     const float rs = scum[Q - 1];
     const bool single = !exact && scum[0] - rs <= kMaxSpan * kLog2e;
+    // only the rows the intra-chunk MFMAs read (whole 32-token K steps up to the
+    // chunk's last row); rows past them are left as they are
+    const int xrows = ((len + 31) >> 5) << 5;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int u = tid + nthr * k;
         const int t = u >> 3, c8 = u & 7;
         uint4 v = xr[k];
+        if (t >= xrows) continue;
         if (!exact) {
             const float rk = single ? rs : scum[(t | 31) < Q ? (t | 31) : Q - 1];
             const float gt = __builtin_amdgcn_exp2f(rk - scum[t]) *
@@ -1839,6 +2119,9 @@ void launch_state_passing(const PrefillDims &d, const float *states, const float
     }
 }
 
+constexpr int64_t kMultiMinItems = 1024;   // items from which the multi-item kernel runs
+constexpr int64_t kMultiBlocks = 512;      // its blocks: two per CU
+
 template <int Q, bool CKPT, bool SEG, typename TS>
 static void launch_state_scan_k(const PrefillDims &d, const void *x, const void *B,
                                 const int32_t *meta, const float *cum, const float *dtc,
@@ -1846,6 +2129,23 @@ static void launch_state_scan_k(const PrefillDims &d, const void *x, const void 
                                 void *entering, void *ckpt, const SegBufs &seg, hipStream_t st)
 {
     const size_t smem = (size_t)Q * (kScanLDX + kScanLDB) * sizeof(bf16);
+    if constexpr (!SEG) {
+        // batches of short sequences (on average at most half a chunk each) with
+        // many items: persistent blocks, two per CU, several items each
+        const int64_t items = (int64_t)d.S * d.H * (128 / kScanNSL);
+        if ((int64_t)d.T * 2 <= (int64_t)d.S * d.Q && items >= kMultiMinItems) {
+            static size_t raised_m = 0;
+            allow_lds(reinterpret_cast<const void *>(&state_scan_multi_kernel<Q, CKPT, TS>), smem,
+                      raised_m);
+            const unsigned nblk = (unsigned)(items < kMultiBlocks ? items : kMultiBlocks);
+            hipLaunchKernelGGL((state_scan_multi_kernel<Q, CKPT, TS>), dim3(nblk), dim3(512), smem,
+                               st, d.S, d.H, d.G, d.max_chunks, d.num_slots,
+                               static_cast<const bf16 *>(x), static_cast<const bf16 *>(B), meta,
+                               cum, dtc, static_cast<TS *>(cache), idx, has_init,
+                               static_cast<bf16 *>(entering), static_cast<TS *>(ckpt), d.sr);
+            return;
+        }
+    }
     static size_t raised = 0;
     allow_lds(reinterpret_cast<const void *>(&state_scan_fast_kernel<Q, CKPT, SEG, TS>), smem,
               raised);

@@ -151,6 +151,11 @@ E2E_CASES = [
     # pairs over the XCDs (one head per group)
     ((400, 77, 130), 16, 64, 128, 16, 64, BF16, F32, True),
     ((700, 260, 5, 90), 16, 64, 128, 16, 128, BF16, BF16, False),
+    # 64 mostly short sequences x 8 heads (1024 state items): the fused state pass
+    # with persistent blocks walking several items, item boundaries after one or
+    # two chunks and empty sequences
+    ((1, 0, 200, 5, 64, 17, 0, 129) * 8, 8, 64, 128, 2, 128, BF16, F32, True),
+    ((3, 40, 0, 9, 130, 1, 22, 31) * 8, 8, 64, 128, 2, 128, BF16, BF16, False),
 ]
 
 
