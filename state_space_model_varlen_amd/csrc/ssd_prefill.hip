@@ -1322,6 +1322,9 @@ void state_scan_multi_kernel(
     for (int k = 0; k < nmine; ++k) {
         const bool have_next = k + 1 < nmine;
         const Item nxt = make_item(mnext, k + 1);   // (the last item again when there is none)
+        // the metadata of the item after the next (requested before this item's
+        // tile loads, so it has arrived when those are waited for)
+        meta_load(mnext2, k + 2);
         // an empty sequence makes one pass over zero tiles with its stores off
         const int cend = cur.hi > cur.lo ? cur.hi : cur.lo + 1;
         for (int c = cur.lo; c < cend; ++c) {
@@ -1362,9 +1365,6 @@ void state_scan_multi_kernel(
             float ivn[2][4];
             init_load(ivn, tgt);
             fetch(R, tgt, last ? nxt.lo : c + 1);
-            // the metadata of the item after the next, requested after the tiles so
-            // that staging the next chunk does not wait for it
-            meta_load(mnext2, k + 2);
             __syncthreads();
 
             const int64_t off = ((int64_t)c * H + cur.h) * PN + cur.run;
