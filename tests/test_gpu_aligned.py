@@ -43,6 +43,9 @@ CASES = [
     ((600, 32, 1, 257), (4224, 0, 255, 1), 8, 64, 128, 2, 256, BF16, F32),
     ((33, 200, 500), (100, 128, 7), 8, 64, 128, 8, 128, BF16, BF16),
     ((70, 5), (-3, 2 ** 30), 4, 64, 16, 4, 32, F32, BF16),
+    # 64 mostly short sequences x 8 heads: the multi-item state pass in align mode
+    ((3, 70, 0, 9, 130, 1, 22, 31) * 8, (5, 100, 0, 127, 1, 64, 300, 2) * 8, 8, 64, 128, 2, 128,
+     BF16, BF16),
 ]
 
 
