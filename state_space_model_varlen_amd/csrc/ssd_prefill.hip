@@ -920,7 +920,7 @@ void state_scan_fast_kernel(
     const float *__restrict__ dtc, TS *cache, const int32_t *__restrict__ idx,
     const uint8_t *__restrict__ has_init, bf16 *__restrict__ entering, TS *__restrict__ ckpt,
     SrCtx sr, int nseg, float *__restrict__ seg_fin, float *__restrict__ seg_L,
-    float *__restrict__ seg_F, int32_t *__restrict__ seg_I)
+    float *__restrict__ seg_F, int32_t *__restrict__ seg_I, int lpt)
 {
     constexpr int P = 64, N = 128, NSL = kScanNSL, NS = N / NSL;
     constexpr int LDX = kScanLDX, LDB = kScanLDB;
@@ -934,12 +934,40 @@ void state_scan_fast_kernel(
     // long and short sequences gives every XCD the same chain lengths, and the
     // heads that share a B group sit side by side on one XCD
     const int nsg = SEG ? nseg : 1;
-    const int nblk = S * nsg * H * NS;
-    const int lb = xcd_logical_block(blockIdx.x, nblk);
-    const int q = lb % NS, sb = (lb / NS) % (S * nsg), h = lb / (NS * S * nsg);
-    const int s = sb / nsg, b = sb - s * nsg;
-    const int g = h / (H / G);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int q, h, s, b, sb;
+    if (!SEG && lpt) {
+        // Longest chain first (few sequences, heads a multiple of 8): XCD x owns
+        // heads [x H / 8, (x + 1) H / 8) of every sequence, and its blocks go out
+        // in order of the sequences' chunk counts, longest first, so that the
+        // long chains start in the first round on every XCD. Every wave ranks the
+        // sequences itself (count descending, then index): rank r -> sequence s.
+        const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+        const int hx = H / kXcds;
+        const int r = slot / (hx * NS), rem = slot - r * (hx * NS);
+        h = xcd * hx + rem / NS;
+        q = rem - (rem / NS) * NS;
+        const int sl = lane < S ? lane : S - 1;
+        const int cnt = meta[sl + 1] - meta[sl];
+        int rank = 0;
+        for (int t = 0; t < S; ++t) {
+            const int ct = __shfl(cnt, t);
+            rank += (ct > cnt || (ct == cnt && t < lane)) ? 1 : 0;
+        }
+        const unsigned long long hit = __ballot(lane < S && rank == r);
+        s = hit ? __builtin_ctzll(hit) : 0;
+        b = 0;
+        sb = s;
+    } else {
+        const int nblk = S * nsg * H * NS;
+        const int lb = xcd_logical_block(blockIdx.x, nblk);
+        q = lb % NS;
+        sb = (lb / NS) % (S * nsg);
+        h = lb / (NS * S * nsg);
+        s = sb / nsg;
+        b = sb - s * nsg;
+    }
+    const int g = h / (H / G);
     const int r16 = lane & 15, kg = lane >> 4;
     const int pw = wave & 3, nh = wave >> 2;
     const int n0 = q * NSL;
@@ -2151,11 +2179,13 @@ static void launch_state_scan_k(const PrefillDims &d, const void *x, const void 
               raised);
     const int nseg = SEG ? seg.nseg : 1;
     const unsigned nblk = (unsigned)((int64_t)d.S * nseg * d.H * (128 / kScanNSL));
+    // longest chain first: few sequences (one wave ranks them), heads a multiple of 8
+    const int lpt = !SEG && d.S > 1 && d.S <= 64 && d.H % kXcds == 0;
     hipLaunchKernelGGL((state_scan_fast_kernel<Q, CKPT, SEG, TS>), dim3(nblk), dim3(512), smem,
                        st, d.S, d.H, d.G, d.max_chunks, d.num_slots, static_cast<const bf16 *>(x),
                        static_cast<const bf16 *>(B), meta, cum, dtc, static_cast<TS *>(cache), idx,
                        has_init, static_cast<bf16 *>(entering), static_cast<TS *>(ckpt), d.sr,
-                       nseg, seg.fin, seg.L, seg.F, seg.I);
+                       nseg, seg.fin, seg.L, seg.F, seg.I, lpt);
     if constexpr (SEG) {
         const int PN = 64 * 128;
         const int ncar = d.S * d.H * (PN / 1024);
