@@ -1758,7 +1758,6 @@ void chunk_scan_fast_kernel(
     constexpr int kStepsB = Q / 32;                   // K steps of row tile B (at most)
     constexpr int kStepsA = Q / 64 > 0 ? Q / 64 : 1;  // K steps of row tile A (at most)
     constexpr int kHVec = P * N / 8 / nthr > 0 ? P * N / 8 / nthr : 1;
-    const int r16 = lane & 15, kg = lane >> 4;
     const int len = ci.len;
 
     const int ntiles = (len + 15) / 16;
