@@ -48,10 +48,19 @@
  *   device data gives wrong numbers, never an out-of-bounds access.
  *   Duplicate slot indices within one call are a caller error (the writes
  *   race).
- * - Precision: all recurrence arithmetic in float32. With bf16 inputs the
- *   dense intra-chunk contractions run on bf16 MFMA with float32 accumulation;
- *   results are rounded to their storage dtype (round to nearest even) only
- *   when stored.
+ * - Precision: all recurrence arithmetic in float32; results are rounded to
+ *   their storage dtype (round to nearest even) when stored. With bf16 inputs
+ *   the dense contractions run on bf16 MFMA with float32 accumulation, so their
+ *   operands are bf16: x, B, C as given, and rounded to bf16 first: CB, the
+ *   decay-scaled B (exp(cum_last - cum_t) dt_t B_t) and x (exp(R - cum_j) dt_j
+ *   x_j), and each chunk's entering state (stored in bf16 between the launches).
+ *   Two partial results are rounded to bf16 before the last step: y's SSM part
+ *   before D_h x is added (y is then rounded again when stored), and in a
+ *   segmented call the entering state local + exp(F) carry (each term bf16).
+ *   With A_h dt <= 0 (a decaying state, as in Mamba2) these roundings stay far
+ *   inside the tolerances the tests apply (2e-2 absolute + 1e-2 relative per
+ *   element); with A_h dt > 0 the state grows, and the rounding of the state
+ *   term scales with the state's size rather than with y's.
  * - Supported on the GPU: headdim P in {16, 64}, d_state N in {16, 128},
  *   chunk_size Q in {32, 64, 128, 256}, dtypes float32 and bfloat16. Other
  *   shapes return SSD_ERR_UNSUPPORTED.
@@ -130,9 +139,10 @@ typedef struct {
  *   prefix_lens   [S] int32 on the device: align mode (see
  *                 ssd_combined_varlen_aligned); prefill only
  *   sr_seed       stochastic rounding of fp16 state stores (vLLM PR #61501,
- *                 "Test plan": a float16 SSM cache with stochastic rounding
- *                 and a configurable number of Philox rounds; "Changes": one
- *                 seed per step read from a device buffer). Points to one
+ *                 "Serve and client commands": a float16 SSM cache with
+ *                 stochastic rounding and a configurable number of Philox
+ *                 rounds; "Details", its list of changes: one seed per step
+ *                 read from a device buffer). Points to one
  *                 uint64 on the device, read by the kernels, so a caller can
  *                 refresh it per step without host synchronisation. Requires
  *                 state_dtype SSD_F16. NULL: round to nearest even.
@@ -178,7 +188,9 @@ size_t ssd_workspace_bytes(const ssd_problem *p);  /* for ssd_combined_varlen */
  *                                   (mc = ssd_max_chunks)
  *                 [2S+2+3mc+s]      tokens in sequence s's first chunk, s < S
  *   dA_cumsum   out, float32 [H, max_chunks, Q]: inclusive cumsum of dt*A_h over
- *               the chunk's tokens; positions past the chunk's end hold its last value
+ *               the chunk's tokens; positions past the chunk's end hold the chunk's
+ *               total again (summed in another order: equal to the last position's
+ *               value within float32 rounding)
  *   dt_chunk    out, float32 [H, max_chunks, Q]: dt per chunk position, 0 past the end
  * Rows c >= nc of dA_cumsum / dt_chunk are left unwritten.
  */
@@ -348,7 +360,7 @@ int ssd_combined_varlen_dt(const ssd_problem *p, const ssd_dt_transform *dt_tran
 
 /*
  * Align-mode prefill (vLLM PR #55688, "Summary": prefix caching in the align
- * cache mode; checkpoints serve prefix reuse, vLLM PR #61501 "Changes"): sequence s
+ * cache mode; checkpoints serve prefix reuse, vLLM PR #61501 "Details"): sequence s
  * continues after prefix_lens[s] cached tokens, and chunk boundaries fall on
  * absolute token positions that are multiples of Q, so its first chunk holds
  * Q - (prefix_lens[s] mod Q) tokens (Q when that is 0) and every checkpoint

@@ -4,9 +4,10 @@ TEST INFRASTRUCTURE ONLY: imported by the test suite, never by the GPU library.
 
 The pages run the SSM cache in float16 with stochastic rounding driven by a
 Philox generator with a configurable number of rounds and one seed per step
-read from a device buffer (vLLM PR #61501, sections "Test plan" and
-"Changes": --mamba-ssm-cache-dtype float16, --enable-mamba-cache-stochastic-
-rounding, --mamba-cache-philox-rounds 5, and the per-step ReplaySSM seed).
+read from a device buffer (vLLM PR #61501, section "Serve and client
+commands": --mamba-ssm-cache-dtype float16, --enable-mamba-cache-stochastic-
+rounding, --mamba-cache-philox-rounds 5; section "Details", its list of
+changes: the per-step ReplaySSM seed).
 They define neither the rounding nor the stream layout; the readings here:
 
 * Stochastic rounding of x (float32) to fp16: with lo, hi the adjacent fp16

@@ -342,8 +342,12 @@ def max_chunks_aligned(p: ssd_problem) -> int:
     return int(_lib.ssd_max_chunks_aligned(ctypes.byref(p)))
 
 
+def workspace_bytes_aligned(p: ssd_problem) -> int:
+    return int(_lib.ssd_workspace_bytes_aligned(ctypes.byref(p)))
+
+
 def alloc_workspace_aligned(p: ssd_problem, device="cuda") -> torch.Tensor:
-    n = int(_lib.ssd_workspace_bytes_aligned(ctypes.byref(p)))
+    n = workspace_bytes_aligned(p)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 

@@ -4,6 +4,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
@@ -12,7 +13,7 @@ SOURCES = ["ssd_api.cpp", "ssd_prefill.hip", "ssd_decode.hip", "ssd_replay.hip"]
 HEADERS = ["ssd_device.h", "ssd_launch.h"]
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 instructions stay off (the compiler would otherwise form
     # v_pk_* from float2 code)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -25,18 +26,34 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into the shared library (always rebuilds)."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-I", os.path.join(PKG, "..", "include"), "-o", tmp] + srcs
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed building libssd_mi355x.so")
-    os.replace(tmp, LIB)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source (in parallel, one hipcc per file) and link the shared
+    library (always rebuilds)."""
+    tag = f".tmp{os.getpid()}"
+    inc = ["-I", os.path.join(PKG, "..", "include")]
+    objs = [os.path.join(CSRC, s + tag + ".o") for s in SOURCES]
+    jobs = [[hipcc()] + HIPCC_FLAGS + inc + ["-c", "-o", o, os.path.join(CSRC, s)]
+            for s, o in zip(SOURCES, objs)]
+    try:
+        with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1, 8)) as ex:
+            for f in [ex.submit(_run, j, verbose) for j in jobs]:
+                f.result()
+        tmp = LIB + tag
+        _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+        os.replace(tmp, LIB)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     return LIB
 
 

@@ -20,8 +20,9 @@ bool gpu_shape_ok(int P, int N) { return (P == 16 || P == 64) && (N == 16 || N =
 
 bool chunk_ok(int Q) { return Q == 32 || Q == 64 || Q == 128 || Q == 256; }
 
-// Shape / dtype checks of a prefill descriptor (no pointers).
-int check_problem(const ssd_problem *p)
+// Shape / dtype checks of a prefill descriptor (no pointers); `aligned`: the
+// chunk bound of align mode (T / Q + 2 S), which sizes the grids of that mode.
+int check_problem(const ssd_problem *p, bool aligned = false)
 {
     if (!p) return SSD_ERR_NULL;
     if (p->total_tokens < 0 || p->num_seqs < 0 || p->nheads <= 0 || p->headdim <= 0 ||
@@ -32,7 +33,8 @@ int check_problem(const ssd_problem *p)
     if (!dtype_ok(p->in_dtype) || !state_dtype_ok(p->state_dtype)) return SSD_ERR_DTYPE;
     if (!gpu_shape_ok(p->headdim, p->d_state) || !chunk_ok(p->chunk_size)) return SSD_ERR_UNSUPPORTED;
     // grid limits: chunks and heads index grid dimensions
-    const int64_t mc = (int64_t)p->total_tokens / p->chunk_size + p->num_seqs;
+    const int64_t mc = (int64_t)p->total_tokens / p->chunk_size +
+                       (aligned ? 2 : 1) * (int64_t)p->num_seqs;
     if (mc > 65535 || p->nheads > 65535) return SSD_ERR_UNSUPPORTED;
     if (mc * p->nheads * 2 > 0x7fffffffLL) return SSD_ERR_UNSUPPORTED;
     if ((int64_t)p->num_seqs * p->nheads * ((p->headdim * p->d_state + 1023) / 1024) > 0x7fffffffLL)
@@ -304,7 +306,7 @@ static int combined(const ssd_problem *p, const ssd::DtTf &tf, const void *x, co
                     const ssd::SrCtx &sr = ssd::SrCtx())
 {
     const bool aligned = prefix != nullptr;
-    int rc = check_problem(p);
+    int rc = check_problem(p, aligned);
     if (rc) return rc;
     if (!x || !dt || !A || !B || !C || !cu_seqlens || !state_cache || !state_indices || !y ||
         !workspace)
@@ -407,13 +409,13 @@ int ssd_combined_varlen_ex(const ssd_problem *p, const ssd_options *opt, const v
 
 int64_t ssd_max_chunks_aligned(const ssd_problem *p)
 {
-    if (check_problem(p) != SSD_OK) return 0;
+    if (check_problem(p, true) != SSD_OK) return 0;
     return max_chunks_of(p, true);
 }
 
 size_t ssd_workspace_bytes_aligned(const ssd_problem *p)
 {
-    if (check_problem(p) != SSD_OK) return 0;
+    if (check_problem(p, true) != SSD_OK) return 0;
     return workspace_layout(p, true).total;
 }
 

@@ -259,7 +259,7 @@ __global__ __launch_bounds__(256) void round_f16_kernel(const float *__restrict_
 {
     const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (e0 >= n) return;
-    const SrKey srk = sr_key(sr, in);
+    const SrKey srk = sr_key_checked(sr);   // (in may hold fewer than 8 bytes)
     if (e0 + 4 <= n && (reinterpret_cast<uintptr_t>(out + e0) & 7u) == 0) {
         const float v[4] = {in[e0], in[e0 + 1], in[e0 + 2], in[e0 + 3]};
         put4<f16>(out + e0, v, srk, (uint64_t)e0, (uint32_t)kind);

@@ -264,6 +264,19 @@ __device__ __forceinline__ SrKey sr_key(const SrCtx &c, const void *standin)
     k.rounds = c.seed ? c.rounds : 0;
     return k;
 }
+// The same without a stand-in (the seed is read only when there is one), for
+// kernels with no array known to hold 8 bytes.
+__device__ __forceinline__ SrKey sr_key_checked(const SrCtx &c)
+{
+    SrKey k;
+    if (c.seed) {
+        const uint64_t s = *c.seed;
+        k.k0 = (uint32_t)s;
+        k.k1 = (uint32_t)(s >> 32);
+        k.rounds = c.rounds;
+    }
+    return k;
+}
 
 // 4 consecutive state values to storage; e = flat index of the first one in the
 // destination array (a multiple of 4), kind = its stream. Only fp16 stores round

@@ -1621,7 +1621,8 @@ __device__ __forceinline__ void scan_row_tile(
                 // exp(cum_i - R) comes after the loop, so A is CB as stored
                 af = __builtin_bit_cast(bf16x8, cbf[ks]);
             } else if (!exact) {
-                // CB is zero above the diagonal (see bmm), and e is finite: no mask
+                // CB is zero above the diagonal (see bmm), and e is finite (at most
+                // exp(kMaxSpan): the cumsum does not increase in this mode): no mask
                 const float e = __builtin_amdgcn_exp2f(ci2 - scum[j0 + 31 < Q ? j0 + 31 : Q - 1]);
 #pragma unroll
                 for (int v = 0; v < 8; ++v) af[v] = static_cast<bf16>(cbv[v] * e);
@@ -1830,17 +1831,23 @@ void chunk_scan_fast_kernel(
         }
     }
     __syncthreads();
-    // scaling factors of x: G_j = exp(R_k - cum_j) dt_j; exact mode when a span is too large
+    // scaling factors of x: G_j = exp(R_k - cum_j) dt_j. The factored modes need a
+    // cumsum that never increases (A_h dt_j <= 0, the decaying case) and block
+    // spans of at most kMaxSpan: a factor exp(cum_i - R_k) with i past block k is
+    // then at most 1, and at most exp(kMaxSpan) inside it. A chunk with a larger
+    // span, or with any step where A_h dt_j > 0, takes the exact mode.
     bool big = false;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int t = (tid + nthr * k) >> 3;
         const float rk = scum[(t | 31) < Q ? (t | 31) : Q - 1];
-        big |= fabsf(rk - scum[t]) > kMaxSpan * kLog2e;
+        const float prev = t > 0 ? scum[t - 1] : 0.0f;
+        big |= fabsf(rk - scum[t]) > kMaxSpan * kLog2e || scum[t] > prev;
     }
     const bool exact = __syncthreads_or(big) != 0;
-    // whole-chunk reference when the chunk's decay span fits (every factor in
-    // [exp(-span), exp(span)]): R = cum at the chunk's end (positions past it hold it)
+    // whole-chunk reference when the chunk's decay span fits (the cumsum does not
+    // increase here, so every factor is in [exp(-span), exp(span)]): R = cum at the
+    // chunk's end (positions past it hold it)
     const float rs = scum[Q - 1];
     const bool single = !exact && scum[0] - rs <= kMaxSpan * kLog2e;
     // only the rows the intra-chunk MFMAs read (whole 32-token K steps up to the

@@ -1,6 +1,7 @@
 """Shared pieces of the GPU parity tests: run the HIP path on seeded inputs,
-compute the oracle's answer (optionally on a sample of heads / sequences), and
-compare with the stated tolerances.
+compute the oracle's answer (the full-size workloads' cached states from the
+oracle over each sequence's seeded prefix), and compare with the stated
+tolerances.
 
 Tolerances (element-wise |gpu - oracle| <= atol + rtol * |oracle|):
   float32 inputs and state: atol 1e-4, rtol 0
@@ -60,6 +61,18 @@ def assert_close(got, want, in_dtype, what, normalised=True):
     return float(err.max()) if err.size else 0.0
 
 
+def assert_normalised(got, want, in_dtype, what):
+    """Only the normalised bound ||gpu - oracle||_2 / ||oracle||_2 (and finite values):
+    for results whose elements come from heavy cancellation between much larger
+    terms, where an element-wise bound relative to the element is meaningless."""
+    g, w = to64(got), to64(want)
+    assert g.shape == w.shape, (what, g.shape, w.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite values"
+    rel = float(np.linalg.norm(g - w)) / max(float(np.linalg.norm(w)), 1e-300)
+    assert rel <= norm_tol(in_dtype), f"{what}: normalised error {rel:.3e}"
+    return rel
+
+
 def select_heads(x, dt, A, B, C, D, heads, ngroups):
     """Restrict a problem to a subset of heads; B and C are expanded per head
     (one group per kept head) so the oracle's group map stays right."""
@@ -85,6 +98,55 @@ def prefix_final_states(inp, seqs, heads, nthreads=0):
                                       nthreads=nthreads)
         out[k] = fin[0]
     return out
+
+
+_PREFIX_STATES = {}
+
+
+def workload_prefix_states(inp, members, pack=4):
+    """The oracle's state after each member's seeded prefix, every head, rounded
+    to the cache dtype: a torch tensor [len(members), H, P, N]. ``members`` are
+    sequences (prefill) or requests (decode) that start from a cached state.
+    Prefixes are run ``pack`` at a time as one packed batch (OpenMP spreads the
+    (sequence, head) pairs over the host threads). Kept for the session: the
+    full-size tests of one workload share them."""
+    cfg = inp.cfg
+    key = (cfg, tuple(int(m) for m in members))
+    if key not in _PREFIX_STATES:
+        H, P, N = cfg.nheads, cfg.headdim, cfg.d_state
+        out = torch.empty(len(members), H, P, N, dtype=cfg.state_dtype)
+        L = cfg.prefix_len
+        for k0 in range(0, len(members), pack):
+            grp = list(members[k0:k0 + pack])
+            toks = [inp.prefix_tokens(int(m)) for m in grp]
+            x, dt, B, C = (torch.cat([t[i] for t in toks]) for i in range(4))
+            cu = np.arange(len(grp) + 1, dtype=np.int32) * L
+            _, fin, _ = oracle.recurrence(x, dt, inp.A, B, C, None, cu, 256)
+            out[k0:k0 + len(grp)] = oracle.round_to(fin, cfg.state_dtype)
+        _PREFIX_STATES[key] = out
+    return _PREFIX_STATES[key]
+
+
+def workload_cache(inp, members=None):
+    """The workload's state cache: every slot NaN, except the slots of the
+    sequences (prefill: those with has_initial) or requests (decode: all) that
+    start from a cached state, which hold the oracle's state after their seeded
+    prefix, rounded to the cache dtype (the oracle continues from that rounded
+    value)."""
+    cfg = inp.cfg
+    if members is None:
+        if hasattr(inp, "has_initial"):
+            members = [] if inp.has_initial is None else \
+                [s for s in range(len(inp.state_indices)) if int(inp.has_initial[s])]
+        else:
+            members = list(range(len(inp.state_indices)))
+    cache = torch.full((cfg.num_slots, cfg.nheads, cfg.headdim, cfg.d_state), float("nan"),
+                       dtype=cfg.state_dtype)
+    if members:
+        states = workload_prefix_states(inp, members)
+        for k, m in enumerate(members):
+            cache[int(inp.state_indices[m])] = states[k]
+    return cache
 
 
 def gpu_prefill(inp, cache, chunk_size, checkpoints=False, D=True, has_initial="cfg"):

@@ -91,6 +91,19 @@ def test_invalid_problems_rejected(kw, status):
     assert rc == status
 
 
+def test_align_mode_chunk_bound_checked_before_launch():
+    """Align mode bounds the chunks by T / Q + 2 S, which sizes its grids: a batch
+    within the plain bound (T / Q + S <= 65535) but past the align-mode one is
+    rejected before anything is enqueued."""
+    p = P(total_tokens=64 * 40000, num_seqs=20000, num_slots=20000)
+    assert ssd.max_chunks(p) == 40000 + 20000
+    assert ssd.max_chunks_aligned(p) == 0 and ssd.workspace_bytes_aligned(p) == 0
+    fake = ctypes.c_void_p(256)
+    rc = ssd._lib.ssd_combined_varlen_aligned(ctypes.byref(p), *([fake] * 14),
+                                              ctypes.c_size_t(1 << 40), None)
+    assert rc == 4
+
+
 def test_bad_dtype_code():
     p = P()
     p.in_dtype = 7

@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import ssd_synth as sy
-from gpu_helpers import DEV, assert_close, looser, select_heads
+from gpu_helpers import DEV, assert_close, looser, select_heads, workload_cache
 
 pytestmark = pytest.mark.gpu
 
@@ -74,31 +74,32 @@ def test_aligned_prefill_matches_oracle(case):
     assert torch.isnan(ck[nc:].float()).all()        # rows past the chunks stay unwritten
 
 
-def test_c3_mixed_varlen_aligned_sampled_heads():
+def test_c3_mixed_varlen_aligned_full():
     """The 8-sequence mixed batch with checkpoints in align mode: odd sequences
-    continue after 4224 cached tokens (first chunk 128 tokens), even ones start
-    fresh; the oracle checks four heads of every sequence."""
+    continue after 4224 cached tokens (first chunk 128 tokens) from the oracle's
+    state after their own seeded prefix, even ones start fresh. The oracle checks
+    every (sequence, head), one B/C group (8 heads) at a time to bound the host
+    memory of its per-token states."""
     cfg = sy.C3
     inp = sy.make_prefill(cfg)
-    H, P, N, G, Q = cfg.nheads, cfg.headdim, cfg.d_state, cfg.ngroups, cfg.chunk_size
-    cache = sy.nan_cache(cfg.num_slots, H, P, N, cfg.state_dtype)
-    g = torch.Generator().manual_seed(19)
-    for s in range(cfg.num_seqs):
-        if int(inp.has_initial[s]):
-            cache[int(inp.state_indices[s])] = (torch.randn(H, P, N, generator=g) * 0.03
-                                                ).to(cfg.state_dtype)
+    H, G, Q = cfg.nheads, cfg.ngroups, cfg.chunk_size
+    cache = workload_cache(inp)
     prefix = [cfg.prefix_len if int(inp.has_initial[s]) else 0 for s in range(cfg.num_seqs)]
     y, after, ck = _gpu_aligned(inp, cache, Q, prefix)
-    heads = [0, 9, 36, 63]
-    x, dt, A, B, C, D = select_heads(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, heads, G)
-    sub = cache[:, heads]
-    ref = oracle.prefill_aligned(x, dt, A, B, C, D, inp.cu_seqlens, inp.state_indices,
-                                 inp.has_initial, sub, Q, prefix)
-    assert_close(y[:, heads], ref["y"], BF16, "c3 aligned y", normalised=False)
     used = inp.state_indices.long()
-    assert_close(after[used][:, heads], ref["final"], BF16, "c3 aligned final states")
-    nc = len(ref["ckpt"])
-    # chunks: 1, 7 for the fresh 32- and 1600-token sequences; after 4224 cached tokens
-    # the 600-token ones cut as 128 + 256 + 216 and the 128-token ones as one chunk
-    assert nc == 24
-    assert_close(ck[:nc][:, heads], ref["ckpt"], BF16, "c3 aligned checkpoints")
+    hpg = H // G
+    for g in range(G):
+        heads = list(range(g * hpg, (g + 1) * hpg))
+        x, dt, A, B, C, D = select_heads(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, heads, G)
+        ref = oracle.prefill_aligned(x, dt, A, B, C, D, inp.cu_seqlens, inp.state_indices,
+                                     inp.has_initial, cache[:, heads], Q, prefix)
+        assert_close(y[:, heads], ref["y"], BF16, f"c3 aligned y, group {g}", normalised=False)
+        assert_close(after[used][:, heads], ref["final"], BF16,
+                     f"c3 aligned final states, group {g}")
+        nc = len(ref["ckpt"])
+        # chunks: 1, 7 for the fresh 32- and 1600-token sequences; after 4224 cached
+        # tokens the 600-token ones cut as 128 + 256 + 216 and the 128-token ones as
+        # one chunk
+        assert nc == 24
+        assert_close(ck[:nc][:, heads], ref["ckpt"], BF16, f"c3 aligned checkpoints, group {g}")
+    assert torch.isnan(ck[24:].float()).all()

@@ -6,9 +6,8 @@ import numpy as np
 import pytest
 import torch
 
-import oracle
 import ssd_synth as sy
-from gpu_helpers import DEV, assert_close, looser
+from gpu_helpers import DEV, assert_close, looser, workload_cache
 from oracle import replay as oracle_replay
 
 pytestmark = pytest.mark.gpu
@@ -144,21 +143,11 @@ def test_replay_agrees_with_stored_states_path():
     assert_close(c_replay, c_plain, F32, "states of the two paths")
 
 
-def test_c4_replay_full_sampled():
+def test_c4_replay_full():
     """The MTP verify workload (128 requests x 3 tokens, 128 heads, bf16 cache of 512
-    slots) through ReplaySSM with a 16-entry ring, 6 steps; the oracle follows four
-    sampled requests (all their heads), starting from states of seeded prefixes."""
+    slots) through ReplaySSM with a 16-entry ring, 6 steps; every request starts from
+    the oracle's state after its own seeded prefix, and the oracle follows every
+    request (all heads): y, rings, cursors and checkpoints after each step."""
     cfg = sy.C4
-    H, P, N = cfg.nheads, cfg.headdim, cfg.d_state
-    d0 = sy.make_decode(cfg)
-    cache = sy.nan_cache(cfg.num_slots, H, P, N, cfg.state_dtype)
-    g = torch.Generator().manual_seed(4)
-    for r in range(cfg.num_reqs):
-        cache[int(d0.state_indices[r])] = (torch.randn(H, P, N, generator=g) * 0.03
-                                           ).to(cfg.state_dtype)
-    sample = [0, 37, 90, 127]
-    for r in sample:
-        px, pdt, pB, pC = d0.prefix_tokens(r)
-        _, fin, _ = oracle.recurrence(px, pdt, d0.A, pB, pC, None, [0, cfg.prefix_len], 256)
-        cache[int(d0.state_indices[r])] = oracle.round_to(fin[0], cfg.state_dtype)
-    _run_steps(cfg, 16, cache, steps=6, sample=sample)
+    cache = workload_cache(sy.make_decode(cfg))
+    _run_steps(cfg, 16, cache, steps=6)

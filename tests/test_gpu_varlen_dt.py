@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import ssd_synth as sy
-from gpu_helpers import DEV, assert_close, looser, select_heads, to64
+from gpu_helpers import DEV, assert_close, looser
 
 pytestmark = pytest.mark.gpu
 
@@ -162,9 +162,9 @@ def test_prefill_with_fused_dt(case):
         assert_close(ckpt.cpu()[:nc], ref["ckpt"], looser(ti, ts), "checkpoints")
 
 
-def test_c1_layer_prefill_fused_dt_sampled_heads():
+def test_c1_layer_prefill_fused_dt_full():
     """The 4096-token, 80-head layer with the step-size preprocessing fused in; the
-    oracle checks four heads."""
+    oracle checks every head (y, the final state, and y's SSM part with D = 0)."""
     ssd = _ssd()
     cfg = sy.C1
     inp = sy.make_prefill(cfg)
@@ -172,16 +172,18 @@ def test_c1_layer_prefill_fused_dt_sampled_heads():
     bias = torch.from_numpy(inp.dt_bias).float()
     p = ssd.make_problem(T, 1, H, P, N, G, Q, 1, cfg.in_dtype, cfg.state_dtype)
     tf = ssd.make_dt_transform(bias.to(DEV), sy.DT_MIN, sy.DT_MAX)
-    cache = torch.zeros(1, H, P, N, device=DEV)
-    y = torch.empty(T, H, P, dtype=BF16, device=DEV)
-    ssd.ssd_combined_varlen_dt(p, tf, inp.x.to(DEV), inp.dt_raw.to(DEV), inp.A.to(DEV),
-                               inp.B.to(DEV), inp.C.to(DEV), inp.D.to(DEV), inp.cu_seqlens.to(DEV),
-                               cache, inp.state_indices.to(DEV), None, y, None,
-                               ssd.alloc_workspace(p, DEV))
-    torch.cuda.synchronize()
-    heads = [0, 27, 54, 79]
     dt_ref = torch.from_numpy(oracle.dt_preprocess(inp.dt_raw, bias, sy.DT_MIN, sy.DT_MAX))
-    x, dt, A, B, C, D = select_heads(inp.x, dt_ref, inp.A, inp.B, inp.C, inp.D, heads, G)
-    ry, rf, _ = oracle.recurrence(x, dt, A, B, C, D, [0, T], Q)
-    assert_close(y.cpu()[:, heads], ry, BF16, "c1 y (fused dt)", normalised=False)
-    assert_close(cache.cpu()[0, heads], rf[0], BF16, "c1 final state (fused dt)")
+    for with_d in (True, False):
+        cache = torch.zeros(1, H, P, N, device=DEV)
+        y = torch.empty(T, H, P, dtype=BF16, device=DEV)
+        ssd.ssd_combined_varlen_dt(p, tf, inp.x.to(DEV), inp.dt_raw.to(DEV), inp.A.to(DEV),
+                                   inp.B.to(DEV), inp.C.to(DEV),
+                                   inp.D.to(DEV) if with_d else None, inp.cu_seqlens.to(DEV),
+                                   cache, inp.state_indices.to(DEV), None, y, None,
+                                   ssd.alloc_workspace(p, DEV))
+        torch.cuda.synchronize()
+        ry, rf, _ = oracle.recurrence(inp.x, dt_ref, inp.A, inp.B, inp.C,
+                                      inp.D if with_d else None, [0, T], Q)
+        tag = "" if with_d else " (D = 0)"
+        assert_close(y.cpu(), ry, BF16, "c1 y (fused dt)" + tag, normalised=not with_d)
+        assert_close(cache.cpu()[0], rf[0], BF16, "c1 final state (fused dt)" + tag)
