@@ -85,7 +85,9 @@ enum ssd_status {
     SSD_ERR_UNSUPPORTED = 4, /* valid but not built for the GPU (P, N, Q outside the sets above) */
     SSD_ERR_WORKSPACE = 5,   /* workspace smaller than ssd_workspace_bytes() */
     SSD_ERR_HIP = 6,         /* a kernel launch failed */
-    SSD_ERR_ALIGN = 7        /* an array pointer is not 16-byte aligned */
+    SSD_ERR_ALIGN = 7,       /* an array pointer is not 16-byte aligned */
+    SSD_ERR_SCRATCH = 8      /* the problem needs more workspace than the static scratch
+                                array of ssd_combined_varlen_noalloc holds */
 };
 
 /* SSD_F16 is a state dtype only (state caches, checkpoints, per-token and
@@ -517,6 +519,29 @@ int ssd_replay_materialize(const ssu_problem *p, int32_t ring_len, void *ckpt,
                            const void *ring_x, const void *ring_dt, const void *ring_B,
                            int32_t *cursor, const int32_t *state_indices, const float *A,
                            void *stream);
+
+/*
+ * ssd_combined_varlen that allocates nothing and takes no workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Arguments, semantics
+ * and results are those of ssd_combined_varlen (the same launches, bit for
+ * bit); the workspace is a static device array of the library,
+ * SSD_NOALLOC_SCRATCH_BYTES (128 MiB) per GPU, held on every GPU the library
+ * runs on until the process ends. Its device address is looked up on the
+ * first call on each device (that device current: the device of `stream`).
+ * A problem whose ssd_workspace_bytes exceeds it returns SSD_ERR_SCRATCH and
+ * enqueues nothing. All calls on one GPU share that GPU's array: calls that
+ * overlap on one GPU (other streams, other threads) race on it; calls queued
+ * on one stream are safe. The call allocates nothing (no hipMalloc, no
+ * library allocation) and needs no clearing of the array.
+ */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+size_t ssd_noalloc_scratch_bytes(void);   /* SSD_NOALLOC_SCRATCH_BYTES */
+int ssd_combined_varlen_noalloc(const ssd_problem *p, const void *x, const void *dt,
+                                const float *A, const void *B, const void *C, const float *D,
+                                const int32_t *cu_seqlens, void *state_cache,
+                                const int32_t *state_indices, const uint8_t *has_initial_state,
+                                void *y, void *checkpoints, void *stream);
 
 #ifdef __cplusplus
 }

@@ -99,6 +99,8 @@ _SIGS = {
     "ssd_replay_update": ([_up, ctypes.c_int32] + [_vp] * 14, ctypes.c_int),
     "ssd_replay_advance": ([_up, ctypes.c_int32] + [_vp] * 4, ctypes.c_int),
     "ssd_replay_materialize": ([_up, ctypes.c_int32] + [_vp] * 8, ctypes.c_int),
+    "ssd_noalloc_scratch_bytes": ([], ctypes.c_size_t),
+    "ssd_combined_varlen_noalloc": ([_pp] + [_vp] * 13, ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -302,6 +304,31 @@ def ssd_combined_varlen(p: ssd_problem, x, dt, A, B, C, D, cu_seqlens, state_cac
         _ptr(workspace, "workspace", torch.uint8), ctypes.c_size_t(workspace.numel()),
         _stream(stream))
     _check("ssd_combined_varlen", rc)
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the static scratch array of ssd_combined_varlen_noalloc."""
+    return int(_lib.ssd_noalloc_scratch_bytes())
+
+
+def ssd_combined_varlen_noalloc(p: ssd_problem, x, dt, A, B, C, D, cu_seqlens, state_cache,
+                                state_indices, has_initial_state, y, checkpoints, stream=None):
+    """ssd_combined_varlen with the library's static scratch array as its workspace
+    (no allocation; problems needing more than noalloc_scratch_bytes() are rejected)."""
+    T, S, H, P, N, G, Q, mc = _dims(p)
+    ti, ts = _TORCH[p.in_dtype], _TORCH[p.state_dtype]
+    rc = _lib.ssd_combined_varlen_noalloc(
+        ctypes.byref(p), _ptr(x, "x", ti, (T, H, P)), _ptr(dt, "dt", ti, (T, H)),
+        _ptr(A, "A", torch.float32, (H,)), _ptr(B, "B", ti, (T, G, N)),
+        _ptr(C, "C", ti, (T, G, N)), _ptr(D, "D", torch.float32, (H,), optional=True),
+        _ptr(cu_seqlens, "cu_seqlens", torch.int32, (S + 1,)),
+        _ptr(state_cache, "state_cache", ts, (p.num_slots, H, P, N)),
+        _ptr(state_indices, "state_indices", torch.int32, (S,)),
+        _ptr(has_initial_state, "has_initial_state", torch.uint8, (S,), optional=True),
+        _ptr(y, "y", ti, (T, H, P)),
+        _ptr(checkpoints, "checkpoints", ts, (mc, H, P, N), optional=True),
+        _stream(stream))
+    _check("ssd_combined_varlen_noalloc", rc)
 
 
 # ---------------------------------------------------------------------------

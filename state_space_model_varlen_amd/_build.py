@@ -9,7 +9,8 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libssd_mi355x.so")
-SOURCES = ["ssd_api.cpp", "ssd_prefill.hip", "ssd_decode.hip", "ssd_replay.hip"]
+SOURCES = ["ssd_api.cpp", "ssd_prefill.hip", "ssd_decode.hip", "ssd_replay.hip",
+           "ssd_noalloc.hip"]
 HEADERS = ["ssd_device.h", "ssd_launch.h"]
 
 HIPCC_FLAGS = [

@@ -169,6 +169,7 @@ const char *ssd_status_string(int status)
     case SSD_ERR_WORKSPACE: return "workspace too small";
     case SSD_ERR_HIP: return "HIP launch failure";
     case SSD_ERR_ALIGN: return "array pointer not 16-byte aligned";
+    case SSD_ERR_SCRATCH: return "problem needs more workspace than the no-alloc scratch array holds";
     default: return "unknown status";
     }
 }

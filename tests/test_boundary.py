@@ -31,8 +31,8 @@ def test_header_functions_are_exported():
 
 def test_version_and_status_strings():
     assert ssd.abi_version() == 1
-    for s in range(8):
-        assert ssd.status_string(s)
+    for s in range(9):
+        assert ssd.status_string(s) != "unknown status"
     assert ssd.status_string(99) == "unknown status"
 
 
@@ -102,6 +102,19 @@ def test_align_mode_chunk_bound_checked_before_launch():
     rc = ssd._lib.ssd_combined_varlen_aligned(ctypes.byref(p), *([fake] * 14),
                                               ctypes.c_size_t(1 << 40), None)
     assert rc == 4
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch_on_the_host():
+    """The no-alloc entry point checks the problem's workspace against its static
+    array before looking anything up on a device or enqueueing."""
+    p = P(total_tokens=16384, num_seqs=64, nheads=64, headdim=64, d_state=128, ngroups=8,
+          chunk_size=256, num_slots=64, in_dtype=torch.bfloat16, state_dtype=torch.bfloat16)
+    assert ssd.workspace_bytes(p) > ssd.noalloc_scratch_bytes() == 128 << 20
+    fake = ctypes.c_void_p(256)
+    assert ssd._lib.ssd_combined_varlen_noalloc(ctypes.byref(p), *([fake] * 12), None) == 8
+    # an invalid problem gets the status of ssd_combined_varlen
+    assert ssd._lib.ssd_combined_varlen_noalloc(ctypes.byref(P(nheads=0)), *([fake] * 12),
+                                                None) == 2
 
 
 def test_bad_dtype_code():
