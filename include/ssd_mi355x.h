@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 1
+#define SSD_ABI_VERSION 2
 
 enum ssd_status {
     SSD_OK = 0,
@@ -149,6 +149,7 @@ typedef struct {
  *                 refresh it per step without host synchronisation. Requires
  *                 state_dtype SSD_F16. NULL: round to nearest even.
  *   sr_rounds     Philox4x32 rounds, 1..16 (e.g. 5 or 10)
+ *   trace         per-launch timing events (ssd_launch_trace below)
  * Rounding: x becomes the fp16 value above or below it in magnitude, the
  * farther one with probability (|x| - |lo|) / (|hi| - |lo|), drawn as
  * (w >> 8) / 2^24 from a 32-bit word w (non-finite values and |x| > 65504
@@ -157,11 +158,28 @@ typedef struct {
  * seed); kinds: 0 final states, 1 checkpoints, 2 per-token states,
  * 3 ReplaySSM checkpoints. e is the flat element index in that array.
  */
+/*
+ * Per-launch timing of a prefill call (ssd_options.trace; profiling only): the
+ * call's k-th kernel launch records its own start on events[2k] and its end on
+ * events[2k + 1] (hipExtLaunchKernelGGL: the kernel's execution, as a kernel
+ * trace times it), so hipEventElapsedTime(events[2k], events[2k + 1]) is its
+ * duration. The events are hipEvent_t handles the caller created with timing
+ * enabled; launches whose pair lies at or past `capacity` events run without.
+ */
+#define SSD_TRACE_MAX_LAUNCHES 16
+typedef struct ssd_launch_trace {
+    void *const *events;    /* [capacity] hipEvent_t (2 per launch), or NULL (names only) */
+    int32_t capacity;
+    int32_t count;          /* out: kernel launches of the call */
+    const char *names[SSD_TRACE_MAX_LAUNCHES];   /* out: static name of launch k */
+} ssd_launch_trace;
+
 typedef struct {
     const ssd_dt_transform *dt_transform;
     const int32_t *prefix_lens;
     const uint64_t *sr_seed;
     int32_t sr_rounds;
+    ssd_launch_trace *trace;   /* host struct, or NULL; ssd_combined_varlen_ex only */
 } ssd_options;
 
 /* SSD_ABI_VERSION of the built library. */

@@ -55,9 +55,18 @@ class ssd_dt_transform(ctypes.Structure):
                 ("dt_max", ctypes.c_float)]
 
 
+TRACE_MAX_LAUNCHES = 16
+
+
+class ssd_launch_trace(ctypes.Structure):
+    _fields_ = [("events", ctypes.POINTER(ctypes.c_void_p)), ("capacity", ctypes.c_int32),
+                ("count", ctypes.c_int32), ("names", ctypes.c_char_p * TRACE_MAX_LAUNCHES)]
+
+
 class ssd_options(ctypes.Structure):
     _fields_ = [("dt_transform", ctypes.c_void_p), ("prefix_lens", ctypes.c_void_p),
-                ("sr_seed", ctypes.c_void_p), ("sr_rounds", ctypes.c_int32)]
+                ("sr_seed", ctypes.c_void_p), ("sr_rounds", ctypes.c_int32),
+                ("trace", ctypes.POINTER(ssd_launch_trace))]
 
 
 _vp = ctypes.c_void_p
@@ -490,16 +499,64 @@ def ssd_state_commit_varlen(p: ssu_problem, cu_seqlens, state_cache, state_indic
 # ---------------------------------------------------------------------------
 # options: dt preprocessing, align mode, stochastic rounding of fp16 states
 
-def make_options(dt_transform=None, prefix_lens=None, sr_seed=None, sr_rounds: int = 10):
+def make_options(dt_transform=None, prefix_lens=None, sr_seed=None, sr_rounds: int = 10,
+                 trace=None):
     """ssd_options; sr_seed: a 1-element int64 GPU tensor (read by the kernels, so it can
-    be refreshed per step). The struct keeps references to the tensors it points at."""
+    be refreshed per step); trace: a LaunchTrace. The struct keeps references to the
+    objects it points at."""
     o = ssd_options()
     o.dt_transform = None if dt_transform is None else ctypes.addressof(dt_transform)
     o.prefix_lens = None if prefix_lens is None else _ptr(prefix_lens, "prefix_lens", torch.int32)
     o.sr_seed = None if sr_seed is None else _ptr(sr_seed, "sr_seed", torch.int64, (1,))
     o.sr_rounds = int(sr_rounds) if sr_seed is not None else 0
-    o._refs = (dt_transform, prefix_lens, sr_seed)
+    o.trace = None if trace is None else ctypes.pointer(trace.struct)
+    o._refs = (dt_transform, prefix_lens, sr_seed, trace)
     return o
+
+
+class LaunchTrace:
+    """Per-launch timing of a prefill call (ssd_launch_trace): two HIP events per
+    kernel launch, on which the launch records its own start and end. The events
+    are created without the system-scope fence that HIP events carry by default
+    (hipEventDisableSystemFence), so recording them does not write back the caches
+    between the launches and the intervals are the kernels' own. After the call
+    and a synchronisation, ``durations_us()`` gives (name, us) per launch."""
+
+    _DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence
+
+    def __init__(self, capacity: int = 2 * TRACE_MAX_LAUNCHES):
+        # the HIP runtime torch and this library already share (by its soname)
+        self._hip = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD | os.RTLD_GLOBAL)
+        self._handles = (ctypes.c_void_p * capacity)()
+        for k in range(capacity):
+            rc = self._hip.hipEventCreateWithFlags(ctypes.byref(self._handles, k * 8),
+                                                   ctypes.c_uint(self._DISABLE_SYSTEM_FENCE))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.struct = ssd_launch_trace()
+        self.struct.events = ctypes.cast(self._handles, ctypes.POINTER(ctypes.c_void_p))
+        self.struct.capacity = capacity
+        self.struct.count = 0
+
+    def _elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self._hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self._handles[a]),
+                                           ctypes.c_void_p(self._handles[b]))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def durations_us(self):
+        n = min(int(self.struct.count), len(self._handles) // 2, TRACE_MAX_LAUNCHES)
+        return [(self.struct.names[k].decode(), self._elapsed_ms(2 * k, 2 * k + 1) * 1e3)
+                for k in range(n)]
+
+    def __del__(self):
+        hip = getattr(self, "_hip", None)
+        if hip is not None:
+            for h in self._handles:
+                if h:
+                    hip.hipEventDestroy(ctypes.c_void_p(h))
 
 
 def ssd_combined_varlen_ex(p: ssd_problem, options: ssd_options, x, dt, A, B, C, D, cu_seqlens,

@@ -154,6 +154,21 @@ Workspace workspace_layout(const ssd_problem *p, bool aligned = false)
 
 }  // namespace
 
+namespace ssd {
+
+bool trace_events(ssd_launch_trace *t, const char *name, void **start, void **stop)
+{
+    if (!t) return false;
+    const int k = t->count++;
+    if (k < SSD_TRACE_MAX_LAUNCHES) t->names[k] = name;
+    if (!t->events || 2 * (int64_t)k + 1 >= t->capacity) return false;
+    *start = t->events[2 * k];
+    *stop = t->events[2 * k + 1];
+    return true;
+}
+
+}  // namespace ssd
+
 extern "C" {
 
 int ssd_abi_version(void) { return SSD_ABI_VERSION; }
@@ -304,7 +319,7 @@ static int combined(const ssd_problem *p, const ssd::DtTf &tf, const void *x, co
                     const int32_t *cu_seqlens, void *state_cache, const int32_t *state_indices,
                     const uint8_t *has_initial_state, void *y, void *checkpoints, void *workspace,
                     size_t workspace_bytes, void *stream, const int32_t *prefix = nullptr,
-                    const ssd::SrCtx &sr = ssd::SrCtx())
+                    const ssd::SrCtx &sr = ssd::SrCtx(), ssd_launch_trace *trace = nullptr)
 {
     const bool aligned = prefix != nullptr;
     int rc = check_problem(p, aligned);
@@ -322,6 +337,8 @@ static int combined(const ssd_problem *p, const ssd::DtTf &tf, const void *x, co
     ssd::PrefillDims d = dims_of(p, aligned);
     d.prefix = prefix;
     d.sr = sr;
+    d.trace = trace;
+    if (trace) trace->count = 0;
     char *base = static_cast<char *>(workspace);
     int32_t *meta = reinterpret_cast<int32_t *>(base + w.meta);
     float *cum = reinterpret_cast<float *>(base + w.cum);
@@ -405,7 +422,7 @@ int ssd_combined_varlen_ex(const ssd_problem *p, const ssd_options *opt, const v
     if (rc) return rc;
     return combined(p, tf, x, dt, A, B, C, D, cu_seqlens, state_cache, state_indices,
                     has_initial_state, y, checkpoints, workspace, workspace_bytes, stream,
-                    opt ? opt->prefix_lens : nullptr, sr);
+                    opt ? opt->prefix_lens : nullptr, sr, opt ? opt->trace : nullptr);
 }
 
 int64_t ssd_max_chunks_aligned(const ssd_problem *p)

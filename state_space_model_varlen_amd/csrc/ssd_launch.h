@@ -6,7 +6,14 @@
 #include <stddef.h>
 #include <stdint.h>
 
+struct ssd_launch_trace;   // include/ssd_mi355x.h
+
 namespace ssd {
+
+// Per-launch timing of a combined call: every launch names itself; with a
+// trace whose event array has room, it gets the two events (start, end) that
+// its launch must record and true, else false.
+bool trace_events(ssd_launch_trace *t, const char *name, void **start, void **stop);
 
 // The layer's step-size preprocessing, applied where dt is read:
 // dt = min(max(softplus(dt_raw + bias[h]), lo), hi) when `on`.
@@ -34,6 +41,7 @@ struct PrefillDims {
     // align mode: prefix[s] tokens precede sequence s, chunk boundaries fall on
     // absolute multiples of Q (nullptr: chunks start at each sequence's start)
     const int32_t *prefix = nullptr;
+    ssd_launch_trace *trace = nullptr;   // per-launch timing (nullptr: none)
 };
 
 struct DecodeDims {

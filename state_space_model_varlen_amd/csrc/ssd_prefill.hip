@@ -9,8 +9,22 @@
 // dt * A_h inside the chunk.
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "ssd_device.h"
 #include "ssd_launch.h"
+
+// A kernel launch of the prefill; under a launch trace, hipExtLaunchKernelGGL
+// records the kernel's own start and end on the trace's two events for it.
+#define SSD_LAUNCH(d, name, kernel, grid, block, smem, st, ...)                                \
+    do {                                                                                       \
+        void *ev0_ = nullptr, *ev1_ = nullptr;                                                 \
+        if (ssd::trace_events((d).trace, (name), &ev0_, &ev1_))                                \
+            hipExtLaunchKernelGGL(kernel, grid, block, smem, st, static_cast<hipEvent_t>(ev0_), \
+                                  static_cast<hipEvent_t>(ev1_), 0u, __VA_ARGS__);             \
+        else                                                                                   \
+            hipLaunchKernelGGL(kernel, grid, block, smem, st, __VA_ARGS__);                    \
+    } while (0)
 
 namespace ssd {
 
@@ -1915,7 +1929,7 @@ static void launch_cumsum_t(const PrefillDims &d, const void *dt, const float *A
                             int32_t *meta, float *cum, float *dto, hipStream_t st, const DtTf &tf)
 {
     dim3 grid(d.max_chunks, (d.H + kCumsumHeadsPerBlock - 1) / kCumsumHeadsPerBlock);
-    hipLaunchKernelGGL(chunk_cumsum_kernel<TIn>, grid, dim3(256), 0, st, d.T, d.S, d.H, d.Q,
+    SSD_LAUNCH(d, "chunk_cumsum", chunk_cumsum_kernel<TIn>, grid, dim3(256), 0, st, d.T, d.S, d.H, d.Q,
                        d.max_chunks, static_cast<const TIn *>(dt), A, cu, meta, cum, dto, tf,
                        d.prefix);
 }
@@ -1927,7 +1941,7 @@ static void launch_prep_t(const PrefillDims &d, const void *dt, const float *A, 
 {
     const int HB = (d.H + kCumsumHeadsPerBlock - 1) / kCumsumHeadsPerBlock;
     dim3 grid(d.max_chunks, HB + d.G * (d.Q / 16));
-    hipLaunchKernelGGL((chunk_prep_kernel<TIn, N>), grid, dim3(256), 0, st, d.T, d.S, d.H, d.G, d.Q,
+    SSD_LAUNCH(d, "chunk_prep", (chunk_prep_kernel<TIn, N>), grid, dim3(256), 0, st, d.T, d.S, d.H, d.G, d.Q,
                        d.max_chunks, static_cast<const TIn *>(dt), A, cu, meta, cum, dto,
                        static_cast<const TIn *>(B), static_cast<const TIn *>(C),
                        static_cast<TIn *>(CB), tf, d.prefix);
@@ -1961,7 +1975,7 @@ static void launch_state_t(const PrefillDims &d, const void *x, const void *B, c
                            const float *cum, const float *dtc, float *states, hipStream_t st)
 {
     dim3 grid(d.H, d.max_chunks);
-    hipLaunchKernelGGL((chunk_state_kernel<TIn, P, N>), grid, dim3(256), 0, st, d.S, d.H, d.G, d.Q,
+    SSD_LAUNCH(d, "chunk_state", (chunk_state_kernel<TIn, P, N>), grid, dim3(256), 0, st, d.S, d.H, d.G, d.Q,
                        d.max_chunks, static_cast<const TIn *>(x), static_cast<const TIn *>(B),
                        meta, cum, dtc, states);
 }
@@ -1971,7 +1985,7 @@ static void launch_bmm_t(const PrefillDims &d, const void *B, const void *C, con
                          void *CB, hipStream_t st)
 {
     dim3 grid(d.max_chunks, d.G, d.Q / 16);
-    hipLaunchKernelGGL((bmm_kernel<TIn, N>), grid, dim3(256), 0, st, d.S, d.G, d.Q, d.max_chunks,
+    SSD_LAUNCH(d, "bmm_chunk", (bmm_kernel<TIn, N>), grid, dim3(256), 0, st, d.S, d.G, d.Q, d.max_chunks,
                        static_cast<const TIn *>(B), static_cast<const TIn *>(C), meta,
                        static_cast<TIn *>(CB));
 }
@@ -1992,7 +2006,7 @@ static void launch_scan_t(const PrefillDims &d, const void *x, const void *C, co
     const size_t smem = scan_smem<TIn, P, N>(d.Q);
     static size_t raised = 0;
     allow_lds(reinterpret_cast<const void *>(&chunk_scan_kernel<TIn, P, N>), smem, raised);
-    hipLaunchKernelGGL((chunk_scan_kernel<TIn, P, N>), grid, dim3(256), smem, st, d.S, d.H, d.G,
+    SSD_LAUNCH(d, "chunk_scan", (chunk_scan_kernel<TIn, P, N>), grid, dim3(256), smem, st, d.S, d.H, d.G,
                        d.Q, d.max_chunks, static_cast<const TIn *>(x), static_cast<const TIn *>(C),
                        D, meta, cum, dtc, static_cast<const TIn *>(CB),
                        static_cast<const TIn *>(entering), static_cast<TIn *>(y));
@@ -2007,7 +2021,7 @@ static void launch_state_fast(const PrefillDims &d, const void *x, const void *B
     static size_t raised = 0;
     allow_lds(reinterpret_cast<const void *>(&chunk_state_fast_kernel<Q>), smem, raised);
     const unsigned nblk = (unsigned)((int64_t)d.max_chunks * 2 * d.H);
-    hipLaunchKernelGGL(chunk_state_fast_kernel<Q>, dim3(nblk), dim3(256), smem, st, d.S, d.H, d.G,
+    SSD_LAUNCH(d, "chunk_state", chunk_state_fast_kernel<Q>, dim3(nblk), dim3(256), smem, st, d.S, d.H, d.G,
                        d.max_chunks, static_cast<const bf16 *>(x), static_cast<const bf16 *>(B),
                        meta, cum, dtc, states);
 }
@@ -2029,7 +2043,7 @@ static void launch_scan_fast_s(const PrefillDims &d, const void *x, const void *
     const int64_t rounds = (pairs + kXcds - 1) / kXcds;
     const unsigned nblk = (unsigned)(by_chunk ? rounds * kXcds * (d.H / d.G)
                                               : (int64_t)d.max_chunks * d.H);
-    hipLaunchKernelGGL((chunk_scan_fast_kernel<Q, SEG>), dim3(nblk), dim3(2 * Q), smem, st, d.S,
+    SSD_LAUNCH(d, SEG ? "chunk_scan_segmented" : "chunk_scan", (chunk_scan_fast_kernel<Q, SEG>), dim3(nblk), dim3(2 * Q), smem, st, d.S,
                        d.H, d.G, d.max_chunks, static_cast<const bf16 *>(x),
                        static_cast<const bf16 *>(C), D, meta, cum, dtc,
                        static_cast<const bf16 *>(CB), static_cast<const bf16 *>(entering),
@@ -2082,7 +2096,7 @@ static void launch_bmm_pair(const PrefillDims &d, const void *B, const void *C, 
     const size_t smem = (size_t)Q * kCbLDB * sizeof(bf16);
     static size_t raised = 0;
     allow_lds(reinterpret_cast<const void *>(&bmm_pair_kernel<Q>), smem, raised);
-    hipLaunchKernelGGL(bmm_pair_kernel<Q>, dim3((unsigned)((int64_t)d.max_chunks * d.G)),
+    SSD_LAUNCH(d, "bmm_chunk_pairs", bmm_pair_kernel<Q>, dim3((unsigned)((int64_t)d.max_chunks * d.G)),
                        dim3(2 * Q), smem, st, d.S, d.G, static_cast<const bf16 *>(B),
                        static_cast<const bf16 *>(C), meta, static_cast<bf16 *>(CB));
 }
@@ -2122,7 +2136,7 @@ static void launch_sp_t(const PrefillDims &d, const float *states, const float *
     // latency) when the state splits evenly and there are still enough blocks
     const int64_t blocks4 = (int64_t)d.S * d.H * (PN / 4096);
     if (PN % 4096 == 0 && blocks4 >= kSpMinBlocks) {
-        hipLaunchKernelGGL((state_passing_kernel<TS, TE, 4>), dim3((unsigned)blocks4), dim3(256), 0,
+        SSD_LAUNCH(d, "state_passing", (state_passing_kernel<TS, TE, 4>), dim3((unsigned)blocks4), dim3(256), 0,
                            st, d.S, d.H, PN, d.Q, d.max_chunks, d.num_slots, states, cum, meta,
                            static_cast<TS *>(cache), idx, has_init, static_cast<TE *>(entering),
                            static_cast<TS *>(ckpt), d.sr);
@@ -2130,7 +2144,7 @@ static void launch_sp_t(const PrefillDims &d, const float *states, const float *
     }
     const int EB = (PN + 1023) / 1024;
     dim3 grid((unsigned)((int64_t)d.S * d.H * EB));
-    hipLaunchKernelGGL((state_passing_kernel<TS, TE, 1>), grid, dim3(256), 0, st, d.S, d.H, PN,
+    SSD_LAUNCH(d, "state_passing", (state_passing_kernel<TS, TE, 1>), grid, dim3(256), 0, st, d.S, d.H, PN,
                        d.Q, d.max_chunks, d.num_slots, states, cum, meta, static_cast<TS *>(cache),
                        idx, has_init, static_cast<TE *>(entering), static_cast<TS *>(ckpt), d.sr);
 }
@@ -2172,7 +2186,7 @@ static void launch_state_scan_k(const PrefillDims &d, const void *x, const void 
             allow_lds(reinterpret_cast<const void *>(&state_scan_multi_kernel<Q, CKPT, TS>), smem,
                       raised_m);
             const unsigned nblk = (unsigned)(items < kMultiBlocks ? items : kMultiBlocks);
-            hipLaunchKernelGGL((state_scan_multi_kernel<Q, CKPT, TS>), dim3(nblk), dim3(512), smem,
+            SSD_LAUNCH(d, "chunk_state_passing_multi", (state_scan_multi_kernel<Q, CKPT, TS>), dim3(nblk), dim3(512), smem,
                                st, d.S, d.H, d.G, d.max_chunks, d.num_slots,
                                static_cast<const bf16 *>(x), static_cast<const bf16 *>(B), meta,
                                cum, dtc, static_cast<TS *>(cache), idx, has_init,
@@ -2187,7 +2201,7 @@ static void launch_state_scan_k(const PrefillDims &d, const void *x, const void 
     const unsigned nblk = (unsigned)((int64_t)d.S * nseg * d.H * (128 / kScanNSL));
     // longest chain first: few sequences (one wave ranks them), heads a multiple of 8
     const int lpt = !SEG && d.S > 1 && d.S <= 64 && d.H % kXcds == 0;
-    hipLaunchKernelGGL((state_scan_fast_kernel<Q, CKPT, SEG, TS>), dim3(nblk), dim3(512), smem,
+    SSD_LAUNCH(d, SEG ? "chunk_state_passing_segmented" : "chunk_state_passing", (state_scan_fast_kernel<Q, CKPT, SEG, TS>), dim3(nblk), dim3(512), smem,
                        st, d.S, d.H, d.G, d.max_chunks, d.num_slots, static_cast<const bf16 *>(x),
                        static_cast<const bf16 *>(B), meta, cum, dtc, static_cast<TS *>(cache), idx,
                        has_init, static_cast<bf16 *>(entering), static_cast<TS *>(ckpt), d.sr,
@@ -2196,7 +2210,7 @@ static void launch_state_scan_k(const PrefillDims &d, const void *x, const void 
         const int PN = 64 * 128;
         const int ncar = d.S * d.H * (PN / 1024);
         const int nbmm = seg.CB ? d.max_chunks * d.G * (d.Q / 16) : 0;
-        hipLaunchKernelGGL(state_carry_kernel<TS>, dim3((unsigned)(nbmm + ncar)), dim3(256), 0, st,
+        SSD_LAUNCH(d, nbmm ? "state_carry_and_bmm" : "state_carry", state_carry_kernel<TS>, dim3((unsigned)(nbmm + ncar)), dim3(256), 0, st,
                            d.S, d.H, PN, nseg, d.max_chunks, d.num_slots, meta, seg.fin, seg.L,
                            static_cast<bf16 *>(seg.carry), static_cast<TS *>(cache), idx, d.sr,
                            nbmm, d.G, d.Q, static_cast<const bf16 *>(B),

@@ -18,20 +18,51 @@ def test_more_than_one_gpu_is_refused():
     assert r.stdout == ""
 
 
-def test_prefill_bytes_of_the_layer_prefill():
+def test_launch_bytes_and_flops_of_the_layer_prefill():
     """4096 tokens, 80 heads, headdim 64, d_state 128, one group, chunk 256, bf16
-    inputs: 16 chunks. Each figure is the sum of the tensors the kernel must read
-    or write once, counted by hand here."""
+    inputs, float32 state, no cached state: 16 chunks, the state pass cut into 3
+    segments. Each figure is the sum of the tensors the launch must read or write
+    once, counted by hand here."""
+    import ssd_synth as sy
     T, S, H, P, N, G, Q, nc = 4096, 1, 80, 64, 128, 1, 256, 16
-    b = bench.prefill_bytes(T, S, H, P, N, G, Q, nc, 2, 4, 0, False)
+    assert bench.segments(sy.C1) == 3
+    w = bench.layer_work(sy.C1, 3)
+    assert (w.T, w.S, w.nc, w.ex, w.es, w.s_init) == (T, S, nc, 2, 4, 0)
     x = T * H * P * 2                      # x (and y): 41.9 MB each
     bc = T * G * N * 2                     # B or C
     per_chunk = 2 * H * nc * Q * 4         # cumsum and dt, float32
     entering = nc * H * P * N * 2          # entering states, bf16
     final = S * H * P * N * 4              # the final state, float32
     cb = nc * G * (16 * 17 // 2) * 256 * 2   # causal 16 x 16 tiles of CB, bf16
-    assert b["chunk_cumsum"] == T * H * 2 + per_chunk
-    assert b["chunk_state_passing"] == x + bc + per_chunk + entering + final
-    assert b["chunk_scan"] == 2 * x + bc + per_chunk + cb + entering
-    assert round(b["chunk_scan"] / 1e6, 1) == 109.6
-    assert round(b["chunk_state_passing"] / 1e6, 1) == 69.2
+    fins = 3 * H * P * N * 4                 # segment final states, float32
+    assert bench.launch_bytes("chunk_cumsum", w) == T * H * 2 + per_chunk
+    assert bench.launch_bytes("chunk_scan", w) == 2 * x + bc + per_chunk + cb + entering
+    assert round(bench.launch_bytes("chunk_scan", w) / 1e6, 1) == 109.6
+    # the scope document's per-kernel table counts entering states in float32: 130.5 MB
+    # there (CB's causal half element by element), 130.6 MB here (whole 16 x 16 tiles)
+    assert round(bench.launch_bytes("chunk_scan", w, entering_bytes=4) / 1e6, 1) == 130.6
+    assert bench.launch_bytes("chunk_scan_segmented", w) == \
+        2 * x + bc + per_chunk + cb + entering + 2 * H * P * N * 2
+    assert bench.launch_bytes("chunk_state_passing_segmented", w) == \
+        x + bc + per_chunk + entering + fins
+    assert bench.launch_bytes("state_carry_and_bmm", w) == \
+        fins + 3 * H * P * N * 2 + final + 2 * bc + cb
+    # flops: causal intra-chunk 80 * 64 * 256 * 257 per chunk plus the state term
+    # 2 * 80 * 64 * 128 * 256 per chunk: 10.76 GFLOP
+    assert bench.launch_flops("chunk_scan_segmented", w) == \
+        16 * (H * P * 256 * 257 + 2 * H * P * N * 256)
+    assert round(bench.launch_flops("chunk_scan", w) / 1e9, 2) == 10.76
+    assert bench.launch_flops("chunk_state_passing_segmented", w) == 16 * 2 * H * P * N * 256
+
+
+def test_kernel_names_map_to_launches():
+    n = lambda k: bench.launch_name(k)[0]
+    assert n("_ZN3ssd22chunk_scan_fast_kernelILi256ELb1EEEviii") == "chunk_scan_segmented"
+    assert n("_ZN3ssd22chunk_scan_fast_kernelILi256ELb0EEEviii") == "chunk_scan"
+    assert n("_ZN3ssd22state_scan_fast_kernelILi256ELb0ELb1EfEEvii") == \
+        "chunk_state_passing_segmented"
+    assert n("_ZN3ssd22state_scan_fast_kernelILi256ELb1ELb0EfEEvii") == "chunk_state_passing"
+    assert n("void ssd::state_carry_kernel<float>(int, int") == "state_carry_and_bmm"
+    assert n("_ZN3ssd19chunk_cumsum_kernelIDF16bEEvii") == "chunk_cumsum"
+    assert n("_ZN3ssd15bmm_pair_kernelILi256EEEvii") == "bmm_chunk_pairs"
+    assert n("at::native::vectorized_elementwise_kernel") is None

@@ -362,6 +362,38 @@ def test_c1_layer_prefill_full():
     assert_close(yd, ref["y"] - to64(inp.D)[None, :, None] * to64(inp.x), BF16, "c1 y (D = 0)")
 
 
+def test_launch_trace_names_and_times_every_launch():
+    """ssd_options.trace on the layer call: an event before each kernel launch and
+    one after the last. The launches are named in order, every interval is
+    positive, and y and the final state are bit for bit those of the untraced
+    call."""
+    ssd = _ssd()
+    cfg = sy.C1
+    inp = sy.make_prefill(cfg)
+    H, P, N, Q = cfg.nheads, cfg.headdim, cfg.d_state, cfg.chunk_size
+    p = ssd.make_problem(cfg.total_tokens, 1, H, P, N, cfg.ngroups, Q, 1, BF16, F32)
+    args = [t.to(DEV) for t in (inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.cu_seqlens)]
+    outs = []
+    tr = ssd.LaunchTrace()
+    for opt in (None, ssd.make_options(trace=tr)):
+        cache = torch.zeros(1, H, P, N, device=DEV)
+        y = torch.empty(cfg.total_tokens, H, P, dtype=BF16, device=DEV)
+        ws = ssd.alloc_workspace(p, DEV)
+        if opt is None:
+            ssd.ssd_combined_varlen(p, *args, cache, inp.state_indices.to(DEV), None, y, None, ws)
+        else:
+            ssd.ssd_combined_varlen_ex(p, opt, *args, cache, inp.state_indices.to(DEV), None, y,
+                                       None, ws)
+        torch.cuda.synchronize()
+        outs.append((y.cpu(), cache.cpu()))
+    d = tr.durations_us()
+    assert [n for n, _ in d] == ["chunk_cumsum", "chunk_state_passing_segmented",
+                                 "state_carry_and_bmm", "chunk_scan_segmented"]
+    assert all(us > 0 for _, us in d), d
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert torch.equal(outs[0][1], outs[1][1])
+
+
 def _full_continuation(cfg, checkpoints):
     """Full-size prefill from cached states: every sequence with an initial state
     starts from the oracle's state after its own seeded prefix (rounded to the
