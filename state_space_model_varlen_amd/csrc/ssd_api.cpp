@@ -339,6 +339,12 @@ static int combined(const ssd_problem *p, const ssd::DtTf &tf, const void *x, co
     d.sr = sr;
     d.trace = trace;
     if (trace) trace->count = 0;
+    // short sequences: one launch, no workspace
+    if (ssd::short_scan_path(d)) {
+        ssd::launch_short_scan(d, x, dt, A, B, C, D, cu_seqlens, state_cache, state_indices,
+                               has_initial_state, y, checkpoints, stream, tf);
+        return launch_status();
+    }
     char *base = static_cast<char *>(workspace);
     int32_t *meta = reinterpret_cast<int32_t *>(base + w.meta);
     float *cum = reinterpret_cast<float *>(base + w.cum);

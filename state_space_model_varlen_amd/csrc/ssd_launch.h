@@ -111,6 +111,17 @@ void launch_chunk_scan(const PrefillDims &d, const void *x, const void *C, const
                        const void *entering, void *y, void *stream,
                        const SegBufs *seg = nullptr);
 
+// Batches of short sequences (bf16, headdim 64, d_state 128, on average at most
+// half a chunk per sequence: 2 T <= S Q): the whole prefill in one launch, one
+// block per (sequence, head) walking its sequence in sub-chunks, with the
+// initial state read from and the final state written to the cache slot, and
+// no workspace.
+bool short_scan_path(const PrefillDims &d);
+void launch_short_scan(const PrefillDims &d, const void *x, const void *dt, const float *A,
+                       const void *B, const void *C, const float *D, const int32_t *cu,
+                       void *cache, const int32_t *idx, const uint8_t *has_init, void *y,
+                       void *ckpt, void *stream, const DtTf &tf);
+
 // cu (optional): packed-varlen requests, request r owning tokens cu[r] .. cu[r+1]-1
 // of Ttot packed rows; without it request r owns tokens r T .. r T + T - 1.
 void launch_state_update(const DecodeDims &d, void *cache, const int32_t *idx, const void *x,

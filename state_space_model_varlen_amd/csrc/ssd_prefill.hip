@@ -1908,6 +1908,289 @@ void chunk_scan_fast_kernel(
 }
 
 // ===========================================================================
+// Batches of short sequences in one launch. One block of four waves per
+// (sequence, head) walks its sequence in sub-chunks of SUB (32 or 64) tokens, cut
+// so that none crosses a chunk boundary (every checkpoint is then a sub-chunk's
+// exit state), and does both halves of the scan for each sub-chunk: y from the
+// intra-sub-chunk product, the state the sub-chunk enters with and D x; then
+// the state it passes on. The initial state is read from the cache slot once
+// and the final state written back to it: no cumsum, CB, entering or chunk
+// state goes through HBM. Chunking is exact algebra, so the sub-chunk size
+// changes results only by rounding.
+//
+// Per sub-chunk (len tokens, local cum = inclusive cumsum of dt A_h), wave w
+// (rows past the sub-chunk leave a wave idle in (a)-(c)):
+//   (a) CB^T tiles (j x i) for its row tile i in [16 w, 16 w + 16): B rows
+//       times C rows over N; each output tile is half of a split-K A fragment
+//       of (b), taken element by element as CB[i][j] exp(cum_i - cum_j) dt_j
+//       for j <= i (exact exponentials, no decay factoring);
+//   (b) y_i += sum_j A_ij x_j over its row tile, all 64 p;
+//   (c) y_i += exp(cum_i) C_i . H_in^T (H_in in bf16 from LDS), + D_h x_i;
+//   (d) its 16 state columns p in [16 w, 16 w + 16), all 128 n, in MFMA
+//       accumulators across sub-chunks: H <- exp(cum_last) H
+//       + sum_t (exp(cum_last - cum_t) dt_t B_t) x_t^T.
+constexpr int kShortLDX = 72;    // x tile pitch (bf16)
+constexpr int kShortLDB = 136;   // B tile and state tile pitch (bf16): 68 dwords, conflict-free
+constexpr int kShortLDY = 72;    // y staging tile pitch (bf16)
+
+template <int SUB, typename TS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void short_scan_kernel(
+    int T, int S, int H, int G, int Q, int num_slots, const bf16 *__restrict__ x,
+    const bf16 *__restrict__ dt, const float *__restrict__ A, const bf16 *__restrict__ B,
+    const bf16 *__restrict__ C, const float *__restrict__ D, const int32_t *__restrict__ cu,
+    TS *cache, const int32_t *__restrict__ idx, const uint8_t *__restrict__ has_init,
+    bf16 *__restrict__ y, TS *__restrict__ ckpt, SrCtx sr, DtTf tf,
+    const int32_t *__restrict__ prefix)
+{
+    constexpr int P = 64, N = 128, LDX = kShortLDX, LDB = kShortLDB, LDY = kShortLDY;
+    static_assert(SUB == 32 || SUB == 64, "sub-chunks of 32 or 64 tokens");
+    constexpr int KS = SUB / 32;           // 32-token K steps per sub-chunk
+    __shared__ __attribute__((aligned(16))) bf16 xs[SUB * LDX];   // x_t (raw)
+    __shared__ __attribute__((aligned(16))) bf16 bs[SUB * LDB];   // B_t (raw)
+    // the entering state H_in[p][n] (bf16); after (c) the waves' y staging tiles
+    __shared__ __attribute__((aligned(16))) bf16 hs[P * LDB];
+    __shared__ int s_acc[4];
+
+    // (sequence, head) in logical order (s G + g) (H / G) + h % (H / G): each XCD
+    // takes a contiguous range, so the heads sharing a sequence's B and C rows sit
+    // on one L2
+    const int lb = xcd_logical_block(blockIdx.x, S * H);
+    const int s = lb / H, h = lb - s * H;
+    const int g = h / (H / G);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int PN = P * N;
+
+    int a = cu[s], b = cu[s + 1];
+    a = clampi(a, 0, T);
+    b = clampi(b, 0, T);
+    b = b > a ? b : a;
+    const int L = b - a;
+    const int f = first_chunk_len(Q, prefix, s);     // tokens of the first chunk
+    const int slot = idx[s];
+    const bool slot_ok = slot >= 0 && slot < num_slots;
+    const bool read_init = slot_ok && has_init != nullptr && has_init[s] != 0;
+    const SrKey srk = sr_key_checked(sr);
+    const float Ah = A[h];
+    const float bias = tf.bias ? tf.bias[h] : 0.0f;
+    const float Dh = D ? D[h] : 0.0f;
+
+    // chunk_cu[s]: the first checkpoint row of this sequence (checkpoints only)
+    int crow = 0;
+    if (ckpt != nullptr) {
+        int part = 0;
+        for (int t = tid; t < s; t += 256) {
+            const int ta = clampi(cu[t], 0, T), tb = clampi(cu[t + 1], 0, T);
+            const int tl = tb > ta ? tb - ta : 0;
+            const int tf_ = first_chunk_len(Q, prefix, t);
+            part += tl == 0 ? 0 : (tl <= tf_ ? 1 : 1 + (tl - tf_ + Q - 1) / Q);
+        }
+        part = (int)group_sum((float)part, kWave);   // (exact: counts stay far below 2^24)
+        if (lane == 0) s_acc[w] = part;
+        __syncthreads();
+        crow = s_acc[0] + s_acc[1] + s_acc[2] + s_acc[3];
+    }
+
+    // this lane's state elements (d): p = 16 w + r16, n = 16 nt + 4 kg + 0..3
+    const int pcol = 16 * w + r16;
+    TS *cslot = cache + ((int64_t)(slot_ok ? slot : 0) * H + h) * PN + (int64_t)pcol * N + 4 * kg;
+    f32x4 hst[8];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+        float v[4];
+        load4<TS>(cslot + 16 * nt, v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hst[nt][e] = read_init ? v[e] : 0.0f;
+    }
+
+    const uint32_t xrow = (uint32_t)H * P * 2, nrow = (uint32_t)G * N * 2;
+    // sub-chunks: never past a chunk boundary (the first chunk has f tokens, the
+    // others Q), at most SUB tokens
+    int pos = 0, chunk_end = f < L ? f : L, k = 0;
+    while (pos < L) {
+        const int len = chunk_end - pos < SUB ? chunk_end - pos : SUB;
+        const int st = a + pos;
+        // ---- loads: dt (one token per lane), x and B tiles, this wave's C rows
+        const int tq = lane < len ? lane : len - 1;
+        float dtv = to_f32(dt[(int64_t)(st + tq) * H + h]);
+        const rsrc_t rx = make_rsrc(x + ((int64_t)st * H + h) * P, (uint32_t)(len - 1) * xrow + P * 2);
+        const rsrc_t rb = make_rsrc(B + ((int64_t)st * G + g) * N, (uint32_t)(len - 1) * nrow + N * 2);
+        const rsrc_t rc = make_rsrc(C + ((int64_t)st * G + g) * N, (uint32_t)(len - 1) * nrow + N * 2);
+        uint4 xr[SUB / 32], br[SUB / 16], cfr[4];
+#pragma unroll
+        for (int q = 0; q < SUB / 32; ++q) {   // SUB rows x 8 vectors over 256 threads
+            const int u = tid + 256 * q;
+            xr[q] = buf_ld16(rx, (uint32_t)(u >> 3) * xrow + 16 * (u & 7));
+        }
+#pragma unroll
+        for (int q = 0; q < SUB / 16; ++q) {   // SUB rows x 16 vectors
+            const int u = tid + 256 * q;
+            br[q] = buf_ld16(rb, (uint32_t)(u >> 4) * nrow + 16 * (u & 15));
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)         // C row 16 w + r16, n = 32 kk + 8 kg .. + 7
+            cfr[kk] = buf_ld16(rc, (uint32_t)(16 * w + r16) * nrow + 64 * kk + 16 * kg);
+        __builtin_amdgcn_sched_barrier(0);
+        if (tf.on) dtv = dt_transform(tf, dtv, bias);
+        dtv = lane < len ? dtv : 0.0f;        // (lanes past SUB: len <= SUB)
+        const float cum = wave_inclusive_sum(dtv * Ah, lane);
+        const float cl = __shfl(cum, len - 1);
+        const float wt = __expf(cl - cum) * dtv;     // weight of token `lane` in the state
+
+        __syncthreads();   // the previous sub-chunk's reads of xs, bs, hs are done
+#pragma unroll
+        for (int q = 0; q < SUB / 32; ++q) {
+            const int u = tid + 256 * q;
+            *reinterpret_cast<uint4 *>(xs + (u >> 3) * LDX + 8 * (u & 7)) = xr[q];
+        }
+#pragma unroll
+        for (int q = 0; q < SUB / 16; ++q) {
+            const int u = tid + 256 * q;
+            *reinterpret_cast<uint4 *>(bs + (u >> 4) * LDB + 8 * (u & 15)) = br[q];
+        }
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+            const float v4[4] = {hst[nt][0], hst[nt][1], hst[nt][2], hst[nt][3]};
+            store4<bf16>(hs + pcol * LDB + 16 * nt + 4 * kg, v4);
+        }
+        __syncthreads();
+
+        // ---- (a) + (b): intra-sub-chunk product for row tile w
+        const int i0 = 16 * w;
+        f32x4 yacc[4];
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) yacc[pt] = zero4();
+        if (i0 < len) {
+            const int ii = i0 + r16;                 // this lane's row in the A fragments
+            const float cum_i = __shfl(cum, ii);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (32 * ks > i0 + 15) break;        // (uniform over the wave)
+                // CB^T tiles j in [32 ks, 32 ks + 16) and [32 ks + 16, 32 ks + 32)
+                f32x4 cbt[2];
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    cbt[half] = zero4();
+                    const int j0 = 32 * ks + 16 * half;
+                    if (j0 <= i0 + 15) {
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk) {
+                            const bf16x8 bfr = *reinterpret_cast<const bf16x8 *>(
+                                bs + (j0 + r16) * LDB + 32 * kk + 8 * kg);
+                            cbt[half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                bfr, __builtin_bit_cast(bf16x8, cfr[kk]), cbt[half], 0, 0, 0);
+                        }
+                    }
+                }
+                // A fragment, split K order: v < 4 -> j = 32 ks + 4 kg + v,
+                // v >= 4 -> j = 32 ks + 16 + 4 kg + v - 4
+                bf16x8 af;
+#pragma unroll
+                for (int v = 0; v < 8; ++v) {
+                    const int j = 32 * ks + 4 * kg + (v & 3) + ((v >> 2) << 4);
+                    const float cj = __shfl(cum, j), dj = __shfl(dtv, j);
+                    const float m = cbt[v >> 2][v & 3] * __expf(cum_i - cj) * dj;
+                    af[v] = static_cast<bf16>(j <= ii ? m : 0.0f);
+                }
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) {
+                    const bf16x8 xf = mfma_frag_tr_split(xs, LDX, 32 * ks, 16 * pt, lane);
+                    yacc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, xf, yacc[pt], 0, 0, 0);
+                }
+            }
+            // ---- (c): exp(cum_i) C_i . H_in^T, then D x (rows i0 + 4 kg + v, p = 16 pt + r16)
+            f32x4 sacc[4];
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) sacc[pt] = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) {
+                    const bf16x8 hf = *reinterpret_cast<const bf16x8 *>(
+                        hs + (16 * pt + r16) * LDB + 32 * kk + 8 * kg);
+                    sacc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, cfr[kk]), hf, sacc[pt], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int i = i0 + 4 * kg + v;
+                const float ei = __expf(__shfl(cum, i));
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) {
+                    const float xv = static_cast<float>(xs[i * LDX + 16 * pt + r16]);
+                    yacc[pt][v] += ei * sacc[pt][v] + Dh * xv;
+                }
+            }
+        }
+        __syncthreads();   // every wave is done reading hs: it becomes the y staging area
+
+        // ---- y: through this wave's staging tile as 16-byte row stores
+        if (i0 < len) {
+            bf16 *yw = hs + w * 16 * LDY;
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    yw[(4 * kg + v) * LDY + 16 * pt + r16] = static_cast<bf16>(yacc[pt][v]);
+            wave_lds_sync();
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int r = (lane >> 3) + 8 * q, c8 = lane & 7;
+                const uint4 v = *reinterpret_cast<const uint4 *>(yw + r * LDY + 8 * c8);
+                if (i0 + r < len)
+                    *reinterpret_cast<uint4 *>(y + ((int64_t)(st + i0 + r) * H + h) * P + 8 * c8) = v;
+            }
+        }
+
+        // ---- (d): the state passed on, this wave's 16 columns p
+        const float decay = __expf(cl);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hst[nt][e] *= decay;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (32 * ks >= len) break;               // (uniform)
+            float wv[8];
+#pragma unroll
+            for (int v = 0; v < 8; ++v) wv[v] = __shfl(wt, 32 * ks + 4 * kg + (v & 3) + ((v >> 2) << 4));
+            const bf16x8 xf = mfma_frag_tr_split(xs, LDX, 32 * ks, 16 * w, lane);
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) {
+                const bf16x8 braw = mfma_frag_tr_split(bs, LDB, 32 * ks, 16 * nt, lane);
+                bf16x8 bw;
+#pragma unroll
+                for (int v = 0; v < 8; ++v) bw[v] = static_cast<bf16>(static_cast<float>(braw[v]) * wv[v]);
+                hst[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw, xf, hst[nt], 0, 0, 0);
+            }
+        }
+        pos += len;
+        if (pos == chunk_end) {
+            // the exit state of chunk k: its checkpoint
+            if (ckpt != nullptr) {
+                const int64_t off = ((int64_t)(crow + k) * H + h) * PN + (int64_t)pcol * N + 4 * kg;
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt) {
+                    const float v4[4] = {hst[nt][0], hst[nt][1], hst[nt][2], hst[nt][3]};
+                    put4<TS>(ckpt + off + 16 * nt, v4, srk, (uint64_t)(off + 16 * nt), kSrCkpt);
+                }
+            }
+            ++k;
+            chunk_end = chunk_end + Q < L ? chunk_end + Q : L;
+        }
+    }
+    if (slot_ok) {
+        const int64_t fo = ((int64_t)slot * H + h) * PN + (int64_t)pcol * N + 4 * kg;
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+            const float v4[4] = {hst[nt][0], hst[nt][1], hst[nt][2], hst[nt][3]};
+            put4<TS>(cslot + 16 * nt, v4, srk, (uint64_t)(fo + 16 * nt), kSrFinal);
+        }
+    }
+}
+
+// ===========================================================================
 // Launchers.
 static inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
@@ -2278,6 +2561,42 @@ void launch_state_scan(const PrefillDims &d, const void *x, const void *B, const
         launch_state_scan_t<bf16>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, seg, st);
     else
         launch_state_scan_t<float>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, seg, st);
+}
+
+constexpr int kShortSub = 32;   // tokens per sub-chunk of the short-sequence kernel (32 measured
+                                // faster than 64 on 32 x 32-token continuations)
+
+bool short_scan_path(const PrefillDims &d)
+{
+    return use_fast(d) && d.S > 0 && 2 * (int64_t)d.T <= (int64_t)d.S * d.Q;
+}
+
+template <typename TS>
+static void launch_short_t(const PrefillDims &d, const void *x, const void *dt, const float *A,
+                           const void *B, const void *C, const float *D, const int32_t *cu,
+                           void *cache, const int32_t *idx, const uint8_t *has_init, void *y,
+                           void *ckpt, hipStream_t st, const DtTf &tf)
+{
+    const unsigned nblk = (unsigned)((int64_t)d.S * d.H);
+    SSD_LAUNCH(d, "short_scan", (short_scan_kernel<kShortSub, TS>), dim3(nblk), dim3(256), 0, st, d.T, d.S,
+               d.H, d.G, d.Q, d.num_slots, static_cast<const bf16 *>(x),
+               static_cast<const bf16 *>(dt), A, static_cast<const bf16 *>(B),
+               static_cast<const bf16 *>(C), D, cu, static_cast<TS *>(cache), idx, has_init,
+               static_cast<bf16 *>(y), static_cast<TS *>(ckpt), d.sr, tf, d.prefix);
+}
+
+void launch_short_scan(const PrefillDims &d, const void *x, const void *dt, const float *A,
+                       const void *B, const void *C, const float *D, const int32_t *cu,
+                       void *cache, const int32_t *idx, const uint8_t *has_init, void *y,
+                       void *ckpt, void *stream, const DtTf &tf)
+{
+    hipStream_t st = as_stream(stream);
+    if (d.state_f16)
+        launch_short_t<f16>(d, x, dt, A, B, C, D, cu, cache, idx, has_init, y, ckpt, st, tf);
+    else if (d.state_bf16)
+        launch_short_t<bf16>(d, x, dt, A, B, C, D, cu, cache, idx, has_init, y, ckpt, st, tf);
+    else
+        launch_short_t<float>(d, x, dt, A, B, C, D, cu, cache, idx, has_init, y, ckpt, st, tf);
 }
 
 void launch_chunk_scan(const PrefillDims &d, const void *x, const void *C, const float *D,

@@ -163,6 +163,26 @@ def test_prefill_bf16_segmented_fp16_cache():
     assert torch.equal(after2.view(torch.int16), after.view(torch.int16))
 
 
+def test_prefill_bf16_short_path_fp16_cache():
+    """A batch of short sequences (the one-launch path) with an fp16 cache,
+    checkpoints and Philox-5 stochastic rounding: within the bf16 tolerance of the
+    oracle, the same bits for the same seed, other bits for another seed."""
+    Q = 256
+    inp, cache = _problem((20, 1, 0, 90, 33, 64) * 4, 8, 64, 128, 2, Q, BF16, 815)
+    y, after, ck = _prefill(inp, cache, Q, seed=31, rounds=5)
+    ref = oracle.prefill(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.cu_seqlens,
+                         inp.state_indices, inp.has_initial, cache, Q, checkpoints=True)
+    assert_close(y, ref["y"], BF16, "y", normalised=False)
+    used = inp.state_indices.long()
+    assert_close(after[used], ref["final"], BF16, "final states")
+    assert_close(ck[:len(ref["ckpt"])], ref["ckpt"], BF16, "checkpoints")
+    _, after2, ck2 = _prefill(inp, cache, Q, seed=31, rounds=5)
+    assert torch.equal(after2.view(torch.int16), after.view(torch.int16))
+    assert torch.equal(ck2.view(torch.int16), ck.view(torch.int16))
+    _, after3, _ = _prefill(inp, cache, Q, seed=32, rounds=5)
+    assert not torch.equal(after3[used].view(torch.int16), after[used].view(torch.int16))
+
+
 @pytest.mark.parametrize("keep", [True, False])
 def test_decode_fp16_states(keep):
     ssd = _ssd()

@@ -231,8 +231,10 @@ def test_packing_is_bitwise_invariant():
     """A packed batch gives the same bits as each sequence run alone: chunks
     start at every sequence's first token, so the work per sequence is identical.
     (A sequence's chain is cut into min(segment limit, its chunks) segments; here
-    no sequence has more chunks than the limit of either run, so the cuts agree.)"""
-    lens, H, P, N, G, Q = (300, 17, 513, 64), 4, 64, 128, 2, 128
+    no sequence has more chunks than the limit of either run, so the cuts agree.
+    Every sequence holds more than half a chunk, so no run takes the one-launch
+    path for short sequences, whose sub-chunks round differently.)"""
+    lens, H, P, N, G, Q = (300, 70, 513, 65), 4, 64, 128, 2, 128
     S = len(lens)
     inp = sy.random_problem(9, lens, H, P, N, G, Q, BF16, F32, num_slots=S,
                             has_initial=[True, False, True, True])
@@ -499,6 +501,77 @@ def test_growing_state_positive_A(growth):
                 assert_close(g_, w_, BF16, f"{what} {tag}", normalised=not (D and what == "y"))
             else:
                 assert_normalised(g_, w_, BF16, f"{what} {tag}")
+
+
+SHORT_CASES = [
+    # seqlens, H, G, Q, state dtype, checkpoints: batches whose sequences hold on
+    # average at most half a chunk (2 T <= S Q) run in one launch, one block per
+    # (sequence, head) walking sub-chunks of at most 64 tokens
+    ((32,) * 16, 16, 2, 256, BF16, False),
+    ((1, 0, 63, 64, 65, 127, 128, 129, 0, 200, 2, 3) + (1,) * 12, 8, 2, 128, F32, True),
+    ((5, 300, 0, 17, 31, 32, 33, 1) * 4, 8, 8, 256, BF16, True),
+    ((40, 9, 0, 100, 20, 1) * 3, 8, 4, 64, F32, True),
+    ((7, 40, 1, 2, 0) * 4, 4, 1, 32, BF16, True),
+]
+
+
+@pytest.mark.parametrize("case", SHORT_CASES, ids=lambda c: f"S{len(c[0])}_H{c[1]}_Q{c[3]}_"
+                         f"{str(c[4])[6:]}_{'ckpt' if c[5] else 'nockpt'}")
+def test_short_sequence_path(case):
+    """The one-launch path for short sequences against the oracle: sequences of 0,
+    1, 63-65, 127-129 and 200-300 tokens (several sub-chunks and chunks), cached
+    and zero starts, checkpoints, NaN in every slot no sequence may read; y with D
+    and without (normalised), final states, checkpoints, untouched slots."""
+    lens, H, G, Q, ts, ck = case
+    S = len(lens)
+    assert 2 * sum(lens) <= S * Q
+    inp = sy.random_problem(980 + SHORT_CASES.index(case), lens, H, 64, 128, G, Q, BF16, ts,
+                            num_slots=2 * S + 3, has_initial=[s % 3 != 2 for s in range(S)])
+    cache = _cache_with_states(inp, 2 * S + 3, ts)
+    y, after, ckpt = gpu_prefill(inp, cache, Q, checkpoints=ck)
+    ref = oracle.prefill(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.cu_seqlens,
+                         inp.state_indices, inp.has_initial, cache, Q, checkpoints=ck)
+    assert_close(y, ref["y"], BF16, "y", normalised=False)
+    used = inp.state_indices.long()
+    assert_close(after[used], ref["final"], looser(BF16, ts), "final states")
+    if ck:
+        assert_close(ckpt[:len(ref["ckpt"])], ref["ckpt"], looser(BF16, ts), "checkpoints")
+    others = [k for k in range(cache.shape[0]) if k not in set(used.tolist())]
+    bits = torch.int16 if ts == BF16 else torch.int32
+    assert torch.equal(after[others].view(bits), cache[others].view(bits))
+    yd, _, _ = gpu_prefill(inp, cache, Q, D=False)
+    refd = oracle.prefill(inp.x, inp.dt, inp.A, inp.B, inp.C, None, inp.cu_seqlens,
+                          inp.state_indices, inp.has_initial, cache, Q)
+    assert_close(yd, refd["y"], BF16, "y without D")
+
+
+def test_short_sequence_path_bad_slots_and_launch_count():
+    """Slot indices outside [0, num_slots) on the short path: the sequence starts
+    from zero and nothing is written. The call is one launch."""
+    ssd = _ssd()
+    lens = (30, 2, 41, 0)
+    inp = sy.random_problem(990, lens, 8, 64, 128, 2, 256, BF16, F32, num_slots=5,
+                            has_initial=[True] * 4)
+    cache = _cache_with_states(inp, 5, F32, nan_unused=False)
+    inp.state_indices[:] = torch.tensor([7, -3, 1, 99], dtype=torch.int32)
+    y, after, _ = gpu_prefill(inp, cache, 256)
+    ref = oracle.prefill(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.cu_seqlens,
+                         torch.tensor([0, 0, 1, 0]), torch.tensor([0, 0, 1, 0], dtype=torch.uint8),
+                         cache, 256)
+    assert_close(y, ref["y"], BF16, "y", normalised=False)
+    assert torch.equal(after[[0, 2, 3, 4]], cache[[0, 2, 3, 4]])
+    assert_close(after[1], ref["cache"][1], BF16, "slot 1 final state")
+    T = sum(lens)
+    p = ssd.make_problem(T, 4, 8, 64, 128, 2, 256, 5, BF16, F32)
+    tr = ssd.LaunchTrace()
+    g_cache = cache.to(DEV)
+    ssd.ssd_combined_varlen_ex(p, ssd.make_options(trace=tr), inp.x.to(DEV), inp.dt.to(DEV),
+                               inp.A.to(DEV), inp.B.to(DEV), inp.C.to(DEV), inp.D.to(DEV),
+                               inp.cu_seqlens.to(DEV), g_cache, inp.state_indices.to(DEV),
+                               inp.has_initial.to(DEV), torch.empty_like(y, device=DEV), None,
+                               ssd.alloc_workspace(p, DEV))
+    torch.cuda.synchronize()
+    assert [n for n, _ in tr.durations_us()] == ["short_scan"]
 
 
 SEG_CASES = [
