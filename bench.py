@@ -114,6 +114,9 @@ def launch_bytes(name, w: Work, entering_bytes=None):
         "state_carry_and_bmm": fin + S * w.nseg * HPN * ex + S * HPN * es + 2 * bc + cb,
         "chunk_scan": 2 * x + bc + per_chunk + cb + ent,
         "chunk_scan_segmented": 2 * x + bc + per_chunk + cb + ent + carry,
+        # the one-launch short-sequence path: x, dt, B, C in, y out, initial and
+        # final states, checkpoints
+        "short_scan": 2 * x + T * H * ex + 2 * bc + cache_io,
     }
     return table.get(name)
 
@@ -175,6 +178,7 @@ KERNEL_PATTERNS = [
      PREFILL_SOURCES),
     (r"state_scan_fast_kernel", "chunk_state_passing", PREFILL_SOURCES),
     (r"state_carry_kernel", "state_carry_and_bmm", PREFILL_SOURCES),
+    (r"short_scan_kernel", "short_scan", PREFILL_SOURCES),
     (r"chunk_scan_fast_kernelILi\d+ELb1E", "chunk_scan_segmented", PREFILL_SOURCES),
     (r"chunk_scan_fast_kernel|chunk_scan_kernel", "chunk_scan", PREFILL_SOURCES),
     (r"state_passing_kernel", "state_passing", PREFILL_SOURCES),

@@ -65,4 +65,5 @@ def test_kernel_names_map_to_launches():
     assert n("void ssd::state_carry_kernel<float>(int, int") == "state_carry_and_bmm"
     assert n("_ZN3ssd19chunk_cumsum_kernelIDF16bEEvii") == "chunk_cumsum"
     assert n("_ZN3ssd15bmm_pair_kernelILi256EEEvii") == "bmm_chunk_pairs"
+    assert n("void ssd::short_scan_kernel<32, float>(int, int") == "short_scan"
     assert n("at::native::vectorized_elementwise_kernel") is None
