@@ -111,6 +111,11 @@ def launch_bytes(name, w: Work, entering_bytes=None):
         "chunk_state_passing": x + bc + per_chunk + ent + cache_io,
         "chunk_state_passing_multi": x + bc + per_chunk + ent + cache_io,
         "chunk_state_passing_segmented": x + bc + per_chunk + ent + w.s_init * HPN * es + fin,
+        # the same launches doing the cumsum themselves: dt read, cumsum and dt rows
+        # written; unsegmented, CB as well (C read, CB written)
+        "chunk_state_passing_segmented_prep":
+            x + bc + T * H * ex + per_chunk + ent + w.s_init * HPN * es + fin,
+        "chunk_state_passing_prep_bmm": x + 2 * bc + T * H * ex + per_chunk + ent + cache_io + cb,
         "state_carry_and_bmm": fin + S * w.nseg * HPN * ex + S * HPN * es + 2 * bc + cb,
         "chunk_scan": 2 * x + bc + per_chunk + cb + ent,
         "chunk_scan_segmented": 2 * x + bc + per_chunk + cb + ent + carry,
@@ -131,6 +136,8 @@ def launch_flops(name, w: Work):
     cbf = sum(G * N * v * (v + 1) for v in q)            # C B^T, causal
     if name.startswith("chunk_scan"):
         return intra + state_term
+    if name == "chunk_state_passing_prep_bmm":
+        return chunk_state + cbf
     if name.startswith("chunk_state_passing"):
         return chunk_state
     if name in ("bmm_chunk", "bmm_chunk_pairs", "state_carry_and_bmm", "chunk_prep"):
@@ -174,8 +181,12 @@ KERNEL_PATTERNS = [
     (r"bmm_pair_kernel", "bmm_chunk_pairs", PREFILL_SOURCES),
     (r"bmm_kernel", "bmm_chunk", PREFILL_SOURCES),
     (r"state_scan_multi_kernel", "chunk_state_passing_multi", PREFILL_SOURCES),
-    (r"state_scan_fast_kernelILi\d+ELb[01]ELb1E", "chunk_state_passing_segmented",
-     PREFILL_SOURCES),
+    (r"state_scan_fast_kernelILi\d+ELb[01]ELb1ELb1E|state_scan_fast_kernel<\d+, \w+, true, true",
+     "chunk_state_passing_segmented_prep", PREFILL_SOURCES),
+    (r"state_scan_fast_kernelILi\d+ELb[01]ELb0ELb1E|state_scan_fast_kernel<\d+, \w+, false, true",
+     "chunk_state_passing_prep_bmm", PREFILL_SOURCES),
+    (r"state_scan_fast_kernelILi\d+ELb[01]ELb1E|state_scan_fast_kernel<\d+, \w+, true",
+     "chunk_state_passing_segmented", PREFILL_SOURCES),
     (r"state_scan_fast_kernel", "chunk_state_passing", PREFILL_SOURCES),
     (r"state_carry_kernel", "state_carry_and_bmm", PREFILL_SOURCES),
     (r"short_scan_kernel", "short_scan", PREFILL_SOURCES),

@@ -305,18 +305,29 @@ int ssd_chunk_scan(const ssd_problem *p, const void *x, const void *C, const flo
 
 /*
  * The whole prefill: steps 1-5 enqueued on one stream with no host
- * synchronisation (three or four launches; how the steps are grouped depends
+ * synchronisation (one to four launches; how the steps are grouped depends
  * on the shapes), intermediates in the caller's workspace (vLLM PR #61501,
  * sections "Details" and "Claims"; vLLM PR #62922, section "Details").
  * Semantics are those of the five steps composed: every initial state is
  * read as it was before the call even though the call overwrites the slot.
- * For bf16 inputs with headdim 64 and d_state 128, steps 2 and 3 run as
- * ssd_chunk_state_passing (and the workspace holds no chunk states). When
- * such a call has no checkpoints and few (sequence, head) pairs, each
- * sequence's chunk chain is cut into segments that run in parallel and are
- * chained afterwards (the recurrence is linear in its starting state); the
- * workspace then also holds the segments' states. Results agree with the
- * unsegmented path within rounding, not bit for bit.
+ * For bf16 inputs with headdim 64 and d_state 128:
+ *   - steps 2 and 3 run as ssd_chunk_state_passing (and the workspace holds
+ *     no chunk states);
+ *   - with at most 256 sequences, steps 1 and 4 run inside that launch (its
+ *     blocks find their chunks from cu_seqlens and scan dt themselves, and
+ *     leave in the workspace the metadata, cumsum, dt and CB the steps would
+ *     write, bit for bit): the call is two launches, state and chunk scan,
+ *     and its results equal those of ssd_chunk_cumsum, ssd_bmm_chunk,
+ *     ssd_chunk_state_passing and ssd_chunk_scan called one by one, bit for
+ *     bit;
+ *   - with no checkpoints and few (sequence, head) pairs, each sequence's
+ *     chunk chain is cut into segments that run in parallel and are chained
+ *     afterwards by one more launch, which also computes CB (the recurrence
+ *     is linear in its starting state); the workspace then also holds the
+ *     segments' states. Results agree with the unsegmented path within
+ *     rounding, not bit for bit;
+ *   - batches of short sequences (on average at most half a chunk each) run
+ *     as one launch that uses no workspace.
  *   workspace        device buffer of at least ssd_workspace_bytes(p) bytes,
  *                    256-byte aligned; its contents on entry do not matter
  *   checkpoints      [max_chunks,H,P,N] state_dtype or NULL

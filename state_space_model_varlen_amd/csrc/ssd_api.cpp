@@ -366,6 +366,26 @@ static int combined(const ssd_problem *p, const ssd::DtTf &tf, const void *x, co
         seg.C = C;
         seg.CB = cb;
     }
+    // few sequences: steps 1 and 4 inside the state launch (step 4 in the carry
+    // launch when segmented), so the call is two or three launches
+    if (ssd::own_prep_path(d)) {
+        ssd::OwnPrep own;
+        own.dt = dt;
+        own.A = A;
+        own.cu = cu_seqlens;
+        own.tf = tf;
+        own.meta = meta;
+        own.cum = cum;
+        own.dtc = dtc;
+        if (seg.nseg <= 1) {
+            own.C = C;
+            own.CB = cb;
+        }
+        ssd::launch_state_scan(d, x, B, meta, cum, dtc, state_cache, state_indices,
+                               has_initial_state, entering, checkpoints, stream, &seg, &own);
+        ssd::launch_chunk_scan(d, x, C, D, meta, cum, dtc, cb, entering, y, stream, &seg);
+        return launch_status();
+    }
     // steps 1 and 4 in one launch; or (segmented) step 4 beside the carry step;
     // or, with many (chunk, group) pairs, step 4 one pair per block after step 1
     if (seg.nseg > 1) {

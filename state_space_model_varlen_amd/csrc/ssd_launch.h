@@ -96,10 +96,30 @@ struct SegBufs {
 };
 // Segments the combined call uses for these dimensions (1: unsegmented).
 int state_segments(const PrefillDims &d);
+
+// The combined call's state launch doing steps 1 and 4 as well (own_prep_path:
+// the fused state path with at most kOwnPrepMaxSeqs sequences): its state
+// blocks find their chunks from cu_seqlens and scan dt themselves, and publish
+// the metadata, cumsum and dt rows (meta, cum, dtc) that the later launches
+// read; with CB set (unsegmented), one block per (chunk, group) pair after the
+// state blocks computes CB. No cumsum, prep or bmm launch then runs.
+struct OwnPrep {
+    const void *dt = nullptr;
+    const float *A = nullptr;
+    const int32_t *cu = nullptr;
+    DtTf tf;
+    int32_t *meta = nullptr;
+    float *cum = nullptr, *dtc = nullptr;
+    const void *C = nullptr;
+    void *CB = nullptr;
+};
+constexpr int kOwnPrepMaxSeqs = 256;
+bool own_prep_path(const PrefillDims &d);
+
 void launch_state_scan(const PrefillDims &d, const void *x, const void *B, const int32_t *meta,
                        const float *cum, const float *dtc, void *cache, const int32_t *idx,
                        const uint8_t *has_init, void *entering, void *ckpt, void *stream,
-                       const SegBufs *seg = nullptr);
+                       const SegBufs *seg = nullptr, const OwnPrep *own = nullptr);
 void launch_bmm(const PrefillDims &d, const void *B, const void *C, const int32_t *meta, void *CB,
                 void *stream);
 // Whether launch_bmm computes CB with one block per (chunk, group) pair (bf16,

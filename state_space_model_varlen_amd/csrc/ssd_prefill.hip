@@ -191,6 +191,98 @@ __device__ __forceinline__ void publish_chunk(int S, int c, const ChunkInfo &ci,
     m[2] = ci.len;
 }
 
+// The same chunk counts for one wave alone, for kernels that run before any
+// metadata exists (the combined call's state launch): sequences are taken 64 at
+// a time, so the cost grows with S (callers keep S small). Results are the same
+// in every lane and are returned through readfirstlane, so that the compiler
+// keeps them in scalar registers: a buffer resource built from a value it takes
+// for a per-lane one makes every load through it a loop over lanes.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Sequence base + lane: chunk count, clamped token range [a, b), first-chunk length.
+struct LaneSeq {
+    int cnt, a, b, f;
+};
+__device__ __forceinline__ LaneSeq lane_seq(int T, int S, int Q, const int32_t *__restrict__ cu,
+                                            const int32_t *__restrict__ prefix, int base, int lane)
+{
+    LaneSeq r{0, 0, 0, Q};
+    const int s = base + lane;
+    if (s < S) {
+        r.a = clampi(cu[s], 0, T);
+        r.b = clampi(cu[s + 1], 0, T);
+        const int L = r.b > r.a ? r.b - r.a : 0;
+        r.f = first_chunk_len(Q, prefix, s);
+        r.cnt = L == 0 ? 0 : (L <= r.f ? 1 : 1 + (L - r.f + Q - 1) / Q);
+    }
+    return r;
+}
+
+// Sequence s: its first chunk index (not clamped), chunk count, clamped token
+// range and first-chunk length; also the batch's total chunk count.
+struct SeqSpan {
+    int c0, cnt, a, b, f, total;
+};
+__device__ __forceinline__ SeqSpan wave_seq_span(int T, int S, int Q, const int32_t *__restrict__ cu,
+                                                 const int32_t *__restrict__ prefix, int s, int lane)
+{
+    SeqSpan r{0, 0, 0, 0, Q, 0};
+    int running = 0;
+    for (int base = 0; base < S; base += kWave) {
+        const LaneSeq ls = lane_seq(T, S, Q, cu, prefix, base, lane);
+        const int incl = wave_inclusive_sum_int(ls.cnt, lane);
+        if (s >= base && s < base + kWave) {   // (uniform: s is the same in every lane)
+            const int src = s - base;
+            r.c0 = running + __shfl(incl - ls.cnt, src);
+            r.cnt = __shfl(ls.cnt, src);
+            r.a = __shfl(ls.a, src);
+            r.b = __shfl(ls.b, src);
+            r.f = __shfl(ls.f, src);
+        }
+        running += __shfl(incl, kWave - 1);
+    }
+    r.total = uniform(running);
+    r.c0 = uniform(r.c0);
+    r.cnt = uniform(r.cnt);
+    r.a = uniform(r.a);
+    r.b = uniform(r.b);
+    r.f = uniform(r.f);
+    return r;
+}
+
+// Chunk c: (sequence, first token, token count), sequence -1 past the last chunk.
+__device__ __forceinline__ ChunkInfo wave_find_chunk(int T, int S, int Q,
+                                                     const int32_t *__restrict__ cu,
+                                                     const int32_t *__restrict__ prefix, int c,
+                                                     int lane)
+{
+    ChunkInfo ci;
+    ci.seq = -1;
+    ci.start = 0;
+    ci.len = 0;
+    int running = 0;
+    for (int base = 0; base < S; base += kWave) {
+        const LaneSeq ls = lane_seq(T, S, Q, cu, prefix, base, lane);
+        const int incl = wave_inclusive_sum_int(ls.cnt, lane);
+        const int first = running + incl - ls.cnt;
+        const unsigned long long hit = __ballot(ls.cnt > 0 && c >= first && c < first + ls.cnt);
+        if (hit) {
+            const int src = __builtin_ctzll(hit);
+            const int k = c - __shfl(first, src), f = __shfl(ls.f, src);
+            const int a = __shfl(ls.a, src), b = __shfl(ls.b, src);
+            ci.seq = base + src;
+            ci.start = a + (k == 0 ? 0 : f + (k - 1) * Q);
+            const int cap = k == 0 ? f : Q;
+            ci.len = b - ci.start < cap ? b - ci.start : cap;
+        }
+        running += __shfl(incl, kWave - 1);
+    }
+    ci.seq = uniform(ci.seq);
+    ci.start = uniform(ci.start);
+    ci.len = uniform(ci.len);
+    return ci;
+}
+
 template <typename TIn>
 __global__ __launch_bounds__(256) void chunk_cumsum_kernel(
     int T, int S, int H, int Q, int max_chunks, const TIn *__restrict__ dt,
@@ -539,19 +631,14 @@ __global__ __launch_bounds__(256) void bmm_kernel(int S, int G, int Q, int max_c
 constexpr int kCbLDB = 136;       // B row pitch in LDS (bf16): 68 dwords, conflict-free b128 reads
 constexpr int kCbPairMin = 128;   // pairs from which the per-pair kernel is used
 
-template <int Q>
-__global__ __launch_bounds__(2 * Q) void bmm_pair_kernel(int S, int G,
-                                                         const bf16 *__restrict__ B,
-                                                         const bf16 *__restrict__ C,
-                                                         const int32_t *__restrict__ meta,
-                                                         bf16 *__restrict__ CB)
+// The pair body for a block of NT >= 2 Q threads (waves past Q / 32 only take
+// part in the barrier); bs: Q x kCbLDB bf16 of LDS.
+template <int Q, int NT>
+__device__ __forceinline__ void cb_pair(int G, int c, int g, const ChunkInfo &ci,
+                                        const bf16 *__restrict__ B, const bf16 *__restrict__ C,
+                                        bf16 *__restrict__ CB, bf16 *bs)
 {
-    constexpr int N = 128, NT = 2 * Q, KV = Q * (N / 8) / NT;
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    bf16 *bs = reinterpret_cast<bf16 *>(smem);   // [Q][kCbLDB]
-    const int c = blockIdx.x / G, g = blockIdx.x - c * G;
-    const ChunkInfo ci = chunk_info(meta, S, c);
-    if (ci.len <= 0) return;
+    constexpr int N = 128, KV = Q * (N / 8) / NT > 0 ? Q * (N / 8) / NT : 1;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, kg = lane >> 4;
     const int len = ci.len;
@@ -580,6 +667,7 @@ __global__ __launch_bounds__(2 * Q) void bmm_pair_kernel(int S, int G,
         *reinterpret_cast<uint4 *>(bs + (u >> 4) * kCbLDB + 8 * (u & 15)) = bv[k];
     }
     __syncthreads();
+    if (wave >= Q / 32) return;   // (no row tiles: the C loads above read nothing)
     bf16 *cbc = CB + ((int64_t)c * G + g) * Q * Q;
     const int ntiles = (len + 15) / 16;
 #pragma unroll
@@ -606,6 +694,20 @@ __global__ __launch_bounds__(2 * Q) void bmm_pair_kernel(int S, int G,
             store4<bf16>(cbc + cb_frag_offset(Q, i, jc), v4);
         }
     }
+}
+
+template <int Q>
+__global__ __launch_bounds__(2 * Q) void bmm_pair_kernel(int S, int G,
+                                                         const bf16 *__restrict__ B,
+                                                         const bf16 *__restrict__ C,
+                                                         const int32_t *__restrict__ meta,
+                                                         bf16 *__restrict__ CB)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int c = blockIdx.x / G, g = blockIdx.x - c * G;
+    const ChunkInfo ci = chunk_info(meta, S, c);
+    if (ci.len <= 0) return;
+    cb_pair<Q, 2 * Q>(G, c, g, ci, B, C, CB, reinterpret_cast<bf16 *>(smem));
 }
 
 bool cb_by_pair(const PrefillDims &d)
@@ -921,12 +1023,24 @@ constexpr int kScanLDB = kScanNSL + 16;
 template <int Q> struct StateScanRegs {
     static constexpr int kXV = (Q * 8 + 511) / 512;    // x vectors (8 bf16) per thread
     static constexpr int kBV = (Q * 8 + 511) / 512;    // B vectors per thread (8 per row)
+    static constexpr int kE = (Q + kWave - 1) / kWave; // dt positions per lane of wave 0
     uint4 x[kXV], b[kBV];
     float cm[kBV], dt[kBV];                            // cum and dt of the B rows
     float cl;                                          // cum at the chunk's last token
+    uint32_t dr[kE];                                   // raw bf16 dt (own-prep mode)
 };
 
-template <int Q, bool CKPT, bool SEG, typename TS>
+// With OWN (the combined call, few sequences) the same launch also does step 1
+// and, unsegmented, step 4, so that neither needs a launch of its own:
+//   - every state block finds its sequence's chunks from cu_seqlens and scans
+//     dt * A_h over each chunk itself (wave 0, as the cumsum kernel does, in
+//     the same order: the same cum values bit for bit) into the unused pad
+//     columns of its LDS x rows, one chunk ahead;
+//   - the blocks of column slice 0 publish what the later launches read: the
+//     cumsum and dt rows of their head, and (head 0) the chunk metadata;
+//   - own.CB set: max_chunks G more blocks after the state blocks compute CB,
+//     one (chunk, group) pair each, in the CUs the short chains leave free.
+template <int Q, bool CKPT, bool SEG, bool OWN, typename TS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
 void state_scan_fast_kernel(
     int S, int H, int G, int max_chunks, int num_slots, const bf16 *__restrict__ x,
@@ -934,13 +1048,16 @@ void state_scan_fast_kernel(
     const float *__restrict__ dtc, TS *cache, const int32_t *__restrict__ idx,
     const uint8_t *__restrict__ has_init, bf16 *__restrict__ entering, TS *__restrict__ ckpt,
     SrCtx sr, int nseg, float *__restrict__ seg_fin, float *__restrict__ seg_L,
-    float *__restrict__ seg_F, int32_t *__restrict__ seg_I, int lpt)
+    float *__restrict__ seg_F, int32_t *__restrict__ seg_I, int lpt, OwnPrep own, int T,
+    const int32_t *__restrict__ prefix)
 {
     constexpr int P = 64, N = 128, NSL = kScanNSL, NS = N / NSL;
     constexpr int LDX = kScanLDX, LDB = kScanLDB;
+    constexpr int E = StateScanRegs<Q>::kE;
+    static_assert(LDX >= P + 2, "the cum / dt pad of an x row");
     typedef StateScanRegs<Q> Regs;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    bf16 *xs = reinterpret_cast<bf16 *>(smem);   // [Q][LDX]  x_t
+    bf16 *xs = reinterpret_cast<bf16 *>(smem);   // [Q][LDX]  x_t (OWN: cum_t, dt_t at column P)
     bf16 *bs = xs + Q * LDX;                     // [Q][LDB]  w_t B_t (slice columns)
 
     // logical order (head, segment of sequence, column slice): each XCD takes a
@@ -948,7 +1065,19 @@ void state_scan_fast_kernel(
     // long and short sequences gives every XCD the same chain lengths, and the
     // heads that share a B group sit side by side on one XCD
     const int nsg = SEG ? nseg : 1;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+    if constexpr (OWN) {
+        const int nstate = S * nsg * H * NS;
+        if ((int)blockIdx.x >= nstate) {
+            // CB of one (chunk, group) pair, through this kernel's LDS
+            const int pr = (int)blockIdx.x - nstate, c = pr / G, g = pr - c * G;
+            const ChunkInfo ci = wave_find_chunk(T, S, Q, own.cu, prefix, c, lane);
+            if (ci.len > 0)   // (the same in every wave)
+                cb_pair<Q, 512>(G, c, g, ci, B, static_cast<const bf16 *>(own.C),
+                                static_cast<bf16 *>(own.CB), xs);
+            return;
+        }
+    }
     int q, h, s, b, sb;
     if (!SEG && lpt) {
         // Longest chain first (few sequences, heads a multiple of 8): XCD x owns
@@ -961,8 +1090,16 @@ void state_scan_fast_kernel(
         const int r = slot / (hx * NS), rem = slot - r * (hx * NS);
         h = xcd * hx + rem / NS;
         q = rem - (rem / NS) * NS;
-        const int sl = lane < S ? lane : S - 1;
-        const int cnt = meta[sl + 1] - meta[sl];
+        int cnt;
+        if constexpr (OWN) {
+            // the clamped counts the metadata would hold (S <= 64 here)
+            const LaneSeq ls = lane_seq(T, S, Q, own.cu, prefix, 0, lane);
+            const int incl = wave_inclusive_sum_int(ls.cnt, lane), excl = incl - ls.cnt;
+            cnt = (incl < max_chunks ? incl : max_chunks) - (excl < max_chunks ? excl : max_chunks);
+        } else {
+            const int sl = lane < S ? lane : S - 1;
+            cnt = meta[sl + 1] - meta[sl];
+        }
         int rank = 0;
         for (int t = 0; t < S; ++t) {
             const int ct = __shfl(cnt, t);
@@ -992,14 +1129,31 @@ void state_scan_fast_kernel(
     // every per-sequence value is requested before any is used (one memory
     // latency): chunk range, token range, slot, has-initial flag
     const int tokoff = (S + 1) + 3 * max_chunks;
-    int c0 = meta[s], c1 = meta[s + 1];
-    const int first = meta[tokoff + s];
-    int end = meta[tokoff + s + 1];
-    int fcl = meta[tokoff + (S + 1) + s];   // length of the first chunk (Q unless aligned)
+    int c0, c1, first, end, fcl, total = 0;   // fcl: first chunk's length (Q unless aligned)
+    SrKey srk;
+    float Ah = 0.0f, bh = 0.0f;
+    if constexpr (OWN) {
+        const SeqSpan sp = wave_seq_span(T, S, Q, own.cu, prefix, s, lane);
+        c0 = sp.c0;
+        c1 = sp.c0 + sp.cnt;
+        first = sp.a;
+        end = sp.b;
+        fcl = sp.f;
+        total = sp.total;
+        srk = sr_key_checked(sr);
+        Ah = own.A[h];
+        bh = own.tf.bias ? own.tf.bias[h] : 0.0f;
+    } else {
+        c0 = meta[s];
+        c1 = meta[s + 1];
+        first = meta[tokoff + s];
+        end = meta[tokoff + s + 1];
+        fcl = meta[tokoff + (S + 1) + s];
+        srk = sr_key(sr, meta);
+    }
     const int slot = idx[s];
     // (with no flag array, a byte of idx stands in and the flag is ignored)
     const uint8_t hflag = (has_init != nullptr ? has_init : reinterpret_cast<const uint8_t *>(idx))[s];
-    const SrKey srk = sr_key(sr, meta);
     __builtin_amdgcn_sched_barrier(0);
     c0 = c0 < max_chunks ? c0 : max_chunks;
     c1 = c1 < max_chunks ? c1 : max_chunks;
@@ -1019,6 +1173,30 @@ void state_scan_fast_kernel(
     // chunk c of the sequence: tokens first + off(c) .., at most cap(c) of them
     auto chunk_off = [&](int c) { return c == c0 ? 0 : fcl + (c - c0 - 1) * Q; };
     auto chunk_cap = [&](int c) { return c == c0 ? fcl : Q; };
+    if constexpr (OWN) {
+        // the per-sequence metadata (chunk_cu, clamped cu_seqlens, first-chunk
+        // lengths), and after the last sequence the chunk slots no chunk fills
+        if (h == 0 && q == 0 && b == 0) {
+            if (tid == 0) {
+                own.meta[s] = c0;
+                own.meta[tokoff + s] = first;
+                own.meta[tokoff + (S + 1) + s] = fcl;
+                if (s == S - 1) {
+                    own.meta[S] = total < max_chunks ? total : max_chunks;
+                    own.meta[tokoff + S] = end;
+                }
+            }
+            if (s == S - 1) {
+                for (int cc = (total < max_chunks ? total : max_chunks) + tid; cc < max_chunks;
+                     cc += 512) {
+                    int32_t *m = own.meta + (S + 1) + 3 * cc;
+                    m[0] = -1;
+                    m[1] = 0;
+                    m[2] = 0;
+                }
+            }
+        }
+    }
     const bool slot_ok = slot >= 0 && slot < num_slots;
     TS *cslot = cache + ((int64_t)(slot_ok ? slot : 0) * H + h) * PN + run;
 
@@ -1044,34 +1222,113 @@ void state_scan_fast_kernel(
         to[k] = u < Q * 8 ? (uint32_t)(u >> 3) * 4 : 0xfffffff0u;
     }
 
+    // chunk c clamped to the block's range: its first token, and its token
+    // count (0 past the block's last chunk)
+    auto chunk_at = [&](int c, int &st) {
+        const bool any = c < hi;
+        c = c < hi ? c : hi - 1;
+        c = c > lo ? c : lo;
+        st = first + chunk_off(c);
+        const int len = end - st < chunk_cap(c) ? end - st : chunk_cap(c);
+        return any ? len : 0;
+    };
     // Loads of chunk c's tiles through buffer resources that end at the chunk's
     // last row: rows past it read as zero. Past the last chunk (and for a
     // sequence with no chunk) every resource is empty and nothing is read.
     auto fetch = [&](Regs &R, int c) {
         const bool any = c < hi;
+        int st;
+        const int len = chunk_at(c, st);
         c = c < hi ? c : hi - 1;
         c = c > lo ? c : lo;
-        const int st = first + chunk_off(c);
-        int len = end - st < chunk_cap(c) ? end - st : chunk_cap(c);
-        len = any ? len : 0;
         const rsrc_t rx = make_rsrc(x + ((int64_t)st * H + h) * P,
                                     any ? (uint32_t)(len - 1) * xrow + P * 2 : 0u);
         const rsrc_t rb = make_rsrc(B + ((int64_t)st * G + g) * N + n0,
                                     any ? (uint32_t)(len - 1) * brow + NSL * 2 : 0u);
-        const int64_t row = ((int64_t)h * max_chunks + c) * Q;
-        const rsrc_t rc = make_rsrc(cum + row, any ? (uint32_t)len * 4 : 0u);
-        const rsrc_t rd = make_rsrc(dtc + row, any ? (uint32_t)len * 4 : 0u);
-        // (the cumsum at the chunk's last token first: a vector load, since a
-        // scalar one would share its wait counter with the LDS reads of the
-        // MFMA phase and stall them on global latency)
-        R.cl = buf_ldf(rc, (uint32_t)(len - 1) * 4);
+        if constexpr (OWN) {
+            // raw dt of the chunk for wave 0 first (its scan runs before the
+            // x and B tiles are needed); the other waves' resource is empty
+            const rsrc_t rt = make_rsrc(static_cast<const bf16 *>(own.dt) + (int64_t)st * H + h,
+                                        any && wave == 0 ? (uint32_t)(len - 1) * H * 2 + 2 : 0u);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                R.dr[e] = __builtin_amdgcn_raw_buffer_load_b16(rt, (lane * E + e) * H * 2, 0, 0);
+        } else {
+            const int64_t row = ((int64_t)h * max_chunks + c) * Q;
+            const rsrc_t rc = make_rsrc(cum + row, any ? (uint32_t)len * 4 : 0u);
+            // (the cumsum at the chunk's last token first: a vector load, since a
+            // scalar one would share its wait counter with the LDS reads of the
+            // MFMA phase and stall them on global latency)
+            R.cl = buf_ldf(rc, (uint32_t)(len - 1) * 4);
+        }
 #pragma unroll
         for (int k = 0; k < Regs::kXV; ++k) R.x[k] = buf_ld16(rx, xo[k]);
 #pragma unroll
         for (int k = 0; k < Regs::kBV; ++k) {
             R.b[k] = buf_ld16(rb, bo[k]);
-            R.cm[k] = buf_ldf(rc, to[k]);
-            R.dt[k] = buf_ldf(rd, to[k]);
+            if constexpr (!OWN) {
+                const int64_t row = ((int64_t)h * max_chunks + c) * Q;
+                const rsrc_t rc = make_rsrc(cum + row, any ? (uint32_t)len * 4 : 0u);
+                const rsrc_t rd = make_rsrc(dtc + row, any ? (uint32_t)len * 4 : 0u);
+                R.cm[k] = buf_ldf(rc, to[k]);
+                R.dt[k] = buf_ldf(rd, to[k]);
+            }
+        }
+    };
+
+    // OWN: wave 0 scans dt * A_h over chunk c (fetched into R) into the pad
+    // columns of the x rows (cum_t, dt_t as two floats at column P of row t),
+    // positions past the chunk's end holding the last cum and dt 0; slice 0
+    // publishes the rows, head 0 the chunk's (sequence, start, length).
+    auto scan_chunk = [&](const Regs &R, int c) {
+        if (wave != 0) return;
+        int st;
+        const int len = chunk_at(c, st);
+        float vals[4], loc[4], run = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vals[e] = e < E ? __uint_as_float(R.dr[e < E ? e : 0] << 16) : 0.0f;
+        if (own.tf.on) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vals[e] = dt_transform(own.tf, vals[e], bh);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = lane * E + e;
+            vals[e] = (e < E && i < len) ? vals[e] : 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            run += vals[e] * Ah;
+            loc[e] = run;
+        }
+        const float incl = wave_inclusive_sum(run, lane);
+        const float off = incl - run;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int i = lane * E + e;
+            if (i < Q) {
+                float2 cd;
+                cd.x = off + loc[e];
+                cd.y = vals[e];
+                *reinterpret_cast<float2 *>(xs + i * LDX + P) = cd;
+            }
+        }
+        if (q == 0 && c < hi) {
+            const int64_t row = ((int64_t)h * max_chunks + c) * Q;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int i = lane * E + e;
+                if (i < Q) {
+                    own.cum[row + i] = off + loc[e];
+                    own.dtc[row + i] = vals[e];
+                }
+            }
+            if (h == 0 && lane == 0) {
+                int32_t *m = own.meta + (S + 1) + 3 * c;
+                m[0] = s;
+                m[1] = st;
+                m[2] = len;
+            }
         }
     };
 
@@ -1084,6 +1341,10 @@ void state_scan_fast_kernel(
         const int st = first + chunk_off(c);
         const int len = end - st < chunk_cap(c) ? end - st : chunk_cap(c);
         __syncthreads();   // the previous chunk's MFMA reads of xs / bs are done
+        // (OWN: the cumsum at the chunk's last token from its x row's pad; an
+        // empty chunk's pads hold zeros)
+        const float cl = OWN ? reinterpret_cast<const float *>(xs + (len > 0 ? len - 1 : 0) * LDX + P)[0]
+                             : R.cl;
 #pragma unroll
         for (int k = 0; k < Regs::kXV; ++k) {
             const int u = tid + 512 * k;
@@ -1094,7 +1355,16 @@ void state_scan_fast_kernel(
             const int u = tid + 512 * k;
             if (u < Q * 8) {
                 const int t = u >> 3;
-                const float w = t < len ? __expf(R.cl - R.cm[k]) * R.dt[k] : 0.0f;
+                float cmt, dtt;
+                if constexpr (OWN) {
+                    const float2 cd = *reinterpret_cast<const float2 *>(xs + t * LDX + P);
+                    cmt = cd.x;
+                    dtt = cd.y;
+                } else {
+                    cmt = R.cm[k];
+                    dtt = R.dt[k];
+                }
+                const float w = t < len ? __expf(cl - cmt) * dtt : 0.0f;
                 const uint32_t w4[4] = {R.b[k].x, R.b[k].y, R.b[k].z, R.b[k].w};
                 float f[8];
 #pragma unroll
@@ -1105,13 +1375,13 @@ void state_scan_fast_kernel(
                 Vec16<bf16>::store(bs + t * LDB + 8 * (u & 7), f);
             }
         }
-        const float decay = __expf(R.cl);
+        const float decay = __expf(cl);
         if constexpr (SEG) {
             if (live && q == 0 && tid == 0) {
                 seg_F[(int64_t)h * max_chunks + c] = F;
                 if (h == 0) seg_I[c] = b > 0 ? sb : -1;
             }
-            F += R.cl;
+            F += cl;
         }
         fetch(R, c + 1);
         __syncthreads();
@@ -1160,6 +1430,7 @@ void state_scan_fast_kernel(
                 }
             }
         }
+        if constexpr (OWN) scan_chunk(R, c + 1);   // (read after the next step's first barrier)
     };
 
     // The first chunk's tiles are requested together with the initial state; the
@@ -1168,6 +1439,7 @@ void state_scan_fast_kernel(
     Regs R;
     fetch(R, lo);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (OWN) scan_chunk(R, lo);
     const bool read_init = slot_ok && has_init != nullptr && hflag != 0 && b == 0;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -2453,14 +2725,15 @@ void launch_state_passing(const PrefillDims &d, const float *states, const float
 constexpr int64_t kMultiMinItems = 1024;   // items from which the multi-item kernel runs
 constexpr int64_t kMultiBlocks = 512;      // its blocks: two per CU
 
-template <int Q, bool CKPT, bool SEG, typename TS>
+template <int Q, bool CKPT, bool SEG, bool OWN, typename TS>
 static void launch_state_scan_k(const PrefillDims &d, const void *x, const void *B,
                                 const int32_t *meta, const float *cum, const float *dtc,
                                 void *cache, const int32_t *idx, const uint8_t *has_init,
-                                void *entering, void *ckpt, const SegBufs &seg, hipStream_t st)
+                                void *entering, void *ckpt, const SegBufs &seg,
+                                const OwnPrep &own, hipStream_t st)
 {
     const size_t smem = (size_t)Q * (kScanLDX + kScanLDB) * sizeof(bf16);
-    if constexpr (!SEG) {
+    if constexpr (!SEG && !OWN) {
         // batches of short sequences (on average at most half a chunk each) with
         // many items: persistent blocks, two per CU, several items each
         const int64_t items = (int64_t)d.S * d.H * (128 / kScanNSL);
@@ -2478,17 +2751,21 @@ static void launch_state_scan_k(const PrefillDims &d, const void *x, const void 
         }
     }
     static size_t raised = 0;
-    allow_lds(reinterpret_cast<const void *>(&state_scan_fast_kernel<Q, CKPT, SEG, TS>), smem,
+    allow_lds(reinterpret_cast<const void *>(&state_scan_fast_kernel<Q, CKPT, SEG, OWN, TS>), smem,
               raised);
     const int nseg = SEG ? seg.nseg : 1;
-    const unsigned nblk = (unsigned)((int64_t)d.S * nseg * d.H * (128 / kScanNSL));
+    const int64_t nstate = (int64_t)d.S * nseg * d.H * (128 / kScanNSL);
+    // OWN, unsegmented: the CB blocks, one per (chunk, group) pair
+    const int64_t ncb = OWN && !SEG && own.CB ? (int64_t)d.max_chunks * d.G : 0;
     // longest chain first: few sequences (one wave ranks them), heads a multiple of 8
     const int lpt = !SEG && d.S > 1 && d.S <= 64 && d.H % kXcds == 0;
-    SSD_LAUNCH(d, SEG ? "chunk_state_passing_segmented" : "chunk_state_passing", (state_scan_fast_kernel<Q, CKPT, SEG, TS>), dim3(nblk), dim3(512), smem,
+    const char *name = OWN ? (SEG ? "chunk_state_passing_segmented_prep" : "chunk_state_passing_prep_bmm")
+                           : (SEG ? "chunk_state_passing_segmented" : "chunk_state_passing");
+    SSD_LAUNCH(d, name, (state_scan_fast_kernel<Q, CKPT, SEG, OWN, TS>), dim3((unsigned)(nstate + ncb)), dim3(512), smem,
                        st, d.S, d.H, d.G, d.max_chunks, d.num_slots, static_cast<const bf16 *>(x),
                        static_cast<const bf16 *>(B), meta, cum, dtc, static_cast<TS *>(cache), idx,
                        has_init, static_cast<bf16 *>(entering), static_cast<TS *>(ckpt), d.sr,
-                       nseg, seg.fin, seg.L, seg.F, seg.I, lpt);
+                       nseg, seg.fin, seg.L, seg.F, seg.I, lpt, own, d.T, d.prefix);
     if constexpr (SEG) {
         const int PN = 64 * 128;
         const int ncar = d.S * d.H * (PN / 1024);
@@ -2501,34 +2778,51 @@ static void launch_state_scan_k(const PrefillDims &d, const void *x, const void 
     }
 }
 
+template <int Q, bool OWN, typename TS>
+static void launch_state_scan_o(const PrefillDims &d, const void *x, const void *B,
+                                const int32_t *meta, const float *cum, const float *dtc,
+                                void *cache, const int32_t *idx, const uint8_t *has_init,
+                                void *entering, void *ckpt, const SegBufs *seg,
+                                const OwnPrep &own, hipStream_t st)
+{
+    if (ckpt)
+        launch_state_scan_k<Q, true, false, OWN, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init,
+                                                     entering, ckpt, SegBufs(), own, st);
+    else if (seg && seg->nseg > 1)
+        launch_state_scan_k<Q, false, true, OWN, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init,
+                                                     entering, ckpt, *seg, own, st);
+    else
+        launch_state_scan_k<Q, false, false, OWN, TS>(d, x, B, meta, cum, dtc, cache, idx,
+                                                      has_init, entering, ckpt, SegBufs(), own, st);
+}
+
 template <int Q, typename TS>
 static void launch_state_scan_q(const PrefillDims &d, const void *x, const void *B,
                                 const int32_t *meta, const float *cum, const float *dtc,
                                 void *cache, const int32_t *idx, const uint8_t *has_init,
-                                void *entering, void *ckpt, const SegBufs *seg, hipStream_t st)
+                                void *entering, void *ckpt, const SegBufs *seg,
+                                const OwnPrep *own, hipStream_t st)
 {
-    if (ckpt)
-        launch_state_scan_k<Q, true, false, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init,
-                                                entering, ckpt, SegBufs(), st);
-    else if (seg && seg->nseg > 1)
-        launch_state_scan_k<Q, false, true, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init,
-                                                entering, ckpt, *seg, st);
+    if (own)
+        launch_state_scan_o<Q, true, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering,
+                                         ckpt, seg, *own, st);
     else
-        launch_state_scan_k<Q, false, false, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init,
-                                                 entering, ckpt, SegBufs(), st);
+        launch_state_scan_o<Q, false, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering,
+                                          ckpt, seg, OwnPrep(), st);
 }
 
 template <typename TS>
 static void launch_state_scan_t(const PrefillDims &d, const void *x, const void *B,
                                 const int32_t *meta, const float *cum, const float *dtc,
                                 void *cache, const int32_t *idx, const uint8_t *has_init,
-                                void *entering, void *ckpt, const SegBufs *seg, hipStream_t st)
+                                void *entering, void *ckpt, const SegBufs *seg,
+                                const OwnPrep *own, hipStream_t st)
 {
     switch (d.Q) {
-    case 32: launch_state_scan_q<32, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, seg, st); break;
-    case 64: launch_state_scan_q<64, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, seg, st); break;
-    case 128: launch_state_scan_q<128, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, seg, st); break;
-    default: launch_state_scan_q<256, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, seg, st); break;
+    case 32: launch_state_scan_q<32, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, seg, own, st); break;
+    case 64: launch_state_scan_q<64, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, seg, own, st); break;
+    case 128: launch_state_scan_q<128, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, seg, own, st); break;
+    default: launch_state_scan_q<256, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, seg, own, st); break;
     }
 }
 
@@ -2548,19 +2842,24 @@ int state_segments(const PrefillDims &d)
     return n > 1 ? (int)n : 1;
 }
 
+bool own_prep_path(const PrefillDims &d)
+{
+    return use_fast(d) && d.S > 0 && d.S <= kOwnPrepMaxSeqs;
+}
+
 void launch_state_scan(const PrefillDims &d, const void *x, const void *B, const int32_t *meta,
                        const float *cum, const float *dtc, void *cache, const int32_t *idx,
                        const uint8_t *has_init, void *entering, void *ckpt, void *stream,
-                       const SegBufs *seg)
+                       const SegBufs *seg, const OwnPrep *own)
 {
     if (d.S <= 0) return;
     hipStream_t st = as_stream(stream);
     if (d.state_f16)
-        launch_state_scan_t<f16>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, seg, st);
+        launch_state_scan_t<f16>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, seg, own, st);
     else if (d.state_bf16)
-        launch_state_scan_t<bf16>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, seg, st);
+        launch_state_scan_t<bf16>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, seg, own, st);
     else
-        launch_state_scan_t<float>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, seg, st);
+        launch_state_scan_t<float>(d, x, B, meta, cum, dtc, cache, idx, has_init, entering, ckpt, seg, own, st);
 }
 
 constexpr int kShortSub = 32;   // tokens per sub-chunk of the short-sequence kernel (32 measured

@@ -47,6 +47,9 @@ def test_launch_bytes_and_flops_of_the_layer_prefill():
         x + bc + per_chunk + entering + fins
     assert bench.launch_bytes("state_carry_and_bmm", w) == \
         fins + 3 * H * P * N * 2 + final + 2 * bc + cb
+    # the state launch doing the cumsum itself: dt read, cumsum and dt rows written
+    assert bench.launch_bytes("chunk_state_passing_segmented_prep", w) == \
+        x + bc + T * H * 2 + per_chunk + entering + fins
     # flops: causal intra-chunk 80 * 64 * 256 * 257 per chunk plus the state term
     # 2 * 80 * 64 * 128 * 256 per chunk: 10.76 GFLOP
     assert bench.launch_flops("chunk_scan_segmented", w) == \
@@ -59,9 +62,17 @@ def test_kernel_names_map_to_launches():
     n = lambda k: bench.launch_name(k)[0]
     assert n("_ZN3ssd22chunk_scan_fast_kernelILi256ELb1EEEviii") == "chunk_scan_segmented"
     assert n("_ZN3ssd22chunk_scan_fast_kernelILi256ELb0EEEviii") == "chunk_scan"
-    assert n("_ZN3ssd22state_scan_fast_kernelILi256ELb0ELb1EfEEvii") == \
+    assert n("_ZN3ssd22state_scan_fast_kernelILi256ELb0ELb1ELb0EfEEvii") == \
         "chunk_state_passing_segmented"
-    assert n("_ZN3ssd22state_scan_fast_kernelILi256ELb1ELb0EfEEvii") == "chunk_state_passing"
+    assert n("_ZN3ssd22state_scan_fast_kernelILi256ELb1ELb0ELb0EfEEvii") == "chunk_state_passing"
+    assert n("_ZN3ssd22state_scan_fast_kernelILi256ELb0ELb1ELb1EfEEvii") == \
+        "chunk_state_passing_segmented_prep"
+    assert n("_ZN3ssd22state_scan_fast_kernelILi256ELb1ELb0ELb1EfEEvii") == \
+        "chunk_state_passing_prep_bmm"
+    assert n("void ssd::state_scan_fast_kernel<256, true, false, true, float>(int") == \
+        "chunk_state_passing_prep_bmm"
+    assert n("void ssd::state_scan_fast_kernel<128, false, true, false, bf16>(int") == \
+        "chunk_state_passing_segmented"
     assert n("void ssd::state_carry_kernel<float>(int, int") == "state_carry_and_bmm"
     assert n("_ZN3ssd19chunk_cumsum_kernelIDF16bEEvii") == "chunk_cumsum"
     assert n("_ZN3ssd15bmm_pair_kernelILi256EEEvii") == "bmm_chunk_pairs"

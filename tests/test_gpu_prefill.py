@@ -389,11 +389,103 @@ def test_launch_trace_names_and_times_every_launch():
         torch.cuda.synchronize()
         outs.append((y.cpu(), cache.cpu()))
     d = tr.durations_us()
-    assert [n for n, _ in d] == ["chunk_cumsum", "chunk_state_passing_segmented",
-                                 "state_carry_and_bmm", "chunk_scan_segmented"]
+    assert [n for n, _ in d] == ["chunk_state_passing_segmented_prep", "state_carry_and_bmm",
+                                 "chunk_scan_segmented"]
     assert all(us > 0 for _, us in d), d
     assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
     assert torch.equal(outs[0][1], outs[1][1])
+
+
+OWN_CASES = [
+    # seqlens, H, G, Q, state dtype, checkpoints: segmented or not, longest chain
+    # first (S <= 64, H a multiple of 8) or not, sequences counted in several waves
+    # of 64 (S > 64), empty sequences, a 1-token chunk
+    ((40, 300, 700, 5), 16, 2, 128, F32, True),
+    ((600, 32, 1600), 8, 1, 256, BF16, True),
+    ((100, 900, 0, 20, 400), 64, 8, 256, F32, False),
+    ((1500,), 8, 1, 128, F32, False),
+    ((257, 0, 3, 129), 6, 3, 64, BF16, False),
+    (tuple(20 + (37 * i) % 280 for i in range(70)), 8, 2, 64, F32, True),
+]
+
+
+@pytest.mark.parametrize("case", OWN_CASES, ids=lambda c: f"S{len(c[0])}_H{c[1]}_Q{c[3]}_"
+                         f"{str(c[4])[6:]}_{'ckpt' if c[5] else 'nockpt'}")
+def test_state_launch_with_own_prep_matches_steps_bitwise(case):
+    """The combined call (few sequences) runs the cumsum and CB inside its state
+    launch. What that launch publishes (chunk metadata, cumsum and dt rows, CB)
+    equals, bit for bit, what ssd_chunk_cumsum and ssd_bmm_chunk write; unsegmented,
+    so do y, the final states, the checkpoints and the entering states of the
+    step-by-step chain (the same kernels and arithmetic after the cumsum)."""
+    lens, H, G, Q, ts, ckpt = case
+    P, N = 64, 128
+    S, T = len(lens), sum(lens)
+    inp = sy.random_problem(970 + OWN_CASES.index(case), lens, H, P, N, G, Q, BF16, ts,
+                            num_slots=S + 2, has_initial=[s % 3 != 1 for s in range(S)])
+    cache = _cache_with_states(inp, S + 2, ts)
+    ssd = _ssd()
+    p = ssd.make_problem(T, S, H, P, N, G, Q, S + 2, BF16, ts)
+    mc = ssd.max_chunks(p)
+    x, dt, A, B, C, D = (t.to(DEV) for t in (inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D))
+    cu, idx, hi = inp.cu_seqlens.to(DEV), inp.state_indices.to(DEV), inp.has_initial.to(DEV)
+
+    # (both sides' buffers cleared: CB tiles past a chunk's rows are never written)
+    ws = ssd.alloc_workspace(p, DEV).zero_()
+    c1 = cache.to(DEV)
+    y1 = torch.empty(T, H, P, dtype=BF16, device=DEV)
+    k1 = torch.empty(mc, H, P, N, dtype=ts, device=DEV) if ckpt else None
+    tr = ssd.LaunchTrace(8)
+    ssd.ssd_combined_varlen_ex(p, ssd.make_options(trace=tr), x, dt, A, B, C, D, cu, c1, idx, hi,
+                               y1, k1, ws)
+    torch.cuda.synchronize()
+    names = [n for n, _ in tr.durations_us()]
+    segmented = names[0] == "chunk_state_passing_segmented_prep"
+    assert names == (["chunk_state_passing_segmented_prep", "state_carry_and_bmm",
+                      "chunk_scan_segmented"] if segmented
+                     else ["chunk_state_passing_prep_bmm", "chunk_scan"]), names
+    assert segmented == (not ckpt and len(lens) * H * 2 < 512 and mc > 1)
+
+    buf = {k: v.zero_() for k, v in ssd.alloc_step_buffers(p, DEV).items()}
+    c2 = cache.to(DEV)
+    y2 = torch.empty(T, H, P, dtype=BF16, device=DEV)
+    k2 = torch.empty(mc, H, P, N, dtype=ts, device=DEV) if ckpt else None
+    ssd.ssd_chunk_cumsum(p, dt, A, cu, buf["chunk_meta"], buf["dA_cumsum"], buf["dt_chunk"])
+    ssd.ssd_bmm_chunk(p, B, C, buf["chunk_meta"], buf["CB"])
+    ssd.ssd_chunk_state_passing(p, x, B, buf["chunk_meta"], buf["dA_cumsum"], buf["dt_chunk"],
+                                c2, idx, hi, buf["entering"], k2)
+    ssd.ssd_chunk_scan(p, x, C, D, buf["chunk_meta"], buf["dA_cumsum"], buf["dt_chunk"],
+                       buf["CB"], buf["entering"], y2)
+    torch.cuda.synchronize()
+
+    # the workspace as the combined call lays it out: metadata, cumsum, dt, CB,
+    # entering states (the fused state path keeps no chunk states)
+    r = lambda v: (v + 255) // 256 * 256
+    nm = ssd.chunk_meta_count(p)
+    o_cum = r(4 * nm)
+    o_dt = o_cum + r(4 * H * mc * Q)
+    o_cb = o_dt + r(4 * H * mc * Q)
+    o_ent = o_cb + r(2 * mc * G * Q * Q)
+    wsc = ws.cpu()
+    view = lambda o, n, dt_: wsc[o:o + n * torch.tensor([], dtype=dt_).element_size()].view(dt_)
+    meta1 = view(0, nm, torch.int32)
+    meta2 = buf["chunk_meta"].cpu()
+    assert torch.equal(meta1, meta2)
+    nc = int(meta2[S])
+    cum1 = view(o_cum, H * mc * Q, torch.int32).view(H, mc, Q)[:, :nc]
+    dt1 = view(o_dt, H * mc * Q, torch.int32).view(H, mc, Q)[:, :nc]
+    assert torch.equal(cum1, buf["dA_cumsum"].cpu().view(torch.int32)[:, :nc])
+    assert torch.equal(dt1, buf["dt_chunk"].cpu().view(torch.int32)[:, :nc])
+    cb1 = view(o_cb, mc * G * Q * Q, torch.int16).view(mc, G, Q, Q)[:nc]
+    assert torch.equal(cb1, buf["CB"].cpu().view(torch.int16)[:nc])
+    if segmented:
+        return
+    ent1 = view(o_ent, mc * H * P * N, torch.int16).view(mc, H, P, N)[:nc]
+    assert torch.equal(ent1, buf["entering"].cpu().view(torch.int16)[:nc])
+    assert torch.equal(y1.cpu().view(torch.int16), y2.cpu().view(torch.int16))
+    bits = torch.int16 if ts == BF16 else torch.int32
+    assert torch.equal(c1.cpu().view(bits), c2.cpu().view(bits))
+    if ckpt:
+        assert torch.equal(k1.cpu()[:nc].view(bits), k2.cpu()[:nc].view(bits))
 
 
 def _full_continuation(cfg, checkpoints):
