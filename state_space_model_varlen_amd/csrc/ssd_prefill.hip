@@ -136,7 +136,12 @@ __device__ __forceinline__ ChunkInfo found_chunk(int Q, const int *s_found)
     return ci;
 }
 
-// Wavefront prefix sum of dt * A_h over chunk c for head h (one wave).
+// Wavefront prefix sum of dt * A_h over chunk c for head h (one wave). The
+// chunk is taken in blocks of 64 positions, position 64 j + lane in block j:
+// a wave prefix sum per block, the blocks chained in order,
+//   cum = (((tot_0 + tot_1) + ...) + tot_{j-1}) + incl_j,
+// which is also the order in which the combined call's state launch, with one
+// wave per block, forms it (the two give the same values bit for bit).
 template <typename TIn>
 __device__ __forceinline__ void cumsum_wave(int H, int Q, int max_chunks, int c, int h,
                                             const ChunkInfo &ci, int lane,
@@ -144,41 +149,35 @@ __device__ __forceinline__ void cumsum_wave(int H, int Q, int max_chunks, int c,
                                             float *__restrict__ cum_out, float *__restrict__ dt_out,
                                             const DtTf &tf)
 {
-    const int E = (Q + kWave - 1) / kWave;  // positions per lane (<= 4)
+    constexpr int J = 4;                    // blocks of 64 positions (Q <= 256)
     const float Ah = A[h];
     const float bh = tf.bias ? tf.bias[h] : 0.0f;
-    float vals[4], loc[4], run = 0.0f;
+    float vals[J];
     // (loads at clamped positions, zeroed after: no branch between a load and its use)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int i = lane * E + e;
+    for (int j = 0; j < J; ++j) {
+        const int i = kWave * j + lane;
         const int ic = i < ci.len ? i : ci.len - 1;
-        vals[e] = to_f32(dt[(int64_t)(ci.start + ic) * H + h]);
+        vals[j] = to_f32(dt[(int64_t)(ci.start + ic) * H + h]);
     }
     if (tf.on) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vals[e] = dt_transform(tf, vals[e], bh);
+        for (int j = 0; j < J; ++j) vals[j] = dt_transform(tf, vals[j], bh);
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int i = lane * E + e;
-        vals[e] = (e < E && i < ci.len) ? vals[e] : 0.0f;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        run += vals[e] * Ah;
-        loc[e] = run;
-    }
-    const float incl = wave_inclusive_sum(run, lane);
-    const float off = incl - run;
     const int64_t row = ((int64_t)h * max_chunks + c) * Q;
+    float off = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int i = lane * E + e;
-        if (e < E && i < Q) {
-            cum_out[row + i] = off + loc[e];
-            dt_out[row + i] = vals[e];
+    for (int j = 0; j < J; ++j) {
+        const int i = kWave * j + lane;
+        if (kWave * j >= Q) break;
+        const float v = i < ci.len ? vals[j] : 0.0f;
+        const float incl = wave_inclusive_sum(v * Ah, lane);
+        if (i < Q) {
+            cum_out[row + i] = j == 0 ? incl : off + incl;
+            dt_out[row + i] = v;
         }
+        const float tot = __shfl(incl, kWave - 1);
+        off = j == 0 ? tot : off + tot;
     }
 }
 
@@ -1023,19 +1022,21 @@ constexpr int kScanLDB = kScanNSL + 16;
 template <int Q> struct StateScanRegs {
     static constexpr int kXV = (Q * 8 + 511) / 512;    // x vectors (8 bf16) per thread
     static constexpr int kBV = (Q * 8 + 511) / 512;    // B vectors per thread (8 per row)
-    static constexpr int kE = (Q + kWave - 1) / kWave; // dt positions per lane of wave 0
+    static constexpr int kJ = (Q + kWave - 1) / kWave; // 64-position blocks of a chunk
     uint4 x[kXV], b[kBV];
     float cm[kBV], dt[kBV];                            // cum and dt of the B rows
     float cl;                                          // cum at the chunk's last token
-    uint32_t dr[kE];                                   // raw bf16 dt (own-prep mode)
+    uint32_t dr;                                       // raw bf16 dt (OWN: waves < kJ)
 };
 
 // With OWN (the combined call, few sequences) the same launch also does step 1
 // and, unsegmented, step 4, so that neither needs a launch of its own:
 //   - every state block finds its sequence's chunks from cu_seqlens and scans
-//     dt * A_h over each chunk itself (wave 0, as the cumsum kernel does, in
-//     the same order: the same cum values bit for bit) into the unused pad
-//     columns of its LDS x rows, one chunk ahead;
+//     dt * A_h over each chunk itself, one chunk ahead: wave w < Q / 64 takes
+//     positions 64 w .. + 63 (a wave prefix sum, kept with dt in the unused pad
+//     columns of the LDS x rows, and the block's total), and the staging of the
+//     next step chains the blocks in order - the cumsum kernel's order, so the
+//     values are the same bit for bit;
 //   - the blocks of column slice 0 publish what the later launches read: the
 //     cumsum and dt rows of their head, and (head 0) the chunk metadata;
 //   - own.CB set: max_chunks G more blocks after the state blocks compute CB,
@@ -1053,11 +1054,12 @@ void state_scan_fast_kernel(
 {
     constexpr int P = 64, N = 128, NSL = kScanNSL, NS = N / NSL;
     constexpr int LDX = kScanLDX, LDB = kScanLDB;
-    constexpr int E = StateScanRegs<Q>::kE;
-    static_assert(LDX >= P + 2, "the cum / dt pad of an x row");
+    constexpr int J = StateScanRegs<Q>::kJ;
+    static_assert(LDX >= P + 4, "the cum / dt / block-total pad of an x row");
     typedef StateScanRegs<Q> Regs;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    bf16 *xs = reinterpret_cast<bf16 *>(smem);   // [Q][LDX]  x_t (OWN: cum_t, dt_t at column P)
+    bf16 *xs = reinterpret_cast<bf16 *>(smem);   // [Q][LDX]  x_t (OWN: pad floats at column P:
+                                                 //  block prefix sum, dt; row j < J: block j's total)
     bf16 *bs = xs + Q * LDX;                     // [Q][LDB]  w_t B_t (slice columns)
 
     // logical order (head, segment of sequence, column slice): each XCD takes a
@@ -1246,13 +1248,12 @@ void state_scan_fast_kernel(
         const rsrc_t rb = make_rsrc(B + ((int64_t)st * G + g) * N + n0,
                                     any ? (uint32_t)(len - 1) * brow + NSL * 2 : 0u);
         if constexpr (OWN) {
-            // raw dt of the chunk for wave 0 first (its scan runs before the
-            // x and B tiles are needed); the other waves' resource is empty
+            // raw dt of position 64 w + lane for waves w < J first (their scan
+            // runs before the x and B tiles are needed); the others read nothing
             const rsrc_t rt = make_rsrc(static_cast<const bf16 *>(own.dt) + (int64_t)st * H + h,
-                                        any && wave == 0 ? (uint32_t)(len - 1) * H * 2 + 2 : 0u);
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                R.dr[e] = __builtin_amdgcn_raw_buffer_load_b16(rt, (lane * E + e) * H * 2, 0, 0);
+                                        any && wave < J ? (uint32_t)(len - 1) * H * 2 + 2 : 0u);
+            R.dr = __builtin_amdgcn_raw_buffer_load_b16(rt, (uint32_t)(kWave * wave + lane) * H * 2,
+                                                        0, 0);
         } else {
             const int64_t row = ((int64_t)h * max_chunks + c) * Q;
             const rsrc_t rc = make_rsrc(cum + row, any ? (uint32_t)len * 4 : 0u);
@@ -1276,60 +1277,42 @@ void state_scan_fast_kernel(
         }
     };
 
-    // OWN: wave 0 scans dt * A_h over chunk c (fetched into R) into the pad
-    // columns of the x rows (cum_t, dt_t as two floats at column P of row t),
-    // positions past the chunk's end holding the last cum and dt 0; slice 0
-    // publishes the rows, head 0 the chunk's (sequence, start, length).
+    // OWN: wave w < J scans dt * A_h over positions 64 w .. + 63 of chunk c
+    // (fetched into R) into the pads of those x rows (prefix sum within the
+    // 64-position block, dt; positions past the chunk's end add nothing and
+    // hold dt 0) and the block's total into the pad of row w; the staging of
+    // the step that folds chunk c chains the blocks (cum_at).
     auto scan_chunk = [&](const Regs &R, int c) {
-        if (wave != 0) return;
+        if (wave >= J) return;
         int st;
         const int len = chunk_at(c, st);
-        float vals[4], loc[4], run = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vals[e] = e < E ? __uint_as_float(R.dr[e < E ? e : 0] << 16) : 0.0f;
-        if (own.tf.on) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) vals[e] = dt_transform(own.tf, vals[e], bh);
+        const int i = kWave * wave + lane;
+        float v = __uint_as_float(R.dr << 16);
+        if (own.tf.on) v = dt_transform(own.tf, v, bh);
+        v = i < len ? v : 0.0f;
+        const float incl = wave_inclusive_sum(v * Ah, lane);
+        if (i < Q) {
+            float2 cd;
+            cd.x = incl;
+            cd.y = v;
+            *reinterpret_cast<float2 *>(xs + i * LDX + P) = cd;
         }
+        if (lane == kWave - 1) reinterpret_cast<float *>(xs + wave * LDX + P)[2] = incl;
+    };
+    // cum at position t of the chunk staged in xs (after the barrier that
+    // follows scan_chunk): the totals of the blocks before t's, then its own
+    // prefix sum; also its dt
+    auto cum_at = [&](int t, float &dtv) {
+        const float2 cd = *reinterpret_cast<const float2 *>(xs + t * LDX + P);
+        dtv = cd.y;
+        const int jb = t >> 6;
+        float off = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = lane * E + e;
-            vals[e] = (e < E && i < len) ? vals[e] : 0.0f;
+        for (int j = 0; j < J - 1; ++j) {
+            const float tj = reinterpret_cast<const float *>(xs + j * LDX + P)[2];
+            if (j < jb) off = j == 0 ? tj : off + tj;
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            run += vals[e] * Ah;
-            loc[e] = run;
-        }
-        const float incl = wave_inclusive_sum(run, lane);
-        const float off = incl - run;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const int i = lane * E + e;
-            if (i < Q) {
-                float2 cd;
-                cd.x = off + loc[e];
-                cd.y = vals[e];
-                *reinterpret_cast<float2 *>(xs + i * LDX + P) = cd;
-            }
-        }
-        if (q == 0 && c < hi) {
-            const int64_t row = ((int64_t)h * max_chunks + c) * Q;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const int i = lane * E + e;
-                if (i < Q) {
-                    own.cum[row + i] = off + loc[e];
-                    own.dtc[row + i] = vals[e];
-                }
-            }
-            if (h == 0 && lane == 0) {
-                int32_t *m = own.meta + (S + 1) + 3 * c;
-                m[0] = s;
-                m[1] = st;
-                m[2] = len;
-            }
-        }
+        return jb == 0 ? cd.x : off + cd.x;
     };
 
     // one iteration: stage chunk c from R into LDS, refill R with chunk c + 1,
@@ -1341,25 +1324,29 @@ void state_scan_fast_kernel(
         const int st = first + chunk_off(c);
         const int len = end - st < chunk_cap(c) ? end - st : chunk_cap(c);
         __syncthreads();   // the previous chunk's MFMA reads of xs / bs are done
-        // (OWN: the cumsum at the chunk's last token from its x row's pad; an
-        // empty chunk's pads hold zeros)
-        const float cl = OWN ? reinterpret_cast<const float *>(xs + (len > 0 ? len - 1 : 0) * LDX + P)[0]
-                             : R.cl;
+        // (OWN: the cumsum at the chunk's last token from the pads; an empty
+        // chunk's pads hold zeros)
+        float cl = R.cl;
+        if constexpr (OWN) {
+            float unused;
+            cl = cum_at(len > 0 ? len - 1 : 0, unused);
+        }
+        // (u < Q * 8 holds for every thread where 512 (k + 1) <= Q * 8; said so at
+        // compile time, so that no path skips a staging and leaves its registers
+        // counted as loads in flight)
 #pragma unroll
         for (int k = 0; k < Regs::kXV; ++k) {
             const int u = tid + 512 * k;
-            if (u < Q * 8) st16(xs + (u >> 3) * LDX + 8 * (u & 7), R.x[k]);
+            if (512 * (k + 1) <= Q * 8 || u < Q * 8) st16(xs + (u >> 3) * LDX + 8 * (u & 7), R.x[k]);
         }
 #pragma unroll
         for (int k = 0; k < Regs::kBV; ++k) {
             const int u = tid + 512 * k;
-            if (u < Q * 8) {
+            if (512 * (k + 1) <= Q * 8 || u < Q * 8) {
                 const int t = u >> 3;
                 float cmt, dtt;
                 if constexpr (OWN) {
-                    const float2 cd = *reinterpret_cast<const float2 *>(xs + t * LDX + P);
-                    cmt = cd.x;
-                    dtt = cd.y;
+                    cmt = cum_at(t, dtt);
                 } else {
                     cmt = R.cm[k];
                     dtt = R.dt[k];
@@ -1376,6 +1363,50 @@ void state_scan_fast_kernel(
             }
         }
         const float decay = __expf(cl);
+
+        // Every store of the step is issued here, before the next chunk's loads:
+        // the memory operations issued after those loads are then only loads,
+        // which the compiler counts exactly, and its waits for them never wait
+        // for a store (stores that depend on the block or the chunk would make
+        // it count conservatively). acc still holds the state entering chunk c,
+        // which is also the checkpoint of chunk c - 1.
+        if (live) {
+            const int64_t off = ((int64_t)c * H + h) * PN + run;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                float v[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+                store4<bf16>(entering + off + 16 * j, v);
+            }
+            if constexpr (CKPT) {
+                if (c > lo) {
+                    const int64_t pk = off - (int64_t)H * PN;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        float v[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+                        put4<TS>(ckpt + pk + 16 * j, v, srk, (uint64_t)(pk + 16 * j), kSrCkpt);
+                    }
+                }
+            }
+            if constexpr (OWN) {
+                // slice 0 publishes the chunk's cumsum and dt rows (thread t < Q:
+                // position t), head 0 its (sequence, start, length)
+                if (q == 0) {
+                    if (tid < Q) {
+                        float dtt;
+                        const float cmt = cum_at(tid, dtt);
+                        const int64_t row = ((int64_t)h * max_chunks + c) * Q;
+                        own.cum[row + tid] = cmt;
+                        own.dtc[row + tid] = dtt;
+                    }
+                    if (h == 0 && tid == 0) {
+                        int32_t *m = own.meta + (S + 1) + 3 * c;
+                        m[0] = s;
+                        m[1] = st;
+                        m[2] = len;
+                    }
+                }
+            }
+        }
         if constexpr (SEG) {
             if (live && q == 0 && tid == 0) {
                 seg_F[(int64_t)h * max_chunks + c] = F;
@@ -1386,14 +1417,6 @@ void state_scan_fast_kernel(
         fetch(R, c + 1);
         __syncthreads();
 
-        const int64_t off = ((int64_t)c * H + h) * PN + run;
-        if (live) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                float v[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
-                store4<bf16>(entering + off + 16 * j, v);
-            }
-        }
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -1421,15 +1444,6 @@ void state_scan_fast_kernel(
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], xf, acc[j], 0, 0, 0);
-        if constexpr (CKPT) {
-            if (live) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    float w[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
-                    put4<TS>(ckpt + off + 16 * j, w, srk, (uint64_t)(off + 16 * j), kSrCkpt);
-                }
-            }
-        }
         if constexpr (OWN) scan_chunk(R, c + 1);   // (read after the next step's first barrier)
     };
 
@@ -1449,6 +1463,18 @@ void state_scan_fast_kernel(
     do {
         step(R, c);
     } while (++c < hi);
+    if constexpr (CKPT) {
+        // the last chunk's checkpoint (the others were written one step later,
+        // as the state entering the next chunk)
+        if (hi > lo) {
+            const int64_t pk = ((int64_t)(hi - 1) * H + h) * PN + run;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                float v[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+                put4<TS>(ckpt + pk + 16 * j, v, srk, (uint64_t)(pk + 16 * j), kSrCkpt);
+            }
+        }
+    }
 
     if constexpr (SEG) {
         // the segment's local final state and total decay, for the carry step
