@@ -114,9 +114,9 @@ def launch_bytes(name, w: Work, entering_bytes=None):
         # the same launches doing the cumsum themselves: dt read, cumsum and dt rows
         # written; unsegmented, CB as well (C read, CB written)
         "chunk_state_passing_segmented_prep":
-            x + bc + T * H * ex + per_chunk + ent + w.s_init * HPN * es + fin,
+            x + 2 * bc + T * H * ex + per_chunk + ent + w.s_init * HPN * es + fin + cb,
         "chunk_state_passing_prep_bmm": x + 2 * bc + T * H * ex + per_chunk + ent + cache_io + cb,
-        "state_carry_and_bmm": fin + S * w.nseg * HPN * ex + S * HPN * es + 2 * bc + cb,
+        "state_carry": fin + S * w.nseg * HPN * ex + S * HPN * es,
         "chunk_scan": 2 * x + bc + per_chunk + cb + ent,
         "chunk_scan_segmented": 2 * x + bc + per_chunk + cb + ent + carry,
         # the one-launch short-sequence path: x, dt, B, C in, y out, initial and
@@ -136,11 +136,11 @@ def launch_flops(name, w: Work):
     cbf = sum(G * N * v * (v + 1) for v in q)            # C B^T, causal
     if name.startswith("chunk_scan"):
         return intra + state_term
-    if name == "chunk_state_passing_prep_bmm":
+    if name in ("chunk_state_passing_prep_bmm", "chunk_state_passing_segmented_prep"):
         return chunk_state + cbf
     if name.startswith("chunk_state_passing"):
         return chunk_state
-    if name in ("bmm_chunk", "bmm_chunk_pairs", "state_carry_and_bmm", "chunk_prep"):
+    if name in ("bmm_chunk", "bmm_chunk_pairs", "chunk_prep"):
         return cbf
     return 0
 
@@ -188,7 +188,7 @@ KERNEL_PATTERNS = [
     (r"state_scan_fast_kernelILi\d+ELb[01]ELb1E|state_scan_fast_kernel<\d+, \w+, true",
      "chunk_state_passing_segmented", PREFILL_SOURCES),
     (r"state_scan_fast_kernel", "chunk_state_passing", PREFILL_SOURCES),
-    (r"state_carry_kernel", "state_carry_and_bmm", PREFILL_SOURCES),
+    (r"state_carry_kernel", "state_carry", PREFILL_SOURCES),
     (r"short_scan_kernel", "short_scan", PREFILL_SOURCES),
     (r"chunk_scan_fast_kernelILi\d+ELb1E", "chunk_scan_segmented", PREFILL_SOURCES),
     (r"chunk_scan_fast_kernel|chunk_scan_kernel", "chunk_scan", PREFILL_SOURCES),

@@ -363,11 +363,9 @@ static int combined(const ssd_problem *p, const ssd::DtTf &tf, const void *x, co
         seg.L = reinterpret_cast<float *>(base + w.seg_L);
         seg.F = reinterpret_cast<float *>(base + w.seg_F);
         seg.I = reinterpret_cast<int32_t *>(base + w.seg_I);
-        seg.C = C;
-        seg.CB = cb;
     }
-    // few sequences: steps 1 and 4 inside the state launch (step 4 in the carry
-    // launch when segmented), so the call is two or three launches
+    // few sequences: steps 1 and 4 inside the state launch, so the call is two
+    // launches, or three with the carry step of a segmented state pass
     if (ssd::own_prep_path(d)) {
         ssd::OwnPrep own;
         own.dt = dt;
@@ -377,20 +375,17 @@ static int combined(const ssd_problem *p, const ssd::DtTf &tf, const void *x, co
         own.meta = meta;
         own.cum = cum;
         own.dtc = dtc;
-        if (seg.nseg <= 1) {
-            own.C = C;
-            own.CB = cb;
-        }
+        own.C = C;
+        own.CB = cb;
         ssd::launch_state_scan(d, x, B, meta, cum, dtc, state_cache, state_indices,
                                has_initial_state, entering, checkpoints, stream, &seg, &own);
         ssd::launch_chunk_scan(d, x, C, D, meta, cum, dtc, cb, entering, y, stream, &seg);
         return launch_status();
     }
-    // steps 1 and 4 in one launch; or (segmented) step 4 beside the carry step;
-    // or, with many (chunk, group) pairs, step 4 one pair per block after step 1
-    if (seg.nseg > 1) {
-        ssd::launch_chunk_cumsum(d, dt, A, cu_seqlens, meta, cum, dtc, stream, tf);
-    } else if (ssd::cb_by_pair(d)) {
+    // (more sequences: never segmented, see state_segments) steps 1 and 4 in one
+    // launch, or, with many (chunk, group) pairs, step 4 one pair per block after
+    // step 1
+    if (ssd::cb_by_pair(d)) {
         ssd::launch_chunk_cumsum(d, dt, A, cu_seqlens, meta, cum, dtc, stream, tf);
         ssd::launch_bmm(d, B, C, meta, cb, stream);
     } else {
@@ -398,13 +393,13 @@ static int combined(const ssd_problem *p, const ssd::DtTf &tf, const void *x, co
     }
     if (ssd::fused_state_path(d)) {
         ssd::launch_state_scan(d, x, B, meta, cum, dtc, state_cache, state_indices,
-                               has_initial_state, entering, checkpoints, stream, &seg);
+                               has_initial_state, entering, checkpoints, stream);
     } else {
         ssd::launch_chunk_state(d, x, B, meta, cum, dtc, states, stream);
         ssd::launch_state_passing(d, states, cum, meta, state_cache, state_indices,
                                   has_initial_state, entering, checkpoints, stream);
     }
-    ssd::launch_chunk_scan(d, x, C, D, meta, cum, dtc, cb, entering, y, stream, &seg);
+    ssd::launch_chunk_scan(d, x, C, D, meta, cum, dtc, cb, entering, y, stream);
     return launch_status();
 }
 

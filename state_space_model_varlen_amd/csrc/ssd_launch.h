@@ -83,16 +83,13 @@ bool fused_state_path(const PrefillDims &d);
 // the segment's global index s nseg + b (I, [max_chunks], -1 in a first
 // segment). The carry step then chains the segments into each one's true
 // starting state (carry, bf16 [S nseg][H][P][N]) and writes the final states;
-// the chunk scan adds exp(F) carry to the local entering states.
-// With C and CB set, the carry launch also computes CB (step 4), so that the
-// call runs step 1 alone (launch_chunk_cumsum) instead of launch_chunk_prep.
+// the chunk scan adds exp(F) carry to the local entering states. Segments are
+// used only together with OwnPrep (below).
 struct SegBufs {
     int nseg = 1;
     float *fin = nullptr, *L = nullptr, *F = nullptr;
     int32_t *I = nullptr;
     void *carry = nullptr;
-    const void *C = nullptr;
-    void *CB = nullptr;
 };
 // Segments the combined call uses for these dimensions (1: unsegmented).
 int state_segments(const PrefillDims &d);
@@ -101,8 +98,8 @@ int state_segments(const PrefillDims &d);
 // the fused state path with at most kOwnPrepMaxSeqs sequences): its state
 // blocks find their chunks from cu_seqlens and scan dt themselves, and publish
 // the metadata, cumsum and dt rows (meta, cum, dtc) that the later launches
-// read; with CB set (unsegmented), one block per (chunk, group) pair after the
-// state blocks computes CB. No cumsum, prep or bmm launch then runs.
+// read; with CB set, one block per (chunk, group) pair after the state blocks
+// computes CB. No cumsum, prep or bmm launch then runs.
 struct OwnPrep {
     const void *dt = nullptr;
     const float *A = nullptr;

@@ -1781,24 +1781,14 @@ void state_scan_multi_kernel(
 // final state goes to the cache slot as the unsegmented path writes it.
 constexpr int kMaxSeg = 8;
 
-//
-// The same launch computes CB (step 4, which only the chunk scan reads) in its
-// first nbmm blocks, one CB row tile each, beside the carry blocks.
 template <typename TS>
 __global__ __launch_bounds__(256) void state_carry_kernel(
     int S, int H, int PN, int nseg, int max_chunks, int num_slots,
     const int32_t *__restrict__ meta, const float *__restrict__ seg_fin,
     const float *__restrict__ seg_L, bf16 *__restrict__ carry, TS *cache,
-    const int32_t *__restrict__ idx, SrCtx sr, int nbmm, int G, int Q,
-    const bf16 *__restrict__ B, const bf16 *__restrict__ C, bf16 *__restrict__ CB)
+    const int32_t *__restrict__ idx, SrCtx sr)
 {
-    if ((int)blockIdx.x < nbmm) {
-        const int tiles = Q / 16, y = blockIdx.x;
-        const int c = y / (G * tiles), g = (y / tiles) % G, z = y % tiles;
-        bmm_rows<bf16, 128>(G, Q, c, g, z, chunk_info(meta, S, c), B, C, CB);
-        return;
-    }
-    const int bx = blockIdx.x - nbmm;
+    const int bx = blockIdx.x;
     const int per = PN / 1024;
     const int e0 = (bx % per) * 1024 + 4 * threadIdx.x;
     const int h = (bx / per) % H, s = bx / (per * H);
@@ -2782,7 +2772,7 @@ static void launch_state_scan_k(const PrefillDims &d, const void *x, const void 
     const int nseg = SEG ? seg.nseg : 1;
     const int64_t nstate = (int64_t)d.S * nseg * d.H * (128 / kScanNSL);
     // OWN, unsegmented: the CB blocks, one per (chunk, group) pair
-    const int64_t ncb = OWN && !SEG && own.CB ? (int64_t)d.max_chunks * d.G : 0;
+    const int64_t ncb = OWN && own.CB ? (int64_t)d.max_chunks * d.G : 0;
     // longest chain first: few sequences (one wave ranks them), heads a multiple of 8
     const int lpt = !SEG && d.S > 1 && d.S <= 64 && d.H % kXcds == 0;
     const char *name = OWN ? (SEG ? "chunk_state_passing_segmented_prep" : "chunk_state_passing_prep_bmm")
@@ -2795,12 +2785,9 @@ static void launch_state_scan_k(const PrefillDims &d, const void *x, const void 
     if constexpr (SEG) {
         const int PN = 64 * 128;
         const int ncar = d.S * d.H * (PN / 1024);
-        const int nbmm = seg.CB ? d.max_chunks * d.G * (d.Q / 16) : 0;
-        SSD_LAUNCH(d, nbmm ? "state_carry_and_bmm" : "state_carry", state_carry_kernel<TS>, dim3((unsigned)(nbmm + ncar)), dim3(256), 0, st,
+        SSD_LAUNCH(d, "state_carry", state_carry_kernel<TS>, dim3((unsigned)ncar), dim3(256), 0, st,
                            d.S, d.H, PN, nseg, d.max_chunks, d.num_slots, meta, seg.fin, seg.L,
-                           static_cast<bf16 *>(seg.carry), static_cast<TS *>(cache), idx, d.sr,
-                           nbmm, d.G, d.Q, static_cast<const bf16 *>(B),
-                           static_cast<const bf16 *>(seg.C), static_cast<bf16 *>(seg.CB));
+                           static_cast<bf16 *>(seg.carry), static_cast<TS *>(cache), idx, d.sr);
     }
 }
 
@@ -2814,10 +2801,13 @@ static void launch_state_scan_o(const PrefillDims &d, const void *x, const void 
     if (ckpt)
         launch_state_scan_k<Q, true, false, OWN, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init,
                                                      entering, ckpt, SegBufs(), own, st);
-    else if (seg && seg->nseg > 1)
-        launch_state_scan_k<Q, false, true, OWN, TS>(d, x, B, meta, cum, dtc, cache, idx, has_init,
-                                                     entering, ckpt, *seg, own, st);
-    else
+    else if (OWN && seg && seg->nseg > 1) {
+        // (segments come only with the own-prep path: state_segments() needs few
+        // (sequence, head) pairs, so few sequences)
+        if constexpr (OWN)
+            launch_state_scan_k<Q, false, true, true, TS>(d, x, B, meta, cum, dtc, cache, idx,
+                                                          has_init, entering, ckpt, *seg, own, st);
+    } else
         launch_state_scan_k<Q, false, false, OWN, TS>(d, x, B, meta, cum, dtc, cache, idx,
                                                       has_init, entering, ckpt, SegBufs(), own, st);
 }

@@ -45,11 +45,11 @@ def test_launch_bytes_and_flops_of_the_layer_prefill():
         2 * x + bc + per_chunk + cb + entering + 2 * H * P * N * 2
     assert bench.launch_bytes("chunk_state_passing_segmented", w) == \
         x + bc + per_chunk + entering + fins
-    assert bench.launch_bytes("state_carry_and_bmm", w) == \
-        fins + 3 * H * P * N * 2 + final + 2 * bc + cb
-    # the state launch doing the cumsum itself: dt read, cumsum and dt rows written
+    assert bench.launch_bytes("state_carry", w) == fins + 3 * H * P * N * 2 + final
+    # the state launch doing the cumsum and CB itself: dt and C read, cumsum and dt
+    # rows and CB written
     assert bench.launch_bytes("chunk_state_passing_segmented_prep", w) == \
-        x + bc + T * H * 2 + per_chunk + entering + fins
+        x + 2 * bc + T * H * 2 + per_chunk + entering + fins + cb
     # flops: causal intra-chunk 80 * 64 * 256 * 257 per chunk plus the state term
     # 2 * 80 * 64 * 128 * 256 per chunk: 10.76 GFLOP
     assert bench.launch_flops("chunk_scan_segmented", w) == \
@@ -73,7 +73,7 @@ def test_kernel_names_map_to_launches():
         "chunk_state_passing_prep_bmm"
     assert n("void ssd::state_scan_fast_kernel<128, false, true, false, bf16>(int") == \
         "chunk_state_passing_segmented"
-    assert n("void ssd::state_carry_kernel<float>(int, int") == "state_carry_and_bmm"
+    assert n("void ssd::state_carry_kernel<float>(int, int") == "state_carry"
     assert n("_ZN3ssd19chunk_cumsum_kernelIDF16bEEvii") == "chunk_cumsum"
     assert n("_ZN3ssd15bmm_pair_kernelILi256EEEvii") == "bmm_chunk_pairs"
     assert n("void ssd::short_scan_kernel<32, float>(int, int") == "short_scan"

@@ -389,7 +389,7 @@ def test_launch_trace_names_and_times_every_launch():
         torch.cuda.synchronize()
         outs.append((y.cpu(), cache.cpu()))
     d = tr.durations_us()
-    assert [n for n, _ in d] == ["chunk_state_passing_segmented_prep", "state_carry_and_bmm",
+    assert [n for n, _ in d] == ["chunk_state_passing_segmented_prep", "state_carry",
                                  "chunk_scan_segmented"]
     assert all(us > 0 for _, us in d), d
     assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
@@ -440,7 +440,7 @@ def test_state_launch_with_own_prep_matches_steps_bitwise(case):
     torch.cuda.synchronize()
     names = [n for n, _ in tr.durations_us()]
     segmented = names[0] == "chunk_state_passing_segmented_prep"
-    assert names == (["chunk_state_passing_segmented_prep", "state_carry_and_bmm",
+    assert names == (["chunk_state_passing_segmented_prep", "state_carry",
                       "chunk_scan_segmented"] if segmented
                      else ["chunk_state_passing_prep_bmm", "chunk_scan"]), names
     assert segmented == (not ckpt and len(lens) * H * 2 < 512 and mc > 1)
