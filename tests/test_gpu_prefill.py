@@ -406,6 +406,9 @@ OWN_CASES = [
     ((1500,), 8, 1, 128, F32, False),
     ((257, 0, 3, 129), 6, 3, 64, BF16, False),
     (tuple(20 + (37 * i) % 280 for i in range(70)), 8, 2, 64, F32, True),
+    # chunk 32: one wave scans, half of its lanes past the chunk
+    ((100, 37, 260), 8, 2, 32, BF16, True),
+    ((300, 45), 4, 1, 32, F32, False),
 ]
 
 
