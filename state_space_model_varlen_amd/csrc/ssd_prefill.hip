@@ -1886,7 +1886,7 @@ __device__ __forceinline__ void scan_row_tile(
     int i0, int nk, const uint4 *cbf, bool exact, bool single, float rs, int len, int lane,
     rsrc_t rc, uint32_t crow, const float *scum, const float *sdt, const bf16 *xs, const bf16 *hs,
     bf16 *yw, rsrc_t rx, uint32_t xrow, int H, float Dh, bf16 *yout, const bf16 *CBc, int nrt,
-    int nnk, uint4 *ncf, bool prefetch_next)
+    int nnk, uint4 *ncf, bool prefetch_next, const uint4 *xe_pre)
 {
     constexpr int P = 64, N = 128, LDX = kScanXLD, LDH = N + 8;
     if (nk == 0) {
@@ -1901,10 +1901,8 @@ __device__ __forceinline__ void scan_row_tile(
 #pragma unroll
     for (int kk = 0; kk < N / 32; ++kk)
         cr[kk] = buf_ld16(rc, (uint32_t)i * crow + 64 * kk + 16 * kg);   // zeros past len
-    uint4 xe[2];                         // x of the D x term: row r16, p = 32 k + 8 kg + 0..7
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-        xe[k] = buf_ld16(rx, (uint32_t)i * xrow + 64 * k + 16 * kg);     // zeros past len
+    // x of the D x term: row r16, p = 32 k + 8 kg + 0..7 (requested in the prologue)
+    const uint4 xe[2] = {xe_pre[0], xe_pre[1]};
 
     f32x4 acc[P / 16];
 #pragma unroll
@@ -2111,6 +2109,15 @@ void chunk_scan_fast_kernel(
     const bf16 *CBc = CB + ((int64_t)c * G + g) * Q * Q;
     uint4 cbf[kStepsB];
     load_cb_frags<kStepsB>(CBc, Q, rtB, lane, nkB, cbf);
+    // the x rows of both row tiles for the epilogue's D x term (row 16 rt + lane % 16,
+    // p = 32 k + 8 (lane / 16) + 0..7), requested with the staging loads of the same
+    // rows, while those lines are in flight or in L2 (zeros past len)
+    uint4 xeB[2], xeA[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        xeB[k] = buf_ld16(rx, (uint32_t)(16 * rtB + (lane & 15)) * xrow + 64 * k + 16 * (lane >> 4));
+        xeA[k] = buf_ld16(rx, (uint32_t)(16 * rtA + (lane & 15)) * xrow + 64 * k + 16 * (lane >> 4));
+    }
     scum[iq] = cmv * kLog2e;          // (threads past Q rewrite position Q - 1 with the
     sdt[iq] = dtv;                     //  same values: no branch, so the loads stay first)
 #pragma unroll
@@ -2188,11 +2195,12 @@ void chunk_scan_fast_kernel(
                                        scum, sdt,
                                        xs, hs, yw, rx, xrow, H, Dh,
                                        y + ((int64_t)ci.start * H + h) * P, CBc, rtA, nkA, caf,
-                                       true);
+                                       true, xeB);
     scan_row_tile<Q, kStepsA, kStepsA>(16 * rtA, nkA, caf, exact, single, rs, len, lane, rc, crow,
                                        scum, sdt,
                                        xs, hs, yw, rx, xrow, H, Dh,
-                                       y + ((int64_t)ci.start * H + h) * P, CBc, 0, 0, caf, false);
+                                       y + ((int64_t)ci.start * H + h) * P, CBc, 0, 0, caf, false,
+                                       xeA);
 }
 
 // ===========================================================================
