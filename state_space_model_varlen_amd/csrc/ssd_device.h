@@ -396,6 +396,31 @@ __device__ __forceinline__ void buf_st8(rsrc_t r, uint32_t off, uint2 v) {
     typedef int v2i __attribute__((ext_vector_type(2)));
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i, v), r, (int)off, 0, 0);
 }
+// 4 consecutive state values of type T at byte offset `off` as floats; zeros at
+// or past the resource's size (an empty resource reads nothing)
+template <typename T> __device__ __forceinline__ void buf_load4(rsrc_t r, uint32_t off, float *v);
+template <> __device__ __forceinline__ void buf_load4<float>(rsrc_t r, uint32_t off, float *v) {
+    const uint4 w = buf_ld16(r, off);
+    v[0] = __uint_as_float(w.x);
+    v[1] = __uint_as_float(w.y);
+    v[2] = __uint_as_float(w.z);
+    v[3] = __uint_as_float(w.w);
+}
+template <> __device__ __forceinline__ void buf_load4<bf16>(rsrc_t r, uint32_t off, float *v) {
+    const auto w = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    v[0] = __uint_as_float((uint32_t)w[0] << 16);
+    v[1] = __uint_as_float((uint32_t)w[0] & 0xffff0000u);
+    v[2] = __uint_as_float((uint32_t)w[1] << 16);
+    v[3] = __uint_as_float((uint32_t)w[1] & 0xffff0000u);
+}
+template <> __device__ __forceinline__ void buf_load4<f16>(rsrc_t r, uint32_t off, float *v) {
+    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+    const f16x4 q = __builtin_bit_cast(f16x4, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+    v[0] = static_cast<float>(q[0]);
+    v[1] = static_cast<float>(q[1]);
+    v[2] = static_cast<float>(q[2]);
+    v[3] = static_cast<float>(q[3]);
+}
 // four floats as bf16 (round to nearest even), in one 8-byte word
 __device__ __forceinline__ uint2 pack_bf16x4(const float *v) {
     typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));

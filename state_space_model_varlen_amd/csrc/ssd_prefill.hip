@@ -1202,11 +1202,15 @@ void state_scan_fast_kernel(
     const bool slot_ok = slot >= 0 && slot < num_slots;
     TS *cslot = cache + ((int64_t)(slot_ok ? slot : 0) * H + h) * PN + run;
 
-    // the initial state is loaded whatever the flag says (slot 0 stands in for
-    // a bad slot) and selected once the first chunk's loads are also out
+    // the initial state, through a resource that is empty when the block does
+    // not start from it (no cached state, a bad slot, a later segment): zeros
+    // then, and no memory read
+    const bool want_init = slot_ok && has_init != nullptr && hflag != 0 && b == 0;
+    const rsrc_t rinit = make_rsrc(cache + ((int64_t)(slot_ok ? slot : 0) * H + h) * PN,
+                                   want_init ? (uint32_t)(PN * sizeof(TS)) : 0u);
     float iv[2][4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) load4<TS>(cslot + 16 * j, iv[j]);
+    for (int j = 0; j < 2; ++j) buf_load4<TS>(rinit, (uint32_t)((run + 16 * j) * sizeof(TS)), iv[j]);
     f32x4 acc[2];
 
     // byte offsets inside a chunk's tiles (the same for every chunk)
