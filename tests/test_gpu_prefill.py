@@ -146,6 +146,56 @@ def test_steps_match_chunked_oracle(case):
     assert_close(y, r["y"], ti, "y")
 
 
+MULTI_CASES = [
+    # seqlens, state dtype, checkpoints: 64 short sequences x 8 heads x 2 column
+    # slices = 1024 items, on average under half a chunk: ssd_chunk_state_passing
+    # runs its persistent multi-item kernel (item boundaries after one or two
+    # chunks, empty sequences)
+    ((1, 0, 200, 5, 64, 17, 0, 129) * 8, F32, True),
+    ((3, 40, 0, 9, 130, 1, 22, 31) * 8, BF16, False),
+]
+
+
+@pytest.mark.parametrize("case", MULTI_CASES, ids=lambda c: f"{str(c[1])[6:]}_"
+                         f"{'ckpt' if c[2] else 'nockpt'}")
+def test_step_state_passing_on_short_batches(case):
+    lens, ts, ck = case
+    H, P, N, G, Q = 8, 64, 128, 2, 128
+    S, T = len(lens), sum(lens)
+    assert 2 * T <= S * Q and S * H * 2 >= 1024
+    inp = sy.random_problem(990 + MULTI_CASES.index(case), lens, H, P, N, G, Q, BF16, ts,
+                            num_slots=S + 3, has_initial=[s % 2 == 0 for s in range(S)])
+    cache = _cache_with_states(inp, S + 3, ts)
+    ssd = _ssd()
+    p = ssd.make_problem(T, S, H, P, N, G, Q, S + 3, BF16, ts)
+    buf = ssd.alloc_step_buffers(p, DEV)
+    mc = ssd.max_chunks(p)
+    g_cache = cache.to(DEV)
+    ckpt = torch.empty(mc, H, P, N, dtype=ts, device=DEV) if ck else None
+    ssd.ssd_chunk_cumsum(p, inp.dt.to(DEV), inp.A.to(DEV), inp.cu_seqlens.to(DEV),
+                         buf["chunk_meta"], buf["dA_cumsum"], buf["dt_chunk"])
+    ssd.ssd_chunk_state_passing(p, inp.x.to(DEV), inp.B.to(DEV), buf["chunk_meta"],
+                                buf["dA_cumsum"], buf["dt_chunk"], g_cache,
+                                inp.state_indices.to(DEV), inp.has_initial.to(DEV),
+                                buf["entering"], ckpt)
+    torch.cuda.synchronize()
+    init = oracle.f64(cache[inp.state_indices.long()])
+    hin = inp.has_initial.numpy()
+    init[hin == 0] = 0.0
+    r = chunked.scan(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.cu_seqlens.numpy(), Q,
+                     init=init, has_init=hin)
+    nc = len(r["meta"]["seq"])
+    assert_close(buf["entering"][:nc], r["entering"], BF16, "entering states")
+    if ck:
+        assert_close(ckpt[:nc], r["ckpt"], looser(BF16, ts), "checkpoints")
+    used = inp.state_indices.long()
+    after = g_cache.cpu()
+    assert_close(after[used], r["final"], looser(BF16, ts), "final states")
+    others = [k for k in range(S + 3) if k not in set(used.tolist())]
+    bits = torch.int16 if ts == BF16 else torch.int32
+    assert torch.equal(after[others].view(bits), cache[others].view(bits))
+
+
 # --------------------------------------------------------------------------------------
 # end to end vs the sequential recurrence
 
@@ -161,11 +211,12 @@ E2E_CASES = [
     # pairs over the XCDs (one head per group)
     ((400, 77, 130), 16, 64, 128, 16, 64, BF16, F32, True),
     ((700, 260, 5, 90), 16, 64, 128, 16, 128, BF16, BF16, False),
-    # 64 mostly short sequences x 8 heads (1024 state items): the fused state pass
-    # with persistent blocks walking several items, item boundaries after one or
-    # two chunks and empty sequences
+    # 64 mostly short sequences x 8 heads (on average under half a chunk): the
+    # one-launch short-sequence kernel, sequences of one or two chunks and empty ones
     ((1, 0, 200, 5, 64, 17, 0, 129) * 8, 8, 64, 128, 2, 128, BF16, F32, True),
     ((3, 40, 0, 9, 130, 1, 22, 31) * 8, 8, 64, 128, 2, 128, BF16, BF16, False),
+    # more than 256 sequences: the cumsum, CB and state launches of their own
+    (tuple(40 + (13 * i) % 90 for i in range(300)), 2, 64, 128, 1, 64, BF16, F32, True),
 ]
 
 
