@@ -1241,7 +1241,7 @@ void state_scan_fast_kernel(
     // Loads of chunk c's tiles through buffer resources that end at the chunk's
     // last row: rows past it read as zero. Past the last chunk (and for a
     // sequence with no chunk) every resource is empty and nothing is read.
-    auto fetch = [&](Regs &R, int c) {
+    auto fetch_x = [&](Regs &R, int c) {
         const bool any = c < hi;
         int st;
         const int len = chunk_at(c, st);
@@ -1249,8 +1249,6 @@ void state_scan_fast_kernel(
         c = c > lo ? c : lo;
         const rsrc_t rx = make_rsrc(x + ((int64_t)st * H + h) * P,
                                     any ? (uint32_t)(len - 1) * xrow + P * 2 : 0u);
-        const rsrc_t rb = make_rsrc(B + ((int64_t)st * G + g) * N + n0,
-                                    any ? (uint32_t)(len - 1) * brow + NSL * 2 : 0u);
         if constexpr (OWN) {
             // raw dt of position 64 w + lane for waves w < J first (their scan
             // runs before the x and B tiles are needed); the others read nothing
@@ -1268,6 +1266,15 @@ void state_scan_fast_kernel(
         }
 #pragma unroll
         for (int k = 0; k < Regs::kXV; ++k) R.x[k] = buf_ld16(rx, xo[k]);
+    };
+    auto fetch_b = [&](Regs &R, int c) {
+        const bool any = c < hi;
+        int st;
+        const int len = chunk_at(c, st);
+        c = c < hi ? c : hi - 1;
+        c = c > lo ? c : lo;
+        const rsrc_t rb = make_rsrc(B + ((int64_t)st * G + g) * N + n0,
+                                    any ? (uint32_t)(len - 1) * brow + NSL * 2 : 0u);
 #pragma unroll
         for (int k = 0; k < Regs::kBV; ++k) {
             R.b[k] = buf_ld16(rb, bo[k]);
@@ -1319,9 +1326,10 @@ void state_scan_fast_kernel(
         return jb == 0 ? cd.x : off + cd.x;
     };
 
-    // one iteration: stage chunk c from R into LDS, refill R with chunk c + 1,
-    // then fold chunk c into the running state. An empty sequence makes one pass
-    // over zero tiles (it changes nothing) with its stores switched off.
+    // one iteration: the step's stores, then stage chunk c from R into LDS,
+    // refilling R with chunk c + 1 as each half of it is staged (x, then B), then
+    // fold chunk c into the running state. An empty sequence makes one pass over
+    // zero tiles (it changes nothing) with its stores switched off.
     float F = 0.0f;   // log decay from the block's first chunk to chunk c
     auto step = [&](Regs &R, int c) {
         const bool live = c < hi;
@@ -1335,39 +1343,6 @@ void state_scan_fast_kernel(
             float unused;
             cl = cum_at(len > 0 ? len - 1 : 0, unused);
         }
-        // (u < Q * 8 holds for every thread where 512 (k + 1) <= Q * 8; said so at
-        // compile time, so that no path skips a staging and leaves its registers
-        // counted as loads in flight)
-#pragma unroll
-        for (int k = 0; k < Regs::kXV; ++k) {
-            const int u = tid + 512 * k;
-            if (512 * (k + 1) <= Q * 8 || u < Q * 8) st16(xs + (u >> 3) * LDX + 8 * (u & 7), R.x[k]);
-        }
-#pragma unroll
-        for (int k = 0; k < Regs::kBV; ++k) {
-            const int u = tid + 512 * k;
-            if (512 * (k + 1) <= Q * 8 || u < Q * 8) {
-                const int t = u >> 3;
-                float cmt, dtt;
-                if constexpr (OWN) {
-                    cmt = cum_at(t, dtt);
-                } else {
-                    cmt = R.cm[k];
-                    dtt = R.dt[k];
-                }
-                const float w = t < len ? __expf(cl - cmt) * dtt : 0.0f;
-                const uint32_t w4[4] = {R.b[k].x, R.b[k].y, R.b[k].z, R.b[k].w};
-                float f[8];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    f[2 * i] = __uint_as_float(w4[i] << 16) * w;
-                    f[2 * i + 1] = __uint_as_float(w4[i] & 0xffff0000u) * w;
-                }
-                Vec16<bf16>::store(bs + t * LDB + 8 * (u & 7), f);
-            }
-        }
-        const float decay = __expf(cl);
-
         // Every store of the step is issued here, before the next chunk's loads:
         // the memory operations issued after those loads are then only loads,
         // which the compiler counts exactly, and its waits for them never wait
@@ -1418,7 +1393,42 @@ void state_scan_fast_kernel(
             }
             F += cl;
         }
-        fetch(R, c + 1);
+        // Staging (u < Q * 8 holds for every thread where 512 (k + 1) <= Q * 8; said
+        // so at compile time, so that no path skips a staging and leaves its
+        // registers counted as loads in flight)
+#pragma unroll
+        for (int k = 0; k < Regs::kXV; ++k) {
+            const int u = tid + 512 * k;
+            if (512 * (k + 1) <= Q * 8 || u < Q * 8) st16(xs + (u >> 3) * LDX + 8 * (u & 7), R.x[k]);
+        }
+        fetch_x(R, c + 1);   // (R.x is free again: the next chunk's x is in flight
+                             //  while B is scaled and staged)
+#pragma unroll
+        for (int k = 0; k < Regs::kBV; ++k) {
+            const int u = tid + 512 * k;
+            if (512 * (k + 1) <= Q * 8 || u < Q * 8) {
+                const int t = u >> 3;
+                float cmt, dtt;
+                if constexpr (OWN) {
+                    cmt = cum_at(t, dtt);
+                } else {
+                    cmt = R.cm[k];
+                    dtt = R.dt[k];
+                }
+                const float w = t < len ? __expf(cl - cmt) * dtt : 0.0f;
+                const uint32_t w4[4] = {R.b[k].x, R.b[k].y, R.b[k].z, R.b[k].w};
+                float f[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    f[2 * i] = __uint_as_float(w4[i] << 16) * w;
+                    f[2 * i + 1] = __uint_as_float(w4[i] & 0xffff0000u) * w;
+                }
+                Vec16<bf16>::store(bs + t * LDB + 8 * (u & 7), f);
+            }
+        }
+        const float decay = __expf(cl);
+
+        fetch_b(R, c + 1);
         __syncthreads();
 
 #pragma unroll
@@ -1455,7 +1465,8 @@ void state_scan_fast_kernel(
     // loop body runs at least once, so no branch separates these loads from their
     // use and the compiler's wait counts stay exact.
     Regs R;
-    fetch(R, lo);
+    fetch_x(R, lo);
+    fetch_b(R, lo);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (OWN) scan_chunk(R, lo);
     const bool read_init = slot_ok && has_init != nullptr && hflag != 0 && b == 0;
