@@ -1241,14 +1241,21 @@ void state_scan_fast_kernel(
     // Loads of chunk c's tiles through buffer resources that end at the chunk's
     // last row: rows past it read as zero. Past the last chunk (and for a
     // sequence with no chunk) every resource is empty and nothing is read.
-    auto fetch_x = [&](Regs &R, int c) {
+    auto fetch_xv = [&](uint4 *xr, int c) {
+        const bool any = c < hi;
+        int st;
+        const int len = chunk_at(c, st);
+        const rsrc_t rx = make_rsrc(x + ((int64_t)st * H + h) * P,
+                                    any ? (uint32_t)(len - 1) * xrow + P * 2 : 0u);
+#pragma unroll
+        for (int k = 0; k < Regs::kXV; ++k) xr[k] = buf_ld16(rx, xo[k]);
+    };
+    auto fetch_dt = [&](Regs &R, int c) {
         const bool any = c < hi;
         int st;
         const int len = chunk_at(c, st);
         c = c < hi ? c : hi - 1;
         c = c > lo ? c : lo;
-        const rsrc_t rx = make_rsrc(x + ((int64_t)st * H + h) * P,
-                                    any ? (uint32_t)(len - 1) * xrow + P * 2 : 0u);
         if constexpr (OWN) {
             // raw dt of position 64 w + lane for waves w < J first (their scan
             // runs before the x and B tiles are needed); the others read nothing
@@ -1264,8 +1271,6 @@ void state_scan_fast_kernel(
             // MFMA phase and stall them on global latency)
             R.cl = buf_ldf(rc, (uint32_t)(len - 1) * 4);
         }
-#pragma unroll
-        for (int k = 0; k < Regs::kXV; ++k) R.x[k] = buf_ld16(rx, xo[k]);
     };
     auto fetch_b = [&](Regs &R, int c) {
         const bool any = c < hi;
@@ -1326,12 +1331,13 @@ void state_scan_fast_kernel(
         return jb == 0 ? cd.x : off + cd.x;
     };
 
-    // one iteration: the step's stores, then stage chunk c from R into LDS,
-    // refilling R with chunk c + 1 as each half of it is staged (x, then B), then
-    // fold chunk c into the running state. An empty sequence makes one pass over
-    // zero tiles (it changes nothing) with its stores switched off.
+    // one iteration: the step's stores, then stage chunk c into LDS - x from the
+    // register set xcur, refilled with chunk c + 2 (the two sets alternate), B
+    // from R.b, refilled with chunk c + 1, dt one chunk ahead too - then fold
+    // chunk c into the running state. An empty sequence makes one pass over zero
+    // tiles (it changes nothing) with its stores switched off.
     float F = 0.0f;   // log decay from the block's first chunk to chunk c
-    auto step = [&](Regs &R, int c) {
+    auto step = [&](Regs &R, uint4 *xcur, int c) {
         const bool live = c < hi;
         const int st = first + chunk_off(c);
         const int len = end - st < chunk_cap(c) ? end - st : chunk_cap(c);
@@ -1396,13 +1402,13 @@ void state_scan_fast_kernel(
         // Staging (u < Q * 8 holds for every thread where 512 (k + 1) <= Q * 8; said
         // so at compile time, so that no path skips a staging and leaves its
         // registers counted as loads in flight)
+        fetch_dt(R, c + 1);
 #pragma unroll
         for (int k = 0; k < Regs::kXV; ++k) {
             const int u = tid + 512 * k;
-            if (512 * (k + 1) <= Q * 8 || u < Q * 8) st16(xs + (u >> 3) * LDX + 8 * (u & 7), R.x[k]);
+            if (512 * (k + 1) <= Q * 8 || u < Q * 8) st16(xs + (u >> 3) * LDX + 8 * (u & 7), xcur[k]);
         }
-        fetch_x(R, c + 1);   // (R.x is free again: the next chunk's x is in flight
-                             //  while B is scaled and staged)
+        fetch_xv(xcur, c + 2);   // (x two chunks ahead, in the set just staged)
 #pragma unroll
         for (int k = 0; k < Regs::kBV; ++k) {
             const int u = tid + 512 * k;
@@ -1465,8 +1471,11 @@ void state_scan_fast_kernel(
     // loop body runs at least once, so no branch separates these loads from their
     // use and the compiler's wait counts stay exact.
     Regs R;
-    fetch_x(R, lo);
+    uint4 x2[Regs::kXV];
+    fetch_dt(R, lo);
+    fetch_xv(R.x, lo);
     fetch_b(R, lo);
+    fetch_xv(x2, lo + 1);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (OWN) scan_chunk(R, lo);
     const bool read_init = slot_ok && has_init != nullptr && hflag != 0 && b == 0;
@@ -1476,7 +1485,9 @@ void state_scan_fast_kernel(
         for (int e = 0; e < 4; ++e) acc[j][e] = read_init ? iv[j][e] : 0.0f;
     int c = lo;
     do {
-        step(R, c);
+        step(R, R.x, c);
+        if (++c >= hi) break;
+        step(R, x2, c);
     } while (++c < hi);
     if constexpr (CKPT) {
         // the last chunk's checkpoint (the others were written one step later,
