@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 2
+#define SSD_ABI_VERSION 3
 
 enum ssd_status {
     SSD_OK = 0,
@@ -152,11 +152,12 @@ typedef struct {
  *   trace         per-launch timing events (ssd_launch_trace below)
  * Rounding: x becomes the fp16 value above or below it in magnitude, the
  * farther one with probability (|x| - |lo|) / (|hi| - |lo|), drawn as
- * (w >> 8) / 2^24 from a 32-bit word w (non-finite values and |x| > 65504
- * round to nearest even). Element e of a destination array of kind k takes
- * word e mod 4 of Philox4x32-R(counter = (e/4 low, e/4 high, k, 0), key =
- * seed); kinds: 0 final states, 1 checkpoints, 2 per-token states,
- * 3 ReplaySSM checkpoints. e is the flat element index in that array.
+ * d / 2^16 from a 16-bit draw d (non-finite values and |x| > 65504 round to
+ * nearest even). Element e of a destination array of kind k takes the 16-bit
+ * half e mod 2 (low half first) of word (e/2) mod 4 of
+ * Philox4x32-R(counter = (e/8 low, e/8 high, k, 0), key = seed); kinds:
+ * 0 final states, 1 checkpoints, 2 per-token states, 3 ReplaySSM checkpoints.
+ * e is the flat element index in that array.
  */
 /*
  * Per-launch timing of a prefill call (ssd_options.trace; profiling only): the

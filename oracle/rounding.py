@@ -15,16 +15,23 @@ They define neither the rounding nor the stream layout; the readings here:
   (|x| - |lo|) / (|hi| - |lo|) and lo otherwise, so its expectation is x.
   The probability is exact in float32 (a difference of nearby floats over a
   power of two). Non-finite values and |x| > 65504 round to nearest even.
-* The uniform draw is u = (w >> 8) / 2^24 from a 32-bit word w; round up when
-  u < probability.
-* Words come from Philox4x32 with R rounds (Salmon, Moraes, Dror, Shaw,
+* The uniform draw is u = d / 2^16 from a 16-bit draw d; round up when
+  u < probability. The probability is a multiple of 2^-13 wherever the fp16
+  spacing is that of a normal number (|x - lo| is a multiple of the float32
+  spacing, 2^-23 of the binade, and |hi - lo| is 2^-10 of it), and of at most
+  2^-16 for |x| >= 2^-17, so there the draw is exactly unbiased; below 2^-17
+  the chance of rounding up is the probability rounded up to a multiple of
+  2^-16.
+* Draws come from Philox4x32 with R rounds (Salmon, Moraes, Dror, Shaw,
   "Parallel random numbers: as easy as 1, 2, 3", SC 2011): a 128-bit counter,
   a 64-bit key, per round two 32x32 -> 64-bit products with the multipliers
   0xD2511F53 and 0xCD9E8D57, the key bumped by 0x9E3779B9 and 0xBB67AE85
   between rounds. Element e of a destination array of kind k (0 final states,
-  1 checkpoints, 2 per-token states, 3 ReplaySSM checkpoints) takes word
-  e mod 4 of Philox(counter = (e // 4 low 32 bits, e // 4 high 32 bits, k, 0),
-  key = (seed low 32 bits, seed high 32 bits)).
+  1 checkpoints, 2 per-token states, 3 ReplaySSM checkpoints) takes the 16-bit
+  half e mod 2 (the low half first) of word (e // 2) mod 4 of
+  Philox(counter = (e // 8 low 32 bits, e // 8 high 32 bits, k, 0),
+  key = (seed low 32 bits, seed high 32 bits)): one call serves 8 consecutive
+  elements.
 """
 from __future__ import annotations
 
@@ -53,15 +60,18 @@ def philox4x32(counter, key, rounds: int = 10):
     return np.stack([v.astype(np.uint32) for v in c], axis=-1)
 
 
-def words_for(n: int, seed: int, kind: int, rounds: int, first: int = 0) -> np.ndarray:
-    """The 32-bit words of elements first .. first + n - 1 of a destination array."""
+def draws_for(n: int, seed: int, kind: int, rounds: int, first: int = 0) -> np.ndarray:
+    """The 16-bit draws (as uint32 below 2^16) of elements first .. first + n - 1
+    of a destination array."""
     e = np.arange(first, first + n, dtype=np.uint64)
-    blk = e // np.uint64(4)
+    blk = e // np.uint64(8)
     ctr = np.stack([blk & MASK, blk >> np.uint64(32), np.full_like(blk, kind),
                     np.zeros_like(blk)], axis=-1).astype(np.uint32)
     key = np.array([seed & MASK, (seed >> 32) & MASK], dtype=np.uint32)
     out = philox4x32(ctr, key, rounds)
-    return out[np.arange(n), (e % np.uint64(4)).astype(np.int64)]
+    word = out[np.arange(n), ((e // np.uint64(2)) % np.uint64(4)).astype(np.int64)]
+    half = (e % np.uint64(2)).astype(np.uint32)
+    return (word >> (np.uint32(16) * half)) & np.uint32(0xFFFF)
 
 
 def _f16_neighbours(x32: np.ndarray):
@@ -76,15 +86,15 @@ def _f16_neighbours(x32: np.ndarray):
     return lo, hi
 
 
-def stochastic_round_f16(x, words) -> np.ndarray:
-    """Stochastic rounding of float32 values with the given 32-bit words."""
+def stochastic_round_f16(x, draws) -> np.ndarray:
+    """Stochastic rounding of float32 values with the given 16-bit draws."""
     x32 = np.asarray(x, dtype=np.float32)
-    words = np.asarray(words, dtype=np.uint32)
+    draws = np.asarray(draws, dtype=np.uint32)
     lo, hi = _f16_neighbours(x32)
     a, l32, h32 = np.abs(x32), np.abs(lo.astype(np.float32)), np.abs(hi.astype(np.float32))
     with np.errstate(invalid="ignore", divide="ignore"):
         prob = (a - l32) / (h32 - l32)
-    u = (words >> np.uint32(8)).astype(np.float32) * np.float32(2.0 ** -24)
+    u = draws.astype(np.float32) * np.float32(2.0 ** -16)
     out = np.where(u < prob, hi, lo)
     plain = ~np.isfinite(x32) | (a > np.float32(65504.0)) | (a == l32)
     with np.errstate(over="ignore"):

@@ -132,9 +132,12 @@ __global__ __launch_bounds__(256) void state_update_kernel(
                 if (inter && tid + 256 * k < NCH) {
                     // written once and read only by a later rollback: stream past the caches
                     const int64_t io = (rt * H + h) * PN + (int64_t)pk[k] * N + n0;
-                    if (std::is_same<TS, f16>::value && srk.rounds > 0)
-                        put_run<TS, 8>(inter + io, st[k], srk, (uint64_t)io, kSrStates);
-                    else
+                    if constexpr (std::is_same<TS, f16>::value) {
+                        if (srk.rounds > 0)
+                            store8_sr_nt(inter + io, st[k], srk, (uint64_t)io, kSrStates);
+                        else
+                            store8_nt(inter + io, st[k]);
+                    } else
                         store8_nt(inter + io, st[k]);
                 }
             }
@@ -252,32 +255,34 @@ void launch_state_commit(const DecodeDims &d, void *cache, const int32_t *idx, c
 }
 
 // fp32 -> fp16 of n values with the state stores' rounding (element e of
-// stream `kind`), 4 values per thread.
+// stream `kind`), 8 values (one Philox call) per thread.
 __global__ __launch_bounds__(256) void round_f16_kernel(const float *__restrict__ in,
                                                         f16 *__restrict__ out, int64_t n, SrCtx sr,
                                                         int kind)
 {
-    const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
     if (e0 >= n) return;
     const SrKey srk = sr_key_checked(sr);   // (in may hold fewer than 8 bytes)
-    if (e0 + 4 <= n && (reinterpret_cast<uintptr_t>(out + e0) & 7u) == 0) {
-        const float v[4] = {in[e0], in[e0 + 1], in[e0 + 2], in[e0 + 3]};
-        put4<f16>(out + e0, v, srk, (uint64_t)e0, (uint32_t)kind);
+    if (e0 + 8 <= n && (reinterpret_cast<uintptr_t>(out + e0) & 15u) == 0) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = in[e0 + j];
+        put_run<f16, 8>(out + e0, v, srk, (uint64_t)e0, (uint32_t)kind);
         return;
     }
-    const uint64_t blk = (uint64_t)e0 >> 2;
-    const uint4 w = philox4x32(make_uint4((uint32_t)blk, (uint32_t)(blk >> 32), (uint32_t)kind, 0u),
-                               srk.k0, srk.k1, srk.rounds);
+    const uint4 w = sr_words(srk, (uint64_t)e0, (uint32_t)kind);
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-    for (int j = 0; j < 4 && e0 + j < n; ++j)
-        out[e0 + j] = srk.rounds > 0 ? sr_f16(in[e0 + j], ws[j]) : static_cast<f16>(in[e0 + j]);
+    for (int j = 0; j < 8 && e0 + j < n; ++j) {
+        const uint32_t d = (j & 1) ? sr_hi16(ws[j >> 1]) : sr_lo16(ws[j >> 1]);
+        out[e0 + j] = srk.rounds > 0 ? sr_f16(in[e0 + j], d) : static_cast<f16>(in[e0 + j]);
+    }
 }
 
 void launch_round_f16(const float *in, void *out, int64_t n, const SrCtx &sr, int kind,
                       void *stream)
 {
     if (n <= 0) return;
-    const int64_t groups = (n + 3) / 4;
+    const int64_t groups = (n + 7) / 8;
     hipLaunchKernelGGL(round_f16_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0,
                        reinterpret_cast<hipStream_t>(stream), in, static_cast<f16 *>(out), n, sr,
                        kind);

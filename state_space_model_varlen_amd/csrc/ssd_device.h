@@ -207,8 +207,10 @@ template <> __device__ __forceinline__ void store4<f16>(f16 *p, const float *v) 
 // numbers: as easy as 1, 2, 3", SC 2011): per round two 32 x 32 -> 64-bit
 // products of counter words with fixed multipliers, the high halves mixed with
 // the other counter words and the key, the key bumped by two Weyl constants
-// between rounds. Element e of a destination array of kind k takes word e % 4
-// of Philox(counter = (e / 4 low, e / 4 high, k, 0), key = seed).
+// between rounds. Element e of a destination array of kind k takes the 16-bit
+// half e % 2 (low half first) of word (e / 2) % 4 of
+// Philox(counter = (e / 8 low, e / 8 high, k, 0), key = seed): one call draws
+// for 8 consecutive elements.
 __device__ __forceinline__ uint4 philox4x32(uint4 c, uint32_t k0, uint32_t k1, int rounds)
 {
     for (int r = 0; r < rounds; ++r) {
@@ -226,23 +228,74 @@ __device__ __forceinline__ uint4 philox4x32(uint4 c, uint32_t k0, uint32_t k1, i
 }
 
 // x rounded to one of the two fp16 values bracketing it: the one away from zero
-// with probability (|x| - |lo|) / (|hi| - |lo|) (exact in float32: a difference of
-// nearby floats over a power of two), drawn as (w >> 8) / 2^24 < probability.
-// Non-finite values and |x| > 65504 round to nearest even.
-__device__ __forceinline__ f16 sr_f16(float x, uint32_t w)
+// with probability (|x| - |lo|) / (|hi| - |lo|), taken when d / 2^16 < probability
+// for a 16-bit draw d (d < 2^16). The probability has at most 13 fractional bits
+// for normal fp16 spacings and at most 16 for |x| >= 2^-17, so there the draw is
+// exactly unbiased. Non-finite values and |x| > 65504 round to nearest even.
+//
+// Without branches or fp16 conversions on the stochastic side:
+// - fp16 normal range (|x| >= 2^-14): the probability is L / 2^13 for the 13
+//   float32 mantissa bits L that fp16 drops, and d / 2^16 < L / 2^13 exactly
+//   when (d >> 3) < L, i.e. when adding 8191 - (d >> 3) to |x|'s bits carries
+//   into the kept bits; truncating then gives hi (the carry may step the
+//   exponent, as it should) or lo. The fp16 bits are the float32 bits shifted
+//   by 13 with the exponent rebased by 127 - 15 = 112.
+// - below 2^-14 (fp16 subnormals, spacing 2^-24): t = |x| 2^24 is exact, lo is
+//   floor(t) units of 2^-24 and the probability is t - floor(t), both exact.
+__device__ __forceinline__ f16 sr_f16(float x, uint32_t d)
 {
-    const float a = fabsf(x);
-    const f16 rne = static_cast<f16>(x);
-    if (!(a <= 65504.0f)) return rne;
-    const uint16_t bits = __builtin_bit_cast(uint16_t, rne);
-    const uint16_t lob = fabsf(static_cast<float>(rne)) > a ? (uint16_t)(bits - 1) : bits;
-    const float l = fabsf(static_cast<float>(__builtin_bit_cast(f16, lob)));
-    const float h = fabsf(static_cast<float>(__builtin_bit_cast(f16, (uint16_t)(lob + 1))));
-    // u < (a - l) / (h - l), taken as u (h - l) < a - l: h - l is a power of two
-    // (the fp16 spacing below h) and a - l is exact, so both sides are exact and
-    // the test is the same as with the quotient, without a division
-    const float u = static_cast<float>(w >> 8) * 0x1p-24f;
-    return __builtin_bit_cast(f16, (a != l && u * (h - l) < a - l) ? (uint16_t)(lob + 1) : lob);
+    const uint32_t xb = __builtin_bit_cast(uint32_t, x);
+    const uint32_t ab = xb & 0x7FFFFFFFu;
+    const float a = __builtin_bit_cast(float, ab);
+    const uint32_t nb = ((ab + (8191u - (d >> 3))) >> 13) - (112u << 10);
+    const float t = fminf(a, 0x1p-14f) * 0x1p24f;     // (clamped: used below 2^-14 only)
+    const float fl = floorf(t);
+    const uint32_t sb = (uint32_t)fl + (static_cast<float>(d) * 0x1p-16f < t - fl ? 1u : 0u);
+    const uint32_t mag = a < 0x1p-14f ? sb : nb;
+    const uint16_t res = (uint16_t)(mag | ((xb >> 16) & 0x8000u));
+    return a <= 65504.0f ? __builtin_bit_cast(f16, res) : static_cast<f16>(x);
+}
+
+// M values (M even) rounded as by sr_f16, packed two fp16 values per word
+// (value 2 j in the low half of out[j]); value 2 j draws the low 16 bits of
+// w[j], value 2 j + 1 the high 16 bits. In the fp16 normal range
+// (2^-14 <= |x| <= 65504) only the carry step runs: t = (bits(x) + 8191 -
+// (d >> 3)) >> 13 holds |x|'s kept bits in its low 16 (the sign bit 31 does
+// not reach them), and adding 0x4000 modulo 2^16 rebases the exponent
+// (t - (112 << 10)). The general rule runs behind a wave-uniform branch,
+// when some lane holds a value outside that range.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+template <int M>
+__device__ __forceinline__ void sr_f16_pairs(const float *v, const uint32_t *w, uint32_t *out)
+{
+    static_assert(M % 2 == 0, "pairs");
+    uint32_t xb[M], worst = 0;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        xb[i] = __builtin_bit_cast(uint32_t, v[i]);
+        // 2 (|x| bits - bits(2^-14)), modulo 2^32: above 2 (bits(65504) - bits(2^-14))
+        // for |x| < 2^-14, |x| > 65504, infinities and NaNs
+        const uint32_t off = (xb[i] << 1) - (0x38800000u << 1);
+        worst = off > worst ? off : worst;
+    }
+    if (__builtin_amdgcn_ballot_w64(worst > ((0x477FE000u - 0x38800000u) << 1)) == 0) {
+#pragma unroll
+        for (int j = 0; j < M / 2; ++j) {
+            const uint32_t ta = (xb[2 * j] + (((w[j] >> 3) & 0x1FFFu) ^ 0x1FFFu)) >> 13;
+            const uint32_t tb = (xb[2 * j + 1] + ((w[j] >> 19) ^ 0x1FFFu)) >> 13;
+            u16x2 m = {(unsigned short)ta, (unsigned short)tb};
+            m += (u16x2){0x4000, 0x4000};
+            const uint32_t sign = ((xb[2 * j] >> 16) & 0x8000u) | (xb[2 * j + 1] & 0x80000000u);
+            out[j] = __builtin_bit_cast(uint32_t, m) | sign;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < M / 2; ++j) {
+            const uint32_t lo = __builtin_bit_cast(uint16_t, sr_f16(v[2 * j], w[j] & 0xFFFFu));
+            const uint32_t hi = __builtin_bit_cast(uint16_t, sr_f16(v[2 * j + 1], w[j] >> 16));
+            out[j] = lo | (hi << 16);
+        }
+    }
 }
 
 // Philox streams of the state arrays a kernel writes
@@ -278,6 +331,15 @@ __device__ __forceinline__ SrKey sr_key_checked(const SrCtx &c)
     return k;
 }
 
+// The four words that draw for elements 8 (e / 8) .. 8 (e / 8) + 7 of stream kind.
+__device__ __forceinline__ uint4 sr_words(const SrKey &k, uint64_t e, uint32_t kind) {
+    const uint64_t blk = e >> 3;
+    return philox4x32(make_uint4((uint32_t)blk, (uint32_t)(blk >> 32), kind, 0u), k.k0, k.k1,
+                      k.rounds);
+}
+__device__ __forceinline__ uint32_t sr_lo16(uint32_t w) { return w & 0xFFFFu; }
+__device__ __forceinline__ uint32_t sr_hi16(uint32_t w) { return w >> 16; }
+
 // 4 consecutive state values to storage; e = flat index of the first one in the
 // destination array (a multiple of 4), kind = its stream. Only fp16 stores round
 // stochastically.
@@ -292,16 +354,30 @@ __device__ __forceinline__ void put4<f16>(f16 *p, const float *v, const SrKey &k
         store4<f16>(p, v);
         return;
     }
-    const uint64_t blk = e >> 2;
-    const uint4 w = philox4x32(make_uint4((uint32_t)blk, (uint32_t)(blk >> 32), kind, 0u), k.k0,
-                               k.k1, k.rounds);
-    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-    f16x4 q;
-    q[0] = sr_f16(v[0], w.x);
-    q[1] = sr_f16(v[1], w.y);
-    q[2] = sr_f16(v[2], w.z);
-    q[3] = sr_f16(v[3], w.w);
-    *reinterpret_cast<f16x4 *>(p) = q;
+    const uint4 w = sr_words(k, e, kind);
+    // elements 8 (e / 8) .. + 3 take words 0 and 1, the next four words 2 and 3
+    const bool upper = (e >> 2) & 1;
+    const uint32_t ws[2] = {upper ? w.z : w.x, upper ? w.w : w.y};
+    uint32_t q[2];
+    sr_f16_pairs<4>(v, ws, q);
+    *reinterpret_cast<uint2 *>(p) = make_uint2(q[0], q[1]);
+}
+// 8 consecutive state values (elements e .. e + 7 of stream kind, e a multiple
+// of 8) stochastically rounded to fp16 with one Philox call, as 16 bytes;
+// k.rounds > 0.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f16x8 sr8_f16(const float *v, const SrKey &k, uint64_t e,
+                                         uint32_t kind) {
+    const uint4 w = sr_words(k, e, kind);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    uint32_t q[4];
+    sr_f16_pairs<8>(v, ws, q);
+    return __builtin_bit_cast(f16x8, make_uint4(q[0], q[1], q[2], q[3]));
+}
+// The same stored at p (16-byte aligned)
+__device__ __forceinline__ void put8_sr(f16 *p, const float *v, const SrKey &k, uint64_t e,
+                                        uint32_t kind) {
+    *reinterpret_cast<f16x8 *>(p) = sr8_f16(v, k, e, kind);
 }
 
 // ---------------------------------------------------------------------------
@@ -362,14 +438,19 @@ template <typename T, int M> __device__ __forceinline__ void store_run(T *p, con
 #pragma unroll
     for (int i = 0; i < M / E; ++i) Vec16<T>::store(p + E * i, v + E * i);
 }
-// M consecutive state values (M a multiple of 4, e as for put4)
+// M consecutive state values (M a multiple of 8, e a multiple of 8, p 16-byte
+// aligned for fp16)
 template <typename T, int M>
 __device__ __forceinline__ void put_run(T *p, const float *v, const SrKey &k, uint64_t e,
                                         uint32_t kind) {
     if constexpr (std::is_same<T, f16>::value) {
-        static_assert(M % 4 == 0, "runs of 4");
+        static_assert(M % 8 == 0, "runs of 8");
+        if (k.rounds == 0) {
+            store_run<f16, M>(p, v);
+            return;
+        }
 #pragma unroll
-        for (int i = 0; i < M / 4; ++i) put4<f16>(p + 4 * i, v + 4 * i, k, e + 4 * i, kind);
+        for (int i = 0; i < M / 8; ++i) put8_sr(p + 8 * i, v + 8 * i, k, e + 8 * i, kind);
     } else {
         store_run<T, M>(p, v);
     }

@@ -23,6 +23,12 @@ __device__ __forceinline__ void store8_nt(f16 *p, const float *v) {
     for (int i = 0; i < 8; ++i) q[i] = static_cast<f16>(v[i]);
     __builtin_nontemporal_store(__builtin_bit_cast(u32x4, q), reinterpret_cast<u32x4 *>(p));
 }
+// 8 fp16 values with stochastic rounding (elements e .. e + 7 of stream kind)
+__device__ __forceinline__ void store8_sr_nt(f16 *p, const float *v, const SrKey &k, uint64_t e,
+                                             uint32_t kind) {
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sr8_f16(v, k, e, kind)),
+                                reinterpret_cast<u32x4 *>(p));
+}
 __device__ __forceinline__ void store8_nt(float *p, const float *v) {
     const f32x4 lo = {v[0], v[1], v[2], v[3]}, hi = {v[4], v[5], v[6], v[7]};
     __builtin_nontemporal_store(lo, reinterpret_cast<f32x4 *>(p));

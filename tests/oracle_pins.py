@@ -475,22 +475,25 @@ def pin_philox_known_answers(lib=None, rnd=None):
         key = np.array([int(v, 16) for v in cs["key"]], dtype=np.uint32)
         got = r.philox4x32(ctr, key, 10)
         assert [int(v) for v in got] == [int(v, 16) for v in cs["out"]], cs
-    # element e of stream k takes word e % 4 of the block e // 4
+    # element e of stream k takes the 16-bit half e % 2 (low first) of word
+    # (e // 2) % 4 of the block e // 8
     seed, kind = 0x0123456789ABCDEF, 3
-    w = r.words_for(11, seed, kind, 7, first=(1 << 34) + 2)
-    for j, e in enumerate(range((1 << 34) + 2, (1 << 34) + 13)):
-        blk = e // 4
+    d = r.draws_for(21, seed, kind, 7, first=(1 << 35) + 3)
+    for j, e in enumerate(range((1 << 35) + 3, (1 << 35) + 24)):
+        blk = e // 8
         ctr = np.array([blk & 0xFFFFFFFF, blk >> 32, kind, 0], dtype=np.uint32)
         key = np.array([seed & 0xFFFFFFFF, seed >> 32], dtype=np.uint32)
-        assert int(w[j]) == int(r.philox4x32(ctr, key, 7)[e % 4])
+        word = int(r.philox4x32(ctr, key, 7)[(e // 2) % 4])
+        assert int(d[j]) == (word >> (16 * (e % 2))) & 0xFFFF
 
 
 def pin_stochastic_rounding(lib=None, rnd=None):
     """fp32 -> fp16 stochastic rounding: the two candidates are the fp16 values
     bracketing x (found by brute force over every finite fp16 value), the draw
-    u = (w >> 8) / 2^24 goes up exactly when u < (|x| - |lo|) / (|hi| - |lo|),
-    representable and special values pass unchanged or round to nearest, and the
-    mean over random words is x."""
+    u = d / 2^16 goes up exactly when u < (|x| - |lo|) / (|hi| - |lo|), that
+    probability has at most 16 fractional bits for |x| >= 2^-17 (so a 16-bit
+    draw is exactly unbiased there), representable and special values pass
+    unchanged or round to nearest, and the mean over random draws is x."""
     r = rnd or oracle_rounding
     allh = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
     fin = np.unique(allh[np.isfinite(allh)].astype(np.float32))
@@ -503,14 +506,18 @@ def pin_stochastic_rounding(lib=None, rnd=None):
     lo_mag, hi_mag = fin[i], fin[np.minimum(i + 1, len(fin) - 1)]
     sign = np.where(x < 0, -1.0, 1.0).astype(np.float32)
     up = r.stochastic_round_f16(x, np.zeros(len(x), np.uint32)).astype(np.float32)
-    down = r.stochastic_round_f16(x, np.full(len(x), 0xFFFFFFFF, np.uint32)).astype(np.float32)
+    down = r.stochastic_round_f16(x, np.full(len(x), 0xFFFF, np.uint32)).astype(np.float32)
     np.testing.assert_array_equal(down, sign * lo_mag)
     np.testing.assert_array_equal(up[~exact], (sign * hi_mag)[~exact])
     np.testing.assert_array_equal(up[exact], x[exact])
+    # the probability's fractional bits, measured in float64 from the bracket
+    big = np.abs(x) >= 2.0 ** -17
+    prob = ((np.abs(x).astype(np.float64) - lo_mag) / (hi_mag - lo_mag))[big & ~exact]
+    assert np.all(prob * 2.0 ** 16 == np.floor(prob * 2.0 ** 16))
     # the threshold: x half way between neighbours goes up for u just below 1/2 only
     half = np.float32(1.0 + 2.0 ** -11)                          # fp16 ulp at 1 is 2^-10
-    w_lo = np.array([(2 ** 23 - 1) << 8], np.uint32)
-    w_hi = np.array([(2 ** 23) << 8], np.uint32)
+    w_lo = np.array([2 ** 15 - 1], np.uint32)
+    w_hi = np.array([2 ** 15], np.uint32)
     assert float(r.stochastic_round_f16(np.array([half]), w_lo)[0]) == 1.0 + 2.0 ** -10
     assert float(r.stochastic_round_f16(np.array([half]), w_hi)[0]) == 1.0
     assert float(r.stochastic_round_f16(np.array([-half]), w_lo)[0]) == -(1.0 + 2.0 ** -10)
@@ -521,7 +528,7 @@ def pin_stochastic_rounding(lib=None, rnd=None):
     assert np.isnan(r.stochastic_round_f16(np.array([np.nan], np.float32), [0])[0])
     # unbiased: 4096 random words per value
     xs = np.repeat(x[:64], 4096)
-    ws = g.integers(0, 2 ** 32, size=len(xs), dtype=np.uint64).astype(np.uint32)
+    ws = g.integers(0, 2 ** 16, size=len(xs), dtype=np.uint64).astype(np.uint32)
     mean = r.stochastic_round_f16(xs, ws).astype(np.float64).reshape(64, 4096).mean(axis=1)
     ulp = (hi_mag - lo_mag)[:64].astype(np.float64)
     assert np.all(np.abs(mean - x[:64]) <= 6 * 0.5 * ulp / 64.0 + 1e-12)

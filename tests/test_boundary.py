@@ -30,7 +30,7 @@ def test_header_functions_are_exported():
 
 
 def test_version_and_status_strings():
-    assert ssd.abi_version() == 2
+    assert ssd.abi_version() == 3
     for s in range(9):
         assert ssd.status_string(s) != "unknown status"
     assert ssd.status_string(99) == "unknown status"

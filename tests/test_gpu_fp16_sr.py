@@ -38,13 +38,18 @@ def test_round_f16_bit_exact(seed, rounds, kind):
     x = np.concatenate([g.standard_normal(3000) * 0.03, g.standard_normal(500) * 300.0,
                         g.uniform(-6e-5, 6e-5, 400), g.uniform(-3e-7, 3e-7, 60),
                         np.arange(-8, 8, dtype=np.float32) / 8,       # exact fp16 values
+                        # across the subnormal / normal boundary 2^-14, fp32 subnormals,
+                        # multiples of the subnormal spacing 2^-24, the top binade
+                        np.float32(2.0 ** -14) * (1 + g.uniform(-3e-3, 3e-3, 200)),
+                        g.standard_normal(40) * 1e-40, np.arange(-5, 6) * 2.0 ** -25,
+                        g.uniform(65400.0, 65504.0, 60), [65504.0, -65504.0, 65519.0, 65520.0],
                         [np.inf, -np.inf, np.nan, 70000.0, 65510.0, 0.0, -0.0]]).astype(np.float32)
     n = len(x) - 1                       # a ragged tail (not a multiple of 4)
     xg = torch.from_numpy(x[:n]).to(DEV)
     out = torch.empty(n, dtype=F16, device=DEV)
     ssd.ssd_round_f16(xg, out, sr_seed=_seed(seed), sr_rounds=rounds, kind=kind)
     torch.cuda.synchronize()
-    want = rnd.stochastic_round_f16(x[:n], rnd.words_for(n, _u64(seed), kind, rounds))
+    want = rnd.stochastic_round_f16(x[:n], rnd.draws_for(n, _u64(seed), kind, rounds))
     got = out.cpu().numpy()
     assert np.array_equal(got.view(np.uint16), want.view(np.uint16)), \
         int(np.sum(got.view(np.uint16) != want.view(np.uint16)))
@@ -109,7 +114,8 @@ def test_prefill_fp32_inputs_fp16_cache_within_one_step():
     # deterministic for a seed, different for another
     _, after2, ck2 = _prefill(inp, cache, Q, seed=12345)
     assert torch.equal(after2.view(torch.int16), after.view(torch.int16))
-    assert torch.equal(ck2.view(torch.int16), ck.view(torch.int16))
+    nck = len(ref["ckpt"])            # rows past the last checkpoint are never written
+    assert torch.equal(ck2[:nck].view(torch.int16), ck[:nck].view(torch.int16))
     _, after3, _ = _prefill(inp, cache, Q, seed=54321)
     assert not torch.equal(after3[used].view(torch.int16), after[used].view(torch.int16))
 
@@ -145,7 +151,8 @@ def test_prefill_bf16_fused_path_fp16_cache():
     assert_close(ck[:len(ref["ckpt"])], ref["ckpt"], BF16, "checkpoints")
     _, after2, ck2 = _prefill(inp, cache, Q, seed=99, rounds=5)
     assert torch.equal(after2.view(torch.int16), after.view(torch.int16))
-    assert torch.equal(ck2.view(torch.int16), ck.view(torch.int16))
+    nck = len(ref["ckpt"])            # rows past the last checkpoint are never written
+    assert torch.equal(ck2[:nck].view(torch.int16), ck[:nck].view(torch.int16))
 
 
 def test_prefill_bf16_segmented_fp16_cache():
@@ -178,7 +185,8 @@ def test_prefill_bf16_short_path_fp16_cache():
     assert_close(ck[:len(ref["ckpt"])], ref["ckpt"], BF16, "checkpoints")
     _, after2, ck2 = _prefill(inp, cache, Q, seed=31, rounds=5)
     assert torch.equal(after2.view(torch.int16), after.view(torch.int16))
-    assert torch.equal(ck2.view(torch.int16), ck.view(torch.int16))
+    nck = len(ref["ckpt"])            # rows past the last checkpoint are never written
+    assert torch.equal(ck2[:nck].view(torch.int16), ck[:nck].view(torch.int16))
     _, after3, _ = _prefill(inp, cache, Q, seed=32, rounds=5)
     assert not torch.equal(after3[used].view(torch.int16), after[used].view(torch.int16))
 

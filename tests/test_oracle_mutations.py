@@ -201,6 +201,8 @@ ROUNDING_MUTATIONS = [
     ("rounds_toward_the_nearer", "out = np.where(u < prob, hi, lo)",
      "out = np.where(u < 1 - prob, hi, lo)"),
     ("stream_ignored", "np.full_like(blk, kind)", "np.zeros_like(blk)"),
+    ("halves_swapped", "(word >> (np.uint32(16) * half))", "(word >> (np.uint32(16) * (1 - half)))"),
+    ("four_per_call", "blk = e // np.uint64(8)", "blk = e // np.uint64(4)"),
 ]
 
 
