@@ -195,7 +195,7 @@ KERNEL_PATTERNS = [
     (r"state_passing_kernel", "state_passing", PREFILL_SOURCES),
     (r"chunk_state_fast_kernel|chunk_state_kernel", "chunk_state", PREFILL_SOURCES),
     (r"state_update_kernel", "selective_state_update", DECODE_SOURCES),
-    (r"replay_update_fast_kernel|replay_update_kernel", "replay_update", REPLAY_SOURCES),
+    (r"replay_update_wave_kernel|replay_update_kernel", "replay_update", REPLAY_SOURCES),
 ]
 
 

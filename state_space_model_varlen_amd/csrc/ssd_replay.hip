@@ -207,18 +207,25 @@ __global__ __launch_bounds__(256) void replay_update_kernel(
 }
 
 // Verify step for bf16 inputs and checkpoints, P = 64, N = 128, T <= 4 and
-// W <= 16 KT. Block (h, r) of 4 waves; wave w owns state rows p = 16 w .. + 15.
-// Taking the history and the window as one run of tokens k = 0 .. n + T - 1
-// (history first) with lambda_k = A sum_{k' <= k} dt_k', every output is the
-// dual (quadratic) form of the recurrence over that run:
+// W <= 16 KT. Taking the history and the window as one run of tokens
+// k = 0 .. n + T - 1 (history first) with lambda_k = A sum_{k' <= k} dt_k',
+// every output is the dual (quadratic) form of the recurrence over that run:
 //   y_t = exp(lambda_{n+t}) (C_t . ckpt) + D x_t
 //         + sum_{k <= n+t} exp(lambda_{n+t} - lambda_k) dt_k (C_t . B_k) x_k.
 // C . ckpt and C . B are MFMA products (the checkpoint rows are read straight
 // from memory as operand fragments); the decay weights and the sums over at
 // most 16 KT tokens are a few scalars per lane. No state is built per token:
 // the state after the history is formed only when it becomes the checkpoint.
+//
+// One wave per (head, request), four independent waves per block (heads
+// 4 b .. 4 b + 3 of one request). Each wave holds all 64 checkpoint rows as
+// MFMA operand fragments (16 KB of loads in flight per wave), and the
+// (token, token) work - C_t . B_k, lambda, the decay weights - is done once
+// per head. Lane p then forms y_t[p] from coalesced loads of x_k[p] and the
+// weights, broadcast from LDS. Only wave-level synchronisation: a wave past
+// the last head leaves at once.
 template <int KT>
-__global__ __launch_bounds__(256) void replay_update_fast_kernel(
+__global__ __launch_bounds__(256) void replay_update_wave_kernel(
     int T, int H, int G, int num_slots, int W, bf16 *ckpt, bf16 *ring_x, bf16 *ring_dt,
     bf16 *ring_B, const int32_t *__restrict__ cursor, const int32_t *__restrict__ idx,
     const bf16 *__restrict__ x, const bf16 *__restrict__ dt, const float *__restrict__ A,
@@ -226,24 +233,24 @@ __global__ __launch_bounds__(256) void replay_update_fast_kernel(
     bf16 *__restrict__ y)
 {
     constexpr int P = 64, N = 128, NK = 16 * KT;   // token slots: history + window
-    __shared__ float s_dt[4][NK];                  // per wave: dt_k
-    __shared__ float s_lam[4][NK];                 // lambda_k
-    __shared__ float s_g[4][16][NK];               // decay-weighted C_t . B_k
-    __shared__ float s_y[4][16][16];               // C_t . ckpt, row p
-    __shared__ __attribute__((aligned(16))) bf16 s_b[4][NK][N];   // B_k (checkpoint rewrite)
-    const int h = blockIdx.x, r = blockIdx.y;
+    __shared__ float s_g[4][4][NK];                // per wave: weights G[t][k]
+    __shared__ float s_ys[4][4][P];                // C_t . ckpt, [t][p]
+    __shared__ float s_w[4][NK];                   // checkpoint rewrite: token weights
+    __shared__ bf16 s_x[4][NK][P];                 // x_k[p]
+    __shared__ __attribute__((aligned(16))) bf16 s_b[4][NK][N];   // B_k
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int h = 4 * blockIdx.x + w, r = blockIdx.y;
+    if (h >= H) return;
     const int r16 = lane & 15, kg = lane >> 4;
     const int g = h / (H / G);
     const int L = W - T;
 
-    const int p = 16 * w + r16;
     // ---- every load first, in dependency order (no branch between a load and
     // its use): the window's C (A fragments, row t = r16; rows past T read as
     // zero) needs nothing, the checkpoint and the cursor need the slot, the ring
     // loads need the cursor
     const rsrc_t rc = make_rsrc(C + ((int64_t)r * T * G + g) * N, (uint32_t)((T - 1) * G * N + N) * 2);
-    uint4 cf[4], kf[4];
+    uint4 cf[4], kf[4][4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) cf[ks] = buf_ld16(rc, (uint32_t)(r16 * G * N + 32 * ks + 8 * kg) * 2);
     const int slot = idx[r];
@@ -251,9 +258,12 @@ __global__ __launch_bounds__(256) void replay_update_fast_kernel(
     const int64_t cs = slot_ok ? slot : 0;
     // (an invalid slot reads slot 0's cursor and checkpoint, both discarded)
     const int cur0 = cursor[2 * cs], cur1 = cursor[2 * cs + 1];
-    const bf16 *ckrow = ckpt + ((cs * H + h) * P + p) * N;
+    const bf16 *ckh = ckpt + (cs * H + h) * P * N;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) kf[ks] = *reinterpret_cast<const uint4 *>(ckrow + 32 * ks + 8 * kg);
+    for (int pg = 0; pg < 4; ++pg)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            kf[pg][ks] = *reinterpret_cast<const uint4 *>(ckh + (16 * pg + r16) * N + 32 * ks + 8 * kg);
     const float Ah = A[h];
     const float Dh = D ? D[h] : 0.0f;
     __builtin_amdgcn_sched_barrier(0);
@@ -264,7 +274,7 @@ __global__ __launch_bounds__(256) void replay_update_fast_kernel(
         const int q = start + k;
         return q < W ? q : q - W;
     };
-    // B and dt of token k = 16 kt + r16: ring for k < n, window token k - n, zero after
+    // B and dt of token slot k = 16 kt + r16: ring for k < n, window token k - n
     uint4 bfr[KT][4];
     bf16 dtraw[KT];
     float dtk[KT];
@@ -281,26 +291,32 @@ __global__ __launch_bounds__(256) void replay_update_fast_kernel(
             bfr[kt][ks] = *reinterpret_cast<const uint4 *>(bsrc + 32 * ks + 8 * kg);
         dtraw[kt] = *dsrc;
     }
-    // x_k[p] for every token slot, and x_t[p] of this lane's window token t = kg
-    float xk[NK];
+    // x_k[p] for every token slot, lane p (one 128-byte row per slot), and x_t[p]
+    // of the window tokens
+    bf16 xkr[NK], xtr[4];
 #pragma unroll
     for (int k = 0; k < NK; ++k) {
         const bool hist = k < n;
         const int tw = clamp_int(k - n, 0, T - 1);
-        const bf16 *src = hist ? ring_x + ((cs * W + ring_pos(k)) * H + h) * P + p
-                               : x + (((int64_t)r * T + tw) * H + h) * P + p;
-        xk[k] = to_f32(*src);
+        const bf16 *src = hist ? ring_x + ((cs * W + ring_pos(k)) * H + h) * P
+                               : x + (((int64_t)r * T + tw) * H + h) * P;
+        xkr[k] = src[lane];
     }
-    const int tl = kg < T ? kg : T - 1;
-    const bf16 xtraw = x[(((int64_t)r * T + tl) * H + h) * P + p];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int tl = t < T ? t : T - 1;
+        xtr[t] = x[(((int64_t)r * T + tl) * H + h) * P + lane];
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- masks, then the MFMA products (C_t . ckpt)[t][p] and (C_t . B_k)[t][k]
     const uint32_t kslot = slot_ok ? 0xffffffffu : 0u;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        kf[ks].x &= kslot; kf[ks].y &= kslot; kf[ks].z &= kslot; kf[ks].w &= kslot;
-    }
+    for (int pg = 0; pg < 4; ++pg)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            kf[pg][ks].x &= kslot; kf[pg][ks].y &= kslot; kf[pg][ks].z &= kslot; kf[pg][ks].w &= kslot;
+        }
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
         const int k = 16 * kt + r16;
@@ -311,13 +327,16 @@ __global__ __launch_bounds__(256) void replay_update_fast_kernel(
         }
         dtk[kt] = k < n + T ? to_f32(dtraw[kt]) : 0.0f;
     }
+    f32x4 ys[4], cb[KT];
 #pragma unroll
-    for (int k = 0; k < NK; ++k) xk[k] = k < n + T ? xk[k] : 0.0f;
-    f32x4 ys = zero4(), cb[KT];
+    for (int pg = 0; pg < 4; ++pg) {
+        ys[pg] = zero4();
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-        ys = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cf[ks]),
-                                                     __builtin_bit_cast(bf16x8, kf[ks]), ys, 0, 0, 0);
+        for (int ks = 0; ks < 4; ++ks)
+            ys[pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cf[ks]),
+                                                             __builtin_bit_cast(bf16x8, kf[pg][ks]),
+                                                             ys[pg], 0, 0, 0);
+    }
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
         cb[kt] = zero4();
@@ -328,113 +347,136 @@ __global__ __launch_bounds__(256) void replay_update_fast_kernel(
                                                              cb[kt], 0, 0, 0);
     }
 
-    // ---- lambda_k (a running sum over the token slots, read back from LDS)
-    float *sdt = s_dt[w], *slam = s_lam[w];
-    if (kg == 0) {
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt) sdt[16 * kt + r16] = dtk[kt];
-    }
-    wave_lds_sync();
+    // ---- lambda_k = A sum_{k' <= k} dt_k', summed in token order; lane r16
+    // keeps lambda of slot 16 kt + r16 (dt of slot 16 kt + j sits in lane j)
     float lk[KT];
     {
         float run = 0.0f;
 #pragma unroll
-        for (int k = 0; k < NK; ++k) {
-            run += Ah * sdt[k];
+        for (int kt = 0; kt < KT; ++kt) {
+            float mine = 0.0f;
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-                if (k == 16 * kt + r16) lk[kt] = run;
+            for (int j = 0; j < 16; ++j) {
+                run += Ah * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dtk[kt]), j));
+                mine = r16 == j ? run : mine;
+            }
+            lk[kt] = mine;
         }
     }
+    // lambda of token slot m (m uniform, m < NK)
+    auto lam_at = [&](int m) {
+        const float v = KT > 1 && (m >> 4) ? lk[KT > 1 ? 1 : 0] : lk[0];
+        return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), m & 15));
+    };
+    float lt[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) lt[t] = lam_at(n + (t < T ? t : T - 1));
+
+    // ---- weights G[t][k] = [k <= n + t] exp(lambda_{n+t} - lambda_k) dt_k CB[t][k]
+    // (lanes of row 0 hold rows t = v of CB) and C_t . ckpt to LDS as [t][p]
+    float *sg = &s_g[w][0][0], *sy = &s_ys[w][0][0];
     if (kg == 0) {
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) slam[16 * kt + r16] = lk[kt];
-    }
-    wave_lds_sync();
-    // weights G[t][k] = [k <= n + t] exp(lambda_{n+t} - lambda_k) dt_k CB[t][k], t = 4 kg + v
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int t = 4 * kg + v;
-        const float ln = slam[n + t < NK ? n + t : NK - 1];
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-            const int k = 16 * kt + r16;
-            const float gv = __expf(ln - lk[kt]) * dtk[kt] * cb[kt][v];
-            s_g[w][t][k] = (t < T && k <= n + t) ? gv : 0.0f;
-        }
-        s_y[w][t][r16] = ys[v];
-    }
-    wave_lds_sync();
-
-    // ---- y_t[p], lane (p, t = kg)
-    if (kg < T) {
-        const int t = kg;
-        float acc = __expf(slam[n + t]) * s_y[w][t][r16];
-#pragma unroll
-        for (int k = 0; k < NK; ++k) acc += s_g[w][t][k] * xk[k];
-        acc += Dh * to_f32(xtraw);
-        y[(((int64_t)r * T + t) * H + h) * P + p] = from_f32<bf16>(acc);
-    }
-
-    // ---- the window's inputs join the ring (B by the group's first head, dt by wave 0)
-    if (slot_ok) {
-        if (kg < T) ring_x[((cs * W + ring_pos(n + kg)) * H + h) * P + p] = xtraw;
-        if (w == 0) {
+        for (int v = 0; v < 4; ++v) {
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) {
                 const int k = 16 * kt + r16;
-                if (k >= n && k < n + T) {
-                    const int64_t e = cs * W + ring_pos(k);
-                    if (kg == 0) ring_dt[e * H + h] = dtraw[kt];
-                    if (h % (H / G) == 0) {
+                const float gv = __expf(lt[v] - lk[kt]) * dtk[kt] * cb[kt][v];
+                sg[v * NK + k] = (v < T && k <= n + v) ? gv : 0.0f;
+            }
 #pragma unroll
-                        for (int ks = 0; ks < 4; ++ks)
-                            *reinterpret_cast<uint4 *>(ring_B + (e * G + g) * N + 32 * ks + 8 * kg) =
-                                bfr[kt][ks];
-                    }
+            for (int pg = 0; pg < 4; ++pg) sy[v * P + 16 * pg + r16] = ys[pg][v];
+        }
+    }
+    wave_lds_sync();
+
+    // ---- y_t[p], lane p
+    float xk[NK];
+#pragma unroll
+    for (int k = 0; k < NK; ++k) xk[k] = k < n + T ? to_f32(xkr[k]) : 0.0f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        if (t >= T) break;
+        float acc = __expf(lt[t]) * sy[t * P + lane];
+#pragma unroll
+        for (int k = 0; k < NK; ++k) acc += sg[t * NK + k] * xk[k];
+        acc += Dh * to_f32(xtr[t]);
+        y[(((int64_t)r * T + t) * H + h) * P + lane] = from_f32<bf16>(acc);
+    }
+
+    // ---- the window's inputs join the ring (B by the group's first head)
+    if (slot_ok) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            if (t < T) ring_x[((cs * W + ring_pos(n + t)) * H + h) * P + lane] = xtr[t];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+            const int k = 16 * kt + r16;
+            if (k >= n && k < n + T) {
+                const int64_t e = cs * W + ring_pos(k);
+                if (kg == 0) ring_dt[e * H + h] = dtraw[kt];
+                if (h % (H / G) == 0) {
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks)
+                        *reinterpret_cast<uint4 *>(ring_B + (e * G + g) * N + 32 * ks + 8 * kg) =
+                            bfr[kt][ks];
                 }
             }
         }
     }
 
     // ---- checkpoint rewrite: the state after the history,
-    //   exp(lambda_{n-1}) ckpt + sum_{i<n} exp(lambda_{n-1} - lambda_i) dt_i x_i (x) B_i
+    //   exp(lambda_{n-1}) ckpt + sum_{i<n} exp(lambda_{n-1} - lambda_i) dt_i x_i (x) B_i,
+    // one 16-row group at a time (lane (r16, kg): row 16 pg + r16, columns
+    // 32 ks + 8 kg .. + 7, the layout the checkpoint was loaded in). The rows
+    // are read again here (this wave's own, still in L2) rather than kept in
+    // registers from the MFMA phase: that frees 64 VGPRs for all the other
+    // steps, three waves per SIMD instead of two.
     if (ck) {
+        const float lh = n > 0 ? lam_at(n - 1) : 0.0f;
+        bf16 (*sb)[N] = s_b[w];
+        bf16 (*sx)[P] = s_x[w];
+        float *sw = s_w[w];
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
+        for (int kt = 0; kt < KT; ++kt) {
+            const int k = 16 * kt + r16;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
-                *reinterpret_cast<uint4 *>(&s_b[w][16 * kt + r16][32 * ks + 8 * kg]) = bfr[kt][ks];
-        wave_lds_sync();
-        const float lh = n > 0 ? slam[n - 1] : 0.0f;
-        const float a0 = __expf(lh);
-        float st[4][8];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            Raw8<bf16> kr;
-            kr.w = kf[ks];
-            kr.widen(st[ks]);
-#pragma unroll
-            for (int v = 0; v < 8; ++v) st[ks][v] *= a0;
+                *reinterpret_cast<uint4 *>(&sb[k][32 * ks + 8 * kg]) = bfr[kt][ks];
+            if (kg == 0) sw[k] = k < n ? __expf(lh - lk[kt]) * dtk[kt] : 0.0f;
         }
 #pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            if (i < n) {
-                const float u = __expf(lh - slam[i]) * sdt[i] * xk[i];
+        for (int k = 0; k < NK; ++k) sx[k][lane] = xkr[k];
+        wave_lds_sync();
+        const float a0 = __expf(lh);
+        bf16 *ckw = ckpt + (cs * H + h) * P * N;
+#pragma unroll
+        for (int pg = 0; pg < 4; ++pg) {
+            const int p = 16 * pg + r16;
+            float st[4][8];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                Raw8<bf16> kr;
+                kr.w = *reinterpret_cast<const uint4 *>(ckw + p * N + 32 * ks + 8 * kg);
+                kr.widen(st[ks]);
+#pragma unroll
+                for (int v = 0; v < 8; ++v) st[ks][v] *= a0;
+            }
+            for (int i = 0; i < n; ++i) {
+                const float u = sw[i] * to_f32(sx[i][p]);
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     Raw8<bf16> br;
-                    br.w = *reinterpret_cast<const uint4 *>(&s_b[w][i][32 * ks + 8 * kg]);
+                    br.w = *reinterpret_cast<const uint4 *>(&sb[i][32 * ks + 8 * kg]);
                     float b8[8];
                     br.widen(b8);
 #pragma unroll
                     for (int v = 0; v < 8; ++v) st[ks][v] += u * b8[v];
                 }
             }
-        }
-        bf16 *dst = ckpt + ((cs * H + h) * P + p) * N;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) store_run<bf16, 8>(dst + 32 * ks + 8 * kg, st[ks]);
+            for (int ks = 0; ks < 4; ++ks) store_run<bf16, 8>(ckw + p * N + 32 * ks + 8 * kg, st[ks]);
+        }
     }
 }
 
@@ -593,7 +635,8 @@ void launch_replay_update(const DecodeDims &d, int W, void *ckpt, void *rx, void
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (d.in_bf16 && d.state_bf16 && d.P == 64 && d.N == 128 && d.T <= 4 && W <= 32) {
 #define SSD_REPLAY_FAST(KT)                                                                       \
-    hipLaunchKernelGGL((replay_update_fast_kernel<KT>), dim3(d.H, d.R), dim3(256), 0, st, d.T,    \
+    hipLaunchKernelGGL((replay_update_wave_kernel<KT>), dim3((d.H + 3) / 4, d.R), dim3(256), 0, st, \
+                       d.T,                                                                       \
                        d.H, d.G, d.num_slots, W, static_cast<bf16 *>(ckpt), static_cast<bf16 *>(rx), \
                        static_cast<bf16 *>(rdt), static_cast<bf16 *>(rB), cursor, idx,            \
                        static_cast<const bf16 *>(x), static_cast<const bf16 *>(dt), A,            \
