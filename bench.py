@@ -4,10 +4,13 @@
 One step = one ssd_combined_varlen call over the single-sequence Mamba2 layer
 prefill: L = 4096 tokens, 80 heads, headdim 64, d_state 128, 1 group, chunk 256,
 bf16 x/B/C/dt, fp32 A/D/state. Inputs are seeded synthetic draws, resident in
-HBM before the timed region. Each timed call starts with the 256 MB last-level
-cache flushed (a 512 MiB device write, outside the timed interval), so nothing
-the call reads is left over from the call before. `value` = tokens / s of the
-median call (one layer); `ms_per_step` = that median.
+HBM before the timed region. Each timed call starts with the caches holding none
+of its data: a 512 MiB device read (outside the timed interval) evicts the 256 MB
+last-level cache and the L2s, so nothing the call reads is left over from the
+call before. `value` = tokens / s of the median call (one layer); `ms_per_step` =
+that median. (A 512 MiB write instead would leave up to 256 MB of unrelated dirty
+lines whose write-back the timed call would pay for; that median is reported
+beside it as cold_after_write_flush.)
 
 The same JSON line also carries:
   warm          the same call back to back on resident inputs (context)
@@ -45,6 +48,16 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, published
 FLUSH_BYTES = 512 << 20         # twice the 256 MB last-level cache
+
+
+def flush_caches(flush, write=False):
+    """Evict every cache level: a read of the whole flush buffer (its lines stay
+    clean), or with write a fill (which leaves them dirty)."""
+    import torch
+    if write:
+        flush.fill_(1)
+    else:
+        flush.view(torch.int32).sum()
 CALIBRATION_BYTES = 256 << 20   # the --copy-calibration copy
 
 
@@ -394,18 +407,18 @@ def pct(vals, q):
     return float(np.percentile(np.asarray(vals), q))
 
 
-def time_cold(pf, stream, flush, warmup, steps, torch):
-    """Cache-flushed calls: the flush write, then the call between two events.
+def time_cold(pf, stream, flush, warmup, steps, torch, write_flush=False):
+    """Cache-flushed calls: the flush, then the call between two events.
     Returns (per-call us list, wall seconds of the timed loop)."""
     for _ in range(warmup):
-        flush.fill_(1)
+        flush_caches(flush, write_flush)
         pf.call(stream)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     t0 = time.perf_counter()
     for a, b in evs:
-        flush.fill_(1)
+        flush_caches(flush, write_flush)
         a.record(stream)
         pf.call(stream)
         b.record(stream)
@@ -420,7 +433,7 @@ def trace_cold(pf, stream, flush, steps, ssd, torch):
     opt = ssd.make_options(trace=tr)
     acc, names = {}, None
     for _ in range(steps):
-        flush.fill_(1)
+        flush_caches(flush)
         pf.call(stream, opt)
         torch.cuda.synchronize()
         d = tr.durations_us()
@@ -635,10 +648,15 @@ def main():
     dom = max(names, key=lambda n: means[n])
     roofline = roofline_of(dom, means, w, "layer_L4096")
 
-    warm = None
+    warm = dirty = None
     if not args.headline_only:
         wus = spin_avg_us(lambda: pf.call(stream), max(args.steps, 50), stream, torch)
         warm = {"us_per_step": round(wus, 3), "tokens_per_s": round(T / (wus * 1e-6), 1)}
+        dt_, _ = time_cold(pf, stream, flush, 3, args.steps, torch, write_flush=True)
+        dirty = {"median_us": round(pct(dt_, 50), 3),
+                 "tokens_per_s": round(T / (pct(dt_, 50) * 1e-6), 1),
+                 "flush": "512 MiB write before each call (its dirty lines are written back "
+                          "during the call)"}
 
     decode = replay = None
     others, extras = {}, {}
@@ -841,7 +859,7 @@ def main():
                    "seq_len": T, "num_seqs": cfg.num_seqs, "nheads": cfg.nheads,
                    "headdim": cfg.headdim, "d_state": cfg.d_state, "ngroups": cfg.ngroups,
                    "chunk_size": Q, "inputs": "bf16 x/B/C/dt, fp32 A/D/state",
-                   "timing": "median of the cache-flushed calls (512 MiB write before each)",
+                   "timing": "median of the cache-flushed calls (512 MiB read before each)",
                    "parallelism": "single GPU"},
         "cold_stats_us": {"median": round(med, 3), "mean": round(sum(times) / len(times), 3),
                           "p10": round(pct(times, 10), 3), "p90": round(pct(times, 90), 3),
@@ -849,6 +867,7 @@ def main():
         "roofline": roofline,
         "launches": launches,
         "warm": warm,
+        "cold_after_write_flush": dirty,
         "hbm_copy_GBps": copy_gbps,
         "other_prefill_shapes": others,
         "decode": decode,
