@@ -245,10 +245,12 @@ __global__ __launch_bounds__(256) void replay_update_wave_kernel(
     const int g = h / (H / G);
     const int L = W - T;
 
-    // ---- every load first, in dependency order (no branch between a load and
-    // its use): the window's C (A fragments, row t = r16; rows past T read as
-    // zero) needs nothing, the checkpoint and the cursor need the slot, the ring
-    // loads need the cursor
+    // ---- loads in two phases (no branch between a load and its use). First the
+    // window's C (A fragments, row t = r16; rows past T read as zero), the
+    // checkpoint and the cursor, and C_t . ckpt on MFMA straight into LDS; then
+    // the token slots' B, dt and x (L2-resident rows). The checkpoint fragments
+    // (64 VGPRs) are then never live together with the token rows, which keeps
+    // the kernel at four waves per SIMD: 16 KB of checkpoint in flight per wave.
     const rsrc_t rc = make_rsrc(C + ((int64_t)r * T * G + g) * N, (uint32_t)((T - 1) * G * N + N) * 2);
     uint4 cf[4], kf[4][4];
 #pragma unroll
@@ -266,6 +268,26 @@ __global__ __launch_bounds__(256) void replay_update_wave_kernel(
             kf[pg][ks] = *reinterpret_cast<const uint4 *>(ckh + (16 * pg + r16) * N + 32 * ks + 8 * kg);
     const float Ah = A[h];
     const float Dh = D ? D[h] : 0.0f;
+    __builtin_amdgcn_sched_barrier(0);
+    float *sg = &s_g[w][0][0], *sy = &s_ys[w][0][0];
+    {
+        const uint32_t kslot = slot_ok ? 0xffffffffu : 0u;
+#pragma unroll
+        for (int pg = 0; pg < 4; ++pg) {
+            f32x4 ys = zero4();
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                uint4 kv = kf[pg][ks];
+                kv.x &= kslot; kv.y &= kslot; kv.z &= kslot; kv.w &= kslot;
+                ys = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cf[ks]),
+                                                             __builtin_bit_cast(bf16x8, kv), ys, 0, 0, 0);
+            }
+            if (kg == 0) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) sy[v * P + 16 * pg + r16] = ys[v];
+            }
+        }
+    }
     __builtin_amdgcn_sched_barrier(0);
     const int start = clamp_int(cur0, 0, W - 1);
     const int n = slot_ok ? clamp_int(cur1, 0, L) : 0;
@@ -309,14 +331,7 @@ __global__ __launch_bounds__(256) void replay_update_wave_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- masks, then the MFMA products (C_t . ckpt)[t][p] and (C_t . B_k)[t][k]
-    const uint32_t kslot = slot_ok ? 0xffffffffu : 0u;
-#pragma unroll
-    for (int pg = 0; pg < 4; ++pg)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            kf[pg][ks].x &= kslot; kf[pg][ks].y &= kslot; kf[pg][ks].z &= kslot; kf[pg][ks].w &= kslot;
-        }
+    // ---- masks, then the MFMA products (C_t . B_k)[t][k]
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
         const int k = 16 * kt + r16;
@@ -327,16 +342,7 @@ __global__ __launch_bounds__(256) void replay_update_wave_kernel(
         }
         dtk[kt] = k < n + T ? to_f32(dtraw[kt]) : 0.0f;
     }
-    f32x4 ys[4], cb[KT];
-#pragma unroll
-    for (int pg = 0; pg < 4; ++pg) {
-        ys[pg] = zero4();
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            ys[pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cf[ks]),
-                                                             __builtin_bit_cast(bf16x8, kf[pg][ks]),
-                                                             ys[pg], 0, 0, 0);
-    }
+    f32x4 cb[KT];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
         cb[kt] = zero4();
@@ -374,7 +380,6 @@ __global__ __launch_bounds__(256) void replay_update_wave_kernel(
 
     // ---- weights G[t][k] = [k <= n + t] exp(lambda_{n+t} - lambda_k) dt_k CB[t][k]
     // (lanes of row 0 hold rows t = v of CB) and C_t . ckpt to LDS as [t][p]
-    float *sg = &s_g[w][0][0], *sy = &s_ys[w][0][0];
     if (kg == 0) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -384,8 +389,6 @@ __global__ __launch_bounds__(256) void replay_update_wave_kernel(
                 const float gv = __expf(lt[v] - lk[kt]) * dtk[kt] * cb[kt][v];
                 sg[v * NK + k] = (v < T && k <= n + v) ? gv : 0.0f;
             }
-#pragma unroll
-            for (int pg = 0; pg < 4; ++pg) sy[v * P + 16 * pg + r16] = ys[pg][v];
         }
     }
     wave_lds_sync();
