@@ -283,3 +283,90 @@ def test_replay_fp16_checkpoints():
     ys2, ck2 = run(77)
     assert torch.equal(ck2.view(torch.int16), ck.view(torch.int16))
     assert all(torch.equal(a, b) for a, b in zip(ys, ys2))
+
+
+# ---------------------------------------------------------------------------
+# Every store path of the fp16 cache against the rounding's definition, bit for
+# bit: the same problem with a float32 cache gives the exact values that the
+# fp16 run rounds (the state arithmetic is float32 whatever the cache dtype, and
+# no initial state is read, or an fp16-exact one), so the fp16 bits must equal
+# the oracle's stochastic rounding of those values with the draws of their flat
+# indices in the destination array (stream 0 final states, 1 checkpoints, 2
+# per-token states).
+
+def _combined_ts(inp, nslots, Q, ts, seed=None, rounds=5, ck=True):
+    ssd = _ssd()
+    T, S = int(inp.cu_seqlens[-1]), len(inp.cu_seqlens) - 1
+    H, P, N, G = inp.x.shape[1], inp.x.shape[2], inp.B.shape[2], inp.B.shape[1]
+    p = ssd.make_problem(T, S, H, P, N, G, Q, nslots, inp.x.dtype, ts)
+    opt = ssd.make_options(sr_seed=None if seed is None else _seed(seed), sr_rounds=rounds)
+    cache = torch.zeros(nslots, H, P, N, dtype=ts, device=DEV)
+    y = torch.empty(T, H, P, dtype=inp.x.dtype, device=DEV)
+    ckpt = torch.zeros(ssd.max_chunks(p), H, P, N, dtype=ts, device=DEV) if ck else None
+    ssd.ssd_combined_varlen_ex(p, opt, inp.x.to(DEV), inp.dt.to(DEV), inp.A.to(DEV),
+                               inp.B.to(DEV), inp.C.to(DEV), inp.D.to(DEV),
+                               inp.cu_seqlens.to(DEV), cache, inp.state_indices.to(DEV),
+                               torch.zeros(S, dtype=torch.uint8, device=DEV), y, ckpt,
+                               ssd.alloc_workspace(p, DEV))
+    torch.cuda.synchronize()
+    return cache.cpu(), None if ckpt is None else ckpt.cpu()
+
+
+def _rounded(exact, seed, kind, rounds):
+    flat = exact.numpy().reshape(-1)
+    return rnd.stochastic_round_f16(flat, rnd.draws_for(flat.size, _u64(seed), kind, rounds)
+                                    ).reshape(exact.shape).view(np.uint16)
+
+
+@pytest.mark.parametrize("lens,H,Q,ck,path", [
+    ((1500,), 4, 128, False, "segmented state pass: carry stores"),
+    ((600, 32, 1, 257), 8, 256, True, "fused state kernel: checkpoints and finals"),
+    ((20, 1, 0, 90, 33, 64) * 4, 8, 256, True, "short-sequence kernel"),
+])
+def test_prefill_fp16_stores_bit_exact(lens, H, Q, ck, path):
+    S, seed, rounds = len(lens), 0x5EED5EED1234, 5
+    inp = sy.random_problem(816, lens, H, 64, 128, 2, Q, BF16, F16, num_slots=2 * S + 1,
+                            has_initial=[False] * S)
+    c32, k32 = _combined_ts(inp, 2 * S + 1, Q, F32, ck=ck)
+    c16, k16 = _combined_ts(inp, 2 * S + 1, Q, F16, seed=seed, rounds=rounds, ck=ck)
+    used = inp.state_indices.long().numpy()
+    want = _rounded(c32, seed, 0, rounds)
+    got = c16.numpy().view(np.uint16)
+    assert np.array_equal(got[used], want[used]), (path, int(np.sum(got[used] != want[used])))
+    if ck:
+        # (rows past the last checkpoint stay zero in both runs, and zero rounds to zero)
+        wk, gk = _rounded(k32, seed, 1, rounds), k16.numpy().view(np.uint16)
+        assert np.array_equal(gk, wk), (path, int(np.sum(gk != wk)))
+
+
+@pytest.mark.parametrize("keep", [True, False])
+def test_decode_fp16_stores_bit_exact(keep):
+    ssd = _ssd()
+    R, T, H, P, N, G, ns, seed, rounds = 6, 3, 8, 64, 128, 2, 13, 0xABCDEF0123, 5
+    cfg = sy.DecodeConfig("sr_bits", R, T, H, P, N, G, BF16, F16, ns, 8, 840)
+    d = sy.make_decode(cfg)
+    g = torch.Generator().manual_seed(5)
+    c16 = torch.zeros(ns, H, P, N, dtype=F16)
+    for s in d.state_indices:
+        c16[int(s)] = (torch.randn(H, P, N, generator=g) * 0.05).half()
+    args = [t.to(DEV) for t in (d.x, d.dt, d.A, d.B, d.C, d.D)]
+
+    def run(ts, sd):
+        up = ssd.make_ssu_problem(R, T, H, P, N, G, ns, BF16, ts)
+        opt = ssd.make_options(sr_seed=None if sd is None else _seed(sd), sr_rounds=rounds)
+        cache = c16.to(ts).to(DEV)
+        y = torch.empty(R, T, H, P, dtype=BF16, device=DEV)
+        inter = torch.empty(R, T, H, P, N, dtype=ts, device=DEV) if keep else None
+        ssd.selective_state_update_ex(up, opt, cache, d.state_indices.to(DEV), *args, y, inter)
+        torch.cuda.synchronize()
+        return cache.cpu(), None if inter is None else inter.cpu()
+
+    a32, i32 = run(F32, None)
+    a16, i16 = run(F16, seed)
+    if keep:
+        want, got = _rounded(i32, seed, 2, rounds), i16.numpy().view(np.uint16)
+        assert np.array_equal(got, want), int(np.sum(got != want))
+    else:
+        used = d.state_indices.long().numpy()
+        want, got = _rounded(a32, seed, 0, rounds), a16.numpy().view(np.uint16)
+        assert np.array_equal(got[used], want[used]), int(np.sum(got[used] != want[used]))
