@@ -370,3 +370,50 @@ def test_decode_fp16_stores_bit_exact(keep):
         used = d.state_indices.long().numpy()
         want, got = _rounded(a32, seed, 0, rounds), a16.numpy().view(np.uint16)
         assert np.array_equal(got[used], want[used]), int(np.sum(got[used] != want[used]))
+
+
+def test_replay_fp16_store_bit_exact():
+    """The ReplaySSM checkpoint store (stream 3): two verify steps that leave the
+    checkpoint alone (the history stays below the ring's capacity), then a
+    materialisation, once with float32 checkpoints and once with fp16 ones holding
+    the same (fp16-exact) values; the fp16 bits are the oracle's rounding of the
+    float32 result."""
+    ssd = _ssd()
+    R, T, H, P, N, G, W, ns, seed, rounds = 4, 2, 4, 64, 128, 2, 16, 9, 0x1234567, 5
+    cfg = sy.DecodeConfig("sr_replay_bits", R, T, H, P, N, G, BF16, F16, ns, 8, 850)
+    base = sy.make_decode(cfg)
+    idx = base.state_indices
+    g = torch.Generator().manual_seed(9)
+    c16 = torch.zeros(ns, H, P, N, dtype=F16)
+    for s in idx:
+        c16[int(s)] = (torch.randn(H, P, N, generator=g) * 0.05).half()
+    steps = []
+    for k in range(2):
+        d = sy.make_decode(sy.DecodeConfig("sr_replay_bits", R, T, H, P, N, G, BF16, F16, ns, 8,
+                                           850 + 1000 * (k + 1)))
+        steps.append((d.x, d.dt, d.B, d.C, d.num_accepted))
+
+    def run(ts, sd):
+        up = ssd.make_ssu_problem(R, T, H, P, N, G, ns, BF16, ts)
+        opt = ssd.make_options(sr_seed=None if sd is None else _seed(sd), sr_rounds=rounds)
+        rings = ssd.alloc_replay_rings(up, W, DEV)
+        ck = c16.to(ts).to(DEV)
+        for x, dt, B, C, acc in steps:
+            y = torch.empty(R, T, H, P, dtype=BF16, device=DEV)
+            ssd.ssd_replay_update_ex(up, opt, W, ck, rings["ring_x"], rings["ring_dt"],
+                                     rings["ring_B"], rings["cursor"], idx.to(DEV), x.to(DEV),
+                                     dt.to(DEV), base.A.to(DEV), B.to(DEV), C.to(DEV),
+                                     base.D.to(DEV), y)
+            ssd.ssd_replay_advance(up, W, rings["cursor"], idx.to(DEV), acc.to(DEV))
+        assert int(rings["cursor"].cpu()[:, 1].max()) + T <= W - T   # (no rewrite so far)
+        ssd.ssd_replay_materialize_ex(up, opt, W, ck, rings["ring_x"], rings["ring_dt"],
+                                      rings["ring_B"], rings["cursor"], idx.to(DEV),
+                                      base.A.to(DEV))
+        torch.cuda.synchronize()
+        return ck.cpu()
+
+    k32 = run(F32, None)
+    k16 = run(F16, seed)
+    used = idx.long().numpy()
+    want, got = _rounded(k32, seed, 3, rounds), k16.numpy().view(np.uint16)
+    assert np.array_equal(got[used], want[used]), int(np.sum(got[used] != want[used]))
