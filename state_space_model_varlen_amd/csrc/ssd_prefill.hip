@@ -1039,8 +1039,13 @@ template <int Q> struct StateScanRegs {
 //     values are the same bit for bit;
 //   - the blocks of column slice 0 publish what the later launches read: the
 //     cumsum and dt rows of their head, and (head 0) the chunk metadata;
-//   - own.CB set: max_chunks G more blocks after the state blocks compute CB,
-//     one (chunk, group) pair each, in the CUs the short chains leave free.
+//   - own.CB set: max_chunks G more blocks compute CB, one (chunk, group) pair
+//     each, in the CUs the short chains leave free: after the state blocks, or
+//     in longest-chain-first order right after the first round of them (ahead
+//     of the shorter chains, which are each mostly start-up latency), their
+//     count then padded to a multiple of 8 so that the state blocks behind them
+//     keep their XCD.
+constexpr int kStateRound = 512;   // state blocks in flight at once: two per CU
 template <int Q, bool CKPT, bool SEG, bool OWN, typename TS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
 void state_scan_fast_kernel(
@@ -1068,52 +1073,82 @@ void state_scan_fast_kernel(
     // heads that share a B group sit side by side on one XCD
     const int nsg = SEG ? nseg : 1;
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+    int bid = (int)blockIdx.x;   // the state block's index (past the CB blocks)
     if constexpr (OWN) {
         const int nstate = S * nsg * H * NS;
-        if ((int)blockIdx.x >= nstate) {
+        int cb_at = nstate, cb_n = max_chunks * G;
+        if (!SEG && lpt) {
+            const int per_rank = H * NS;
+            const int r1 = (kStateRound + per_rank - 1) / per_rank * per_rank;
+            cb_at = r1 < nstate ? r1 : nstate;
+            cb_n = own.CB != nullptr ? (cb_n + kXcds - 1) / kXcds * kXcds : 0;
+        }
+        if (!SEG && lpt ? bid >= cb_at && bid < cb_at + cb_n : bid >= nstate) {
             // CB of one (chunk, group) pair, through this kernel's LDS
-            const int pr = (int)blockIdx.x - nstate, c = pr / G, g = pr - c * G;
+            const int pr = bid - cb_at, c = pr / G, g = pr - c * G;
+            if (!SEG && lpt && c >= max_chunks) return;   // (padding)
             const ChunkInfo ci = wave_find_chunk(T, S, Q, own.cu, prefix, c, lane);
             if (ci.len > 0)   // (the same in every wave)
                 cb_pair<Q, 512>(G, c, g, ci, B, static_cast<const bf16 *>(own.C),
                                 static_cast<bf16 *>(own.CB), xs);
             return;
         }
+        if (!SEG && lpt && bid >= cb_at) bid -= cb_n;
     }
     int q, h, s, b, sb;
+    // longest chain first with OWN: the sequence's span, cache slot and
+    // has-initial flag come from the same per-lane loads as the ranking (one
+    // memory latency; with no flag array a byte of idx stands in and the flag
+    // is ignored)
+    SeqSpan lsp{0, 0, 0, 0, Q, 0};
+    int lslot = 0, lflag = 0;
     if (!SEG && lpt) {
         // Longest chain first (few sequences, heads a multiple of 8): XCD x owns
         // heads [x H / 8, (x + 1) H / 8) of every sequence, and its blocks go out
         // in order of the sequences' chunk counts, longest first, so that the
         // long chains start in the first round on every XCD. Every wave ranks the
         // sequences itself (count descending, then index): rank r -> sequence s.
-        const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+        const int xcd = bid % kXcds, slot = bid / kXcds;
         const int hx = H / kXcds;
         const int r = slot / (hx * NS), rem = slot - r * (hx * NS);
         h = xcd * hx + rem / NS;
         q = rem - (rem / NS) * NS;
-        int cnt;
+        auto pick = [&](int cnt) {
+            int rank = 0;
+            for (int t = 0; t < S; ++t) {
+                const int ct = __shfl(cnt, t);
+                rank += (ct > cnt || (ct == cnt && t < lane)) ? 1 : 0;
+            }
+            const unsigned long long hit = __ballot(lane < S && rank == r);
+            return hit ? (int)__builtin_ctzll(hit) : 0;
+        };
         if constexpr (OWN) {
-            // the clamped counts the metadata would hold (S <= 64 here)
+            // lane = sequence (S <= 64 here): its slot and flag, then its span
+            // (requested before the span's loads wait)
+            const int sl = lane < S ? lane : 0;
+            const int il = idx[sl];
+            const int fl = (has_init != nullptr ? has_init : reinterpret_cast<const uint8_t *>(idx))[sl];
             const LaneSeq ls = lane_seq(T, S, Q, own.cu, prefix, 0, lane);
             const int incl = wave_inclusive_sum_int(ls.cnt, lane), excl = incl - ls.cnt;
-            cnt = (incl < max_chunks ? incl : max_chunks) - (excl < max_chunks ? excl : max_chunks);
+            // ranked by the clamped counts the metadata would hold
+            s = pick((incl < max_chunks ? incl : max_chunks) - (excl < max_chunks ? excl : max_chunks));
+            lsp.c0 = uniform(__shfl(excl, s));
+            lsp.cnt = uniform(__shfl(ls.cnt, s));
+            lsp.a = uniform(__shfl(ls.a, s));
+            lsp.b = uniform(__shfl(ls.b, s));
+            lsp.f = uniform(__shfl(ls.f, s));
+            lsp.total = uniform(__shfl(incl, kWave - 1));
+            lslot = uniform(__shfl(il, s));
+            lflag = uniform(__shfl(fl, s));
         } else {
             const int sl = lane < S ? lane : S - 1;
-            cnt = meta[sl + 1] - meta[sl];
+            s = pick(meta[sl + 1] - meta[sl]);
         }
-        int rank = 0;
-        for (int t = 0; t < S; ++t) {
-            const int ct = __shfl(cnt, t);
-            rank += (ct > cnt || (ct == cnt && t < lane)) ? 1 : 0;
-        }
-        const unsigned long long hit = __ballot(lane < S && rank == r);
-        s = hit ? __builtin_ctzll(hit) : 0;
         b = 0;
         sb = s;
     } else {
         const int nblk = S * nsg * H * NS;
-        const int lb = xcd_logical_block(blockIdx.x, nblk);
+        const int lb = xcd_logical_block(bid, nblk);
         q = lb % NS;
         sb = (lb / NS) % (S * nsg);
         h = lb / (NS * S * nsg);
@@ -1135,7 +1170,7 @@ void state_scan_fast_kernel(
     SrKey srk;
     float Ah = 0.0f, bh = 0.0f;
     if constexpr (OWN) {
-        const SeqSpan sp = wave_seq_span(T, S, Q, own.cu, prefix, s, lane);
+        const SeqSpan sp = !SEG && lpt ? lsp : wave_seq_span(T, S, Q, own.cu, prefix, s, lane);
         c0 = sp.c0;
         c1 = sp.c0 + sp.cnt;
         first = sp.a;
@@ -1153,9 +1188,11 @@ void state_scan_fast_kernel(
         fcl = meta[tokoff + (S + 1) + s];
         srk = sr_key(sr, meta);
     }
-    const int slot = idx[s];
+    const bool early = OWN && !SEG && lpt;
+    const int slot = early ? lslot : idx[s];
     // (with no flag array, a byte of idx stands in and the flag is ignored)
-    const uint8_t hflag = (has_init != nullptr ? has_init : reinterpret_cast<const uint8_t *>(idx))[s];
+    const uint8_t hflag = early ? (uint8_t)lflag
+                                : (has_init != nullptr ? has_init : reinterpret_cast<const uint8_t *>(idx))[s];
     __builtin_amdgcn_sched_barrier(0);
     c0 = c0 < max_chunks ? c0 : max_chunks;
     c1 = c1 < max_chunks ? c1 : max_chunks;
@@ -2805,10 +2842,12 @@ static void launch_state_scan_k(const PrefillDims &d, const void *x, const void 
               raised);
     const int nseg = SEG ? seg.nseg : 1;
     const int64_t nstate = (int64_t)d.S * nseg * d.H * (128 / kScanNSL);
-    // OWN, unsegmented: the CB blocks, one per (chunk, group) pair
-    const int64_t ncb = OWN && own.CB ? (int64_t)d.max_chunks * d.G : 0;
     // longest chain first: few sequences (one wave ranks them), heads a multiple of 8
     const int lpt = !SEG && d.S > 1 && d.S <= 64 && d.H % kXcds == 0;
+    // OWN: the CB blocks, one per (chunk, group) pair (padded to a multiple of 8
+    // in longest-chain-first order, where they go out among the state blocks)
+    int64_t ncb = OWN && own.CB ? (int64_t)d.max_chunks * d.G : 0;
+    if (lpt) ncb = (ncb + kXcds - 1) / kXcds * kXcds;
     const char *name = OWN ? (SEG ? "chunk_state_passing_segmented_prep" : "chunk_state_passing_prep_bmm")
                            : (SEG ? "chunk_state_passing_segmented" : "chunk_state_passing");
     SSD_LAUNCH(d, name, (state_scan_fast_kernel<Q, CKPT, SEG, OWN, TS>), dim3((unsigned)(nstate + ncb)), dim3(512), smem,
