@@ -203,7 +203,8 @@ KERNEL_PATTERNS = [
     (r"state_scan_fast_kernel", "chunk_state_passing", PREFILL_SOURCES),
     (r"state_carry_kernel", "state_carry", PREFILL_SOURCES),
     (r"short_scan_kernel", "short_scan", PREFILL_SOURCES),
-    (r"chunk_scan_fast_kernelILi\d+ELb1E", "chunk_scan_segmented", PREFILL_SOURCES),
+    (r"chunk_scan_fast_kernelILi\d+ELb1E|chunk_scan_fast_kernel<\d+, true",
+     "chunk_scan_segmented", PREFILL_SOURCES),
     (r"chunk_scan_fast_kernel|chunk_scan_kernel", "chunk_scan", PREFILL_SOURCES),
     (r"state_passing_kernel", "state_passing", PREFILL_SOURCES),
     (r"chunk_state_fast_kernel|chunk_state_kernel", "chunk_state", PREFILL_SOURCES),

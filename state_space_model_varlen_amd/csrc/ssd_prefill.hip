@@ -2069,14 +2069,14 @@ __device__ __forceinline__ void scan_row_tile(
     wave_lds_sync();
 }
 
-template <int Q, bool SEG>
+template <int Q, bool SEG, bool BYC>
 __global__ __launch_bounds__(2 * Q) __attribute__((amdgpu_waves_per_eu(4)))
 void chunk_scan_fast_kernel(
     int S, int H, int G, int max_chunks, const bf16 *__restrict__ x,
     const bf16 *__restrict__ C, const float *__restrict__ D, const int32_t *__restrict__ meta,
     const float *__restrict__ cum, const float *__restrict__ dtc, const bf16 *__restrict__ CB,
     const bf16 *__restrict__ entering, bf16 *__restrict__ y, const int32_t *__restrict__ seg_I,
-    const float *__restrict__ seg_F, const bf16 *__restrict__ carry, int by_chunk)
+    const float *__restrict__ seg_F, const bf16 *__restrict__ carry)
 {
     constexpr int P = 64, N = 128, LDX = kScanXLD, LDH = N + 8;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -2085,27 +2085,50 @@ void chunk_scan_fast_kernel(
     bf16 *ys = hs + P * LDH;                                   // [Q / 32][P][kScanLDR]
     float *scum = reinterpret_cast<float *>(ys + (Q / 32) * P * kScanLDR);  // [Q] cum * log2(e)
     float *sdt = scum + Q;                                     // [Q]
+    // Chunks of 128 or more tokens (few state registers per thread): everything
+    // that depends on the unit alone is requested before anything is waited on -
+    // the chunk's metadata, its segment and decay, its cumsum and dt rows and the
+    // entering state - so the start pays one memory latency instead of a chain of
+    // them; what depends on the chunk's tokens or segment (x, C, CB, the carried
+    // state) follows once the metadata is in. (No branch comes before those
+    // requests, so the kernel's arguments are read in one batch.) Smaller chunks
+    // keep the loads in the order of use: their many state registers per thread
+    // would stay live across the start.
+    constexpr bool kEarly = Q >= 128;
+    // (the arguments read through vector loads or written, in registers before
+    // the first scheduling barrier below: one batch of argument loads; the
+    // metadata and segment arrays stay out of this, so that the compiler still
+    // reads them through scalar loads)
+    if constexpr (kEarly)
+        asm volatile("" ::"s"(x), "s"(C), "s"(cum), "s"(dtc), "s"(CB), "s"(entering), "s"(y),
+                     "s"(carry), "s"(S), "s"(H), "s"(G), "s"(max_chunks));
 
-    // Unit (chunk c, head h). With by_chunk, the (chunk, group) pairs u = c G + g
+    // Unit (chunk c, head h). With BYC, the (chunk, group) pairs u = c G + g
     // are dealt to the XCDs as u mod 8, each with all heads of its group: every
     // XCD gets the same share of real chunks, whatever the padding of max_chunks
     // and however the chunk lengths vary along the batch (the grid is padded to
-    // whole rounds of 8 pairs; the padding blocks leave at once). Otherwise each
-    // XCD takes one contiguous range of units in order c H + h. Either way the
-    // heads that read one (chunk, group)'s C and CB share an L2.
+    // whole rounds of 8 pairs; the padding blocks leave at once, after their
+    // requests with kEarly). Otherwise each XCD takes one contiguous range of
+    // units in order c H + h. Either way the heads that read one (chunk,
+    // group)'s C and CB share an L2.
     int h, c;
-    if (by_chunk) {
+    bool pad = false;
+    if constexpr (BYC) {
         const int hpg = H / G;
         const int slot = blockIdx.x / kXcds, m = slot / hpg;
         const int u = (int)(blockIdx.x % kXcds) + kXcds * m;
         c = u / G;
         h = (u - c * G) * hpg + (slot - m * hpg);
-        if (c >= max_chunks) return;
+        pad = c >= max_chunks;
+        c = pad ? max_chunks - 1 : c;
     } else {
         const int lb = xcd_logical_block(blockIdx.x, max_chunks * H);
         h = lb % H;
         c = lb / H;
     }
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int nthr = 2 * Q;
+    constexpr int kHVec = P * N / 8 / nthr > 0 ? P * N / 8 / nthr : 1;
     const ChunkInfo ci = chunk_info(meta, S, c);
     // segmented state passing: the entering state is the stored local one plus
     // exp(F) times the segment's starting state (none in a first segment)
@@ -2115,13 +2138,40 @@ void chunk_scan_fast_kernel(
         sid = seg_I[c];
         sF = seg_F[(int64_t)h * max_chunks + c];
     }
-    if (ci.len <= 0) return;
+    const float *cumrow = cum + ((int64_t)h * max_chunks + c) * Q;
+    const float *dtrow = dtc + ((int64_t)h * max_chunks + c) * Q;
+    const int iq = tid < Q ? tid : Q - 1;          // 2 Q threads: one position each
+    const bf16 *hin = entering + ((int64_t)c * H + h) * P * N;
+    float cmv, dtv;
+    uint4 hr[kHVec];
+    auto load_rows = [&]() {
+        cmv = cumrow[iq];
+        dtv = dtrow[iq];
+        __builtin_amdgcn_sched_barrier(0);   // (the scheduler would otherwise move them last)
+#pragma unroll
+        for (int k = 0; k < kHVec; ++k) {
+            const int u = tid + nthr * k;
+            hr[k] = ld16(hin + (u >> 4) * N + 8 * (u & 15));
+        }
+    };
+    if constexpr (kEarly) {
+        load_rows();
+        __builtin_amdgcn_sched_barrier(0);
+        if (pad || ci.len <= 0) {
+            // (consumed on this path too, so that the compiler keeps the requests
+            // ahead of the branch instead of moving them into the other path)
+#pragma unroll
+            for (int k = 0; k < kHVec; ++k) asm volatile("" ::"v"(hr[k].x));
+            asm volatile("" ::"v"(cmv), "v"(dtv), "v"(sF), "v"(sid));
+            return;
+        }
+    } else {
+        if (pad || ci.len <= 0) return;
+        load_rows();
+    }
     const int g = h / (H / G);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    constexpr int nthr = 2 * Q;
     constexpr int kStepsB = Q / 32;                   // K steps of row tile B (at most)
     constexpr int kStepsA = Q / 64 > 0 ? Q / 64 : 1;  // K steps of row tile A (at most)
-    constexpr int kHVec = P * N / 8 / nthr > 0 ? P * N / 8 / nthr : 1;
     const int len = ci.len;
 
     const int ntiles = (len + 15) / 16;
@@ -2136,21 +2186,9 @@ void chunk_scan_fast_kernel(
     const uint32_t xrow = (uint32_t)H * P * 2, crow = (uint32_t)G * N * 2;
     const rsrc_t rx = make_rsrc(x + ((int64_t)ci.start * H + h) * P, (uint32_t)(len - 1) * xrow + P * 2);
     const rsrc_t rc = make_rsrc(C + ((int64_t)ci.start * G + g) * N, (uint32_t)(len - 1) * crow + N * 2);
-    // requests in the order they are needed (the wait counter is in order): cum and
-    // dt, the entering state, x, then the CB fragments of the larger row tile B
-    // (tile A's follow later)
-    const float *cumrow = cum + ((int64_t)h * max_chunks + c) * Q;
-    const float *dtrow = dtc + ((int64_t)h * max_chunks + c) * Q;
-    const int iq = tid < Q ? tid : Q - 1;          // 2 Q threads: one position each
-    const float cmv = cumrow[iq], dtv = dtrow[iq];
-    __builtin_amdgcn_sched_barrier(0);   // (the scheduler would otherwise move them last)
-    const bf16 *hin = entering + ((int64_t)c * H + h) * P * N;
-    uint4 hr[kHVec];
-#pragma unroll
-    for (int k = 0; k < kHVec; ++k) {
-        const int u = tid + nthr * k;
-        hr[k] = ld16(hin + (u >> 4) * N + 8 * (u & 15));
-    }
+    // requests in the order they are needed (the wait counter is in order), after
+    // cum, dt and the entering state: the carried state, x, then the CB fragments
+    // of the larger row tile B (tile A's follow later)
     uint4 hc[kHVec];
     if constexpr (SEG) {
         const bool has = sid >= 0;
@@ -2181,6 +2219,7 @@ void chunk_scan_fast_kernel(
         xeB[k] = buf_ld16(rx, (uint32_t)(16 * rtB + (lane & 15)) * xrow + 64 * k + 16 * (lane >> 4));
         xeA[k] = buf_ld16(rx, (uint32_t)(16 * rtA + (lane & 15)) * xrow + 64 * k + 16 * (lane >> 4));
     }
+    if constexpr (kEarly) __builtin_amdgcn_sched_barrier(0);   // (every request out first)
     scum[iq] = cmv * kLog2e;          // (threads past Q rewrite position Q - 1 with the
     sdt[iq] = dtv;                     //  same values: no branch, so the loads stay first)
 #pragma unroll
@@ -2668,29 +2707,40 @@ static void launch_state_fast(const PrefillDims &d, const void *x, const void *B
                        meta, cum, dtc, states);
 }
 
+template <int Q, bool SEG, bool BYC>
+static void launch_scan_fast_b(const PrefillDims &d, const void *x, const void *C, const float *D,
+                               const int32_t *meta, const float *cum, const float *dtc,
+                               const void *CB, const void *entering, void *y, const SegBufs &seg,
+                               unsigned nblk, hipStream_t st)
+{
+    const size_t smem = (size_t)Q * (kScanXLD * sizeof(bf16) + 2 * sizeof(float)) +
+                        (size_t)64 * (128 + 8) * sizeof(bf16) +
+                        (size_t)(Q / 32) * 64 * kScanLDR * sizeof(bf16);
+    static size_t raised = 0;
+    allow_lds(reinterpret_cast<const void *>(&chunk_scan_fast_kernel<Q, SEG, BYC>), smem, raised);
+    SSD_LAUNCH(d, SEG ? "chunk_scan_segmented" : "chunk_scan", (chunk_scan_fast_kernel<Q, SEG, BYC>), dim3(nblk), dim3(2 * Q), smem, st, d.S,
+                       d.H, d.G, d.max_chunks, static_cast<const bf16 *>(x),
+                       static_cast<const bf16 *>(C), D, meta, cum, dtc,
+                       static_cast<const bf16 *>(CB), static_cast<const bf16 *>(entering),
+                       static_cast<bf16 *>(y), seg.I, seg.F, static_cast<const bf16 *>(seg.carry));
+}
+
 template <int Q, bool SEG>
 static void launch_scan_fast_s(const PrefillDims &d, const void *x, const void *C, const float *D,
                                const int32_t *meta, const float *cum, const float *dtc,
                                const void *CB, const void *entering, void *y, const SegBufs &seg,
                                hipStream_t st)
 {
-    const size_t smem = (size_t)Q * (kScanXLD * sizeof(bf16) + 2 * sizeof(float)) +
-                        (size_t)64 * (128 + 8) * sizeof(bf16) +
-                        (size_t)(Q / 32) * 64 * kScanLDR * sizeof(bf16);
-    static size_t raised = 0;
-    allow_lds(reinterpret_cast<const void *>(&chunk_scan_fast_kernel<Q, SEG>), smem, raised);
     // (chunk, group)-interleaved XCD order once there are at least two pairs per XCD
     const int64_t pairs = (int64_t)d.max_chunks * d.G;
-    const int by_chunk = pairs >= 2 * kXcds;
+    const bool by_chunk = pairs >= 2 * kXcds;
     const int64_t rounds = (pairs + kXcds - 1) / kXcds;
     const unsigned nblk = (unsigned)(by_chunk ? rounds * kXcds * (d.H / d.G)
                                               : (int64_t)d.max_chunks * d.H);
-    SSD_LAUNCH(d, SEG ? "chunk_scan_segmented" : "chunk_scan", (chunk_scan_fast_kernel<Q, SEG>), dim3(nblk), dim3(2 * Q), smem, st, d.S,
-                       d.H, d.G, d.max_chunks, static_cast<const bf16 *>(x),
-                       static_cast<const bf16 *>(C), D, meta, cum, dtc,
-                       static_cast<const bf16 *>(CB), static_cast<const bf16 *>(entering),
-                       static_cast<bf16 *>(y), seg.I, seg.F, static_cast<const bf16 *>(seg.carry),
-                       by_chunk);
+    if (by_chunk)
+        launch_scan_fast_b<Q, SEG, true>(d, x, C, D, meta, cum, dtc, CB, entering, y, seg, nblk, st);
+    else
+        launch_scan_fast_b<Q, SEG, false>(d, x, C, D, meta, cum, dtc, CB, entering, y, seg, nblk, st);
 }
 
 template <int Q>

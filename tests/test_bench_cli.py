@@ -60,8 +60,11 @@ def test_launch_bytes_and_flops_of_the_layer_prefill():
 
 def test_kernel_names_map_to_launches():
     n = lambda k: bench.launch_name(k)[0]
-    assert n("_ZN3ssd22chunk_scan_fast_kernelILi256ELb1EEEviii") == "chunk_scan_segmented"
-    assert n("_ZN3ssd22chunk_scan_fast_kernelILi256ELb0EEEviii") == "chunk_scan"
+    assert n("_ZN3ssd22chunk_scan_fast_kernelILi256ELb1ELb1EEEviii") == "chunk_scan_segmented"
+    assert n("_ZN3ssd22chunk_scan_fast_kernelILi256ELb0ELb1EEEviii") == "chunk_scan"
+    assert n("_ZN3ssd22chunk_scan_fast_kernelILi128ELb0ELb0EEEviii") == "chunk_scan"
+    assert n("void ssd::chunk_scan_fast_kernel<256, true, false>(int") == "chunk_scan_segmented"
+    assert n("void ssd::chunk_scan_fast_kernel<256, false, true>(int") == "chunk_scan"
     assert n("_ZN3ssd22state_scan_fast_kernelILi256ELb0ELb1ELb0EfEEvii") == \
         "chunk_state_passing_segmented"
     assert n("_ZN3ssd22state_scan_fast_kernelILi256ELb1ELb0ELb0EfEEvii") == "chunk_state_passing"
