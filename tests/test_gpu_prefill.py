@@ -453,6 +453,9 @@ OWN_CASES = [
     # of 64 (S > 64), empty sequences, a 1-token chunk
     ((40, 300, 700, 5), 16, 2, 128, F32, True),
     ((600, 32, 1600), 8, 1, 256, BF16, True),
+    # more state blocks than one round (5 x 64 x 2 = 640): the CB blocks go out
+    # after the first 512, their 30 padded to 32
+    ((300, 900, 40, 1200, 130), 64, 2, 256, F32, True),
     ((100, 900, 0, 20, 400), 64, 8, 256, F32, False),
     ((1500,), 8, 1, 128, F32, False),
     ((257, 0, 3, 129), 6, 3, 64, BF16, False),
