@@ -2107,8 +2107,8 @@ void chunk_scan_fast_kernel(
     // are dealt to the XCDs as u mod 8, each with all heads of its group: every
     // XCD gets the same share of real chunks, whatever the padding of max_chunks
     // and however the chunk lengths vary along the batch (the grid is padded to
-    // whole rounds of 8 pairs; the padding blocks leave at once, after their
-    // requests with kEarly). Otherwise each XCD takes one contiguous range of
+    // whole rounds of 8 pairs; the padding blocks leave at once, with kEarly
+    // after requests that read nothing). Otherwise each XCD takes one contiguous range of
     // units in order c H + h. Either way the heads that read one (chunk,
     // group)'s C and CB share an L2.
     int h, c;
@@ -2145,13 +2145,17 @@ void chunk_scan_fast_kernel(
     float cmv, dtv;
     uint4 hr[kHVec];
     auto load_rows = [&]() {
-        cmv = cumrow[iq];
-        dtv = dtrow[iq];
+        // (through resources that are empty for a padding block: nothing read)
+        const rsrc_t rcm = make_rsrc(cumrow, pad ? 0u : (uint32_t)Q * 4);
+        const rsrc_t rdt = make_rsrc(dtrow, pad ? 0u : (uint32_t)Q * 4);
+        const rsrc_t rh = make_rsrc(hin, pad ? 0u : (uint32_t)(P * N * 2));
+        cmv = buf_ldf(rcm, (uint32_t)iq * 4);
+        dtv = buf_ldf(rdt, (uint32_t)iq * 4);
         __builtin_amdgcn_sched_barrier(0);   // (the scheduler would otherwise move them last)
 #pragma unroll
         for (int k = 0; k < kHVec; ++k) {
             const int u = tid + nthr * k;
-            hr[k] = ld16(hin + (u >> 4) * N + 8 * (u & 15));
+            hr[k] = buf_ld16(rh, (uint32_t)((u >> 4) * N + 8 * (u & 15)) * 2);
         }
     };
     if constexpr (kEarly) {
