@@ -257,3 +257,41 @@ def random_problem(seed: int, seqlens: Sequence[int], nheads: int, headdim: int,
 def nan_cache(num_slots: int, H: int, P: int, N: int, dtype: torch.dtype) -> torch.Tensor:
     """A state cache whose every slot is NaN: slots a call must not read stay NaN."""
     return torch.full((num_slots, H, P, N), float("nan"), dtype=dtype)
+
+
+@dataclasses.dataclass
+class LongPrefillInputs:
+    x: torch.Tensor          # [T,H,P]  bf16, on the given device
+    dt: torch.Tensor         # [T,H]    bf16 (post-activation)
+    A: torch.Tensor          # [H] float32
+    B: torch.Tensor          # [T,G,N]  bf16
+    C: torch.Tensor          # [T,G,N]  bf16
+    D: torch.Tensor          # [H] float32
+    cu_seqlens: torch.Tensor  # [S+1] int32
+    state_indices: torch.Tensor  # [S] int32
+
+
+def long_prefill(seed: int, seqlens: Sequence[int], nheads: int, headdim: int, d_state: int,
+                 ngroups: int, device) -> LongPrefillInputs:
+    """A prefill too large to draw on the host in float64 (tests of the largest
+    tensors): the same distributions as token_block, drawn by torch's seeded
+    generator on ``device`` in float32 and rounded to bf16 there. Slot s for
+    sequence s; layer parameters from layer_params."""
+    lens = tuple(int(v) for v in seqlens)
+    T, S = int(sum(lens)), len(lens)
+    A, dt_bias, D = layer_params(seed, nheads)
+    g = torch.Generator(device=device).manual_seed(seed)
+    bf = torch.bfloat16
+    x = torch.randn(T, nheads, headdim, generator=g, device=device).to(bf)
+    z = torch.randn(T, nheads, generator=g, device=device)
+    bias = torch.tensor(dt_bias, dtype=torch.float32, device=device)
+    dt = torch.clamp(torch.nn.functional.softplus(z + bias[None, :]), DT_MIN, DT_MAX).to(bf)
+    scale = 1.0 / math.sqrt(d_state)
+    B = (torch.randn(T, ngroups, d_state, generator=g, device=device) * scale).to(bf)
+    C = (torch.randn(T, ngroups, d_state, generator=g, device=device) * scale).to(bf)
+    cu = np.zeros(S + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lens)
+    return LongPrefillInputs(
+        x=x, dt=dt, A=to_dtype(A, torch.float32).to(device), B=B, C=C,
+        D=to_dtype(D, torch.float32).to(device), cu_seqlens=torch.from_numpy(cu).to(device),
+        state_indices=torch.arange(S, dtype=torch.int32, device=device))

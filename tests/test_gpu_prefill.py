@@ -783,3 +783,28 @@ def test_segmented_state_passing(case):
     torch.cuda.synchronize()
     assert_close(g_cache.cpu()[used], to64(after[used]), looser(BF16, ts),
                  "segmented vs unsegmented final states")
+
+
+@pytest.mark.parametrize("nseq", [1, 4], ids=["one_sequence_segmented", "four_sequences_ranked"])
+def test_long_prefill_2gb_tensors_sampled_heads(nseq):
+    """The largest tensors: 262144 tokens x 64 heads x headdim 64, so x and y hold
+    2.1 GB of bf16 each (byte offsets past 2^31) and the entering states 1.07 GB
+    (1025 chunk slots). One sequence takes the segmented state pass (4 segments of
+    256 chunks), four take the longest-chain-first pass (chains of 256 chunks).
+    Heads 0 and 41 of y and of every final state against the oracle's recurrence
+    over the same inputs (the heads are independent; B and C are shared, G = 1)."""
+    ssd = _ssd()
+    T, H, P, N, G, Q = 262144, 64, 64, 128, 1, 256
+    inp = sy.long_prefill(7, [T // nseq] * nseq, H, P, N, G, DEV)
+    p = ssd.make_problem(T, nseq, H, P, N, G, Q, nseq, BF16, F32)
+    cache = torch.full((nseq, H, P, N), float("nan"), device=DEV)
+    y = torch.empty(T, H, P, dtype=BF16, device=DEV)
+    ssd.ssd_combined_varlen(p, inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.cu_seqlens, cache,
+                            inp.state_indices, None, y, None, ssd.alloc_workspace(p, DEV))
+    torch.cuda.synchronize()
+    heads = [0, 41]
+    ref_y, ref_fin, _ = oracle.recurrence(
+        inp.x[:, heads].cpu(), inp.dt[:, heads].cpu(), inp.A[heads].cpu(), inp.B.cpu(),
+        inp.C.cpu(), inp.D[heads].cpu(), inp.cu_seqlens.cpu(), Q)
+    assert_close(y[:, heads].cpu(), ref_y, BF16, "long prefill y")
+    assert_close(cache[:, heads].cpu(), ref_fin, BF16, "long prefill final states")
