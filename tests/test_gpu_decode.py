@@ -145,3 +145,36 @@ def test_c4_mtp_verify_full():
     used = set(d.state_indices.tolist())
     others = [k for k in range(cfg.num_slots) if k not in used]
     assert torch.isnan(after[others].float()).all()
+
+
+@pytest.mark.parametrize("keep", [True, False], ids=["per_token_states", "cache_written"])
+def test_state_update_cache_past_4gb(keep):
+    """A bf16 cache of 2560 slots x 128 heads x 64 x 128 (5.4 GB): the requests'
+    slots lie past 2^31 and 2^32 bytes. y, the per-token states and the written
+    slots against the oracle (run on a cache holding only those slots, renumbered);
+    a NaN slot next to a written one stays NaN."""
+    ssd = _ssd()
+    R, T, H, P, N, G, slots = 4, 3, 128, 64, 128, 8, 2560
+    cfg = sy.DecodeConfig("dec_big", R, T, H, P, N, G, BF16, BF16, slots, 8, 321)
+    d = sy.make_decode(cfg)
+    sidx = torch.tensor([slots - 1, 2100, 1, 2400], dtype=torch.int32)
+    g = torch.Generator().manual_seed(5)
+    small = (torch.randn(R, H, P, N, generator=g) * 0.05).to(BF16)
+    g_cache = torch.full((slots, H, P, N), float("nan"), dtype=BF16, device=DEV)
+    g_cache[sidx.long().to(DEV)] = small.to(DEV)
+    up = ssd.make_ssu_problem(R, T, H, P, N, G, slots, BF16, BF16)
+    y = torch.empty(R, T, H, P, dtype=BF16, device=DEV)
+    inter = torch.empty(R, T, H, P, N, dtype=BF16, device=DEV) if keep else None
+    ssd.selective_state_update(up, g_cache, sidx.to(DEV), d.x.to(DEV), d.dt.to(DEV),
+                               d.A.to(DEV), d.B.to(DEV), d.C.to(DEV), d.D.to(DEV), y, inter)
+    torch.cuda.synchronize()
+    ref = oracle.state_update(small, torch.arange(R, dtype=torch.int32), d.x, d.dt, d.A, d.B,
+                              d.C, d.D, keep)
+    assert_close(y.cpu(), ref["y"], BF16, "y", normalised=False)
+    after = g_cache[sidx.long().to(DEV)].cpu()
+    if keep:
+        assert_close(inter.cpu(), ref["states"], BF16, "per-token states")
+        assert torch.equal(after.view(torch.int16), small.view(torch.int16))
+    else:
+        assert_close(after, ref["final"], BF16, "final states")
+    assert torch.isnan(g_cache[slots - 2].float()).all()

@@ -151,3 +151,51 @@ def test_c4_replay_full():
     cfg = sy.C4
     cache = workload_cache(sy.make_decode(cfg))
     _run_steps(cfg, 16, cache, steps=6)
+
+
+def test_replay_slots_past_4gb():
+    """Checkpoints of 2560 slots x 128 heads x 64 x 128 in bf16 (5.4 GB) and input
+    rings of 32 tokens: the requests' slots lie past 2^31 and 2^32 bytes of the
+    checkpoints. Three verify + advance steps and the materialisation against the
+    oracle's state machine on a layer holding only those slots (renumbered): y,
+    the rings bit for bit, the cursors and the checkpoints after every step."""
+    ssd = _ssd()
+    R, T, H, P, N, G, W, slots = 4, 3, 128, 64, 128, 8, 32, 2560
+    cfg = sy.DecodeConfig("replay_big", R, T, H, P, N, G, BF16, BF16, slots, 8, 654)
+    sidx = torch.tensor([slots - 1, 2100, 1, 2400], dtype=torch.int32)
+    g = torch.Generator().manual_seed(9)
+    small = (torch.randn(R, H, P, N, generator=g) * 0.05).to(BF16)
+    g_ckpt = torch.full((slots, H, P, N), float("nan"), dtype=BF16, device=DEV)
+    g_ckpt[sidx.long().to(DEV)] = small.to(DEV)
+    up = ssd.make_ssu_problem(R, T, H, P, N, G, slots, BF16, BF16)
+    rings = ssd.alloc_replay_rings(up, W, DEV)
+    layer = oracle_replay.ReplayLayer(small, W, G, BF16)
+    oidx = torch.arange(R, dtype=torch.int32)
+    at = sidx.long().to(DEV)
+    A = cfg_A(cfg)
+    for step in range(3):
+        d = _step_inputs(cfg, step, sidx)
+        y = torch.empty(R, T, H, P, dtype=BF16, device=DEV)
+        ssd.ssd_replay_update(up, W, g_ckpt, rings["ring_x"], rings["ring_dt"], rings["ring_B"],
+                              rings["cursor"], sidx.to(DEV), d.x.to(DEV), d.dt.to(DEV),
+                              A.to(DEV), d.B.to(DEV), d.C.to(DEV), d.D.to(DEV), y)
+        yref = oracle_replay.replay_update(layer, oidx, d.x, d.dt, A, d.B, d.C, d.D)
+        torch.cuda.synchronize()
+        assert_close(y.cpu(), yref, BF16, f"step {step} y", normalised=False)
+        for name, ref in (("ring_x", layer.ring_x), ("ring_dt", layer.ring_dt),
+                          ("ring_B", layer.ring_B)):
+            got = rings[name][at].cpu()
+            assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8)), f"step {step}: {name}"
+        assert_close(g_ckpt[at].cpu(), layer.ckpt, BF16, f"step {step} checkpoints")
+        acc = d.num_accepted
+        ssd.ssd_replay_advance(up, W, rings["cursor"], sidx.to(DEV), acc.to(DEV))
+        oracle_replay.replay_advance(layer, oidx, acc.numpy(), T)
+        torch.cuda.synchronize()
+        assert np.array_equal(rings["cursor"][at].cpu().numpy(), layer.cursor), step
+    ssd.ssd_replay_materialize(up, W, g_ckpt, rings["ring_x"], rings["ring_dt"], rings["ring_B"],
+                               rings["cursor"], sidx.to(DEV), A.to(DEV))
+    oracle_replay.replay_materialize(layer, oidx, A)
+    torch.cuda.synchronize()
+    assert_close(g_ckpt[at].cpu(), layer.ckpt, BF16, "materialised checkpoints")
+    assert np.array_equal(rings["cursor"][at].cpu().numpy(), layer.cursor)
+    assert torch.isnan(g_ckpt[slots - 2].float()).all()
