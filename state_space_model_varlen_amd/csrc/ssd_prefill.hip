@@ -1354,17 +1354,25 @@ void state_scan_fast_kernel(
     };
     // cum at position t of the chunk staged in xs (after the barrier that
     // follows scan_chunk): the totals of the blocks before t's, then its own
-    // prefix sum; also its dt
+    // prefix sum; also its dt. The running sums of the block totals are read
+    // from the pads once per step (read_boff), in the order the cumsum kernel
+    // adds them.
+    float boff[J];   // the totals of the blocks before block j
+    auto read_boff = [&]() {
+        boff[0] = 0.0f;
+#pragma unroll
+        for (int j = 1; j < J; ++j) {
+            const float tj = reinterpret_cast<const float *>(xs + (j - 1) * LDX + P)[2];
+            boff[j] = j == 1 ? tj : boff[j - 1] + tj;
+        }
+    };
     auto cum_at = [&](int t, float &dtv) {
         const float2 cd = *reinterpret_cast<const float2 *>(xs + t * LDX + P);
         dtv = cd.y;
         const int jb = t >> 6;
         float off = 0.0f;
 #pragma unroll
-        for (int j = 0; j < J - 1; ++j) {
-            const float tj = reinterpret_cast<const float *>(xs + j * LDX + P)[2];
-            if (j < jb) off = j == 0 ? tj : off + tj;
-        }
+        for (int j = 1; j < J; ++j) off = jb == j ? boff[j] : off;
         return jb == 0 ? cd.x : off + cd.x;
     };
 
@@ -1383,6 +1391,7 @@ void state_scan_fast_kernel(
         // chunk's pads hold zeros)
         float cl = R.cl;
         if constexpr (OWN) {
+            read_boff();
             float unused;
             cl = cum_at(len > 0 ? len - 1 : 0, unused);
         }
