@@ -259,42 +259,46 @@ __device__ __forceinline__ f16 sr_f16(float x, uint32_t d)
 // M values (M even) rounded as by sr_f16, packed two fp16 values per word
 // (value 2 j in the low half of out[j]); value 2 j draws the low 16 bits of
 // w[j], value 2 j + 1 the high 16 bits. In the fp16 normal range
-// (2^-14 <= |x| <= 65504) only the carry step runs: t = (bits(x) + 8191 -
-// (d >> 3)) >> 13 holds |x|'s kept bits in its low 16 (the sign bit 31 does
-// not reach them), and adding 0x4000 modulo 2^16 rebases the exponent
-// (t - (112 << 10)). The general rule runs behind a wave-uniform branch,
-// when some lane holds a value outside that range.
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+// (2^-14 <= |x| <= 65504) only the carry step runs, and gfx950 has it as one
+// instruction: v_cvt_sr_f16_f32 adds the top 13 bits of its 32-bit random
+// operand to the 13 float32 mantissa bits that fp16 drops, truncates, and
+// writes the fp16 result with its sign into the half of the destination that
+// its word-select operand names (the other half kept). The carry step adds
+// 8191 - (d >> 3), which for d = the low 16 bits of w is the top 13 bits of
+// ~w << 16, and for d = the high 16 bits the top 13 bits of ~w itself. (The
+// instruction's use of its operand was checked on the device value by value
+// against this carry rule over the whole normal range; below 2^-14 it still
+// adds 13 bits at the normal-range position, which is not the rule there.
+// The bit-exact tests compare every store with the oracle's rounding.)
+// Value slot i of the M is redone with the general rule, behind a
+// wave-uniform branch, when some lane holds a value outside the normal range
+// in that slot: state values near zero are common, and deciding per slot
+// rather than once for all M keeps most slots on the one-instruction path.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 template <int M>
 __device__ __forceinline__ void sr_f16_pairs(const float *v, const uint32_t *w, uint32_t *out)
 {
     static_assert(M % 2 == 0, "pairs");
-    uint32_t xb[M], worst = 0;
 #pragma unroll
-    for (int i = 0; i < M; ++i) {
-        xb[i] = __builtin_bit_cast(uint32_t, v[i]);
-        // 2 (|x| bits - bits(2^-14)), modulo 2^32: above 2 (bits(65504) - bits(2^-14))
-        // for |x| < 2^-14, |x| > 65504, infinities and NaNs
-        const uint32_t off = (xb[i] << 1) - (0x38800000u << 1);
-        worst = off > worst ? off : worst;
-    }
-    if (__builtin_amdgcn_ballot_w64(worst > ((0x477FE000u - 0x38800000u) << 1)) == 0) {
+    for (int j = 0; j < M / 2; ++j) {
+        const uint32_t nw = ~w[j];
+        f16x2 q = {};
+        q = __builtin_amdgcn_cvt_sr_f16_f32(q, v[2 * j], nw << 16, false);
+        q = __builtin_amdgcn_cvt_sr_f16_f32(q, v[2 * j + 1], nw, true);
+        uint32_t r = __builtin_bit_cast(uint32_t, q);
 #pragma unroll
-        for (int j = 0; j < M / 2; ++j) {
-            const uint32_t ta = (xb[2 * j] + (((w[j] >> 3) & 0x1FFFu) ^ 0x1FFFu)) >> 13;
-            const uint32_t tb = (xb[2 * j + 1] + ((w[j] >> 19) ^ 0x1FFFu)) >> 13;
-            u16x2 m = {(unsigned short)ta, (unsigned short)tb};
-            m += (u16x2){0x4000, 0x4000};
-            const uint32_t sign = ((xb[2 * j] >> 16) & 0x8000u) | (xb[2 * j + 1] & 0x80000000u);
-            out[j] = __builtin_bit_cast(uint32_t, m) | sign;
+        for (int h = 0; h < 2; ++h) {
+            // 2 (|x| bits - bits(2^-14)), modulo 2^32: above 2 (bits(65504) - bits(2^-14))
+            // for |x| < 2^-14, |x| > 65504, infinities and NaNs
+            const uint32_t off = (__builtin_bit_cast(uint32_t, v[2 * j + h]) << 1) -
+                                 (0x38800000u << 1);
+            if (__builtin_amdgcn_ballot_w64(off > ((0x477FE000u - 0x38800000u) << 1)) != 0) {
+                const uint32_t g = __builtin_bit_cast(
+                    uint16_t, sr_f16(v[2 * j + h], h ? w[j] >> 16 : w[j] & 0xFFFFu));
+                r = h ? (r & 0xFFFFu) | (g << 16) : (r & 0xFFFF0000u) | g;
+            }
         }
-    } else {
-#pragma unroll
-        for (int j = 0; j < M / 2; ++j) {
-            const uint32_t lo = __builtin_bit_cast(uint16_t, sr_f16(v[2 * j], w[j] & 0xFFFFu));
-            const uint32_t hi = __builtin_bit_cast(uint16_t, sr_f16(v[2 * j + 1], w[j] >> 16));
-            out[j] = lo | (hi << 16);
-        }
+        out[j] = r;
     }
 }
 

@@ -59,6 +59,27 @@ def test_round_f16_bit_exact(seed, rounds, kind):
     assert torch.equal(out.cpu().view(torch.int16), xg.cpu().half().view(torch.int16))
 
 
+@pytest.mark.parametrize("seed,rounds,kind", [(0xFEEDFACE, 5, 2), (-9, 10, 1)])
+def test_round_f16_normal_range_bit_exact(seed, rounds, kind):
+    """Only values in the fp16 normal range (2^-14 .. 65504, both signs, every
+    binade, the end points included), so every wave takes the carry-step path
+    and none the general rule."""
+    ssd = _ssd()
+    g = np.random.default_rng(182)
+    n = 64 * 256 * 4 + 13                # many waves and a ragged tail
+    mag = np.exp2(g.uniform(-14.0, 16.0, n)).clip(2.0 ** -14, 65504.0)
+    mag[:4] = [2.0 ** -14, 65504.0, 1.0, 2.0 ** -14 * (1 + 2.0 ** -12)]
+    x = (mag * np.where(g.random(n) < 0.5, -1.0, 1.0)).astype(np.float32)
+    out = torch.empty(n, dtype=F16, device=DEV)
+    ssd.ssd_round_f16(torch.from_numpy(x).to(DEV), out, sr_seed=_seed(seed), sr_rounds=rounds,
+                      kind=kind)
+    torch.cuda.synchronize()
+    want = rnd.stochastic_round_f16(x, rnd.draws_for(n, _u64(seed), kind, rounds))
+    got = out.cpu().numpy()
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16)), \
+        int(np.sum(got.view(np.uint16) != want.view(np.uint16)))
+
+
 def _f16_step_bound(ref):
     """One fp16 step at the value (the spacing of the bracketing fp16 values)."""
     a = np.abs(np.asarray(ref, dtype=np.float64)).astype(np.float32)
