@@ -80,6 +80,35 @@ def test_round_f16_normal_range_bit_exact(seed, rounds, kind):
         int(np.sum(got.view(np.uint16) != want.view(np.uint16)))
 
 
+def test_round_f16_one_off_range_slot_per_wave():
+    """Normal-range values everywhere except one value per 512 (one wave of
+    ssd_round_f16, 8 consecutive values per lane): in wave k, lane 7 k mod 64 holds
+    an fp16 subnormal, a zero, an overflow or a non-finite value in value slot
+    k mod 8. Every wave then mixes slots that take the general rule with slots that
+    do not; every 9th wave is left all normal."""
+    ssd = _ssd()
+    g = np.random.default_rng(183)
+    waves = 72
+    n = 512 * waves + 5
+    mag = np.exp2(g.uniform(-14.0, 16.0, n)).clip(2.0 ** -14, 65504.0)
+    x = (mag * np.where(g.random(n) < 0.5, -1.0, 1.0)).astype(np.float32)
+    odd = np.array([3e-6, -4.5e-7, 0.0, -0.0, 6.0e-5, 2.0 ** -24, 65519.0, -70000.0, np.inf,
+                    np.nan, 1e-40, 2.0 ** -14 * (1 - 2.0 ** -20)], dtype=np.float32)
+    for k in range(waves):
+        if k % 9 == 8:
+            continue
+        x[512 * k + 8 * ((7 * k) % 64) + k % 8] = odd[k % len(odd)]
+    out = torch.empty(n, dtype=F16, device=DEV)
+    ssd.ssd_round_f16(torch.from_numpy(x).to(DEV), out, sr_seed=_seed(0x51075107), sr_rounds=5,
+                      kind=3)
+    torch.cuda.synchronize()
+    want = rnd.stochastic_round_f16(x, rnd.draws_for(n, _u64(0x51075107), 3, 5))
+    got = out.cpu().numpy().view(np.uint16)
+    want = want.view(np.uint16)
+    nan = np.isnan(x)
+    assert np.array_equal(got[~nan], want[~nan]), int(np.sum(got[~nan] != want[~nan]))
+    assert np.all(np.isnan(out.cpu().numpy()[nan]))
+
 def _f16_step_bound(ref):
     """One fp16 step at the value (the spacing of the bracketing fp16 values)."""
     a = np.abs(np.asarray(ref, dtype=np.float64)).astype(np.float32)
