@@ -246,7 +246,7 @@ def load_counters(shape, name):
 
 def profile_commands(shape):
     sel = "--headline-only" if shape == "layer_L4096" else f"--shape {shape}"
-    out = f"gpurun_out/prof/{shape}"
+    out = f"prof_raw/{shape}"
     run = f"python3 bench.py {sel} --no-cpu-baseline"
     return [
         f"rocprofv3 --kernel-trace --stats --output-format csv -d {out}/trace -o run -- {run}",
