@@ -274,6 +274,7 @@ __device__ __forceinline__ f16 sr_f16(float x, uint32_t d)
 // wave-uniform branch, when some lane holds a value outside the normal range
 // in that slot: state values near zero are common, and deciding per slot
 // rather than once for all M keeps most slots on the one-instruction path.
+// Inside the branch the lanes in the normal range keep the convert's result.
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 template <int M>
 __device__ __forceinline__ void sr_f16_pairs(const float *v, const uint32_t *w, uint32_t *out)
@@ -293,8 +294,19 @@ __device__ __forceinline__ void sr_f16_pairs(const float *v, const uint32_t *w, 
             const uint32_t off = (__builtin_bit_cast(uint32_t, v[2 * j + h]) << 1) -
                                  (0x38800000u << 1);
             if (__builtin_amdgcn_ballot_w64(off > ((0x477FE000u - 0x38800000u) << 1)) != 0) {
-                const uint32_t g = __builtin_bit_cast(
-                    uint16_t, sr_f16(v[2 * j + h], h ? w[j] >> 16 : w[j] & 0xFFFFu));
+                // sr_f16's rule where the convert's result does not apply: below
+                // 2^-14, floor(t) units of 2^-24 plus one when d / 2^16 < t - floor(t)
+                // (t = |x| 2^24, every step exact; the truncating conversion is the
+                // floor of t >= 0); above 65504 and for non-finite values, nearest
+                const float xv = v[2 * j + h];
+                const float a = fabsf(xv);
+                const float t = fminf(a, 0x1p-14f) * 0x1p24f;   // (at most 2^10)
+                const uint32_t d = h ? w[j] >> 16 : w[j] & 0xFFFFu;
+                const uint32_t sb =
+                    (uint32_t)t + ((float)d < __builtin_amdgcn_fractf(t) * 65536.0f ? 1u : 0u);
+                uint32_t g = h ? r >> 16 : r & 0xFFFFu;
+                g = a < 0x1p-14f ? sb | ((__builtin_bit_cast(uint32_t, xv) >> 16) & 0x8000u) : g;
+                g = a <= 65504.0f ? g : (uint32_t)__builtin_bit_cast(uint16_t, static_cast<f16>(xv));
                 r = h ? (r & 0xFFFFu) | (g << 16) : (r & 0xFFFF0000u) | g;
             }
         }
